@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for the Gated DeltaNet-2 prefill and decode workloads.
+
+This module only draws and shapes random numbers; it holds none of the recurrence's
+arithmetic. Both the HIP path's tests and the oracle's tests take their inputs from here.
+
+Distributions follow the layer the pages describe: q and k pass through an L2 norm per head
+and the gates are sigmoids of token projections (page "NVIDIA представила Gated DeltaNet-2 с
+канал-wise гейтами …", paragraphs "Техническая схема" and "Архитектурно"); the state is
+262,144 floats per layer per batch element, i.e. 16 heads of 128x128 (page "NVIDIA улучшила
+память LLM без роста затрат на контекст", section "Аналитика"). Since no trained projections
+exist here, the pre-activations are standard normals:
+
+    q, k  = L2normalize(N(0,1)) over d_k          v = N(0,1)
+    b, w  = sigmoid(N(0,1)) per channel           alpha = sigmoid(N(alpha_mu, 1)) per key channel
+    S0    = N(0, s0_std^2) (or zero)              beta (scalar gates) = sigmoid(N(0,1)) per token
+
+Draw order (numpy backend): q, k, v, b, w, alpha, S0, then beta. Values are drawn in float32
+and rounded to bfloat16 with round-to-nearest-even when dtype is bf16; the same rounded
+tensors go to the GPU and to the oracle.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One named input recipe (shapes, dtype and distributions)."""
+    name: str
+    B: int
+    T: int
+    H: int
+    d_k: int
+    d_v: int
+    dtype: str = "bf16"  # "bf16" or "fp32": dtype of q, k, v, alpha, b, w
+    alpha_mu: float = 3.0
+    s0_std: float = 0.1  # 0 => zero initial state
+    gates: str = "general"  # "general", "gdn" (scalar alpha and beta), "kda" (scalar beta)
+    seed: int = 20250
+
+
+# Named workloads. Sizes follow the pages' 1.3B setting (16 heads of 128x128).
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", B=1, T=256, H=2, d_k=32, d_v=32, dtype="fp32",
+                          s0_std=0.0, seed=20250),
+    "prefill_1p3b": Workload("prefill_1p3b", B=8, T=4096, H=16, d_k=128, d_v=128, seed=20251),
+    "long_prefill": Workload("long_prefill", B=1, T=131072, H=16, d_k=128, d_v=128,
+                             alpha_mu=5.0, seed=20252),
+    "gdn_scalar": Workload("gdn_scalar", B=8, T=4096, H=16, d_k=128, d_v=128, gates="gdn",
+                           seed=20253),
+    "kda_scalar": Workload("kda_scalar", B=8, T=4096, H=16, d_k=128, d_v=128, gates="kda",
+                           seed=20253),
+}
+
+DECODE_WORKLOAD = dict(B=256, H=16, d_k=128, d_v=128, steps=1000, alpha_mu=3.0, s0_std=0.1,
+                       seed=20254)
+
+
+def scaled(wl: Workload, **changes) -> Workload:
+    """The same recipe at other sizes (e.g. fewer tokens for a test)."""
+    return dataclasses.replace(wl, **changes)
+
+
+def _torch_dtype(name: str):
+    return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+
+
+def _l2n(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-12)).astype(np.float32)
+
+
+def make_inputs(wl: Workload, *, device: str = "cpu") -> dict:
+    """Draw one workload's inputs.
+
+    Returns a dict of torch tensors on `device`: q, k, alpha, b [B, T, H, d_k];
+    v, w [B, T, H, d_v]; S0 [B, H, d_k, d_v] float32 or None. With scalar gates,
+    alpha is [B, T, H] for "gdn", b holds beta as [B, T, H] and w is None; the keys
+    "alpha_scalar" and "beta_scalar" say which. Generation uses numpy's PCG64 on the host.
+    """
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
+    f32 = np.float32
+    q = _l2n(rng.standard_normal((B, T, H, dk), dtype=f32))
+    k = _l2n(rng.standard_normal((B, T, H, dk), dtype=f32))
+    v = rng.standard_normal((B, T, H, dv), dtype=f32)
+    b = _sigmoid(rng.standard_normal((B, T, H, dk), dtype=f32))
+    w = _sigmoid(rng.standard_normal((B, T, H, dv), dtype=f32))
+    a_shape = (B, T, H) if wl.gates == "gdn" else (B, T, H, dk)
+    alpha = _sigmoid(rng.standard_normal(a_shape, dtype=f32) + f32(wl.alpha_mu))
+    S0 = None
+    if wl.s0_std > 0:
+        S0 = rng.standard_normal((B, H, dk, dv), dtype=f32) * f32(wl.s0_std)
+    beta_scalar = wl.gates in ("gdn", "kda")
+    if beta_scalar:
+        b = _sigmoid(rng.standard_normal((B, T, H), dtype=f32))
+        w = None
+    dt = _torch_dtype(wl.dtype)
+
+    def t(x):
+        return None if x is None else torch.from_numpy(x).to(dt).to(device)
+
+    return dict(q=t(q), k=t(k), v=t(v), alpha=t(alpha), b=t(b), w=t(w),
+                S0=None if S0 is None else torch.from_numpy(S0).to(device),
+                alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)
+
+
+def make_decode_inputs(B: int, H: int, d_k: int, d_v: int, steps: int, *, seed: int,
+                       alpha_mu: float = 3.0, s0_std: float = 0.1, dtype: str = "bf16",
+                       device: str = "cpu", generator: str = "numpy") -> dict:
+    """Inputs for `steps` consecutive single-token steps.
+
+    Returns q, k, alpha, b [steps, B, H, d_k]; v, w [steps, B, H, d_v]; S0 [B, H, d_k, d_v].
+    generator="numpy" draws on the host (PCG64, as make_inputs); generator="torch" draws with
+    a seeded torch.Generator on `device` (Philox on a GPU), which is much faster for the
+    thousand-step decode workload. Both are deterministic for a given seed.
+    """
+    dt = _torch_dtype(dtype)
+    if generator == "numpy":
+        rng = np.random.Generator(np.random.PCG64(seed))
+        f32 = np.float32
+        q = _l2n(rng.standard_normal((steps, B, H, d_k), dtype=f32))
+        k = _l2n(rng.standard_normal((steps, B, H, d_k), dtype=f32))
+        v = rng.standard_normal((steps, B, H, d_v), dtype=f32)
+        b = _sigmoid(rng.standard_normal((steps, B, H, d_k), dtype=f32))
+        w = _sigmoid(rng.standard_normal((steps, B, H, d_v), dtype=f32))
+        alpha = _sigmoid(rng.standard_normal((steps, B, H, d_k), dtype=f32) + f32(alpha_mu))
+        S0 = rng.standard_normal((B, H, d_k, d_v), dtype=f32) * f32(s0_std)
+        out = {n: torch.from_numpy(x).to(dt).to(device)
+               for n, x in dict(q=q, k=k, v=v, b=b, w=w, alpha=alpha).items()}
+        out["S0"] = torch.from_numpy(S0).to(device)
+        return out
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+    def l2n(x):
+        return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    q = l2n(randn(steps, B, H, d_k)).to(dt)
+    k = l2n(randn(steps, B, H, d_k)).to(dt)
+    v = randn(steps, B, H, d_v).to(dt)
+    b = torch.sigmoid(randn(steps, B, H, d_k)).to(dt)
+    w = torch.sigmoid(randn(steps, B, H, d_v)).to(dt)
+    alpha = torch.sigmoid(randn(steps, B, H, d_k) + alpha_mu).to(dt)
+    S0 = randn(B, H, d_k, d_v) * s0_std
+    return dict(q=q, k=k, v=v, b=b, w=w, alpha=alpha, S0=S0)
+
+
+def make_inputs_torch(wl: Workload, *, device: str) -> dict:
+    """As make_inputs, but drawn with a seeded torch.Generator on `device`.
+
+    Used where host generation would dominate (the full-size benchmark workloads);
+    deterministic for a given seed, with the same recipe as make_inputs.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed)
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
+    dt = _torch_dtype(wl.dtype)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+    def l2n(x):
+        return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    q = l2n(randn(B, T, H, dk)).to(dt)
+    k = l2n(randn(B, T, H, dk)).to(dt)
+    v = randn(B, T, H, dv).to(dt)
+    b = torch.sigmoid(randn(B, T, H, dk)).to(dt)
+    w = torch.sigmoid(randn(B, T, H, dv)).to(dt)
+    a_shape = (B, T, H) if wl.gates == "gdn" else (B, T, H, dk)
+    alpha = torch.sigmoid(randn(*a_shape) + wl.alpha_mu).to(dt)
+    S0 = randn(B, H, dk, dv) * wl.s0_std if wl.s0_std > 0 else None
+    beta_scalar = wl.gates in ("gdn", "kda")
+    if beta_scalar:
+        b = torch.sigmoid(randn(B, T, H)).to(dt)
+        w = None
+    return dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=S0,
+                alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)

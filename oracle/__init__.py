@@ -1,0 +1,151 @@
+"""fp64 CPU oracle for the Gated DeltaNet-2 recurrence.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import this package. The product path (``gated_delta_rule_25_amd``) never
+imports it and shares no code with it.
+
+The arithmetic lives in ``gdn2_oracle.c`` (plain C, float64, one token at a time); this
+module only compiles it with gcc, converts arrays to contiguous float64 and calls it.
+
+Source of the update rule: the page "NVIDIA представила Gated DeltaNet-2 с канал-wise гейтами
+для раздельного стирания и записи в линейном внимании", paragraph "Техническая схема",
+state-update equation S_t = (I - k_t (b_t*k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t*v_t)^T.
+The readout o_t = S_t^T q_t (updated state) is a reading, not printed on the pages.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against a hand-worked example,
+brute-force transition products, closed forms and textbook special cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn2_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgdn2_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = False, out_path: str | None = None, src_path: str | None = None) -> str:
+    """Compile the C oracle with gcc (plain -O2, IEEE arithmetic, no -ffast-math)."""
+    out = out_path or _LIB_PATH
+    src = src_path or _SRC
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+               "-std=c11", "-Wall", "-o", tmp, src, "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str | None = None):
+    """Load (building first if needed) the oracle library; returns a ctypes handle."""
+    global _lib
+    if path is not None:
+        lib = ctypes.CDLL(path)
+        _declare(lib)
+        return lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            _declare(lib)
+            _lib = lib
+    return _lib
+
+
+def _declare(lib) -> None:
+    p = ctypes.c_void_p
+    L = ctypes.c_long
+    lib.gdn2_oracle_forward.argtypes = [p, p, p, p, p, p, p, p, p, L, L, L, L, L, ctypes.c_int]
+    lib.gdn2_oracle_forward.restype = ctypes.c_int
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(x) -> np.ndarray:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor: exact upcast on the CPU
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward(q, k, v, alpha, b, w, S0=None, *, threads: int | None = None, lib=None):
+    """Run the recurrence over [B, T, H, d] inputs in float64.
+
+    q, k, alpha, b: [B, T, H, d_k]; v, w: [B, T, H, d_v]; S0: [B, H, d_k, d_v] or None (zeros).
+    Scalar-gate forms (Gated DeltaNet / KDA) are passed here already broadcast to these
+    shapes (see ``broadcast_gates``). Returns (o [B, T, H, d_v], S_T [B, H, d_k, d_v]) as
+    float64 numpy arrays. Inputs may be numpy arrays or CPU/GPU torch tensors; values are
+    upcast exactly to float64.
+    """
+    q, k, v, alpha, b, w = (_f64(x) for x in (q, k, v, alpha, b, w))
+    S0 = _f64(S0)
+    if q.ndim != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, x, d in (("k", k, dk), ("alpha", alpha, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
+        if x.shape != (B, T, H, d):
+            raise ValueError(f"{name} has shape {x.shape}, expected {(B, T, H, d)}")
+    if S0 is not None and S0.shape != (B, H, dk, dv):
+        raise ValueError(f"S0 has shape {S0.shape}, expected {(B, H, dk, dv)}")
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    S_T = np.zeros((B, H, dk, dv), dtype=np.float64)
+    lib = lib or load_library()
+    rc = lib.gdn2_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                 _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
+                                 int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"gdn2_oracle_forward failed with status {rc}")
+    return o, S_T
+
+
+def decode_step(q, k, v, alpha, b, w, S, *, threads: int | None = None, lib=None):
+    """One single-token step: inputs [B, H, d], state S [B, H, d_k, d_v].
+
+    This is ``forward`` with T = 1. Returns (o [B, H, d_v], S_new [B, H, d_k, d_v]).
+    """
+    xs = [_f64(x) for x in (q, k, v, alpha, b, w)]
+    xs = [x[:, None] for x in xs]  # [B, H, d] -> [B, 1, H, d]
+    o, S_new = forward(*xs, S0=S, threads=threads, lib=lib)
+    return o[:, 0], S_new
+
+
+def broadcast_gates(alpha, b, w, d_k: int, d_v: int, *, alpha_scalar: bool, beta_scalar: bool):
+    """Materialise scalar gates as the per-channel gates the general rule takes.
+
+    Gated DeltaNet and KDA are the general rule with collapsed gates: with one scalar
+    beta_t, b_t = beta_t * 1_{d_k} and w_t = beta_t * 1_{d_v}; Gated DeltaNet also has a
+    scalar decay alpha_t broadcast over the key channels (page "NVIDIA улучшила память LLM
+    без роста затрат на контекст", the authors' quote on the earlier models as special
+    cases). alpha / b given as [..., 1] or [...] scalars per (b, t, h); w is ignored when
+    beta_scalar is set.
+    """
+    alpha = _f64(alpha)
+    b = _f64(b)
+    if alpha_scalar:
+        a = alpha if alpha.shape[-1:] == (1,) else alpha[..., None]
+        alpha = np.broadcast_to(a, a.shape[:-1] + (d_k,)).copy()
+    if beta_scalar:
+        be = b if b.shape[-1:] == (1,) else b[..., None]
+        b = np.broadcast_to(be, be.shape[:-1] + (d_k,)).copy()
+        w = np.broadcast_to(be, be.shape[:-1] + (d_v,)).copy()
+    else:
+        w = _f64(w)
+    return alpha, b, w

@@ -1,0 +1,62 @@
+"""The fp64 oracle against its pins (hand examples, brute force, closed forms, collapses)."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as P
+
+
+def _fwd(q, k, v, alpha, b, w, S0):
+    return oracle.forward(q, k, v, alpha, b, w, S0, threads=2)
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(_fwd)
+
+
+def test_decode_step_is_forward_with_one_token():
+    rng = np.random.default_rng(10)
+    q, k, v, a, b, w, S0 = P.random_inputs(rng, 3, 4, 2, 5, 3)
+    o_all, S_all = oracle.forward(q, k, v, a, b, w, S0)
+    S = S0
+    for t in range(4):
+        o_t, S = oracle.decode_step(q[:, t], k[:, t], v[:, t], a[:, t], b[:, t], w[:, t], S)
+        np.testing.assert_array_equal(o_t, o_all[:, t])
+    np.testing.assert_array_equal(S, S_all)
+
+
+def test_split_sequence_equals_whole():
+    rng = np.random.default_rng(11)
+    ins = P.random_inputs(rng, 2, 13, 2, 4, 6)
+    q, k, v, a, b, w, S0 = ins
+    o, S_T = oracle.forward(*ins)
+    o1, S1 = oracle.forward(q[:, :5], k[:, :5], v[:, :5], a[:, :5], b[:, :5], w[:, :5], S0)
+    o2, S2 = oracle.forward(q[:, 5:], k[:, 5:], v[:, 5:], a[:, 5:], b[:, 5:], w[:, 5:], S1)
+    np.testing.assert_array_equal(np.concatenate([o1, o2], axis=1), o)
+    np.testing.assert_array_equal(S2, S_T)
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(12)
+    ins = P.random_inputs(rng, 3, 9, 5, 4, 4)
+    o1, S1 = oracle.forward(*ins, threads=1)
+    o7, S7 = oracle.forward(*ins, threads=7)
+    np.testing.assert_array_equal(o1, o7)
+    np.testing.assert_array_equal(S1, S7)
+
+
+def test_empty_sequence_returns_initial_state():
+    rng = np.random.default_rng(13)
+    q, k, v, a, b, w, S0 = P.random_inputs(rng, 2, 0, 3, 4, 5)
+    o, S_T = oracle.forward(q, k, v, a, b, w, S0)
+    assert o.shape == (2, 0, 3, 5)
+    np.testing.assert_array_equal(S_T, S0)
+
+
+def test_broadcast_gates_shapes():
+    a = np.full((1, 2, 3), 0.5)
+    be = np.full((1, 2, 3), 0.25)
+    A, Bk, W = oracle.broadcast_gates(a, be, None, 4, 6, alpha_scalar=True, beta_scalar=True)
+    assert A.shape == (1, 2, 3, 4) and Bk.shape == (1, 2, 3, 4) and W.shape == (1, 2, 3, 6)
+    assert (A == 0.5).all() and (Bk == 0.25).all() and (W == 0.25).all()
