@@ -1,0 +1,178 @@
+"""Gated DeltaNet-2 recurrence on AMD Instinct MI355X: thin Python binding of libgdn2.so.
+
+The compute lives in the C-ABI library (include/gdn2.h, HIP kernels for gfx950). This module
+only checks tensor metadata, passes device pointers and the current HIP stream, and turns
+status codes into exceptions. PyTorch provides device memory and streams. There is no fallback:
+if the library is not built or no GPU is present, calls raise.
+
+    o, S_T = chunk_fwd(q, k, v, alpha, b, w, S0)        # prefill, chunk length 64
+    o, S_T = recurrent_fwd(q, k, v, alpha, b, w, S0)    # token-by-token fp32 prefill
+    o = decode_step(q, k, v, alpha, b, w, S)            # one token, S updated in place
+
+Shapes: q, k, alpha, b [B, T, H, d_k]; v, w [B, T, H, d_v]; states [B, H, d_k, d_v] float32;
+decode drops the T axis. Scalar gates: alpha [B, T, H] (alpha_scalar) and b = beta [B, T, H]
+with w None (beta_scalar) -- inferred from the shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to it)
+
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes",
+           "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+_lib = None
+
+BF16, F32 = 0, 1
+ALPHA_SCALAR, BETA_SCALAR = 1, 2
+_STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
+           4: "GDN2_ERR_ALIGN", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP", 7: "GDN2_ERR_WORKSPACE"}
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdn2.so (built by gated_delta_rule_25_amd.build); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m gated_delta_rule_25_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    lib.gdn2_chunk_fwd.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
+    lib.gdn2_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn2_recurrent_fwd.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p]
+    lib.gdn2_recurrent_fwd.restype = ctypes.c_int
+    lib.gdn2_decode_step.argtypes = [p] * 8 + [i32] * 4 + [ctypes.c_int, u32, p]
+    lib.gdn2_decode_step.restype = ctypes.c_int
+    lib.gdn2_status_str.argtypes = [ctypes.c_int]
+    lib.gdn2_status_str.restype = ctypes.c_char_p
+    lib.gdn2_abi_version.argtypes = []
+    lib.gdn2_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_inputs(q, k, v, alpha, b, w, ndim_tok: int):
+    ins = [x for x in (q, k, v, alpha, b, w) if x is not None]
+    dt = q.dtype
+    for x in ins:
+        if not x.is_cuda:
+            raise ValueError("inputs must be GPU tensors")
+        if not x.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+        if x.dtype != dt:
+            raise TypeError("q, k, v, alpha, b, w must share one dtype")
+    if q.dim() != ndim_tok:
+        raise ValueError(f"q must have {ndim_tok} dimensions")
+    flags = 0
+    if alpha.dim() == ndim_tok - 1:
+        flags |= ALPHA_SCALAR
+    if w is None:
+        if b.dim() != ndim_tok - 1:
+            raise ValueError("w may be None only with a scalar beta passed as b")
+        flags |= BETA_SCALAR
+    return flags
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _state_out(S0, B, H, dk, dv, device, S_out):
+    if S_out is None:
+        S_out = torch.empty(B, H, dk, dv, device=device, dtype=torch.float32)
+    if S0 is not None and (S0.dtype != torch.float32 or not S0.is_contiguous()):
+        raise TypeError("S0 must be a contiguous float32 tensor")
+    return S_out
+
+
+def chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
+    return int(load().gdn2_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v,
+                                                     BF16 if dtype == torch.bfloat16 else F32,
+                                                     flags))
+
+
+def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspace=None,
+              stream=None):
+    """Chunkwise prefill (C = 64). Returns (o [B, T, H, d_v] fp32, S_T [B, H, d_k, d_v])."""
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 4)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty(B, T, H, dv, device=q.device, dtype=torch.float32)
+    S_out = _state_out(S0, B, H, dk, dv, q.device, S_out)
+    dt = _dtype_code(q)
+    need = int(lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                            _ptr(o), _ptr(S_out), B, T, H, dk, dv, dt, flags, _ptr(workspace),
+                            ws_bytes, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd", st)
+    return o, S_out
+
+
+def recurrent_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, stream=None):
+    """Token-by-token fp32 prefill. Returns (o, S_T) like chunk_fwd."""
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 4)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty(B, T, H, dv, device=q.device, dtype=torch.float32)
+    S_out = _state_out(S0, B, H, dk, dv, q.device, S_out)
+    st = lib.gdn2_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                _ptr(S0), _ptr(o), _ptr(S_out), B, T, H, dk, dv, _dtype_code(q),
+                                flags, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_recurrent_fwd", st)
+    return o, S_out
+
+
+def decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
+    """One decode step on [B, H, d] inputs; updates S [B, H, d_k, d_v] in place, returns o."""
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 3)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if S.dtype != torch.float32 or not S.is_contiguous():
+        raise TypeError("S must be a contiguous float32 tensor")
+    if o is None:
+        o = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
+    st = lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S),
+                              _ptr(o), B, H, dk, dv, _dtype_code(q), flags, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_decode_step", st)
+    return o

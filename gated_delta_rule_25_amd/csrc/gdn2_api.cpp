@@ -1,0 +1,185 @@
+// gdn2_api.cpp -- the C ABI declared in include/gdn2.h: argument checks, then launches.
+//
+// Every check runs on the host before anything is enqueued, so an argument error leaves the
+// stream untouched. The library holds no state and allocates nothing.
+#include "../../include/gdn2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace {
+
+bool dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+    Range r;
+    if (p && bytes) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + bytes;
+    }
+    return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Element counts for the prefill layouts; false on overflow.
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+    if (a != 0 && b > (UINT64_MAX >> 2) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+struct Sizes {
+    uint64_t tok = 0;     // B*T*H
+    uint64_t qk = 0;      // B*T*H*d_k elements
+    uint64_t vw = 0;      // B*T*H*d_v elements
+    uint64_t state = 0;   // B*H*d_k*d_v elements
+    uint64_t scalar = 0;  // B*T*H elements (scalar gates)
+};
+
+bool sizes_of(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, Sizes* s) {
+    uint64_t bt, bh;
+    return mul_ok((uint64_t)B, (uint64_t)T, &bt) && mul_ok(bt, (uint64_t)H, &s->tok) &&
+           mul_ok(s->tok, (uint64_t)dk, &s->qk) && mul_ok(s->tok, (uint64_t)dv, &s->vw) &&
+           mul_ok((uint64_t)B, (uint64_t)H, &bh) && mul_ok(bh, (uint64_t)dk * (uint64_t)dv, &s->state) &&
+           (s->scalar = s->tok, true) && s->qk < (1ull << 62) && s->vw < (1ull << 62);
+}
+
+// Shared validation for prefill (T >= 0 tokens) and decode (T == 1, S0 == S_out == S).
+gdn2_status validate(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* b, const void* w, const float* S0, const float* o,
+                     const float* S_out, int32_t B, int32_t T, int32_t H, int32_t dk,
+                     int32_t dv, gdn2_dtype dt, uint32_t flags, bool decode) {
+    if (dt != GDN2_BF16 && dt != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR)) return GDN2_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
+    if (!dim_ok(dk) || !dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
+    Sizes sz;
+    if (!sizes_of(B, T, H, dk, dv, &sz)) return GDN2_ERR_SHAPE;
+    const bool bscalar = (flags & GDN2_BETA_SCALAR) != 0;
+    const bool ascalar = (flags & GDN2_ALPHA_SCALAR) != 0;
+    if (bscalar && w) return GDN2_ERR_UNSUPPORTED;  // w is implied by beta
+    if (T > 0) {
+        if (!q || !k || !v || !alpha || !b || !o || (!bscalar && !w)) return GDN2_ERR_NULL;
+    }
+    if (decode && (!S0 || !S_out)) return GDN2_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, b, w, S0, o, S_out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
+
+    const uint64_t es = dt == GDN2_BF16 ? 2 : 4;
+    const Range rq = range_of(q, sz.qk * es), rk = range_of(k, sz.qk * es);
+    const Range rv = range_of(v, sz.vw * es);
+    const Range ra = range_of(alpha, (ascalar ? sz.scalar : sz.qk) * es);
+    const Range rb = range_of(b, (bscalar ? sz.scalar : sz.qk) * es);
+    const Range rw = range_of(w, sz.vw * es);
+    const Range rS0 = range_of(S0, sz.state * 4), rSo = range_of(S_out, sz.state * 4);
+    const Range ro = range_of(o, sz.vw * 4);
+    const Range ins[] = {rq, rk, rv, ra, rb, rw};
+    for (const Range& r : ins) {
+        if (overlap(ro, r) || overlap(rSo, r)) return GDN2_ERR_ALIAS;
+        if (decode && overlap(rS0, r)) return GDN2_ERR_ALIAS;
+    }
+    if (overlap(ro, rS0) || overlap(ro, rSo)) return GDN2_ERR_ALIAS;
+    if (overlap(rS0, rSo) && !(rS0.lo == rSo.lo && rS0.hi == rSo.hi)) return GDN2_ERR_ALIAS;
+    return GDN2_OK;
+}
+
+gdn2_status run_recurrent(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* b, const void* w, const float* S0, float* o,
+                          float* S_out, int32_t B, int32_t T, int32_t H, int32_t dk,
+                          int32_t dv, gdn2_dtype dt, uint32_t flags, hipStream_t s) {
+    if (!S_out && T == 0) return GDN2_OK;
+    gdn2::RecurrentArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, T, H, dk, dv,
+                          dt == GDN2_BF16, flags};
+    return gdn2::launch_recurrent(a, s) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                               const void* b, const void* w, const float* S0, float* o,
+                               float* S_out, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                               int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                               void* stream) {
+    const gdn2_status st = validate(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v,
+                                    in_dtype, gate_flags, false);
+    if (st != GDN2_OK) return st;
+    return run_recurrent(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
+                         gate_flags, static_cast<hipStream_t>(stream));
+}
+
+size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                      int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags) {
+    if (B <= 0 || H <= 0 || T < 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    return gdn2::chunk_workspace_bytes(B, T, H, d_k, d_v, in_dtype == GDN2_BF16, gate_flags);
+}
+
+gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                           const void* b, const void* w, const float* S0, float* o,
+                           float* S_out, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                           int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    gdn2_status st = validate(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
+                              gate_flags, false);
+    if (st != GDN2_OK) return st;
+    const bool bf16 = in_dtype == GDN2_BF16;
+    if (!gdn2::chunk_supported(d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
+    const size_t need = gdn2::chunk_workspace_bytes(B, T, H, d_k, d_v, bf16, gate_flags);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return GDN2_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {  // nothing to chunk: S_out <- S0 (or zeros)
+        return run_recurrent(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
+                             gate_flags, s);
+    }
+    gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, bf16, gate_flags,
+                      workspace, workspace_bytes};
+    const hipError_t e = gdn2::launch_chunk(a, s);
+    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status gdn2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                             const void* b, const void* w, float* S, float* o, int32_t B,
+                             int32_t H, int32_t d_k, int32_t d_v, gdn2_dtype in_dtype,
+                             uint32_t gate_flags, void* stream) {
+    // A [B, H, d] input is a [B, 1, H, d] input: the decode step is one token of prefill.
+    const gdn2_status st = validate(q, k, v, alpha, b, w, S, o, S, B, 1, H, d_k, d_v, in_dtype,
+                                    gate_flags, true);
+    if (st != GDN2_OK) return st;
+    return run_recurrent(q, k, v, alpha, b, w, S, o, S, B, 1, H, d_k, d_v, in_dtype,
+                         gate_flags, static_cast<hipStream_t>(stream));
+}
+
+const char* gdn2_status_str(gdn2_status s) {
+    switch (s) {
+        case GDN2_OK: return "ok";
+        case GDN2_ERR_NULL: return "a required pointer is NULL";
+        case GDN2_ERR_SHAPE: return "invalid shape";
+        case GDN2_ERR_UNSUPPORTED: return "unsupported head size, dtype or flags";
+        case GDN2_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case GDN2_ERR_ALIAS: return "an output overlaps an input";
+        case GDN2_ERR_HIP: return "HIP launch error";
+        case GDN2_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+int gdn2_abi_version(void) { return GDN2_ABI_VERSION; }
+
+}  // extern "C"

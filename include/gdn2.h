@@ -1,0 +1,134 @@
+/*
+ * gdn2.h -- C ABI of the Gated DeltaNet-2 recurrence library for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (pages, cited by title and paragraph):
+ *   [GDN2-summary] "NVIDIA представила Gated DeltaNet-2 с канал-wise гейтами для раздельного
+ *                  стирания и записи в линейном внимании" (edge.aivizor.me)
+ *   [GDN2-news]    "NVIDIA улучшила память LLM без роста затрат на контекст" (arddev.tech)
+ *
+ * The operation. For every batch element b and head h independently, over tokens t = 1..T:
+ *
+ *     S_t = (I - k_t (b_t (.) k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t (.) v_t)^T
+ *     o_t = S_t^T q_t
+ *
+ * The update is [GDN2-summary, paragraph "Техническая схема", state-update equation]: alpha_t
+ * is the channel-wise decay on the key axis, b_t in [0,1]^{d_k} the erase gate (key axis) and
+ * w_t in [0,1]^{d_v} the write gate (value axis). The readout on the updated state is not
+ * printed on the pages; it is the linear-attention reading of a history compressed into a
+ * fixed state [GDN2-news, section "Контекст"]. No output scale is applied (pre-scale q).
+ *
+ * Scalar gates give the earlier models [GDN2-news, the authors' quote on special cases;
+ * GDN2-summary, paragraph "Архитектурно"]: with one scalar beta_t per token, b_t = beta_t*1
+ * and w_t = beta_t*1 (KDA when alpha stays channel-wise, Gated DeltaNet when alpha_t is a
+ * scalar too). The flags below select these forms without materialising the gates.
+ *
+ * Layouts (row-major, contiguous, no padding):
+ *   prefill  q, k, alpha, b : [B, T, H, d_k]     v, w, o : [B, T, H, d_v]
+ *            scalar alpha   : [B, T, H]          scalar beta (passed as b) : [B, T, H]
+ *   decode   q, k, alpha, b : [B, H, d_k]        v, w, o : [B, H, d_v]
+ *            scalar alpha / beta : [B, H]
+ *   state    S0, S_out, S   : [B, H, d_k, d_v] float32 (row i = key channel i)
+ * Inputs q, k, v, alpha, b, w share one element type (in_dtype); o and the state are float32.
+ *
+ * Ownership and execution. All pointers are device pointers owned by the caller (HIP device
+ * memory, e.g. allocated by PyTorch). The library allocates nothing, keeps no state between
+ * calls and is reentrant. Calls only enqueue kernels on `stream` (a hipStream_t; NULL is the
+ * null stream) and return at once; inputs must stay alive and unchanged until the stream
+ * passes the work.
+ *
+ * Errors. Argument errors are detected on the host and returned with nothing enqueued. A
+ * failed launch returns GDN2_ERR_HIP. Device faults surface at the caller's next
+ * synchronisation. Nothing is printed and nothing aborts.
+ *
+ * Preconditions not checked on the device: finite inputs; alpha in (0, 1] on the prefill
+ * path (it takes log alpha); |S|, |o| and the per-chunk intermediates below 6.5e4 on the
+ * bf16 prefill path (its matrix-core operands are fp16).
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN2_ABI_VERSION 1
+
+typedef enum {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN2_ERR_SHAPE = 2,       /* B <= 0, H <= 0, T < 0, or a size that overflows */
+    GDN2_ERR_UNSUPPORTED = 3, /* (d_k, d_v), dtype or flags not supported */
+    GDN2_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    GDN2_ERR_ALIAS = 5,       /* an output overlaps an input (other than S_out == S0) */
+    GDN2_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    GDN2_ERR_WORKSPACE = 7    /* workspace missing or smaller than required */
+} gdn2_status;
+
+typedef enum { GDN2_BF16 = 0, GDN2_F32 = 1 } gdn2_dtype;
+
+enum {
+    GDN2_ALPHA_SCALAR = 1u, /* alpha holds one decay per token, broadcast over d_k */
+    GDN2_BETA_SCALAR = 2u   /* b holds one beta per token: b = beta*1_{d_k}, w = beta*1_{d_v};
+                               w must be NULL */
+};
+
+/*
+ * Chunkwise-parallel prefill. Runs the recurrence over T tokens from the initial state S0
+ * (NULL = zeros), writes o for every token and the final state to S_out (NULL = not stored;
+ * S_out == S0 is allowed, partial overlap is not). T == 0 copies S0 (or zeros) to S_out.
+ *
+ * The chunk length is 64 and the cumulative channel-wise decay is absorbed into the rank-1
+ * factors of a WY/UT representation [GDN2-summary, paragraph "Реализация"]; the result equals
+ * the token-by-token recurrence up to rounding. bf16 inputs use fp16 matrix-core operands with
+ * fp32 accumulation and an fp32 state; fp32 inputs are computed in fp32 throughout.
+ *
+ * Supported: d_k == d_v in {32, 64, 128}; in_dtype GDN2_BF16 or GDN2_F32; any flags above.
+ * Workspace: pass a buffer of at least gdn2_chunk_fwd_workspace_bytes(...) bytes (it may be
+ * 0, in which case workspace may be NULL).
+ */
+gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
+                           const void *b, const void *w, const float *S0, float *o,
+                           float *S_out, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                           int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when none). */
+size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                      int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
+
+/*
+ * Token-by-token prefill: the same result as gdn2_chunk_fwd, computed one token at a time in
+ * fp32 (each state column tile stays in registers for the whole sequence). Same arguments,
+ * layouts, errors and aliasing rules; no workspace. Supported: d_k, d_v in {32, 64, 128}.
+ */
+gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v, const void *alpha,
+                               const void *b, const void *w, const float *S0, float *o,
+                               float *S_out, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                               int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                               void *stream);
+
+/*
+ * One decode step for B*H independent sequences, constant memory per sequence (the state is
+ * the whole history [GDN2-news, section "Контекст"]). Updates S in place,
+ *     S <- (I - k (b (.) k)^T) Diag(alpha) S + k (w (.) v)^T,
+ * and writes o = S^T q on the updated state. fp32 arithmetic; one read and one write of each
+ * state. Supported: d_k, d_v in {32, 64, 128}.
+ */
+gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const void *alpha,
+                             const void *b, const void *w, float *S, float *o, int32_t B,
+                             int32_t H, int32_t d_k, int32_t d_v, gdn2_dtype in_dtype,
+                             uint32_t gate_flags, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *gdn2_status_str(gdn2_status s);
+
+/* GDN2_ABI_VERSION of the built library. */
+int gdn2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN2_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad arguments
+on the host. No call here reaches a kernel launch, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+LIB = os.path.join(ROOT, "gated_delta_rule_25_amd", "libgdn2.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libgdn2.so not built (run python -m gated_delta_rule_25_amd.build)")
+    import gated_delta_rule_25_amd as g
+    return g.load()
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ("gdn2_chunk_fwd", "gdn2_decode_step", "gdn2_recurrent_fwd",
+                 "gdn2_chunk_fwd_workspace_bytes", "gdn2_status_str", "gdn2_abi_version"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in gdn2.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn2_abi_version() == 1
+    for code in range(8):
+        assert lib.gdn2_status_str(code)
+    assert lib.gdn2_status_str(0) == b"ok"
+
+
+P = ctypes.c_void_p
+FAKE = [P(0x10000 * (i + 1)) for i in range(12)]  # distinct, 16-byte aligned, never dereferenced
+
+
+def chunk_call(lib, ptrs=None, B=1, T=4, H=1, dk=32, dv=32, dt=0, flags=0, ws=None, wsb=0):
+    p = list(FAKE[:9]) if ptrs is None else ptrs
+    return lib.gdn2_chunk_fwd(*p, B, T, H, dk, dv, dt, flags, ws, wsb, None)
+
+
+def test_chunk_rejects_bad_arguments(lib):
+    assert chunk_call(lib, B=0) == 2
+    assert chunk_call(lib, T=-1) == 2
+    assert chunk_call(lib, dk=48) == 3
+    assert chunk_call(lib, dv=256) == 3
+    assert chunk_call(lib, dt=7) == 3
+    assert chunk_call(lib, flags=4) == 3
+    p = list(FAKE[:9])
+    p[0] = None
+    assert chunk_call(lib, p) == 1  # q missing
+    p = list(FAKE[:9])
+    p[7] = None
+    assert chunk_call(lib, p) == 1  # o missing
+    p = list(FAKE[:9])
+    p[1] = P(0x20008)
+    assert chunk_call(lib, p) == 4  # misaligned k
+    p = list(FAKE[:9])
+    p[7] = p[0]
+    assert chunk_call(lib, p) == 5  # o overlaps q
+    p = list(FAKE[:9])
+    assert chunk_call(lib, p, flags=2) == 3  # beta scalar but w given
+
+
+def test_chunk_rejects_partial_state_alias(lib):
+    p = list(FAKE[:9])
+    p[6] = P(0x900000)
+    p[8] = P(0x900010)  # S_out overlaps S0 without being equal
+    assert chunk_call(lib, p) == 5
+
+
+def test_decode_rejects_bad_arguments(lib):
+    f = lib.gdn2_decode_step
+    p = list(FAKE[:8])
+    assert f(*p, 0, 1, 128, 128, 0, 0, None) == 2
+    assert f(*p, 1, 1, 96, 128, 0, 0, None) == 3
+    q = list(p)
+    q[6] = None  # S missing
+    assert f(*q, 1, 1, 128, 128, 0, 0, None) == 1
+    q = list(p)
+    q[7] = q[6]  # o overlaps S
+    assert f(*q, 1, 1, 128, 128, 0, 0, None) == 5
+
+
+def test_recurrent_rejects_bad_arguments(lib):
+    f = lib.gdn2_recurrent_fwd
+    p = list(FAKE[:9])
+    assert f(*p, 1, 4, 0, 64, 64, 0, 0, None) == 2
+    assert f(*p, 1, 4, 1, 64, 16, 0, 0, None) == 3
