@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark: Gated DeltaNet-2 chunkwise prefill tokens/s and decode-state HBM GB/s on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Prefill workload: one 1.3B-scale layer, B=8, H=16, T=4096, d_k=d_v=128 (262,144 state floats
+per batch element), bf16 q/k/v/alpha/b/w, fp32 S0 ~ N(0, 0.1^2), fp32 o and final state.
+Synthetic seeded inputs (no datasets or weights), resident in HBM before timing starts.
+A timed step is one gdn2_chunk_fwd call over the whole batch; `value` = B*T / (step time).
+
+Decode workload (reported beside it): B=256 (and B=1024, whose 1 GiB state cannot sit in
+the 256 MB Infinity Cache), H=16, d=128, fp32 state updated in place over consecutive steps.
+
+Prints ONE JSON line. `roofline` is for the prefill kernel: algorithmic bytes per launch over
+the kernel's average duration (HIP events on the launch stream) against 8 TB/s HBM3E.
+`cpu_baseline` times the fp64 oracle (tests-only code, timed here as a reported baseline) on a
+bounded sample of the same workload with all host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
+    # q, k, alpha, b (bf16) + v, w (bf16) + o (fp32) + S0 read and S_T write amortised over T
+    return 4 * dk * 2 + 2 * dv * 2 + 4 * dv + 8 * dk * dv / T
+
+
+def prefill_flops_per_head_token(dk: int, dv: int, C: int = 64) -> float:
+    # three state products (W S, Q_hat S, K_bar^T Delta) + five triangular C x C products
+    # (A, P, W = T E_hat, U~ = T U, P Delta; counted at half) + the UT solve
+    return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3
+
+
+def decode_bytes_per_head(dk: int, dv: int) -> float:
+    return 2 * 4 * dk * dv + 4 * dk * 2 + 2 * dv * 2 + 4 * dv
+
+
+def time_prefill(g, ins, steps, warmup, impl):
+    import torch
+    fn = g.chunk_fwd if impl == "chunk" else g.recurrent_fwd
+    args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")]
+    B, T, H, dk = ins["q"].shape
+    dv = ins["v"].shape[-1]
+    o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.float32)
+    S_out = torch.empty(B, H, dk, dv, device="cuda", dtype=torch.float32)
+    kw = dict(o=o, S_out=S_out)
+    if impl == "chunk":
+        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
+        if need:
+            kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
+    for _ in range(warmup):
+        fn(*args, ins["S0"], **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn(*args, ins["S0"], **kw)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return wall, kern_ms
+
+
+def time_decode(g, B, H, d, steps, warmup, seed):
+    import torch
+    from gated_delta_rule_25_amd.inputs import make_decode_inputs
+    pool = min(steps, 64)
+    ins = make_decode_inputs(B, H, d, d, pool, seed=seed, device="cuda", generator="torch")
+    S = ins["S0"].clone()
+    o = torch.empty(B, H, d, device="cuda", dtype=torch.float32)
+    xs = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")]
+    for i in range(warmup):
+        g.decode_step(*[x[i % pool] for x in xs], S, o=o)
+    S.copy_(ins["S0"])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    step_in = [[x[i % pool] for x in xs] for i in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        g.decode_step(*step_in[i], S, o=o)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    del ins, S, o, xs, step_in
+    return wall, kern_ms
+
+
+def cpu_baseline(ins_gpu, n_heads: int):
+    """Time the fp64 oracle on n_heads full-length (b, h) sequences of the same inputs."""
+    import torch
+
+    import oracle
+    B, T, H, dk = ins_gpu["q"].shape
+    sel = [(i // H, i % H) for i in range(n_heads)]
+
+    def pick(x, tok=True):
+        if tok:
+            return torch.stack([x[b, :, h] for b, h in sel])[:, :, None].cpu()
+        return torch.stack([x[b, h] for b, h in sel])[:, None].cpu()
+
+    sub = {n: pick(ins_gpu[n]) for n in ("q", "k", "v", "alpha", "b", "w")}
+    S0 = pick(ins_gpu["S0"], tok=False)
+    threads = oracle.default_threads()
+    q, k, v, a, b, w = (oracle._f64(sub[n]) for n in ("q", "k", "v", "alpha", "b", "w"))
+    S0 = oracle._f64(S0)
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, a, b, w, S0, threads=threads)
+    dt = time.perf_counter() - t0
+    head_tokens_per_s = n_heads * T / dt
+    return dict(value=head_tokens_per_s / H, unit="tokens/s", cores=min(threads, n_heads),
+                kind="oracle",
+                sample=f"{n_heads} of {B * H} (b,h) sequences at full T={T}, d={dk}; "
+                       f"{dt:.2f} s wall; tokens/s = head-tokens/s / H (H={H})")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--impl", choices=["chunk", "recurrent"], default="chunk")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the (b, h) "
+              "sequences are independent, so a multi-GPU run is B or H sharded with no "
+              "communication and its throughput is N times the one-GPU figure.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gated_delta_rule_25_amd as g
+    from gated_delta_rule_25_amd.inputs import WORKLOADS, make_inputs_torch
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    g.load()
+    wl = WORKLOADS["prefill_1p3b"]
+    ins = make_inputs_torch(wl, device="cuda")
+    torch.cuda.synchronize()
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
+
+    wall, kern_ms = time_prefill(g, ins, args.steps, args.warmup, args.impl)
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    head_tokens = B * T * H
+    bytes_launch = prefill_bytes_per_head_token(dk, dv, T) * head_tokens
+    flops_launch = prefill_flops_per_head_token(dk, dv) * head_tokens
+    achieved_gbs = bytes_launch / (kern_avg * 1e-3) / 1e9
+    tflops = flops_launch / (kern_avg * 1e-3) / 1e12
+    print(f"[bench] prefill {args.impl}: {kern_avg:.3f} ms/launch (events), "
+          f"{ms_per_step:.3f} ms/step (wall), {achieved_gbs:.0f} GB/s, {tflops:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    dec = {}
+    for Bd, steps in ((256, args.decode_steps), (1024, max(1, args.decode_steps // 5))):
+        dwall, dms = time_decode(g, Bd, 16, 128, steps, 10, seed=20254)
+        davg = sum(dms) / len(dms)
+        dbytes = decode_bytes_per_head(128, 128) * Bd * 16
+        dec[f"B{Bd}"] = dict(steps=steps, kernel_ms=round(davg, 5),
+                             ms_per_step_wall=round(dwall * 1e3 / steps, 5),
+                             gbs=round(dbytes / (davg * 1e-3) / 1e9, 1),
+                             frac=round(dbytes / (davg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             head_state_updates_per_s=round(Bd * 16 / (davg * 1e-3), 1))
+        print(f"[bench] decode B={Bd}: {davg * 1e3:.1f} us/step, {dec[f'B{Bd}']['gbs']} GB/s",
+              file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ins, args.cpu_heads)
+        print(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": "GDN-2 chunk fwd tokens/s (B8,H16,T4k,d128) + decode state HBM GB/s",
+        "value": round(B * T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f16-mfma/f32-state" if args.impl == "chunk" else "bf16-in/f32",
+        "data": "synthetic",
+        "config": {"workload": "GDN-2 layer prefill B8 H16 T4096 d_k=d_v=128, chunk 64",
+                   "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
+                   "impl": args.impl, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel_ms": round(kern_avg, 4),
+                     "algorithmic_bytes": int(bytes_launch),
+                     "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

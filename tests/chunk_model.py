@@ -162,3 +162,111 @@ def chunk_forward_model(q, k, v, alpha, b, w, S0=None, *, C=64, prec=None):
         K_bar = vr(kc * vr(np.exp(vr(Gam[L - 1] - Gam))))
         S = vr(gam[L - 1][:, None] * S + product(K_bar.T, Delta, p["carry"], p["carry"], acc))
     return o, S
+
+
+def _split_bf16(x):
+    hi = round_bf16(x)
+    return hi, round_bf16(round_f32(x - hi))
+
+
+def _mm16(a, b):
+    """fp16 operands, fp32 result (one matrix-core pass)."""
+    return round_f32(round_f16(a) @ round_f16(b))
+
+
+def _mm_bf16x3(a, b):
+    """bf16 hi/lo split operands, hi*hi + hi*lo + lo*hi, fp32 result."""
+    ah, al = _split_bf16(a)
+    bh, bl = _split_bf16(b)
+    return round_f32(ah @ bh + ah @ bl + al @ bh)
+
+
+def kernel_scheme_model(q, k, v, alpha, b, w, S0=None):
+    """The chunk kernel's exact operand-precision scheme for bf16 inputs, in numpy.
+
+    C = 64 in four 16-row blocks. Vector math in fp32. Gram blocks below the diagonal: fp16
+    operands with block-boundary references (row side exp(local), times exp(G_I - G_{J+1})
+    when blocks are not adjacent; column side exp(blocktot_J - local)). Diagonal Gram blocks:
+    bf16 hi/lo split operands (three passes) with the block's 8th row as reference, so no
+    factor exceeds the decay of 8 tokens. UT inverse: 16x16 diagonal blocks by fp32 forward
+    substitution, merged at 32 and 64 rows by fp16 products. W, U~ and the state-chain
+    products take fp16 operands with fp32 results; the state stays fp32.
+    """
+    q, k, v, alpha, b, w = (np.asarray(x, dtype=np.float64) for x in (q, k, v, alpha, b, w))
+    T_len, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else round_f32(np.array(S0, dtype=np.float64))
+    o = np.zeros((T_len, dv))
+    C = 64
+    for c0 in range(0, T_len, C):
+        L = min(C, T_len - c0)
+        pad = C - L
+
+        def P_(x, fill):
+            x = x[c0:c0 + L]
+            return np.concatenate([x, np.full((pad, x.shape[1]), fill)]) if pad else x
+        qc, kc, bc = P_(q, 0.0), P_(k, 0.0), P_(b, 0.0)
+        ac = P_(alpha, 1.0)
+        vc, wc = P_(v, 0.0), P_(w, 0.0)
+        g = round_f32(np.log(ac))
+        local = np.zeros_like(g)
+        for blk in range(4):
+            run = np.zeros(dk)
+            for r in range(16 * blk, 16 * blk + 16):
+                run = round_f32(run + g[r])
+                local[r] = run
+        tot = local[15::16]  # [4, dk] block totals
+        G = np.zeros((5, dk))
+        for n in range(1, 5):
+            G[n] = round_f32(G[n - 1] + tot[n - 1])
+        Gam = round_f32(np.repeat(G[:4], 16, axis=0) + local)
+        e = round_f32(bc * kc)
+        A = np.zeros((C, C))
+        Pm = np.zeros((C, C))
+        for I in range(4):
+            rI = slice(16 * I, 16 * I + 16)
+            fr = round_f32(np.exp(local[rI]))
+            e_ref = round_f32(e[rI] * fr)
+            q_ref = round_f32(qc[rI] * fr)
+            X = local[16 * I + 7]
+            fm = round_f32(np.exp(round_f32(local[rI] - X)))
+            km = round_f32(kc[rI] * round_f32(np.exp(round_f32(X - local[rI]))))
+            A[rI, rI] = _mm_bf16x3(round_f32(e[rI] * fm), km.T)
+            Pm[rI, rI] = _mm_bf16x3(round_f32(qc[rI] * fm), km.T)
+            for J in range(I):
+                rJ = slice(16 * J, 16 * J + 16)
+                kt = round_f32(kc[rJ] * round_f32(np.exp(round_f32(tot[J] - local[rJ]))))
+                cIJ = round_f32(np.exp(round_f32(G[I] - G[J + 1])))
+                A[rI, rJ] = _mm16(round_f32(e_ref * cIJ), kt.T)
+                Pm[rI, rJ] = _mm16(round_f32(q_ref * cIJ), kt.T)
+        A = np.tril(A, -1)
+        Pm = np.tril(Pm, 0)
+        # UT inverse
+        Tm = np.zeros((C, C))
+        for I in range(4):
+            rI = slice(16 * I, 16 * I + 16)
+            a = A[rI, rI]
+            t = np.zeros((16, 16))
+            for r in range(16):
+                t[r, r] = 1.0
+                if r:
+                    t[r, :r] = round_f32(-(a[r, :r] @ t[:r, :r]))
+            Tm[rI, rI] = t
+        for I, J in ((1, 0), (3, 2)):
+            rI, rJ = slice(16 * I, 16 * I + 16), slice(16 * J, 16 * J + 16)
+            X = _mm16(A[rI, rJ], Tm[rJ, rJ])
+            Tm[rI, rJ] = -_mm16(Tm[rI, rI], X)
+        Y = _mm16(A[32:, :32], Tm[:32, :32])
+        Tm[32:, :32] = -_mm16(Tm[32:, 32:], Y)
+        gam = round_f32(np.exp(Gam))
+        E_hat = round_f32(e * gam)
+        W = _mm16(Tm, E_hat)
+        U = round_f32(wc * vc)
+        Ut = _mm16(Tm, U)
+        Q_hat = round_f32(qc * gam)
+        Delta = round_f32(Ut - _mm16(W, S))
+        O = round_f32(_mm16(Q_hat, S) + _mm16(Pm, Delta))
+        o[c0:c0 + L] = O[:L]
+        K_bar = round_f32(kc * round_f32(np.exp(round_f32(Gam[C - 1] - Gam))))
+        S = round_f32(gam[C - 1][:, None] * S + _mm16(K_bar.T, Delta))
+    return o, S

@@ -1,0 +1,181 @@
+"""GPU parity: the chunkwise (C = 64) prefill kernel against the fp64 oracle.
+
+Bars (normwise max relative error, see parity.py): <= 1e-5 for fp32 inputs (fp32 matrix-core
+operands throughout) and <= 2e-3 for bf16 inputs (fp16 operands, fp32 accumulation and state),
+on o and on the final state. Sizes span several chunks and a ragged last chunk.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import banner, normwise_err
+from gated_delta_rule_25_amd.inputs import WORKLOADS, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+TOL32 = 1e-5
+TOL16 = 2e-3
+
+
+def _g():
+    import gated_delta_rule_25_amd as g
+    return g
+
+
+def _oracle(ins):
+    a, b, w = ins["alpha"], ins["b"], ins["w"]
+    dk, dv = ins["q"].shape[-1], ins["v"].shape[-1]
+    if ins.get("alpha_scalar") or ins.get("beta_scalar"):
+        a, b, w = oracle.broadcast_gates(a, b, w, dk, dv, alpha_scalar=ins["alpha_scalar"],
+                                         beta_scalar=ins["beta_scalar"])
+    return oracle.forward(ins["q"], ins["k"], ins["v"], a, b, w, ins["S0"])
+
+
+def _cuda(ins):
+    return {n: (x.cuda() if hasattr(x, "cuda") else x) for n, x in ins.items()}
+
+
+def _run(ins, **kw):
+    d = _cuda(ins)
+    out = _g().chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(name, ins, tol):
+    o_ref, S_ref = _oracle(ins)
+    o, S_T = _run(ins)
+    eo, es = normwise_err(o, o_ref), normwise_err(S_T, S_ref)
+    print(f"  {name}: o err {eo:.2e}  S_T err {es:.2e}", flush=True)
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+FP32_CASES = [
+    ("tiny_fp32_full", WORKLOADS["tiny_fp32"]),
+    ("fp32_d32_ragged_s0", scaled(WORKLOADS["tiny_fp32"], B=2, T=150, H=3, s0_std=0.1)),
+    ("fp32_d64_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=2, d_k=64, d_v=64,
+                               dtype="fp32")),
+    ("fp32_d64_gdn", scaled(WORKLOADS["gdn_scalar"], B=1, T=130, H=2, d_k=64, d_v=64,
+                            dtype="fp32")),
+    ("fp32_d32_kda", scaled(WORKLOADS["kda_scalar"], B=1, T=96, H=3, d_k=32, d_v=32,
+                            dtype="fp32")),
+]
+
+
+@pytest.mark.parametrize("name,wl", FP32_CASES, ids=[c[0] for c in FP32_CASES])
+def test_chunk_fp32_matches_oracle(name, wl):
+    banner(f"chunk fp32 {name} {wl}")
+    _check(name, make_inputs(wl), TOL32)
+
+
+BF16_CASES = [
+    ("bf16_d128_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=3)),
+    ("bf16_d128_T1", scaled(WORKLOADS["prefill_1p3b"], B=1, T=1, H=2)),
+    ("bf16_d128_T63", scaled(WORKLOADS["prefill_1p3b"], B=1, T=63, H=2)),
+    ("bf16_d128_T64", scaled(WORKLOADS["prefill_1p3b"], B=1, T=64, H=2)),
+    ("bf16_d128_T65", scaled(WORKLOADS["prefill_1p3b"], B=1, T=65, H=2)),
+    ("bf16_d128_zero_s0", scaled(WORKLOADS["prefill_1p3b"], B=1, T=300, H=2, s0_std=0.0)),
+    ("bf16_d128_slow_decay", scaled(WORKLOADS["long_prefill"], T=1000, H=3)),
+    ("bf16_d128_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=1, T=260, H=3, alpha_mu=-2.0)),
+    ("bf16_d64", scaled(WORKLOADS["prefill_1p3b"], B=3, T=190, H=2, d_k=64, d_v=64)),
+    ("bf16_d32", scaled(WORKLOADS["prefill_1p3b"], B=2, T=130, H=5, d_k=32, d_v=32)),
+    ("bf16_d128_gdn", scaled(WORKLOADS["gdn_scalar"], B=1, T=257, H=3)),
+    ("bf16_d128_kda", scaled(WORKLOADS["kda_scalar"], B=1, T=257, H=3)),
+    ("bf16_d64_gdn", scaled(WORKLOADS["gdn_scalar"], B=2, T=100, H=2, d_k=64, d_v=64)),
+]
+
+
+@pytest.mark.parametrize("name,wl", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_chunk_bf16_matches_oracle(name, wl):
+    banner(f"chunk bf16 {name} {wl}")
+    _check(name, make_inputs(wl), TOL16)
+
+
+def test_chunk_zero_tokens_copies_state():
+    banner("chunk T=0")
+    ins = _cuda(make_inputs(scaled(WORKLOADS["prefill_1p3b"], B=2, T=0, H=3)))
+    o, S_T = _g().chunk_fwd(ins["q"], ins["k"], ins["v"], ins["alpha"], ins["b"], ins["w"],
+                            ins["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(S_T, ins["S0"])
+
+
+def test_chunk_state_in_place_and_split_invariance():
+    """fwd(T1) then fwd(T2) from its state equals fwd(T1 + T2), with S_out aliasing S0."""
+    banner("chunk split invariance, in-place state")
+    g = _g()
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=2)
+    ins = _cuda(make_inputs(wl))
+    names = ("q", "k", "v", "alpha", "b", "w")
+    o_full, S_full = g.chunk_fwd(*[ins[n] for n in names], ins["S0"])
+    S = ins["S0"].clone()
+    T1 = 77
+    o1, _ = g.chunk_fwd(*[ins[n][:, :T1].contiguous() for n in names], S, S_out=S)
+    o2, _ = g.chunk_fwd(*[ins[n][:, T1:].contiguous() for n in names], S, S_out=S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(make_inputs(wl))
+    assert normwise_err(torch.cat([o1, o2], 1), o_ref) <= TOL16
+    assert normwise_err(S, S_ref) <= TOL16
+    assert normwise_err(S, S_full.double().cpu().numpy()) <= TOL16
+
+
+def test_chunk_then_decode_equals_longer_prefill():
+    banner("chunk(T) + decode == chunk(T+1)")
+    g = _g()
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=2, T=131, H=2)
+    ins = _cuda(make_inputs(wl))
+    names = ("q", "k", "v", "alpha", "b", "w")
+    o_all, S_all = g.chunk_fwd(*[ins[n] for n in names], ins["S0"])
+    o_pre, S = g.chunk_fwd(*[ins[n][:, :-1].contiguous() for n in names], ins["S0"])
+    o_last = g.decode_step(*[ins[n][:, -1].contiguous() for n in names], S)
+    torch.cuda.synchronize()
+    ref = o_all[:, -1].double().cpu().numpy()
+    assert normwise_err(o_last, ref) <= TOL16
+    assert normwise_err(S, S_all.double().cpu().numpy()) <= TOL16
+
+
+def test_chunk_is_deterministic():
+    banner("chunk bitwise determinism")
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=2, T=190, H=3)
+    ins = make_inputs(wl)
+    o1, S1 = _run(ins)
+    o2, S2 = _run(ins)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_chunk_exact_write_invariant():
+    """b = 1, q = k with exactly-unit bf16 keys: every o_t equals w_t * v_t (any decay)."""
+    banner("chunk exact-write invariant")
+    rng = np.random.default_rng(3)
+    B, T, H, d = 1, 150, 2, 128
+    k = np.zeros((B, T, H, d), np.float32)
+    idx = rng.integers(0, d, size=(B, T, H, 4))
+    signs = rng.choice([-0.5, 0.5], size=(B, T, H, 4))
+    for t in range(T):  # four distinct channels of +-1/2: norm exactly 1
+        for h in range(H):
+            ch = rng.choice(d, 4, replace=False)
+            k[0, t, h, ch] = signs[0, t, h]
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=B, T=T, H=H)
+    ins = make_inputs(wl)
+    kt = torch.from_numpy(k).to(torch.bfloat16)
+    ins["k"] = kt
+    ins["q"] = kt.clone()
+    ins["b"] = torch.ones_like(ins["b"])
+    o, _ = _run(ins)
+    expect = (ins["w"].double() * ins["v"].double()).numpy()
+    assert normwise_err(o, expect) <= TOL16
+
+
+FULL = [
+    ("prefill_1p3b", WORKLOADS["prefill_1p3b"]),
+    ("gdn_scalar", WORKLOADS["gdn_scalar"]),
+    ("kda_scalar", WORKLOADS["kda_scalar"]),
+]
+
+
+@pytest.mark.parametrize("name,wl", FULL, ids=[c[0] for c in FULL])
+def test_chunk_full_size_all_heads(name, wl):
+    """The benchmark's launch configuration, B8 H16 T4096 d128, every head against the oracle."""
+    banner(f"chunk full {name}")
+    _check(name, make_inputs(wl), TOL16)
