@@ -143,7 +143,11 @@ def main(argv=None):
     ap.add_argument("--impl", choices=["chunk", "recurrent"], default="chunk")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (reference for HBM byte "
+                         "counters)")
+    ap.add_argument("--skip-decode", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the (b, h) "
@@ -179,7 +183,9 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     dec = {}
-    for Bd, steps in ((256, args.decode_steps), (1024, max(1, args.decode_steps // 5))):
+    decode_runs = () if args.skip_decode else ((256, args.decode_steps),
+                                               (1024, max(1, args.decode_steps // 5)))
+    for Bd, steps in decode_runs:
         dwall, dms = time_decode(g, Bd, 16, 128, steps, 10, seed=20254)
         davg = sum(dms) / len(dms)
         dbytes = decode_bytes_per_head(128, 128) * Bd * 16
@@ -190,6 +196,14 @@ def main(argv=None):
                              head_state_updates_per_s=round(Bd * 16 / (davg * 1e-3), 1))
         print(f"[bench] decode B={Bd}: {davg * 1e3:.1f} us/step, {dec[f'B{Bd}']['gbs']} GB/s",
               file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, device="cuda", dtype=torch.float32)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -60,3 +60,33 @@ def test_broadcast_gates_shapes():
     A, Bk, W = oracle.broadcast_gates(a, be, None, 4, 6, alpha_scalar=True, beta_scalar=True)
     assert A.shape == (1, 2, 3, 4) and Bk.shape == (1, 2, 3, 4) and W.shape == (1, 2, 3, 6)
     assert (A == 0.5).all() and (Bk == 0.25).all() and (W == 0.25).all()
+
+
+def test_chunk_algebra_matches_oracle():
+    """The chunkwise WY/UT form (tests/chunk_model.py) equals the sequential recurrence in fp64,
+    for chunk lengths that do and do not divide T."""
+    import chunk_model
+    rng = np.random.default_rng(21)
+    q, k, v, a, b, w, S0 = P.random_inputs(rng, 1, 70, 1, 6, 5)
+    o_ref, S_ref = oracle.forward(q, k, v, a, b, w, S0)
+    f = lambda x: x[0, :, 0]
+    for C in (1, 7, 16, 64, 70):
+        o, S = chunk_model.chunk_forward_model(f(q), f(k), f(v), f(a), f(b), f(w), S0[0, 0], C=C)
+        np.testing.assert_allclose(o, o_ref[0, :, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(S, S_ref[0, 0], rtol=0, atol=1e-12)
+
+
+def test_kernel_precision_scheme_meets_bar():
+    """The chunk kernel's operand-rounding scheme, emulated, stays inside 2e-3 (bf16 inputs)."""
+    import torch
+    import chunk_model
+    from gated_delta_rule_25_amd.inputs import WORKLOADS, make_inputs, scaled
+    ins = make_inputs(scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=1, d_k=32, d_v=32))
+    o_ref, S_ref = oracle.forward(*(ins[n] for n in ("q", "k", "v", "alpha", "b", "w")), ins["S0"])
+    f = lambda x: x[0, :, 0].double().numpy()
+    o, S = chunk_model.kernel_scheme_model(*(f(ins[n]) for n in ("q", "k", "v", "alpha", "b", "w")),
+                                           ins["S0"][0, 0].double().numpy())
+    eo = np.abs(o - o_ref[0, :, 0]).max() / np.abs(o_ref[0, :, 0]).max()
+    es = np.abs(S - S_ref[0, 0]).max() / np.abs(S_ref[0, 0]).max()
+    assert eo < 2e-3 and es < 2e-3, (eo, es)
+    assert eo > 1e-5  # fp16 rounding is really being emulated
