@@ -13,25 +13,28 @@
 // + k_t (w_t v_t)^T with o_t = S_t^T q_t [same page, paragraph "Техническая схема"].
 //
 // Mapping. One workgroup (4 wavefronts) owns one (b, h) and a tile of DVT value columns; the
-// columns of S evolve independently given W and U~, so tiles need no communication. The
-// sequence is walked chunk by chunk:
-//   A  wave I loads token rows 16I..16I+15 (lane = row, 8 channels per K-step) and scans the
-//      log2-decay over its 16 rows with lane shuffles; block totals go through LDS.
-//   B  factors: Q_hat, E_hat^T, K_bar^T, U^T and the block-referenced K~ go to LDS; the
-//      diagonal 16x16 Gram blocks are formed in registers. Their factors are referenced to
-//      the block's 8th row, so no factor exceeds the decay of 8 tokens, and they use a bf16
-//      hi/lo split (three passes) with the fp32 exponent range.
+// columns of S evolve independently given T, E_hat and U, so tiles need no communication. The
+// inputs of chunk n+1 are loaded into registers while chunk n is processed. Per chunk:
+//   A  wave I takes token rows 16I..16I+15 (lane = row, 8 channels per K-step), converts
+//      alpha to log2 and scans it over its 16 rows with row-shift DPP adds; block totals and
+//      each block's 8th-row value go to LDS.
+//   -  decay tables, once per (block, channel): exp2 of the block references, of the earlier
+//      blocks' total G_I, and the factors that link them, so each element needs two exp2.
+//   B  factors: Q_hat, -E_hat, K_bar^T, U and block-referenced K~ tiles go to LDS. The diagonal
+//      16x16 Gram blocks are formed in registers with factors referenced to the block's 8th
+//      row (no factor exceeds the decay of 8 tokens): one fp16 pass when all of the wave's
+//      operands fit fp16, else a bf16 hi/lo split (three passes, fp32 exponent range).
 //   C  Gram blocks below the diagonal: row side exp2(local), column side
-//      exp2(blocktot - local), both <= 1, times exp2(G_I - G_{J+1}) <= 1 for non-adjacent
-//      blocks; one fp16 pass. Then each wave inverts its 16x16 diagonal block of (I + A) by
-//      fp32 forward substitution.
+//      exp2(blocktot - local), both <= 1, and for non-adjacent blocks a column side pre-scaled
+//      by exp2(G_I - G_{J+1}) <= 1; one fp16 pass. Each wave inverts its 16x16 diagonal block
+//      of (I + A) in fp32, right-looking (each finished column updates the rows below).
 //   D,E  the 16x16 inverses are merged into the 64x64 T at 32 and 64 rows:
-//      T21 = -T22 A21 T11 per 32-row half, then T[32:,:32] = -T[32:,32:] A[32:,:32] T[:32,:32].
-//   F  W = T E_hat (stored negated), then the state chain: each wave owns 16 state columns,
-//      held in accumulator registers (fp32) for the whole sequence, and computes
-//      Delta = U~ + (-W) S, O = Q_hat S + P Delta, S = gamma_last S + K_bar^T Delta.
-//      Accumulator tiles feed the next product directly: operand k-slots are chosen to match
-//      the accumulator layout (kap below), and the A operands read LDS in the same order.
+//      T10 = -T11 A10 T00 per 32-row half, then T[32:,:32] = -T[32:,32:] A[32:,:32] T[:32,:32].
+//   F  the state chain: each wave owns 16 state columns, held in accumulator registers (fp32)
+//      for the whole sequence, and computes D' = U - E_hat S, Delta = T D' (= U~ - W S),
+//      O = Q_hat S + P Delta, S = gamma_last S + K_bar^T Delta. Accumulator tiles feed the next
+//      product directly: operand k-slots are chosen to match the accumulator layout (kap
+//      below), and the A operands read LDS in the same order.
 //
 // Precision: with bf16 inputs the products take fp16 operands (fp32 accumulation, fp32 state,
 // fp32 o); with fp32 inputs they take fp32 operands (v_mfma_f32_16x16x4_f32).
@@ -133,31 +136,105 @@ struct Prec<false> {
     }
 };
 
+// ---- small helpers -------------------------------------------------------------------------
+
+// Value of lane (l16 - N) within each row of 16 lanes, 0 for the first N lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, true));
+}
+
+// Eight input elements of one row as loaded (packed bf16: one 16-byte vector; fp32: two).
+template <bool BF16>
+struct Raw8 {
+    uint4 u[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> gload8(const void* base, long idx) {
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        r.u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+        r.u[0] = p[0];
+        r.u[1] = p[1];
+    }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> fill8(float x) {
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        const uint32_t h = __float_as_uint(x) >> 16;  // exact for 0 and 1
+        const uint32_t p = h | (h << 16);
+        r.u[0] = make_uint4(p, p, p, p);
+    } else {
+        const uint32_t p = __float_as_uint(x);
+        r.u[0] = r.u[1] = make_uint4(p, p, p, p);
+    }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* x) {
+    if constexpr (BF16) {
+        const uint32_t w[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            x[4 * h + 0] = __uint_as_float(r.u[h].x);
+            x[4 * h + 1] = __uint_as_float(r.u[h].y);
+            x[4 * h + 2] = __uint_as_float(r.u[h].z);
+            x[4 * h + 3] = __uint_as_float(r.u[h].w);
+        }
+    }
+}
+
+__device__ __forceinline__ void lds_read8f(const float* p, float* x) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // ---- LDS layout ----------------------------------------------------------------------------
+// Per-(block, channel) decay tables, index t of tab[t][DK] (log2 domain, X = local value at a
+// block's 8th row, G_I = sum of earlier block totals, gC = chunk total):
+//   0..3 exp2(X_I)   4..7 exp2(G_I)   8..11 exp2(tot_I - X_I)   12..15 exp2(gC - G_{I+1})
+//   16 exp2(gC)      17 exp2(tot_1)   18 exp2(tot_1 + tot_2)    19 exp2(tot_2)
+constexpr int kTabs = 20;
+
 template <int DK, int DVT, bool F16>
 struct Smem {
     using E = typename Prec<F16>::E;
+    static constexpr int ES = (int)sizeof(E);
     static constexpr int PAD = Prec<F16>::kPad;
-    static constexpr int DKP = DK + PAD;   // token-major rows (channels)
-    static constexpr int CHP = CH + PAD;   // channel- or token-major rows of 64 tokens
-    static constexpr int A32P = CH + 4;    // fp32 A rows
-    // byte offsets
-    static constexpr int oTot = 0;                                  // float [4][DK]
-    static constexpr int oGC = oTot + 4 * DK * 4;                   // float [DK]
-    static constexpr int oQh = oGC + DK * 4;                        // E [64][DKP]
-    static constexpr int oEhT = oQh + CH * DKP * (int)sizeof(E);    // E [DK][CHP]
-    static constexpr int oKbT = oEhT + DK * CHP * (int)sizeof(E);   // E [DK][CHP]
-    static constexpr int oUT = oKbT + DK * CHP * (int)sizeof(E);    // E [DVT][CHP]
-    static constexpr int oP = oUT + DVT * CHP * (int)sizeof(E);     // E [64][CHP]
-    static constexpr int oTm = oP + CH * CHP * (int)sizeof(E);      // E [64][CHP]
-    static constexpr int oR = oTm + CH * CHP * (int)sizeof(E);      // union region
-    static constexpr int oKt = oR;                                  // E [48][DKP]
-    static constexpr int oA = oKt + 48 * DKP * (int)sizeof(E);      // float [64][A32P]
-    static constexpr int oWn = oR;                                  // E [64][DKP] (after A dies)
-    static constexpr int endR1 = oA + CH * A32P * 4;
-    static constexpr int endR2 = oWn + CH * DKP * (int)sizeof(E);
-    static constexpr int bytes = endR1 > endR2 ? endR1 : endR2;
-    static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
+    static constexpr int DKP = DK + PAD;  // token-major rows over channels
+    static constexpr int CHP = CH + PAD;  // rows over 64 tokens
+    static constexpr int A32P = CH + 4;   // fp32 A rows
+    static constexpr int UP = DVT + 4;    // fp32 U rows
+    static constexpr int oTot = 0;                          // float [4][DK]
+    static constexpr int oX = oTot + 4 * DK * 4;            // float [4][DK]
+    static constexpr int oTab = oX + 4 * DK * 4;            // float [kTabs][DK]
+    static constexpr int oQh = oTab + kTabs * DK * 4;       // E [64][DKP]   q_hat
+    static constexpr int oEn = oQh + CH * DKP * ES;         // E [64][DKP]   -e_hat
+    static constexpr int oKbT = oEn + CH * DKP * ES;        // E [DK][CHP]   k_bar^T
+    static constexpr int oP = oKbT + DK * CHP * ES;         // E [64][CHP]   P
+    static constexpr int oTm = oP + CH * CHP * ES;          // E [64][CHP]   T
+    static constexpr int oKt = oTm + CH * CHP * ES;         // E [48][DKP]   k~ of blocks 0..2
+    static constexpr int oKs = oKt + 48 * DKP * ES;         // E [3][16][DKP] k~ of pairs (2,0),(3,0),(3,1)
+    static constexpr int oA = oKs + 48 * DKP * ES;          // float [64][A32P] A below the diagonal
+    static constexpr int oAd = oA + CH * A32P * 4;          // float [4][16][16] diagonal A^T
+    static constexpr int oU = oAd + 4 * 256 * 4;            // float [64][UP] U = w v
+    static constexpr int bytes = oU + CH * UP * 4;
+    static constexpr bool fits = bytes <= 160 * 1024;
 };
 
 template <int DK, int DVT, bool BF16, bool AS, bool BS>
@@ -171,24 +248,28 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
     using E = typename PR::E;
     using Frag = typename PR::Frag;
     using SM = Smem<DK, DVT, F16>;
+    static_assert(SM::fits, "LDS budget exceeded");
     constexpr int NKS = DK / 32;   // K-steps over channels
     constexpr int NMK = DK / 16;   // 16-row tiles over channels
     constexpr int NWC = DVT / 16;  // waves owning state columns
     constexpr int CPL = DK / 4;    // channels per lane in the token-major layout
-    constexpr int DKP = SM::DKP, CHP = SM::CHP, A32P = SM::A32P;
+    constexpr int NCV = DVT / 4;   // value columns per lane in the token-major layout
+    constexpr int DKP = SM::DKP, CHP = SM::CHP, A32P = SM::A32P, UP = SM::UP;
 
     __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
     float* ldsTot = reinterpret_cast<float*>(smem + SM::oTot);
-    float* ldsGC = reinterpret_cast<float*>(smem + SM::oGC);
+    float* ldsX = reinterpret_cast<float*>(smem + SM::oX);
+    float* tab = reinterpret_cast<float*>(smem + SM::oTab);
     E* Qh = reinterpret_cast<E*>(smem + SM::oQh);
-    E* EhT = reinterpret_cast<E*>(smem + SM::oEhT);
+    E* En = reinterpret_cast<E*>(smem + SM::oEn);
     E* KbT = reinterpret_cast<E*>(smem + SM::oKbT);
-    E* UT = reinterpret_cast<E*>(smem + SM::oUT);
     E* Pm = reinterpret_cast<E*>(smem + SM::oP);
     E* Tm = reinterpret_cast<E*>(smem + SM::oTm);
     E* Kt = reinterpret_cast<E*>(smem + SM::oKt);
+    E* Ks = reinterpret_cast<E*>(smem + SM::oKs);
     float* A32 = reinterpret_cast<float*>(smem + SM::oA);
-    E* Wn = reinterpret_cast<E*>(smem + SM::oWn);
+    float* AdT = reinterpret_cast<float*>(smem + SM::oAd);
+    float* U32 = reinterpret_cast<float*>(smem + SM::oU);
 
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
 
@@ -203,6 +284,8 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
     const int hh = bh % H, bb = bh / H;
     const int mycol = tile * DVT + wv * 16 + l16;  // state column owned in the chain
     const bool chain = wv < NWC;
+    const int I = wv;              // 16-row block handled in the gate and Gram phases
+    const int r = 16 * I + l16;    // chunk row of this lane in those phases
 
     // Upper-triangle blocks of P and T are zero and never written again.
     for (int idx = threadIdx.x; idx < CH * CH; idx += blockDim.x) {
@@ -222,162 +305,269 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S0) ? S0[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
 
+    // Inputs of one chunk row for this lane, loaded one chunk ahead.
+    Raw8<BF16> rq[NKS], rk[NKS], rb[NKS], ra[NKS], rv[NCV / 8], rw[NCV / 8];
+    float ras = 1.f, rbs = 0.f;
+    auto fetch = [&](int n) {
+        const int t = n * CH + r;
+        const bool valid = t < T;
+        const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int c0 = 32 * s + 8 * g;
+            rq[s] = valid ? gload8<BF16>(q, tok * DK + c0) : fill8<BF16>(0.f);
+            rk[s] = valid ? gload8<BF16>(k, tok * DK + c0) : fill8<BF16>(0.f);
+            if constexpr (!BS) rb[s] = valid ? gload8<BF16>(b, tok * DK + c0) : fill8<BF16>(0.f);
+            if constexpr (!AS) ra[s] = valid ? gload8<BF16>(alpha, tok * DK + c0) : fill8<BF16>(1.f);
+        }
+        if constexpr (AS) ras = valid ? load_one<BF16>(alpha, tok) : 1.f;
+        if constexpr (BS) rbs = valid ? load_one<BF16>(b, tok) : 0.f;
+        const int v0 = tile * DVT + g * NCV;
+#pragma unroll
+        for (int u = 0; u < NCV / 8; ++u) {
+            rv[u] = valid ? gload8<BF16>(v, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
+            if constexpr (!BS) rw[u] = valid ? gload8<BF16>(w, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
+        }
+    };
+
     const int nch = (T + CH - 1) / CH;
+    fetch(0);
     for (int n = 0; n < nch; ++n) {
         const int t0 = n * CH;
         const int L = min(CH, T - t0);
 
-        // ---------------- A: loads and in-block log2-decay scan ----------------
-        const int I = wv;
-        const int r = 16 * I + l16;
-        const bool valid = r < L;
-        const long tok = ((long)bb * T + (t0 + (valid ? r : 0))) * H + hh;
-        float qv[CPL], kv[CPL], bv[CPL], lg[CPL];  // index 8s+i <-> channel 32s + 8g + i
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            const int c0 = 32 * s + 8 * g;
-            if (valid) {
-                load_vec<8, BF16>(q, tok * DK + c0, &qv[8 * s]);
-                load_vec<8, BF16>(k, tok * DK + c0, &kv[8 * s]);
-                if constexpr (!BS) load_vec<8, BF16>(b, tok * DK + c0, &bv[8 * s]);
-                if constexpr (!AS) load_vec<8, BF16>(alpha, tok * DK + c0, &lg[8 * s]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    qv[8 * s + i] = kv[8 * s + i] = bv[8 * s + i] = 0.f;
-                    lg[8 * s + i] = 1.f;
-                }
-            }
-        }
+        // ---------------- A: log2-decay and its scan over the block's 16 rows ----------------
+        float lg[CPL];
         if constexpr (AS) {
-            const float a = valid ? load_one<BF16>(alpha, tok) : 1.f;
+            float x1 = lg2(ras);
+            x1 += row_shr<1>(x1);
+            x1 += row_shr<2>(x1);
+            x1 += row_shr<4>(x1);
+            x1 += row_shr<8>(x1);
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) lg[e] = a;
+            for (int e = 0; e < CPL; ++e) lg[e] = x1;
+        } else {
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) unpack8<BF16>(ra[s], &lg[8 * s]);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) lg[e] = lg2(lg[e]);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) lg[e] += row_shr<1>(lg[e]);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) lg[e] += row_shr<2>(lg[e]);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) lg[e] += row_shr<4>(lg[e]);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) lg[e] += row_shr<8>(lg[e]);
         }
-        if constexpr (BS) {
-            const float be = valid ? load_one<BF16>(b, tok) : 0.f;
+        if (l16 == 15 || l16 == 7) {
+            float* dst = (l16 == 15 ? ldsTot : ldsX) + I * DK;
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) bv[e] = be;
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) lg[e] = lg2(lg[e]);
-        // inclusive scan over the 16 rows of the block (lanes l16 = 0..15 of each group)
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) {
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                const float y = __shfl_up(lg[e], d, 16);
-                if (l16 >= d) lg[e] += y;
+            for (int s = 0; s < NKS; ++s) {
+                float4* p = reinterpret_cast<float4*>(dst + 32 * s + 8 * g);
+                p[0] = make_float4(lg[8 * s], lg[8 * s + 1], lg[8 * s + 2], lg[8 * s + 3]);
+                p[1] = make_float4(lg[8 * s + 4], lg[8 * s + 5], lg[8 * s + 6], lg[8 * s + 7]);
             }
         }
-        if (l16 == 15) {
-#pragma unroll
-            for (int s = 0; s < NKS; ++s)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ldsTot[I * DK + 32 * s + 8 * g + i] = lg[8 * s + i];
+        __syncthreads();
+
+        // ---------------- decay tables, once per (block, channel) ----------------
+        for (int idx = threadIdx.x; idx < kTabs * DK; idx += blockDim.x) {
+            const int t = idx / DK, c = idx % DK;
+            const float t0v = ldsTot[c], t1v = ldsTot[DK + c], t2v = ldsTot[2 * DK + c];
+            const float t3v = ldsTot[3 * DK + c];
+            const float G[5] = {0.f, t0v, t0v + t1v, t0v + t1v + t2v, t0v + t1v + t2v + t3v};
+            const float tot[4] = {t0v, t1v, t2v, t3v};
+            const int Ib = t & 3;
+            float e;
+            if (t < 4) e = ldsX[Ib * DK + c];
+            else if (t < 8) e = G[Ib];
+            else if (t < 12) e = tot[Ib] - ldsX[Ib * DK + c];
+            else if (t < 16) e = G[4] - G[Ib + 1];
+            else if (t == 16) e = G[4];
+            else if (t == 17) e = t1v;
+            else if (t == 18) e = t1v + t2v;
+            else e = t2v;
+            tab[t * DK + c] = ex2(e);
         }
         __syncthreads();
 
         // ---------------- B: factors, LDS operand tiles, diagonal Gram blocks ----------------
-        float er[CPL], qr[CPL];  // row-side Gram factors referenced to the block start
+        Frag erf[NKS], qrf[NKS];  // row-side Gram factors (block-start reference)
         {
+            // Diagonal Gram blocks use one fp16 pass; if any of the wave's operands does not
+            // fit fp16 the block is recomputed below with a bf16 hi/lo split.
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            float vmax = 0.f;
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
-                float qh[8], eh[8], kb[8], kt[8], em[8], qm[8], km[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int e = 8 * s + i;
-                    const int c = 32 * s + 8 * g + i;
-                    float Gi = 0.f, gC = 0.f;
-#pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        const float t = ldsTot[J * DK + c];
-                        if (J < I) Gi += t;
-                        gC += t;
-                    }
-                    const float totI = ldsTot[I * DK + c];
-                    const float X = __shfl(lg[e], 7, 16);  // local value at the block's 8th row
-                    const float Gam = Gi + lg[e];
-                    const float gam = ex2(Gam);
-                    const float ebk = bv[e] * kv[e];
-                    qh[i] = qv[e] * gam;
-                    eh[i] = ebk * gam;
-                    kb[i] = kv[e] * ex2(gC - Gam);
-                    kt[i] = kv[e] * ex2(totI - lg[e]);
-                    const float fl = ex2(lg[e]);
-                    er[e] = ebk * fl;
-                    qr[e] = qv[e] * fl;
-                    const float fm = ex2(lg[e] - X);
-                    em[i] = ebk * fm;
-                    qm[i] = qv[e] * fm;
-                    km[i] = kv[e] * ex2(X - lg[e]);
-                    if (wv == 0 && l16 == 0) ldsGC[c] = ex2(gC);
-                }
                 const int c0 = 32 * s + 8 * g;
-                PR::store8(&Qh[r * DKP + c0], qh);
-                if (I < 3) PR::store8(&Kt[r * DKP + c0], kt);
+                float qx[8], kx[8], bx[8], X8[8], fX[8], fG[8], fTX[8], fCG[8];
+                unpack8<BF16>(rq[s], qx);
+                unpack8<BF16>(rk[s], kx);
+                if constexpr (BS) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) bx[i] = rbs;
+                } else {
+                    unpack8<BF16>(rb[s], bx);
+                }
+                lds_read8f(ldsX + I * DK + c0, X8);
+                lds_read8f(tab + (0 + I) * DK + c0, fX);
+                lds_read8f(tab + (4 + I) * DK + c0, fG);
+                lds_read8f(tab + (8 + I) * DK + c0, fTX);
+                lds_read8f(tab + (12 + I) * DK + c0, fCG);
+                float em[8], qm[8], km[8], er[8], qr[8], qh[8], en[8], kt[8], kb[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    EhT[(c0 + i) * CHP + r] = (E)eh[i];
-                    KbT[(c0 + i) * CHP + r] = (E)kb[i];
+                    const float d = lg[8 * s + i] - X8[i];
+                    const float fm = ex2(d), fmi = ex2(-d);
+                    const float bk = bx[i] * kx[i];
+                    em[i] = bk * fm;
+                    qm[i] = qx[i] * fm;
+                    km[i] = kx[i] * fmi;
+                    vmax = fmaxf(vmax, fmaxf(fabsf(em[i]), fmaxf(fabsf(qm[i]), fabsf(km[i]))));
+                    const float fl = fm * fX[i];
+                    er[i] = bk * fl;
+                    qr[i] = qx[i] * fl;
+                    const float gam = fl * fG[i];
+                    qh[i] = qx[i] * gam;
+                    en[i] = -(bk * gam);
+                    kt[i] = km[i] * fTX[i];
+                    kb[i] = kt[i] * fCG[i];
                 }
-                PR::mma_wide(accA, em, km);
-                PR::mma_wide(accP, qm, km);
+                erf[s] = PR::make(er);
+                qrf[s] = PR::make(qr);
+                {
+                    const Frag kmf = PR::make(km);
+                    PR::mma(accA, PR::make(em), kmf);
+                    PR::mma(accP, PR::make(qm), kmf);
+                }
+                PR::store8(&Qh[r * DKP + c0], qh);
+                PR::store8(&En[r * DKP + c0], en);
+                if (I < 3) PR::store8(&Kt[r * DKP + c0], kt);
+                if (I < 2) {
+                    float c8[8], ks[8];
+                    if (I == 0) {
+                        lds_read8f(tab + 17 * DK + c0, c8);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ks[i] = kt[i] * c8[i];
+                        PR::store8(&Ks[(0 * 16 + l16) * DKP + c0], ks);
+                        lds_read8f(tab + 18 * DK + c0, c8);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ks[i] = kt[i] * c8[i];
+                        PR::store8(&Ks[(1 * 16 + l16) * DKP + c0], ks);
+                    } else {
+                        lds_read8f(tab + 19 * DK + c0, c8);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ks[i] = kt[i] * c8[i];
+                        PR::store8(&Ks[(2 * 16 + l16) * DKP + c0], ks);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) KbT[(c0 + i) * CHP + r] = (E)kb[i];
+            }
+            if (F16 && !__all(vmax < 32768.f)) {
+                // Strong decay inside the block: redo the diagonal Gram block with bf16 hi/lo
+                // operands. The chunk row is reloaded (the registers already hold the next use).
+                accA = f4{0.f, 0.f, 0.f, 0.f};
+                accP = f4{0.f, 0.f, 0.f, 0.f};
+                const int t = t0 + r;
+                const bool valid = t < T;
+                const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
+                float lg2v[CPL];
+                if constexpr (AS) {
+                    float x1 = lg2(valid ? load_one<BF16>(alpha, tok) : 1.f);
+                    x1 += row_shr<1>(x1);
+                    x1 += row_shr<2>(x1);
+                    x1 += row_shr<4>(x1);
+                    x1 += row_shr<8>(x1);
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e) lg2v[e] = x1;
+                } else {
+#pragma unroll
+                    for (int s = 0; s < NKS; ++s)
+                        unpack8<BF16>(valid ? gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g) : fill8<BF16>(1.f),
+                                      &lg2v[8 * s]);
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e) {
+                        float x1 = lg2(lg2v[e]);
+                        x1 += row_shr<1>(x1);
+                        x1 += row_shr<2>(x1);
+                        x1 += row_shr<4>(x1);
+                        x1 += row_shr<8>(x1);
+                        lg2v[e] = x1;
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    const int c0 = 32 * s + 8 * g;
+                    float qx[8], kx[8], bx[8], X8[8], em[8], qm[8], km[8];
+                    unpack8<BF16>(valid ? gload8<BF16>(q, tok * DK + c0) : fill8<BF16>(0.f), qx);
+                    unpack8<BF16>(valid ? gload8<BF16>(k, tok * DK + c0) : fill8<BF16>(0.f), kx);
+                    if constexpr (BS) {
+                        const float be = valid ? load_one<BF16>(b, tok) : 0.f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) bx[i] = be;
+                    } else {
+                        unpack8<BF16>(valid ? gload8<BF16>(b, tok * DK + c0) : fill8<BF16>(0.f), bx);
+                    }
+                    lds_read8f(ldsX + I * DK + c0, X8);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float d = lg2v[8 * s + i] - X8[i];
+                        const float fm = ex2(d);
+                        em[i] = bx[i] * kx[i] * fm;
+                        qm[i] = qx[i] * fm;
+                        km[i] = kx[i] * ex2(-d);
+                    }
+                    PR::mma_wide(accA, em, km);
+                    PR::mma_wide(accP, qm, km);
+                }
             }
             // accumulator layout: row 4g+j of the block, column l16
+            float4 at;
+            at.x = (4 * g + 0) > l16 ? accA[0] : 0.f;
+            at.y = (4 * g + 1) > l16 ? accA[1] : 0.f;
+            at.z = (4 * g + 2) > l16 ? accA[2] : 0.f;
+            at.w = (4 * g + 3) > l16 ? accA[3] : 0.f;
+            *reinterpret_cast<float4*>(AdT + I * 256 + l16 * 16 + 4 * g) = at;  // A_II^T[col][row]
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rr = 4 * g + j;
-                A32[(16 * I + rr) * A32P + 16 * I + l16] = rr > l16 ? accA[j] : 0.f;
                 Pm[(16 * I + rr) * CHP + 16 * I + l16] = (E)(rr >= l16 ? accP[j] : 0.f);
             }
-            // U^T for this workgroup's value tile: lane (row r, group g) covers DVT/4 columns
+            // U = w v for this lane's row and NCV value columns
             {
-                constexpr int NC = DVT / 4;
-                float vv[NC], ww[NC];
-                const int cl0 = g * NC;
-                const long vtok = ((long)bb * T + (t0 + (valid ? r : 0))) * H + hh;
-                if (valid) {
-                    load_vec<NC, BF16>(v, vtok * DV + tile * DVT + cl0, vv);
+                float* up = U32 + r * UP + g * NCV;
+#pragma unroll
+                for (int u = 0; u < NCV / 8; ++u) {
+                    float vx[8], wx[8];
+                    unpack8<BF16>(rv[u], vx);
                     if constexpr (BS) {
 #pragma unroll
-                        for (int i = 0; i < NC; ++i) ww[i] = bv[0];
+                        for (int i = 0; i < 8; ++i) wx[i] = rbs;
                     } else {
-                        load_vec<NC, BF16>(w, vtok * DV + tile * DVT + cl0, ww);
+                        unpack8<BF16>(rw[u], wx);
                     }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NC; ++i) vv[i] = ww[i] = 0.f;
+                    float4* p = reinterpret_cast<float4*>(up + 8 * u);
+                    p[0] = make_float4(wx[0] * vx[0], wx[1] * vx[1], wx[2] * vx[2], wx[3] * vx[3]);
+                    p[1] = make_float4(wx[4] * vx[4], wx[5] * vx[5], wx[6] * vx[6], wx[7] * vx[7]);
                 }
-#pragma unroll
-                for (int i = 0; i < NC; ++i) UT[(cl0 + i) * CHP + r] = (E)(ww[i] * vv[i]);
             }
         }
         __syncthreads();
 
-        // ---------------- C: Gram blocks below the diagonal; diagonal UT inverses ----------------
+        // ---------------- C: next chunk's loads; Gram blocks below the diagonal; T_II ----------------
+        if (n + 1 < nch) fetch(n + 1);
         for (int J = 0; J < I; ++J) {
+            const E* kb_ = (J == I - 1) ? Kt + (16 * J) * DKP
+                                        : Ks + (16 * (I == 2 ? 0 : (J == 0 ? 1 : 2))) * DKP;
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
-                float ea[8], qa[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int e = 8 * s + i;
-                    const int c = 32 * s + 8 * g + i;
-                    float cij = 1.f;
-                    if (J < I - 1) {  // exp2(G_I - G_{J+1}) = exp2(sum of the blocks between)
-                        float between = 0.f;
-                        for (int Jm = J + 1; Jm < I; ++Jm) between += ldsTot[Jm * DK + c];
-                        cij = ex2(between);
-                    }
-                    ea[i] = er[e] * cij;
-                    qa[i] = qr[e] * cij;
-                }
-                const Frag kf = PR::lds8(&Kt[(16 * J + l16) * DKP + 32 * s + 8 * g]);
-                PR::mma(accA, PR::make(ea), kf);
-                PR::mma(accP, PR::make(qa), kf);
+                const Frag kf = PR::lds8(kb_ + l16 * DKP + 32 * s + 8 * g);
+                PR::mma(accA, erf[s], kf);
+                PR::mma(accP, qrf[s], kf);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -386,18 +576,18 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 Pm[rr * CHP + 16 * J + l16] = (E)accP[j];
             }
         }
-        // T_II = (I + A_II)^-1 by forward substitution; lane l16 of group 0 owns column l16
+        // T_II = (I + A_II)^-1, right-looking: once column m of T is final, it updates the rows below
         if (g == 0) {
-            float tc[16];
+            float acc[16], tc[16];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) tc[m] = (m == l16) ? 1.f : 0.f;
-            const float* Ab = A32 + (16 * I) * A32P + 16 * I;
+            for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+            const float* Ab = AdT + I * 256;
 #pragma unroll
-            for (int rr = 1; rr < 16; ++rr) {
-                float acc = 0.f;
+            for (int m = 0; m < 16; ++m) {
+                const float tm = m < l16 ? 0.f : (m == l16 ? 1.f : -acc[m]);
+                tc[m] = tm;
 #pragma unroll
-                for (int m = 0; m < rr; ++m) acc = fmaf(Ab[rr * A32P + m], tc[m], acc);
-                if (rr > l16) tc[rr] = -acc;
+                for (int rr = m + 1; rr < 16; ++rr) acc[rr] = fmaf(Ab[m * 16 + rr], tm, acc[rr]);
             }
 #pragma unroll
             for (int m = 0; m < 16; ++m) Tm[(16 * I + m) * CHP + 16 * I + l16] = (E)tc[m];
@@ -464,25 +654,7 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         }
         __syncthreads();
 
-        // ---------------- F1: -W = -T E_hat into LDS (overlays K~ and A) ----------------
-        for (int nt = wv; nt < NMK; nt += 4) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s <= mt / 2; ++s) {
-                    const E* tr = &Tm[(16 * mt + l16) * CHP + 32 * s];
-                    const E* er_ = &EhT[(16 * nt + l16) * CHP + 32 * s];
-                    PR::mma(acc, PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g),
-                            PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g));
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Wn[(16 * mt + 4 * g + j) * DKP + 16 * nt + l16] = (E)(-acc[j]);
-            }
-        }
-        __syncthreads();
-
-        // ---------------- F2: the state chain for this wave's 16 columns ----------------
+        // ---------------- F: the state chain for this wave's 16 columns ----------------
         if (chain) {
             // state as B operand: K-step s covers channels 32s..32s+31 = tiles 2s, 2s+1
             Frag Sf[NKS];
@@ -496,29 +668,22 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 }
                 Sf[s] = PR::make(sv);
             }
+            // D' = U - E_hat S and O = Q_hat S
             f4 D[4], O[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                D[mt] = f4{0.f, 0.f, 0.f, 0.f};
-                O[mt] = f4{0.f, 0.f, 0.f, 0.f};
-                // U~ = T U
 #pragma unroll
-                for (int s = 0; s <= mt / 2; ++s) {
-                    const E* tr = &Tm[(16 * mt + l16) * CHP + 32 * s];
-                    const E* ur = &UT[(16 * wv + l16) * CHP + 32 * s];
-                    PR::mma(D[mt], PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g),
-                            PR::lds_pair(ur + 4 * g, ur + 16 + 4 * g));
-                }
-                // Delta = U~ + (-W) S ; O = Q_hat S
+                for (int j = 0; j < 4; ++j) D[mt][j] = U32[(16 * mt + 4 * g + j) * UP + 16 * wv + l16];
+                O[mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
-                    const E* wr = &Wn[(16 * mt + l16) * DKP + 32 * s];
+                    const E* er_ = &En[(16 * mt + l16) * DKP + 32 * s];
                     const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
-                    PR::mma(D[mt], PR::lds_pair(wr + 4 * g, wr + 16 + 4 * g), Sf[s]);
+                    PR::mma(D[mt], PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g), Sf[s]);
                     PR::mma(O[mt], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g), Sf[s]);
                 }
             }
-            // Delta as B operand over tokens: K-step s2 covers tokens 32 s2 .. 32 s2 + 31
+            // Delta = T D' (T lower triangular: token K-steps s2 <= mt / 2)
             Frag Df[2];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -527,6 +692,26 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 for (int i = 0; i < 4; ++i) {
                     dv_[i] = D[2 * s2][i];
                     dv_[i + 4] = D[2 * s2 + 1][i];
+                }
+                Df[s2] = PR::make(dv_);
+            }
+            f4 Dl[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                Dl[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 <= mt / 2; ++s2) {
+                    const E* tr = &Tm[(16 * mt + l16) * CHP + 32 * s2];
+                    PR::mma(Dl[mt], PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g), Df[s2]);
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                float dv_[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dv_[i] = Dl[2 * s2][i];
+                    dv_[i + 4] = Dl[2 * s2 + 1][i];
                 }
                 Df[s2] = PR::make(dv_);
             }
@@ -547,8 +732,11 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
             // S <- Diag(gamma_last) S + K_bar^T Delta
 #pragma unroll
             for (int mk = 0; mk < NMK; ++mk) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Sacc[mk][j] *= ldsGC[16 * mk + 4 * g + j];
+                const float4 gc = *reinterpret_cast<const float4*>(tab + 16 * DK + 16 * mk + 4 * g);
+                Sacc[mk][0] *= gc.x;
+                Sacc[mk][1] *= gc.y;
+                Sacc[mk][2] *= gc.z;
+                Sacc[mk][3] *= gc.w;
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const E* kr = &KbT[(16 * mk + l16) * CHP + 32 * s2];
@@ -595,7 +783,7 @@ hipError_t launch_flags(const ChunkArgs& a, hipStream_t s) {
 bool chunk_supported(int DK, int DV, bool bf16) {
     if (DK != DV) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
-    return DK == 32 || DK == 64;
+    return DK == 32 || DK == 64;  // fp32 operand tiles of d = 128 exceed the LDS budget
 }
 
 size_t chunk_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16, uint32_t flags) {

@@ -181,8 +181,11 @@ def _mm_bf16x3(a, b):
     return round_f32(ah @ bh + ah @ bl + al @ bh)
 
 
-def kernel_scheme_model(q, k, v, alpha, b, w, S0=None):
+def kernel_scheme_model(q, k, v, alpha, b, w, S0=None, *, delta_form="TU-WS", diag="bf16x3"):
     """The chunk kernel's exact operand-precision scheme for bf16 inputs, in numpy.
+
+    delta_form "TU-WS" forms W = T E_hat and U~ = T U first; "T(U-ES)" applies T after
+    subtracting E_hat S (no W). diag "bf16x3" or "f16" selects the diagonal Gram operands.
 
     C = 64 in four 16-row blocks. Vector math in fp32. Gram blocks below the diagonal: fp16
     operands with block-boundary references (row side exp(local), times exp(G_I - G_{J+1})
@@ -231,8 +234,9 @@ def kernel_scheme_model(q, k, v, alpha, b, w, S0=None):
             X = local[16 * I + 7]
             fm = round_f32(np.exp(round_f32(local[rI] - X)))
             km = round_f32(kc[rI] * round_f32(np.exp(round_f32(X - local[rI]))))
-            A[rI, rI] = _mm_bf16x3(round_f32(e[rI] * fm), km.T)
-            Pm[rI, rI] = _mm_bf16x3(round_f32(qc[rI] * fm), km.T)
+            mm_diag = _mm_bf16x3 if diag == "bf16x3" else _mm16
+            A[rI, rI] = mm_diag(round_f32(e[rI] * fm), km.T)
+            Pm[rI, rI] = mm_diag(round_f32(qc[rI] * fm), km.T)
             for J in range(I):
                 rJ = slice(16 * J, 16 * J + 16)
                 kt = round_f32(kc[rJ] * round_f32(np.exp(round_f32(tot[J] - local[rJ]))))
@@ -260,11 +264,14 @@ def kernel_scheme_model(q, k, v, alpha, b, w, S0=None):
         Tm[32:, :32] = -_mm16(Tm[32:, 32:], Y)
         gam = round_f32(np.exp(Gam))
         E_hat = round_f32(e * gam)
-        W = _mm16(Tm, E_hat)
         U = round_f32(wc * vc)
-        Ut = _mm16(Tm, U)
         Q_hat = round_f32(qc * gam)
-        Delta = round_f32(Ut - _mm16(W, S))
+        if delta_form == "TU-WS":
+            W = _mm16(Tm, E_hat)
+            Ut = _mm16(Tm, U)
+            Delta = round_f32(Ut - _mm16(W, S))
+        else:  # Delta = T (U - E_hat S)
+            Delta = _mm16(Tm, round_f32(U - _mm16(E_hat, S)))
         O = round_f32(_mm16(Q_hat, S) + _mm16(Pm, Delta))
         o[c0:c0 + L] = O[:L]
         K_bar = round_f32(kc * round_f32(np.exp(round_f32(Gam[C - 1] - Gam))))
