@@ -32,7 +32,7 @@
 //      T10 = -T11 A10 T00 per 32-row half, then T[32:,:32] = -T[32:,32:] A[32:,:32] T[:32,:32].
 //   F  the state chain: each wave owns 16 state columns, held in accumulator registers (fp32)
 //      for the whole sequence, and computes D' = U - E_hat S, Delta = T D' (= U~ - W S),
-//      O = Q_hat S + P Delta, S = gamma_last S + K_bar^T Delta. Accumulator tiles feed the next
+//      O^T = S^T Q_hat^T + Delta^T P^T, S = gamma_last S + K_bar^T Delta. Accumulator tiles feed the next
 //      product directly: operand k-slots are chosen to match the accumulator layout (kap
 //      below), and the A operands read LDS in the same order.
 //
@@ -57,6 +57,14 @@ constexpr int CH = 64;  // chunk length
 __device__ __forceinline__ int kap(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS only. Waves exchange data through LDS alone, so global
+// loads in flight (the next chunk's inputs) and global stores need not drain at a barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
 // ---- operand precision policies ---------------------------------------------------------
@@ -305,33 +313,51 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S0) ? S0[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
 
-    // Inputs of one chunk row for this lane, loaded one chunk ahead.
+    // Inputs of one chunk row for this lane, loaded one chunk ahead. The loads of the next
+    // chunk are issued in portions spread over the current one, each as soon as its registers
+    // are free (part 0: alpha after the scan; 1: q, v, w after the factors; 2: k and 3: b
+    // during the state chain), so the vector-memory queue never backs up into the issuing wave.
     Raw8<BF16> rq[NKS], rk[NKS], rb[NKS], ra[NKS], rv[NCV / 8], rw[NCV / 8];
     float ras = 1.f, rbs = 0.f;
-    auto fetch = [&](int n) {
+    auto fetch = [&](int n, int part) {
         const int t = n * CH + r;
         const bool valid = t < T;
         const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
+        if (part == 0) {
+            if constexpr (AS) {
+                ras = valid ? load_one<BF16>(alpha, tok) : 1.f;
+            } else {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            const int c0 = 32 * s + 8 * g;
-            rq[s] = valid ? gload8<BF16>(q, tok * DK + c0) : fill8<BF16>(0.f);
-            rk[s] = valid ? gload8<BF16>(k, tok * DK + c0) : fill8<BF16>(0.f);
-            if constexpr (!BS) rb[s] = valid ? gload8<BF16>(b, tok * DK + c0) : fill8<BF16>(0.f);
-            if constexpr (!AS) ra[s] = valid ? gload8<BF16>(alpha, tok * DK + c0) : fill8<BF16>(1.f);
-        }
-        if constexpr (AS) ras = valid ? load_one<BF16>(alpha, tok) : 1.f;
-        if constexpr (BS) rbs = valid ? load_one<BF16>(b, tok) : 0.f;
-        const int v0 = tile * DVT + g * NCV;
+                for (int s = 0; s < NKS; ++s)
+                    ra[s] = valid ? gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g) : fill8<BF16>(1.f);
+            }
+        } else if (part == 1) {
 #pragma unroll
-        for (int u = 0; u < NCV / 8; ++u) {
-            rv[u] = valid ? gload8<BF16>(v, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
-            if constexpr (!BS) rw[u] = valid ? gload8<BF16>(w, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
+            for (int s = 0; s < NKS; ++s)
+                rq[s] = valid ? gload8<BF16>(q, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+            const int v0 = tile * DVT + g * NCV;
+#pragma unroll
+            for (int u = 0; u < NCV / 8; ++u) {
+                rv[u] = valid ? gload8<BF16>(v, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
+                if constexpr (!BS) rw[u] = valid ? gload8<BF16>(w, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
+            }
+        } else if (part == 2) {
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                rk[s] = valid ? gload8<BF16>(k, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+        } else {
+            if constexpr (BS) {
+                rbs = valid ? load_one<BF16>(b, tok) : 0.f;
+            } else {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s)
+                    rb[s] = valid ? gload8<BF16>(b, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+            }
         }
     };
 
     const int nch = (T + CH - 1) / CH;
-    fetch(0);
+    for (int part = 0; part < 4; ++part) fetch(0, part);
     for (int n = 0; n < nch; ++n) {
         const int t0 = n * CH;
         const int L = min(CH, T - t0);
@@ -369,28 +395,39 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 p[1] = make_float4(lg[8 * s + 4], lg[8 * s + 5], lg[8 * s + 6], lg[8 * s + 7]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- decay tables, once per (block, channel) ----------------
-        for (int idx = threadIdx.x; idx < kTabs * DK; idx += blockDim.x) {
-            const int t = idx / DK, c = idx % DK;
-            const float t0v = ldsTot[c], t1v = ldsTot[DK + c], t2v = ldsTot[2 * DK + c];
-            const float t3v = ldsTot[3 * DK + c];
-            const float G[5] = {0.f, t0v, t0v + t1v, t0v + t1v + t2v, t0v + t1v + t2v + t3v};
-            const float tot[4] = {t0v, t1v, t2v, t3v};
-            const int Ib = t & 3;
-            float e;
-            if (t < 4) e = ldsX[Ib * DK + c];
-            else if (t < 8) e = G[Ib];
-            else if (t < 12) e = tot[Ib] - ldsX[Ib * DK + c];
-            else if (t < 16) e = G[4] - G[Ib + 1];
-            else if (t == 16) e = G[4];
-            else if (t == 17) e = t1v;
-            else if (t == 18) e = t1v + t2v;
-            else e = t2v;
-            tab[t * DK + c] = ex2(e);
+        const bool more = n + 1 < nch;
+        if (more) fetch(n + 1, 0);
+        {
+            constexpr int TPC = 256 / DK;  // threads per channel
+            const int c = threadIdx.x % DK, part = threadIdx.x / DK;
+            float tot[4], X[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                tot[J] = ldsTot[J * DK + c];
+                X[J] = ldsX[J * DK + c];
+            }
+            const float G[5] = {0.f, tot[0], tot[0] + tot[1], tot[0] + tot[1] + tot[2],
+                                tot[0] + tot[1] + tot[2] + tot[3]};
+            float e[kTabs];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                e[J] = X[J];
+                e[4 + J] = G[J];
+                e[8 + J] = tot[J] - X[J];
+                e[12 + J] = G[4] - G[J + 1];
+            }
+            e[16] = G[4];
+            e[17] = tot[1];
+            e[18] = tot[1] + tot[2];
+            e[19] = tot[2];
+#pragma unroll
+            for (int t = 0; t < kTabs; ++t)
+                if (t % TPC == part) tab[t * DK + c] = ex2(e[t]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- B: factors, LDS operand tiles, diagonal Gram blocks ----------------
         Frag erf[NKS], qrf[NKS];  // row-side Gram factors (block-start reference)
@@ -555,10 +592,10 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- C: next chunk's loads; Gram blocks below the diagonal; T_II ----------------
-        if (n + 1 < nch) fetch(n + 1);
+        if (more) fetch(n + 1, 1);
         for (int J = 0; J < I; ++J) {
             const E* kb_ = (J == I - 1) ? Kt + (16 * J) * DKP
                                         : Ks + (16 * (I == 2 ? 0 : (J == 0 ? 1 : 2))) * DKP;
@@ -576,23 +613,38 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 Pm[rr * CHP + 16 * J + l16] = (E)accP[j];
             }
         }
-        // T_II = (I + A_II)^-1, right-looking: once column m of T is final, it updates the rows below
+        // T_II = (I + A_II)^-1, right-looking: once column m of T is final, it updates the rows
+        // below. Column m + 1 of A_II is read from LDS while column m is applied.
         if (g == 0) {
             float acc[16], tc[16];
 #pragma unroll
             for (int m = 0; m < 16; ++m) acc[m] = 0.f;
-            const float* Ab = AdT + I * 256;
+            const float4* Ab4 = reinterpret_cast<const float4*>(AdT + I * 256);
+            float4 cur[4], nxt[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) cur[q4] = Ab4[q4];
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
+                if (m + 1 < 16) {
+#pragma unroll
+                    for (int q4 = (m + 2) / 4; q4 < 4; ++q4) nxt[q4] = Ab4[(m + 1) * 4 + q4];
+                }
                 const float tm = m < l16 ? 0.f : (m == l16 ? 1.f : -acc[m]);
                 tc[m] = tm;
 #pragma unroll
-                for (int rr = m + 1; rr < 16; ++rr) acc[rr] = fmaf(Ab[m * 16 + rr], tm, acc[rr]);
+                for (int q4 = (m + 1) / 4; q4 < 4; ++q4) {
+                    const float av[4] = {cur[q4].x, cur[q4].y, cur[q4].z, cur[q4].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * q4 + i > m) acc[4 * q4 + i] = fmaf(av[i], tm, acc[4 * q4 + i]);
+                }
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
             }
 #pragma unroll
             for (int m = 0; m < 16; ++m) Tm[(16 * I + m) * CHP + 16 * I + l16] = (E)tc[m];
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- D: T10 = -T11 A10 T00 and T32 = -T33 A32 T22 ----------------
         if (wv == 1 || wv == 3) {
@@ -616,7 +668,7 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
 #pragma unroll
             for (int j = 0; j < 4; ++j) Tm[(16 * Ib + 4 * g + j) * CHP + 16 * Jb + l16] = (E)(-Y[j]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- E: T[32:, :32] = -T[32:, 32:] A[32:, :32] T[:32, :32] ----------------
         if (wv < 2) {
@@ -652,9 +704,10 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 for (int j = 0; j < 4; ++j) Tm[(16 * Ib + 4 * g + j) * CHP + 16 * Jb + l16] = (E)(-Z[j]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- F: the state chain for this wave's 16 columns ----------------
+        if (more) fetch(n + 1, 2);
         if (chain) {
             // state as B operand: K-step s covers channels 32s..32s+31 = tiles 2s, 2s+1
             Frag Sf[NKS];
@@ -668,7 +721,9 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 }
                 Sf[s] = PR::make(sv);
             }
-            // D' = U - E_hat S and O = Q_hat S
+            // D' = U - E_hat S, and O^T = S^T Q_hat^T: the state fragments serve as the A
+            // operand of the transposed product, so O^T tile nt holds, per lane, four
+            // consecutive state columns (rows 4g..4g+3) of token 16 nt + l16.
             f4 D[4], O[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -680,9 +735,10 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     const E* er_ = &En[(16 * mt + l16) * DKP + 32 * s];
                     const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
                     PR::mma(D[mt], PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g), Sf[s]);
-                    PR::mma(O[mt], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g), Sf[s]);
+                    PR::mma(O[mt], Sf[s], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g));
                 }
             }
+            if (more) fetch(n + 1, 3);
             // Delta = T D' (T lower triangular: token K-steps s2 <= mt / 2)
             Frag Df[2];
 #pragma unroll
@@ -715,18 +771,18 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                 }
                 Df[s2] = PR::make(dv_);
             }
-            // O += P Delta, then store the valid rows
+            // O^T += Delta^T P^T (P lower triangular), then store four columns per lane
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-                for (int s2 = 0; s2 <= mt / 2; ++s2) {
-                    const E* pr = &Pm[(16 * mt + l16) * CHP + 32 * s2];
-                    PR::mma(O[mt], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g), Df[s2]);
+                for (int s2 = 0; s2 <= nt / 2; ++s2) {
+                    const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
+                    PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * mt + 4 * g + j;
-                    if (row < L) o[(((long)bb * T + t0 + row) * H + hh) * DV + mycol] = O[mt][j];
+                const int row = 16 * nt + l16;
+                if (row < L) {
+                    float* op = o + (((long)bb * T + t0 + row) * H + hh) * DV + tile * DVT + 16 * wv + 4 * g;
+                    *reinterpret_cast<float4*>(op) = make_float4(O[nt][0], O[nt][1], O[nt][2], O[nt][3]);
                 }
             }
             // S <- Diag(gamma_last) S + K_bar^T Delta
@@ -743,8 +799,10 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     PR::mma(Sacc[mk], PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g), Df[s2]);
                 }
             }
+        } else if (more) {
+            fetch(n + 1, 3);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (chain && S_out) {
