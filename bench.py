@@ -49,7 +49,7 @@ def decode_bytes_per_head(dk: int, dv: int) -> float:
 
 def time_prefill(g, ins, steps, warmup, impl):
     import torch
-    fn = g.chunk_fwd if impl == "chunk" else g.recurrent_fwd
+    fn = g.recurrent_fwd if impl == "recurrent" else g.chunk_fwd
     args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")]
     B, T, H, dk = ins["q"].shape
     dv = ins["v"].shape[-1]
@@ -60,6 +60,8 @@ def time_prefill(g, ins, steps, warmup, impl):
         need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
         if need:
             kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
+    elif impl == "fused":
+        kw["fused"] = True
     for _ in range(warmup):
         fn(*args, ins["S0"], **kw)
     torch.cuda.synchronize()
@@ -140,7 +142,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--impl", choices=["chunk", "recurrent"], default="chunk")
+    ap.add_argument("--impl", choices=["chunk", "fused", "recurrent"], default="chunk",
+                    help="chunk: two-kernel chunkwise path (with workspace); fused: single-kernel "
+                         "chunkwise path; recurrent: token-by-token kernel")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128)
@@ -222,7 +226,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-in/f16-mfma/f32-state" if args.impl == "chunk" else "bf16-in/f32",
+        "dtype": "bf16-in/f32" if args.impl == "recurrent" else "bf16-in/f16-mfma/f32-state",
         "data": "synthetic",
         "config": {"workload": "GDN-2 layer prefill B8 H16 T4096 d_k=d_v=128, chunk 64",
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,

@@ -122,8 +122,12 @@ def chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) 
 
 
 def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspace=None,
-              stream=None):
-    """Chunkwise prefill (C = 64). Returns (o [B, T, H, d_v] fp32, S_T [B, H, d_k, d_v])."""
+              fused=False, stream=None):
+    """Chunkwise prefill (C = 64). Returns (o [B, T, H, d_v] fp32, S_T [B, H, d_k, d_v]).
+
+    With a workspace (allocated here unless given) the library runs its two-kernel path;
+    fused=True passes none and runs the single-kernel path.
+    """
     lib = load()
     flags = _check_inputs(q, k, v, alpha, b, w, 4)
     B, T, H, dk = q.shape
@@ -132,7 +136,7 @@ def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspa
         o = torch.empty(B, T, H, dv, device=q.device, dtype=torch.float32)
     S_out = _state_out(S0, B, H, dk, dv, q.device, S_out)
     dt = _dtype_code(q)
-    need = int(lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
+    need = 0 if fused else int(lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
     if need and workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

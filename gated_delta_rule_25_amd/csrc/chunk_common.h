@@ -1,0 +1,183 @@
+// chunk_common.h -- device helpers shared by the chunkwise prefill kernels (gfx950).
+#pragma once
+
+#include "common.h"
+
+namespace gdn2 {
+namespace chunk {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;  // chunk length
+
+// k-slot i of lane group g inside a 32-wide K-step, matching two stacked accumulator tiles:
+// slots 0..3 are rows 4g..4g+3 of the first tile, slots 4..7 rows 4g..4g+3 of the second.
+__device__ __forceinline__ int kap(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS only. Waves exchange data through LDS alone, so global
+// loads in flight (the next chunk's inputs) and global stores need not drain at a barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- operand precision policies ---------------------------------------------------------
+template <bool F16>
+struct Prec;
+
+template <>
+struct Prec<true> {
+    using E = _Float16;
+    static constexpr int kPad = 8;  // 16 bytes of row padding
+    using Frag = h8;
+    __device__ static Frag make(const float* x) {
+        Frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (_Float16)x[i];
+        return f;
+    }
+    // slots 0..3 from p0[0..3], slots 4..7 from p1[0..3]
+    __device__ static Frag lds_pair(const E* p0, const E* p1) {
+        const h4 a = *reinterpret_cast<const h4*>(p0);
+        const h4 b = *reinterpret_cast<const h4*>(p1);
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    __device__ static Frag lds8(const E* p) { return *reinterpret_cast<const h8*>(p); }
+    __device__ static void store8(E* p, const float* x) { *reinterpret_cast<h8*>(p) = make(x); }
+    __device__ static void mma(f4& c, const Frag& a, const Frag& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    // Gram diagonal blocks: bf16 hi/lo split of both operands, hi*hi + hi*lo + lo*hi.
+    __device__ static void mma_wide(f4& c, const float* a, const float* b) {
+        b8 ah, al, bh, bl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const __bf16 x = (__bf16)a[i];
+            ah[i] = x;
+            al[i] = (__bf16)(a[i] - (float)x);
+            const __bf16 y = (__bf16)b[i];
+            bh[i] = y;
+            bl[i] = (__bf16)(b[i] - (float)y);
+        }
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Prec<false> {
+    using E = float;
+    static constexpr int kPad = 4;
+    struct Frag {
+        float v[8];
+    };
+    __device__ static Frag make(const float* x) {
+        Frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f.v[i] = x[i];
+        return f;
+    }
+    __device__ static Frag lds_pair(const E* p0, const E* p1) {
+        const float4 a = *reinterpret_cast<const float4*>(p0);
+        const float4 b = *reinterpret_cast<const float4*>(p1);
+        return Frag{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+    }
+    __device__ static Frag lds8(const E* p) { return lds_pair(p, p + 4); }
+    __device__ static void store8(E* p, const float* x) {
+        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    // 16x16x4 fp32 passes: pass i contracts slot i of every lane group.
+    __device__ static void mma(f4& c, const Frag& a, const Frag& b) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], c, 0, 0, 0);
+    }
+    __device__ static void mma_wide(f4& c, const float* a, const float* b) {
+        mma(c, make(a), make(b));
+    }
+};
+
+// ---- small helpers -------------------------------------------------------------------------
+
+// Value of lane (l16 - N) within each row of 16 lanes, 0 for the first N lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, true));
+}
+
+// Eight input elements of one row as loaded (packed bf16: one 16-byte vector; fp32: two).
+template <bool BF16>
+struct Raw8 {
+    uint4 u[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> gload8(const void* base, long idx) {
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        r.u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+        r.u[0] = p[0];
+        r.u[1] = p[1];
+    }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> fill8(float x) {
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        const uint32_t h = __float_as_uint(x) >> 16;  // exact for 0 and 1
+        const uint32_t p = h | (h << 16);
+        r.u[0] = make_uint4(p, p, p, p);
+    } else {
+        const uint32_t p = __float_as_uint(x);
+        r.u[0] = r.u[1] = make_uint4(p, p, p, p);
+    }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* x) {
+    if constexpr (BF16) {
+        const uint32_t w[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            x[4 * h + 0] = __uint_as_float(r.u[h].x);
+            x[4 * h + 1] = __uint_as_float(r.u[h].y);
+            x[4 * h + 2] = __uint_as_float(r.u[h].z);
+            x[4 * h + 3] = __uint_as_float(r.u[h].w);
+        }
+    }
+}
+
+__device__ __forceinline__ void lds_read8f(const float* p, float* x) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Per-(block, channel) decay tables, index t of tab[t][DK] (log2 domain, X = local value at a
+// block's 8th row, G_I = sum of earlier block totals, gC = chunk total):
+//   0..3 exp2(X_I)   4..7 exp2(G_I)   8..11 exp2(tot_I - X_I)   12..15 exp2(gC - G_{I+1})
+//   16 exp2(gC)      17 exp2(tot_1)   18 exp2(tot_1 + tot_2)    19 exp2(tot_2)
+constexpr int kTabs = 20;
+
+}  // namespace chunk
+}  // namespace gdn2

@@ -1,0 +1,734 @@
+// chunk_split.hip -- chunkwise (C = 64) Gated DeltaNet-2 prefill as two kernels on gfx950.
+//
+// Same method and arithmetic as chunk.hip [page "NVIDIA представила Gated DeltaNet-2 с
+// канал-wise гейтами …", paragraph "Реализация": chunkwise WY form, C = 64, cumulative
+// channel-wise decay absorbed into the rank-1 factors], split where the dependence on the
+// state begins:
+//
+//   prep   one workgroup per (b, h, chunk), all independent. Gate prep, Gram blocks and the UT
+//          inverse, as in chunk.hip phases A-E; it writes the chunk's state-free operands to a
+//          workspace blob: Q_hat, -E_hat (token-major), K_bar^T, P, T (fp16 for bf16 inputs)
+//          and gamma_last (fp32).
+//   chain  one workgroup per (b, h, 64 value columns), walking the chunks in order. The blob of
+//          chunk n+1 and its v, w rows are copied straight into LDS (global_load_lds, no
+//          registers) while chunk n is processed, so the chain waves hold little more than the
+//          fp32 state and their MFMA operands:
+//              D' = U - E_hat S,  Delta = T D',  O^T = S^T Q_hat^T + Delta^T P^T,
+//              S <- Diag(gamma_last) S + K_bar^T Delta.
+//
+// The blob's byte layout equals the chain kernel's LDS layout (with its row padding), so the
+// copy is a flat 16-byte-per-lane stream. The host walks the sequence in ranges of chunks
+// through a workspace ring (prep of a range, then chain of the range, the state carried in
+// S_out), so the ring can be sized to stay in the Infinity Cache.
+#include "chunk_common.h"
+#include "kernels.h"
+
+namespace gdn2 {
+
+namespace {
+
+using namespace chunk;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// Per-chunk operand blob (also the chain kernel's LDS buffer layout).
+template <int DK, bool F16>
+struct Blob {
+    using E = typename Prec<F16>::E;
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int PAD = Prec<F16>::kPad;
+    static constexpr int DKP = DK + PAD;
+    static constexpr int CHP = CH + PAD;
+    static constexpr int oQh = 0;                       // E [64][DKP]
+    static constexpr int oEn = oQh + CH * DKP * ES;     // E [64][DKP]
+    static constexpr int oKbT = oEn + CH * DKP * ES;    // E [DK][CHP]
+    static constexpr int oP = oKbT + DK * CHP * ES;     // E [64][CHP]
+    static constexpr int oTm = oP + CH * CHP * ES;      // E [64][CHP]
+    static constexpr int oGC = oTm + CH * CHP * ES;     // float [DK]
+    static constexpr int bytes = (oGC + DK * 4 + 255) / 256 * 256;
+};
+
+// Copy `bytes` (a multiple of 16) from global to LDS, 1 KiB per wavefront instruction: lane i
+// of the wave moves 16 bytes to LDS base + 16 i. Counted by vmcnt; the caller waits.
+__device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int wave, int lane) {
+    for (int off = wave * 1024; off < bytes; off += 4 * 1024) {
+        if (off + lane * 16 < bytes)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(g + off + lane * 16), (lds_ptr_t)(l + off), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// ------------------------------------------------------------------------------------------
+// prep: one (b, h, chunk)
+template <int DK, bool F16>
+struct PrepSmem {
+    using E = typename Prec<F16>::E;
+    using BL = Blob<DK, F16>;
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int DKP = BL::DKP, CHP = BL::CHP;
+    static constexpr int oTot = 0;                      // float [4][DK]
+    static constexpr int oX = oTot + 4 * DK * 4;        // float [4][DK]
+    static constexpr int oTab = oX + 4 * DK * 4;        // float [kTabs][DK]
+    static constexpr int oOut = oTab + kTabs * DK * 4;  // K_bar^T, P, T exactly as in the blob
+    static constexpr int oKbT = oOut;
+    static constexpr int oP = oKbT + DK * CHP * ES;
+    static constexpr int oTm = oP + CH * CHP * ES;
+    static constexpr int outBytes = (BL::oGC - BL::oKbT);
+    static constexpr int oKt = oOut + outBytes;         // E [48][DKP]
+    static constexpr int oA = oKt + 48 * DKP * ES;      // E [64][CHP] A below the diagonal
+    static constexpr int oAd = oA + CH * CHP * ES;      // float [4][16][16] diagonal A^T
+    static constexpr int bytes = oAd + 4 * 256 * 4;
+    static_assert(BL::oP - BL::oKbT == DK * CHP * ES && BL::oTm - BL::oP == CH * CHP * ES, "layout");
+    static_assert(bytes <= 80 * 1024, "prep LDS must allow two workgroups per CU");
+};
+
+template <int DK, bool BF16, bool AS, bool BS>
+__global__ void __launch_bounds__(256, 2)
+prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
+            const void* __restrict__ alpha, const void* __restrict__ b, int B, int T, int H,
+            int n_first, int n_count, char* __restrict__ ws) {
+    constexpr bool F16 = BF16;
+    using PR = Prec<F16>;
+    using E = typename PR::E;
+    using Frag = typename PR::Frag;
+    using BL = Blob<DK, F16>;
+    using SM = PrepSmem<DK, F16>;
+    constexpr int NKS = DK / 32, CPL = DK / 4;
+    constexpr int DKP = BL::DKP, CHP = BL::CHP;
+
+    __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
+    float* ldsTot = reinterpret_cast<float*>(smem + SM::oTot);
+    float* ldsX = reinterpret_cast<float*>(smem + SM::oX);
+    float* tab = reinterpret_cast<float*>(smem + SM::oTab);
+    E* KbT = reinterpret_cast<E*>(smem + SM::oKbT);
+    E* Pm = reinterpret_cast<E*>(smem + SM::oP);
+    E* Tm = reinterpret_cast<E*>(smem + SM::oTm);
+    E* Kt = reinterpret_cast<E*>(smem + SM::oKt);
+    E* A16 = reinterpret_cast<E*>(smem + SM::oA);
+    float* AdT = reinterpret_cast<float*>(smem + SM::oAd);
+
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int BH = B * H;
+    const int bh = blockIdx.x % BH, nc = blockIdx.x / BH;
+    const int hh = bh % H, bb = bh / H;
+    const int n = n_first + nc;
+    const int t0 = n * CH;
+    char* blob = ws + ((size_t)bh * n_count + nc) * BL::bytes;
+    const int I = wv, r = 16 * I + l16;
+
+    for (int idx = threadIdx.x; idx < CH * CH; idx += blockDim.x) {
+        const int rr = idx / CH, cc = idx % CH;
+        if ((cc >> 4) > (rr >> 4)) {
+            Pm[rr * CHP + cc] = (E)0.f;
+            Tm[rr * CHP + cc] = (E)0.f;
+        }
+    }
+
+    // ---- A: inputs of this lane's row, log2-decay and its in-block scan ----
+    const int t = t0 + r;
+    const bool valid = t < T;
+    const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
+    Raw8<BF16> rq[NKS], rk[NKS], rb[NKS];
+    float lg[CPL];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        const int c0 = 32 * s + 8 * g;
+        rq[s] = valid ? gload8<BF16>(q, tok * DK + c0) : fill8<BF16>(0.f);
+        rk[s] = valid ? gload8<BF16>(k, tok * DK + c0) : fill8<BF16>(0.f);
+        if constexpr (!BS) rb[s] = valid ? gload8<BF16>(b, tok * DK + c0) : fill8<BF16>(0.f);
+        if constexpr (!AS)
+            unpack8<BF16>(valid ? gload8<BF16>(alpha, tok * DK + c0) : fill8<BF16>(1.f), &lg[8 * s]);
+    }
+    const float rbs = BS ? (valid ? load_one<BF16>(b, tok) : 0.f) : 0.f;
+    if constexpr (AS) {
+        float x1 = lg2(valid ? load_one<BF16>(alpha, tok) : 1.f);
+        x1 += row_shr<1>(x1);
+        x1 += row_shr<2>(x1);
+        x1 += row_shr<4>(x1);
+        x1 += row_shr<8>(x1);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) lg[e] = x1;
+    } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) lg[e] = lg2(lg[e]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) lg[e] += row_shr<1>(lg[e]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) lg[e] += row_shr<2>(lg[e]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) lg[e] += row_shr<4>(lg[e]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) lg[e] += row_shr<8>(lg[e]);
+    }
+    if (l16 == 15 || l16 == 7) {
+        float* dst = (l16 == 15 ? ldsTot : ldsX) + I * DK;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            float4* p = reinterpret_cast<float4*>(dst + 32 * s + 8 * g);
+            p[0] = make_float4(lg[8 * s], lg[8 * s + 1], lg[8 * s + 2], lg[8 * s + 3]);
+            p[1] = make_float4(lg[8 * s + 4], lg[8 * s + 5], lg[8 * s + 6], lg[8 * s + 7]);
+        }
+    }
+    lds_barrier();
+
+    // ---- decay tables (see chunk_common.h) ----
+    {
+        constexpr int TPC = 256 / DK;
+        const int c = threadIdx.x % DK, part = threadIdx.x / DK;
+        float tot[4], X[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            tot[J] = ldsTot[J * DK + c];
+            X[J] = ldsX[J * DK + c];
+        }
+        const float G[5] = {0.f, tot[0], tot[0] + tot[1], tot[0] + tot[1] + tot[2],
+                            tot[0] + tot[1] + tot[2] + tot[3]};
+        float e[kTabs];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            e[J] = X[J];
+            e[4 + J] = G[J];
+            e[8 + J] = tot[J] - X[J];
+            e[12 + J] = G[4] - G[J + 1];
+        }
+        e[16] = G[4];
+        e[17] = tot[1];
+        e[18] = tot[1] + tot[2];
+        e[19] = tot[2];
+#pragma unroll
+        for (int tt = 0; tt < kTabs; ++tt)
+            if (tt % TPC == part) tab[tt * DK + c] = ex2(e[tt]);
+    }
+    lds_barrier();
+
+    // ---- B: factors; Q_hat and -E_hat straight to the blob; diagonal Gram blocks ----
+    float er[CPL], qr[CPL];
+    {
+        f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        E* bQh = reinterpret_cast<E*>(blob + BL::oQh);
+        E* bEn = reinterpret_cast<E*>(blob + BL::oEn);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int c0 = 32 * s + 8 * g;
+            float qx[8], kx[8], bx[8], X8[8], fX[8], fG[8], fTX[8], fCG[8];
+            unpack8<BF16>(rq[s], qx);
+            unpack8<BF16>(rk[s], kx);
+            if constexpr (BS) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bx[i] = rbs;
+            } else {
+                unpack8<BF16>(rb[s], bx);
+            }
+            lds_read8f(ldsX + I * DK + c0, X8);
+            lds_read8f(tab + (0 + I) * DK + c0, fX);
+            lds_read8f(tab + (4 + I) * DK + c0, fG);
+            lds_read8f(tab + (8 + I) * DK + c0, fTX);
+            lds_read8f(tab + (12 + I) * DK + c0, fCG);
+            float em[8], qm[8], km[8], qh[8], en[8], kt[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float d = lg[8 * s + i] - X8[i];
+                const float fm = ex2(d), fmi = ex2(-d);
+                const float bk = bx[i] * kx[i];
+                em[i] = bk * fm;
+                qm[i] = qx[i] * fm;
+                km[i] = kx[i] * fmi;
+                const float fl = fm * fX[i];
+                er[8 * s + i] = bk * fl;
+                qr[8 * s + i] = qx[i] * fl;
+                const float gam = fl * fG[i];
+                qh[i] = qx[i] * gam;
+                en[i] = -(bk * gam);
+                kt[i] = km[i] * fTX[i];
+                KbT[(c0 + i) * CHP + r] = (E)(kt[i] * fCG[i]);
+            }
+            {
+                const Frag kmf = PR::make(km);
+                PR::mma(accA, PR::make(em), kmf);
+                PR::mma(accP, PR::make(qm), kmf);
+            }
+            PR::store8(&bQh[r * DKP + c0], qh);
+            PR::store8(&bEn[r * DKP + c0], en);
+            if (I < 3) PR::store8(&Kt[r * DKP + c0], kt);
+        }
+        bool finite = true;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) finite = finite && __builtin_isfinite(accA[j]) && __builtin_isfinite(accP[j]);
+        if (F16 && !__all(finite)) {
+            // Strong decay inside the block: redo the diagonal block with bf16 hi/lo operands.
+            accA = f4{0.f, 0.f, 0.f, 0.f};
+            accP = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const int c0 = 32 * s + 8 * g;
+                float qx[8], kx[8], bx[8], X8[8], em[8], qm[8], km[8];
+                unpack8<BF16>(rq[s], qx);
+                unpack8<BF16>(rk[s], kx);
+                if constexpr (BS) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) bx[i] = rbs;
+                } else {
+                    unpack8<BF16>(rb[s], bx);
+                }
+                lds_read8f(ldsX + I * DK + c0, X8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float d = lg[8 * s + i] - X8[i];
+                    const float fm = ex2(d);
+                    em[i] = bx[i] * kx[i] * fm;
+                    qm[i] = qx[i] * fm;
+                    km[i] = kx[i] * ex2(-d);
+                }
+                PR::mma_wide(accA, em, km);
+                PR::mma_wide(accP, qm, km);
+            }
+        }
+        float4 at;
+        at.x = (4 * g + 0) > l16 ? accA[0] : 0.f;
+        at.y = (4 * g + 1) > l16 ? accA[1] : 0.f;
+        at.z = (4 * g + 2) > l16 ? accA[2] : 0.f;
+        at.w = (4 * g + 3) > l16 ? accA[3] : 0.f;
+        *reinterpret_cast<float4*>(AdT + I * 256 + l16 * 16 + 4 * g) = at;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 4 * g + j;
+            Pm[(16 * I + rr) * CHP + 16 * I + l16] = (E)(rr >= l16 ? accP[j] : 0.f);
+        }
+    }
+    lds_barrier();
+
+    // ---- C: Gram blocks below the diagonal; T_II ----
+    for (int J = 0; J < I; ++J) {
+        f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        // non-adjacent blocks: row factors times exp2(G_I - G_{J+1}) (tables 17..19)
+        const float* cij = (J == I - 1) ? nullptr : tab + (I == 2 ? 17 : (J == 0 ? 18 : 19)) * DK;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int c0 = 32 * s + 8 * g;
+            float ea[8], qa[8];
+            if (cij) {
+                float c8[8];
+                lds_read8f(cij + c0, c8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ea[i] = er[8 * s + i] * c8[i];
+                    qa[i] = qr[8 * s + i] * c8[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ea[i] = er[8 * s + i];
+                    qa[i] = qr[8 * s + i];
+                }
+            }
+            const Frag kf = PR::lds8(Kt + (16 * J + l16) * DKP + c0);
+            PR::mma(accA, PR::make(ea), kf);
+            PR::mma(accP, PR::make(qa), kf);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 16 * I + 4 * g + j;
+            A16[rr * CHP + 16 * J + l16] = (E)accA[j];
+            Pm[rr * CHP + 16 * J + l16] = (E)accP[j];
+        }
+    }
+    if (g == 0) {
+        float acc[16], tc[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+        const float4* Ab4 = reinterpret_cast<const float4*>(AdT + I * 256);
+        float4 cur[4], nxt[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) cur[q4] = Ab4[q4];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            if (m + 1 < 16) {
+#pragma unroll
+                for (int q4 = (m + 2) / 4; q4 < 4; ++q4) nxt[q4] = Ab4[(m + 1) * 4 + q4];
+            }
+            const float tm = m < l16 ? 0.f : (m == l16 ? 1.f : -acc[m]);
+            tc[m] = tm;
+#pragma unroll
+            for (int q4 = (m + 1) / 4; q4 < 4; ++q4) {
+                const float av[4] = {cur[q4].x, cur[q4].y, cur[q4].z, cur[q4].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * q4 + i > m) acc[4 * q4 + i] = fmaf(av[i], tm, acc[4 * q4 + i]);
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) Tm[(16 * I + m) * CHP + 16 * I + l16] = (E)tc[m];
+    }
+    lds_barrier();
+
+    // ---- D: T10 = -T11 A10 T00 and T32 = -T33 A32 T22 ----
+    if (wv == 1 || wv == 3) {
+        const int Ib = wv, Jb = wv - 1;
+        float af[8], bf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[i] = (float)A16[(16 * Ib + l16) * CHP + 16 * Jb + 4 * g + i];
+            bf[i] = (float)Tm[(16 * Jb + 4 * g + i) * CHP + 16 * Jb + l16];
+            af[i + 4] = bf[i + 4] = 0.f;
+        }
+        f4 X = {0.f, 0.f, 0.f, 0.f};
+        PR::mma(X, PR::make(af), PR::make(bf));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[i] = (float)Tm[(16 * Ib + l16) * CHP + 16 * Ib + 4 * g + i];
+            bf[i] = X[i];
+        }
+        f4 Y = {0.f, 0.f, 0.f, 0.f};
+        PR::mma(Y, PR::make(af), PR::make(bf));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Tm[(16 * Ib + 4 * g + j) * CHP + 16 * Jb + l16] = (E)(-Y[j]);
+    }
+    lds_barrier();
+
+    // ---- E: T[32:, :32] = -T[32:, 32:] A[32:, :32] T[:32, :32] ----
+    if (wv < 2) {
+        const int Jb = wv;
+        f4 Yt[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int Ib = 2 + u;
+            const E* ar = &A16[(16 * Ib + l16) * CHP];
+            float bf[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bf[i] = (float)Tm[kap(g, i) * CHP + 16 * Jb + l16];
+            Yt[u] = f4{0.f, 0.f, 0.f, 0.f};
+            PR::mma(Yt[u], PR::lds_pair(ar + 4 * g, ar + 16 + 4 * g), PR::make(bf));
+        }
+        float yb[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            yb[i] = Yt[0][i];
+            yb[i + 4] = Yt[1][i];
+        }
+        const Frag yf = PR::make(yb);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int Ib = 2 + u;
+            const E* row = &Tm[(16 * Ib + l16) * CHP + 32];
+            f4 Z = {0.f, 0.f, 0.f, 0.f};
+            PR::mma(Z, PR::lds_pair(row + 4 * g, row + 16 + 4 * g), yf);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Tm[(16 * Ib + 4 * g + j) * CHP + 16 * Jb + l16] = (E)(-Z[j]);
+        }
+    }
+    lds_barrier();
+
+    // ---- out: K_bar^T, P, T (contiguous in LDS and in the blob) and gamma_last ----
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(smem + SM::oOut);
+        uint4* dst = reinterpret_cast<uint4*>(blob + BL::oKbT);
+        for (int i = threadIdx.x; i < SM::outBytes / 16; i += blockDim.x) dst[i] = src[i];
+        float* gc = reinterpret_cast<float*>(blob + BL::oGC);
+        for (int c = threadIdx.x; c < DK; c += blockDim.x) gc[c] = tab[16 * DK + c];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// chain: one (b, h, value tile), chunks n_first .. n_first + n_count - 1
+template <int DK, int DVT, bool F16>
+struct ChainSmem {
+    using BL = Blob<DK, F16>;
+    static constexpr int VWB = CH * DVT * (F16 ? 2 : 4);  // one of v, w for the tile
+    static constexpr int oBuf0 = 0;
+    static constexpr int oBuf1 = BL::bytes;
+    static constexpr int oV = 2 * BL::bytes;
+    static constexpr int oW = oV + VWB;
+    static constexpr int bytes = oW + VWB;
+    static constexpr bool fits = bytes <= 160 * 1024;
+};
+
+template <int DK, int DVT, bool BF16, bool BS>
+__global__ void __launch_bounds__(256, 1)
+chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
+             const void* __restrict__ beta, const float* S_in, float* __restrict__ o,
+             float* S_out, int B, int T, int H, int DV, int n_first, int n_count,
+             const char* __restrict__ ws) {
+    constexpr bool F16 = BF16;
+    using PR = Prec<F16>;
+    using E = typename PR::E;
+    using Frag = typename PR::Frag;
+    using BL = Blob<DK, F16>;
+    using SM = ChainSmem<DK, DVT, F16>;
+    static_assert(SM::fits, "chain LDS budget exceeded");
+    constexpr int NKS = DK / 32, NMK = DK / 16, NWC = DVT / 16;
+    constexpr int DKP = BL::DKP, CHP = BL::CHP;
+    constexpr int IES = BF16 ? 2 : 4;          // input element size
+    constexpr int ROWB = DVT * IES;            // bytes of one v (or w) row of the tile
+    constexpr int LPR = ROWB / 16;             // lanes per row in the v/w copy
+
+    __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
+
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int tiles = DV / DVT;
+    const int x = blockIdx.x;
+    const int grp = x / (8 * tiles), within = x % (8 * tiles);
+    const int tile = within / 8;
+    const int bh = grp * 8 + (within % 8);
+    if (bh >= B * H) return;
+    const int hh = bh % H, bb = bh / H;
+    const bool chain = wv < NWC;
+    const int mycol = tile * DVT + wv * 16 + l16;
+    const char* blobs = ws + (size_t)bh * n_count * BL::bytes;
+
+    // v (and w) rows of chunk n, this tile's columns, into LDS; rows past T are skipped
+    auto dma_vw = [&](int n) {
+        const int t0 = n * CH;
+        for (int base = wv * 64; base < CH * LPR; base += 256) {
+            const int idx = base + lane;
+            const int row = idx / LPR, seg = idx % LPR;
+            if (t0 + row < T) {
+                const long tok = ((long)bb * T + t0 + row) * H + hh;
+                const char* gv = static_cast<const char*>(v) + (tok * DV + tile * DVT) * IES + seg * 16;
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)gv, (lds_ptr_t)(smem + SM::oV + base * 16), 16, 0, 0);
+                if constexpr (!BS) {
+                    const char* gw = static_cast<const char*>(w) + (tok * DV + tile * DVT) * IES + seg * 16;
+                    __builtin_amdgcn_global_load_lds((gbl_ptr_t)gw, (lds_ptr_t)(smem + SM::oW + base * 16), 16, 0, 0);
+                }
+            }
+        }
+    };
+
+    f4 Sacc[NMK];
+    const long sbase = (long)bh * DK * DV;
+#pragma unroll
+    for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            Sacc[mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
+
+    dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv, lane);
+    dma_vw(n_first);
+
+    for (int nc = 0; nc < n_count; ++nc) {
+        const int n = n_first + nc;
+        const int t0 = n * CH;
+        const int L = min(CH, T - t0);
+        char* buf = smem + ((nc & 1) ? SM::oBuf1 : SM::oBuf0);
+        const E* Qh = reinterpret_cast<const E*>(buf + BL::oQh);
+        const E* En = reinterpret_cast<const E*>(buf + BL::oEn);
+        const E* KbT = reinterpret_cast<const E*>(buf + BL::oKbT);
+        const E* Pm = reinterpret_cast<const E*>(buf + BL::oP);
+        const E* Tm = reinterpret_cast<const E*>(buf + BL::oTm);
+        const float* gC = reinterpret_cast<const float*>(buf + BL::oGC);
+
+        wait_dma();
+        lds_barrier();  // chunk nc's blob and v, w are in LDS; buffer nc+1 is free
+        if (nc + 1 < n_count)
+            dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
+                     BL::bytes, wv, lane);
+
+        // D' starts as U = w v (rows past the sequence end are zero)
+        f4 D[4];
+        if (chain) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 16 * mt + 4 * g + j;
+                    const int cl = wv * 16 + l16;
+                    float vv, ww;
+                    if constexpr (BF16) {
+                        vv = bf16_to_f32(reinterpret_cast<const uint16_t*>(smem + SM::oV)[row * DVT + cl]);
+                    } else {
+                        vv = reinterpret_cast<const float*>(smem + SM::oV)[row * DVT + cl];
+                    }
+                    if constexpr (BS) {
+                        const long tok = ((long)bb * T + t0 + (row < L ? row : 0)) * H + hh;
+                        ww = load_one<BF16>(beta, tok);
+                    } else if constexpr (BF16) {
+                        ww = bf16_to_f32(reinterpret_cast<const uint16_t*>(smem + SM::oW)[row * DVT + cl]);
+                    } else {
+                        ww = reinterpret_cast<const float*>(smem + SM::oW)[row * DVT + cl];
+                    }
+                    D[mt][j] = row < L ? ww * vv : 0.f;
+                }
+            }
+        }
+        lds_barrier();  // every wave has read v, w of chunk nc
+        if (nc + 1 < n_count) dma_vw(n + 1);
+
+        if (chain) {
+            Frag Sf[NKS];
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                float sv[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sv[i] = Sacc[2 * s][i];
+                    sv[i + 4] = Sacc[2 * s + 1][i];
+                }
+                Sf[s] = PR::make(sv);
+            }
+            // D' = U - E_hat S ; O^T = S^T Q_hat^T
+            f4 O[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                O[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    const E* er_ = &En[(16 * mt + l16) * DKP + 32 * s];
+                    const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
+                    PR::mma(D[mt], PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g), Sf[s]);
+                    PR::mma(O[mt], Sf[s], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g));
+                }
+            }
+            // Delta = T D'
+            Frag Df[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                float dv_[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dv_[i] = D[2 * s2][i];
+                    dv_[i + 4] = D[2 * s2 + 1][i];
+                }
+                Df[s2] = PR::make(dv_);
+            }
+            f4 Dl[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                Dl[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 <= mt / 2; ++s2) {
+                    const E* tr = &Tm[(16 * mt + l16) * CHP + 32 * s2];
+                    PR::mma(Dl[mt], PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g), Df[s2]);
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                float dv_[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dv_[i] = Dl[2 * s2][i];
+                    dv_[i + 4] = Dl[2 * s2 + 1][i];
+                }
+                Df[s2] = PR::make(dv_);
+            }
+            // O^T += Delta^T P^T, store four columns per lane
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+                for (int s2 = 0; s2 <= nt / 2; ++s2) {
+                    const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
+                    PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
+                }
+                const int row = 16 * nt + l16;
+                if (row < L) {
+                    float* op = o + (((long)bb * T + t0 + row) * H + hh) * DV + tile * DVT + 16 * wv + 4 * g;
+                    *reinterpret_cast<float4*>(op) = make_float4(O[nt][0], O[nt][1], O[nt][2], O[nt][3]);
+                }
+            }
+            // S <- Diag(gamma_last) S + K_bar^T Delta
+#pragma unroll
+            for (int mk = 0; mk < NMK; ++mk) {
+                const float4 gc = *reinterpret_cast<const float4*>(gC + 16 * mk + 4 * g);
+                Sacc[mk][0] *= gc.x;
+                Sacc[mk][1] *= gc.y;
+                Sacc[mk][2] *= gc.z;
+                Sacc[mk][3] *= gc.w;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const E* kr = &KbT[(16 * mk + l16) * CHP + 32 * s2];
+                    PR::mma(Sacc[mk], PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g), Df[s2]);
+                }
+            }
+        }
+    }
+
+    if (chain && S_out) {
+#pragma unroll
+        for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                S_out[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] = Sacc[mk][j];
+    }
+}
+
+template <int DK, bool BF16>
+constexpr bool split_fits() {
+    constexpr int DVT = DK < 64 ? DK : 64;
+    return ChainSmem<DK, DVT, BF16>::fits;
+}
+
+template <int DK, bool BF16, bool AS, bool BS>
+hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
+    constexpr int DVT = DK < 64 ? DK : 64;
+    using BL = Blob<DK, BF16>;
+    const int BH = a.B * a.H;
+    const int nch = (a.T + CH - 1) / CH;
+    const size_t state_bytes = (size_t)BH * a.DK * a.DV * 4;
+    float* Sbuf = a.S_out;
+    char* ws = static_cast<char*>(a.workspace);
+    if (!Sbuf) {
+        Sbuf = reinterpret_cast<float*>(ws);
+        ws += state_bytes;
+    }
+    const size_t ring = a.workspace_bytes - (a.S_out ? 0 : state_bytes);
+    const size_t per_chunk = (size_t)BH * BL::bytes;
+    int R = (int)(ring / per_chunk);
+    if (R < 1) return hipErrorInvalidValue;
+    if (R > nch) R = nch;
+    const int tiles = a.DV / DVT;
+    const int chain_blocks = (BH + 7) / 8 * 8 * tiles;
+    for (int n0 = 0; n0 < nch; n0 += R) {
+        const int cnt = nch - n0 < R ? nch - n0 : R;
+        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
+                           a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(256), 0, st, a.v,
+                           a.w, a.b, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int DK, bool BF16>
+hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
+    switch (a.flags & 3u) {
+        case 0: return launch_split_t<DK, BF16, false, false>(a, s);
+        case 1: return launch_split_t<DK, BF16, true, false>(a, s);
+        case 2: return launch_split_t<DK, BF16, false, true>(a, s);
+        default: return launch_split_t<DK, BF16, true, true>(a, s);
+    }
+}
+
+}  // namespace
+
+bool split_supported(int DK, int DV, bool bf16) {
+    if (DK != DV) return false;
+    if (bf16) return DK == 32 || DK == 64 || DK == 128;
+    return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
+}
+
+size_t split_chunk_bytes(int B, int H, int DK, bool bf16) {
+    size_t blob = 0;
+    if (bf16) {
+        blob = DK == 32 ? Blob<32, true>::bytes : DK == 64 ? Blob<64, true>::bytes : Blob<128, true>::bytes;
+    } else {
+        blob = Blob<32, false>::bytes;
+    }
+    return (size_t)B * H * blob;
+}
+
+hipError_t launch_split(const ChunkArgs& a, hipStream_t s) {
+    if (!split_supported(a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
+    if (a.bf16) {
+        switch (a.DK) {
+            case 32: return launch_split_flags<32, true>(a, s);
+            case 64: return launch_split_flags<64, true>(a, s);
+            default: return launch_split_flags<128, true>(a, s);
+        }
+    }
+    return launch_split_flags<32, false>(a, s);
+}
+
+}  // namespace gdn2

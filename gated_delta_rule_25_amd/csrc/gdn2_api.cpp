@@ -14,6 +14,14 @@ namespace {
 
 bool dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
 
+// Recommended size of the two-kernel path's ring of per-chunk operand blobs.
+constexpr size_t kRingBytes = (size_t)1 << 40;
+
+// Smallest workspace the two-kernel path accepts: the state buffer and one chunk slot.
+size_t split_min_bytes(int32_t B, int32_t H, int32_t dk, int32_t dv, bool bf16) {
+    return (size_t)B * H * dk * dv * 4 + gdn2::split_chunk_bytes(B, H, dk, bf16);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Range {
@@ -125,8 +133,15 @@ gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v, cons
 
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags) {
-    if (B <= 0 || H <= 0 || T < 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
-    return gdn2::chunk_workspace_bytes(B, T, H, d_k, d_v, in_dtype == GDN2_BF16, gate_flags);
+    if (B <= 0 || H <= 0 || T <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    const bool bf16 = in_dtype == GDN2_BF16;
+    if (!gdn2::split_supported(d_k, d_v, bf16)) return 0;
+    const size_t nch = ((size_t)T + 63) / 64;
+    const size_t per_chunk = gdn2::split_chunk_bytes(B, H, d_k, bf16);
+    size_t ring = kRingBytes / per_chunk;  // chunk slots in the recommended ring
+    if (ring < 1) ring = 1;
+    if (ring > nch) ring = nch;
+    return split_min_bytes(B, H, d_k, d_v, bf16) - per_chunk + ring * per_chunk;
 }
 
 gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
@@ -138,10 +153,23 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                               gate_flags, false);
     if (st != GDN2_OK) return st;
     const bool bf16 = in_dtype == GDN2_BF16;
-    if (!gdn2::chunk_supported(d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
-    const size_t need = gdn2::chunk_workspace_bytes(B, T, H, d_k, d_v, bf16, gate_flags);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
-    if (workspace && !aligned16(workspace)) return GDN2_ERR_ALIGN;
+    const bool split = workspace && workspace_bytes > 0 && gdn2::split_supported(d_k, d_v, bf16);
+    if (split) {
+        const size_t min_bytes = split_min_bytes(B, H, d_k, d_v, bf16);
+        if (workspace_bytes < min_bytes) return GDN2_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+        const Range rws = range_of(workspace, workspace_bytes);
+        const uint64_t es = bf16 ? 2 : 4;
+        Sizes sz;
+        sizes_of(B, T, H, d_k, d_v, &sz);
+        const Range others[] = {range_of(q, sz.qk * es), range_of(k, sz.qk * es), range_of(v, sz.vw * es),
+                                range_of(alpha, sz.qk * es), range_of(b, sz.qk * es), range_of(w, sz.vw * es),
+                                range_of(S0, sz.state * 4), range_of(o, sz.vw * 4), range_of(S_out, sz.state * 4)};
+        for (const Range& r : others)
+            if (overlap(rws, r)) return GDN2_ERR_ALIAS;
+    } else if (!gdn2::chunk_supported(d_k, d_v, bf16)) {
+        return GDN2_ERR_UNSUPPORTED;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) {  // nothing to chunk: S_out <- S0 (or zeros)
         return run_recurrent(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
@@ -149,7 +177,7 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
     }
     gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, bf16, gate_flags,
                       workspace, workspace_bytes};
-    const hipError_t e = gdn2::launch_chunk(a, s);
+    const hipError_t e = split ? gdn2::launch_split(a, s) : gdn2::launch_chunk(a, s);
     if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }

@@ -31,9 +31,15 @@ struct ChunkArgs {
     void* workspace;
     size_t workspace_bytes;
 };
-// Returns hipErrorNotSupported when no chunk kernel covers the arguments.
+// Single-kernel path (no workspace). Returns hipErrorNotSupported when it does not cover
+// the arguments.
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
-size_t chunk_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16, uint32_t flags);
 bool chunk_supported(int DK, int DV, bool bf16);
+
+// Two-kernel path (prep + chain) through a workspace ring of per-chunk operand blobs.
+// Workspace = state buffer (B*H*DK*DV fp32) + R chunk slots of split_chunk_bytes each.
+hipError_t launch_split(const ChunkArgs& a, hipStream_t s);
+bool split_supported(int DK, int DV, bool bf16);
+size_t split_chunk_bytes(int B, int H, int DK, bool bf16);
 
 }  // namespace gdn2

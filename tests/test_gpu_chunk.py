@@ -43,11 +43,11 @@ def _run(ins, **kw):
     return out
 
 
-def _check(name, ins, tol):
+def _check(name, ins, tol, fused=False):
     o_ref, S_ref = _oracle(ins)
-    o, S_T = _run(ins)
+    o, S_T = _run(ins, fused=fused)
     eo, es = normwise_err(o, o_ref), normwise_err(S_T, S_ref)
-    print(f"  {name}: o err {eo:.2e}  S_T err {es:.2e}", flush=True)
+    print(f"  {name} ({'fused' if fused else 'split'}): o err {eo:.2e}  S_T err {es:.2e}", flush=True)
     assert eo <= tol and es <= tol, (eo, es)
 
 
@@ -63,10 +63,11 @@ FP32_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
 @pytest.mark.parametrize("name,wl", FP32_CASES, ids=[c[0] for c in FP32_CASES])
-def test_chunk_fp32_matches_oracle(name, wl):
-    banner(f"chunk fp32 {name} {wl}")
-    _check(name, make_inputs(wl), TOL32)
+def test_chunk_fp32_matches_oracle(name, wl, fused):
+    banner(f"chunk fp32 {name} fused={fused} {wl}")
+    _check(name, make_inputs(wl), TOL32, fused)
 
 
 BF16_CASES = [
@@ -86,10 +87,11 @@ BF16_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
 @pytest.mark.parametrize("name,wl", BF16_CASES, ids=[c[0] for c in BF16_CASES])
-def test_chunk_bf16_matches_oracle(name, wl):
-    banner(f"chunk bf16 {name} {wl}")
-    _check(name, make_inputs(wl), TOL16)
+def test_chunk_bf16_matches_oracle(name, wl, fused):
+    banner(f"chunk bf16 {name} fused={fused} {wl}")
+    _check(name, make_inputs(wl), TOL16, fused)
 
 
 def test_chunk_zero_tokens_copies_state():
@@ -174,8 +176,27 @@ FULL = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
 @pytest.mark.parametrize("name,wl", FULL, ids=[c[0] for c in FULL])
-def test_chunk_full_size_all_heads(name, wl):
+def test_chunk_full_size_all_heads(name, wl, fused):
     """The benchmark's launch configuration, B8 H16 T4096 d128, every head against the oracle."""
-    banner(f"chunk full {name}")
-    _check(name, make_inputs(wl), TOL16)
+    banner(f"chunk full {name} fused={fused}")
+    _check(name, make_inputs(wl), TOL16, fused)
+
+
+def test_chunk_split_small_ring():
+    """The two-kernel path with a ring of 3 chunk slots (several prep/chain rounds, the state
+    carried between rounds) equals the oracle."""
+    banner("chunk split, 3-slot ring")
+    import gated_delta_rule_25_amd as g
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=2, T=450, H=3)
+    ins = make_inputs(wl)
+    d = _cuda(ins)
+    B, T, H, dk = d["q"].shape
+    per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dk) - B * H * dk * dk * 4
+    ws = torch.empty(B * H * dk * dk * 4 + 3 * per_chunk, dtype=torch.uint8, device="cuda")
+    o, S_T = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"],
+                         workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(ins)
+    assert normwise_err(o, o_ref) <= TOL16 and normwise_err(S_T, S_ref) <= TOL16
