@@ -47,7 +47,7 @@ def decode_bytes_per_head(dk: int, dv: int) -> float:
     return 2 * 4 * dk * dv + 4 * dk * 2 + 2 * dv * 2 + 4 * dv
 
 
-def time_prefill(g, ins, steps, warmup, impl):
+def time_prefill(g, ins, steps, warmup, impl, ring_mb=None):
     import torch
     fn = g.recurrent_fwd if impl == "recurrent" else g.chunk_fwd
     args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")]
@@ -58,6 +58,11 @@ def time_prefill(g, ins, steps, warmup, impl):
     kw = dict(o=o, S_out=S_out)
     if impl == "chunk":
         need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
+        if need and ring_mb is not None:
+            state = B * H * dk * dv * 4
+            per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv) - state
+            slots = max(1, int(ring_mb * 2**20) // per_chunk)
+            need = min(need, state + slots * per_chunk)
         if need:
             kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
     elif impl == "fused":
@@ -152,6 +157,8 @@ def main(argv=None):
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte "
                          "counters)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--ring-mb", type=float, default=None,
+                    help="size the two-kernel path's workspace ring to about this many MiB")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the (b, h) "
@@ -174,7 +181,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
 
-    wall, kern_ms = time_prefill(g, ins, args.steps, args.warmup, args.impl)
+    wall, kern_ms = time_prefill(g, ins, args.steps, args.warmup, args.impl, args.ring_mb)
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = sum(kern_ms) / len(kern_ms)
     head_tokens = B * T * H

@@ -49,16 +49,31 @@ struct Blob {
     static constexpr int bytes = (oGC + DK * 4 + 255) / 256 * 256;
 };
 
-// Copy `bytes` (a multiple of 16) from global to LDS, 1 KiB per wavefront instruction: lane i
-// of the wave moves 16 bytes to LDS base + 16 i. Counted by vmcnt; the caller waits.
-__device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int wave, int lane) {
-    for (int off = wave * 1024; off < bytes; off += 4 * 1024) {
+// Copy `bytes` (a multiple of 16) from global to LDS with one wavefront, 1 KiB per
+// instruction: lane i moves 16 bytes to LDS base + 16 i. Counted by vmcnt; the caller waits.
+__device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int lane) {
+    for (int off = 0; off < bytes; off += 1024) {
         if (off + lane * 16 < bytes)
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(g + off + lane * 16), (lds_ptr_t)(l + off), 16, 0, 0);
     }
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Scheduling hint for a run of P products that each read one LDS operand fragment: issue the
+// first LA reads, then alternate one product and one read, so every matrix-core instruction
+// finds its operand already loaded.
+template <int P, int LA = 4>
+__device__ __forceinline__ void lookahead_schedule() {
+    constexpr int la = P < LA ? P : LA;
+    __builtin_amdgcn_sched_group_barrier(0x100, la, 0);
+#pragma unroll
+    for (int i = 0; i < P - la; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, la, 0);
+}
 
 // ------------------------------------------------------------------------------------------
 // prep: one (b, h, chunk)
@@ -446,8 +461,10 @@ struct ChainSmem {
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
+// 5 wavefronts: four state-chain waves (16 state columns each) and one copy wave that streams
+// the next chunk's operands into LDS.
 template <int DK, int DVT, bool BF16, bool BS>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(320, 1)
 chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
              const void* __restrict__ beta, const float* S_in, float* __restrict__ o,
              float* S_out, int B, int T, int H, int DV, int n_first, int n_count,
@@ -482,7 +499,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     // v (and w) rows of chunk n, this tile's columns, into LDS; rows past T are skipped
     auto dma_vw = [&](int n) {
         const int t0 = n * CH;
-        for (int base = wv * 64; base < CH * LPR; base += 256) {
+        for (int base = 0; base < CH * LPR; base += 64) {
             const int idx = base + lane;
             const int row = idx / LPR, seg = idx % LPR;
             if (t0 + row < T) {
@@ -505,8 +522,11 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
 
-    dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv, lane);
-    dma_vw(n_first);
+    if (wv == 4) {
+        dma_flat(blobs, smem + SM::oBuf0, BL::bytes, lane);
+        dma_vw(n_first);
+        wait_dma();
+    }
 
     for (int nc = 0; nc < n_count; ++nc) {
         const int n = n_first + nc;
@@ -520,11 +540,10 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         const E* Tm = reinterpret_cast<const E*>(buf + BL::oTm);
         const float* gC = reinterpret_cast<const float*>(buf + BL::oGC);
 
-        wait_dma();
         lds_barrier();  // chunk nc's blob and v, w are in LDS; buffer nc+1 is free
-        if (nc + 1 < n_count)
+        if (wv == 4 && nc + 1 < n_count)
             dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
-                     BL::bytes, wv, lane);
+                     BL::bytes, lane);
 
         // D' starts as U = w v (rows past the sequence end are zero)
         f4 D[4];
@@ -554,7 +573,6 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
             }
         }
         lds_barrier();  // every wave has read v, w of chunk nc
-        if (nc + 1 < n_count) dma_vw(n + 1);
 
         if (chain) {
             Frag Sf[NKS];
@@ -581,6 +599,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                     PR::mma(O[mt], Sf[s], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g));
                 }
             }
+            if constexpr (F16) lookahead_schedule<8 * NKS, 6>();
             // Delta = T D'
             Frag Df[2];
 #pragma unroll
@@ -603,6 +622,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                     PR::mma(Dl[mt], PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g), Df[s2]);
                 }
             }
+            if constexpr (F16) lookahead_schedule<6>();
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 float dv_[8];
@@ -641,6 +661,12 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                     PR::mma(Sacc[mk], PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g), Df[s2]);
                 }
             }
+            if constexpr (F16) lookahead_schedule<2 * NMK>();
+        } else if (wv == 4) {
+            // the copy wave: v, w of the next chunk, then wait for both copies before the next
+            // chunk's first barrier
+            if (nc + 1 < n_count) dma_vw(n + 1);
+            wait_dma();
         }
     }
 
@@ -683,7 +709,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         const int cnt = nch - n0 < R ? nch - n0 : R;
         hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
                            a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(256), 0, st, a.v,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(320), 0, st, a.v,
                            a.w, a.b, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
