@@ -49,10 +49,11 @@ struct Blob {
     static constexpr int bytes = (oGC + DK * 4 + 255) / 256 * 256;
 };
 
-// Copy `bytes` (a multiple of 16) from global to LDS with one wavefront, 1 KiB per
-// instruction: lane i moves 16 bytes to LDS base + 16 i. Counted by vmcnt; the caller waits.
-__device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int lane) {
-    for (int off = 0; off < bytes; off += 1024) {
+// Copy `bytes` (a multiple of 16) from global to LDS with `nw` wavefronts (this one is `cw`),
+// 1 KiB per instruction: lane i moves 16 bytes to LDS base + 16 i. Counted by vmcnt; the
+// caller waits.
+__device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int cw, int nw, int lane) {
+    for (int off = cw * 1024; off < bytes; off += nw * 1024) {
         if (off + lane * 16 < bytes)
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(g + off + lane * 16), (lds_ptr_t)(l + off), 16, 0, 0);
     }
@@ -145,20 +146,32 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int t = t0 + r;
     const bool valid = t < T;
     const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
-    Raw8<BF16> rq[NKS], rk[NKS], rb[NKS];
+    // All loads are issued before any is used: alpha first (the scan needs it at once), then
+    // q, k, b; vmcnt counts in issue order, so waiting for alpha leaves the rest in flight.
+    Raw8<BF16> rq[NKS], rk[NKS], rb[NKS], ra[NKS];
     float lg[CPL];
+    float ras = 1.f;
+    if constexpr (AS) {
+        ras = valid ? load_one<BF16>(alpha, tok) : 1.f;
+    } else {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            ra[s] = valid ? gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g) : fill8<BF16>(1.f);
+    }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
         const int c0 = 32 * s + 8 * g;
         rq[s] = valid ? gload8<BF16>(q, tok * DK + c0) : fill8<BF16>(0.f);
         rk[s] = valid ? gload8<BF16>(k, tok * DK + c0) : fill8<BF16>(0.f);
         if constexpr (!BS) rb[s] = valid ? gload8<BF16>(b, tok * DK + c0) : fill8<BF16>(0.f);
-        if constexpr (!AS)
-            unpack8<BF16>(valid ? gload8<BF16>(alpha, tok * DK + c0) : fill8<BF16>(1.f), &lg[8 * s]);
     }
     const float rbs = BS ? (valid ? load_one<BF16>(b, tok) : 0.f) : 0.f;
+    if constexpr (!AS) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) unpack8<BF16>(ra[s], &lg[8 * s]);
+    }
     if constexpr (AS) {
-        float x1 = lg2(valid ? load_one<BF16>(alpha, tok) : 1.f);
+        float x1 = lg2(ras);
         x1 += row_shr<1>(x1);
         x1 += row_shr<2>(x1);
         x1 += row_shr<4>(x1);
@@ -349,7 +362,10 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
             Pm[rr * CHP + 16 * J + l16] = (E)accP[j];
         }
     }
-    if (g == 0) {
+    {
+        // T_II = (I + A_II)^-1, right-looking; every lane group computes it (lane l16 owns
+        // column l16) so the solve shares a basic block with the Gram products above and the
+        // scheduler can overlap the two. Group 0 writes the result.
         float acc[16], tc[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc[m] = 0.f;
@@ -375,8 +391,10 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
         }
+        if (g == 0) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) Tm[(16 * I + m) * CHP + 16 * I + l16] = (E)tc[m];
+            for (int m = 0; m < 16; ++m) Tm[(16 * I + m) * CHP + 16 * I + l16] = (E)tc[m];
+        }
     }
     lds_barrier();
 
@@ -461,10 +479,11 @@ struct ChainSmem {
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
-// 5 wavefronts: four state-chain waves (16 state columns each) and one copy wave that streams
-// the next chunk's operands into LDS.
+// 8 wavefronts: four state-chain waves (16 state columns each) and four copy waves that stream
+// the next chunk's operands into LDS (a wave keeps at most ~63 copies in flight, so one copy
+// wave alone cannot cover the latency).
 template <int DK, int DVT, bool BF16, bool BS>
-__global__ void __launch_bounds__(320, 1)
+__global__ void __launch_bounds__(512, 1)
 chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
              const void* __restrict__ beta, const float* S_in, float* __restrict__ o,
              float* S_out, int B, int T, int H, int DV, int n_first, int n_count,
@@ -499,7 +518,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     // v (and w) rows of chunk n, this tile's columns, into LDS; rows past T are skipped
     auto dma_vw = [&](int n) {
         const int t0 = n * CH;
-        for (int base = 0; base < CH * LPR; base += 64) {
+        for (int base = (wv - 4) * 64; base < CH * LPR; base += 4 * 64) {
             const int idx = base + lane;
             const int row = idx / LPR, seg = idx % LPR;
             if (t0 + row < T) {
@@ -522,8 +541,9 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
 
-    if (wv == 4) {
-        dma_flat(blobs, smem + SM::oBuf0, BL::bytes, lane);
+    const bool copier = wv >= 4;
+    if (copier) {
+        dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv - 4, 4, lane);
         dma_vw(n_first);
         wait_dma();
     }
@@ -541,9 +561,6 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         const float* gC = reinterpret_cast<const float*>(buf + BL::oGC);
 
         lds_barrier();  // chunk nc's blob and v, w are in LDS; buffer nc+1 is free
-        if (wv == 4 && nc + 1 < n_count)
-            dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
-                     BL::bytes, lane);
 
         // D' starts as U = w v (rows past the sequence end are zero)
         f4 D[4];
@@ -662,10 +679,14 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                 }
             }
             if constexpr (F16) lookahead_schedule<2 * NMK>();
-        } else if (wv == 4) {
-            // the copy wave: v, w of the next chunk, then wait for both copies before the next
-            // chunk's first barrier
-            if (nc + 1 < n_count) dma_vw(n + 1);
+        } else if (copier) {
+            // copy waves: the next chunk's blob and v, w rows, then wait for the copies before
+            // the next chunk's first barrier
+            if (nc + 1 < n_count) {
+                dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
+                         BL::bytes, wv - 4, 4, lane);
+                dma_vw(n + 1);
+            }
             wait_dma();
         }
     }
@@ -709,7 +730,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         const int cnt = nch - n0 < R ? nch - n0 : R;
         hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
                            a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(320), 0, st, a.v,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(512), 0, st, a.v,
                            a.w, a.b, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
