@@ -142,10 +142,10 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S0) ? S0[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
 
-    // Inputs of one chunk row for this lane, loaded ahead. alpha (part 0) and v, w (part 1) of
-    // the next chunk are issued as soon as their registers are free; q, k, b (part 2) after the
-    // state chain, so that the chain runs with few live registers. Spreading the loads keeps
-    // the vector-memory queue from backing up into the issuing wave.
+    // Inputs of one chunk row for this lane, loaded one chunk ahead. The loads of the next
+    // chunk are issued in portions spread over the current one, each as soon as its registers
+    // are free (part 0: alpha after the scan; 1: q, v, w after the factors; 2: k and 3: b
+    // during the state chain), so the vector-memory queue never backs up into the issuing wave.
     Raw8<BF16> rq[NKS], rk[NKS], rb[NKS], ra[NKS], rv[NCV / 8], rw[NCV / 8];
     float ras = 1.f, rbs = 0.f;
     auto fetch = [&](int n, int part) {
@@ -161,25 +161,32 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     ra[s] = valid ? gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g) : fill8<BF16>(1.f);
             }
         } else if (part == 1) {
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                rq[s] = valid ? gload8<BF16>(q, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
             const int v0 = tile * DVT + g * NCV;
 #pragma unroll
             for (int u = 0; u < NCV / 8; ++u) {
                 rv[u] = valid ? gload8<BF16>(v, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
                 if constexpr (!BS) rw[u] = valid ? gload8<BF16>(w, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
             }
-        } else {
+        } else if (part == 2) {
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                rq[s] = valid ? gload8<BF16>(q, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+            for (int s = 0; s < NKS; ++s)
                 rk[s] = valid ? gload8<BF16>(k, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
-                if constexpr (!BS) rb[s] = valid ? gload8<BF16>(b, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+        } else {
+            if constexpr (BS) {
+                rbs = valid ? load_one<BF16>(b, tok) : 0.f;
+            } else {
+#pragma unroll
+                for (int s = 0; s < NKS; ++s)
+                    rb[s] = valid ? gload8<BF16>(b, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
             }
-            if constexpr (BS) rbs = valid ? load_one<BF16>(b, tok) : 0.f;
         }
     };
 
     const int nch = (T + CH - 1) / CH;
-    for (int part = 0; part < 3; ++part) fetch(0, part);
+    for (int part = 0; part < 4; ++part) fetch(0, part);
     for (int n = 0; n < nch; ++n) {
         const int t0 = n * CH;
         const int L = min(CH, T - t0);
@@ -531,6 +538,7 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         lds_barrier();
 
         // ---------------- F: the state chain for this wave's 16 columns ----------------
+        if (more) fetch(n + 1, 2);
         if (chain) {
             // state as B operand: K-step s covers channels 32s..32s+31 = tiles 2s, 2s+1
             Frag Sf[NKS];
@@ -561,6 +569,7 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     PR::mma(O[mt], Sf[s], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g));
                 }
             }
+            if (more) fetch(n + 1, 3);
             // Delta = T D' (T lower triangular: token K-steps s2 <= mt / 2)
             Frag Df[2];
 #pragma unroll
@@ -621,8 +630,9 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     PR::mma(Sacc[mk], PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g), Df[s2]);
                 }
             }
+        } else if (more) {
+            fetch(n + 1, 3);
         }
-        if (more) fetch(n + 1, 2);
         lds_barrier();
     }
 
