@@ -157,6 +157,9 @@ def main(argv=None):
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte "
                          "counters)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--workload", default="prefill_1p3b",
+                    choices=["prefill_1p3b", "long_prefill", "gdn_scalar", "kda_scalar"],
+                    help="prefill input recipe to time (the headline figure uses prefill_1p3b)")
     ap.add_argument("--ring-mb", type=float, default=None,
                     help="size the two-kernel path's workspace ring to about this many MiB")
     args = ap.parse_args(argv)
@@ -176,7 +179,7 @@ def main(argv=None):
         print("no GPU visible", file=sys.stderr)
         return 1
     g.load()
-    wl = WORKLOADS["prefill_1p3b"]
+    wl = WORKLOADS[args.workload]
     ins = make_inputs_torch(wl, device="cuda")
     torch.cuda.synchronize()
     B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v

@@ -46,7 +46,8 @@ struct Blob {
     static constexpr int oP = oKbT + DK * CHP * ES;     // E [64][CHP]
     static constexpr int oTm = oP + CH * CHP * ES;      // E [64][CHP]
     static constexpr int oGC = oTm + CH * CHP * ES;     // float [DK]
-    static constexpr int bytes = (oGC + DK * 4 + 255) / 256 * 256;
+    static constexpr int oBeta = oGC + DK * 4;          // float [64] scalar beta per row (scalar-beta gates)
+    static constexpr int bytes = (oBeta + CH * 4 + 255) / 256 * 256;
 };
 
 // Copy `bytes` (a multiple of 16) from global to LDS with `nw` wavefronts (this one is `cw`),
@@ -60,6 +61,11 @@ __device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int 
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Raw buffer over [base, base + bytes): loads at offsets past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 
 // Scheduling hint for a run of P products that each read one LDS operand fragment: issue the
 // first LA reads, then alternate one product and one read, so every matrix-core instruction
@@ -462,6 +468,9 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         for (int i = threadIdx.x; i < SM::outBytes / 16; i += blockDim.x) dst[i] = src[i];
         float* gc = reinterpret_cast<float*>(blob + BL::oGC);
         for (int c = threadIdx.x; c < DK; c += blockDim.x) gc[c] = tab[16 * DK + c];
+        if constexpr (BS) {
+            if (g == 0) reinterpret_cast<float*>(blob + BL::oBeta)[r] = rbs;
+        }
     }
 }
 
@@ -470,22 +479,22 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
 template <int DK, int DVT, bool F16>
 struct ChainSmem {
     using BL = Blob<DK, F16>;
-    static constexpr int VWB = CH * DVT * (F16 ? 2 : 4);  // one of v, w for the tile
+    static constexpr int VWB = CH * 16 * (F16 ? 2 : 4);  // one of v, w: 64 rows x 16 columns
     static constexpr int oBuf0 = 0;
     static constexpr int oBuf1 = BL::bytes;
-    static constexpr int oV = 2 * BL::bytes;
-    static constexpr int oW = oV + VWB;
-    static constexpr int bytes = oW + VWB;
+    static constexpr int oVW = 2 * BL::bytes;             // per chain wave: v then w
+    static constexpr int bytes = oVW + (DVT / 16) * 2 * VWB;
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
 // 8 wavefronts: four state-chain waves (16 state columns each) and four copy waves that stream
-// the next chunk's operands into LDS (a wave keeps at most ~63 copies in flight, so one copy
-// wave alone cannot cover the latency).
+// the next chunk's blob into LDS while the chain waves work on the current one. Each chain wave
+// copies its own v, w columns into a private LDS slot, one chunk ahead, so no barrier guards
+// them.
 template <int DK, int DVT, bool BF16, bool BS>
 __global__ void __launch_bounds__(512, 1)
 chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
-             const void* __restrict__ beta, const float* S_in, float* __restrict__ o,
+             const float* S_in, float* __restrict__ o,
              float* S_out, int B, int T, int H, int DV, int n_first, int n_count,
              const char* __restrict__ ws) {
     constexpr bool F16 = BF16;
@@ -497,9 +506,6 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     static_assert(SM::fits, "chain LDS budget exceeded");
     constexpr int NKS = DK / 32, NMK = DK / 16, NWC = DVT / 16;
     constexpr int DKP = BL::DKP, CHP = BL::CHP;
-    constexpr int IES = BF16 ? 2 : 4;          // input element size
-    constexpr int ROWB = DVT * IES;            // bytes of one v (or w) row of the tile
-    constexpr int LPR = ROWB / 16;             // lanes per row in the v/w copy
 
     __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
 
@@ -515,24 +521,6 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     const int mycol = tile * DVT + wv * 16 + l16;
     const char* blobs = ws + (size_t)bh * n_count * BL::bytes;
 
-    // v (and w) rows of chunk n, this tile's columns, into LDS; rows past T are skipped
-    auto dma_vw = [&](int n) {
-        const int t0 = n * CH;
-        for (int base = (wv - 4) * 64; base < CH * LPR; base += 4 * 64) {
-            const int idx = base + lane;
-            const int row = idx / LPR, seg = idx % LPR;
-            if (t0 + row < T) {
-                const long tok = ((long)bb * T + t0 + row) * H + hh;
-                const char* gv = static_cast<const char*>(v) + (tok * DV + tile * DVT) * IES + seg * 16;
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)gv, (lds_ptr_t)(smem + SM::oV + base * 16), 16, 0, 0);
-                if constexpr (!BS) {
-                    const char* gw = static_cast<const char*>(w) + (tok * DV + tile * DVT) * IES + seg * 16;
-                    __builtin_amdgcn_global_load_lds((gbl_ptr_t)gw, (lds_ptr_t)(smem + SM::oW + base * 16), 16, 0, 0);
-                }
-            }
-        }
-    };
-
     f4 Sacc[NMK];
     const long sbase = (long)bh * DK * DV;
 #pragma unroll
@@ -541,11 +529,40 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
 
+    // v and w rows of this wave's 16 columns for one chunk, copied into the wave's LDS slot
+    // through buffer resources over this sequence's rows: rows past the sequence end fall outside
+    // the buffer and arrive as zeros. The host keeps the byte offsets below 2^31. A scalar beta
+    // comes with the chunk's blob instead of w.
+    using Raw = typename std::conditional<BF16, uint16_t, uint32_t>::type;
+    constexpr int IES = (int)sizeof(Raw);
+    constexpr int LPR = 16 * IES / 16;  // lanes per 16-column row
+    constexpr int RPI = 64 / LPR;       // rows per copy instruction
+    const long seq = (long)bb * T * H;  // first token row of this sequence
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(static_cast<const char*>(v) + seq * DV * IES, T * H * DV * IES);
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(static_cast<const char*>(BS ? v : w) + seq * DV * IES, T * H * DV * IES);
+    char* vw_lds = smem + SM::oVW + (chain ? wv : 0) * 2 * SM::VWB;
+    const Raw* v_l = reinterpret_cast<const Raw*>(vw_lds);
+    const Raw* w_l = reinterpret_cast<const Raw*>(vw_lds + SM::VWB);
+    auto dma_vw = [&](int n) {
+        const unsigned col0 = (unsigned)(tile * DVT + wv * 16);
+#pragma unroll
+        for (int k = 0; k < CH / RPI; ++k) {
+            const unsigned row = (unsigned)(n * CH + k * RPI + lane / LPR);
+            const unsigned off = ((row * H + hh) * DV + col0) * IES + (lane % LPR) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lds_ptr_t)(vw_lds + k * 1024), 16, off, 0, 0, 0);
+            if constexpr (!BS)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(vw_lds + SM::VWB + k * 1024), 16, off,
+                                                         0, 0, 0);
+        }
+    };
+    auto raw_f = [](Raw r) { return BF16 ? __uint_as_float((uint32_t)r << 16) : __uint_as_float((uint32_t)r); };
+
     const bool copier = wv >= 4;
     if (copier) {
         dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv - 4, 4, lane);
-        dma_vw(n_first);
         wait_dma();
+    } else if (chain) {
+        dma_vw(n_first);
     }
 
     for (int nc = 0; nc < n_count; ++nc) {
@@ -559,39 +576,24 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         const E* Pm = reinterpret_cast<const E*>(buf + BL::oP);
         const E* Tm = reinterpret_cast<const E*>(buf + BL::oTm);
         const float* gC = reinterpret_cast<const float*>(buf + BL::oGC);
+        const float* betaL = reinterpret_cast<const float*>(buf + BL::oBeta);
 
-        lds_barrier();  // chunk nc's blob and v, w are in LDS; buffer nc+1 is free
+        lds_barrier();  // chunk nc's blob is in LDS; the other buffer is free
 
-        // D' starts as U = w v (rows past the sequence end are zero)
-        f4 D[4];
         if (chain) {
+            // D' starts as U = w v, from this wave's slot (its copy, and the o stores issued
+            // after it, have completed once vmcnt is zero)
+            wait_dma();
+            f4 D[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * mt + 4 * g + j;
-                    const int cl = wv * 16 + l16;
-                    float vv, ww;
-                    if constexpr (BF16) {
-                        vv = bf16_to_f32(reinterpret_cast<const uint16_t*>(smem + SM::oV)[row * DVT + cl]);
-                    } else {
-                        vv = reinterpret_cast<const float*>(smem + SM::oV)[row * DVT + cl];
-                    }
-                    if constexpr (BS) {
-                        const long tok = ((long)bb * T + t0 + (row < L ? row : 0)) * H + hh;
-                        ww = load_one<BF16>(beta, tok);
-                    } else if constexpr (BF16) {
-                        ww = bf16_to_f32(reinterpret_cast<const uint16_t*>(smem + SM::oW)[row * DVT + cl]);
-                    } else {
-                        ww = reinterpret_cast<const float*>(smem + SM::oW)[row * DVT + cl];
-                    }
-                    D[mt][j] = row < L ? ww * vv : 0.f;
+                    const float ww = BS ? betaL[row] : raw_f(w_l[row * 16 + l16]);
+                    D[mt][j] = ww * raw_f(v_l[row * 16 + l16]);
                 }
-            }
-        }
-        lds_barrier();  // every wave has read v, w of chunk nc
-
-        if (chain) {
+            if (nc + 1 < n_count) dma_vw(n + 1);
             Frag Sf[NKS];
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
@@ -680,13 +682,11 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
             }
             if constexpr (F16) lookahead_schedule<2 * NMK>();
         } else if (copier) {
-            // copy waves: the next chunk's blob and v, w rows, then wait for the copies before
-            // the next chunk's first barrier
-            if (nc + 1 < n_count) {
+            // copy waves: the next chunk's blob, then wait for the copies before the next
+            // chunk's barrier
+            if (nc + 1 < n_count)
                 dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
                          BL::bytes, wv - 4, 4, lane);
-                dma_vw(n + 1);
-            }
             wait_dma();
         }
     }
@@ -731,7 +731,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
                            a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
         hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(512), 0, st, a.v,
-                           a.w, a.b, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
+                           a.w, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -750,8 +750,10 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool split_supported(int DK, int DV, bool bf16) {
+bool split_supported(int T, int H, int DK, int DV, bool bf16) {
     if (DK != DV) return false;
+    // the chain kernel addresses one sequence's v, w rows with 32-bit byte offsets
+    if ((long long)T * H * DV * (bf16 ? 2 : 4) >= (1ll << 31)) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
     return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
 }
@@ -767,7 +769,7 @@ size_t split_chunk_bytes(int B, int H, int DK, bool bf16) {
 }
 
 hipError_t launch_split(const ChunkArgs& a, hipStream_t s) {
-    if (!split_supported(a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
+    if (!split_supported(a.T, a.H, a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
     if (a.bf16) {
         switch (a.DK) {
             case 32: return launch_split_flags<32, true>(a, s);

@@ -135,7 +135,7 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags) {
     if (B <= 0 || H <= 0 || T <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
     const bool bf16 = in_dtype == GDN2_BF16;
-    if (!gdn2::split_supported(d_k, d_v, bf16)) return 0;
+    if (!gdn2::split_supported(T, H, d_k, d_v, bf16)) return 0;
     const size_t nch = ((size_t)T + 63) / 64;
     const size_t per_chunk = gdn2::split_chunk_bytes(B, H, d_k, bf16);
     size_t ring = kRingBytes / per_chunk;  // chunk slots in the recommended ring
@@ -153,7 +153,7 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                               gate_flags, false);
     if (st != GDN2_OK) return st;
     const bool bf16 = in_dtype == GDN2_BF16;
-    const bool split = workspace && workspace_bytes > 0 && gdn2::split_supported(d_k, d_v, bf16);
+    const bool split = workspace && workspace_bytes > 0 && gdn2::split_supported(T, H, d_k, d_v, bf16);
     if (split) {
         const size_t min_bytes = split_min_bytes(B, H, d_k, d_v, bf16);
         if (workspace_bytes < min_bytes) return GDN2_ERR_WORKSPACE;

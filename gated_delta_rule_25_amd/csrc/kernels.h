@@ -39,7 +39,7 @@ bool chunk_supported(int DK, int DV, bool bf16);
 // Two-kernel path (prep + chain) through a workspace ring of per-chunk operand blobs.
 // Workspace = state buffer (B*H*DK*DV fp32) + R chunk slots of split_chunk_bytes each.
 hipError_t launch_split(const ChunkArgs& a, hipStream_t s);
-bool split_supported(int DK, int DV, bool bf16);
+bool split_supported(int T, int H, int DK, int DV, bool bf16);
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16);
 
 }  // namespace gdn2
