@@ -11,8 +11,10 @@ A timed step is one gdn2_chunk_fwd call over the whole batch; `value` = B*T / (s
 Decode workload (reported beside it): B=256 (and B=1024, whose 1 GiB state cannot sit in
 the 256 MB Infinity Cache), H=16, d=128, fp32 state updated in place over consecutive steps.
 
-Prints ONE JSON line. `roofline` is for the prefill kernel: algorithmic bytes per launch over
-the kernel's average duration (HIP events on the launch stream) against 8 TB/s HBM3E.
+Prints ONE JSON line. `roofline` is for the prefill call (with a workspace: the prep kernel and
+the chain kernel that one gdn2_chunk_fwd call enqueues): algorithmic bytes per call over the
+call's average duration (HIP events on the launch stream) against 8 TB/s HBM3E; `traffic` is
+the HBM bytes per call that rocprofv3 counted for the same kernels.
 `cpu_baseline` times the fp64 oracle (tests-only code, timed here as a reported baseline) on a
 bounded sample of the same workload with all host cores.
 """
@@ -31,6 +33,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per gdn2_chunk_fwd call at B8 H16 T4096 d128 bf16, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE scaled by a 1 GiB copy (profiles/chunk_fwd_bf16_B8_H16_T4096_d128.txt), for the
+# kernels as they stand; set to None when a kernel changes until the counters are taken again.
+MEASURED_TRAFFIC = {"chunk": 2298.6e6, "fused": None, "recurrent": None}
+
 
 def prefill_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
     # q, k, alpha, b (bf16) + v, w (bf16) + o (fp32) + S0 read and S_T write amortised over T
@@ -41,6 +48,13 @@ def prefill_flops_per_head_token(dk: int, dv: int, C: int = 64) -> float:
     # three state products (W S, Q_hat S, K_bar^T Delta) + five triangular C x C products
     # (A, P, W = T E_hat, U~ = T U, P Delta; counted at half) + the UT solve
     return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3
+
+
+KERNELS = {
+    "chunk": "prep_kernel + chain_kernel (one gdn2_chunk_fwd call with a workspace)",
+    "fused": "chunk_kernel (one gdn2_chunk_fwd call without a workspace)",
+    "recurrent": "recurrent_kernel (gdn2_recurrent_fwd)",
+}
 
 
 def decode_bytes_per_head(dk: int, dv: int) -> float:
@@ -238,12 +252,14 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16-in/f32" if args.impl == "recurrent" else "bf16-in/f16-mfma/f32-state",
         "data": "synthetic",
-        "config": {"workload": "GDN-2 layer prefill B8 H16 T4096 d_k=d_v=128, chunk 64",
+        "config": {"workload": f"GDN-2 layer prefill ({wl.name}) B{B} H{H} T{T} d_k=d_v={dk}, chunk 64",
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
                    "impl": args.impl, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": (MEASURED_TRAFFIC.get(args.impl)
+                                 if args.workload == "prefill_1p3b" else None),
+                     "kernels": KERNELS[args.impl],
                      "kernel_ms": round(kern_avg, 4),
                      "algorithmic_bytes": int(bytes_launch),
                      "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},

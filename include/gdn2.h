@@ -31,10 +31,11 @@
  * Inputs q, k, v, alpha, b, w share one element type (in_dtype); o and the state are float32.
  *
  * Ownership and execution. All pointers are device pointers owned by the caller (HIP device
- * memory, e.g. allocated by PyTorch). The library allocates nothing, keeps no state between
- * calls and is reentrant. Calls only enqueue kernels on `stream` (a hipStream_t; NULL is the
- * null stream) and return at once; inputs must stay alive and unchanged until the stream
- * passes the work.
+ * memory, e.g. allocated by PyTorch), the chunked prefill's optional workspace included. The
+ * library allocates nothing, keeps no state between calls and is reentrant (two calls in
+ * flight at once need two workspaces). Calls only enqueue kernels on `stream` (a hipStream_t;
+ * NULL is the null stream) and return at once; inputs must stay alive and unchanged until the
+ * stream passes the work.
  *
  * Errors. Argument errors are detected on the host and returned with nothing enqueued. A
  * failed launch returns GDN2_ERR_HIP. Device faults surface at the caller's next
@@ -85,9 +86,24 @@ enum {
  * the token-by-token recurrence up to rounding. bf16 inputs use fp16 matrix-core operands with
  * fp32 accumulation and an fp32 state; fp32 inputs are computed in fp32 throughout.
  *
- * Supported: d_k == d_v in {32, 64, 128}; in_dtype GDN2_BF16 or GDN2_F32; any flags above.
- * Workspace: pass a buffer of at least gdn2_chunk_fwd_workspace_bytes(...) bytes (it may be
- * 0, in which case workspace may be NULL).
+ * The workspace selects how the chunks are scheduled; the result is the same either way.
+ *  - workspace != NULL with workspace_bytes > 0 (and the sizes supported below): two kernels. A prep kernel, parallel
+ *    over every (b, h, chunk), computes each chunk's decay-scaled factors, its 64x64 Gram
+ *    products and the UT inverse T, and stores them as one operand block per chunk in the
+ *    workspace; a chain kernel then runs the state recurrence chunk by chunk from those blocks.
+ *    Supported: bf16 with d in {32, 64, 128}, fp32 with d = 32, and T*H*d_v*elem_size < 2^31
+ *    bytes per sequence. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v] first
+ *    when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand blocks.
+ *    R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with
+ *    fewer slots than chunks the two kernels alternate over rounds of R chunks. The buffer must
+ *    be 256-byte aligned (else GDN2_ERR_ALIGN), hold the state and one slot (else
+ *    GDN2_ERR_WORKSPACE) and overlap no input or output (else GDN2_ERR_ALIAS). Its contents
+ *    are scratch on entry and on return.
+ *  - no workspace, or sizes the two-kernel path does not take: one kernel, one workgroup
+ *    per (b, h, 64-column tile of the state) computing each chunk's factors and then its part
+ *    of the state recurrence. Supported: bf16 with d in {32, 64, 128}, fp32 with d in {32, 64};
+ *    other sizes return GDN2_ERR_UNSUPPORTED.
+ * d_k must equal d_v. Any flags above.
  */
 gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
                            const void *b, const void *w, const float *S0, float *o,
@@ -95,7 +111,9 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                            void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace gdn2_chunk_fwd needs for these sizes (0 when none). */
+/* Workspace bytes for the two-kernel path of gdn2_chunk_fwd at these sizes: the state buffer
+ * (when S_out may be NULL) plus one slot per chunk, so that one round covers the sequence. 0 when
+ * the two-kernel path does not take these sizes (pass NULL; the single kernel runs). */
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
 
