@@ -37,7 +37,10 @@ template <int DK, bool F16>
 struct Blob {
     using E = typename Prec<F16>::E;
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int PAD = Prec<F16>::kPad;
+    // Rows padded by 4 elements. For the fp16 operands that makes the row stride 2 dwords more
+    // than a multiple of 32 banks, so the 8-byte fragment reads of 16 consecutive rows (one
+    // 16-lane group of ds_read_b64) hit 32 distinct banks.
+    static constexpr int PAD = 4;
     static constexpr int DKP = DK + PAD;
     static constexpr int CHP = CH + PAD;
     static constexpr int oQh = 0;                       // E [64][DKP]
@@ -61,6 +64,27 @@ __device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int 
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// All but the newest four vector-memory operations done (vmcnt(4)).
+__device__ __forceinline__ void wait_vm_but4() { __builtin_amdgcn_s_waitcnt(0x0f74); }
+
+// Eight elements to a blob row position: two 8-byte stores for fp16 (blob rows are 8-byte
+// aligned), two 16-byte stores for fp32.
+template <typename E>
+__device__ __forceinline__ void store8_rows(E* p, const float* x) {
+    if constexpr (sizeof(E) == 2) {
+        h4 a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = (_Float16)x[i];
+            b[i] = (_Float16)x[i + 4];
+        }
+        reinterpret_cast<h4*>(p)[0] = a;
+        reinterpret_cast<h4*>(p)[1] = b;
+    } else {
+        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+}
 
 // Raw buffer over [base, base + bytes): loads at offsets past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -98,8 +122,9 @@ struct PrepSmem {
     static constexpr int oP = oKbT + DK * CHP * ES;
     static constexpr int oTm = oP + CH * CHP * ES;
     static constexpr int outBytes = (BL::oGC - BL::oKbT);
-    static constexpr int oKt = oOut + outBytes;         // E [48][DKP]
-    static constexpr int oA = oKt + 48 * DKP * ES;      // E [64][CHP] A below the diagonal
+    static constexpr int KTP = DK + Prec<F16>::kPad;    // 16-byte rows for 16-byte accesses
+    static constexpr int oKt = oOut + outBytes;         // E [48][KTP]
+    static constexpr int oA = oKt + 48 * KTP * ES;      // E [64][CHP] A below the diagonal
     static constexpr int oAd = oA + CH * CHP * ES;      // float [4][16][16] diagonal A^T
     static constexpr int bytes = oAd + 4 * 256 * 4;
     static_assert(BL::oP - BL::oKbT == DK * CHP * ES && BL::oTm - BL::oP == CH * CHP * ES, "layout");
@@ -283,9 +308,9 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
                 PR::mma(accA, PR::make(em), kmf);
                 PR::mma(accP, PR::make(qm), kmf);
             }
-            PR::store8(&bQh[r * DKP + c0], qh);
-            PR::store8(&bEn[r * DKP + c0], en);
-            if (I < 3) PR::store8(&Kt[r * DKP + c0], kt);
+            store8_rows(&bQh[r * DKP + c0], qh);
+            store8_rows(&bEn[r * DKP + c0], en);
+            if (I < 3) PR::store8(&Kt[r * SM::KTP + c0], kt);
         }
         bool finite = true;
 #pragma unroll
@@ -357,7 +382,7 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     qa[i] = qr[8 * s + i];
                 }
             }
-            const Frag kf = PR::lds8(Kt + (16 * J + l16) * DKP + c0);
+            const Frag kf = PR::lds8(Kt + (16 * J + l16) * SM::KTP + c0);
             PR::mma(accA, PR::make(ea), kf);
             PR::mma(accP, PR::make(qa), kf);
         }
@@ -520,6 +545,9 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     const bool chain = wv < NWC;
     const int mycol = tile * DVT + wv * 16 + l16;
     const char* blobs = ws + (size_t)bh * n_count * BL::bytes;
+    // o row of token l16 of chunk 0, this lane's four columns; token t is t * H * DV further on
+    float* const o_lane = o + (((long)bb * T + l16) * H + hh) * DV + tile * DVT + 16 * wv + 4 * g;
+    const long o_tok = (long)H * DV;
 
     f4 Sacc[NMK];
     const long sbase = (long)bh * DK * DV;
@@ -547,7 +575,10 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         const unsigned col0 = (unsigned)(tile * DVT + wv * 16);
 #pragma unroll
         for (int k = 0; k < CH / RPI; ++k) {
-            const unsigned row = (unsigned)(n * CH + k * RPI + lane / LPR);
+            // slot position p holds token row 16 (p / 16) + 4 (p % 4) + (p / 4) % 4, so that the
+            // four rows 4 g + j (g = 0..3) read together sit in consecutive 32-byte slots
+            const int p = k * RPI + lane / LPR;
+            const unsigned row = (unsigned)(n * CH + 16 * (p / 16) + 4 * (p % 4) + (p / 4) % 4);
             const unsigned off = ((row * H + hh) * DV + col0) * IES + (lane % LPR) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lds_ptr_t)(vw_lds + k * 1024), 16, off, 0, 0, 0);
             if constexpr (!BS)
@@ -581,19 +612,27 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         lds_barrier();  // chunk nc's blob is in LDS; the other buffer is free
 
         if (chain) {
-            // D' starts as U = w v, from this wave's slot (its copy, and the o stores issued
-            // after it, have completed once vmcnt is zero)
-            wait_dma();
+            // D' starts as U = w v, from this wave's slot. Its copy was issued before the previous
+            // chunk's four o stores (all rows of a chunk that is not the last are valid), so
+            // vmcnt(4) covers it and leaves those stores in flight.
+            if (nc == 0) {
+                wait_dma();
+            } else {
+                wait_vm_but4();
+            }
             f4 D[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * mt + 4 * g + j;
-                    const float ww = BS ? betaL[row] : raw_f(w_l[row * 16 + l16]);
-                    D[mt][j] = ww * raw_f(v_l[row * 16 + l16]);
+                    const int row = 16 * mt + 4 * g + j, slot = 16 * mt + 4 * j + g;
+                    const float ww = BS ? betaL[row] : raw_f(w_l[slot * 16 + l16]);
+                    D[mt][j] = ww * raw_f(v_l[slot * 16 + l16]);
                 }
             if (nc + 1 < n_count) dma_vw(n + 1);
+            float4 gcv[NMK];  // gamma_last of this lane's state rows
+#pragma unroll
+            for (int mk = 0; mk < NMK; ++mk) gcv[mk] = *reinterpret_cast<const float4*>(gC + 16 * mk + 4 * g);
             Frag Sf[NKS];
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
@@ -652,7 +691,8 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                 }
                 Df[s2] = PR::make(dv_);
             }
-            // O^T += Delta^T P^T, store four columns per lane
+            // O^T += Delta^T P^T and S <- Diag(gamma_last) S + K_bar^T Delta: independent
+            // products on one pipelined stream of operand reads
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
@@ -660,27 +700,27 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                     const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
                     PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
                 }
-                const int row = 16 * nt + l16;
-                if (row < L) {
-                    float* op = o + (((long)bb * T + t0 + row) * H + hh) * DV + tile * DVT + 16 * wv + 4 * g;
-                    *reinterpret_cast<float4*>(op) = make_float4(O[nt][0], O[nt][1], O[nt][2], O[nt][3]);
-                }
             }
-            // S <- Diag(gamma_last) S + K_bar^T Delta
 #pragma unroll
             for (int mk = 0; mk < NMK; ++mk) {
-                const float4 gc = *reinterpret_cast<const float4*>(gC + 16 * mk + 4 * g);
-                Sacc[mk][0] *= gc.x;
-                Sacc[mk][1] *= gc.y;
-                Sacc[mk][2] *= gc.z;
-                Sacc[mk][3] *= gc.w;
+                Sacc[mk][0] *= gcv[mk].x;
+                Sacc[mk][1] *= gcv[mk].y;
+                Sacc[mk][2] *= gcv[mk].z;
+                Sacc[mk][3] *= gcv[mk].w;
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const E* kr = &KbT[(16 * mk + l16) * CHP + 32 * s2];
                     PR::mma(Sacc[mk], PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g), Df[s2]);
                 }
             }
-            if constexpr (F16) lookahead_schedule<2 * NMK>();
+            if constexpr (F16) lookahead_schedule<6 + 2 * NMK, 6>();
+            // o rows of this chunk: four consecutive columns per lane, one 16-byte store each
+            float* const op = o_lane + (long)t0 * o_tok;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                if (16 * nt + l16 < L)
+                    *reinterpret_cast<float4*>(op + 16 * nt * o_tok) = make_float4(O[nt][0], O[nt][1], O[nt][2], O[nt][3]);
+            }
         } else if (copier) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
             // chunk's barrier
