@@ -64,8 +64,12 @@ __device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int 
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-// All but the newest four vector-memory operations done (vmcnt(4)).
-__device__ __forceinline__ void wait_vm_but4() { __builtin_amdgcn_s_waitcnt(0x0f74); }
+// All but the newest N (< 16) vector-memory operations done (vmcnt(N)).
+template <int N>
+__device__ __forceinline__ void wait_vm_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // Eight elements to a blob row position: two 8-byte stores for fp16 (blob rows are 8-byte
 // aligned), two 16-byte stores for fp32.
@@ -92,18 +96,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 // Scheduling hint for a run of P products that each read one LDS operand fragment: issue the
-// first LA reads, then alternate one product and one read, so every matrix-core instruction
-// finds its operand already loaded.
-template <int P, int LA = 4>
+// first LA reads, then alternate MPR products (those sharing one read operand) and one read, so
+// every matrix-core instruction finds its operand already loaded.
+template <int P, int LA = 4, int MPR = 1>
 __device__ __forceinline__ void lookahead_schedule() {
     constexpr int la = P < LA ? P : LA;
     __builtin_amdgcn_sched_group_barrier(0x100, la, 0);
 #pragma unroll
     for (int i = 0; i < P - la; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, la, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, la * MPR, 0);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -501,23 +505,33 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
 
 // ------------------------------------------------------------------------------------------
 // chain: one (b, h, value tile), chunks n_first .. n_first + n_count - 1
+// Chain kernel shape: each chain wave owns NT 16-column state tiles, which share every operand
+// read from LDS; the copy waves stream the next chunk's block.
+constexpr int kChainNT = 1;
+constexpr int kChainThreads = 2 * (kChainNT == 1 ? 4 : 2) * 64;
+
 template <int DK, int DVT, bool F16>
 struct ChainSmem {
     using BL = Blob<DK, F16>;
-    static constexpr int VWB = CH * 16 * (F16 ? 2 : 4);  // one of v, w: 64 rows x 16 columns
+    static constexpr int NT = kChainNT;
+    static constexpr int NWC = DVT / (16 * NT);                 // chain waves
+    static constexpr int CW0 = NT == 1 ? 4 : 2;                 // first copy wave = copy waves
+    static constexpr int threads = kChainThreads;
+    static_assert(threads == 2 * CW0 * 64, "wave layout");
+    static constexpr int VWB = CH * 16 * NT * (F16 ? 2 : 4);  // one of v, w: 64 rows x 16 NT columns
     static constexpr int oBuf0 = 0;
     static constexpr int oBuf1 = BL::bytes;
-    static constexpr int oVW = 2 * BL::bytes;             // per chain wave: v then w
-    static constexpr int bytes = oVW + (DVT / 16) * 2 * VWB;
-    static constexpr bool fits = bytes <= 160 * 1024;
+    static constexpr int oVW = 2 * BL::bytes;                   // per chain wave: v then w
+    static constexpr int bytes = oVW + NWC * 2 * VWB;
+    static constexpr bool fits = bytes <= 160 * 1024 && NWC >= 1 && NWC <= CW0;
 };
 
-// 8 wavefronts: four state-chain waves (16 state columns each) and four copy waves that stream
-// the next chunk's blob into LDS while the chain waves work on the current one. Each chain wave
-// copies its own v, w columns into a private LDS slot, one chunk ahead, so no barrier guards
+// Chain waves 0..NWC-1 hold the state; copy waves CW0..2 CW0-1 stream the next chunk's block into
+// LDS while the chain waves work on the current one (one wave per SIMD when NT = 2). Each chain
+// wave copies its own v, w columns into a private LDS slot, one chunk ahead, so no barrier guards
 // them.
 template <int DK, int DVT, bool BF16, bool BS>
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(kChainThreads, 1)
 chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
              const float* S_in, float* __restrict__ o,
              float* S_out, int B, int T, int H, int DV, int n_first, int n_count,
@@ -528,11 +542,16 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     using Frag = typename PR::Frag;
     using BL = Blob<DK, F16>;
     using SM = ChainSmem<DK, DVT, F16>;
-    static_assert(SM::fits, "chain LDS budget exceeded");
-    constexpr int NKS = DK / 32, NMK = DK / 16, NWC = DVT / 16;
+    static_assert(SM::fits, "chain LDS budget or wave layout");
+    constexpr int NT = SM::NT, NWC = SM::NWC, CW0 = SM::CW0;
+    constexpr int NKS = DK / 32, NMK = DK / 16;
     constexpr int DKP = BL::DKP, CHP = BL::CHP;
 
-    __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
+    // Two arrays: the block buffers and the v/w slots. Separate objects let the compiler see that
+    // a v/w copy in flight cannot alias the block reads that follow it, so it does not wait for
+    // the copy before them.
+    __shared__ __attribute__((aligned(16))) char smem[SM::oVW];
+    __shared__ __attribute__((aligned(16))) char svw[SM::bytes - SM::oVW];
 
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int tiles = DV / DVT;
@@ -543,43 +562,47 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     if (bh >= B * H) return;
     const int hh = bh % H, bb = bh / H;
     const bool chain = wv < NWC;
-    const int mycol = tile * DVT + wv * 16 + l16;
+    const bool copier = wv >= CW0;
+    const int col0 = tile * DVT + (chain ? wv : 0) * 16 * NT;  // this wave's first state column
     const char* blobs = ws + (size_t)bh * n_count * BL::bytes;
-    // o row of token l16 of chunk 0, this lane's four columns; token t is t * H * DV further on
-    float* const o_lane = o + (((long)bb * T + l16) * H + hh) * DV + tile * DVT + 16 * wv + 4 * g;
+    // o row of token l16 of chunk 0 at this lane's four columns of tile 0; token t is t * H * DV on
+    float* const o_lane = o + (((long)bb * T + l16) * H + hh) * DV + col0 + 4 * g;
     const long o_tok = (long)H * DV;
 
-    f4 Sacc[NMK];
+    f4 Sacc[NT][NMK];
     const long sbase = (long)bh * DK * DV;
 #pragma unroll
-    for (int mk = 0; mk < NMK; ++mk)
+    for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            Sacc[mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
+        for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                Sacc[c][mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16]
+                                                 : 0.f;
 
-    // v and w rows of this wave's 16 columns for one chunk, copied into the wave's LDS slot
-    // through buffer resources over this sequence's rows: rows past the sequence end fall outside
-    // the buffer and arrive as zeros. The host keeps the byte offsets below 2^31. A scalar beta
-    // comes with the chunk's blob instead of w.
+    // v and w rows of this wave's columns for one chunk, copied into the wave's LDS slot through
+    // buffer resources over this sequence's rows: rows past the sequence end fall outside the
+    // buffer and arrive as zeros. The host keeps the byte offsets below 2^31. A scalar beta comes
+    // with the chunk's block instead of w.
     using Raw = typename std::conditional<BF16, uint16_t, uint32_t>::type;
     constexpr int IES = (int)sizeof(Raw);
-    constexpr int LPR = 16 * IES / 16;  // lanes per 16-column row
-    constexpr int RPI = 64 / LPR;       // rows per copy instruction
-    const long seq = (long)bb * T * H;  // first token row of this sequence
+    constexpr int ROW = 16 * NT;             // elements per slot row
+    constexpr int LPR = ROW * IES / 16;      // lanes per slot row in a copy
+    constexpr int RPI = 64 / LPR;            // rows per copy instruction
+    const long seq = (long)bb * T * H;       // first token row of this sequence
     const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(static_cast<const char*>(v) + seq * DV * IES, T * H * DV * IES);
     const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(static_cast<const char*>(BS ? v : w) + seq * DV * IES, T * H * DV * IES);
-    char* vw_lds = smem + SM::oVW + (chain ? wv : 0) * 2 * SM::VWB;
+    char* vw_lds = svw + (chain ? wv : 0) * 2 * SM::VWB;
     const Raw* v_l = reinterpret_cast<const Raw*>(vw_lds);
     const Raw* w_l = reinterpret_cast<const Raw*>(vw_lds + SM::VWB);
     auto dma_vw = [&](int n) {
-        const unsigned col0 = (unsigned)(tile * DVT + wv * 16);
 #pragma unroll
         for (int k = 0; k < CH / RPI; ++k) {
-            // slot position p holds token row 16 (p / 16) + 4 (p % 4) + (p / 4) % 4, so that the
-            // four rows 4 g + j (g = 0..3) read together sit in consecutive 32-byte slots
+            // slot row p holds token row 16 (p / 16) + 4 (p % 4) + (p / 4) % 4, so that the four
+            // rows 4 g + j (g = 0..3) read together sit in consecutive slot rows
             const int p = k * RPI + lane / LPR;
             const unsigned row = (unsigned)(n * CH + 16 * (p / 16) + 4 * (p % 4) + (p / 4) % 4);
-            const unsigned off = ((row * H + hh) * DV + col0) * IES + (lane % LPR) * 16;
+            const unsigned off = ((row * H + hh) * DV + (unsigned)col0) * IES + (lane % LPR) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lds_ptr_t)(vw_lds + k * 1024), 16, off, 0, 0, 0);
             if constexpr (!BS)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(vw_lds + SM::VWB + k * 1024), 16, off,
@@ -587,10 +610,19 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         }
     };
     auto raw_f = [](Raw r) { return BF16 ? __uint_as_float((uint32_t)r << 16) : __uint_as_float((uint32_t)r); };
+    // two stacked 16-row accumulator tiles as one operand fragment (the kap() slot order)
+    auto stack = [](const f4& lo, const f4& hi) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            t[i] = lo[i];
+            t[i + 4] = hi[i];
+        }
+        return PR::make(t);
+    };
 
-    const bool copier = wv >= 4;
     if (copier) {
-        dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv - 4, 4, lane);
+        dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv - CW0, CW0, lane);
         wait_dma();
     } else if (chain) {
         dma_vw(n_first);
@@ -613,84 +645,78 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
 
         if (chain) {
             // D' starts as U = w v, from this wave's slot. Its copy was issued before the previous
-            // chunk's four o stores (all rows of a chunk that is not the last are valid), so
-            // vmcnt(4) covers it and leaves those stores in flight.
+            // chunk's o stores (4 NT of them: all rows of a chunk that is not the last are valid),
+            // so this wait covers it and leaves those stores in flight.
             if (nc == 0) {
                 wait_dma();
             } else {
-                wait_vm_but4();
+                wait_vm_but<4 * NT>();
             }
-            f4 D[4];
+            f4 D[NT][4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * mt + 4 * g + j, slot = 16 * mt + 4 * j + g;
-                    const float ww = BS ? betaL[row] : raw_f(w_l[slot * 16 + l16]);
-                    D[mt][j] = ww * raw_f(v_l[slot * 16 + l16]);
-                }
-            if (nc + 1 < n_count) dma_vw(n + 1);
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = 16 * mt + 4 * g + j, slot = 16 * mt + 4 * j + g, cl = 16 * c + l16;
+                        const float ww = BS ? betaL[row] : raw_f(w_l[slot * ROW + cl]);
+                        D[c][mt][j] = ww * raw_f(v_l[slot * ROW + cl]);
+                    }
             float4 gcv[NMK];  // gamma_last of this lane's state rows
 #pragma unroll
             for (int mk = 0; mk < NMK; ++mk) gcv[mk] = *reinterpret_cast<const float4*>(gC + 16 * mk + 4 * g);
-            Frag Sf[NKS];
+            __builtin_amdgcn_sched_barrier(0);  // keep these reads out of the operand pipeline below
+            Frag Sf[NT][NKS];
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                float sv[8];
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sv[i] = Sacc[2 * s][i];
-                    sv[i + 4] = Sacc[2 * s + 1][i];
-                }
-                Sf[s] = PR::make(sv);
-            }
-            // D' = U - E_hat S ; O^T = S^T Q_hat^T
-            f4 O[4];
+                for (int s = 0; s < NKS; ++s) Sf[c][s] = stack(Sacc[c][2 * s], Sacc[c][2 * s + 1]);
+            // D' = U - E_hat S ; O^T = S^T Q_hat^T (each operand read feeds all NT tiles)
+            f4 O[NT][4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                O[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NT; ++c) O[c][mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
                     const E* er_ = &En[(16 * mt + l16) * DKP + 32 * s];
                     const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
-                    PR::mma(D[mt], PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g), Sf[s]);
-                    PR::mma(O[mt], Sf[s], PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g));
+                    const Frag ef = PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) PR::mma(D[c][mt], ef, Sf[c][s]);
+                    const Frag qf = PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) PR::mma(O[c][mt], Sf[c][s], qf);
                 }
             }
-            if constexpr (F16) lookahead_schedule<8 * NKS, 6>();
+            if constexpr (F16) lookahead_schedule<8 * NKS, 6, NT>();
+            // the next chunk's v, w into this wave's slot, now that its reads are long done
+            if (nc + 1 < n_count) dma_vw(n + 1);
             // Delta = T D'
-            Frag Df[2];
+            Frag Df[NT][2];
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                float dv_[8];
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dv_[i] = D[2 * s2][i];
-                    dv_[i + 4] = D[2 * s2 + 1][i];
-                }
-                Df[s2] = PR::make(dv_);
-            }
-            f4 Dl[4];
+                for (int s2 = 0; s2 < 2; ++s2) Df[c][s2] = stack(D[c][2 * s2], D[c][2 * s2 + 1]);
+            f4 Dl[NT][4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                Dl[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NT; ++c) Dl[c][mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 <= mt / 2; ++s2) {
                     const E* tr = &Tm[(16 * mt + l16) * CHP + 32 * s2];
-                    PR::mma(Dl[mt], PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g), Df[s2]);
+                    const Frag tf = PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) PR::mma(Dl[c][mt], tf, Df[c][s2]);
                 }
             }
-            if constexpr (F16) lookahead_schedule<6>();
+            if constexpr (F16) lookahead_schedule<6, 4, NT>();
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                float dv_[8];
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dv_[i] = Dl[2 * s2][i];
-                    dv_[i + 4] = Dl[2 * s2 + 1][i];
-                }
-                Df[s2] = PR::make(dv_);
-            }
+                for (int s2 = 0; s2 < 2; ++s2) Df[c][s2] = stack(Dl[c][2 * s2], Dl[c][2 * s2 + 1]);
             // O^T += Delta^T P^T and S <- Diag(gamma_last) S + K_bar^T Delta: independent
             // products on one pipelined stream of operand reads
 #pragma unroll
@@ -698,45 +724,58 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
 #pragma unroll
                 for (int s2 = 0; s2 <= nt / 2; ++s2) {
                     const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
-                    PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
+                    const Frag pf = PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) PR::mma(O[c][nt], Df[c][s2], pf);
                 }
             }
 #pragma unroll
             for (int mk = 0; mk < NMK; ++mk) {
-                Sacc[mk][0] *= gcv[mk].x;
-                Sacc[mk][1] *= gcv[mk].y;
-                Sacc[mk][2] *= gcv[mk].z;
-                Sacc[mk][3] *= gcv[mk].w;
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    Sacc[c][mk][0] *= gcv[mk].x;
+                    Sacc[c][mk][1] *= gcv[mk].y;
+                    Sacc[c][mk][2] *= gcv[mk].z;
+                    Sacc[c][mk][3] *= gcv[mk].w;
+                }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const E* kr = &KbT[(16 * mk + l16) * CHP + 32 * s2];
-                    PR::mma(Sacc[mk], PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g), Df[s2]);
+                    const Frag kf = PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) PR::mma(Sacc[c][mk], kf, Df[c][s2]);
                 }
             }
-            if constexpr (F16) lookahead_schedule<6 + 2 * NMK, 6>();
-            // o rows of this chunk: four consecutive columns per lane, one 16-byte store each
+            if constexpr (F16) lookahead_schedule<6 + 2 * NMK, 6, NT>();
+            // o rows of this chunk: four consecutive columns per lane and tile, 16-byte stores
             float* const op = o_lane + (long)t0 * o_tok;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                if (16 * nt + l16 < L)
-                    *reinterpret_cast<float4*>(op + 16 * nt * o_tok) = make_float4(O[nt][0], O[nt][1], O[nt][2], O[nt][3]);
+                if (16 * nt + l16 < L) {
+#pragma unroll
+                    for (int c = 0; c < NT; ++c)
+                        *reinterpret_cast<float4*>(op + 16 * nt * o_tok + 16 * c) =
+                            make_float4(O[c][nt][0], O[c][nt][1], O[c][nt][2], O[c][nt][3]);
+                }
             }
         } else if (copier) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
             // chunk's barrier
             if (nc + 1 < n_count)
                 dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
-                         BL::bytes, wv - 4, 4, lane);
+                         BL::bytes, wv - CW0, CW0, lane);
             wait_dma();
         }
     }
 
     if (chain && S_out) {
 #pragma unroll
-        for (int mk = 0; mk < NMK; ++mk)
+        for (int c = 0; c < NT; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                S_out[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] = Sacc[mk][j];
+            for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S_out[sbase + (long)(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16] = Sacc[c][mk][j];
     }
 }
 
@@ -770,7 +809,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         const int cnt = nch - n0 < R ? nch - n0 : R;
         hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
                            a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(512), 0, st, a.v,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(kChainThreads), 0, st, a.v,
                            a.w, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
