@@ -146,6 +146,23 @@ __device__ __forceinline__ Raw8<BF16> fill8(float x) {
     return r;
 }
 
+// r where the row is valid, else eight copies of x. Loads are issued unconditionally (from a
+// clamped, valid row) and replaced here at their first use: branch-free loads let the compiler
+// count the loads in flight exactly and wait only for the ones a use needs.
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> keep_or(const Raw8<BF16>& r, bool valid, float x) {
+    const Raw8<BF16> f = fill8<BF16>(x);
+    Raw8<BF16> o;
+#pragma unroll
+    for (int h = 0; h < (BF16 ? 1 : 2); ++h) {
+        o.u[h].x = valid ? r.u[h].x : f.u[h].x;
+        o.u[h].y = valid ? r.u[h].y : f.u[h].y;
+        o.u[h].z = valid ? r.u[h].z : f.u[h].z;
+        o.u[h].w = valid ? r.u[h].w : f.u[h].w;
+    }
+    return o;
+}
+
 template <bool BF16>
 __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* x) {
     if constexpr (BF16) {

@@ -137,9 +137,8 @@ struct PrepSmem {
 
 template <int DK, bool BF16, bool AS, bool BS>
 __global__ void __launch_bounds__(256, 2)
-prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
-            const void* __restrict__ alpha, const void* __restrict__ b, int B, int T, int H,
-            int n_first, int n_count, char* __restrict__ ws) {
+prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int B, int T, int H,
+            int n_first, int n_count, char* ws) {
     constexpr bool F16 = BF16;
     using PR = Prec<F16>;
     using E = typename PR::E;
@@ -181,32 +180,34 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int t = t0 + r;
     const bool valid = t < T;
     const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
-    // All loads are issued before any is used: alpha first (the scan needs it at once), then
-    // q, k, b; vmcnt counts in issue order, so waiting for alpha leaves the rest in flight.
+    // All loads are issued before any is used, unconditionally (rows past the end read row 0 of
+    // the sequence and are replaced at their first use): alpha first (the scan needs it at once),
+    // then q, k, b. vmcnt counts in issue order, so waiting for alpha leaves the rest in flight.
     Raw8<BF16> rq[NKS], rk[NKS], rb[NKS], ra[NKS];
     float lg[CPL];
-    float ras = 1.f;
+    float ras_raw = 1.f, rbs_raw = 0.f;
     if constexpr (AS) {
-        ras = valid ? load_one<BF16>(alpha, tok) : 1.f;
+        ras_raw = load_one<BF16>(alpha, tok);
     } else {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-            ra[s] = valid ? gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g) : fill8<BF16>(1.f);
+        for (int s = 0; s < NKS; ++s) ra[s] = gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g);
     }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
         const int c0 = 32 * s + 8 * g;
-        rq[s] = valid ? gload8<BF16>(q, tok * DK + c0) : fill8<BF16>(0.f);
-        rk[s] = valid ? gload8<BF16>(k, tok * DK + c0) : fill8<BF16>(0.f);
-        if constexpr (!BS) rb[s] = valid ? gload8<BF16>(b, tok * DK + c0) : fill8<BF16>(0.f);
+        rq[s] = gload8<BF16>(q, tok * DK + c0);
+        rk[s] = gload8<BF16>(k, tok * DK + c0);
+        if constexpr (!BS) rb[s] = gload8<BF16>(b, tok * DK + c0);
     }
-    const float rbs = BS ? (valid ? load_one<BF16>(b, tok) : 0.f) : 0.f;
+    if constexpr (BS) rbs_raw = load_one<BF16>(b, tok);
+    // keep every load above ahead of the scan: no load may be moved below this point
+    asm volatile("" ::: "memory");
     if constexpr (!AS) {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) unpack8<BF16>(ra[s], &lg[8 * s]);
+        for (int s = 0; s < NKS; ++s) unpack8<BF16>(keep_or<BF16>(ra[s], valid, 1.f), &lg[8 * s]);
     }
     if constexpr (AS) {
-        float x1 = lg2(ras);
+        float x1 = lg2(valid ? ras_raw : 1.f);
         x1 += row_shr<1>(x1);
         x1 += row_shr<2>(x1);
         x1 += row_shr<4>(x1);
@@ -276,13 +277,13 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         for (int s = 0; s < NKS; ++s) {
             const int c0 = 32 * s + 8 * g;
             float qx[8], kx[8], bx[8], X8[8], fX[8], fG[8], fTX[8], fCG[8];
-            unpack8<BF16>(rq[s], qx);
-            unpack8<BF16>(rk[s], kx);
+            unpack8<BF16>(keep_or<BF16>(rq[s], valid, 0.f), qx);
+            unpack8<BF16>(keep_or<BF16>(rk[s], valid, 0.f), kx);
             if constexpr (BS) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) bx[i] = rbs;
+                for (int i = 0; i < 8; ++i) bx[i] = valid ? rbs_raw : 0.f;
             } else {
-                unpack8<BF16>(rb[s], bx);
+                unpack8<BF16>(keep_or<BF16>(rb[s], valid, 0.f), bx);
             }
             lds_read8f(ldsX + I * DK + c0, X8);
             lds_read8f(tab + (0 + I) * DK + c0, fX);
@@ -327,13 +328,13 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
             for (int s = 0; s < NKS; ++s) {
                 const int c0 = 32 * s + 8 * g;
                 float qx[8], kx[8], bx[8], X8[8], em[8], qm[8], km[8];
-                unpack8<BF16>(rq[s], qx);
-                unpack8<BF16>(rk[s], kx);
+                unpack8<BF16>(keep_or<BF16>(rq[s], valid, 0.f), qx);
+                unpack8<BF16>(keep_or<BF16>(rk[s], valid, 0.f), kx);
                 if constexpr (BS) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) bx[i] = rbs;
+                    for (int i = 0; i < 8; ++i) bx[i] = valid ? rbs_raw : 0.f;
                 } else {
-                    unpack8<BF16>(rb[s], bx);
+                    unpack8<BF16>(keep_or<BF16>(rb[s], valid, 0.f), bx);
                 }
                 lds_read8f(ldsX + I * DK + c0, X8);
 #pragma unroll
@@ -498,7 +499,7 @@ prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         float* gc = reinterpret_cast<float*>(blob + BL::oGC);
         for (int c = threadIdx.x; c < DK; c += blockDim.x) gc[c] = tab[16 * DK + c];
         if constexpr (BS) {
-            if (g == 0) reinterpret_cast<float*>(blob + BL::oBeta)[r] = rbs;
+            if (g == 0) reinterpret_cast<float*>(blob + BL::oBeta)[r] = valid ? rbs_raw : 0.f;
         }
     }
 }
