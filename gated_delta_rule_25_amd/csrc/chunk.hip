@@ -149,52 +149,56 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
     Raw8<BF16> rq[NKS], rk[NKS], rb[NKS], ra[NKS], rv[NCV / 8], rw[NCV / 8];
     float ras = 1.f, rbs = 0.f;
     auto fetch = [&](int n, int part) {
+        // loads are unconditional (rows past the end read row 0 of the sequence); the values are
+        // replaced at their first use, so the compiler can count the loads in flight exactly
         const int t = n * CH + r;
-        const bool valid = t < T;
-        const long tok = ((long)bb * T + (valid ? t : 0)) * H + hh;
+        const long tok = ((long)bb * T + (t < T ? t : 0)) * H + hh;
         if (part == 0) {
             if constexpr (AS) {
-                ras = valid ? load_one<BF16>(alpha, tok) : 1.f;
+                ras = load_one<BF16>(alpha, tok);
             } else {
 #pragma unroll
                 for (int s = 0; s < NKS; ++s)
-                    ra[s] = valid ? gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g) : fill8<BF16>(1.f);
+                    ra[s] = gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g);
             }
         } else if (part == 1) {
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                rq[s] = valid ? gload8<BF16>(q, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+                rq[s] = gload8<BF16>(q, tok * DK + 32 * s + 8 * g);
             const int v0 = tile * DVT + g * NCV;
 #pragma unroll
             for (int u = 0; u < NCV / 8; ++u) {
-                rv[u] = valid ? gload8<BF16>(v, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
-                if constexpr (!BS) rw[u] = valid ? gload8<BF16>(w, tok * DV + v0 + 8 * u) : fill8<BF16>(0.f);
+                rv[u] = gload8<BF16>(v, tok * DV + v0 + 8 * u);
+                if constexpr (!BS) rw[u] = gload8<BF16>(w, tok * DV + v0 + 8 * u);
             }
         } else if (part == 2) {
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                rk[s] = valid ? gload8<BF16>(k, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+                rk[s] = gload8<BF16>(k, tok * DK + 32 * s + 8 * g);
         } else {
             if constexpr (BS) {
-                rbs = valid ? load_one<BF16>(b, tok) : 0.f;
+                rbs = load_one<BF16>(b, tok);
             } else {
 #pragma unroll
                 for (int s = 0; s < NKS; ++s)
-                    rb[s] = valid ? gload8<BF16>(b, tok * DK + 32 * s + 8 * g) : fill8<BF16>(0.f);
+                    rb[s] = gload8<BF16>(b, tok * DK + 32 * s + 8 * g);
             }
         }
     };
 
+    // o of this sequence as a buffer: rows past the end are dropped, so stores need no branch
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + (long)bb * T * H * DV, (unsigned)T * H * DV * 4u);
     const int nch = (T + CH - 1) / CH;
     for (int part = 0; part < 4; ++part) fetch(0, part);
     for (int n = 0; n < nch; ++n) {
         const int t0 = n * CH;
         const int L = min(CH, T - t0);
+        const bool vrow = t0 + r < T;  // this lane's row exists
 
         // ---------------- A: log2-decay and its scan over the block's 16 rows ----------------
         float lg[CPL];
         if constexpr (AS) {
-            float x1 = lg2(ras);
+            float x1 = lg2(vrow ? ras : 1.f);
             x1 += row_shr<1>(x1);
             x1 += row_shr<2>(x1);
             x1 += row_shr<4>(x1);
@@ -203,7 +207,7 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
             for (int e = 0; e < CPL; ++e) lg[e] = x1;
         } else {
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) unpack8<BF16>(ra[s], &lg[8 * s]);
+            for (int s = 0; s < NKS; ++s) unpack8<BF16>(keep_or<BF16>(ra[s], vrow, 1.f), &lg[8 * s]);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) lg[e] = lg2(lg[e]);
 #pragma unroll
@@ -269,13 +273,13 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
             for (int s = 0; s < NKS; ++s) {
                 const int c0 = 32 * s + 8 * g;
                 float qx[8], kx[8], bx[8], X8[8], fX[8], fG[8], fTX[8], fCG[8];
-                unpack8<BF16>(rq[s], qx);
-                unpack8<BF16>(rk[s], kx);
+                unpack8<BF16>(keep_or<BF16>(rq[s], vrow, 0.f), qx);
+                unpack8<BF16>(keep_or<BF16>(rk[s], vrow, 0.f), kx);
                 if constexpr (BS) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) bx[i] = rbs;
+                    for (int i = 0; i < 8; ++i) bx[i] = vrow ? rbs : 0.f;
                 } else {
-                    unpack8<BF16>(rb[s], bx);
+                    unpack8<BF16>(keep_or<BF16>(rb[s], vrow, 0.f), bx);
                 }
                 lds_read8f(ldsX + I * DK + c0, X8);
                 lds_read8f(tab + (0 + I) * DK + c0, fX);
@@ -410,12 +414,12 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
 #pragma unroll
                 for (int u = 0; u < NCV / 8; ++u) {
                     float vx[8], wx[8];
-                    unpack8<BF16>(rv[u], vx);
+                    unpack8<BF16>(keep_or<BF16>(rv[u], vrow, 0.f), vx);
                     if constexpr (BS) {
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) wx[i] = rbs;
+                        for (int i = 0; i < 8; ++i) wx[i] = vrow ? rbs : 0.f;
                     } else {
-                        unpack8<BF16>(rw[u], wx);
+                        unpack8<BF16>(keep_or<BF16>(rw[u], vrow, 0.f), wx);
                     }
                     float4* p = reinterpret_cast<float4*>(up + 8 * u);
                     p[0] = make_float4(wx[0] * vx[0], wx[1] * vx[1], wx[2] * vx[2], wx[3] * vx[3]);
@@ -610,11 +614,9 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
                     PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
                 }
-                const int row = 16 * nt + l16;
-                if (row < L) {
-                    float* op = o + (((long)bb * T + t0 + row) * H + hh) * DV + tile * DVT + 16 * wv + 4 * g;
-                    *reinterpret_cast<float4*>(op) = make_float4(O[nt][0], O[nt][1], O[nt][2], O[nt][3]);
-                }
+                const unsigned row = (unsigned)(t0 + 16 * nt + l16);
+                store4(rs_o, ((row * H + hh) * DV + tile * DVT + 16 * wv + 4 * g) * 4u, O[nt][0], O[nt][1], O[nt][2],
+                       O[nt][3]);
             }
             // S <- Diag(gamma_last) S + K_bar^T Delta
 #pragma unroll
@@ -669,14 +671,16 @@ hipError_t launch_flags(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool chunk_supported(int DK, int DV, bool bf16) {
+bool chunk_supported(int T, int H, int DK, int DV, bool bf16) {
     if (DK != DV) return false;
+    // o of one sequence is addressed with 32-bit byte offsets
+    if ((long long)T * H * DV * 4 >= (1ll << 32)) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
     return DK == 32 || DK == 64;  // fp32 operand tiles of d = 128 exceed the LDS budget
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s) {
-    if (!chunk_supported(a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
+    if (!chunk_supported(a.T, a.H, a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
     if (a.bf16) {
         switch (a.DK) {
             case 32: return launch_flags<32, true>(a, s);

@@ -28,6 +28,18 @@ __device__ __forceinline__ void lds_barrier() {
 }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Raw buffer over [base, base + bytes): loads at byte offsets past the end return zero and
+// stores there are dropped, so a ragged last chunk needs no branch (and the compiler can count
+// the memory operations in flight exactly).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, unsigned off, float a, float b, float c, float d) {
+    const u32x4 x = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, 0);
+}
+
 // ---- operand precision policies ---------------------------------------------------------
 template <bool F16>
 struct Prec;

@@ -90,10 +90,6 @@ __device__ __forceinline__ void store8_rows(E* p, const float* x) {
     }
 }
 
-// Raw buffer over [base, base + bytes): loads at offsets past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 
 // Scheduling hint for a run of P products that each read one LDS operand fragment: issue the
 // first LA reads, then alternate MPR products (those sharing one read operand) and one read, so
@@ -566,9 +562,11 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     const bool copier = wv >= CW0;
     const int col0 = tile * DVT + (chain ? wv : 0) * 16 * NT;  // this wave's first state column
     const char* blobs = ws + (size_t)bh * n_count * BL::bytes;
-    // o row of token l16 of chunk 0 at this lane's four columns of tile 0; token t is t * H * DV on
-    float* const o_lane = o + (((long)bb * T + l16) * H + hh) * DV + col0 + 4 * g;
-    const long o_tok = (long)H * DV;
+    // o of this sequence as a buffer (rows past the end are dropped): byte offset of token row
+    // l16 of chunk 0 at this lane's four columns of tile 0, and the byte stride of one token
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + (long)bb * T * H * DV, (unsigned)T * H * DV * 4u);
+    const unsigned o_lane = (((unsigned)l16 * H + hh) * DV + col0 + 4 * g) * 4u;
+    const unsigned o_tok = (unsigned)H * DV * 4u;
 
     f4 Sacc[NT][NMK];
     const long sbase = (long)bh * DK * DV;
@@ -591,8 +589,8 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     constexpr int LPR = ROW * IES / 16;      // lanes per slot row in a copy
     constexpr int RPI = 64 / LPR;            // rows per copy instruction
     const long seq = (long)bb * T * H;       // first token row of this sequence
-    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(static_cast<const char*>(v) + seq * DV * IES, T * H * DV * IES);
-    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(static_cast<const char*>(BS ? v : w) + seq * DV * IES, T * H * DV * IES);
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(static_cast<const char*>(v) + seq * DV * IES, (unsigned)T * H * DV * IES);
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(static_cast<const char*>(BS ? v : w) + seq * DV * IES, (unsigned)T * H * DV * IES);
     char* vw_lds = svw + (chain ? wv : 0) * 2 * SM::VWB;
     const Raw* v_l = reinterpret_cast<const Raw*>(vw_lds);
     const Raw* w_l = reinterpret_cast<const Raw*>(vw_lds + SM::VWB);
@@ -646,8 +644,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
 
         if (chain) {
             // D' starts as U = w v, from this wave's slot. Its copy was issued before the previous
-            // chunk's o stores (4 NT of them: all rows of a chunk that is not the last are valid),
-            // so this wait covers it and leaves those stores in flight.
+            // chunk's 4 NT o stores, so this wait covers it and leaves those stores in flight.
             if (nc == 0) {
                 wait_dma();
             } else {
@@ -748,17 +745,14 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                 }
             }
             if constexpr (F16) lookahead_schedule<6 + 2 * NMK, 6, NT>();
-            // o rows of this chunk: four consecutive columns per lane and tile, 16-byte stores
-            float* const op = o_lane + (long)t0 * o_tok;
+            // o rows of this chunk: four consecutive columns per lane and tile, one 16-byte store
+            // each (always 4 NT stores per chunk; rows past the end are dropped by the buffer)
+            const unsigned op = o_lane + (unsigned)t0 * o_tok;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                if (16 * nt + l16 < L) {
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                    for (int c = 0; c < NT; ++c)
-                        *reinterpret_cast<float4*>(op + 16 * nt * o_tok + 16 * c) =
-                            make_float4(O[c][nt][0], O[c][nt][1], O[c][nt][2], O[c][nt][3]);
-                }
-            }
+                for (int c = 0; c < NT; ++c)
+                    store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0], O[c][nt][1], O[c][nt][2], O[c][nt][3]);
         } else if (copier) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
             // chunk's barrier
@@ -832,8 +826,8 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
 
 bool split_supported(int T, int H, int DK, int DV, bool bf16) {
     if (DK != DV) return false;
-    // the chain kernel addresses one sequence's v, w rows with 32-bit byte offsets
-    if ((long long)T * H * DV * (bf16 ? 2 : 4) >= (1ll << 31)) return false;
+    // the chain kernel addresses one sequence's v, w and o rows with 32-bit byte offsets
+    if ((long long)T * H * DV * 4 >= (1ll << 32)) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
     return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
 }

@@ -167,7 +167,7 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                                 range_of(S0, sz.state * 4), range_of(o, sz.vw * 4), range_of(S_out, sz.state * 4)};
         for (const Range& r : others)
             if (overlap(rws, r)) return GDN2_ERR_ALIAS;
-    } else if (!gdn2::chunk_supported(d_k, d_v, bf16)) {
+    } else if (!gdn2::chunk_supported(T, H, d_k, d_v, bf16)) {
         return GDN2_ERR_UNSUPPORTED;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);

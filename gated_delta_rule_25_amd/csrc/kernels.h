@@ -34,7 +34,7 @@ struct ChunkArgs {
 // Single-kernel path (no workspace). Returns hipErrorNotSupported when it does not cover
 // the arguments.
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
-bool chunk_supported(int DK, int DV, bool bf16);
+bool chunk_supported(int T, int H, int DK, int DV, bool bf16);
 
 // Two-kernel path (prep + chain) through a workspace ring of per-chunk operand blobs.
 // Workspace = state buffer (B*H*DK*DV fp32) + R chunk slots of split_chunk_bytes each.

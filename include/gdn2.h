@@ -91,8 +91,7 @@ enum {
  *    over every (b, h, chunk), computes each chunk's decay-scaled factors, its 64x64 Gram
  *    products and the UT inverse T, and stores them as one operand block per chunk in the
  *    workspace; a chain kernel then runs the state recurrence chunk by chunk from those blocks.
- *    Supported: bf16 with d in {32, 64, 128}, fp32 with d = 32, and T*H*d_v*elem_size < 2^31
- *    bytes per sequence. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v] first
+ *    Supported: bf16 with d in {32, 64, 128}, fp32 with d = 32. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v] first
  *    when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand blocks.
  *    R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with
  *    fewer slots than chunks the two kernels alternate over rounds of R chunks. The buffer must
@@ -103,7 +102,9 @@ enum {
  *    per (b, h, 64-column tile of the state) computing each chunk's factors and then its part
  *    of the state recurrence. Supported: bf16 with d in {32, 64, 128}, fp32 with d in {32, 64};
  *    other sizes return GDN2_ERR_UNSUPPORTED.
- * d_k must equal d_v. Any flags above.
+ * d_k must equal d_v, and one sequence's o must stay below 4 GiB (T*H*d_v*4 < 2^32 bytes: the
+ * kernels address a sequence's rows with 32-bit offsets), else GDN2_ERR_UNSUPPORTED. Any flags
+ * above.
  */
 gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
                            const void *b, const void *w, const float *S0, float *o,

@@ -76,6 +76,28 @@ def test_chunk_rejects_bad_arguments(lib):
     assert chunk_call(lib, p, flags=2) == 3  # beta scalar but w given
 
 
+def test_chunk_rejects_sequences_beyond_32bit_offsets(lib):
+    # o of one sequence (T*H*d_v fp32) must stay below 4 GiB: both prefill schedules address a
+    # sequence's rows with 32-bit byte offsets. Pointers 8 GiB apart so nothing overlaps.
+    far = [P(0x200000000 * (i + 1)) for i in range(9)]
+    T = 600_000  # 600000 * 16 * 128 * 4 B = 4.9 GB of o per sequence
+    assert chunk_call(lib, far, B=1, T=T, H=16, dk=128, dv=128) == 3
+    ws = P(0x200000000 * 20)
+    assert chunk_call(lib, far, B=1, T=T, H=16, dk=128, dv=128, ws=ws, wsb=1 << 40) == 3
+    assert lib.gdn2_chunk_fwd_workspace_bytes(1, T, 16, 128, 128, 0, 0) == 0
+
+
+def test_workspace_query_is_state_plus_one_slot_per_chunk(lib):
+    q = lib.gdn2_chunk_fwd_workspace_bytes
+    state = 8 * 16 * 128 * 128 * 4
+    one = q(8, 64, 16, 128, 128, 0, 0)
+    per_chunk = one - state
+    assert per_chunk > 0 and per_chunk % 256 == 0
+    assert q(8, 4096, 16, 128, 128, 0, 0) == state + 64 * per_chunk
+    assert q(8, 4097, 16, 128, 128, 0, 0) == state + 65 * per_chunk  # ragged last chunk
+    assert q(8, 4096, 16, 128, 128, 1, 0) == 0  # fp32 at d = 128: no two-kernel path
+
+
 def test_chunk_rejects_partial_state_alias(lib):
     p = list(FAKE[:9])
     p[6] = P(0x900000)
