@@ -43,14 +43,17 @@ struct Blob {
     static constexpr int PAD = 4;
     static constexpr int DKP = DK + PAD;
     static constexpr int CHP = CH + PAD;
-    static constexpr int oQh = 0;                       // E [64][DKP]
-    static constexpr int oEn = oQh + CH * DKP * ES;     // E [64][DKP]
-    static constexpr int oKbT = oEn + CH * DKP * ES;    // E [DK][CHP]
-    static constexpr int oP = oKbT + DK * CHP * ES;     // E [64][CHP]
-    static constexpr int oTm = oP + CH * CHP * ES;      // E [64][CHP]
-    static constexpr int oGC = oTm + CH * CHP * ES;     // float [DK]
-    static constexpr int oBeta = oGC + DK * 4;          // float [64] scalar beta per row (scalar-beta gates)
-    static constexpr int bytes = (oBeta + CH * 4 + 255) / 256 * 256;
+    // The state recurrence alone needs the prefix [En .. beta]; the outputs also need P and Q_hat.
+    static constexpr int oEn = 0;                       // E [64][DKP]   -E_hat
+    static constexpr int oKbT = oEn + CH * DKP * ES;    // E [DK][CHP]   K_bar^T
+    static constexpr int oTm = oKbT + DK * CHP * ES;    // E [64][CHP]   T
+    static constexpr int oGC = oTm + CH * CHP * ES;     // float [DK]    gamma_last
+    static constexpr int oBeta = oGC + DK * 4;          // float [64]    scalar beta per row (scalar-beta gates)
+    static constexpr int stateBytes = oBeta + CH * 4;
+    static constexpr int oP = stateBytes;               // E [64][CHP]   P
+    static constexpr int oQh = oP + CH * CHP * ES;      // E [64][DKP]   Q_hat
+    static constexpr int bytes = (oQh + CH * DKP * ES + 255) / 256 * 256;
+    static_assert(stateBytes % 16 == 0, "16-byte copies");
 };
 
 // Copy `bytes` (a multiple of 16) from global to LDS with `nw` wavefronts (this one is `cw`),
@@ -117,17 +120,18 @@ struct PrepSmem {
     static constexpr int oTot = 0;                      // float [4][DK]
     static constexpr int oX = oTot + 4 * DK * 4;        // float [4][DK]
     static constexpr int oTab = oX + 4 * DK * 4;        // float [kTabs][DK]
-    static constexpr int oOut = oTab + kTabs * DK * 4;  // K_bar^T, P, T exactly as in the blob
+    static constexpr int oOut = oTab + kTabs * DK * 4;  // K_bar^T, T (as in the blob), then P
     static constexpr int oKbT = oOut;
-    static constexpr int oP = oKbT + DK * CHP * ES;
-    static constexpr int oTm = oP + CH * CHP * ES;
-    static constexpr int outBytes = (BL::oGC - BL::oKbT);
+    static constexpr int oTm = oKbT + DK * CHP * ES;
+    static constexpr int oP = oTm + CH * CHP * ES;
+    static constexpr int out1Bytes = BL::oGC - BL::oKbT;  // K_bar^T and T
+    static constexpr int outBytes = out1Bytes + CH * CHP * ES;
     static constexpr int KTP = DK + Prec<F16>::kPad;    // 16-byte rows for 16-byte accesses
     static constexpr int oKt = oOut + outBytes;         // E [48][KTP]
     static constexpr int oA = oKt + 48 * KTP * ES;      // E [64][CHP] A below the diagonal
     static constexpr int oAd = oA + CH * CHP * ES;      // float [4][16][16] diagonal A^T
     static constexpr int bytes = oAd + 4 * 256 * 4;
-    static_assert(BL::oP - BL::oKbT == DK * CHP * ES && BL::oTm - BL::oP == CH * CHP * ES, "layout");
+    static_assert(BL::oTm - BL::oKbT == DK * CHP * ES && out1Bytes == (DK + CH) * CHP * ES, "layout");
     static_assert(bytes <= 80 * 1024, "prep LDS must allow two workgroups per CU");
 };
 
@@ -487,11 +491,14 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     }
     lds_barrier();
 
-    // ---- out: K_bar^T, P, T (contiguous in LDS and in the blob) and gamma_last ----
+    // ---- out: K_bar^T and T (contiguous in LDS and in the blob), P, gamma_last ----
     {
         const uint4* src = reinterpret_cast<const uint4*>(smem + SM::oOut);
         uint4* dst = reinterpret_cast<uint4*>(blob + BL::oKbT);
-        for (int i = threadIdx.x; i < SM::outBytes / 16; i += blockDim.x) dst[i] = src[i];
+        for (int i = threadIdx.x; i < SM::out1Bytes / 16; i += blockDim.x) dst[i] = src[i];
+        const uint4* srcP = reinterpret_cast<const uint4*>(smem + SM::oP);
+        uint4* dstP = reinterpret_cast<uint4*>(blob + BL::oP);
+        for (int i = threadIdx.x; i < CH * CHP * (int)sizeof(E) / 16; i += blockDim.x) dstP[i] = srcP[i];
         float* gc = reinterpret_cast<float*>(blob + BL::oGC);
         for (int c = threadIdx.x; c < DK; c += blockDim.x) gc[c] = tab[16 * DK + c];
         if constexpr (BS) {
@@ -527,12 +534,32 @@ struct ChainSmem {
 // LDS while the chain waves work on the current one (one wave per SIMD when NT = 2). Each chain
 // wave copies its own v, w columns into a private LDS slot, one chunk ahead, so no barrier guards
 // them.
-template <int DK, int DVT, bool BF16, bool BS>
+// Where one chain launch reads and writes the state, and which chunks each workgroup runs.
+// Workgroup (seg, b·h, tile) runs chunks [first + seg·seg_len, min(first + (seg+1)·seg_len, end))
+// of its sequence; the block of chunk n sits in ring slot n - first.
+struct ChainIO {
+    const void* v;
+    const void* w;
+    float* o;
+    const char* ws;  // blocks [b·h][ring]
+    int ring, first, end, seg_len, nseg;
+    int B, T, H, DV;
+    const float* S_in;  // initial state of (bh, seg): S_in + bh·in_bh + seg·in_seg, rows of in_ld
+    long in_bh, in_seg;
+    int in_ld;
+    float* S_out;  // final state: S_out + bh·out_bh + seg·out_seg, rows of out_ld
+    long out_bh, out_seg;
+    int out_ld;
+    int out_last;  // only the last segment writes S_out
+};
+
+// STATE = true: the state recurrence alone, for the segment transitions of a long sequence. Tiles
+// below DV / DVT run it from a zero state with the true U (their final state is the segment's
+// inhomogeneous part Psi); tiles above run it with U = 0 from the identity on their columns (the
+// transition Phi). No o, and only the block prefix the recurrence reads is copied.
+template <int DK, int DVT, bool BF16, bool BS, bool STATE>
 __global__ void __launch_bounds__(kChainThreads, 1)
-chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
-             const float* S_in, float* __restrict__ o,
-             float* S_out, int B, int T, int H, int DV, int n_first, int n_count,
-             const char* __restrict__ ws) {
+chain_kernel(const ChainIO io) {
     constexpr bool F16 = BF16;
     using PR = Prec<F16>;
     using E = typename PR::E;
@@ -543,6 +570,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     constexpr int NT = SM::NT, NWC = SM::NWC, CW0 = SM::CW0;
     constexpr int NKS = DK / 32, NMK = DK / 16;
     constexpr int DKP = BL::DKP, CHP = BL::CHP;
+    constexpr int COPY = STATE ? BL::stateBytes : BL::bytes;  // bytes of each block copied to LDS
 
     // Two arrays: the block buffers and the v/w slots. Separate objects let the compiler see that
     // a v/w copy in flight cannot alias the block reads that follow it, so it does not wait for
@@ -550,18 +578,31 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     __shared__ __attribute__((aligned(16))) char smem[SM::oVW];
     __shared__ __attribute__((aligned(16))) char svw[SM::bytes - SM::oVW];
 
+    const int T = io.T, H = io.H, DV = io.DV;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-    const int tiles = DV / DVT;
-    const int x = blockIdx.x;
+    const int vt = DV / DVT;                  // value tiles
+    const int tiles = vt + (STATE ? DK / DVT : 0);
+    const int BH = io.B * H, BHp = (BH + 7) / 8 * 8;
+    const int seg = blockIdx.x / (BHp * tiles);
+    const int x = blockIdx.x % (BHp * tiles);
     const int grp = x / (8 * tiles), within = x % (8 * tiles);
     const int tile = within / 8;
     const int bh = grp * 8 + (within % 8);
-    if (bh >= B * H) return;
+    if (bh >= BH || seg >= io.nseg) return;
     const int hh = bh % H, bb = bh / H;
+    const int c_begin = io.first + seg * io.seg_len;
+    const int c_end = min(c_begin + io.seg_len, io.end);
+    const int n_count = c_end - c_begin;
+    if (n_count <= 0) return;
+    const bool phi = STATE && tile >= vt;     // transition tile: U = 0, identity start
     const bool chain = wv < NWC;
     const bool copier = wv >= CW0;
-    const int col0 = tile * DVT + (chain ? wv : 0) * 16 * NT;  // this wave's first state column
-    const char* blobs = ws + (size_t)bh * n_count * BL::bytes;
+    // this wave's first state column: in v space, or in k space for a transition tile
+    const int col0 = (phi ? (tile - vt) : tile) * DVT + (chain ? wv : 0) * 16 * NT;
+    const char* blobs = io.ws + ((size_t)bh * io.ring + (c_begin - io.first)) * BL::bytes;
+    float* const o = io.o;
+    const void* const v = io.v;
+    const void* const w = io.w;
     // o of this sequence as a buffer (rows past the end are dropped): byte offset of token row
     // l16 of chunk 0 at this lane's four columns of tile 0, and the byte stride of one token
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + (long)bb * T * H * DV, (unsigned)T * H * DV * 4u);
@@ -569,15 +610,22 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     const unsigned o_tok = (unsigned)H * DV * 4u;
 
     f4 Sacc[NT][NMK];
-    const long sbase = (long)bh * DK * DV;
+    const float* s_in = io.S_in ? io.S_in + bh * io.in_bh + seg * io.in_seg : nullptr;
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
         for (int mk = 0; mk < NMK; ++mk)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                Sacc[c][mk][j] = (chain && S_in) ? S_in[sbase + (long)(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16]
-                                                 : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * mk + 4 * g + j, col = col0 + 16 * c + l16;
+                float x0 = 0.f;
+                if (phi) {
+                    x0 = row == col ? 1.f : 0.f;
+                } else if (chain && s_in) {
+                    x0 = s_in[(long)row * io.in_ld + col];
+                }
+                Sacc[c][mk][j] = x0;
+            }
 
     // v and w rows of this wave's columns for one chunk, copied into the wave's LDS slot through
     // buffer resources over this sequence's rows: rows past the sequence end fall outside the
@@ -621,14 +669,14 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
     };
 
     if (copier) {
-        dma_flat(blobs, smem + SM::oBuf0, BL::bytes, wv - CW0, CW0, lane);
+        dma_flat(blobs, smem + SM::oBuf0, COPY, wv - CW0, CW0, lane);
         wait_dma();
-    } else if (chain) {
-        dma_vw(n_first);
+    } else if (chain && !phi) {
+        dma_vw(c_begin);
     }
 
     for (int nc = 0; nc < n_count; ++nc) {
-        const int n = n_first + nc;
+        const int n = c_begin + nc;
         const int t0 = n * CH;
         const int L = min(CH, T - t0);
         char* buf = smem + ((nc & 1) ? SM::oBuf1 : SM::oBuf0);
@@ -645,7 +693,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
         if (chain) {
             // D' starts as U = w v, from this wave's slot. Its copy was issued before the previous
             // chunk's 4 NT o stores, so this wait covers it and leaves those stores in flight.
-            if (nc == 0) {
+            if (nc == 0 || STATE) {
                 wait_dma();
             } else {
                 wait_vm_but<4 * NT>();
@@ -659,7 +707,7 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * mt + 4 * g + j, slot = 16 * mt + 4 * j + g, cl = 16 * c + l16;
                         const float ww = BS ? betaL[row] : raw_f(w_l[slot * ROW + cl]);
-                        D[c][mt][j] = ww * raw_f(v_l[slot * ROW + cl]);
+                        D[c][mt][j] = phi ? 0.f : ww * raw_f(v_l[slot * ROW + cl]);
                     }
             float4 gcv[NMK];  // gamma_last of this lane's state rows
 #pragma unroll
@@ -679,18 +727,20 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
                     const E* er_ = &En[(16 * mt + l16) * DKP + 32 * s];
-                    const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
                     const Frag ef = PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g);
 #pragma unroll
                     for (int c = 0; c < NT; ++c) PR::mma(D[c][mt], ef, Sf[c][s]);
-                    const Frag qf = PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g);
+                    if constexpr (!STATE) {
+                        const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
+                        const Frag qf = PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g);
 #pragma unroll
-                    for (int c = 0; c < NT; ++c) PR::mma(O[c][mt], Sf[c][s], qf);
+                        for (int c = 0; c < NT; ++c) PR::mma(O[c][mt], Sf[c][s], qf);
+                    }
                 }
             }
-            if constexpr (F16) lookahead_schedule<8 * NKS, 6, NT>();
+            if constexpr (F16) lookahead_schedule<(STATE ? 4 : 8) * NKS, 6, NT>();
             // the next chunk's v, w into this wave's slot, now that its reads are long done
-            if (nc + 1 < n_count) dma_vw(n + 1);
+            if (nc + 1 < n_count && !phi) dma_vw(n + 1);
             // Delta = T D'
             Frag Df[NT][2];
 #pragma unroll
@@ -717,14 +767,16 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                 for (int s2 = 0; s2 < 2; ++s2) Df[c][s2] = stack(Dl[c][2 * s2], Dl[c][2 * s2 + 1]);
             // O^T += Delta^T P^T and S <- Diag(gamma_last) S + K_bar^T Delta: independent
             // products on one pipelined stream of operand reads
+            if constexpr (!STATE) {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
+                for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-                for (int s2 = 0; s2 <= nt / 2; ++s2) {
-                    const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
-                    const Frag pf = PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g);
+                    for (int s2 = 0; s2 <= nt / 2; ++s2) {
+                        const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
+                        const Frag pf = PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g);
 #pragma unroll
-                    for (int c = 0; c < NT; ++c) PR::mma(O[c][nt], Df[c][s2], pf);
+                        for (int c = 0; c < NT; ++c) PR::mma(O[c][nt], Df[c][s2], pf);
+                    }
                 }
             }
 #pragma unroll
@@ -744,47 +796,116 @@ chain_kernel(const void* __restrict__ v, const void* __restrict__ w,
                     for (int c = 0; c < NT; ++c) PR::mma(Sacc[c][mk], kf, Df[c][s2]);
                 }
             }
-            if constexpr (F16) lookahead_schedule<6 + 2 * NMK, 6, NT>();
-            // o rows of this chunk: four consecutive columns per lane and tile, one 16-byte store
-            // each (always 4 NT stores per chunk; rows past the end are dropped by the buffer)
-            const unsigned op = o_lane + (unsigned)t0 * o_tok;
+            if constexpr (F16) lookahead_schedule<(STATE ? 0 : 6) + 2 * NMK, 6, NT>();
+            if constexpr (!STATE) {
+                // o rows of this chunk: four consecutive columns per lane and tile, one 16-byte
+                // store each (always 4 NT stores per chunk; rows past the end are dropped)
+                const unsigned op = o_lane + (unsigned)t0 * o_tok;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int c = 0; c < NT; ++c)
-                    store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0], O[c][nt][1], O[c][nt][2], O[c][nt][3]);
+                    for (int c = 0; c < NT; ++c)
+                        store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0], O[c][nt][1], O[c][nt][2],
+                               O[c][nt][3]);
+            }
         } else if (copier) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
             // chunk's barrier
             if (nc + 1 < n_count)
-                dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1),
-                         BL::bytes, wv - CW0, CW0, lane);
+                dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1), COPY,
+                         wv - CW0, CW0, lane);
             wait_dma();
         }
     }
 
-    if (chain && S_out) {
+    if (chain && io.S_out && (!io.out_last || seg == io.nseg - 1)) {
+        float* s_out = io.S_out + bh * io.out_bh + seg * io.out_seg + (phi ? DV : 0);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
 #pragma unroll
             for (int mk = 0; mk < NMK; ++mk)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    S_out[sbase + (long)(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16] = Sacc[c][mk][j];
+                    s_out[(long)(16 * mk + 4 * g + j) * io.out_ld + col0 + 16 * c + l16] = Sacc[c][mk][j];
     }
 }
 
-template <int DK, bool BF16>
-constexpr bool split_fits() {
-    constexpr int DVT = DK < 64 ? DK : 64;
-    return ChainSmem<DK, DVT, BF16>::fits;
+// ------------------------------------------------------------------------------------------
+// segment scan: S_in[g + 1] = Phi_g S_in[g] + Psi_g, for one (b, h) and 32 state columns, fp32
+// psiphi: [b·h][G - 1][DK][DV + DK] (Psi in columns 0..DV-1, Phi in DV..DV+DK-1)
+// sseg:   [b·h][G][DK][DV], sseg[·][0] = S0 (or zeros)
+template <int DK>
+__global__ void __launch_bounds__(256, 1)
+scan_kernel(const float* S0, const float* __restrict__ psiphi, float* __restrict__ sseg, int G, int DV) {
+    constexpr int CW = 32;          // state columns per workgroup
+    constexpr int SETS = 256 / DK;  // column sets per row
+    constexpr int CPT = CW / SETS;  // columns per thread
+    __shared__ float cur[DK][CW + 1];
+    const int cols = DV / CW;
+    const int bh = blockIdx.x / cols, c0 = (blockIdx.x % cols) * CW;
+    const int i = threadIdx.x % DK, cb = (threadIdx.x / DK) * CPT;
+    const int ld = DV + DK;
+    float* out = sseg + (long)bh * G * DK * DV;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+        const float x = S0 ? S0[((long)bh * DK + i) * DV + c0 + cb + e] : 0.f;
+        cur[i][cb + e] = x;
+        out[(long)i * DV + c0 + cb + e] = x;
+    }
+    __syncthreads();
+    for (int gg = 0; gg + 1 < G; ++gg) {
+        const float* pp = psiphi + ((long)bh * (G - 1) + gg) * DK * ld + (long)i * ld;
+        float acc[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) acc[e] = pp[c0 + cb + e];
+        for (int k = 0; k < DK; k += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(pp + DV + k);
+#pragma unroll
+            for (int e = 0; e < CPT; ++e)
+                acc[e] += f.x * cur[k][cb + e] + f.y * cur[k + 1][cb + e] + f.z * cur[k + 2][cb + e] +
+                          f.w * cur[k + 3][cb + e];
+        }
+        __syncthreads();  // every read of cur is done
+        out += (long)DK * DV;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            cur[i][cb + e] = acc[e];
+            out[(long)i * DV + c0 + cb + e] = acc[e];
+        }
+        __syncthreads();
+    }
+}
+
+// Segments for a long sequence with few (b, h): enough that the chain fills the chip, each at
+// least 16 chunks long. nseg = 1 means no segmentation.
+struct SplitPlan {
+    int nseg, seg_len;
+    size_t extra_bytes;  // Psi/Phi and the segment start states
+};
+
+SplitPlan split_plan(int B, int T, int H, int DK, int DV) {
+    const int nch = (T + CH - 1) / CH;
+    const int DVT = DK < 64 ? DK : 64;
+    const long wgs = (long)B * H * (DV / DVT);
+    SplitPlan p{1, nch, 0};
+    if (wgs < 256 && nch >= 32) {
+        int g = (int)((256 + wgs - 1) / wgs);
+        if (g > nch / 16) g = nch / 16;
+        if (g >= 2) {
+            p.seg_len = (nch + g - 1) / g;
+            p.nseg = (nch + p.seg_len - 1) / p.seg_len;
+            const size_t BH = (size_t)B * H;
+            p.extra_bytes = (BH * (p.nseg - 1) * DK * (DV + DK) + BH * p.nseg * DK * DV) * 4;
+        }
+    }
+    return p;
 }
 
 template <int DK, bool BF16, bool AS, bool BS>
 hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
     using BL = Blob<DK, BF16>;
-    const int BH = a.B * a.H;
+    const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
     const int nch = (a.T + CH - 1) / CH;
     const size_t state_bytes = (size_t)BH * a.DK * a.DV * 4;
     float* Sbuf = a.S_out;
@@ -793,19 +914,44 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         Sbuf = reinterpret_cast<float*>(ws);
         ws += state_bytes;
     }
-    const size_t ring = a.workspace_bytes - (a.S_out ? 0 : state_bytes);
+    const size_t avail = a.workspace_bytes - (a.S_out ? 0 : state_bytes);
     const size_t per_chunk = (size_t)BH * BL::bytes;
-    int R = (int)(ring / per_chunk);
+    const int tiles = a.DV / DVT;
+    const SplitPlan plan = split_plan(a.B, a.T, a.H, DK, a.DV);
+    const long ld = DK;  // state rows are DK long in k, DV in v
+    if (plan.nseg > 1 && avail >= (size_t)nch * per_chunk + plan.extra_bytes) {
+        // segments: prep over all chunks; each segment's transition (Psi, Phi) from the state
+        // recurrence alone; a scan for every segment's start state; then all segments at once
+        const int G = plan.nseg;
+        float* psiphi = reinterpret_cast<float*>(ws + (size_t)nch * per_chunk);
+        float* sseg = psiphi + (size_t)BH * (G - 1) * DK * (a.DV + DK);
+        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k, a.alpha,
+                           a.b, a.B, a.T, a.H, 0, nch, ws);
+        const ChainIO tr{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G - 1, a.B, a.T, a.H, a.DV,
+                         nullptr, 0, 0, a.DV,
+                         psiphi, (long)(G - 1) * DK * (a.DV + DK), ld * (a.DV + DK), a.DV + DK, 0};
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
+                           dim3(kChainThreads), 0, st, tr);
+        hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 32)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
+        const ChainIO fu{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G, a.B, a.T, a.H, a.DV,
+                         sseg, (long)G * DK * a.DV, ld * a.DV, a.DV,
+                         Sbuf, ld * a.DV, 0, a.DV, 1};
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false>), dim3(G * BHp * tiles), dim3(kChainThreads), 0,
+                           st, fu);
+        return hipGetLastError();
+    }
+    int R = (int)(avail / per_chunk);
     if (R < 1) return hipErrorInvalidValue;
     if (R > nch) R = nch;
-    const int tiles = a.DV / DVT;
-    const int chain_blocks = (BH + 7) / 8 * 8 * tiles;
     for (int n0 = 0; n0 < nch; n0 += R) {
         const int cnt = nch - n0 < R ? nch - n0 : R;
         hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
                            a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS>), dim3(chain_blocks), dim3(kChainThreads), 0, st, a.v,
-                           a.w, n0 == 0 ? a.S0 : Sbuf, a.o, Sbuf, a.B, a.T, a.H, a.DV, n0, cnt, ws);
+        const ChainIO io{a.v, a.w, a.o, ws, cnt, n0, n0 + cnt, cnt, 1, a.B, a.T, a.H, a.DV,
+                         n0 == 0 ? a.S0 : Sbuf, ld * a.DV, 0, a.DV,
+                         Sbuf, ld * a.DV, 0, a.DV, 0};
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false>), dim3(BHp * tiles), dim3(kChainThreads), 0, st,
+                           io);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -830,6 +976,12 @@ bool split_supported(int T, int H, int DK, int DV, bool bf16) {
     if ((long long)T * H * DV * 4 >= (1ll << 32)) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
     return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
+}
+
+size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16) {
+    const size_t nch = ((size_t)T + CH - 1) / CH;
+    const SplitPlan plan = split_plan(B, T, H, DK, DV);
+    return (size_t)B * H * DK * DV * 4 + nch * split_chunk_bytes(B, H, DK, bf16) + plan.extra_bytes;
 }
 
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16) {

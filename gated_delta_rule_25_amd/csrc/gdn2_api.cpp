@@ -14,9 +14,6 @@ namespace {
 
 bool dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
 
-// Recommended size of the two-kernel path's ring of per-chunk operand blobs.
-constexpr size_t kRingBytes = (size_t)1 << 40;
-
 // Smallest workspace the two-kernel path accepts: the state buffer and one chunk slot.
 size_t split_min_bytes(int32_t B, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     return (size_t)B * H * dk * dv * 4 + gdn2::split_chunk_bytes(B, H, dk, bf16);
@@ -136,12 +133,7 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
     if (B <= 0 || H <= 0 || T <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
     const bool bf16 = in_dtype == GDN2_BF16;
     if (!gdn2::split_supported(T, H, d_k, d_v, bf16)) return 0;
-    const size_t nch = ((size_t)T + 63) / 64;
-    const size_t per_chunk = gdn2::split_chunk_bytes(B, H, d_k, bf16);
-    size_t ring = kRingBytes / per_chunk;  // chunk slots in the recommended ring
-    if (ring < 1) ring = 1;
-    if (ring > nch) ring = nch;
-    return split_min_bytes(B, H, d_k, d_v, bf16) - per_chunk + ring * per_chunk;
+    return gdn2::split_workspace_bytes(B, T, H, d_k, d_v, bf16);
 }
 
 gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
@@ -163,7 +155,9 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
         Sizes sz;
         sizes_of(B, T, H, d_k, d_v, &sz);
         const Range others[] = {range_of(q, sz.qk * es), range_of(k, sz.qk * es), range_of(v, sz.vw * es),
-                                range_of(alpha, sz.qk * es), range_of(b, sz.qk * es), range_of(w, sz.vw * es),
+                                range_of(alpha, ((gate_flags & GDN2_ALPHA_SCALAR) ? sz.scalar : sz.qk) * es),
+                                range_of(b, ((gate_flags & GDN2_BETA_SCALAR) ? sz.scalar : sz.qk) * es),
+                                range_of(w, sz.vw * es),
                                 range_of(S0, sz.state * 4), range_of(o, sz.vw * 4), range_of(S_out, sz.state * 4)};
         for (const Range& r : others)
             if (overlap(rws, r)) return GDN2_ERR_ALIAS;

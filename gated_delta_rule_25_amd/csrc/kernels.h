@@ -37,9 +37,12 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
 bool chunk_supported(int T, int H, int DK, int DV, bool bf16);
 
 // Two-kernel path (prep + chain) through a workspace ring of per-chunk operand blobs.
-// Workspace = state buffer (B*H*DK*DV fp32) + R chunk slots of split_chunk_bytes each.
+// Workspace = state buffer (B*H*DK*DV fp32) + R chunk slots of split_chunk_bytes each; with a
+// slot for every chunk plus the segment buffers (split_workspace_bytes), a long sequence with few
+// (b, h) runs its chain in parallel segments.
 hipError_t launch_split(const ChunkArgs& a, hipStream_t s);
 bool split_supported(int T, int H, int DK, int DV, bool bf16);
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16);
+size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16);
 
 }  // namespace gdn2

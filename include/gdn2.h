@@ -94,7 +94,11 @@ enum {
  *    Supported: bf16 with d in {32, 64, 128}, fp32 with d = 32. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v] first
  *    when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand blocks.
  *    R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with
- *    fewer slots than chunks the two kernels alternate over rounds of R chunks. The buffer must
+ *    fewer slots than chunks the two kernels alternate over rounds of R chunks. When B*H is too
+ *    small to fill the GPU and the sequence is long, a workspace of the size the query returns
+ *    also holds per-segment buffers: the sequence is cut into segments whose state transitions
+ *    are computed in parallel and combined by a scan, so the chain runs all segments at once
+ *    (the result is the same recurrence, up to rounding). The buffer must
  *    be 256-byte aligned (else GDN2_ERR_ALIGN), hold the state and one slot (else
  *    GDN2_ERR_WORKSPACE) and overlap no input or output (else GDN2_ERR_ALIAS). Its contents
  *    are scratch on entry and on return.
@@ -113,8 +117,9 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes for the two-kernel path of gdn2_chunk_fwd at these sizes: the state buffer
- * (when S_out may be NULL) plus one slot per chunk, so that one round covers the sequence. 0 when
- * the two-kernel path does not take these sizes (pass NULL; the single kernel runs). */
+ * (when S_out may be NULL), one slot per chunk so that one round covers the sequence, and the
+ * segment buffers when the sizes are segmented. 0 when the two-kernel path does not take these
+ * sizes (pass NULL; the single kernel runs). */
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
 

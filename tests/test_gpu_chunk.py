@@ -200,3 +200,67 @@ def test_chunk_split_small_ring():
     torch.cuda.synchronize()
     o_ref, S_ref = _oracle(ins)
     assert normwise_err(o, o_ref) <= TOL16 and normwise_err(S_T, S_ref) <= TOL16
+
+
+# Long sequences with few (b, h) run the chain in parallel segments (each segment's transition
+# from the state recurrence alone, a scan for the segment start states, then all segments at
+# once). These sizes are long enough to be segmented; the last segment is ragged.
+SEGMENTED = [
+    ("seg_bf16_d128", scaled(WORKLOADS["prefill_1p3b"], B=1, T=4100, H=2), TOL16),
+    ("seg_bf16_d128_slow_decay", scaled(WORKLOADS["long_prefill"], B=1, T=3000, H=2), TOL16),
+    ("seg_bf16_gdn", scaled(WORKLOADS["gdn_scalar"], B=1, T=3000, H=3), TOL16),
+    ("seg_bf16_kda", scaled(WORKLOADS["kda_scalar"], B=1, T=2100, H=2), TOL16),
+    ("seg_bf16_d64", scaled(WORKLOADS["prefill_1p3b"], B=1, T=2500, H=2, d_k=64, d_v=64), TOL16),
+    ("seg_fp32_d32", scaled(WORKLOADS["tiny_fp32"], B=1, T=2100, H=1, s0_std=0.1), TOL32),
+]
+
+
+@pytest.mark.parametrize("name,wl,tol", SEGMENTED, ids=[c[0] for c in SEGMENTED])
+def test_chunk_segmented_matches_oracle(name, wl, tol):
+    banner(f"chunk segmented {name} {wl}")
+    g = _g()
+    B, T, H, d = wl.B, wl.T, wl.H, wl.d_k
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    # the workspace query includes the segment buffers exactly when the sizes are segmented
+    assert g.chunk_fwd_workspace_bytes(B, T, H, d, d, dtype=dt) > B * H * d * d * 4 + \
+        ((T + 63) // 64) * (g.chunk_fwd_workspace_bytes(B, 64, H, d, d, dtype=dt) - B * H * d * d * 4)
+    _check(name, make_inputs(wl), tol)
+
+
+def test_chunk_segmented_in_place_state():
+    """Segmented run with S_out aliasing S0, then the next call continues from that state."""
+    banner("chunk segmented, in-place state")
+    g = _g()
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=1, T=4100, H=2)
+    ins = make_inputs(wl)
+    d = _cuda(ins)
+    names = ("q", "k", "v", "alpha", "b", "w")
+    S = d["S0"].clone()
+    T1 = 2300
+    o1, _ = g.chunk_fwd(*[d[n][:, :T1].contiguous() for n in names], S, S_out=S)
+    o2, _ = g.chunk_fwd(*[d[n][:, T1:].contiguous() for n in names], S, S_out=S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(ins)
+    assert normwise_err(torch.cat([o1, o2], 1), o_ref) <= TOL16
+    assert normwise_err(S, S_ref) <= TOL16
+
+
+def test_chunk_long_context_sampled_heads():
+    """B1 H16 T131072 (the long-context shape, segmented): o and S_T of two heads against the
+    oracle over all 131,072 tokens."""
+    from gated_delta_rule_25_amd.inputs import make_inputs_torch
+    banner("chunk long context, heads 0 and 11")
+    g = _g()
+    wl = WORKLOADS["long_prefill"]
+    ins = make_inputs_torch(wl, device="cuda")
+    names = ("q", "k", "v", "alpha", "b", "w")
+    o, S_T = g.chunk_fwd(*[ins[n] for n in names], ins["S0"])
+    torch.cuda.synchronize()
+    heads = [0, 11]
+    sub = {n: ins[n][:, :, heads].cpu() for n in names}
+    o_ref, S_ref = oracle.forward(*[sub[n] for n in names], ins["S0"][:, heads].cpu())
+    for i, h in enumerate(heads):
+        eo = normwise_err(o[:, :, h:h + 1], o_ref[:, :, i:i + 1])
+        es = normwise_err(S_T[:, h:h + 1], S_ref[:, i:i + 1])
+        print(f"  head {h}: o err {eo:.2e}  S_T err {es:.2e}", flush=True)
+        assert eo <= TOL16 and es <= TOL16, (h, eo, es)
