@@ -90,3 +90,20 @@ def test_kernel_precision_scheme_meets_bar():
     es = np.abs(S - S_ref[0, 0]).max() / np.abs(S_ref[0, 0]).max()
     assert eo < 2e-3 and es < 2e-3, (eo, es)
     assert eo > 1e-5  # fp16 rounding is really being emulated
+
+
+def test_recurrence_is_affine_in_the_initial_state():
+    """S_T(S0) = Phi S0 + S_T(0) and o(S0) = o(0) + o_hom(S0), with Phi the final state of the
+    run with v = 0 started at the identity and o_hom the outputs of the run with v = 0 started at
+    S0. The segmented chunk path combines segments with exactly this identity."""
+    rng = np.random.default_rng(14)
+    B, T, H, dk, dv = 2, 37, 2, 5, 4
+    q, k, v, a, b, w, S0 = P.random_inputs(rng, B, T, H, dk, dv)
+    o, S_T = oracle.forward(q, k, v, a, b, w, S0)
+    o0, S_T0 = oracle.forward(q, k, v, a, b, w, np.zeros_like(S0))
+    eye = np.broadcast_to(np.eye(dk), (B, H, dk, dk)).copy()
+    _, Phi = oracle.forward(q, k, np.zeros((B, T, H, dk)), a, b, np.ones((B, T, H, dk)), eye)
+    np.testing.assert_allclose(S_T, np.einsum("bhij,bhjc->bhic", Phi, S0) + S_T0, rtol=0, atol=1e-12)
+    o_h, _ = oracle.forward(q, k, np.zeros_like(v), a, b, w, S0)
+    np.testing.assert_allclose(o, o0 + o_h, rtol=0, atol=1e-12)
+    assert np.abs(Phi - eye).max() > 1e-3  # the transition is not trivial
