@@ -831,15 +831,16 @@ chain_kernel(const ChainIO io) {
 }
 
 // ------------------------------------------------------------------------------------------
-// segment scan: S_in[g + 1] = Phi_g S_in[g] + Psi_g, for one (b, h) and 32 state columns, fp32
+// segment scan: S_in[g + 1] = Phi_g S_in[g] + Psi_g, for one (b, h) and 8 state columns, fp32
 // psiphi: [b·h][G - 1][DK][DV + DK] (Psi in columns 0..DV-1, Phi in DV..DV+DK-1)
 // sseg:   [b·h][G][DK][DV], sseg[·][0] = S0 (or zeros)
 template <int DK>
 __global__ void __launch_bounds__(256, 1)
 scan_kernel(const float* S0, const float* __restrict__ psiphi, float* __restrict__ sseg, int G, int DV) {
-    constexpr int CW = 32;          // state columns per workgroup
+    constexpr int CW = 8;           // state columns per workgroup
     constexpr int SETS = 256 / DK;  // column sets per row
     constexpr int CPT = CW / SETS;  // columns per thread
+    static_assert(CPT >= 1, "columns per thread");
     __shared__ float cur[DK][CW + 1];
     const int cols = DV / CW;
     const int bh = blockIdx.x / cols, c0 = (blockIdx.x % cols) * CW;
@@ -932,7 +933,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
                          psiphi, (long)(G - 1) * DK * (a.DV + DK), ld * (a.DV + DK), a.DV + DK, 0};
         hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
                            dim3(kChainThreads), 0, st, tr);
-        hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 32)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
+        hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 8)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
         const ChainIO fu{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G, a.B, a.T, a.H, a.DV,
                          sseg, (long)G * DK * a.DV, ld * a.DV, a.DV,
                          Sbuf, ld * a.DV, 0, a.DV, 1};
