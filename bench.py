@@ -99,6 +99,62 @@ def time_prefill(g, ins, steps, warmup, impl, ring_mb=None):
     return wall, kern_ms
 
 
+def time_prefill_cold(g, ins, reps, impl):
+    """Per-call kernel time with a 512 MiB scrub written between calls (evicts the 256 MB
+    Infinity Cache and the L2s), on the launch stream."""
+    import torch
+    args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")]
+    B, T, H, dk = ins["q"].shape
+    dv = ins["v"].shape[-1]
+    o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.float32)
+    S_out = torch.empty(B, H, dk, dv, device="cuda", dtype=torch.float32)
+    kw = dict(o=o, S_out=S_out)
+    if impl == "fused":
+        kw["fused"] = True
+    elif impl == "chunk":
+        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
+        if need:
+            kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
+    fn = g.recurrent_fwd if impl == "recurrent" else g.chunk_fwd
+    scrub = torch.empty(1 << 27, device="cuda", dtype=torch.float32)  # 512 MiB
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(reps + 1):
+        scrub.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*args, ins["S0"], **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            ms.append(e0.elapsed_time(e1))
+    del scrub
+    return sum(ms) / len(ms)
+
+
+def prefill_leg(g, name, steps, impl):
+    """One more prefill workload, timed like the headline one (warm, back to back)."""
+    import torch
+    from gated_delta_rule_25_amd.inputs import WORKLOADS, make_inputs_torch
+    wl = WORKLOADS[name]
+    ins = make_inputs_torch(wl, device="cuda")
+    torch.cuda.synchronize()
+    _, kern_ms = time_prefill(g, ins, steps, 1, impl)
+    avg = sum(kern_ms) / len(kern_ms)
+    head_tokens = wl.B * wl.T * wl.H
+    alg = prefill_bytes_per_head_token(wl.d_k, wl.d_v, wl.T) * head_tokens
+    res = dict(config=f"B{wl.B} H{wl.H} T{wl.T} d{wl.d_k} {wl.dtype} gates={wl.gates}",
+               kernel_ms=round(avg, 4), tokens_per_s=round(wl.B * wl.T / (avg * 1e-3), 1))
+    if wl.gates == "general":  # (scalar gates move fewer input bytes; no byte roofline quoted)
+        res.update(gbs=round(alg / (avg * 1e-3) / 1e9, 1),
+                   frac=round(alg / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    print(f"[bench] {name}: {avg:.3f} ms/launch, {res['tokens_per_s']:.3e} tokens/s", file=sys.stderr,
+          flush=True)
+    del ins
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(g, B, H, d, steps, warmup, seed):
     import torch
     from gated_delta_rule_25_amd.inputs import make_decode_inputs
@@ -171,6 +227,8 @@ def main(argv=None):
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte "
                          "counters)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-others", action="store_true",
+                    help="skip the long-context and scalar-gate prefill legs")
     ap.add_argument("--workload", default="prefill_1p3b",
                     choices=["prefill_1p3b", "long_prefill", "gdn_scalar", "kda_scalar"],
                     help="prefill input recipe to time (the headline figure uses prefill_1p3b)")
@@ -210,6 +268,23 @@ def main(argv=None):
           f"{ms_per_step:.3f} ms/step (wall), {achieved_gbs:.0f} GB/s, {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
+    cold_ms = time_prefill_cold(g, ins, 5, args.impl)
+    print(f"[bench] prefill {args.impl} cold (512 MiB scrub between calls): {cold_ms:.3f} ms/launch",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ins, args.cpu_heads)
+        print(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+    del ins
+    torch.cuda.empty_cache()
+
+    others = {}
+    if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
+        for name, steps in (("long_prefill", 3), ("gdn_scalar", 10), ("kda_scalar", 10)):
+            others[name] = prefill_leg(g, name, steps, args.impl)
+
     dec = {}
     decode_runs = () if args.skip_decode else ((256, args.decode_steps),
                                                (1024, max(1, args.decode_steps // 5)))
@@ -232,12 +307,6 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(ins, args.cpu_heads)
-        print(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores",
-              file=sys.stderr, flush=True)
 
     rec = {
         "metric": "GDN-2 chunk fwd tokens/s (B8,H16,T4k,d128) + decode state HBM GB/s",
@@ -263,6 +332,8 @@ def main(argv=None):
                      "kernel_ms": round(kern_avg, 4),
                      "algorithmic_bytes": int(bytes_launch),
                      "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "cold_ms": round(cold_ms, 4),
+        "other_prefill": others,
         "decode": dec,
         "cpu_baseline": cpu,
     }
