@@ -129,8 +129,11 @@ struct PrepSmem {
     static constexpr int KTP = DK + Prec<F16>::kPad;    // 16-byte rows for 16-byte accesses
     static constexpr int oKt = oOut + outBytes;         // E [48][KTP]
     static constexpr int oA = oKt + 48 * KTP * ES;      // E [64][CHP] A below the diagonal
-    static constexpr int oAd = oA + CH * CHP * ES;      // float [4][16][16] diagonal A^T
-    static constexpr int bytes = oAd + 4 * 256 * 4;
+    // float [4][ADS] diagonal blocks of A^T, each [16][16]; the block stride is 4 floats more than
+    // 256 so that the four 16-lane groups reading four blocks at once hit different banks
+    static constexpr int ADS = 260;
+    static constexpr int oAd = oA + CH * CHP * ES;
+    static constexpr int bytes = oAd + 4 * ADS * 4;
     static_assert(BL::oTm - BL::oKbT == DK * CHP * ES && out1Bytes == (DK + CH) * CHP * ES, "layout");
     static_assert(bytes <= 80 * 1024, "prep LDS must allow two workgroups per CU");
 };
@@ -354,7 +357,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
         at.y = (4 * g + 1) > l16 ? accA[1] : 0.f;
         at.z = (4 * g + 2) > l16 ? accA[2] : 0.f;
         at.w = (4 * g + 3) > l16 ? accA[3] : 0.f;
-        *reinterpret_cast<float4*>(AdT + I * 256 + l16 * 16 + 4 * g) = at;
+        *reinterpret_cast<float4*>(AdT + I * SM::ADS + l16 * 16 + 4 * g) = at;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rr = 4 * g + j;
@@ -364,48 +367,61 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     lds_barrier();
 
     // ---- C: Gram blocks below the diagonal; T_II ----
-    for (int J = 0; J < I; ++J) {
-        f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-        // non-adjacent blocks: row factors times exp2(G_I - G_{J+1}) (tables 17..19)
-        const float* cij = (J == I - 1) ? nullptr : tab + (I == 2 ? 17 : (J == 0 ? 18 : 19)) * DK;
+    // Wave I computes the blocks (I, J < I) of A and P together, so that their LDS reads and
+    // products interleave. Non-adjacent blocks use the row factors times exp2(G_I - G_{J+1})
+    // (tables 17..19).
+    auto gram_blocks = [&](auto nb_c, const float* c0tab, const float* c1tab) {
+        constexpr int NB = decltype(nb_c)::value;
+        f4 accA[NB], accP[NB];
+#pragma unroll
+        for (int J = 0; J < NB; ++J) accA[J] = accP[J] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             const int c0 = 32 * s + 8 * g;
-            float ea[8], qa[8];
-            if (cij) {
-                float c8[8];
-                lds_read8f(cij + c0, c8);
+            float c8[2][8];
+            if constexpr (NB >= 2) lds_read8f(c0tab + c0, c8[0]);
+            if constexpr (NB >= 3) lds_read8f(c1tab + c0, c8[1]);
+            Frag kf[NB];
+#pragma unroll
+            for (int J = 0; J < NB; ++J) kf[J] = PR::lds8(Kt + (16 * J + l16) * SM::KTP + c0);
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                float ea[8], qa[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    ea[i] = er[8 * s + i] * c8[i];
-                    qa[i] = qr[8 * s + i] * c8[i];
+                    const float f = (J == NB - 1) ? 1.f : c8[J][i];
+                    ea[i] = er[8 * s + i] * f;
+                    qa[i] = qr[8 * s + i] * f;
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    ea[i] = er[8 * s + i];
-                    qa[i] = qr[8 * s + i];
-                }
+                PR::mma(accA[J], PR::make(ea), kf[J]);
+                PR::mma(accP[J], PR::make(qa), kf[J]);
             }
-            const Frag kf = PR::lds8(Kt + (16 * J + l16) * SM::KTP + c0);
-            PR::mma(accA, PR::make(ea), kf);
-            PR::mma(accP, PR::make(qa), kf);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rr = 16 * I + 4 * g + j;
-            A16[rr * CHP + 16 * J + l16] = (E)accA[j];
-            Pm[rr * CHP + 16 * J + l16] = (E)accP[j];
+        for (int J = 0; J < NB; ++J) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 16 * I + 4 * g + j;
+                A16[rr * CHP + 16 * J + l16] = (E)accA[J][j];
+                Pm[rr * CHP + 16 * J + l16] = (E)accP[J][j];
+            }
         }
+    };
+    if (wv == 1) {
+        gram_blocks(std::integral_constant<int, 1>{}, nullptr, nullptr);
+    } else if (wv == 2) {
+        gram_blocks(std::integral_constant<int, 2>{}, tab + 17 * DK, nullptr);
+    } else if (wv == 3) {
+        gram_blocks(std::integral_constant<int, 3>{}, tab + 18 * DK, tab + 19 * DK);
     }
-    {
-        // T_II = (I + A_II)^-1, right-looking; every lane group computes it (lane l16 owns
-        // column l16) so the solve shares a basic block with the Gram products above and the
-        // scheduler can overlap the two. Group 0 writes the result.
+    if (wv == 0) {
+        // T_II = (I + A_II)^-1 for the four diagonal blocks, right-looking, by the wave that
+        // has no Gram block above: lane group g solves block g, lane l16 owns column l16.
+        const int Ib = g;
         float acc[16], tc[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc[m] = 0.f;
-        const float4* Ab4 = reinterpret_cast<const float4*>(AdT + I * 256);
+        const float4* Ab4 = reinterpret_cast<const float4*>(AdT + Ib * SM::ADS);
         float4 cur[4], nxt[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) cur[q4] = Ab4[q4];
@@ -427,10 +443,8 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
         }
-        if (g == 0) {
 #pragma unroll
-            for (int m = 0; m < 16; ++m) Tm[(16 * I + m) * CHP + 16 * I + l16] = (E)tc[m];
-        }
+        for (int m = 0; m < 16; ++m) Tm[(16 * Ib + m) * CHP + 16 * Ib + l16] = (E)tc[m];
     }
     lds_barrier();
 
@@ -493,14 +507,31 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 
     // ---- out: K_bar^T and T (contiguous in LDS and in the blob), P, gamma_last ----
     {
+        // (256 threads; every LDS read is issued before the stores)
+        const int tid = threadIdx.x;
+        constexpr int N1 = SM::out1Bytes / 16, NP = CH * CHP * (int)sizeof(E) / 16;
+        constexpr int J1 = (N1 + 255) / 256, JP = (NP + 255) / 256;
         const uint4* src = reinterpret_cast<const uint4*>(smem + SM::oOut);
-        uint4* dst = reinterpret_cast<uint4*>(blob + BL::oKbT);
-        for (int i = threadIdx.x; i < SM::out1Bytes / 16; i += blockDim.x) dst[i] = src[i];
         const uint4* srcP = reinterpret_cast<const uint4*>(smem + SM::oP);
-        uint4* dstP = reinterpret_cast<uint4*>(blob + BL::oP);
-        for (int i = threadIdx.x; i < CH * CHP * (int)sizeof(E) / 16; i += blockDim.x) dstP[i] = srcP[i];
+        uint4 v1[J1], vp[JP];
+#pragma unroll
+        for (int j = 0; j < J1; ++j) v1[j] = src[min(tid + 256 * j, N1 - 1)];
+#pragma unroll
+        for (int j = 0; j < JP; ++j) vp[j] = srcP[min(tid + 256 * j, NP - 1)];
+        // stores through resources bounded by the regions: lanes past the end store nothing
+        const auto rs1 = make_rsrc(blob + BL::oKbT, N1 * 16);
+        const auto rsP = make_rsrc(blob + BL::oP, NP * 16);
+#pragma unroll
+        for (int j = 0; j < J1; ++j)
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&v1[j]), rs1,
+                                                   16 * (tid + 256 * j), 0, 0);
+#pragma unroll
+        for (int j = 0; j < JP; ++j)
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&vp[j]), rsP,
+                                                   16 * (tid + 256 * j), 0, 0);
         float* gc = reinterpret_cast<float*>(blob + BL::oGC);
-        for (int c = threadIdx.x; c < DK; c += blockDim.x) gc[c] = tab[16 * DK + c];
+        static_assert(DK <= 256, "one gamma_last element per thread");
+        if (tid < DK) gc[tid] = tab[16 * DK + tid];
         if constexpr (BS) {
             if (g == 0) reinterpret_cast<float*>(blob + BL::oBeta)[r] = valid ? rbs_raw : 0.f;
         }
