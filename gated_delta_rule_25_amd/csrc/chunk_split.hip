@@ -32,28 +32,43 @@ using namespace chunk;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// Per-chunk operand blob (also the chain kernel's LDS buffer layout).
+// Per-chunk operand blob (also the chain kernel's LDS buffer layout). Matrices are addressed
+// through en() (E_hat, Q_hat: [64][DK]), kbt() (K_bar^T: [DK][64]) and tp() (T, P: [64][64],
+// lower block triangular), in elements; the chain kernel reads 4-element units of 16 consecutive
+// rows at one column, and the layouts give those 16 reads distinct LDS banks.
+//  - fp16: no padding. Within a row the 4-element (8-byte) units are permuted by an XOR with the
+//    row index (row & 15 for rows of 64 dwords or more; (row >> 1) & 7 for rows of 16 dwords,
+//    whose consecutive rows already alternate between the two halves of the banks). T and P keep
+//    only the column blocks the chain reads: 32 columns for rows 0..31, 64 for rows 32..63.
+//  - fp32: rows padded by 4 elements, full 64x64 T and P.
 template <int DK, bool F16>
 struct Blob {
     using E = typename Prec<F16>::E;
     static constexpr int ES = (int)sizeof(E);
-    // Rows padded by 4 elements. For the fp16 operands that makes the row stride 2 dwords more
-    // than a multiple of 32 banks, so the 8-byte fragment reads of 16 consecutive rows (one
-    // 16-lane group of ds_read_b64) hit 32 distinct banks.
-    static constexpr int PAD = 4;
-    static constexpr int DKP = DK + PAD;
-    static constexpr int CHP = CH + PAD;
+    static constexpr int PAD = F16 ? 0 : 4;
+    static constexpr int DKP = DK + PAD, CHP = CH + PAD;
+    static constexpr int TPE = F16 ? 32 * 32 + 32 * 64 : CH * CHP;  // elements of T or P
+    __device__ static int unit_sw(int r, int width) { return width >= 64 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ static int sw(int r, int c, int width) {
+        return F16 ? ((((c >> 2) ^ unit_sw(r, width)) << 2) | (c & 3)) : c;
+    }
+    __device__ static int en(int r, int c) { return r * DKP + sw(r, c, DK); }
+    __device__ static int kbt(int r, int c) { return r * CHP + sw(r, c, CH); }
+    __device__ static int tp(int r, int c) {
+        if constexpr (F16) return r < 32 ? r * 32 + sw(r, c, 32) : 32 * 32 + (r - 32) * 64 + sw(r, c, 64);
+        return r * CHP + c;
+    }
     // The state recurrence alone needs the prefix [En .. beta]; the outputs also need P and Q_hat.
-    static constexpr int oEn = 0;                       // E [64][DKP]   -E_hat
-    static constexpr int oKbT = oEn + CH * DKP * ES;    // E [DK][CHP]   K_bar^T
-    static constexpr int oTm = oKbT + DK * CHP * ES;    // E [64][CHP]   T
-    static constexpr int oGC = oTm + CH * CHP * ES;     // float [DK]    gamma_last
+    static constexpr int oEn = 0;                       // E_hat, negated
+    static constexpr int oKbT = oEn + CH * DKP * ES;    // K_bar^T
+    static constexpr int oTm = oKbT + DK * CHP * ES;    // T
+    static constexpr int oGC = oTm + TPE * ES;          // float [DK]    gamma_last
     static constexpr int oBeta = oGC + DK * 4;          // float [64]    scalar beta per row (scalar-beta gates)
     static constexpr int stateBytes = oBeta + CH * 4;
-    static constexpr int oP = stateBytes;               // E [64][CHP]   P
-    static constexpr int oQh = oP + CH * CHP * ES;      // E [64][DKP]   Q_hat
+    static constexpr int oP = stateBytes;               // P
+    static constexpr int oQh = oP + TPE * ES;           // Q_hat
     static constexpr int bytes = (oQh + CH * DKP * ES + 255) / 256 * 256;
-    static_assert(stateBytes % 16 == 0, "16-byte copies");
+    static_assert(stateBytes % 16 == 0 && oP % 16 == 0, "16-byte copies");
 };
 
 // Copy `bytes` (a multiple of 16) from global to LDS with `nw` wavefronts (this one is `cw`),
@@ -74,10 +89,11 @@ __device__ __forceinline__ void wait_vm_but() {
     __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
 
-// Eight elements to a blob row position: two 8-byte stores for fp16 (blob rows are 8-byte
-// aligned), two 16-byte stores for fp32.
-template <typename E>
-__device__ __forceinline__ void store8_rows(E* p, const float* x) {
+// Eight elements c0..c0+7 (c0 a multiple of 8) of row r of E_hat or Q_hat to the blob: two
+// 8-byte stores for fp16 (the two 4-element units land where en() puts them), two 16-byte
+// stores for fp32.
+template <typename BL, typename E>
+__device__ __forceinline__ void store8_units(E* base, int r, int c0, const float* x) {
     if constexpr (sizeof(E) == 2) {
         h4 a, b;
 #pragma unroll
@@ -85,11 +101,11 @@ __device__ __forceinline__ void store8_rows(E* p, const float* x) {
             a[i] = (_Float16)x[i];
             b[i] = (_Float16)x[i + 4];
         }
-        reinterpret_cast<h4*>(p)[0] = a;
-        reinterpret_cast<h4*>(p)[1] = b;
+        *reinterpret_cast<h4*>(base + BL::en(r, c0)) = a;
+        *reinterpret_cast<h4*>(base + BL::en(r, c0 + 4)) = b;
     } else {
-        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+        reinterpret_cast<float4*>(base + BL::en(r, c0))[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4*>(base + BL::en(r, c0 + 4))[0] = make_float4(x[4], x[5], x[6], x[7]);
     }
 }
 
@@ -116,25 +132,26 @@ struct PrepSmem {
     using E = typename Prec<F16>::E;
     using BL = Blob<DK, F16>;
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int DKP = BL::DKP, CHP = BL::CHP;
+    static constexpr int CHP = BL::CHP;
+    static constexpr int AP = CH + 4;                   // row stride of A (padded: fragment reads)
     static constexpr int oTot = 0;                      // float [4][DK]
     static constexpr int oX = oTot + 4 * DK * 4;        // float [4][DK]
     static constexpr int oTab = oX + 4 * DK * 4;        // float [kTabs][DK]
     static constexpr int oOut = oTab + kTabs * DK * 4;  // K_bar^T, T (as in the blob), then P
     static constexpr int oKbT = oOut;
     static constexpr int oTm = oKbT + DK * CHP * ES;
-    static constexpr int oP = oTm + CH * CHP * ES;
+    static constexpr int oP = oTm + BL::TPE * ES;
     static constexpr int out1Bytes = BL::oGC - BL::oKbT;  // K_bar^T and T
-    static constexpr int outBytes = out1Bytes + CH * CHP * ES;
+    static constexpr int outBytes = out1Bytes + BL::TPE * ES;
     static constexpr int KTP = DK + Prec<F16>::kPad;    // 16-byte rows for 16-byte accesses
     static constexpr int oKt = oOut + outBytes;         // E [48][KTP]
-    static constexpr int oA = oKt + 48 * KTP * ES;      // E [64][CHP] A below the diagonal
+    static constexpr int oA = oKt + 48 * KTP * ES;      // E [64][AP] A below the diagonal
     // float [4][ADS] diagonal blocks of A^T, each [16][16]; the block stride is 4 floats more than
     // 256 so that the four 16-lane groups reading four blocks at once hit different banks
     static constexpr int ADS = 260;
-    static constexpr int oAd = oA + CH * CHP * ES;
+    static constexpr int oAd = oA + CH * AP * ES;
     static constexpr int bytes = oAd + 4 * ADS * 4;
-    static_assert(BL::oTm - BL::oKbT == DK * CHP * ES && out1Bytes == (DK + CH) * CHP * ES, "layout");
+    static_assert(BL::oTm - BL::oKbT == DK * CHP * ES && out1Bytes == DK * CHP * ES + BL::TPE * ES, "layout");
     static_assert(bytes <= 80 * 1024, "prep LDS must allow two workgroups per CU");
 };
 
@@ -149,7 +166,6 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     using BL = Blob<DK, F16>;
     using SM = PrepSmem<DK, F16>;
     constexpr int NKS = DK / 32, CPL = DK / 4;
-    constexpr int DKP = BL::DKP, CHP = BL::CHP;
 
     __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
     float* ldsTot = reinterpret_cast<float*>(smem + SM::oTot);
@@ -173,9 +189,9 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 
     for (int idx = threadIdx.x; idx < CH * CH; idx += blockDim.x) {
         const int rr = idx / CH, cc = idx % CH;
-        if ((cc >> 4) > (rr >> 4)) {
-            Pm[rr * CHP + cc] = (E)0.f;
-            Tm[rr * CHP + cc] = (E)0.f;
+        if ((cc >> 4) > (rr >> 4) && (!F16 || cc < (rr < 32 ? 32 : 64))) {  // stored blocks only
+            Pm[BL::tp(rr, cc)] = (E)0.f;
+            Tm[BL::tp(rr, cc)] = (E)0.f;
         }
     }
 
@@ -309,15 +325,15 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
                 qh[i] = qx[i] * gam;
                 en[i] = -(bk * gam);
                 kt[i] = km[i] * fTX[i];
-                KbT[(c0 + i) * CHP + r] = (E)(kt[i] * fCG[i]);
+                KbT[BL::kbt(c0 + i, r)] = (E)(kt[i] * fCG[i]);
             }
             {
                 const Frag kmf = PR::make(km);
                 PR::mma(accA, PR::make(em), kmf);
                 PR::mma(accP, PR::make(qm), kmf);
             }
-            store8_rows(&bQh[r * DKP + c0], qh);
-            store8_rows(&bEn[r * DKP + c0], en);
+            store8_units<BL>(bQh, r, c0, qh);
+            store8_units<BL>(bEn, r, c0, en);
             if (I < 3) PR::store8(&Kt[r * SM::KTP + c0], kt);
         }
         bool finite = true;
@@ -361,7 +377,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rr = 4 * g + j;
-            Pm[(16 * I + rr) * CHP + 16 * I + l16] = (E)(rr >= l16 ? accP[j] : 0.f);
+            Pm[BL::tp(16 * I + rr, 16 * I + l16)] = (E)(rr >= l16 ? accP[j] : 0.f);
         }
     }
     lds_barrier();
@@ -402,8 +418,8 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rr = 16 * I + 4 * g + j;
-                A16[rr * CHP + 16 * J + l16] = (E)accA[J][j];
-                Pm[rr * CHP + 16 * J + l16] = (E)accP[J][j];
+                A16[rr * SM::AP + 16 * J + l16] = (E)accA[J][j];
+                Pm[BL::tp(rr, 16 * J + l16)] = (E)accP[J][j];
             }
         }
     };
@@ -444,7 +460,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
             for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
         }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) Tm[(16 * Ib + m) * CHP + 16 * Ib + l16] = (E)tc[m];
+        for (int m = 0; m < 16; ++m) Tm[BL::tp(16 * Ib + m, 16 * Ib + l16)] = (E)tc[m];
     }
     lds_barrier();
 
@@ -454,21 +470,21 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
         float af[8], bf[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            af[i] = (float)A16[(16 * Ib + l16) * CHP + 16 * Jb + 4 * g + i];
-            bf[i] = (float)Tm[(16 * Jb + 4 * g + i) * CHP + 16 * Jb + l16];
+            af[i] = (float)A16[(16 * Ib + l16) * SM::AP + 16 * Jb + 4 * g + i];
+            bf[i] = (float)Tm[BL::tp(16 * Jb + 4 * g + i, 16 * Jb + l16)];
             af[i + 4] = bf[i + 4] = 0.f;
         }
         f4 X = {0.f, 0.f, 0.f, 0.f};
         PR::mma(X, PR::make(af), PR::make(bf));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            af[i] = (float)Tm[(16 * Ib + l16) * CHP + 16 * Ib + 4 * g + i];
+            af[i] = (float)Tm[BL::tp(16 * Ib + l16, 16 * Ib + 4 * g + i)];
             bf[i] = X[i];
         }
         f4 Y = {0.f, 0.f, 0.f, 0.f};
         PR::mma(Y, PR::make(af), PR::make(bf));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Tm[(16 * Ib + 4 * g + j) * CHP + 16 * Jb + l16] = (E)(-Y[j]);
+        for (int j = 0; j < 4; ++j) Tm[BL::tp(16 * Ib + 4 * g + j, 16 * Jb + l16)] = (E)(-Y[j]);
     }
     lds_barrier();
 
@@ -479,10 +495,10 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int Ib = 2 + u;
-            const E* ar = &A16[(16 * Ib + l16) * CHP];
+            const E* ar = &A16[(16 * Ib + l16) * SM::AP];
             float bf[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) bf[i] = (float)Tm[kap(g, i) * CHP + 16 * Jb + l16];
+            for (int i = 0; i < 8; ++i) bf[i] = (float)Tm[BL::tp(kap(g, i), 16 * Jb + l16)];
             Yt[u] = f4{0.f, 0.f, 0.f, 0.f};
             PR::mma(Yt[u], PR::lds_pair(ar + 4 * g, ar + 16 + 4 * g), PR::make(bf));
         }
@@ -496,11 +512,11 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int Ib = 2 + u;
-            const E* row = &Tm[(16 * Ib + l16) * CHP + 32];
+            const int rw = 16 * Ib + l16;
             f4 Z = {0.f, 0.f, 0.f, 0.f};
-            PR::mma(Z, PR::lds_pair(row + 4 * g, row + 16 + 4 * g), yf);
+            PR::mma(Z, PR::lds_pair(Tm + BL::tp(rw, 32 + 4 * g), Tm + BL::tp(rw, 48 + 4 * g)), yf);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Tm[(16 * Ib + 4 * g + j) * CHP + 16 * Jb + l16] = (E)(-Z[j]);
+            for (int j = 0; j < 4; ++j) Tm[BL::tp(16 * Ib + 4 * g + j, 16 * Jb + l16)] = (E)(-Z[j]);
         }
     }
     lds_barrier();
@@ -509,7 +525,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     {
         // (256 threads; every LDS read is issued before the stores)
         const int tid = threadIdx.x;
-        constexpr int N1 = SM::out1Bytes / 16, NP = CH * CHP * (int)sizeof(E) / 16;
+        constexpr int N1 = SM::out1Bytes / 16, NP = BL::TPE * (int)sizeof(E) / 16;
         constexpr int J1 = (N1 + 255) / 256, JP = (NP + 255) / 256;
         const uint4* src = reinterpret_cast<const uint4*>(smem + SM::oOut);
         const uint4* srcP = reinterpret_cast<const uint4*>(smem + SM::oP);
@@ -600,7 +616,6 @@ chain_kernel(const ChainIO io) {
     static_assert(SM::fits, "chain LDS budget or wave layout");
     constexpr int NT = SM::NT, NWC = SM::NWC, CW0 = SM::CW0;
     constexpr int NKS = DK / 32, NMK = DK / 16;
-    constexpr int DKP = BL::DKP, CHP = BL::CHP;
     constexpr int COPY = STATE ? BL::stateBytes : BL::bytes;  // bytes of each block copied to LDS
 
     // Two arrays: the block buffers and the v/w slots. Separate objects let the compiler see that
@@ -757,13 +772,13 @@ chain_kernel(const ChainIO io) {
                 for (int c = 0; c < NT; ++c) O[c][mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
-                    const E* er_ = &En[(16 * mt + l16) * DKP + 32 * s];
-                    const Frag ef = PR::lds_pair(er_ + 4 * g, er_ + 16 + 4 * g);
+                    const int rw = 16 * mt + l16;
+                    const Frag ef = PR::lds_pair(En + BL::en(rw, 32 * s + 4 * g), En + BL::en(rw, 32 * s + 16 + 4 * g));
 #pragma unroll
                     for (int c = 0; c < NT; ++c) PR::mma(D[c][mt], ef, Sf[c][s]);
                     if constexpr (!STATE) {
-                        const E* qr_ = &Qh[(16 * mt + l16) * DKP + 32 * s];
-                        const Frag qf = PR::lds_pair(qr_ + 4 * g, qr_ + 16 + 4 * g);
+                        const Frag qf =
+                            PR::lds_pair(Qh + BL::en(rw, 32 * s + 4 * g), Qh + BL::en(rw, 32 * s + 16 + 4 * g));
 #pragma unroll
                         for (int c = 0; c < NT; ++c) PR::mma(O[c][mt], Sf[c][s], qf);
                     }
@@ -785,8 +800,8 @@ chain_kernel(const ChainIO io) {
                 for (int c = 0; c < NT; ++c) Dl[c][mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 <= mt / 2; ++s2) {
-                    const E* tr = &Tm[(16 * mt + l16) * CHP + 32 * s2];
-                    const Frag tf = PR::lds_pair(tr + 4 * g, tr + 16 + 4 * g);
+                    const int rw = 16 * mt + l16;
+                    const Frag tf = PR::lds_pair(Tm + BL::tp(rw, 32 * s2 + 4 * g), Tm + BL::tp(rw, 32 * s2 + 16 + 4 * g));
 #pragma unroll
                     for (int c = 0; c < NT; ++c) PR::mma(Dl[c][mt], tf, Df[c][s2]);
                 }
@@ -803,8 +818,9 @@ chain_kernel(const ChainIO io) {
                 for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
                     for (int s2 = 0; s2 <= nt / 2; ++s2) {
-                        const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
-                        const Frag pf = PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g);
+                        const int rw = 16 * nt + l16;
+                        const Frag pf =
+                            PR::lds_pair(Pm + BL::tp(rw, 32 * s2 + 4 * g), Pm + BL::tp(rw, 32 * s2 + 16 + 4 * g));
 #pragma unroll
                         for (int c = 0; c < NT; ++c) PR::mma(O[c][nt], Df[c][s2], pf);
                     }
@@ -821,8 +837,9 @@ chain_kernel(const ChainIO io) {
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const E* kr = &KbT[(16 * mk + l16) * CHP + 32 * s2];
-                    const Frag kf = PR::lds_pair(kr + 4 * g, kr + 16 + 4 * g);
+                    const int rw = 16 * mk + l16;
+                    const Frag kf =
+                        PR::lds_pair(KbT + BL::kbt(rw, 32 * s2 + 4 * g), KbT + BL::kbt(rw, 32 * s2 + 16 + 4 * g));
 #pragma unroll
                     for (int c = 0; c < NT; ++c) PR::mma(Sacc[c][mk], kf, Df[c][s2]);
                 }
