@@ -12,7 +12,10 @@ Source of the update rule: the page "NVIDIA представила Gated DeltaNe
 state-update equation S_t = (I - k_t (b_t*k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t*v_t)^T.
 The readout o_t = S_t^T q_t (updated state) is a reading, not printed on the pages.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against a hand-worked example,
+``backward`` (reverse mode of the same recurrence) is pinned by ``tests/oracle_bwd_pins.py``
+against finite differences, a closed form, the affine dependence on S0 and automatic
+differentiation of a transition-matrix formulation.
+Every forward function is pinned by ``tests/test_oracle_pins.py`` against a hand-worked example,
 brute-force transition products, closed forms and textbook special cases.
 """
 from __future__ import annotations
@@ -64,6 +67,8 @@ def _declare(lib) -> None:
     L = ctypes.c_long
     lib.gdn2_oracle_forward.argtypes = [p, p, p, p, p, p, p, p, p, L, L, L, L, L, ctypes.c_int]
     lib.gdn2_oracle_forward.restype = ctypes.c_int
+    lib.gdn2_oracle_backward.argtypes = [p] * 16 + [L, L, L, L, L, ctypes.c_int]
+    lib.gdn2_oracle_backward.restype = ctypes.c_int
 
 
 def default_threads() -> int:
@@ -149,3 +154,39 @@ def broadcast_gates(alpha, b, w, d_k: int, d_v: int, *, alpha_scalar: bool, beta
     else:
         w = _f64(w)
     return alpha, b, w
+
+
+def backward(q, k, v, alpha, b, w, S0=None, dO=None, dS_T=None, *, threads: int | None = None, lib=None):
+    """Gradients of L = sum_t <dO_t, o_t> + <dS_T, S_T> in float64 (reverse mode of the
+    recurrence, token by token; see gdn2_oracle.c).
+
+    Shapes as in ``forward``; dO: [B, T, H, d_v] or None (zeros); dS_T: [B, H, d_k, d_v] or None.
+    Returns a dict with dq, dk, dalpha, db ([B, T, H, d_k]), dv, dw ([B, T, H, d_v]) and dS0
+    ([B, H, d_k, d_v]) as float64 numpy arrays.
+    """
+    q, k, v, alpha, b, w = (_f64(x) for x in (q, k, v, alpha, b, w))
+    S0, dO, dS_T = _f64(S0), _f64(dO), _f64(dS_T)
+    if q.ndim != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, x, d in (("k", k, dk), ("alpha", alpha, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
+        if x.shape != (B, T, H, d):
+            raise ValueError(f"{name} has shape {x.shape}, expected {(B, T, H, d)}")
+    if dO is not None and dO.shape != (B, T, H, dv):
+        raise ValueError(f"dO has shape {dO.shape}, expected {(B, T, H, dv)}")
+    for name, x in (("S0", S0), ("dS_T", dS_T)):
+        if x is not None and x.shape != (B, H, dk, dv):
+            raise ValueError(f"{name} has shape {x.shape}, expected {(B, H, dk, dv)}")
+    out = {n: np.zeros((B, T, H, dk)) for n in ("dq", "dk", "dalpha", "db")}
+    out.update({n: np.zeros((B, T, H, dv)) for n in ("dv", "dw")})
+    out["dS0"] = np.zeros((B, H, dk, dv))
+    lib = lib or load_library()
+    rc = lib.gdn2_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                  _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
+                                  _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out["dv"]),
+                                  _ptr(out["dw"]), _ptr(out["dS0"]), B, T, H, dk, dv,
+                                  int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"gdn2_oracle_backward failed with status {rc}")
+    return out
