@@ -41,10 +41,14 @@ def mutant_dir(tmp_path_factory):
 def test_mutant_is_caught(name, mutant_dir):
     old, new = MUTANTS[name]
     src = open(oracle._SRC).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    # the forward pass is everything before the backward's section (which recomputes states
+    # with the same lines; its own mutants live in tests/test_oracle_bwd.py)
+    cut = src.index("/*\n * Backward:")
+    fwd_src, rest = src[:cut], src[cut:]
+    assert fwd_src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
     path = os.path.join(mutant_dir, name + ".c")
     with open(path, "w") as f:
-        f.write(src.replace(old, new))
+        f.write(fwd_src.replace(old, new) + rest)
     lib = oracle.load_library(oracle.build(force=True, out_path=path[:-2] + ".so", src_path=path))
 
     def fwd(q, k, v, alpha, b, w, S0):
