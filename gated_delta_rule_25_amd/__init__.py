@@ -8,6 +8,7 @@ if the library is not built or no GPU is present, calls raise.
     o, S_T = chunk_fwd(q, k, v, alpha, b, w, S0)        # prefill, chunk length 64
     o, S_T = recurrent_fwd(q, k, v, alpha, b, w, S0)    # token-by-token fp32 prefill
     o = decode_step(q, k, v, alpha, b, w, S)            # one token, S updated in place
+    g = chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T)    # gradients (dict: dq, dk, dv, ...)
 
 Shapes: q, k, alpha, b [B, T, H, d_k]; v, w [B, T, H, d_v]; states [B, H, d_k, d_v] float32;
 decode drops the T axis. Scalar gates: alpha [B, T, H] (alpha_scalar) and b = beta [B, T, H]
@@ -20,7 +21,8 @@ import os
 
 import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to it)
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes",
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
+           "chunk_bwd_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +58,10 @@ def load():
     lib.gdn2_chunk_fwd.restype = ctypes.c_int
     lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
     lib.gdn2_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn2_chunk_bwd.argtypes = [p] * 16 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_bwd.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
+    lib.gdn2_chunk_bwd_workspace_bytes.restype = sz
     lib.gdn2_recurrent_fwd.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p]
     lib.gdn2_recurrent_fwd.restype = ctypes.c_int
     lib.gdn2_decode_step.argtypes = [p] * 8 + [i32] * 4 + [ctypes.c_int, u32, p]
@@ -146,6 +152,45 @@ def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspa
     if st != 0:
         raise Gdn2Error("gdn2_chunk_fwd", st)
     return o, S_out
+
+
+def chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
+    return int(load().gdn2_chunk_bwd_workspace_bytes(B, T, H, d_k, d_v,
+                                                     BF16 if dtype == torch.bfloat16 else F32, flags))
+
+
+def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=None, stream=None):
+    """Gradients of sum <dO, o> + <dS_T, S_T> for the prefill (bf16 inputs, general gates).
+
+    Returns a dict of float32 tensors: dq, dk, dalpha, db [B, T, H, d_k], dv, dw [B, T, H, d_v] and
+    dS0 [B, H, d_k, d_v]. `out` may supply any of them; the workspace is allocated here unless given.
+    """
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 4)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, x in (("S0", S0), ("dO", dO), ("dS_T", dS_T)):
+        if x is not None and (x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda):
+            raise TypeError(f"{name} must be a contiguous float32 GPU tensor")
+    out = dict(out or {})
+    f32 = dict(device=q.device, dtype=torch.float32)
+    for name in ("dq", "dk", "dalpha", "db"):
+        out.setdefault(name, torch.empty(B, T, H, dk, **f32))
+    for name in ("dv", "dw"):
+        out.setdefault(name, torch.empty(B, T, H, dv, **f32))
+    out.setdefault("dS0", torch.empty(B, H, dk, dv, **f32))
+    dt = _dtype_code(q)
+    need = int(lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                            _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dS0"]),
+                            B, T, H, dk, dv, dt, flags, _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_bwd", st)
+    return out
 
 
 def recurrent_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, stream=None):

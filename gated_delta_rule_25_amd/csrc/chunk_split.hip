@@ -20,7 +20,7 @@
 // copy is a flat 16-byte-per-lane stream. The host walks the sequence in ranges of chunks
 // through a workspace ring (prep of a range, then chain of the range, the state carried in
 // S_out), so the ring can be sized to stay in the Infinity Cache.
-#include "chunk_common.h"
+#include "chunk_blob.h"
 #include "kernels.h"
 
 namespace gdn2 {
@@ -28,66 +28,6 @@ namespace gdn2 {
 namespace {
 
 using namespace chunk;
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
-
-// Per-chunk operand blob (also the chain kernel's LDS buffer layout). Matrices are addressed
-// through en() (E_hat, Q_hat: [64][DK]), kbt() (K_bar^T: [DK][64]) and tp() (T, P: [64][64],
-// lower block triangular), in elements; the chain kernel reads 4-element units of 16 consecutive
-// rows at one column, and the layouts give those 16 reads distinct LDS banks.
-//  - fp16: no padding. Within a row the 4-element (8-byte) units are permuted by an XOR with the
-//    row index (row & 15 for rows of 64 dwords or more; (row >> 1) & 7 for rows of 16 dwords,
-//    whose consecutive rows already alternate between the two halves of the banks). T and P keep
-//    only the column blocks the chain reads: 32 columns for rows 0..31, 64 for rows 32..63.
-//  - fp32: rows padded by 4 elements, full 64x64 T and P.
-template <int DK, bool F16>
-struct Blob {
-    using E = typename Prec<F16>::E;
-    static constexpr int ES = (int)sizeof(E);
-    static constexpr int PAD = F16 ? 0 : 4;
-    static constexpr int DKP = DK + PAD, CHP = CH + PAD;
-    static constexpr int TPE = F16 ? 32 * 32 + 32 * 64 : CH * CHP;  // elements of T or P
-    __device__ static int unit_sw(int r, int width) { return width >= 64 ? (r & 15) : ((r >> 1) & 7); }
-    __device__ static int sw(int r, int c, int width) {
-        return F16 ? ((((c >> 2) ^ unit_sw(r, width)) << 2) | (c & 3)) : c;
-    }
-    __device__ static int en(int r, int c) { return r * DKP + sw(r, c, DK); }
-    __device__ static int kbt(int r, int c) { return r * CHP + sw(r, c, CH); }
-    __device__ static int tp(int r, int c) {
-        if constexpr (F16) return r < 32 ? r * 32 + sw(r, c, 32) : 32 * 32 + (r - 32) * 64 + sw(r, c, 64);
-        return r * CHP + c;
-    }
-    // The state recurrence alone needs the prefix [En .. beta]; the outputs also need P and Q_hat.
-    static constexpr int oEn = 0;                       // E_hat, negated
-    static constexpr int oKbT = oEn + CH * DKP * ES;    // K_bar^T
-    static constexpr int oTm = oKbT + DK * CHP * ES;    // T
-    static constexpr int oGC = oTm + TPE * ES;          // float [DK]    gamma_last
-    static constexpr int oBeta = oGC + DK * 4;          // float [64]    scalar beta per row (scalar-beta gates)
-    static constexpr int stateBytes = oBeta + CH * 4;
-    static constexpr int oP = stateBytes;               // P
-    static constexpr int oQh = oP + TPE * ES;           // Q_hat
-    static constexpr int bytes = (oQh + CH * DKP * ES + 255) / 256 * 256;
-    static_assert(stateBytes % 16 == 0 && oP % 16 == 0, "16-byte copies");
-};
-
-// Copy `bytes` (a multiple of 16) from global to LDS with `nw` wavefronts (this one is `cw`),
-// 1 KiB per instruction: lane i moves 16 bytes to LDS base + 16 i. Counted by vmcnt; the
-// caller waits.
-__device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int cw, int nw, int lane) {
-    for (int off = cw * 1024; off < bytes; off += nw * 1024) {
-        if (off + lane * 16 < bytes)
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(g + off + lane * 16), (lds_ptr_t)(l + off), 16, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-// All but the newest N (< 16) vector-memory operations done (vmcnt(N)).
-template <int N>
-__device__ __forceinline__ void wait_vm_but() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
-}
 
 // Eight elements c0..c0+7 (c0 a multiple of 8) of row r of E_hat or Q_hat to the blob: two
 // 8-byte stores for fp16 (the two 4-element units land where en() puts them), two 16-byte
@@ -598,6 +538,13 @@ struct ChainIO {
     long out_bh, out_seg;
     int out_ld;
     int out_last;  // only the last segment writes S_out
+    int phi_tiles = 0;  // transition tiles (over d_k) after the value tiles, state-only pass
+    // Saves for the backward pass (state-only pass, sequential): the state at the start of every
+    // chunk, S_save + ((bh * save_nch) + chunk) * DK * DV; D' and Delta rows, [B, T, H, DV] fp32
+    float* S_save = nullptr;
+    int save_nch = 0;
+    float* Dp_save = nullptr;
+    float* Dl_save = nullptr;
 };
 
 // STATE = true: the state recurrence alone, for the segment transitions of a long sequence. Tiles
@@ -627,7 +574,7 @@ chain_kernel(const ChainIO io) {
     const int T = io.T, H = io.H, DV = io.DV;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int vt = DV / DVT;                  // value tiles
-    const int tiles = vt + (STATE ? DK / DVT : 0);
+    const int tiles = vt + io.phi_tiles;
     const int BH = io.B * H, BHp = (BH + 7) / 8 * 8;
     const int seg = blockIdx.x / (BHp * tiles);
     const int x = blockIdx.x % (BHp * tiles);
@@ -714,6 +661,23 @@ chain_kernel(const ChainIO io) {
         return PR::make(t);
     };
 
+    // accumulator tiles of 64 token rows x 16 columns ([mt][j]: row 16 mt + 4 g + j, column l16 of
+    // tile c) to [B, T, H, DV] rows of this sequence; rows past the end are dropped
+    int t0_cur = 0;
+    auto save_rows = [&](float* dst, const f4 (&X)[NT][4]) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + (long)bb * T * H * DV, (unsigned)T * H * DV * 4u);
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const unsigned row = (unsigned)(t0_cur + 16 * mt + 4 * g + j);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(X[c][mt][j]), rs,
+                                                          (int)(((row * H + hh) * DV + col0 + 16 * c + l16) * 4u), 0, 0);
+                }
+    };
+
     if (copier) {
         dma_flat(blobs, smem + SM::oBuf0, COPY, wv - CW0, CW0, lane);
         wait_dma();
@@ -724,6 +688,7 @@ chain_kernel(const ChainIO io) {
     for (int nc = 0; nc < n_count; ++nc) {
         const int n = c_begin + nc;
         const int t0 = n * CH;
+        t0_cur = t0;
         const int L = min(CH, T - t0);
         char* buf = smem + ((nc & 1) ? SM::oBuf1 : SM::oBuf0);
         const E* Qh = reinterpret_cast<const E*>(buf + BL::oQh);
@@ -743,6 +708,17 @@ chain_kernel(const ChainIO io) {
                 wait_dma();
             } else {
                 wait_vm_but<4 * NT>();
+            }
+            if (io.S_save) {
+                // the state at the start of this chunk, for the backward pass
+                float* sv = io.S_save + ((size_t)bh * io.save_nch + n) * DK * DV;
+#pragma unroll
+                for (int c = 0; c < NT; ++c)
+#pragma unroll
+                    for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            sv[(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16] = Sacc[c][mk][j];
             }
             f4 D[NT][4];
 #pragma unroll
@@ -787,6 +763,7 @@ chain_kernel(const ChainIO io) {
             if constexpr (F16) lookahead_schedule<(STATE ? 4 : 8) * NKS, 6, NT>();
             // the next chunk's v, w into this wave's slot, now that its reads are long done
             if (nc + 1 < n_count && !phi) dma_vw(n + 1);
+            if (io.Dp_save) save_rows(io.Dp_save, D);
             // Delta = T D'
             Frag Df[NT][2];
 #pragma unroll
@@ -807,6 +784,7 @@ chain_kernel(const ChainIO io) {
                 }
             }
             if constexpr (F16) lookahead_schedule<6, 4, NT>();
+            if (io.Dl_save) save_rows(io.Dl_save, Dl);
 #pragma unroll
             for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -979,8 +957,10 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         const ChainIO tr{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G - 1, a.B, a.T, a.H, a.DV,
                          nullptr, 0, 0, a.DV,
                          psiphi, (long)(G - 1) * DK * (a.DV + DK), ld * (a.DV + DK), a.DV + DK, 0};
+        ChainIO trp = tr;
+        trp.phi_tiles = DK / DVT;
         hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
-                           dim3(kChainThreads), 0, st, tr);
+                           dim3(kChainThreads), 0, st, trp);
         hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 8)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
         const ChainIO fu{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G, a.B, a.T, a.H, a.DV,
                          sseg, (long)G * DK * a.DV, ld * a.DV, a.DV,
@@ -1017,7 +997,36 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
     }
 }
 
+template <int DK>
+hipError_t launch_states_t(const ChunkArgs& a, char* blobs, float* S_save, float* Dp_save, float* Dl_save,
+                           hipStream_t st) {
+    constexpr int DVT = DK < 64 ? DK : 64;
+    const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
+    const int nch = (a.T + CH - 1) / CH;
+    hipLaunchKernelGGL((prep_kernel<DK, true, false, false>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k, a.alpha,
+                       a.b, a.B, a.T, a.H, 0, nch, blobs);
+    ChainIO io{a.v, a.w, nullptr, blobs, nch, 0, nch, nch, 1, a.B, a.T, a.H, a.DV,
+               a.S0, (long)DK * a.DV, 0, a.DV, nullptr, 0, 0, a.DV, 0};
+    io.S_save = S_save;
+    io.save_nch = nch;
+    io.Dp_save = Dp_save;
+    io.Dl_save = Dl_save;
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true>), dim3(BHp * (a.DV / DVT)), dim3(kChainThreads),
+                       0, st, io);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_split_states(const ChunkArgs& a, char* blobs, float* S_save, float* Dp_save, float* Dl_save,
+                               hipStream_t s) {
+    if (!a.bf16 || a.flags != 0u || !split_supported(a.T, a.H, a.DK, a.DV, true)) return hipErrorNotSupported;
+    switch (a.DK) {
+        case 32: return launch_states_t<32>(a, blobs, S_save, Dp_save, Dl_save, s);
+        case 64: return launch_states_t<64>(a, blobs, S_save, Dp_save, Dl_save, s);
+        default: return launch_states_t<128>(a, blobs, S_save, Dp_save, Dl_save, s);
+    }
+}
 
 bool split_supported(int T, int H, int DK, int DV, bool bf16) {
     if (DK != DV) return false;

@@ -188,6 +188,58 @@ gdn2_status gdn2_decode_step(const void* q, const void* k, const void* v, const 
                          gate_flags, static_cast<hipStream_t>(stream));
 }
 
+size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                      gdn2_dtype in_dtype, uint32_t gate_flags) {
+    if (B <= 0 || H <= 0 || T <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    if (!gdn2::bwd_supported(T, H, d_k, d_v, in_dtype == GDN2_BF16, gate_flags)) return 0;
+    Sizes sz;
+    if (!sizes_of(B, T, H, d_k, d_v, &sz)) return 0;
+    return gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v);
+}
+
+gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,
+                           const void* b, const void* w, const float* S0, const float* dO,
+                           const float* dS_T, float* dq, float* dk, float* dv, float* dalpha,
+                           float* db, float* dw, float* dS0, int32_t B, int32_t T, int32_t H,
+                           int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (in_dtype != GDN2_BF16 || gate_flags != 0u) return GDN2_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN2_ERR_UNSUPPORTED;
+    Sizes sz;
+    if (!sizes_of(B, T, H, d_k, d_v, &sz)) return GDN2_ERR_SHAPE;
+    if (!gdn2::bwd_supported(T, H, d_k, d_v, true, gate_flags)) return GDN2_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !dO || !dq || !dk || !dv || !dalpha || !db || !dw))
+        return GDN2_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
+    size_t need = 0;
+    if (T > 0) {
+        need = gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v);
+        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+    }
+    const Range ins[] = {range_of(q, sz.qk * 2), range_of(k, sz.qk * 2), range_of(v, sz.vw * 2),
+                         range_of(alpha, sz.qk * 2), range_of(b, sz.qk * 2), range_of(w, sz.vw * 2),
+                         range_of(S0, sz.state * 4), range_of(dO, sz.vw * 4), range_of(dS_T, sz.state * 4)};
+    const Range outs[] = {range_of(dq, sz.qk * 4), range_of(dk, sz.qk * 4), range_of(dalpha, sz.qk * 4),
+                          range_of(db, sz.qk * 4), range_of(dv, sz.vw * 4), range_of(dw, sz.vw * 4),
+                          range_of(dS0, sz.state * 4), range_of(T > 0 ? workspace : nullptr, need)};
+    const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+    for (int i = 0; i < nout; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    gdn2::BwdArgs a{q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
+                    B, T, H, d_k, d_v, true, gate_flags, workspace, workspace_bytes};
+    const hipError_t e = gdn2::launch_bwd(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 const char* gdn2_status_str(gdn2_status s) {
     switch (s) {
         case GDN2_OK: return "ok";

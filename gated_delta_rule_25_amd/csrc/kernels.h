@@ -44,5 +44,25 @@ hipError_t launch_split(const ChunkArgs& a, hipStream_t s);
 bool split_supported(int T, int H, int DK, int DV, bool bf16);
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16);
 size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16);
+// Prep over every chunk into `blobs` ([b*h][chunk] operand blocks), then the state-only chain in
+// order, saving the state at the start of every chunk ([b*h][chunk][DK][DV]) and the rows of D'
+// and Delta ([B, T, H, DV]). bf16 inputs, general gates.
+hipError_t launch_split_states(const ChunkArgs& a, char* blobs, float* S_save, float* Dp_save, float* Dl_save,
+                               hipStream_t s);
+
+// Backward of the chunkwise prefill (bf16 inputs, general gates, d_k = d_v in {32, 64, 128}).
+struct BwdArgs {
+    const void *q, *k, *v, *alpha, *b, *w;
+    const float *S0, *dO, *dS_T;
+    float *dq, *dk, *dv, *dalpha, *db, *dw, *dS0;
+    int B, T, H, DK, DV;
+    bool bf16;
+    uint32_t flags;
+    void* workspace;
+    size_t workspace_bytes;
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
+bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags);
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
 
 }  // namespace gdn2

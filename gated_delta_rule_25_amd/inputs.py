@@ -112,6 +112,17 @@ def make_inputs(wl: Workload, *, device: str = "cpu") -> dict:
                 alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)
 
 
+def make_cotangents(wl: Workload, *, device: str = "cpu", final_state: bool = True) -> dict:
+    """Seeded cotangents for the backward: dO [B, T, H, d_v] and dS_T [B, H, d_k, d_v] (or None),
+    both standard normal in float32, drawn from their own stream (seed + 7919)."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 7919))
+    f32 = np.float32
+    dO = rng.standard_normal((wl.B, wl.T, wl.H, wl.d_v), dtype=f32)
+    dS = rng.standard_normal((wl.B, wl.H, wl.d_k, wl.d_v), dtype=f32) if final_state else None
+    return dict(dO=torch.from_numpy(dO).to(device),
+                dS_T=None if dS is None else torch.from_numpy(dS).to(device))
+
+
 def make_decode_inputs(B: int, H: int, d_k: int, d_v: int, steps: int, *, seed: int,
                        alpha_mu: float = 3.0, s0_std: float = 0.1, dtype: str = "bf16",
                        device: str = "cpu", generator: str = "numpy") -> dict:

@@ -146,6 +146,40 @@ gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const 
                              int32_t H, int32_t d_k, int32_t d_v, gdn2_dtype in_dtype,
                              uint32_t gate_flags, void *stream);
 
+/*
+ * Backward of the prefill: the gradients of L = sum_t <dO_t, o_t> + <dS_T, S_T> for the recurrence
+ * above (o_t and S_T as gdn2_chunk_fwd computes them from the same inputs), through the chunkwise
+ * WY form with C = 64 [GDN2-summary, paragraph "Реализация"]. The forward is recomputed inside
+ * the call; nothing from a previous gdn2_chunk_fwd call is needed.
+ *
+ *   inputs   q, k, v, alpha, b, w, S0 as in gdn2_chunk_fwd (S0 NULL = zeros);
+ *            dO [B, T, H, d_v] float32 (required when T > 0);
+ *            dS_T [B, H, d_k, d_v] float32 (NULL = zeros)
+ *   outputs  dq, dk, dalpha, db [B, T, H, d_k] float32; dv, dw [B, T, H, d_v] float32;
+ *            dS0 [B, H, d_k, d_v] float32 (NULL = not stored). Every output is overwritten.
+ *
+ * Supported: bf16 inputs, general gates (gate_flags == 0), d_k == d_v in {32, 64, 128}, and one
+ * sequence's rows below 4 GiB ((T + 64)*H*d_v*4 < 2^32 bytes); anything else returns
+ * GDN2_ERR_UNSUPPORTED. Arithmetic as in the forward: fp16 matrix-core operands with fp32
+ * accumulation for the state chains, fp32 for the per-chunk gradient work.
+ * The workspace (required when T > 0, 256-byte aligned, at least
+ * gdn2_chunk_bwd_workspace_bytes) holds the operand blocks, the state and its gradient at every
+ * chunk boundary and the per-chunk intermediate products; its contents are scratch. No output may
+ * overlap an input, another output or the workspace (GDN2_ERR_ALIAS). Other errors, ownership
+ * and stream semantics as for gdn2_chunk_fwd.
+ */
+gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *alpha,
+                           const void *b, const void *w, const float *S0, const float *dO,
+                           const float *dS_T, float *dq, float *dk, float *dv, float *dalpha,
+                           float *db, float *dw, float *dS0, int32_t B, int32_t T, int32_t H,
+                           int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes gdn2_chunk_bwd needs at these sizes; 0 when it does not take them (or T == 0,
+ * which needs none). */
+size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                      gdn2_dtype in_dtype, uint32_t gate_flags);
+
 /* A static, human-readable name for a status code. */
 const char *gdn2_status_str(gdn2_status s);
 

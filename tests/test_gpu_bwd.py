@@ -1,0 +1,120 @@
+"""GPU parity: the backward of the chunkwise prefill against the fp64 oracle's backward.
+
+The oracle differentiates the token-by-token recurrence (oracle/gdn2_oracle.c, pinned by
+tests/oracle_bwd_pins.py); the library differentiates the chunkwise form. Both take the same
+bf16-rounded inputs and float32 cotangents. Bar: normwise relative error (parity.py) at most
+TOLB = 2e-3 on every gradient, the bar of the bf16 forward (measured: 0.5e-4 to 5.4e-4); sizes span several chunks and a ragged last chunk. The intermediate
+stages (the chunk-start states and the state gradients at chunk ends in the workspace) are
+checked against the oracle too, so a failure names its stage.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import banner, normwise_err
+from gated_delta_rule_25_amd.inputs import WORKLOADS, make_cotangents, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+TOLB = 2e-3
+NAMES = ("dq", "dk", "dv", "dalpha", "db", "dw", "dS0")
+
+
+def _g():
+    import gated_delta_rule_25_amd as g
+    return g
+
+
+def _cuda(x):
+    return None if x is None else x.cuda()
+
+
+def _ref(ins, cot):
+    return oracle.backward(ins["q"], ins["k"], ins["v"], ins["alpha"], ins["b"], ins["w"], ins["S0"],
+                           cot["dO"], cot["dS_T"])
+
+
+def _gpu(ins, cot, workspace=None):
+    g = _g()
+    d = {n: _cuda(ins[n]) for n in ("q", "k", "v", "alpha", "b", "w", "S0")}
+    out = g.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"], _cuda(cot["dO"]),
+                      _cuda(cot["dS_T"]), workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(name, wl, final_state=True, tol=TOLB):
+    ins = make_inputs(wl)
+    cot = make_cotangents(wl, final_state=final_state)
+    ref = _ref(ins, cot)
+    got = _gpu(ins, cot)
+    errs = {n: normwise_err(got[n], ref[n]) for n in NAMES}
+    print(f"  {name}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= tol for e in errs.values()), errs
+
+
+CASES = [
+    ("d32_ragged", scaled(WORKLOADS["prefill_1p3b"], B=1, T=100, H=2, d_k=32, d_v=32)),
+    ("d64_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=150, H=2, d_k=64, d_v=64)),
+    ("d128_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=3)),
+    ("d128_T1", scaled(WORKLOADS["prefill_1p3b"], B=1, T=1, H=2)),
+    ("d128_T64", scaled(WORKLOADS["prefill_1p3b"], B=1, T=64, H=2)),
+    ("d128_T65", scaled(WORKLOADS["prefill_1p3b"], B=1, T=65, H=2)),
+    ("d128_zero_s0", scaled(WORKLOADS["prefill_1p3b"], B=1, T=300, H=2, s0_std=0.0)),
+    ("d128_slow_decay", scaled(WORKLOADS["long_prefill"], B=1, T=700, H=2)),
+]
+
+
+@pytest.mark.parametrize("name,wl", CASES, ids=[c[0] for c in CASES])
+def test_bwd_matches_oracle(name, wl):
+    banner(f"bwd {name} {wl}")
+    _check(name, wl)
+
+
+def test_bwd_without_final_state_cotangent():
+    banner("bwd, dS_T = None")
+    _check("no_dS_T", scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=2), final_state=False)
+
+
+def test_bwd_stages_match_oracle():
+    """The chunk-start states the forward chain saves and the state gradients at chunk ends the
+    reverse chain saves, read back from the workspace, equal the oracle's."""
+    banner("bwd stages")
+    g = _g()
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=1, T=150, H=2)
+    ins = make_inputs(wl)
+    cot = make_cotangents(wl)
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
+    nch = (T + 63) // 64
+    need = g.chunk_bwd_workspace_bytes(B, T, H, dk, dv)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    _gpu(ins, cot, workspace=ws)
+    blob_bytes = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv) - B * H * dk * dv * 4  # one slot
+    off = (nch * blob_bytes + 255) // 256 * 256
+    st_bytes = B * H * nch * dk * dv * 4
+    S_save = ws[off:off + st_bytes].view(torch.float32).view(B * H, nch, dk, dv).cpu().double().numpy()
+    G_save = ws[off + st_bytes:off + 2 * st_bytes].view(torch.float32).view(B * H, nch, dk, dv).cpu().double().numpy()
+    x = {n: ins[n] for n in ("q", "k", "v", "alpha", "b", "w")}
+    for n in range(nch):
+        t0, t1 = 64 * n, min(64 * n + 64, T)
+        _, S_start = oracle.forward(*(v[:, :t0] for v in x.values()), S0=ins["S0"])
+        e = normwise_err(S_save[:, n].reshape(B, H, dk, dv), S_start)
+        # dL/dS at the end of chunk n: the backward of the suffix from there, started at that state
+        _, S_end = oracle.forward(*(v[:, :t1] for v in x.values()), S0=ins["S0"])
+        suf = oracle.backward(*(v[:, t1:] for v in x.values()), S0=S_end, dO=cot["dO"][:, t1:],
+                              dS_T=cot["dS_T"])
+        eg = normwise_err(G_save[:, n].reshape(B, H, dk, dv), suf["dS0"])
+        print(f"  chunk {n}: start state err {e:.2e}, end gradient err {eg:.2e}", flush=True)
+        assert e <= 2e-3 and eg <= TOLB, (n, e, eg)
+
+
+def test_bwd_no_tokens_copies_final_cotangent():
+    banner("bwd, T = 0")
+    g = _g()
+    dS = torch.randn(2, 3, 64, 64, device="cuda")
+    e = torch.empty(2, 0, 3, 64, dtype=torch.bfloat16, device="cuda")
+    dO = torch.empty(2, 0, 3, 64, device="cuda")
+    out = g.chunk_bwd(e, e, e, e, e, e, None, dO, dS)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dS0"], dS)
