@@ -155,6 +155,46 @@ def prefill_leg(g, name, steps, impl):
     return res
 
 
+def bwd_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
+    # q, k, alpha, b, v, w (bf16) + dO (fp32) read; dq, dk, dalpha, db, dv, dw (fp32) written;
+    # S0 and dS_T read and dS0 written, amortised over T
+    return 4 * dk * 2 + 2 * dv * 2 + 4 * dv + 4 * dk * 4 + 2 * dv * 4 + 12 * dk * dv / T
+
+
+def backward_leg(g, steps):
+    """gdn2_chunk_bwd at the prefill shape (B8 H16 T4096 d128 bf16), warm, back to back, on the
+    launch stream."""
+    import torch
+    from gated_delta_rule_25_amd.inputs import WORKLOADS, make_cotangents, make_inputs_torch
+    wl = WORKLOADS["prefill_1p3b"]
+    ins = make_inputs_torch(wl, device="cuda")
+    cot = make_cotangents(wl, device="cuda")
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
+    ws = torch.empty(g.chunk_bwd_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8, device="cuda")
+    out = {}
+    args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w", "S0")] + [cot["dO"], cot["dS_T"]]
+    out = g.chunk_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.chunk_bwd(*args, workspace=ws, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = bwd_bytes_per_head_token(dk, dv, T) * B * T * H
+    res = dict(config=f"B{B} H{H} T{T} d{dk} bf16 gates=general", ms=round(ms, 4),
+               tokens_per_s=round(B * T / (ms * 1e-3), 1), algorithmic_bytes=int(alg),
+               gbs=round(alg / (ms * 1e-3) / 1e9, 1), frac=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               workspace_bytes=int(ws.numel()))
+    print(f"[bench] backward: {ms:.3f} ms/call, {res['tokens_per_s']:.3e} tokens/s, {res['gbs']} GB/s "
+          f"algorithmic ({100 * res['frac']:.1f}% of HBM)", file=sys.stderr, flush=True)
+    del ins, cot, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(g, B, H, d, steps, warmup, seed):
     import torch
     from gated_delta_rule_25_amd.inputs import make_decode_inputs
@@ -227,6 +267,7 @@ def main(argv=None):
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte "
                          "counters)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true", help="skip the backward (gdn2_chunk_bwd) leg")
     ap.add_argument("--skip-others", action="store_true",
                     help="skip the long-context and scalar-gate prefill legs")
     ap.add_argument("--workload", default="prefill_1p3b",
@@ -281,6 +322,9 @@ def main(argv=None):
     torch.cuda.empty_cache()
 
     others = {}
+    bwd = None
+    if not args.skip_backward and args.workload == "prefill_1p3b":
+        bwd = backward_leg(g, 5)
     if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
         for name, steps in (("long_prefill", 3), ("gdn_scalar", 10), ("kda_scalar", 10)):
             others[name] = prefill_leg(g, name, steps, args.impl)
@@ -334,6 +378,7 @@ def main(argv=None):
                      "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         "cold_ms": round(cold_ms, 4),
         "other_prefill": others,
+        "backward": bwd,
         "decode": dec,
         "cpu_baseline": cpu,
     }

@@ -15,7 +15,7 @@
 //     dL/dS  = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'                  (carried to chunk n-1),
 //     dQ_hat = dO S^T,  dE_hat = -dD' S^T,  dK_bar = Delta G'^T,  dgamma_i = sum_j S_ij G'_ij,
 //     dP = dO Delta^T (lower),  dA = -T^T (dDelta D'^T) T^T (strictly lower),
-// then through the factors: with F_rsi = prod_{m=s+1..r} alpha_mi (= e^(G_ri - G_si), never above 1)
+// then through the factors: with F_rsi = prod_{m=s+1..r} alpha_mi (= e^(G_ri - G_si), at most 1)
 //     XA_ri = sum_{s<r} dA_rs k_si F_rsi,   XP_ri = sum_{s<=r} dP_rs k_si F_rsi,
 //     Y_si  = sum_{r>s} dA_rs (b*k)_ri F_rsi + sum_{r>=s} dP_rs q_ri F_rsi,
 //     dq = dQ_hat e^G + XP,  d(b*k) = dE_hat e^G + XA,  dk = dK_bar e^(G_C-G) + Y + b d(b*k),
@@ -29,9 +29,10 @@
 //      columns), the gradient state in MFMA accumulators; writes G' of every chunk, dDelta, dD',
 //      dv, dw and dS0.
 //   3. bwd_contract_kernel: per (b, h, chunk), the products contracted over the value channels
-//      (dQ_hat, dE_hat, dK_bar, dgamma, dP) and dA, in fp32.
-//   4. bwd_key_kernel: per (b, h, chunk), the decay-weighted sums XA, XP, Y by running products
-//      of alpha, the elementwise terms and the reverse cumulative sum; writes dq, dk, db, dalpha.
+//      (dQ_hat, dE_hat, dK_bar, dP, dT) on the matrix cores, dgamma, and dA in fp32.
+//   4. bwd_key_kernel: per (b, h, chunk, 32 key channels), the decay-weighted sums XA, XP, Y
+//      through block references (no factor above 1), the elementwise terms and the reverse
+//      cumulative sum; writes dq, dk, db, dalpha.
 #include "chunk_blob.h"
 #include "kernels.h"
 
@@ -254,128 +255,138 @@ struct ContractIO {
     int B, T, H, DV, nch;
 };
 
+// All five products contract over the value channels j with both operands row-major in j, the
+// fragment layout of the matrix cores: fp16 operands (as in the chains), fp32 accumulation. The
+// value channels are staged in slices of 64 columns; wave w owns output rows 16 w .. 16 w + 15.
 template <int DK>
 __global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO io) {
+    using PR = Prec<true>;
+    using E = _Float16;
+    using Frag = PR::Frag;
     using BL = Blob<DK, true>;
-    constexpr int JS = 32, JP = JS + 1;  // value columns per slice, padded row
-    constexpr int CPT = DK / 16;         // key channels per thread
-    constexpr int SM = (2 * DK + 5 * CH) * JP;
-    static_assert(SM >= 3 * CH * (CH + 1), "the UT adjoint reuses the slice buffers");
-    __shared__ float lds[SM];
-    float* Ss = lds;              // [DK][JP]
-    float* Gs = Ss + DK * JP;     // [DK][JP]
-    float* dOs = Gs + DK * JP;    // [64][JP]
-    float* dDps = dOs + CH * JP;  // [64][JP]
-    float* Dls = dDps + CH * JP;
-    float* dDls = Dls + CH * JP;
-    float* Dps = dDls + CH * JP;
+    constexpr int JS = DK < 64 ? DK : 64;  // value columns per slice (d_v == d_k)
+    constexpr int JP = JS + 4;    // row stride (halves): 2 dwords past a multiple of 32 banks
+    constexpr int NMK = DK / 16;  // 16-channel tiles of the key axis
+    constexpr int SMB = (2 * DK + 5 * CH) * JP * 2;  // bytes of one slice
+    constexpr int TP = CH + 1;
+    constexpr int UTB = 3 * CH * TP * 4;  // the UT adjoint reuses the slice buffers
+    __shared__ __attribute__((aligned(16))) char lds[SMB > UTB ? SMB : UTB];
+    E* Ss = reinterpret_cast<E*>(lds);  // [DK][JP]
+    E* Gs = Ss + DK * JP;               // [DK][JP]
+    E* dOs = Gs + DK * JP;              // [64][JP]: dO, dD', Delta, dDelta, D'
+    E* dDps = dOs + CH * JP;
+    E* Dls = dDps + CH * JP;
+    E* dDls = Dls + CH * JP;
+    E* Dps = dDls + CH * JP;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, DV = io.DV, nch = io.nch;
     const int bh = blockIdx.x / nch, n = blockIdx.x % nch;
     const int hh = bh % H, bb = bh / H;
     const int t0 = n * CH;
-    const int rb = tid / 16, cb = tid % 16;  // rows 4 rb .. 4 rb + 3
-    const float* S = io.S_save + ((size_t)bh * nch + n) * DK * DV;
-    const float* Gp = io.G_save + ((size_t)bh * nch + n) * DK * DV;
+    const size_t cbase = (size_t)bh * nch + n;
+    const float* S = io.S_save + cbase * DK * DV;
+    const float* Gp = io.G_save + cbase * DK * DV;
 
-    float aQ[4][CPT] = {}, aE[4][CPT] = {}, aK[4][CPT] = {}, aP[4][4] = {}, aT[4][4] = {};
-    float ag = 0.f;
+    f4 aQ[NMK], aE[NMK], aK[NMK], aP[4], aT[4];
+#pragma unroll
+    for (int c = 0; c < NMK; ++c) aQ[c] = aE[c] = aK[c] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) aP[c] = aT[c] = f4{0.f, 0.f, 0.f, 0.f};
+
     for (int js = 0; js < DV; js += JS) {
         __syncthreads();
-        for (int x = tid; x < DK * JS; x += 256) {
-            const int i = x / JS, j = x % JS;
-            Ss[i * JP + j] = S[(size_t)i * DV + js + j];
-            Gs[i * JP + j] = Gp[(size_t)i * DV + js + j];
+        for (int x = tid; x < DK * JS / 4; x += 256) {
+            const int i = x / (JS / 4), j = 4 * (x % (JS / 4));
+            const float4 a = *reinterpret_cast<const float4*>(S + (size_t)i * DV + js + j);
+            const float4 b = *reinterpret_cast<const float4*>(Gp + (size_t)i * DV + js + j);
+            *reinterpret_cast<h4*>(Ss + i * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
+            *reinterpret_cast<h4*>(Gs + i * JP + j) = h4{(E)b.x, (E)b.y, (E)b.z, (E)b.w};
         }
-        for (int x = tid; x < CH * JS; x += 256) {
-            const int r = x / JS, j = x % JS;
+        for (int x = tid; x < CH * JS / 4; x += 256) {
+            const int r = x / (JS / 4), j = 4 * (x % (JS / 4));
             const int t = t0 + r;
             const bool ok = t < T;
             const size_t e = (((size_t)bb * T + (ok ? t : 0)) * H + hh) * DV + js + j;
-            dOs[r * JP + j] = ok ? io.dO[e] : 0.f;
-            dDps[r * JP + j] = ok ? io.dDp[e] : 0.f;
-            Dls[r * JP + j] = ok ? io.Dl[e] : 0.f;
-            dDls[r * JP + j] = ok ? io.dDl[e] : 0.f;
-            Dps[r * JP + j] = ok ? io.Dp[e] : 0.f;
+            const float* srcs[5] = {io.dO, io.dDp, io.Dl, io.dDl, io.Dp};
+            E* dsts[5] = {dOs, dDps, Dls, dDls, Dps};
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                float4 a = *reinterpret_cast<const float4*>(srcs[m] + e);
+                if (!ok) a = make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<h4*>(dsts[m] + r * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
+            }
         }
         __syncthreads();
-#pragma unroll 1
-        for (int j = 0; j < JS; ++j) {
-            float o4[4], e4[4], l4[4], d4[4], lc[4], pc[4], s8[CPT], g8[CPT];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = 4 * rb + q;
-                o4[q] = dOs[r * JP + j];
-                e4[q] = dDps[r * JP + j];
-                l4[q] = Dls[r * JP + j];
-                d4[q] = dDls[r * JP + j];
-                lc[q] = Dls[(4 * cb + q) * JP + j];
-                pc[q] = Dps[(4 * cb + q) * JP + j];
+        for (int ks = 0; ks < JS / 32; ++ks) {
+            const int c0 = 32 * ks + 4 * g;
+            auto frag = [&](const E* M, int row) { return PR::lds_pair(M + row * JP + c0, M + row * JP + c0 + 16); };
+            const int r = 16 * wv + l16;
+            const Frag fO = frag(dOs, r), fDp = frag(dDps, r), fL = frag(Dls, r), fdL = frag(dDls, r);
+#pragma unroll
+            for (int c = 0; c < NMK; ++c) {
+                const Frag fS = frag(Ss, 16 * c + l16), fG = frag(Gs, 16 * c + l16);
+                PR::mma(aQ[c], fO, fS);
+                PR::mma(aE[c], fDp, fS);
+                PR::mma(aK[c], fL, fG);
             }
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                s8[c] = Ss[(CPT * cb + c) * JP + j];
-                g8[c] = Gs[(CPT * cb + c) * JP + j];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    aQ[q][c] = fmaf(o4[q], s8[c], aQ[q][c]);
-                    aE[q][c] = fmaf(-e4[q], s8[c], aE[q][c]);
-                    aK[q][c] = fmaf(l4[q], g8[c], aK[q][c]);
-                }
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    aP[q][c] = fmaf(o4[q], lc[c], aP[q][c]);
-                    aT[q][c] = fmaf(d4[q], pc[c], aT[q][c]);
+            for (int c = 0; c < 4; ++c) {
+                if (c <= wv) {
+                    PR::mma(aP[c], fO, frag(Dls, 16 * c + l16));
+                    PR::mma(aT[c], fdL, frag(Dps, 16 * c + l16));
                 }
             }
         }
-        if (tid < DK) {
-            for (int j = 0; j < JS; ++j) ag = fmaf(Ss[tid * JP + j], Gs[tid * JP + j], ag);
-        }
     }
-    const size_t cbase = ((size_t)bh * nch + n);
+    // accumulator [c][j]: row 16 wv + 4 g + j, column 16 c + l16
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 4 * rb + q;
+    for (int c = 0; c < NMK; ++c)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const size_t e = (cbase * CH + r) * DK + CPT * cb + c;
-            io.dQh[e] = aQ[q][c];
-            io.dEh[e] = aE[q][c];
-            io.dKb[e] = aK[q][c];
+        for (int j = 0; j < 4; ++j) {
+            const size_t e = (cbase * CH + 16 * wv + 4 * g + j) * DK + 16 * c + l16;
+            io.dQh[e] = aQ[c][j];
+            io.dEh[e] = -aE[c][j];
+            io.dKb[e] = aK[c][j];
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int cc = 4 * cb + c;
-            io.dPm[(cbase * CH + r) * CH + cc] = cc <= r ? aP[q][c] : 0.f;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * wv + 4 * g + j, cc = 16 * c + l16;
+            io.dPm[(cbase * CH + r) * CH + cc] = (c <= wv && cc <= r) ? aP[c][j] : 0.f;
         }
+    // dgamma_i = sum_j S_ij G'_ij in fp32
+    if (tid < DK) {
+        float ag = 0.f;
+        for (int j = 0; j < DV; j += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(S + (size_t)tid * DV + j);
+            const float4 b = *reinterpret_cast<const float4*>(Gp + (size_t)tid * DV + j);
+            ag += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+        }
+        io.dgam[cbase * DK + tid] = ag;
     }
-    if (tid < DK) io.dgam[cbase * DK + tid] = ag;
 
     // dA = -T^T dT T^T (strictly lower), dT = dDelta D'^T on the lower triangle
     __syncthreads();
-    constexpr int TP = CH + 1;
-    float* Tf = lds;            // [64][TP] T
-    float* Tg = Tf + CH * TP;   // [64][TP] dT
-    float* Xm = Tg + CH * TP;   // [64][TP] T^T dT
+    float* Tf = reinterpret_cast<float*>(lds);  // [64][TP] T
+    float* Tg = Tf + CH * TP;                    // [64][TP] dT
+    float* Xm = Tg + CH * TP;                    // [64][TP] T^T dT
     const _Float16* Tb = reinterpret_cast<const _Float16*>(io.blobs + cbase * BL::bytes + BL::oTm);
     for (int x = tid; x < CH * CH; x += 256) {
         const int r = x / CH, c = x % CH;
         Tf[r * TP + c] = tp_get<BL>(Tb, r, c);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int r = 4 * rb + q, cc = 4 * cb + c;
-            Tg[r * TP + cc] = cc <= r ? aT[q][c] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * wv + 4 * g + j, cc = 16 * c + l16;
+            Tg[r * TP + cc] = (c <= wv && cc <= r) ? aT[c][j] : 0.f;
         }
     __syncthreads();
-    // X = T^T dT: X[r][c] = sum_m T[m][r] dT[m][c]
+    const int rb = tid / 16, cb = tid % 16;  // 4 x 4 tile of rows 4 rb.., columns 4 cb..
     float xacc[4][4] = {};
     for (int m = 0; m < CH; ++m) {
         float tr[4], tc[4];
@@ -394,7 +405,6 @@ __global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO i
 #pragma unroll
         for (int c = 0; c < 4; ++c) Xm[(4 * rb + q) * TP + 4 * cb + c] = xacc[q][c];
     __syncthreads();
-    // dA[r][c] = -sum_m X[r][m] T[c][m], kept for c < r
     float dacc[4][4] = {};
     for (int m = 0; m < CH; ++m) {
         float xr[4], tc[4];
@@ -426,78 +436,119 @@ struct KeyIO {
     int B, T, H, nch;
 };
 
+// One workgroup per (b, h, chunk, 32 key channels): the decay-weighted sums are independent per
+// channel. With G the cumulative log2 decay and 16-row blocks, a factor 2^(G_r - G_s) between
+// blocks J < I splits at a row between them into two factors no larger than 1:
+//   XA, XP (sum over s in J):  2^(G_r - G_e(J)) * [k_s 2^(G_e(J) - G_s)],   e(J) = last row of J,
+//   Y      (sum over r in I):  [x_r 2^(G_r - G_b(I))] * 2^(G_b(I) - G_s),   b(I) = first row of I,
+// so the inner sums are plain multiply-adds over pre-scaled rows; inside a block the factor is
+// taken directly (one exp2 per term).
 template <int DK>
-__global__ void __launch_bounds__(256, 1) bwd_key_kernel(const KeyIO io) {
-    constexpr int AP = CH + 1;
-    constexpr int R = 256 / DK;  // row phases: thread (i, h) owns rows h, h + R, ...
-    __shared__ uint16_t qs[CH * DK], ks[CH * DK], bs[CH * DK], as[CH * DK];
-    __shared__ float dA[CH * AP], dPs[CH * AP];
-    __shared__ float Gm[CH * DK];  // cumulative log2 decay, then dL/dG
-    __shared__ float red[256];
+__global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
+    constexpr int CW = 32;       // key channels per workgroup
+    constexpr int NG = DK / CW;  // channel groups
+    static_assert(DK % CW == 0, "channel groups");
+    __shared__ float dA[CH * CH], dPs[CH * CH];
+    __shared__ float G2[CH * CW];                   // cumulative log2 decay
+    __shared__ float Kp[CH * CW], Ep[CH * CW], Qp[CH * CW];  // pre-scaled rows (Kp then dL/dG)
+    __shared__ uint16_t qs[CH * CW], ks[CH * CW], bs[CH * CW];
+    __shared__ float red[8 * CW];
 
     const int tid = threadIdx.x;
     const int H = io.H, T = io.T, nch = io.nch;
-    const int bh = blockIdx.x / nch, n = blockIdx.x % nch;
+    const int cg = blockIdx.x % NG, item = blockIdx.x / NG;
+    const int bh = item / nch, n = item % nch;
     const int hh = bh % H, bb = bh / H;
-    const int t0 = n * CH;
+    const int t0 = n * CH, c0 = cg * CW;
     const size_t cbase = (size_t)bh * nch + n;
+    auto f = [](uint16_t x) { return __uint_as_float((uint32_t)x << 16); };
     const uint16_t* q = static_cast<const uint16_t*>(io.q);
     const uint16_t* k = static_cast<const uint16_t*>(io.k);
     const uint16_t* al = static_cast<const uint16_t*>(io.alpha);
     const uint16_t* b = static_cast<const uint16_t*>(io.b);
-    for (int x = tid; x < CH * DK; x += 256) {
-        const int r = x / DK, i = x % DK;
+    for (int x = tid; x < CH * CW; x += 256) {
+        const int r = x / CW, i = x % CW;
         const int t = t0 + r;
         const bool ok = t < T;
-        const size_t e = (((size_t)bb * T + (ok ? t : 0)) * H + hh) * DK + i;
+        const size_t e = (((size_t)bb * T + (ok ? t : 0)) * H + hh) * DK + c0 + i;
         qs[x] = ok ? q[e] : 0;
         ks[x] = ok ? k[e] : 0;
         bs[x] = ok ? b[e] : 0;
-        as[x] = ok ? al[e] : (uint16_t)0x3F80;  // 1.0: rows past the end do not decay
+        G2[x] = ok ? __builtin_amdgcn_logf(f(al[e])) : 0.f;  // rows past the end do not decay
     }
     for (int x = tid; x < CH * CH; x += 256) {
-        const int r = x / CH, c = x % CH;
-        dA[r * AP + c] = io.dAm[cbase * CH * CH + x];
-        dPs[r * AP + c] = io.dPm[cbase * CH * CH + x];
+        dA[x] = io.dAm[cbase * CH * CH + x];
+        dPs[x] = io.dPm[cbase * CH * CH + x];
     }
     __syncthreads();
-    auto f = [](uint16_t x) { return __uint_as_float((uint32_t)x << 16); };
-    if (tid < DK) {
+    if (tid < CW) {
         float acc = 0.f;
         for (int r = 0; r < CH; ++r) {
-            acc += __builtin_amdgcn_logf(f(as[r * DK + tid]));
-            Gm[r * DK + tid] = acc;
+            acc += G2[r * CW + tid];
+            G2[r * CW + tid] = acc;
         }
+    }
+    __syncthreads();
+    for (int x = tid; x < CH * CW; x += 256) {
+        const int r = x / CW, i = x % CW, I = r / 16;
+        const float g = G2[x];
+        const float kv = f(ks[x]);
+        Kp[x] = kv * __builtin_amdgcn_exp2f(G2[(16 * I + 15) * CW + i] - g);
+        const float down = __builtin_amdgcn_exp2f(g - G2[(16 * I) * CW + i]);
+        Ep[x] = f(bs[x]) * kv * down;
+        Qp[x] = f(qs[x]) * down;
     }
     __syncthreads();
 
-    const int i = tid % DK, h = tid / DK;
-    const float G63 = Gm[(CH - 1) * DK + i];
-    constexpr int NR = CH / R;
-    float dG[NR];
+    const int i = tid % CW, p = tid / CW;  // rows p, p + 8, ..., p + 56
+    const float G63 = G2[(CH - 1) * CW + i];
+    float dG[8];
     float kb_sum = 0.f;
-    for (int m = 0; m < NR; ++m) {
-        const int r = h + R * m;
-        const float kr = f(ks[r * DK + i]), qr = f(qs[r * DK + i]), br = f(bs[r * DK + i]);
-        // XA, XP: sums over s <= r, F = prod_{m = s+1..r} alpha_m
-        float F = 1.f, XA = 0.f, XP = dPs[r * AP + r] * kr;
-        for (int s = r - 1; s >= 0; --s) {
-            F *= f(as[(s + 1) * DK + i]);
-            const float kf = f(ks[s * DK + i]) * F;
-            XA = fmaf(dA[r * AP + s], kf, XA);
-            XP = fmaf(dPs[r * AP + s], kf, XP);
+#pragma unroll 1
+    for (int m = 0; m < 8; ++m) {
+        const int r = p + 8 * m, I = r / 16;
+        const float Gr = G2[r * CW + i];
+        const float kr = f(ks[r * CW + i]), qr = f(qs[r * CW + i]), br = f(bs[r * CW + i]);
+        // XA, XP: earlier blocks through the block-end references, then the diagonal block
+        float XA = 0.f, XP = 0.f;
+        for (int J = 0; J < I; ++J) {
+            float sA = 0.f, sP = 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int s = 16 * J + u;
+                const float kp = Kp[s * CW + i];
+                sA = fmaf(dA[r * CH + s], kp, sA);
+                sP = fmaf(dPs[r * CH + s], kp, sP);
+            }
+            const float fJ = __builtin_amdgcn_exp2f(Gr - G2[(16 * J + 15) * CW + i]);
+            XA = fmaf(fJ, sA, XA);
+            XP = fmaf(fJ, sP, XP);
         }
-        // Y: sums over r2 >= r, F = prod_{m = r+1..r2} alpha_m
-        float Y = dPs[r * AP + r] * qr;
-        F = 1.f;
-        for (int r2 = r + 1; r2 < CH; ++r2) {
-            F *= f(as[r2 * DK + i]);
-            const float k2 = f(ks[r2 * DK + i]);
-            Y = fmaf(fmaf(dA[r2 * AP + r], f(bs[r2 * DK + i]) * k2, dPs[r2 * AP + r] * f(qs[r2 * DK + i])), F, Y);
+        for (int s = 16 * I; s <= r; ++s) {
+            const float w = f(ks[s * CW + i]) * __builtin_amdgcn_exp2f(Gr - G2[s * CW + i]);
+            if (s < r) XA = fmaf(dA[r * CH + s], w, XA);
+            XP = fmaf(dPs[r * CH + s], w, XP);
         }
-        const float G2 = Gm[r * DK + i];
-        const float eG = __builtin_amdgcn_exp2f(G2), eK = __builtin_amdgcn_exp2f(G63 - G2);
-        const size_t ce = (cbase * CH + r) * DK + i;
+        // Y: later blocks through the block-start references, then the diagonal block
+        float Y = 0.f;
+        for (int I2 = I + 1; I2 < 4; ++I2) {
+            float sY = 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r2 = 16 * I2 + u;
+                sY = fmaf(dA[r2 * CH + r], Ep[r2 * CW + i], fmaf(dPs[r2 * CH + r], Qp[r2 * CW + i], sY));
+            }
+            Y = fmaf(__builtin_amdgcn_exp2f(G2[(16 * I2) * CW + i] - Gr), sY, Y);
+        }
+        for (int r2 = r; r2 < 16 * I + 16; ++r2) {
+            const float w = __builtin_amdgcn_exp2f(G2[r2 * CW + i] - Gr);
+            const float e2 = f(bs[r2 * CW + i]) * f(ks[r2 * CW + i]);
+            float term = dPs[r2 * CH + r] * f(qs[r2 * CW + i]);
+            if (r2 > r) term = fmaf(dA[r2 * CH + r], e2, term);
+            Y = fmaf(term, w, Y);
+        }
+        const float eG = __builtin_amdgcn_exp2f(Gr), eK = __builtin_amdgcn_exp2f(G63 - Gr);
+        const size_t ce = (cbase * CH + r) * DK + c0 + i;
         const float gQ = io.dQh[ce], gE = io.dEh[ce], gK = io.dKb[ce];
         const float Et = br * kr;
         const float dEt = fmaf(gE, eG, XA);
@@ -508,28 +559,29 @@ __global__ void __launch_bounds__(256, 1) bwd_key_kernel(const KeyIO io) {
         kb_sum = fmaf(gK, kr * eK, kb_sum);
         const int t = t0 + r;
         if (t < T) {
-            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + i;
+            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + c0 + i;
             io.dq[e] = dqv;
             io.dk[e] = dkv;
             io.db[e] = dbv;
         }
     }
     red[tid] = kb_sum;
-    __syncthreads();  // every read of Gm is done
+    __syncthreads();  // every read of Kp is done
 #pragma unroll
-    for (int m = 0; m < NR; ++m) Gm[(h + R * m) * DK + i] = dG[m];
+    for (int m = 0; m < 8; ++m) Kp[(p + 8 * m) * CW + i] = dG[m];
     __syncthreads();
-    if (tid < DK) {
-        float extra = io.dgam[cbase * DK + i] * __builtin_amdgcn_exp2f(G63);
-        for (int p = 0; p < R; ++p) extra += red[p * DK + i];
-        // dlog(alpha)_s = sum_{r >= s} dG_r (the last row also carries the gamma and K_bar terms)
+    if (tid < CW) {
+        float extra = io.dgam[cbase * DK + c0 + tid] * __builtin_amdgcn_exp2f(G63);
+        for (int pp = 0; pp < 8; ++pp) extra += red[pp * CW + tid];
+        // dlog(alpha)_r = sum_{r2 >= r} dG_r2 (the last row also carries the gamma and K_bar terms);
+        // alpha_r = 2^(G_r - G_{r-1})
         float acc = extra;
         for (int r = CH - 1; r >= 0; --r) {
-            acc += Gm[r * DK + i];
+            acc += Kp[r * CW + tid];
             const int t = t0 + r;
             if (t < T) {
-                const size_t e = (((size_t)bb * T + t) * H + hh) * DK + i;
-                io.dalpha[e] = acc / f(as[r * DK + i]);
+                const float a = __builtin_amdgcn_exp2f(G2[r * CW + tid] - (r ? G2[(r - 1) * CW + tid] : 0.f));
+                io.dalpha[(((size_t)bb * T + t) * H + hh) * DK + c0 + tid] = acc / a;
             }
         }
     }
@@ -616,7 +668,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_contract_kernel<DK>), dim3(BH * nch), dim3(256), 0, st, xio);
     const KeyIO kio{a.q, a.k, a.alpha, a.b, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
                     a.B, a.T, a.H, nch};
-    hipLaunchKernelGGL((bwd_key_kernel<DK>), dim3(BH * nch), dim3(256), 0, st, kio);
+    hipLaunchKernelGGL((bwd_key_kernel<DK>), dim3(BH * nch * (DK / 32)), dim3(256), 0, st, kio);
     return hipGetLastError();
 }
 

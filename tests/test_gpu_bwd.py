@@ -118,3 +118,27 @@ def test_bwd_no_tokens_copies_final_cotangent():
     out = g.chunk_bwd(e, e, e, e, e, e, None, dO, dS)
     torch.cuda.synchronize()
     assert torch.equal(out["dS0"], dS)
+
+
+def test_bwd_full_size_sampled_heads():
+    """At the benchmark shape (B8 H16 T4096 d128, the launch the bench times), two sampled
+    (b, h) sequences against the oracle's backward of those sequences alone."""
+    banner("bwd full size B8 H16 T4096, heads (0, 0) and (7, 13)")
+    from gated_delta_rule_25_amd.inputs import make_inputs_torch
+    wl = WORKLOADS["prefill_1p3b"]
+    ins = make_inputs_torch(wl, device="cuda")
+    cot = make_cotangents(wl, device="cuda")
+    g = _g()
+    got = g.chunk_bwd(*[ins[n] for n in ("q", "k", "v", "alpha", "b", "w", "S0")], cot["dO"], cot["dS_T"])
+    torch.cuda.synchronize()
+    for bb, hh in ((0, 0), (7, 13)):
+        sl = lambda x: x[bb:bb + 1, :, hh:hh + 1].cpu()
+        ref = oracle.backward(*[sl(ins[n]) for n in ("q", "k", "v", "alpha", "b", "w")],
+                              ins["S0"][bb:bb + 1, hh:hh + 1].cpu(), sl(cot["dO"]),
+                              cot["dS_T"][bb:bb + 1, hh:hh + 1].cpu())
+        errs = {}
+        for n in NAMES:
+            x = got[n][bb:bb + 1, hh:hh + 1] if n == "dS0" else got[n][bb:bb + 1, :, hh:hh + 1]
+            errs[n] = normwise_err(x, ref[n])
+        print(f"  head ({bb}, {hh}): " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+        assert all(e <= TOLB for e in errs.values()), errs
