@@ -466,19 +466,38 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     const uint16_t* k = static_cast<const uint16_t*>(io.k);
     const uint16_t* al = static_cast<const uint16_t*>(io.alpha);
     const uint16_t* b = static_cast<const uint16_t*>(io.b);
-    for (int x = tid; x < CH * CW; x += 256) {
-        const int r = x / CW, i = x % CW;
+    // every global load is issued before the first LDS write, so their latencies overlap
+    constexpr int NX = CH * CW / 256, NA = CH * CH / 256;
+    uint16_t lq[NX], lk[NX], lb[NX], la[NX];
+    float lA[NA], lP[NA];
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+        const int x = tid + 256 * u, r = x / CW, i = x % CW;
         const int t = t0 + r;
-        const bool ok = t < T;
-        const size_t e = (((size_t)bb * T + (ok ? t : 0)) * H + hh) * DK + c0 + i;
-        qs[x] = ok ? q[e] : 0;
-        ks[x] = ok ? k[e] : 0;
-        bs[x] = ok ? b[e] : 0;
-        G2[x] = ok ? __builtin_amdgcn_logf(f(al[e])) : 0.f;  // rows past the end do not decay
+        const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DK + c0 + i;
+        lq[u] = q[e];
+        lk[u] = k[e];
+        lb[u] = b[e];
+        la[u] = al[e];
     }
-    for (int x = tid; x < CH * CH; x += 256) {
-        dA[x] = io.dAm[cbase * CH * CH + x];
-        dPs[x] = io.dPm[cbase * CH * CH + x];
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+        lA[u] = io.dAm[cbase * CH * CH + tid + 256 * u];
+        lP[u] = io.dPm[cbase * CH * CH + tid + 256 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+        const int x = tid + 256 * u, r = x / CW;
+        const bool ok = t0 + r < T;
+        qs[x] = ok ? lq[u] : 0;
+        ks[x] = ok ? lk[u] : 0;
+        bs[x] = ok ? lb[u] : 0;
+        G2[x] = ok ? __builtin_amdgcn_logf(f(la[u])) : 0.f;  // rows past the end do not decay
+    }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+        dA[tid + 256 * u] = lA[u];
+        dPs[tid + 256 * u] = lP[u];
     }
     __syncthreads();
     if (tid < CW) {
@@ -570,19 +589,28 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) Kp[(p + 8 * m) * CW + i] = dG[m];
     __syncthreads();
-    if (tid < CW) {
-        float extra = io.dgam[cbase * DK + c0 + tid] * __builtin_amdgcn_exp2f(G63);
-        for (int pp = 0; pp < 8; ++pp) extra += red[pp * CW + tid];
-        // dlog(alpha)_r = sum_{r2 >= r} dG_r2 (the last row also carries the gamma and K_bar terms);
-        // alpha_r = 2^(G_r - G_{r-1})
-        float acc = extra;
-        for (int r = CH - 1; r >= 0; --r) {
-            acc += Kp[r * CW + tid];
-            const int t = t0 + r;
-            if (t < T) {
-                const float a = __builtin_amdgcn_exp2f(G2[r * CW + tid] - (r ? G2[(r - 1) * CW + tid] : 0.f));
-                io.dalpha[(((size_t)bb * T + t) * H + hh) * DK + c0 + tid] = acc / a;
-            }
+    // dlog(alpha)_r = sum_{r2 >= r} dG_r2, the last row also carrying the gamma and K_bar terms;
+    // thread (i, p) sums rows 8 p .. 8 p + 7, then adds the sums of the segments below it.
+    // alpha_r = 2^(G_r - G_{r-1}).
+    float seg = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) seg += Kp[(8 * p + u) * CW + i];
+    float extra = io.dgam[cbase * DK + c0 + i] * __builtin_amdgcn_exp2f(G63);
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) extra += red[pp * CW + i];
+    __syncthreads();  // every read of red is done
+    red[p * CW + i] = seg;
+    __syncthreads();
+    float acc = extra;
+    for (int pp = 7; pp > p; --pp) acc += red[pp * CW + i];
+#pragma unroll
+    for (int u = 7; u >= 0; --u) {
+        const int r = 8 * p + u;
+        acc += Kp[r * CW + i];
+        const int t = t0 + r;
+        if (t < T) {
+            const float a = __builtin_amdgcn_exp2f(G2[r * CW + i] - (r ? G2[(r - 1) * CW + i] : 0.f));
+            io.dalpha[(((size_t)bb * T + t) * H + hh) * DK + c0 + i] = acc / a;
         }
     }
 }
