@@ -551,7 +551,9 @@ struct ChainIO {
 // below DV / DVT run it from a zero state with the true U (their final state is the segment's
 // inhomogeneous part Psi); tiles above run it with U = 0 from the identity on their columns (the
 // transition Phi). No o, and only the block prefix the recurrence reads is copied.
-template <int DK, int DVT, bool BF16, bool BS, bool STATE>
+// SAVE (state-only pass, for the backward): also write the start state of every chunk and the
+// rows of D' and Delta (ChainIO's save fields).
+template <int DK, int DVT, bool BF16, bool BS, bool STATE, bool SAVE = false>
 __global__ void __launch_bounds__(kChainThreads, 1)
 chain_kernel(const ChainIO io) {
     constexpr bool F16 = BF16;
@@ -574,7 +576,8 @@ chain_kernel(const ChainIO io) {
     const int T = io.T, H = io.H, DV = io.DV;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int vt = DV / DVT;                  // value tiles
-    const int tiles = vt + io.phi_tiles;
+    const int tiles = vt + (STATE ? io.phi_tiles : 0);
+    static_assert(STATE || !SAVE, "saves belong to the state-only pass");
     const int BH = io.B * H, BHp = (BH + 7) / 8 * 8;
     const int seg = blockIdx.x / (BHp * tiles);
     const int x = blockIdx.x % (BHp * tiles);
@@ -709,7 +712,7 @@ chain_kernel(const ChainIO io) {
             } else {
                 wait_vm_but<4 * NT>();
             }
-            if (io.S_save) {
+            if constexpr (SAVE) {
                 // the state at the start of this chunk, for the backward pass
                 float* sv = io.S_save + ((size_t)bh * io.save_nch + n) * DK * DV;
 #pragma unroll
@@ -763,7 +766,7 @@ chain_kernel(const ChainIO io) {
             if constexpr (F16) lookahead_schedule<(STATE ? 4 : 8) * NKS, 6, NT>();
             // the next chunk's v, w into this wave's slot, now that its reads are long done
             if (nc + 1 < n_count && !phi) dma_vw(n + 1);
-            if (io.Dp_save) save_rows(io.Dp_save, D);
+            if constexpr (SAVE) save_rows(io.Dp_save, D);
             // Delta = T D'
             Frag Df[NT][2];
 #pragma unroll
@@ -784,7 +787,7 @@ chain_kernel(const ChainIO io) {
                 }
             }
             if constexpr (F16) lookahead_schedule<6, 4, NT>();
-            if (io.Dl_save) save_rows(io.Dl_save, Dl);
+            if constexpr (SAVE) save_rows(io.Dl_save, Dl);
 #pragma unroll
             for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -1011,8 +1014,8 @@ hipError_t launch_states_t(const ChunkArgs& a, char* blobs, float* S_save, float
     io.save_nch = nch;
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
-    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true>), dim3(BHp * (a.DV / DVT)), dim3(kChainThreads),
-                       0, st, io);
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true>), dim3(BHp * (a.DV / DVT)),
+                       dim3(kChainThreads), 0, st, io);
     return hipGetLastError();
 }
 
