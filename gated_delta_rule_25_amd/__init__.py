@@ -23,14 +23,14 @@ import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to
 
 __all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
            "chunk_bwd_workspace_bytes",
-           "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR"]
+           "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
 _lib = None
 
 BF16, F32 = 0, 1
-ALPHA_SCALAR, BETA_SCALAR = 1, 2
+ALPHA_SCALAR, BETA_SCALAR, QK_L2NORM, GATE_LOGITS = 1, 2, 4, 8
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
            4: "GDN2_ERR_ALIGN", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP", 7: "GDN2_ERR_WORKSPACE"}
 
@@ -86,6 +86,10 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
 
 
+def _prologue_flags(l2norm: bool, gate_logits: bool) -> int:
+    return (QK_L2NORM if l2norm else 0) | (GATE_LOGITS if gate_logits else 0)
+
+
 def _check_inputs(q, k, v, alpha, b, w, ndim_tok: int):
     ins = [x for x in (q, k, v, alpha, b, w) if x is not None]
     dt = q.dtype
@@ -128,14 +132,15 @@ def chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) 
 
 
 def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspace=None,
-              fused=False, stream=None):
+              fused=False, l2norm=False, gate_logits=False, stream=None):
     """Chunkwise prefill (C = 64). Returns (o [B, T, H, d_v] fp32, S_T [B, H, d_k, d_v]).
 
     With a workspace (allocated here unless given) the library runs its two-kernel path;
-    fused=True passes none and runs the single-kernel path.
+    fused=True passes none and runs the single-kernel path. l2norm / gate_logits: the kernels
+    normalise q, k and take the gates through the sigmoid themselves (two-kernel path only).
     """
     lib = load()
-    flags = _check_inputs(q, k, v, alpha, b, w, 4)
+    flags = _check_inputs(q, k, v, alpha, b, w, 4) | _prologue_flags(l2norm, gate_logits)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if o is None:
@@ -193,10 +198,11 @@ def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=No
     return out
 
 
-def recurrent_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, stream=None):
+def recurrent_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, l2norm=False,
+                  gate_logits=False, stream=None):
     """Token-by-token fp32 prefill. Returns (o, S_T) like chunk_fwd."""
     lib = load()
-    flags = _check_inputs(q, k, v, alpha, b, w, 4)
+    flags = _check_inputs(q, k, v, alpha, b, w, 4) | _prologue_flags(l2norm, gate_logits)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if o is None:
@@ -210,10 +216,10 @@ def recurrent_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, str
     return o, S_out
 
 
-def decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
+def decode_step(q, k, v, alpha, b, w, S, *, o=None, l2norm=False, gate_logits=False, stream=None):
     """One decode step on [B, H, d] inputs; updates S [B, H, d_k, d_v] in place, returns o."""
     lib = load()
-    flags = _check_inputs(q, k, v, alpha, b, w, 3)
+    flags = _check_inputs(q, k, v, alpha, b, w, 3) | _prologue_flags(l2norm, gate_logits)
     B, H, dk = q.shape
     dv = v.shape[-1]
     if S.dtype != torch.float32 or not S.is_contiguous():

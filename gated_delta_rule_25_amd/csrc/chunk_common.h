@@ -27,6 +27,12 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+// Logistic sigmoid, and log2 of it in a form that neither overflows nor cancels:
+// log2 sigma(x) = min(x, 0) log2(e) - log2(1 + 2^(-|x| log2(e))). sigma(-inf) = 0, sigma(+inf) = 1.
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + ex2(-1.4426950408889634f * x)); }
+__device__ __forceinline__ float lg2_sigmoid(float x) {
+    return fminf(x, 0.f) * 1.4426950408889634f - lg2(1.f + ex2(-1.4426950408889634f * fabsf(x)));
+}
 
 // Raw buffer over [base, base + bytes): loads at byte offsets past the end return zero and
 // stores there are dropped, so a ragged last chunk needs no branch (and the compiler can count
@@ -148,7 +154,7 @@ template <bool BF16>
 __device__ __forceinline__ Raw8<BF16> fill8(float x) {
     Raw8<BF16> r;
     if constexpr (BF16) {
-        const uint32_t h = __float_as_uint(x) >> 16;  // exact for 0 and 1
+        const uint32_t h = __float_as_uint(x) >> 16;  // exact for 0, 1 and +-inf
         const uint32_t p = h | (h << 16);
         r.u[0] = make_uint4(p, p, p, p);
     } else {

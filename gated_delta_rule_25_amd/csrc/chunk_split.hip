@@ -95,7 +95,9 @@ struct PrepSmem {
     static_assert(bytes <= 80 * 1024, "prep LDS must allow two workgroups per CU");
 };
 
-template <int DK, bool BF16, bool AS, bool BS>
+// PRO (prologue): bit 0, q and k are L2-normalised over d_k per token here; bit 1, alpha and b
+// (or beta) arrive as pre-activations: log2 alpha = log2 sigma(x), b = sigma(x).
+template <int DK, bool BF16, bool AS, bool BS, int PRO = 0>
 __global__ void __launch_bounds__(256, 2)
 prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int B, int T, int H,
             int n_first, int n_count, char* ws) {
@@ -118,6 +120,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     E* A16 = reinterpret_cast<E*>(smem + SM::oA);
     float* AdT = reinterpret_cast<float*>(smem + SM::oAd);
 
+    constexpr bool L2N = (PRO & 1) != 0, GL = (PRO & 2) != 0;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int BH = B * H;
     const int bh = blockIdx.x % BH, nc = blockIdx.x / BH;
@@ -163,10 +166,10 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     asm volatile("" ::: "memory");
     if constexpr (!AS) {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) unpack8<BF16>(keep_or<BF16>(ra[s], valid, 1.f), &lg[8 * s]);
+        for (int s = 0; s < NKS; ++s) unpack8<BF16>(keep_or<BF16>(ra[s], valid, GL ? INFINITY : 1.f), &lg[8 * s]);
     }
     if constexpr (AS) {
-        float x1 = lg2(valid ? ras_raw : 1.f);
+        float x1 = GL ? (valid ? lg2_sigmoid(ras_raw) : 0.f) : lg2(valid ? ras_raw : 1.f);
         x1 += row_shr<1>(x1);
         x1 += row_shr<2>(x1);
         x1 += row_shr<4>(x1);
@@ -175,7 +178,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
         for (int e = 0; e < CPL; ++e) lg[e] = x1;
     } else {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) lg[e] = lg2(lg[e]);
+        for (int e = 0; e < CPL; ++e) lg[e] = GL ? lg2_sigmoid(lg[e]) : lg2(lg[e]);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) lg[e] += row_shr<1>(lg[e]);
 #pragma unroll
@@ -227,6 +230,50 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     lds_barrier();
 
     // ---- B: factors; Q_hat and -E_hat straight to the blob; diagonal Gram blocks ----
+    // Prologue: 1 / |q| and 1 / |k| of this lane's row (the row's channels are spread over the
+    // four lane groups: lanes l16, l16 + 16, l16 + 32, l16 + 48).
+    float nq = 1.f, nk = 1.f;
+    if constexpr (L2N) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            float qx[8], kx[8];
+            unpack8<BF16>(keep_or<BF16>(rq[s], valid, 0.f), qx);
+            unpack8<BF16>(keep_or<BF16>(rk[s], valid, 0.f), kx);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sq = fmaf(qx[i], qx[i], sq);
+                sk = fmaf(kx[i], kx[i], sk);
+            }
+        }
+        sq += __shfl_xor(sq, 16);
+        sk += __shfl_xor(sk, 16);
+        sq += __shfl_xor(sq, 32);
+        sk += __shfl_xor(sk, 32);
+        nq = 1.f / fmaxf(sqrtf(sq), 1e-12f);
+        nk = 1.f / fmaxf(sqrtf(sk), 1e-12f);
+    }
+    // q, k (normalised) and b of 8 channels of this lane's row, for 32-channel step s
+    auto row_gates = [&](int s, float* qx, float* kx, float* bx) {
+        if constexpr (L2N) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qx[i] *= nq;
+                kx[i] *= nk;
+            }
+        }
+        if constexpr (BS) {
+            const float be = GL ? sigmoidf_(rbs_raw) : rbs_raw;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bx[i] = valid ? be : 0.f;
+        } else {
+            unpack8<BF16>(keep_or<BF16>(rb[s], valid, GL ? -INFINITY : 0.f), bx);
+            if constexpr (GL) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bx[i] = sigmoidf_(bx[i]);
+            }
+        }
+    };
     float er[CPL], qr[CPL];
     {
         f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
@@ -238,12 +285,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
             float qx[8], kx[8], bx[8], X8[8], fX[8], fG[8], fTX[8], fCG[8];
             unpack8<BF16>(keep_or<BF16>(rq[s], valid, 0.f), qx);
             unpack8<BF16>(keep_or<BF16>(rk[s], valid, 0.f), kx);
-            if constexpr (BS) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) bx[i] = valid ? rbs_raw : 0.f;
-            } else {
-                unpack8<BF16>(keep_or<BF16>(rb[s], valid, 0.f), bx);
-            }
+            row_gates(s, qx, kx, bx);
             lds_read8f(ldsX + I * DK + c0, X8);
             lds_read8f(tab + (0 + I) * DK + c0, fX);
             lds_read8f(tab + (4 + I) * DK + c0, fG);
@@ -289,12 +331,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
                 float qx[8], kx[8], bx[8], X8[8], em[8], qm[8], km[8];
                 unpack8<BF16>(keep_or<BF16>(rq[s], valid, 0.f), qx);
                 unpack8<BF16>(keep_or<BF16>(rk[s], valid, 0.f), kx);
-                if constexpr (BS) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) bx[i] = valid ? rbs_raw : 0.f;
-                } else {
-                    unpack8<BF16>(keep_or<BF16>(rb[s], valid, 0.f), bx);
-                }
+                row_gates(s, qx, kx, bx);
                 lds_read8f(ldsX + I * DK + c0, X8);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -489,7 +526,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
         static_assert(DK <= 256, "one gamma_last element per thread");
         if (tid < DK) gc[tid] = tab[16 * DK + tid];
         if constexpr (BS) {
-            if (g == 0) reinterpret_cast<float*>(blob + BL::oBeta)[r] = valid ? rbs_raw : 0.f;
+            if (g == 0) reinterpret_cast<float*>(blob + BL::oBeta)[r] = valid ? (GL ? sigmoidf_(rbs_raw) : rbs_raw) : 0.f;
         }
     }
 }
@@ -553,7 +590,8 @@ struct ChainIO {
 // transition Phi). No o, and only the block prefix the recurrence reads is copied.
 // SAVE (state-only pass, for the backward): also write the start state of every chunk and the
 // rows of D' and Delta (ChainIO's save fields).
-template <int DK, int DVT, bool BF16, bool BS, bool STATE, bool SAVE = false>
+// WSIG: w arrives as pre-activations (the prologue's gate logits); U = sigma(w) v.
+template <int DK, int DVT, bool BF16, bool BS, bool STATE, bool SAVE = false, bool WSIG = false>
 __global__ void __launch_bounds__(kChainThreads, 1)
 chain_kernel(const ChainIO io) {
     constexpr bool F16 = BF16;
@@ -731,7 +769,8 @@ chain_kernel(const ChainIO io) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * mt + 4 * g + j, slot = 16 * mt + 4 * j + g, cl = 16 * c + l16;
-                        const float ww = BS ? betaL[row] : raw_f(w_l[slot * ROW + cl]);
+                        float ww = BS ? betaL[row] : raw_f(w_l[slot * ROW + cl]);
+                        if constexpr (WSIG && !BS) ww = sigmoidf_(ww);
                         D[c][mt][j] = phi ? 0.f : ww * raw_f(v_l[slot * ROW + cl]);
                     }
             float4 gcv[NMK];  // gamma_last of this lane's state rows
@@ -931,8 +970,9 @@ SplitPlan split_plan(int B, int T, int H, int DK, int DV) {
     return p;
 }
 
-template <int DK, bool BF16, bool AS, bool BS>
+template <int DK, bool BF16, bool AS, bool BS, int PRO>
 hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
+    constexpr bool WS = (PRO & 2) != 0 && !BS;  // w through the sigmoid in the chain
     constexpr int DVT = DK < 64 ? DK : 64;
     using BL = Blob<DK, BF16>;
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
@@ -955,20 +995,20 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         const int G = plan.nseg;
         float* psiphi = reinterpret_cast<float*>(ws + (size_t)nch * per_chunk);
         float* sseg = psiphi + (size_t)BH * (G - 1) * DK * (a.DV + DK);
-        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k, a.alpha,
+        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS, PRO>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k, a.alpha,
                            a.b, a.B, a.T, a.H, 0, nch, ws);
         const ChainIO tr{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G - 1, a.B, a.T, a.H, a.DV,
                          nullptr, 0, 0, a.DV,
                          psiphi, (long)(G - 1) * DK * (a.DV + DK), ld * (a.DV + DK), a.DV + DK, 0};
         ChainIO trp = tr;
         trp.phi_tiles = DK / DVT;
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true, false, WS>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
                            dim3(kChainThreads), 0, st, trp);
         hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 8)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
         const ChainIO fu{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G, a.B, a.T, a.H, a.DV,
                          sseg, (long)G * DK * a.DV, ld * a.DV, a.DV,
                          Sbuf, ld * a.DV, 0, a.DV, 1};
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false>), dim3(G * BHp * tiles), dim3(kChainThreads), 0,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS>), dim3(G * BHp * tiles), dim3(kChainThreads), 0,
                            st, fu);
         return hipGetLastError();
     }
@@ -977,12 +1017,12 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     if (R > nch) R = nch;
     for (int n0 = 0; n0 < nch; n0 += R) {
         const int cnt = nch - n0 < R ? nch - n0 : R;
-        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
+        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS, PRO>), dim3(BH * cnt), dim3(256), 0, st, a.q, a.k,
                            a.alpha, a.b, a.B, a.T, a.H, n0, cnt, ws);
         const ChainIO io{a.v, a.w, a.o, ws, cnt, n0, n0 + cnt, cnt, 1, a.B, a.T, a.H, a.DV,
                          n0 == 0 ? a.S0 : Sbuf, ld * a.DV, 0, a.DV,
                          Sbuf, ld * a.DV, 0, a.DV, 0};
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false>), dim3(BHp * tiles), dim3(kChainThreads), 0, st,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS>), dim3(BHp * tiles), dim3(kChainThreads), 0, st,
                            io);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -990,13 +1030,23 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     return hipSuccess;
 }
 
+template <int DK, bool BF16, int PRO>
+hipError_t launch_split_gates(const ChunkArgs& a, hipStream_t s) {
+    switch (a.flags & 3u) {
+        case 0: return launch_split_t<DK, BF16, false, false, PRO>(a, s);
+        case 1: return launch_split_t<DK, BF16, true, false, PRO>(a, s);
+        case 2: return launch_split_t<DK, BF16, false, true, PRO>(a, s);
+        default: return launch_split_t<DK, BF16, true, true, PRO>(a, s);
+    }
+}
+
 template <int DK, bool BF16>
 hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
-    switch (a.flags & 3u) {
-        case 0: return launch_split_t<DK, BF16, false, false>(a, s);
-        case 1: return launch_split_t<DK, BF16, true, false>(a, s);
-        case 2: return launch_split_t<DK, BF16, false, true>(a, s);
-        default: return launch_split_t<DK, BF16, true, true>(a, s);
+    switch ((a.flags >> 2) & 3u) {  // prologue: L2 norm of q, k (1), gate pre-activations (2)
+        case 0: return launch_split_gates<DK, BF16, 0>(a, s);
+        case 1: return launch_split_gates<DK, BF16, 1>(a, s);
+        case 2: return launch_split_gates<DK, BF16, 2>(a, s);
+        default: return launch_split_gates<DK, BF16, 3>(a, s);
     }
 }
 

@@ -68,7 +68,8 @@ gdn2_status validate(const void* q, const void* k, const void* v, const void* al
                      const float* S_out, int32_t B, int32_t T, int32_t H, int32_t dk,
                      int32_t dv, gdn2_dtype dt, uint32_t flags, bool decode) {
     if (dt != GDN2_BF16 && dt != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
-    if (flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR)) return GDN2_ERR_UNSUPPORTED;
+    if (flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR | GDN2_QK_L2NORM | GDN2_GATE_LOGITS))
+        return GDN2_ERR_UNSUPPORTED;
     if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
     if (!dim_ok(dk) || !dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
     Sizes sz;
@@ -161,7 +162,8 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                                 range_of(S0, sz.state * 4), range_of(o, sz.vw * 4), range_of(S_out, sz.state * 4)};
         for (const Range& r : others)
             if (overlap(rws, r)) return GDN2_ERR_ALIAS;
-    } else if (!gdn2::chunk_supported(T, H, d_k, d_v, bf16)) {
+    } else if (!gdn2::chunk_supported(T, H, d_k, d_v, bf16) ||
+               (gate_flags & (GDN2_QK_L2NORM | GDN2_GATE_LOGITS))) {  // no prologue on this path
         return GDN2_ERR_UNSUPPORTED;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);

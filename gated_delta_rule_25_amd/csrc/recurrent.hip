@@ -15,6 +15,12 @@
 // and columns 4*cq .. 4*cq+3 of the slice. The two column reductions over d_k are butterflies
 // across the 8 row groups (lane xor 8, 16, 32), so a token needs no LDS and no barrier.
 // The decode step is this kernel with T = 1 and S0 == S_out == S.
+//
+// Prologue (PRO): bit 0, q and k are L2-normalised over d_k per token (their sums of squares
+// ride in the same butterflies, and the reductions are scaled afterwards: r by 1/|k|, the readout
+// by 1/|q|, q.k by both); bit 1, alpha, b and w arrive as pre-activations and go through the
+// logistic sigmoid when loaded [same page, paragraph "Архитектурно": L2-normalised q/k,
+// sigmoid gates].
 #include "common.h"
 #include "kernels.h"
 
@@ -22,7 +28,11 @@ namespace gdn2 {
 
 namespace {
 
-template <int DK, bool BF16, bool ASCALAR, bool BSCALAR>
+__device__ __forceinline__ float sigmoid(float x) {
+    return 1.f / (1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+template <int DK, bool BF16, bool ASCALAR, bool BSCALAR, int PRO>
 __global__ void __launch_bounds__(256)
 recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const void* __restrict__ alpha,
@@ -81,18 +91,31 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
             load_vec<R, BF16>(b, tok * DK + row0, bx);
             load_vec<4, BF16>(w, tok * DV + col0, wx);
         }
+        if constexpr ((PRO & 2) != 0) {
+#pragma unroll
+            for (int m = 0; m < R; ++m) {
+                ax[m] = sigmoid(ax[m]);
+                bx[m] = sigmoid(bx[m]);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) wx[c] = sigmoid(wx[c]);
+        }
     };
 
     if (T > 0) fetch(0, qa, ka, aa, ba, va, wa);
     for (int t = 0; t < T; ++t) {
         if (t + 1 < T) fetch(t + 1, qn, kn, an, bn, vn, wn);
 
-        float r[4] = {0.f, 0.f, 0.f, 0.f}, po[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+        float r[4] = {0.f, 0.f, 0.f, 0.f}, po[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f, sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int m = 0; m < R; ++m) {
             const float e = aa[m] * ba[m] * ka[m];
             const float aq = aa[m] * qa[m];
             qk = fmaf(qa[m], ka[m], qk);
+            if constexpr ((PRO & 1) != 0) {
+                sq = fmaf(qa[m], qa[m], sq);
+                sk = fmaf(ka[m], ka[m], sk);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 r[c] = fmaf(e, S[m][c], r[c]);
@@ -108,6 +131,21 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                 po[c] += __shfl_xor(po[c], sh);
             }
             qk += __shfl_xor(qk, sh);
+            if constexpr ((PRO & 1) != 0) {
+                sq += __shfl_xor(sq, sh);
+                sk += __shfl_xor(sk, sh);
+            }
+        }
+        float nk = 1.f;
+        if constexpr ((PRO & 1) != 0) {
+            nk = 1.f / fmaxf(sqrtf(sk), 1e-12f);
+            const float nq = 1.f / fmaxf(sqrtf(sq), 1e-12f);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                r[c] *= nk;
+                po[c] *= nq;
+            }
+            qk *= nq * nk;
         }
         float delta[4], oc[4];
 #pragma unroll
@@ -118,7 +156,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
         for (int m = 0; m < R; ++m) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) S[m][c] = fmaf(aa[m], S[m][c], ka[m] * delta[c]);
+            for (int c = 0; c < 4; ++c) S[m][c] = fmaf(aa[m], S[m][c], (ka[m] * nk) * delta[c]);
         }
         if (rg == 0) {
             const long tok = ((long)bb * T + t) * H + hh;
@@ -143,24 +181,34 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
 }
 
-template <int DK, bool BF16, bool AS, bool BS>
+template <int DK, bool BF16, bool AS, bool BS, int PRO>
 hipError_t launch_t(const RecurrentArgs& a, hipStream_t s) {
     const int items = a.B * a.H * (a.DV / 32);
     const int waves_per_block = 4;
     const int blocks = (items + waves_per_block - 1) / waves_per_block;
-    hipLaunchKernelGGL((recurrent_kernel<DK, BF16, AS, BS>), dim3(blocks), dim3(64 * waves_per_block),
+    hipLaunchKernelGGL((recurrent_kernel<DK, BF16, AS, BS, PRO>), dim3(blocks), dim3(64 * waves_per_block),
                        0, s, a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, a.o, a.S_out, a.B, a.T, a.H,
                        a.DV);
     return hipGetLastError();
 }
 
+template <int DK, bool BF16, int PRO>
+hipError_t launch_gates(const RecurrentArgs& a, hipStream_t s) {
+    switch (a.flags & 3u) {
+        case 0: return launch_t<DK, BF16, false, false, PRO>(a, s);
+        case 1: return launch_t<DK, BF16, true, false, PRO>(a, s);
+        case 2: return launch_t<DK, BF16, false, true, PRO>(a, s);
+        default: return launch_t<DK, BF16, true, true, PRO>(a, s);
+    }
+}
+
 template <int DK, bool BF16>
 hipError_t launch_flags(const RecurrentArgs& a, hipStream_t s) {
-    switch (a.flags & 3u) {
-        case 0: return launch_t<DK, BF16, false, false>(a, s);
-        case 1: return launch_t<DK, BF16, true, false>(a, s);
-        case 2: return launch_t<DK, BF16, false, true>(a, s);
-        default: return launch_t<DK, BF16, true, true>(a, s);
+    switch ((a.flags >> 2) & 3u) {  // prologue: L2 norm of q, k (1), gate pre-activations (2)
+        case 0: return launch_gates<DK, BF16, 0>(a, s);
+        case 1: return launch_gates<DK, BF16, 1>(a, s);
+        case 2: return launch_gates<DK, BF16, 2>(a, s);
+        default: return launch_gates<DK, BF16, 3>(a, s);
     }
 }
 

@@ -112,6 +112,36 @@ def make_inputs(wl: Workload, *, device: str = "cpu") -> dict:
                 alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)
 
 
+def make_prologue_inputs(wl: Workload, *, device: str = "cpu") -> dict:
+    """Raw inputs for the fused prologue (in-kernel L2 norm and gate logits): q, k standard normal
+    times a per-token scale drawn uniformly from [0.5, 4] (so the norm matters), v standard
+    normal, and the gates as pre-activations: alpha ~ N(alpha_mu, 1), b, w ~ N(0, 1) (scalar
+    forms as in make_inputs). Same dict layout as make_inputs; drawn from seed + 104729."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 104729))
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.d_k, wl.d_v
+    f32 = np.float32
+    q = rng.standard_normal((B, T, H, dk), dtype=f32) * rng.uniform(0.5, 4.0, (B, T, H, 1)).astype(f32)
+    k = rng.standard_normal((B, T, H, dk), dtype=f32) * rng.uniform(0.5, 4.0, (B, T, H, 1)).astype(f32)
+    v = rng.standard_normal((B, T, H, dv), dtype=f32)
+    b = rng.standard_normal((B, T, H, dk), dtype=f32)
+    w = rng.standard_normal((B, T, H, dv), dtype=f32)
+    a_shape = (B, T, H) if wl.gates == "gdn" else (B, T, H, dk)
+    alpha = rng.standard_normal(a_shape, dtype=f32) + f32(wl.alpha_mu)
+    S0 = rng.standard_normal((B, H, dk, dv), dtype=f32) * f32(wl.s0_std) if wl.s0_std > 0 else None
+    beta_scalar = wl.gates in ("gdn", "kda")
+    if beta_scalar:
+        b = rng.standard_normal((B, T, H), dtype=f32)
+        w = None
+    dt = _torch_dtype(wl.dtype)
+
+    def t(x):
+        return None if x is None else torch.from_numpy(x).to(dt).to(device)
+
+    return dict(q=t(q), k=t(k), v=t(v), alpha=t(alpha), b=t(b), w=t(w),
+                S0=None if S0 is None else torch.from_numpy(S0).to(device),
+                alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)
+
+
 def make_cotangents(wl: Workload, *, device: str = "cpu", final_state: bool = True) -> dict:
     """Seeded cotangents for the backward: dO [B, T, H, d_v] and dS_T [B, H, d_k, d_v] (or None),
     both standard normal in float32, drawn from their own stream (seed + 7919)."""

@@ -72,8 +72,18 @@ typedef enum { GDN2_BF16 = 0, GDN2_F32 = 1 } gdn2_dtype;
 
 enum {
     GDN2_ALPHA_SCALAR = 1u, /* alpha holds one decay per token, broadcast over d_k */
-    GDN2_BETA_SCALAR = 2u   /* b holds one beta per token: b = beta*1_{d_k}, w = beta*1_{d_v};
+    GDN2_BETA_SCALAR = 2u,  /* b holds one beta per token: b = beta*1_{d_k}, w = beta*1_{d_v};
                                w must be NULL */
+    /* Prologue flags: the steps in front of the recurrence done inside the kernels, in fp32, on
+     * the inputs as given [GDN2-summary, paragraph "Архитектурно": L2-normalised q/k, sigmoid
+     * gates]. Taken by the two-kernel prefill (gdn2_chunk_fwd with a workspace), the token-by-token
+     * prefill and the decode step; the single-kernel prefill and gdn2_chunk_bwd return
+     * GDN2_ERR_UNSUPPORTED for them. */
+    GDN2_QK_L2NORM = 4u,   /* q and k are normalised per token and head over d_k:
+                              x / max(|x|_2, 1e-12) */
+    GDN2_GATE_LOGITS = 8u  /* alpha, b, w (or the scalar forms) hold pre-activations x; the
+                              gates are the logistic sigmoid 1 / (1 + e^-x), and log alpha is
+                              taken directly as log sigma(x) */
 };
 
 /*

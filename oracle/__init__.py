@@ -190,3 +190,22 @@ def backward(q, k, v, alpha, b, w, S0=None, dO=None, dS_T=None, *, threads: int 
     if rc != 0:
         raise RuntimeError(f"gdn2_oracle_backward failed with status {rc}")
     return out
+
+
+def prologue(q, k, alpha, b, w, *, l2norm: bool, gate_logits: bool):
+    """The steps in front of the recurrence, in float64: q and k L2-normalised per token and head
+    over d_k (x / max(||x||, 1e-12)), and the gates taken through the logistic sigmoid from their
+    pre-activations (page "NVIDIA представила Gated DeltaNet-2 с канал-wise гейтами …",
+    paragraph "Архитектурно": L2-normalised q/k and sigmoid gates). w may be None (scalar beta
+    carried in b). Returns (q, k, alpha, b, w) as float64 numpy arrays.
+    """
+    q, k, alpha, b = (_f64(x) for x in (q, k, alpha, b))
+    w = _f64(w)
+    if l2norm:
+        q = q / np.maximum(np.sqrt(np.sum(q * q, axis=-1, keepdims=True)), 1e-12)
+        k = k / np.maximum(np.sqrt(np.sum(k * k, axis=-1, keepdims=True)), 1e-12)
+    if gate_logits:
+        sig = lambda x: 1.0 / (1.0 + np.exp(-x))
+        alpha, b = sig(alpha), sig(b)
+        w = None if w is None else sig(w)
+    return q, k, alpha, b, w
