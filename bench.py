@@ -61,7 +61,7 @@ def decode_bytes_per_head(dk: int, dv: int) -> float:
     return 2 * 4 * dk * dv + 4 * dk * 2 + 2 * dv * 2 + 4 * dv
 
 
-def time_prefill(g, ins, steps, warmup, impl, ring_mb=None):
+def time_prefill(g, ins, steps, warmup, impl, ring_mb=None, **flags):
     import torch
     fn = g.recurrent_fwd if impl == "recurrent" else g.chunk_fwd
     args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")]
@@ -81,6 +81,7 @@ def time_prefill(g, ins, steps, warmup, impl, ring_mb=None):
             kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
     elif impl == "fused":
         kw["fused"] = True
+    kw.update(flags)
     for _ in range(warmup):
         fn(*args, ins["S0"], **kw)
     torch.cuda.synchronize()
@@ -309,6 +310,17 @@ def main(argv=None):
           f"{ms_per_step:.3f} ms/step (wall), {achieved_gbs:.0f} GB/s, {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
+    prologue = None
+    if args.impl == "chunk" and args.workload == "prefill_1p3b":
+        # the same call with the fused prologue (q, k normalised and the gates taken from
+        # pre-activations inside the kernels; the inputs serve as pre-activations)
+        _, pk = time_prefill(g, ins, max(5, args.steps // 2), 1, args.impl, l2norm=True, gate_logits=True)
+        pms = sum(pk) / len(pk)
+        prologue = dict(kernel_ms=round(pms, 4), tokens_per_s=round(B * T / (pms * 1e-3), 1),
+                        overhead_vs_plain=round(pms / kern_avg - 1.0, 4))
+        print(f"[bench] prefill {args.impl} with the fused prologue: {pms:.3f} ms/launch "
+              f"({100 * prologue['overhead_vs_plain']:+.1f}%)", file=sys.stderr, flush=True)
+
     cold_ms = time_prefill_cold(g, ins, 5, args.impl)
     print(f"[bench] prefill {args.impl} cold (512 MiB scrub between calls): {cold_ms:.3f} ms/launch",
           file=sys.stderr, flush=True)
@@ -379,6 +391,7 @@ def main(argv=None):
         "cold_ms": round(cold_ms, 4),
         "other_prefill": others,
         "backward": bwd,
+        "prologue": prologue,
         "decode": dec,
         "cpu_baseline": cpu,
     }
