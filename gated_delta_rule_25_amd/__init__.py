@@ -23,7 +23,8 @@ import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to
 
 __all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
            "chunk_bwd_workspace_bytes",
-           "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS"]
+           "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
+           "decode_step_slots"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
@@ -62,6 +63,8 @@ def load():
     lib.gdn2_chunk_bwd.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
     lib.gdn2_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn2_decode_step_slots.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p]
+    lib.gdn2_decode_step_slots.restype = ctypes.c_int
     lib.gdn2_recurrent_fwd.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p]
     lib.gdn2_recurrent_fwd.restype = ctypes.c_int
     lib.gdn2_decode_step.argtypes = [p] * 8 + [i32] * 4 + [ctypes.c_int, u32, p]
@@ -230,4 +233,27 @@ def decode_step(q, k, v, alpha, b, w, S, *, o=None, l2norm=False, gate_logits=Fa
                               _ptr(o), B, H, dk, dv, _dtype_code(q), flags, _stream(stream))
     if st != 0:
         raise Gdn2Error("gdn2_decode_step", st)
+    return o
+
+
+def decode_step_slots(q, k, v, alpha, b, w, S_pool, slots, *, o=None, l2norm=False, gate_logits=False,
+                      stream=None):
+    """One decode step over a state pool: batch row i updates S_pool[slots[i]] in place
+    (S_pool [n_slots, H, d_k, d_v] float32, slots [B] int32 on the GPU; rows whose slot is outside
+    the pool are skipped). Returns o [B, H, d_v]."""
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 3) | _prologue_flags(l2norm, gate_logits)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if S_pool.dtype != torch.float32 or not S_pool.is_contiguous():
+        raise TypeError("S_pool must be a contiguous float32 tensor")
+    if slots.dtype != torch.int32 or not slots.is_contiguous() or not slots.is_cuda or slots.numel() != B:
+        raise TypeError("slots must be a contiguous int32 GPU tensor of B entries")
+    if o is None:
+        o = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
+    st = lib.gdn2_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S_pool),
+                                    _ptr(slots), _ptr(o), B, H, dk, dv, S_pool.shape[0], _dtype_code(q),
+                                    flags, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_decode_step_slots", st)
     return o

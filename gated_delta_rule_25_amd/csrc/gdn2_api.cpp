@@ -13,6 +13,8 @@
 namespace {
 
 bool dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
+// The token-by-token kernel (decode, recurrent prefill) also takes 256.
+bool dim_ok_tok(int32_t d) { return dim_ok(d) || d == 256; }
 
 // Smallest workspace the two-kernel path accepts: the state buffer and one chunk slot.
 size_t split_min_bytes(int32_t B, int32_t H, int32_t dk, int32_t dv, bool bf16) {
@@ -66,12 +68,12 @@ bool sizes_of(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, Sizes* s)
 gdn2_status validate(const void* q, const void* k, const void* v, const void* alpha,
                      const void* b, const void* w, const float* S0, const float* o,
                      const float* S_out, int32_t B, int32_t T, int32_t H, int32_t dk,
-                     int32_t dv, gdn2_dtype dt, uint32_t flags, bool decode) {
+                     int32_t dv, gdn2_dtype dt, uint32_t flags, bool decode, bool tok = false) {
     if (dt != GDN2_BF16 && dt != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
     if (flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR | GDN2_QK_L2NORM | GDN2_GATE_LOGITS))
         return GDN2_ERR_UNSUPPORTED;
     if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
-    if (!dim_ok(dk) || !dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
+    if (tok ? (!dim_ok_tok(dk) || !dim_ok_tok(dv)) : (!dim_ok(dk) || !dim_ok(dv))) return GDN2_ERR_UNSUPPORTED;
     Sizes sz;
     if (!sizes_of(B, T, H, dk, dv, &sz)) return GDN2_ERR_SHAPE;
     const bool bscalar = (flags & GDN2_BETA_SCALAR) != 0;
@@ -123,7 +125,7 @@ gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v, cons
                                int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                                void* stream) {
     const gdn2_status st = validate(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v,
-                                    in_dtype, gate_flags, false);
+                                    in_dtype, gate_flags, false, true);
     if (st != GDN2_OK) return st;
     return run_recurrent(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
                          gate_flags, static_cast<hipStream_t>(stream));
@@ -184,10 +186,40 @@ gdn2_status gdn2_decode_step(const void* q, const void* k, const void* v, const 
                              uint32_t gate_flags, void* stream) {
     // A [B, H, d] input is a [B, 1, H, d] input: the decode step is one token of prefill.
     const gdn2_status st = validate(q, k, v, alpha, b, w, S, o, S, B, 1, H, d_k, d_v, in_dtype,
-                                    gate_flags, true);
+                                    gate_flags, true, true);
     if (st != GDN2_OK) return st;
     return run_recurrent(q, k, v, alpha, b, w, S, o, S, B, 1, H, d_k, d_v, in_dtype,
                          gate_flags, static_cast<hipStream_t>(stream));
+}
+
+gdn2_status gdn2_decode_step_slots(const void* q, const void* k, const void* v, const void* alpha,
+                                   const void* b, const void* w, float* S_pool, const int32_t* slots,
+                                   float* o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                                   int32_t n_slots, gdn2_dtype in_dtype, uint32_t gate_flags,
+                                   void* stream) {
+    if (n_slots <= 0) return GDN2_ERR_SHAPE;
+    // the inputs and o are [B, H, d] (checked as one token of B sequences); the pool separately
+    gdn2_status st = validate(q, k, v, alpha, b, w, nullptr, o, nullptr, B, 1, H, d_k, d_v, in_dtype,
+                              gate_flags, false, true);
+    if (st != GDN2_OK) return st;
+    if (!slots || !S_pool) return GDN2_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(slots) & 3u) != 0 || !aligned16(S_pool)) return GDN2_ERR_ALIGN;
+    Sizes sz, pool;
+    if (!sizes_of(B, 1, H, d_k, d_v, &sz) || !sizes_of(n_slots, 1, H, d_k, d_v, &pool)) return GDN2_ERR_SHAPE;
+    const uint64_t es = in_dtype == GDN2_BF16 ? 2 : 4;
+    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
+    const Range rp = range_of(S_pool, pool.state * 4), ro = range_of(o, sz.vw * 4);
+    const Range ins[] = {range_of(q, sz.qk * es), range_of(k, sz.qk * es), range_of(v, sz.vw * es),
+                         range_of(alpha, (as ? sz.scalar : sz.qk) * es), range_of(b, (bs ? sz.scalar : sz.qk) * es),
+                         range_of(w, sz.vw * es), range_of(slots, (uint64_t)B * 4)};
+    for (const Range& r : ins)
+        if (overlap(rp, r) || overlap(ro, r)) return GDN2_ERR_ALIAS;
+    if (overlap(rp, ro)) return GDN2_ERR_ALIAS;
+    gdn2::RecurrentArgs a{q, k, v, alpha, b, w, S_pool, o, S_pool, B, 1, H, d_k, d_v,
+                          in_dtype == GDN2_BF16, gate_flags};
+    a.slots = slots;
+    a.n_slots = n_slots;
+    return gdn2::launch_recurrent(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
 size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,

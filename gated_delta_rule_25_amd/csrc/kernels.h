@@ -16,6 +16,8 @@ struct RecurrentArgs {
     int B, T, H, DK, DV;
     bool bf16;
     uint32_t flags;
+    const int* slots = nullptr;  // decode over a state pool: batch row b uses state slots[b]
+    int n_slots = 0;
 };
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s);
 

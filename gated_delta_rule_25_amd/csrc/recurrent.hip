@@ -38,7 +38,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const void* __restrict__ alpha,
                  const void* __restrict__ b, const void* __restrict__ w,
                  const float* S0, float* __restrict__ o, float* S_out, int B, int T, int H,
-                 int DV) {
+                 int DV, const int* __restrict__ slots, int n_slots) {
     constexpr int R = DK / 8;  // rows per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int item = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
@@ -52,9 +52,16 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int row0 = rg * R;
     const int col0 = tile * 32 + cq * 4;
 
+    // the state of batch row bb: its own, or pool entry slots[bb] (rows whose slot lies outside
+    // the pool are skipped whole)
+    int sb = bb;
+    if (slots) {
+        sb = slots[bb];
+        if (sb < 0 || sb >= n_slots) return;
+    }
     // state slice in registers
     float S[R][4];
-    const long sbase = (long)bh * DK * DV;
+    const long sbase = ((long)sb * H + hh) * DK * DV;
     if (S0) {
 #pragma unroll
         for (int m = 0; m < R; ++m) {
@@ -188,7 +195,7 @@ hipError_t launch_t(const RecurrentArgs& a, hipStream_t s) {
     const int blocks = (items + waves_per_block - 1) / waves_per_block;
     hipLaunchKernelGGL((recurrent_kernel<DK, BF16, AS, BS, PRO>), dim3(blocks), dim3(64 * waves_per_block),
                        0, s, a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, a.o, a.S_out, a.B, a.T, a.H,
-                       a.DV);
+                       a.DV, a.slots, a.n_slots);
     return hipGetLastError();
 }
 
@@ -224,6 +231,7 @@ hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s) {
         case 32: return launch_dtype<32>(a, s);
         case 64: return launch_dtype<64>(a, s);
         case 128: return launch_dtype<128>(a, s);
+        case 256: return launch_dtype<256>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

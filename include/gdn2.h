@@ -136,7 +136,7 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
 /*
  * Token-by-token prefill: the same result as gdn2_chunk_fwd, computed one token at a time in
  * fp32 (each state column tile stays in registers for the whole sequence). Same arguments,
- * layouts, errors and aliasing rules; no workspace. Supported: d_k, d_v in {32, 64, 128}.
+ * layouts, errors and aliasing rules; no workspace. Supported: d_k, d_v in {32, 64, 128, 256}.
  */
 gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v, const void *alpha,
                                const void *b, const void *w, const float *S0, float *o,
@@ -149,7 +149,7 @@ gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v, cons
  * the whole history [GDN2-news, section "Контекст"]). Updates S in place,
  *     S <- (I - k (b (.) k)^T) Diag(alpha) S + k (w (.) v)^T,
  * and writes o = S^T q on the updated state. fp32 arithmetic; one read and one write of each
- * state. Supported: d_k, d_v in {32, 64, 128}.
+ * state. Supported: d_k, d_v in {32, 64, 128, 256}.
  */
 gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const void *alpha,
                              const void *b, const void *w, float *S, float *o, int32_t B,
@@ -189,6 +189,21 @@ gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const vo
  * which needs none). */
 size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                       gdn2_dtype in_dtype, uint32_t gate_flags);
+
+/*
+ * One decode step over a pool of states (serving: the batch rows name their sequences' slots).
+ * Batch row b (inputs q, k, v, alpha, b, w and output o as in gdn2_decode_step, [B, H, d]) updates
+ * S_pool[slots[b]] in place, S_pool being [n_slots, H, d_k, d_v] float32, and writes o[b]. slots
+ * is a device array of B int32 (4-byte aligned). A row whose slot is negative or not below n_slots
+ * is skipped: its o row and the pool are left as they are (padding rows). Two rows naming the
+ * same slot in one call race (the result is unspecified). Same arithmetic, flags and head sizes as
+ * gdn2_decode_step (the state-per-sequence constant decode memory of [GDN2-news, "Контекст"]).
+ */
+gdn2_status gdn2_decode_step_slots(const void *q, const void *k, const void *v, const void *alpha,
+                                   const void *b, const void *w, float *S_pool, const int32_t *slots,
+                                   float *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                                   int32_t n_slots, gdn2_dtype in_dtype, uint32_t gate_flags,
+                                   void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *gdn2_status_str(gdn2_status s);

@@ -123,3 +123,23 @@ def test_recurrent_rejects_bad_arguments(lib):
     p = list(FAKE[:9])
     assert f(*p, 1, 4, 0, 64, 64, 0, 0, None) == 2
     assert f(*p, 1, 4, 1, 64, 16, 0, 0, None) == 3
+
+
+def test_decode_slots_rejects_bad_arguments(lib):
+    f = lib.gdn2_decode_step_slots
+    p = list(FAKE[:6])
+    pool, slots, o = FAKE[6], FAKE[7], FAKE[8]
+    assert f(*p, pool, slots, o, 2, 1, 128, 128, 0, 0, 0, None) == 2      # no slots in the pool
+    assert f(*p, pool, None, o, 2, 1, 128, 128, 4, 0, 0, None) == 1       # slots missing
+    assert f(*p, None, slots, o, 2, 1, 128, 128, 4, 0, 0, None) == 1      # pool missing
+    assert f(*p, pool, P(0x80002), o, 2, 1, 128, 128, 4, 0, 0, None) == 4  # slots misaligned
+    assert f(*p, pool, slots, o, 2, 1, 96, 128, 4, 0, 0, None) == 3       # head size
+    assert f(*p, pool, slots, o, 2, 1, 128, 128, 4, 0, 16, None) == 3     # unknown flag
+    # the pool overlapping an input
+    assert f(*p, P(0x10000), slots, o, 2, 1, 128, 128, 4, 0, 0, None) == 5
+
+
+def test_head_size_256_is_taken_by_decode_and_token_paths_only(lib):
+    # the chunked prefill refuses d = 256 on the host (no launch); decode accepts the size and
+    # fails later only for the fake pointers' aliasing, not for the size
+    assert chunk_call(lib, dk=256, dv=256) == 3
