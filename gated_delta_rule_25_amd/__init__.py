@@ -21,7 +21,7 @@ import os
 
 import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to it)
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
            "chunk_bwd_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
            "decode_step_slots"]
@@ -59,6 +59,10 @@ def load():
     lib.gdn2_chunk_fwd.restype = ctypes.c_int
     lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
     lib.gdn2_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn2_chunk_fwd_varlen.argtypes = [p] * 10 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_fwd_varlen.restype = ctypes.c_int
+    lib.gdn2_chunk_fwd_varlen_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
+    lib.gdn2_chunk_fwd_varlen_workspace_bytes.restype = sz
     lib.gdn2_chunk_bwd.argtypes = [p] * 16 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
     lib.gdn2_chunk_bwd.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
@@ -159,6 +163,46 @@ def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspa
                             ws_bytes, _stream(stream))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_fwd", st)
+    return o, S_out
+
+
+def chunk_fwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
+    return int(load().gdn2_chunk_fwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v,
+                                                            BF16 if dtype == torch.bfloat16 else F32,
+                                                            flags))
+
+
+def chunk_fwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0=None, *, o=None, S_out=None, workspace=None,
+                     l2norm=False, gate_logits=False, stream=None):
+    """Prefill of N = len(cu_seqlens) - 1 sequences packed along the token axis.
+
+    q, k, alpha, b [T_total, H, d_k]; v, w [T_total, H, d_v] (scalar gates [T_total, H]);
+    cu_seqlens int32 on the GPU, sequence s = rows cu_seqlens[s] .. cu_seqlens[s+1] - 1;
+    S0 [N, H, d_k, d_v] or None. Returns (o [T_total, H, d_v] fp32, S_T [N, H, d_k, d_v]).
+    """
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 3) | _prologue_flags(l2norm, gate_logits)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or not cu_seqlens.is_cuda \
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise TypeError("cu_seqlens must be a contiguous 1-d int32 GPU tensor of N + 1 entries")
+    N = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty(T, H, dv, device=q.device, dtype=torch.float32)
+    S_out = _state_out(S0, N, H, dk, dv, q.device, S_out)
+    dt = _dtype_code(q)
+    if workspace is None:
+        need = int(lib.gdn2_chunk_fwd_varlen_workspace_bytes(N, T, H, dk, dv, dt, flags))
+        if need == 0:
+            raise Gdn2Error("gdn2_chunk_fwd_varlen", 3)
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.gdn2_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                   _ptr(o), _ptr(S_out), _ptr(cu_seqlens), N, T, H, dk, dv, dt, flags,
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd_varlen", st)
     return o, S_out
 
 

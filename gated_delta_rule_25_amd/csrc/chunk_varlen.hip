@@ -1,0 +1,143 @@
+// chunk_varlen.hip -- the two-kernel prefill (prep_kernel, chain_kernel) over a packed batch of
+// sequences of different lengths.
+//
+// The sequences lie back to back along the token axis ([T_total, H, d] rows) and are delimited
+// by cumulative lengths cu[0..n] that live on the device. Each sequence is chunked from its own
+// first token [page "NVIDIA представила Gated DeltaNet-2 с канал-wise гейтами …", paragraph
+// "Реализация": the chunkwise form restarts from the sequence's initial state], so a chunk never
+// spans two sequences. The host never reads cu: a one-workgroup kernel turns it into the
+// sequence table (first row, length, first chunk), prep runs over an upper bound of the chunk
+// count (the workgroups past the true count leave at once), and the chain runs one workgroup per
+// (sequence, head, value tile).
+#include "chunk_split_kernels.h"
+
+namespace gdn2 {
+
+namespace {
+
+using namespace chunk;
+
+// Sequence table from cu[0..n]: each bound is clamped to [0, T] and the bounds are made
+// non-decreasing (a running maximum), so any input gives sequences that partition rows inside
+// the batch; start[s] = cu'[s], len[s] = cu'[s+1] - cu'[s], and coff[s] = the sum of
+// ceil(len / C) over the sequences before s (coff[n] = the chunk count). One workgroup walks the
+// bounds in tiles of 256 with two block scans per tile.
+__global__ void __launch_bounds__(256) varlen_table_kernel(const int* __restrict__ cu, int n, int T,
+                                                           int* __restrict__ coff, int* __restrict__ start,
+                                                           int* __restrict__ len) {
+    __shared__ int smax[256], ssum[256], tail[2];
+    const int tid = threadIdx.x;
+    int cmax = 0, csum = 0;  // running maximum and chunk sum carried from the previous tiles
+    for (int base = 0; base <= n; base += 256) {
+        const int i = base + tid;
+        smax[tid] = i <= n ? min(max(cu[i], 0), T) : 0;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {  // inclusive max scan (all values are >= 0)
+            const int y = tid >= d ? smax[tid - d] : 0;
+            __syncthreads();
+            smax[tid] = max(smax[tid], y);
+            __syncthreads();
+        }
+        const int M = max(smax[tid], cmax);
+        const int Mp = tid > 0 ? max(smax[tid - 1], cmax) : cmax;  // bound i - 1
+        const int l = M - Mp;
+        ssum[tid] = (i >= 1 && i <= n) ? (l + CH - 1) / CH : 0;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {  // inclusive sum scan of the chunk counts
+            const int y = tid >= d ? ssum[tid - d] : 0;
+            __syncthreads();
+            ssum[tid] += y;
+            __syncthreads();
+        }
+        const int S = ssum[tid] + csum;
+        if (i <= n) coff[i] = S;
+        if (i < n) start[i] = M;
+        if (i >= 1 && i <= n) len[i - 1] = l;
+        if (tid == 255) {
+            tail[0] = M;
+            tail[1] = S;
+        }
+        __syncthreads();
+        cmax = tail[0];
+        csum = tail[1];
+        __syncthreads();  // tail and the scan arrays are rewritten by the next tile
+    }
+}
+
+template <int DK, bool BF16, bool AS, bool BS, int PRO>
+hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
+    constexpr bool WS = (PRO & 2) != 0 && !BS;  // w through the sigmoid in the chain
+    constexpr int DVT = DK < 64 ? DK : 64;
+    const int N = a.B;
+    const long ring = varlen_chunk_bound(N, a.T);
+    char* ws = static_cast<char*>(a.workspace);
+    int* coff = reinterpret_cast<int*>(ws);
+    int* start = coff + N + 1;
+    int* len = start + N;
+    char* blobs = ws + varlen_table_bytes(N);
+    VarTab vt;
+    vt.coff = coff;
+    vt.start = start;
+    vt.len = len;
+    vt.n = N;
+    hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, N, a.T, coff, start, len);
+    if (ring > 0)
+        hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0, st,
+                           a.q, a.k, a.alpha, a.b, 1, a.T, a.H, 0, (int)ring, blobs, vt);
+    const long ld = DK;
+    ChainIO io{a.v, a.w, a.o, blobs, (int)ring, 0, 0, 0, 1, N, a.T, a.H, a.DV,
+               a.S0, ld * a.DV, 0, a.DV,
+               a.S_out, ld * a.DV, 0, a.DV, 0};
+    io.var = vt;
+    const int BH = N * a.H, BHp = (BH + 7) / 8 * 8;
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS, true>), dim3(BHp * (a.DV / DVT)),
+                       dim3(kChainThreads), 0, st, io);
+    return hipGetLastError();
+}
+
+template <int DK, bool BF16, int PRO>
+hipError_t launch_varlen_gates(const ChunkArgs& a, hipStream_t s) {
+    switch (a.flags & 3u) {
+        case 0: return launch_varlen_t<DK, BF16, false, false, PRO>(a, s);
+        case 1: return launch_varlen_t<DK, BF16, true, false, PRO>(a, s);
+        case 2: return launch_varlen_t<DK, BF16, false, true, PRO>(a, s);
+        default: return launch_varlen_t<DK, BF16, true, true, PRO>(a, s);
+    }
+}
+
+template <int DK, bool BF16>
+hipError_t launch_varlen_flags(const ChunkArgs& a, hipStream_t s) {
+    switch ((a.flags >> 2) & 3u) {
+        case 0: return launch_varlen_gates<DK, BF16, 0>(a, s);
+        case 1: return launch_varlen_gates<DK, BF16, 1>(a, s);
+        case 2: return launch_varlen_gates<DK, BF16, 2>(a, s);
+        default: return launch_varlen_gates<DK, BF16, 3>(a, s);
+    }
+}
+
+}  // namespace
+
+long varlen_chunk_bound(int n, int T) {
+    // sum over sequences of ceil(len / C) <= (sum of len + (C - 1) n) / C
+    return ((long)T + (long)(CH - 1) * n) / CH;
+}
+
+size_t varlen_table_bytes(int n) { return ((size_t)(3 * (size_t)n + 1) * 4 + 255) / 256 * 256; }
+
+size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16) {
+    return varlen_table_bytes(n) + (size_t)varlen_chunk_bound(n, T) * split_chunk_bytes(1, H, DK, bf16);
+}
+
+hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s) {
+    if (!split_supported(a.T, a.H, a.DK, a.DV, a.bf16) || !a.cu_seqlens) return hipErrorNotSupported;
+    if (a.bf16) {
+        switch (a.DK) {
+            case 32: return launch_varlen_flags<32, true>(a, s);
+            case 64: return launch_varlen_flags<64, true>(a, s);
+            default: return launch_varlen_flags<128, true>(a, s);
+        }
+    }
+    return launch_varlen_flags<32, false>(a, s);
+}
+
+}  // namespace gdn2

@@ -180,6 +180,57 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+size_t gdn2_chunk_fwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
+                                             int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags) {
+    if (N <= 0 || H <= 0 || T_total < 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    const bool bf16 = in_dtype == GDN2_BF16;
+    if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return 0;
+    return gdn2::varlen_workspace_bytes(N, T_total, H, d_k, d_v, bf16);
+}
+
+gdn2_status gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                                  const void* b, const void* w, const float* S0, float* o,
+                                  float* S_out, const int32_t* cu_seqlens, int32_t N,
+                                  int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                  gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (N <= 0) return GDN2_ERR_SHAPE;
+    // the token rows are one sequence of T_total tokens as far as sizes go; the states separately
+    gdn2_status st = validate(q, k, v, alpha, b, w, nullptr, o, nullptr, 1, T_total, H, d_k, d_v,
+                              in_dtype, gate_flags, false);
+    if (st != GDN2_OK) return st;
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    if (!workspace) return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_ERR_ALIGN;
+    if ((S0 && !aligned16(S0)) || (S_out && !aligned16(S_out))) return GDN2_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+    const bool bf16 = in_dtype == GDN2_BF16;
+    if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
+    // one workgroup per (chunk bound, head) in prep: the grid must stay below 2^31
+    if (gdn2::varlen_chunk_bound(N, T_total) * H >= (1l << 31)) return GDN2_ERR_SHAPE;
+    Sizes sz, states;
+    if (!sizes_of(1, T_total, H, d_k, d_v, &sz) || !sizes_of(N, 1, H, d_k, d_v, &states)) return GDN2_ERR_SHAPE;
+    if (workspace_bytes < gdn2::varlen_workspace_bytes(N, T_total, H, d_k, d_v, bf16)) return GDN2_ERR_WORKSPACE;
+    const uint64_t es = bf16 ? 2 : 4;
+    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
+    const Range ins[] = {range_of(q, sz.qk * es), range_of(k, sz.qk * es), range_of(v, sz.vw * es),
+                         range_of(alpha, (as ? sz.scalar : sz.qk) * es), range_of(b, (bs ? sz.scalar : sz.qk) * es),
+                         range_of(w, sz.vw * es), range_of(cu_seqlens, ((uint64_t)N + 1) * 4)};
+    const Range rS0 = range_of(S0, states.state * 4), rSo = range_of(S_out, states.state * 4);
+    const Range ro = range_of(o, sz.vw * 4), rws = range_of(workspace, workspace_bytes);
+    for (const Range& r : ins)
+        if (overlap(rSo, r) || overlap(ro, r) || overlap(rws, r)) return GDN2_ERR_ALIAS;
+    if (overlap(ro, rS0) || overlap(ro, rSo) || overlap(rws, rS0) || overlap(rws, rSo) || overlap(rws, ro))
+        return GDN2_ERR_ALIAS;
+    if (overlap(rS0, rSo) && !(rS0.lo == rSo.lo && rS0.hi == rSo.hi)) return GDN2_ERR_ALIAS;
+    gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, N, T_total, H, d_k, d_v, bf16, gate_flags,
+                      workspace, workspace_bytes};
+    a.cu_seqlens = cu_seqlens;
+    const hipError_t e = gdn2::launch_split_varlen(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 gdn2_status gdn2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
                              const void* b, const void* w, float* S, float* o, int32_t B,
                              int32_t H, int32_t d_k, int32_t d_v, gdn2_dtype in_dtype,

@@ -32,6 +32,7 @@ struct ChunkArgs {
     uint32_t flags;
     void* workspace;
     size_t workspace_bytes;
+    const int* cu_seqlens = nullptr;  // packed batch: B + 1 cumulative lengths (device), T = rows
 };
 // Single-kernel path (no workspace). Returns hipErrorNotSupported when it does not cover
 // the arguments.
@@ -46,6 +47,13 @@ hipError_t launch_split(const ChunkArgs& a, hipStream_t s);
 bool split_supported(int T, int H, int DK, int DV, bool bf16);
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16);
 size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16);
+// Two-kernel path over a packed batch of a.B sequences, a.T rows in all, delimited by
+// a.cu_seqlens. Workspace (one round, no segments): the sequence table, then one slot per chunk
+// of an upper bound on the chunk count (varlen_chunk_bound), per head.
+hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s);
+long varlen_chunk_bound(int n, int T);
+size_t varlen_table_bytes(int n);
+size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16);
 // Prep over every chunk into `blobs` ([b*h][chunk] operand blocks), then the state-only chain in
 // order, saving the state at the start of every chunk ([b*h][chunk][DK][DV]) and the rows of D'
 // and Delta ([B, T, H, DV]). bf16 inputs, general gates.

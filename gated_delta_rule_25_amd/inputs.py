@@ -142,6 +142,39 @@ def make_prologue_inputs(wl: Workload, *, device: str = "cpu") -> dict:
                 alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)
 
 
+def packed_lengths(n: int, total: int, *, seed: int, lo: int = 16, hi: int = 4096) -> list:
+    """A length mix for a packed batch: n lengths drawn log-uniformly in [lo, hi], rescaled to sum
+    to `total` (floored; the remainder goes to the last sequence). Serving batches mix short and
+    long prompts; the pages give no length distribution, so this one is a stand-in."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    raw = np.exp(rng.uniform(np.log(lo), np.log(hi), n))
+    ls = np.floor(raw / raw.sum() * total).astype(np.int64)
+    ls[-1] += total - int(ls.sum())
+    return [int(x) for x in ls]
+
+
+def make_packed_inputs(wl: Workload, lengths, *, device: str = "cpu", raw: bool = False) -> dict:
+    """A packed batch of len(lengths) sequences: the workload's recipe drawn as one row of
+    sum(lengths) tokens (B = 1, then the batch axis dropped: q [T_total, H, d_k] ...), one
+    initial state per sequence ([N, H, d_k, d_v], seed + 15485863, or None when s0_std is 0) and
+    cu_seqlens [N + 1] int32. raw=True draws the prologue recipe (make_prologue_inputs)."""
+    T = int(sum(lengths))
+    one = dataclasses.replace(wl, B=1, T=T)
+    ins = (make_prologue_inputs if raw else make_inputs)(one, device="cpu")
+    for n in ("q", "k", "v", "alpha", "b", "w"):
+        if ins[n] is not None:
+            ins[n] = ins[n][0].contiguous().to(device)
+    N = len(lengths)
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 15485863))
+    S0 = None
+    if wl.s0_std > 0:
+        S0 = torch.from_numpy(rng.standard_normal((N, wl.H, wl.d_k, wl.d_v), dtype=np.float32)
+                              * np.float32(wl.s0_std)).to(device)
+    ins["S0"] = S0
+    ins["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(device)
+    return ins
+
+
 def make_cotangents(wl: Workload, *, device: str = "cpu", final_state: bool = True) -> dict:
     """Seeded cotangents for the backward: dO [B, T, H, d_v] and dS_T [B, H, d_k, d_v] (or None),
     both standard normal in float32, drawn from their own stream (seed + 7919)."""

@@ -134,6 +134,46 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
 
 /*
+ * Prefill of N sequences of different lengths packed along the token axis, each run from its
+ * own initial state exactly as gdn2_chunk_fwd runs one sequence (chunks of 64 counted from the
+ * sequence's first token [GDN2-summary, paragraph "Реализация"]; no chunk spans two sequences).
+ * The packing itself is a layout of this library, not of the method.
+ *
+ *   cu_seqlens  [N + 1] int32 in device memory: sequence s is rows cu_seqlens[s] ..
+ *               cu_seqlens[s + 1] - 1. Expected: cu_seqlens[0] == 0, non-decreasing,
+ *               cu_seqlens[N] == T_total (empty sequences allowed). The host does not read it; on
+ *               the device each bound is clamped to [0, T_total] and the bounds are made
+ *               non-decreasing, so other values cannot make the kernels touch memory outside the
+ *               arrays, but rows then left outside every sequence keep their o unwritten.
+ *   q, k, alpha, b  [T_total, H, d_k]; v, w [T_total, H, d_v] (scalar gates [T_total, H]);
+ *               in_dtype, gate_flags and their layouts as in gdn2_chunk_fwd
+ *   S0, S_out   [N, H, d_k, d_v] float32 (S0 NULL = zeros; S_out NULL = not stored;
+ *               S_out == S0 allowed). A sequence without tokens gets S_out = S0.
+ *   o           [T_total, H, d_v] float32
+ *   workspace   required, 256-byte aligned, at least gdn2_chunk_fwd_varlen_workspace_bytes
+ *               (the sequence table, then one operand block per chunk of
+ *               (T_total + 63 N) / 64 chunks per head, which bounds the chunk count); scratch.
+ *
+ * Same two kernels as the workspace path of gdn2_chunk_fwd (one round, no segments), preceded by
+ * a one-workgroup kernel that builds the sequence table. Supported sizes and errors as there:
+ * bf16 with d in {32, 64, 128}, fp32 with d = 32, d_k == d_v, T_total*H*d_v*4 < 2^32, any
+ * flags; GDN2_ERR_NULL without cu_seqlens, GDN2_ERR_WORKSPACE without a workspace or with
+ * fewer bytes than the query returns, GDN2_ERR_ALIGN for a cu_seqlens not 4-byte aligned or a
+ * workspace not 256-byte aligned, GDN2_ERR_ALIAS when an output or the workspace overlaps
+ * anything else (S_out == S0 excepted), GDN2_ERR_SHAPE for N <= 0 or T_total < 0.
+ */
+gdn2_status gdn2_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *alpha,
+                                  const void *b, const void *w, const float *S0, float *o,
+                                  float *S_out, const int32_t *cu_seqlens, int32_t N,
+                                  int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                  gdn2_dtype in_dtype, uint32_t gate_flags, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for gdn2_chunk_fwd_varlen at these sizes; 0 when the sizes are not supported. */
+size_t gdn2_chunk_fwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
+                                             int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
+
+/*
  * Token-by-token prefill: the same result as gdn2_chunk_fwd, computed one token at a time in
  * fp32 (each state column tile stays in registers for the whole sequence). Same arguments,
  * layouts, errors and aliasing rules; no workspace. Supported: d_k, d_v in {32, 64, 128, 256}.

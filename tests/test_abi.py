@@ -143,3 +143,35 @@ def test_head_size_256_is_taken_by_decode_and_token_paths_only(lib):
     # the chunked prefill refuses d = 256 on the host (no launch); decode accepts the size and
     # fails later only for the fake pointers' aliasing, not for the size
     assert chunk_call(lib, dk=256, dv=256) == 3
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    f = lib.gdn2_chunk_fwd_varlen
+    qs = lib.gdn2_chunk_fwd_varlen_workspace_bytes
+    p = [P(0x200000000 * (i + 1)) for i in range(9)]  # 8 GiB apart: nothing overlaps
+    cu = P(0x200000000 * 10)
+    ws = P(0x200000000 * 11)
+    need = qs(4, 1000, 2, 128, 128, 0, 0)
+    # table (3 N + 1 ints, padded to 256 B) then (T + 63 N) / 64 = 19 chunks per head
+    assert need == 256 + 19 * 2 * (qs(1, 64, 1, 128, 128, 0, 0) - 256)
+    assert qs(4, 1000, 2, 128, 128, 1, 0) == 0      # fp32 at d = 128: not supported
+    assert qs(0, 1000, 2, 128, 128, 0, 0) == 0
+
+    def call(ptrs=p, cu=cu, N=4, T=1000, H=2, dk=128, dv=128, dt=0, flags=0, ws=ws, wsb=need):
+        return f(*ptrs, cu, N, T, H, dk, dv, dt, flags, ws, wsb, None)
+
+    assert call(N=0) == 2
+    assert call(T=-1) == 2
+    assert call(cu=None) == 1
+    assert call(cu=P(0x200000000 * 10 + 2)) == 4
+    assert call(ws=None) == 7
+    assert call(wsb=need - 1) == 7
+    assert call(ws=P(0x200000000 * 11 + 128)) == 4     # workspace not 256-byte aligned
+    assert call(dk=256, dv=256) == 3
+    assert call(dt=1) == 3                             # fp32 at d = 128
+    assert call(flags=32) == 3
+    assert call(cu=P(0x200000000 * 8)) == 5            # cu_seqlens overlaps o
+    q = list(p)
+    q[7] = q[1]
+    assert call(ptrs=q) == 5                           # o overlaps k
+    assert call(ws=P(0x200000000 * 7)) == 5            # workspace over S0
