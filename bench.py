@@ -156,6 +156,45 @@ def prefill_leg(g, name, steps, impl):
     return res
 
 
+def varlen_leg(g, steps, ref_ms=None):
+    """gdn2_chunk_fwd_varlen on a packed batch with the headline's token count: 32 sequences in a
+    length mix (packed_lengths), 32,768 rows, H16 d128 bf16; warm, back to back, on the launch
+    stream. ref_ms: the equal-length B8 T4096 call, for the ratio."""
+    import torch
+    from gated_delta_rule_25_amd.inputs import WORKLOADS, make_packed_inputs, packed_lengths
+    wl = WORKLOADS["prefill_1p3b"]
+    lengths = packed_lengths(32, 32768, seed=wl.seed)
+    ins = make_packed_inputs(wl, lengths, device="cuda")
+    H, dk, dv = wl.H, wl.d_k, wl.d_v
+    T = sum(lengths)
+    o = torch.empty(T, H, dv, device="cuda", dtype=torch.float32)
+    S_out = torch.empty(len(lengths), H, dk, dv, device="cuda", dtype=torch.float32)
+    ws = torch.empty(g.chunk_fwd_varlen_workspace_bytes(len(lengths), T, H, dk, dv), dtype=torch.uint8,
+                     device="cuda")
+    args = [ins[n] for n in ("q", "k", "v", "alpha", "b", "w")] + [ins["cu_seqlens"], ins["S0"]]
+    kw = dict(o=o, S_out=S_out, workspace=ws)
+    g.chunk_fwd_varlen(*args, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.chunk_fwd_varlen(*args, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = sum(prefill_bytes_per_head_token(dk, dv, L) * L * H for L in lengths if L > 0)
+    res = dict(config=f"32 sequences packed, {T} rows, lengths {min(lengths)}..{max(lengths)}, H{H} d{dk} bf16",
+               ms=round(ms, 4), tokens_per_s=round(T / (ms * 1e-3), 1), algorithmic_bytes=int(alg),
+               gbs=round(alg / (ms * 1e-3) / 1e9, 1), frac=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               vs_equal_length=(round(ms / ref_ms, 3) if ref_ms else None))
+    print(f"[bench] packed prefill: {ms:.3f} ms/call, {res['tokens_per_s']:.3e} tokens/s, {res['gbs']} GB/s "
+          f"algorithmic", file=sys.stderr, flush=True)
+    del ins, o, S_out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bwd_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
     # q, k, alpha, b, v, w (bf16) + dO (fp32) read; dq, dk, dalpha, db, dv, dw (fp32) written;
     # S0 and dS_T read and dS0 written, amortised over T
@@ -335,6 +374,9 @@ def main(argv=None):
 
     others = {}
     bwd = None
+    packed = None
+    if not args.skip_others and args.workload == "prefill_1p3b" and args.impl == "chunk":
+        packed = varlen_leg(g, 10, kern_avg)
     if not args.skip_backward and args.workload == "prefill_1p3b":
         bwd = backward_leg(g, 5)
     if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
@@ -391,6 +433,7 @@ def main(argv=None):
         "cold_ms": round(cold_ms, 4),
         "other_prefill": others,
         "backward": bwd,
+        "packed_prefill": packed,
         "prologue": prologue,
         "decode": dec,
         "cpu_baseline": cpu,
