@@ -441,8 +441,9 @@ struct KeyIO {
 // blocks J < I splits at a row between them into two factors no larger than 1:
 //   XA, XP (sum over s in J):  2^(G_r - G_e(J)) * [k_s 2^(G_e(J) - G_s)],   e(J) = last row of J,
 //   Y      (sum over r in I):  [x_r 2^(G_r - G_b(I))] * 2^(G_b(I) - G_s),   b(I) = first row of I,
-// so the inner sums are plain multiply-adds over pre-scaled rows; inside a block the factor is
-// taken directly (one exp2 per term).
+// so each block pair's sum is a 16x16 by 16x32 matrix product over pre-scaled rows (fp32 on the
+// matrix cores) followed by one scale per output; inside a block the factor is taken directly
+// (one exp2 per term, on the vector units).
 template <int DK>
 __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     constexpr int CW = 32;       // key channels per workgroup
@@ -485,6 +486,17 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         lA[u] = io.dAm[cbase * CH * CH + tid + 256 * u];
         lP[u] = io.dPm[cbase * CH * CH + tid + 256 * u];
     }
+    // this thread's rows p + 8 m of channel i for the elementwise phase: dQ_hat, dE_hat, dK_bar
+    const int i = tid % CW, p = tid / CW;
+    float gQv[8], gEv[8], gKv[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const size_t ce = (cbase * CH + p + 8 * m) * DK + c0 + i;
+        gQv[m] = io.dQh[ce];
+        gEv[m] = io.dEh[ce];
+        gKv[m] = io.dKb[ce];
+    }
+    const float dgam_i = io.dgam[cbase * DK + c0 + i];
 #pragma unroll
     for (int u = 0; u < NX; ++u) {
         const int x = tid + 256 * u, r = x / CW;
@@ -519,46 +531,93 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     }
     __syncthreads();
 
-    const int i = tid % CW, p = tid / CW;  // rows p, p + 8, ..., p + 56
+    // Blocks off the diagonal on the matrix cores (fp32 16x16x4): wave w takes row block I = w
+    // and both 16-channel tiles. XA, XP of rows in I sum over blocks J < I, Y over blocks I2 > I;
+    // each block's product is scaled by its reference factor per (row, channel) and added. The
+    // 16 block rows are contracted in 4 passes, lane group g holding rows 4 g .. 4 g + 3.
+    {
+        const int I = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+        f4 xa[2], xp[2], yy[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) xa[ct] = xp[ct] = yy[ct] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int J = 0; J < I; ++J) {
+            f4 sa[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+            f4 sp[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ip = 0; ip < 4; ++ip) {
+                const int s = 16 * J + 4 * g + ip;
+                const float a = dA[(16 * I + l16) * CH + s], pp = dPs[(16 * I + l16) * CH + s];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const float kp = Kp[s * CW + 16 * ct + l16];
+                    sa[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, kp, sa[ct], 0, 0, 0);
+                    sp[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp, kp, sp[ct], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const float ge = G2[(16 * J + 15) * CW + 16 * ct + l16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float fJ = __builtin_amdgcn_exp2f(G2[(16 * I + 4 * g + j) * CW + 16 * ct + l16] - ge);
+                    xa[ct][j] = fmaf(fJ, sa[ct][j], xa[ct][j]);
+                    xp[ct][j] = fmaf(fJ, sp[ct][j], xp[ct][j]);
+                }
+            }
+        }
+        for (int I2 = I + 1; I2 < 4; ++I2) {
+            f4 sy[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ip = 0; ip < 4; ++ip) {
+                const int r2 = 16 * I2 + 4 * g + ip;
+                const float a = dA[r2 * CH + 16 * I + l16], pp = dPs[r2 * CH + 16 * I + l16];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    sy[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ep[r2 * CW + 16 * ct + l16], sy[ct], 0, 0, 0);
+                    sy[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp, Qp[r2 * CW + 16 * ct + l16], sy[ct], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const float gb = G2[(16 * I2) * CW + 16 * ct + l16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float f = __builtin_amdgcn_exp2f(gb - G2[(16 * I + 4 * g + j) * CW + 16 * ct + l16]);
+                    yy[ct][j] = fmaf(f, sy[ct][j], yy[ct][j]);
+                }
+            }
+        }
+        __syncthreads();  // every read of Kp, Ep, Qp is done: they take the sums off the diagonal
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int x = (16 * I + 4 * g + j) * CW + 16 * ct + l16;
+                Kp[x] = xa[ct][j];
+                Ep[x] = xp[ct][j];
+                Qp[x] = yy[ct][j];
+            }
+    }
+    __syncthreads();
+
     const float G63 = G2[(CH - 1) * CW + i];
     float dG[8];
     float kb_sum = 0.f;
-#pragma unroll 1
+    // rows p, p + 8, ..., p + 56 (the row's block I changes every other step)
+#pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int r = p + 8 * m, I = r / 16;
         const float Gr = G2[r * CW + i];
         const float kr = f(ks[r * CW + i]), qr = f(qs[r * CW + i]), br = f(bs[r * CW + i]);
-        // XA, XP: earlier blocks through the block-end references, then the diagonal block
-        float XA = 0.f, XP = 0.f;
-        for (int J = 0; J < I; ++J) {
-            float sA = 0.f, sP = 0.f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int s = 16 * J + u;
-                const float kp = Kp[s * CW + i];
-                sA = fmaf(dA[r * CH + s], kp, sA);
-                sP = fmaf(dPs[r * CH + s], kp, sP);
-            }
-            const float fJ = __builtin_amdgcn_exp2f(Gr - G2[(16 * J + 15) * CW + i]);
-            XA = fmaf(fJ, sA, XA);
-            XP = fmaf(fJ, sP, XP);
-        }
+        // XA, XP: the earlier blocks' sums (above), then the diagonal block term by term
+        float XA = Kp[r * CW + i], XP = Ep[r * CW + i];
         for (int s = 16 * I; s <= r; ++s) {
             const float w = f(ks[s * CW + i]) * __builtin_amdgcn_exp2f(Gr - G2[s * CW + i]);
             if (s < r) XA = fmaf(dA[r * CH + s], w, XA);
             XP = fmaf(dPs[r * CH + s], w, XP);
         }
-        // Y: later blocks through the block-start references, then the diagonal block
-        float Y = 0.f;
-        for (int I2 = I + 1; I2 < 4; ++I2) {
-            float sY = 0.f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int r2 = 16 * I2 + u;
-                sY = fmaf(dA[r2 * CH + r], Ep[r2 * CW + i], fmaf(dPs[r2 * CH + r], Qp[r2 * CW + i], sY));
-            }
-            Y = fmaf(__builtin_amdgcn_exp2f(G2[(16 * I2) * CW + i] - Gr), sY, Y);
-        }
+        // Y: the later blocks' sums (above), then the diagonal block term by term
+        float Y = Qp[r * CW + i];
         for (int r2 = r; r2 < 16 * I + 16; ++r2) {
             const float w = __builtin_amdgcn_exp2f(G2[r2 * CW + i] - Gr);
             const float e2 = f(bs[r2 * CW + i]) * f(ks[r2 * CW + i]);
@@ -567,8 +626,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
             Y = fmaf(term, w, Y);
         }
         const float eG = __builtin_amdgcn_exp2f(Gr), eK = __builtin_amdgcn_exp2f(G63 - Gr);
-        const size_t ce = (cbase * CH + r) * DK + c0 + i;
-        const float gQ = io.dQh[ce], gE = io.dEh[ce], gK = io.dKb[ce];
+        const float gQ = gQv[m], gE = gEv[m], gK = gKv[m];
         const float Et = br * kr;
         const float dEt = fmaf(gE, eG, XA);
         const float dqv = fmaf(gQ, eG, XP);
@@ -585,7 +643,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         }
     }
     red[tid] = kb_sum;
-    __syncthreads();  // every read of Kp is done
+    __syncthreads();  // every read of Kp, Ep, Qp is done
 #pragma unroll
     for (int m = 0; m < 8; ++m) Kp[(p + 8 * m) * CW + i] = dG[m];
     __syncthreads();
@@ -595,7 +653,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     float seg = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) seg += Kp[(8 * p + u) * CW + i];
-    float extra = io.dgam[cbase * DK + c0 + i] * __builtin_amdgcn_exp2f(G63);
+    float extra = dgam_i * __builtin_amdgcn_exp2f(G63);
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) extra += red[pp * CW + i];
     __syncthreads();  // every read of red is done
