@@ -76,8 +76,16 @@ struct ChainBwdIO {
     int B, T, H, DV, nch;
 };
 
+// Waves own 16 value columns each. The next (earlier) chunk's block is copied into the other LDS
+// buffer, and its dO, v, w rows loaded into registers, at the start of each step, so the copies
+// run while the current chunk is worked on; the wait at the next step's start finds them done.
 template <int DK>
-__global__ void __launch_bounds__(256, 1) bwd_chain_kernel(const ChainBwdIO io) {
+constexpr int bwd_chain_threads() {
+    return ((DK < 64 ? DK : 64) / 16) * 64;
+}
+
+template <int DK>
+__global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(const ChainBwdIO io) {
     using PR = Prec<true>;
     using E = _Float16;
     using Frag = PR::Frag;
@@ -86,13 +94,7 @@ __global__ void __launch_bounds__(256, 1) bwd_chain_kernel(const ChainBwdIO io) 
     constexpr int DVT = DK < 64 ? DK : 64;
     constexpr int NW = DVT / 16;  // waves, 16 value columns each
 
-    __shared__ __attribute__((aligned(16))) char smem[BL::bytes];
-    const E* En = reinterpret_cast<const E*>(smem + BL::oEn);
-    const E* KbT = reinterpret_cast<const E*>(smem + BL::oKbT);
-    const E* Tm = reinterpret_cast<const E*>(smem + BL::oTm);
-    const E* Pm = reinterpret_cast<const E*>(smem + BL::oP);
-    const E* Qh = reinterpret_cast<const E*>(smem + BL::oQh);
-    const float* gC = reinterpret_cast<const float*>(smem + BL::oGC);
+    __shared__ __attribute__((aligned(16))) char smem[2 * BL::bytes];
 
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, DV = io.DV, nch = io.nch;
@@ -100,6 +102,7 @@ __global__ void __launch_bounds__(256, 1) bwd_chain_kernel(const ChainBwdIO io) 
     const int bh = blockIdx.x / vt, tile = blockIdx.x % vt;
     const int hh = bh % H, bb = bh / H;
     const int col = tile * DVT + 16 * wv + l16;
+    auto blob_of = [&](int n) { return io.blobs + ((size_t)bh * nch + n) * BL::bytes; };
 
     const long seq = (long)bb * T * H;
     const unsigned seq_f32 = (unsigned)T * H * DV * 4u;
@@ -131,12 +134,53 @@ __global__ void __launch_bounds__(256, 1) bwd_chain_kernel(const ChainBwdIO io) 
         return PR::make(t);
     };
 
-    for (int n = nch - 1; n >= 0; --n) {
+    // the rows one chunk needs from memory: dO as B operands (k = token row 32 s2 + kap(g, i),
+    // rows past T read as zero), v and w at rows 16 mt + 4 g + j
+    float xdO[16], xv[16], xw[16];
+    auto fetch = [&](int n) {
         const int t0 = n * CH;
-        lds_barrier();  // every read of the previous block is done
-        dma_flat(io.blobs + ((size_t)bh * nch + n) * BL::bytes, smem, BL::bytes, wv, NW, lane);
-        wait_dma();
-        lds_barrier();
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xdO[8 * s2 + i] = bload_f32(rs_dO, elem(t0 + 32 * s2 + kap(g, i)) * 4u);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned e = elem(t0 + 16 * mt + 4 * g + j);
+                xv[4 * mt + j] = bload_bf16(rs_v, e * 2u);
+                xw[4 * mt + j] = bload_bf16(rs_w, e * 2u);
+            }
+    };
+    if (nch > 0) {
+        dma_flat(blob_of(nch - 1), smem, BL::bytes, wv, NW, lane);
+        fetch(nch - 1);
+    }
+
+    for (int idx = 0; idx < nch; ++idx) {
+        const int n = nch - 1 - idx, t0 = n * CH;
+        wait_dma();     // this wave's part of block n and its rows of chunk n have arrived
+        lds_barrier();  // block n is whole; every read of the other buffer is done
+        if (n > 0) dma_flat(blob_of(n - 1), smem + ((idx + 1) & 1) * BL::bytes, BL::bytes, wv, NW, lane);
+        const char* buf = smem + (idx & 1) * BL::bytes;
+        const E* En = reinterpret_cast<const E*>(buf + BL::oEn);
+        const E* KbT = reinterpret_cast<const E*>(buf + BL::oKbT);
+        const E* Tm = reinterpret_cast<const E*>(buf + BL::oTm);
+        const E* Pm = reinterpret_cast<const E*>(buf + BL::oP);
+        const E* Qh = reinterpret_cast<const E*>(buf + BL::oQh);
+        const float* gC = reinterpret_cast<const float*>(buf + BL::oGC);
+
+        // this chunk's rows, then the loads for the next one (they complete while this one runs)
+        Frag dOf[2];
+        dOf[0] = PR::make(xdO);
+        dOf[1] = PR::make(xdO + 8);
+        float cv[16], cw[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            cv[u] = xv[u];
+            cw[u] = xw[u];
+        }
+        if (n > 0) fetch(n - 1);
 
         // G' of this chunk, for the contraction kernel
         float* gs = io.G_save + ((size_t)bh * nch + n) * DK * DV;
@@ -145,15 +189,6 @@ __global__ void __launch_bounds__(256, 1) bwd_chain_kernel(const ChainBwdIO io) 
 #pragma unroll
             for (int j = 0; j < 4; ++j) gs[(size_t)(16 * mk + 4 * g + j) * DV + col] = G[mk][j];
 
-        // dO of the chunk's rows as B operands (k = token row, n = column); rows past T are zero
-        Frag dOf[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = bload_f32(rs_dO, elem(t0 + 32 * s2 + kap(g, i)) * 4u);
-            dOf[s2] = PR::make(x);
-        }
         Frag Gf[NKS];
 #pragma unroll
         for (int s = 0; s < NKS; ++s) Gf[s] = stack(G[2 * s], G[2 * s + 1]);
@@ -202,9 +237,8 @@ __global__ void __launch_bounds__(256, 1) bwd_chain_kernel(const ChainBwdIO io) 
                 const unsigned e = elem(t0 + 16 * mt + 4 * g + j);
                 bstore_f32(rs_dDl, e * 4u, dL[mt][j]);
                 bstore_f32(rs_dDp, e * 4u, dP[mt][j]);
-                const float vv = bload_bf16(rs_v, e * 2u), ww = bload_bf16(rs_w, e * 2u);
-                bstore_f32(rs_dv, e * 4u, ww * dP[mt][j]);
-                bstore_f32(rs_dw, e * 4u, vv * dP[mt][j]);
+                bstore_f32(rs_dv, e * 4u, cw[4 * mt + j] * dP[mt][j]);
+                bstore_f32(rs_dw, e * 4u, cv[4 * mt + j] * dP[mt][j]);
             }
         // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (En = -E_hat)
         const Frag dPf[2] = {stack(dP[0], dP[1]), stack(dP[2], dP[3])};
@@ -437,238 +471,321 @@ struct KeyIO {
 };
 
 // One workgroup per (b, h, chunk, 32 key channels): the decay-weighted sums are independent per
-// channel. With G the cumulative log2 decay and 16-row blocks, a factor 2^(G_r - G_s) between
-// blocks J < I splits at a row between them into two factors no larger than 1:
-//   XA, XP (sum over s in J):  2^(G_r - G_e(J)) * [k_s 2^(G_e(J) - G_s)],   e(J) = last row of J,
-//   Y      (sum over r in I):  [x_r 2^(G_r - G_b(I))] * 2^(G_b(I) - G_s),   b(I) = first row of I,
-// so each block pair's sum is a 16x16 by 16x32 matrix product over pre-scaled rows (fp32 on the
-// matrix cores) followed by one scale per output; inside a block the factor is taken directly
-// (one exp2 per term, on the vector units).
+// channel. With G the cumulative log2 decay, a factor 2^(G_r - G_s) between row groups X < Y
+// (r in Y, s in X) splits at a row between them into two factors no larger than 1:
+//   XA, XP (sum over s in X):  2^(G_r - G_e(X)) * [k_s 2^(G_e(X) - G_s)],   e(X) = last row of X,
+//   Y      (sum over r in Y):  [x_r 2^(G_r - G_b(Y))] * 2^(G_b(Y) - G_s),   b(Y) = first row of Y,
+// so each group pair's sum is a matrix product over pre-scaled rows (fp32 on the matrix cores)
+// followed by one scale per output. This is applied twice: between 16-row blocks, then between
+// 4-row sub-blocks inside each diagonal block; inside a 4-row sub-block the factor is taken
+// directly (one exp2 per pair).
+//
+// Wave w takes row block I = w; lane (g, l16) owns rows 16 I + 4 g + j (j = 0..3, sub-block
+// 4 I + g) and channels 2 l16 + c (c = 0, 1) of the group, which is the matrix cores' output
+// layout when column l16 of tile c stands for channel 2 l16 + c.
 template <int DK>
 __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     constexpr int CW = 32;       // key channels per workgroup
     constexpr int NG = DK / CW;  // channel groups
     static_assert(DK % CW == 0, "channel groups");
-    __shared__ float dA[CH * CH], dPs[CH * CH];
-    __shared__ float G2[CH * CW];                   // cumulative log2 decay
-    __shared__ float Kp[CH * CW], Ep[CH * CW], Qp[CH * CW];  // pre-scaled rows (Kp then dL/dG)
-    __shared__ uint16_t qs[CH * CW], ks[CH * CW], bs[CH * CW];
-    __shared__ float red[8 * CW];
+    __shared__ __attribute__((aligned(16))) float dA[CH * CH];
+    __shared__ __attribute__((aligned(16))) float dPs[CH * CH];
+    __shared__ float G2[CH * CW];                         // cumulative log2 decay
+    __shared__ float Xk[CH * CW], Xe[CH * CW], Xq[CH * CW];  // pre-scaled rows of k, b*k, q
+    __shared__ float part[16 * CW];                       // per sub-block sums over rows
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, I = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, nch = io.nch;
     const int cg = blockIdx.x % NG, item = blockIdx.x / NG;
     const int bh = item / nch, n = item % nch;
     const int hh = bh % H, bb = bh / H;
     const int t0 = n * CH, c0 = cg * CW;
     const size_t cbase = (size_t)bh * nch + n;
-    auto f = [](uint16_t x) { return __uint_as_float((uint32_t)x << 16); };
-    const uint16_t* q = static_cast<const uint16_t*>(io.q);
-    const uint16_t* k = static_cast<const uint16_t*>(io.k);
-    const uint16_t* al = static_cast<const uint16_t*>(io.alpha);
-    const uint16_t* b = static_cast<const uint16_t*>(io.b);
-    // every global load is issued before the first LDS write, so their latencies overlap
-    constexpr int NX = CH * CW / 256, NA = CH * CH / 256;
-    uint16_t lq[NX], lk[NX], lb[NX], la[NX];
-    float lA[NA], lP[NA];
+    const int ch0 = 2 * l16;  // this lane's first channel in the group
+    const int rb = 16 * I + 4 * g;  // this lane's first row
+    auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+    auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+
+    // ---- loads, all issued before the first use ----
+    const uint32_t* q32 = static_cast<const uint32_t*>(io.q);
+    const uint32_t* k32 = static_cast<const uint32_t*>(io.k);
+    const uint32_t* a32 = static_cast<const uint32_t*>(io.alpha);
+    const uint32_t* b32 = static_cast<const uint32_t*>(io.b);
+    uint32_t rq[4], rk[4], rbv[4], ra[4];
 #pragma unroll
-    for (int u = 0; u < NX; ++u) {
-        const int x = tid + 256 * u, r = x / CW, i = x % CW;
-        const int t = t0 + r;
-        const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DK + c0 + i;
-        lq[u] = q[e];
-        lk[u] = k[e];
-        lb[u] = b[e];
-        la[u] = al[e];
+    for (int j = 0; j < 4; ++j) {
+        const int t = t0 + rb + j;
+        const size_t e = ((((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DK + c0 + ch0) / 2;
+        rq[j] = q32[e];
+        rk[j] = k32[e];
+        rbv[j] = b32[e];
+        ra[j] = a32[e];
     }
+    float lA[16], lP[16];
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
+    for (int u = 0; u < 16; ++u) {
         lA[u] = io.dAm[cbase * CH * CH + tid + 256 * u];
         lP[u] = io.dPm[cbase * CH * CH + tid + 256 * u];
     }
-    // this thread's rows p + 8 m of channel i for the elementwise phase: dQ_hat, dE_hat, dK_bar
-    const int i = tid % CW, p = tid / CW;
-    float gQv[8], gEv[8], gKv[8];
+    float2 gQ[4], gE[4], gK[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const size_t ce = (cbase * CH + p + 8 * m) * DK + c0 + i;
-        gQv[m] = io.dQh[ce];
-        gEv[m] = io.dEh[ce];
-        gKv[m] = io.dKb[ce];
+    for (int j = 0; j < 4; ++j) {
+        const size_t ce = (cbase * CH + rb + j) * DK + c0 + ch0;
+        gQ[j] = *reinterpret_cast<const float2*>(io.dQh + ce);
+        gE[j] = *reinterpret_cast<const float2*>(io.dEh + ce);
+        gK[j] = *reinterpret_cast<const float2*>(io.dKb + ce);
     }
-    const float dgam_i = io.dgam[cbase * DK + c0 + i];
+    const float2 dgam = *reinterpret_cast<const float2*>(io.dgam + cbase * DK + c0 + ch0);
+
+    // this lane's inputs; rows past the end read as zero and do not decay
+    float q[4][2], k[4][2], bb2[4][2], la[4][2], G[4][2];
 #pragma unroll
-    for (int u = 0; u < NX; ++u) {
-        const int x = tid + 256 * u, r = x / CW;
-        const bool ok = t0 + r < T;
-        qs[x] = ok ? lq[u] : 0;
-        ks[x] = ok ? lk[u] : 0;
-        bs[x] = ok ? lb[u] : 0;
-        G2[x] = ok ? __builtin_amdgcn_logf(f(la[u])) : 0.f;  // rows past the end do not decay
+    for (int j = 0; j < 4; ++j) {
+        const bool ok = t0 + rb + j < T;
+        q[j][0] = ok ? lo(rq[j]) : 0.f;
+        q[j][1] = ok ? hi(rq[j]) : 0.f;
+        k[j][0] = ok ? lo(rk[j]) : 0.f;
+        k[j][1] = ok ? hi(rk[j]) : 0.f;
+        bb2[j][0] = ok ? lo(rbv[j]) : 0.f;
+        bb2[j][1] = ok ? hi(rbv[j]) : 0.f;
+        la[j][0] = ok ? __builtin_amdgcn_logf(lo(ra[j])) : 0.f;
+        la[j][1] = ok ? __builtin_amdgcn_logf(hi(ra[j])) : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
+    for (int u = 0; u < 16; ++u) {
         dA[tid + 256 * u] = lA[u];
         dPs[tid + 256 * u] = lP[u];
     }
-    __syncthreads();
-    if (tid < CW) {
+    // ---- G: prefix within the sub-block, then the totals of the sub-blocks before it ----
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
         float acc = 0.f;
-        for (int r = 0; r < CH; ++r) {
-            acc += G2[r * CW + tid];
-            G2[r * CW + tid] = acc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc += la[j][c];
+            G[j][c] = acc;
         }
+        part[(4 * I + g) * CW + ch0 + c] = acc;
     }
     __syncthreads();
-    for (int x = tid; x < CH * CW; x += 256) {
-        const int r = x / CW, i = x % CW, I = r / 16;
-        const float g = G2[x];
-        const float kv = f(ks[x]);
-        Kp[x] = kv * __builtin_amdgcn_exp2f(G2[(16 * I + 15) * CW + i] - g);
-        const float down = __builtin_amdgcn_exp2f(g - G2[(16 * I) * CW + i]);
-        Ep[x] = f(bs[x]) * kv * down;
-        Qp[x] = f(qs[x]) * down;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float pre = 0.f;
+        for (int sb = 0; sb < 4 * I + g; ++sb) pre += part[sb * CW + ch0 + c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            G[j][c] += pre;
+            G2[(rb + j) * CW + ch0 + c] = G[j][c];
+        }
     }
     __syncthreads();
 
-    // Blocks off the diagonal on the matrix cores (fp32 16x16x4): wave w takes row block I = w
-    // and both 16-channel tiles. XA, XP of rows in I sum over blocks J < I, Y over blocks I2 > I;
-    // each block's product is scaled by its reference factor per (row, channel) and added. The
-    // 16 block rows are contracted in 4 passes, lane group g holding rows 4 g .. 4 g + 3.
-    {
-        const int I = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-        f4 xa[2], xp[2], yy[2];
+    // ---- rows pre-scaled against this block's ends: k to its last row, b*k and q to its first ----
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) xa[ct] = xp[ct] = yy[ct] = f4{0.f, 0.f, 0.f, 0.f};
-        for (int J = 0; J < I; ++J) {
-            f4 sa[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-            f4 sp[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    for (int c = 0; c < 2; ++c) {
+        const float Ge = G2[(16 * I + 15) * CW + ch0 + c], Gb = G2[(16 * I) * CW + ch0 + c];
 #pragma unroll
-            for (int ip = 0; ip < 4; ++ip) {
-                const int s = 16 * J + 4 * g + ip;
-                const float a = dA[(16 * I + l16) * CH + s], pp = dPs[(16 * I + l16) * CH + s];
+        for (int j = 0; j < 4; ++j) {
+            const int x = (rb + j) * CW + ch0 + c;
+            const float down = __builtin_amdgcn_exp2f(G[j][c] - Gb);
+            Xk[x] = k[j][c] * __builtin_amdgcn_exp2f(Ge - G[j][c]);
+            Xe[x] = bb2[j][c] * k[j][c] * down;
+            Xq[x] = q[j][c] * down;
+        }
+    }
+    __syncthreads();
+
+    // ---- between 16-row blocks: XA, XP over blocks J < I, Y over blocks I2 > I ----
+    f4 xa[2], xp[2], yy[2];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const float kp = Kp[s * CW + 16 * ct + l16];
-                    sa[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, kp, sa[ct], 0, 0, 0);
-                    sp[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp, kp, sp[ct], 0, 0, 0);
-                }
-            }
+    for (int c = 0; c < 2; ++c) xa[c] = xp[c] = yy[c] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int J = 0; J < I; ++J) {
+        f4 sa[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+        f4 sp[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const float ge = G2[(16 * J + 15) * CW + 16 * ct + l16];
+        for (int ip = 0; ip < 4; ++ip) {
+            const int s2 = 16 * J + 4 * g + ip;
+            const float av = dA[(16 * I + l16) * CH + s2], pv = dPs[(16 * I + l16) * CH + s2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float fJ = __builtin_amdgcn_exp2f(G2[(16 * I + 4 * g + j) * CW + 16 * ct + l16] - ge);
-                    xa[ct][j] = fmaf(fJ, sa[ct][j], xa[ct][j]);
-                    xp[ct][j] = fmaf(fJ, sp[ct][j], xp[ct][j]);
-                }
+            for (int c = 0; c < 2; ++c) {
+                const float kv = Xk[s2 * CW + ch0 + c];
+                sa[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, kv, sa[c], 0, 0, 0);
+                sp[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, kv, sp[c], 0, 0, 0);
             }
         }
-        for (int I2 = I + 1; I2 < 4; ++I2) {
-            f4 sy[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int ip = 0; ip < 4; ++ip) {
-                const int r2 = 16 * I2 + 4 * g + ip;
-                const float a = dA[r2 * CH + 16 * I + l16], pp = dPs[r2 * CH + 16 * I + l16];
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    sy[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ep[r2 * CW + 16 * ct + l16], sy[ct], 0, 0, 0);
-                    sy[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp, Qp[r2 * CW + 16 * ct + l16], sy[ct], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const float gb = G2[(16 * I2) * CW + 16 * ct + l16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float f = __builtin_amdgcn_exp2f(gb - G2[(16 * I + 4 * g + j) * CW + 16 * ct + l16]);
-                    yy[ct][j] = fmaf(f, sy[ct][j], yy[ct][j]);
-                }
-            }
-        }
-        __syncthreads();  // every read of Kp, Ep, Qp is done: they take the sums off the diagonal
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int c = 0; c < 2; ++c) {
+            const float Ge = G2[(16 * J + 15) * CW + ch0 + c];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int x = (16 * I + 4 * g + j) * CW + 16 * ct + l16;
-                Kp[x] = xa[ct][j];
-                Ep[x] = xp[ct][j];
-                Qp[x] = yy[ct][j];
+                const float f = __builtin_amdgcn_exp2f(G[j][c] - Ge);
+                xa[c][j] = fmaf(f, sa[c][j], xa[c][j]);
+                xp[c][j] = fmaf(f, sp[c][j], xp[c][j]);
             }
+        }
     }
-    __syncthreads();
+    for (int I2 = I + 1; I2 < 4; ++I2) {
+        f4 sy[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ip = 0; ip < 4; ++ip) {
+            const int r2 = 16 * I2 + 4 * g + ip;
+            const float av = dA[r2 * CH + 16 * I + l16], pv = dPs[r2 * CH + 16 * I + l16];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                sy[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Xe[r2 * CW + ch0 + c], sy[c], 0, 0, 0);
+                sy[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, Xq[r2 * CW + ch0 + c], sy[c], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float Gb = G2[(16 * I2) * CW + ch0 + c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yy[c][j] = fmaf(__builtin_amdgcn_exp2f(Gb - G[j][c]), sy[c][j], yy[c][j]);
+        }
+    }
+    __syncthreads();  // every read of the block-level rows is done
 
-    const float G63 = G2[(CH - 1) * CW + i];
-    float dG[8];
-    float kb_sum = 0.f;
-    // rows p, p + 8, ..., p + 56 (the row's block I changes every other step)
+    // ---- between 4-row sub-blocks inside the diagonal block: the same with sub-block ends ----
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int r = p + 8 * m, I = r / 16;
-        const float Gr = G2[r * CW + i];
-        const float kr = f(ks[r * CW + i]), qr = f(qs[r * CW + i]), br = f(bs[r * CW + i]);
-        // XA, XP: the earlier blocks' sums (above), then the diagonal block term by term
-        float XA = Kp[r * CW + i], XP = Ep[r * CW + i];
-        for (int s = 16 * I; s <= r; ++s) {
-            const float w = f(ks[s * CW + i]) * __builtin_amdgcn_exp2f(Gr - G2[s * CW + i]);
-            if (s < r) XA = fmaf(dA[r * CH + s], w, XA);
-            XP = fmaf(dPs[r * CH + s], w, XP);
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int x = (rb + j) * CW + ch0 + c;
+            const float down = __builtin_amdgcn_exp2f(G[j][c] - G[0][c]);
+            Xk[x] = k[j][c] * __builtin_amdgcn_exp2f(G[3][c] - G[j][c]);
+            Xe[x] = bb2[j][c] * k[j][c] * down;
+            Xq[x] = q[j][c] * down;
         }
-        // Y: the later blocks' sums (above), then the diagonal block term by term
-        float Y = Qp[r * CW + i];
-        for (int r2 = r; r2 < 16 * I + 16; ++r2) {
-            const float w = __builtin_amdgcn_exp2f(G2[r2 * CW + i] - Gr);
-            const float e2 = f(bs[r2 * CW + i]) * f(ks[r2 * CW + i]);
-            float term = dPs[r2 * CH + r] * f(qs[r2 * CW + i]);
-            if (r2 > r) term = fmaf(dA[r2 * CH + r], e2, term);
-            Y = fmaf(term, w, Y);
-        }
-        const float eG = __builtin_amdgcn_exp2f(Gr), eK = __builtin_amdgcn_exp2f(G63 - Gr);
-        const float gQ = gQv[m], gE = gEv[m], gK = gKv[m];
-        const float Et = br * kr;
-        const float dEt = fmaf(gE, eG, XA);
-        const float dqv = fmaf(gQ, eG, XP);
-        const float dkv = fmaf(gK, eK, Y) + br * dEt;
-        const float dbv = kr * dEt;
-        dG[m] = gQ * qr * eG + gE * Et * eG - gK * kr * eK + Et * XA + qr * XP - kr * Y;
-        kb_sum = fmaf(gK, kr * eK, kb_sum);
-        const int t = t0 + r;
-        if (t < T) {
-            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + c0 + i;
-            io.dq[e] = dqv;
-            io.dk[e] = dkv;
-            io.db[e] = dbv;
+    // (the rows read below belong to this wave's block: its own writes above come first)
+#pragma unroll
+    for (int V = 0; V < 3; ++V) {  // XA, XP of rows in sub-blocks g > V
+        const int s2 = 16 * I + 4 * V + g;
+        const float av = dA[(16 * I + l16) * CH + s2], pv = dPs[(16 * I + l16) * CH + s2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float kv = Xk[s2 * CW + ch0 + c];
+            const f4 z = f4{0.f, 0.f, 0.f, 0.f};
+            const f4 sa = __builtin_amdgcn_mfma_f32_16x16x4f32(av, kv, z, 0, 0, 0);
+            const f4 sp = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, kv, z, 0, 0, 0);
+            const float Ge = G2[(16 * I + 4 * V + 3) * CW + ch0 + c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float f = g > V ? __builtin_amdgcn_exp2f(G[j][c] - Ge) : 0.f;
+                xa[c][j] = fmaf(f, sa[j], xa[c][j]);
+                xp[c][j] = fmaf(f, sp[j], xp[c][j]);
+            }
         }
     }
-    red[tid] = kb_sum;
-    __syncthreads();  // every read of Kp, Ep, Qp is done
 #pragma unroll
-    for (int m = 0; m < 8; ++m) Kp[(p + 8 * m) * CW + i] = dG[m];
-    __syncthreads();
-    // dlog(alpha)_r = sum_{r2 >= r} dG_r2, the last row also carrying the gamma and K_bar terms;
-    // thread (i, p) sums rows 8 p .. 8 p + 7, then adds the sums of the segments below it.
-    // alpha_r = 2^(G_r - G_{r-1}).
-    float seg = 0.f;
+    for (int W = 1; W < 4; ++W) {  // Y of rows in sub-blocks g < W
+        const int r2 = 16 * I + 4 * W + g;
+        const float av = dA[r2 * CH + 16 * I + l16], pv = dPs[r2 * CH + 16 * I + l16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) seg += Kp[(8 * p + u) * CW + i];
-    float extra = dgam_i * __builtin_amdgcn_exp2f(G63);
+        for (int c = 0; c < 2; ++c) {
+            f4 sy = f4{0.f, 0.f, 0.f, 0.f};
+            sy = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Xe[r2 * CW + ch0 + c], sy, 0, 0, 0);
+            sy = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, Xq[r2 * CW + ch0 + c], sy, 0, 0, 0);
+            const float Gb = G2[(16 * I + 4 * W) * CW + ch0 + c];
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) extra += red[pp * CW + i];
-    __syncthreads();  // every read of red is done
-    red[p * CW + i] = seg;
-    __syncthreads();
-    float acc = extra;
-    for (int pp = 7; pp > p; --pp) acc += red[pp * CW + i];
+            for (int j = 0; j < 4; ++j) {
+                const float f = W > g ? __builtin_amdgcn_exp2f(Gb - G[j][c]) : 0.f;
+                yy[c][j] = fmaf(f, sy[j], yy[c][j]);
+            }
+        }
+    }
+
+    // ---- inside this lane's sub-block: pairs j' <= j term by term ----
+    float Asb[4][4], Psb[4][4];  // [row j][column j'] of the sub-block's dA and dP
 #pragma unroll
-    for (int u = 7; u >= 0; --u) {
-        const int r = 8 * p + u;
-        acc += Kp[r * CW + i];
-        const int t = t0 + r;
+    for (int j = 0; j < 4; ++j) {
+        const float4 x = *reinterpret_cast<const float4*>(&dA[(rb + j) * CH + rb]);
+        const float4 y = *reinterpret_cast<const float4*>(&dPs[(rb + j) * CH + rb]);
+        Asb[j][0] = x.x; Asb[j][1] = x.y; Asb[j][2] = x.z; Asb[j][3] = x.w;
+        Psb[j][0] = y.x; Psb[j][1] = y.y; Psb[j][2] = y.z; Psb[j][3] = y.w;
+    }
+    const float G63c[2] = {G2[(CH - 1) * CW + ch0], G2[(CH - 1) * CW + ch0 + 1]};
+    float dG[4][2], kbs[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float XA[4], XP[4], Y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            XA[j] = xa[c][j];
+            XP[j] = fmaf(Psb[j][j], k[j][c], xp[c][j]);
+            Y[j] = fmaf(Psb[j][j], q[j][c], yy[c][j]);
+        }
+#pragma unroll
+        for (int j = 1; j < 4; ++j)
+#pragma unroll
+            for (int jp = 0; jp < j; ++jp) {  // row j, earlier row jp: F = 2^(G_j - G_jp) <= 1
+                const float F = __builtin_amdgcn_exp2f(G[j][c] - G[jp][c]);
+                XA[j] = fmaf(Asb[j][jp] * F, k[jp][c], XA[j]);
+                XP[j] = fmaf(Psb[j][jp] * F, k[jp][c], XP[j]);
+                Y[jp] = fmaf(F, fmaf(Asb[j][jp], bb2[j][c] * k[j][c], Psb[j][jp] * q[j][c]), Y[jp]);
+            }
+        // ---- elementwise: the gradients of q, k, b and dL/dG of each row ----
+        kbs[c] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float gq = c ? gQ[j].y : gQ[j].x, ge = c ? gE[j].y : gE[j].x, gk = c ? gK[j].y : gK[j].x;
+            const float eG = __builtin_amdgcn_exp2f(G[j][c]), eK = __builtin_amdgcn_exp2f(G63c[c] - G[j][c]);
+            const float kr = k[j][c], qr = q[j][c], br = bb2[j][c], Et = br * kr;
+            const float dEt = fmaf(ge, eG, XA[j]);
+            dG[j][c] = gq * qr * eG + ge * Et * eG - gk * kr * eK + Et * XA[j] + qr * XP[j] - kr * Y[j];
+            kbs[c] = fmaf(gk, kr * eK, kbs[c]);
+            XA[j] = fmaf(gq, eG, XP[j]);                 // dq
+            XP[j] = fmaf(gk, eK, Y[j]) + br * dEt;       // dk
+            Y[j] = kr * dEt;                             // db
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // park the outputs of channel c in xa/xp/yy
+            xa[c][j] = XA[j];
+            xp[c][j] = XP[j];
+            yy[c][j] = Y[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = t0 + rb + j;
         if (t < T) {
-            const float a = __builtin_amdgcn_exp2f(G2[r * CW + i] - (r ? G2[(r - 1) * CW + i] : 0.f));
-            io.dalpha[(((size_t)bb * T + t) * H + hh) * DK + c0 + i] = acc / a;
+            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + c0 + ch0;
+            *reinterpret_cast<float2*>(io.dq + e) = make_float2(xa[0][j], xa[1][j]);
+            *reinterpret_cast<float2*>(io.dk + e) = make_float2(xp[0][j], xp[1][j]);
+            *reinterpret_cast<float2*>(io.db + e) = make_float2(yy[0][j], yy[1][j]);
+        }
+    }
+
+    // ---- dlog(alpha)_r = sum over rows r2 >= r of dG_r2; the last row also carries
+    // sum_r dK_bar K_bar and dgamma gamma. alpha_r = 2^(la_r). ----
+    __syncthreads();  // every read of part is done
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float kb = kbs[c];
+        kb += __shfl_xor(kb, 16);
+        kb += __shfl_xor(kb, 32);
+        part[(4 * I + g) * CW + ch0 + c] = dG[0][c] + dG[1][c] + dG[2][c] + dG[3][c];
+        if (g == 0) G2[I * CW + ch0 + c] = kb;  // (G2 is no longer needed: rows 0..3 take the sums)
+    }
+    __syncthreads();
+    float dal[4][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float acc = (c ? dgam.y : dgam.x) * __builtin_amdgcn_exp2f(G63c[c]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += G2[w * CW + ch0 + c];
+        for (int sb = 4 * I + g + 1; sb < 16; ++sb) acc += part[sb * CW + ch0 + c];
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            acc += dG[j][c];
+            dal[j][c] = acc / __builtin_amdgcn_exp2f(la[j][c]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = t0 + rb + j;
+        if (t < T) {
+            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + c0 + ch0;
+            *reinterpret_cast<float2*>(io.dalpha + e) = make_float2(dal[j][0], dal[j][1]);
         }
     }
 }
@@ -748,7 +865,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
     const ChainBwdIO cio{a.v, a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0,
                          a.B, a.T, a.H, a.DV, nch};
-    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3(BH * (a.DV / DVT)), dim3(64 * (DVT / 16)), 0, st, cio);
+    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3(BH * (a.DV / DVT)), dim3(bwd_chain_threads<DK>()), 0, st, cio);
     const ContractIO xio{a.dO, Dp, Dl, dDl, dDp, S_save, G_save, blobs, dQh, dEh, dKb, dPm, dAm, dgam,
                          a.B, a.T, a.H, a.DV, nch};
     hipLaunchKernelGGL((bwd_contract_kernel<DK>), dim3(BH * nch), dim3(256), 0, st, xio);
