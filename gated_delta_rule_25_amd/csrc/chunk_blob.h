@@ -60,11 +60,12 @@ __device__ __forceinline__ void dma_flat(const char* g, char* l, int bytes, int 
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-// All but the newest N (< 16) vector-memory operations done (vmcnt(N)).
+// All but the newest N (< 64) vector-memory operations done (vmcnt(N): low 4 bits in [3:0],
+// high 2 bits in [15:14]).
 template <int N>
 __device__ __forceinline__ void wait_vm_but() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
 }  // namespace chunk

@@ -76,9 +76,54 @@ struct ChainBwdIO {
     int B, T, H, DV, nch;
 };
 
-// Waves own 16 value columns each. The next (earlier) chunk's block is copied into the other LDS
-// buffer, and its dO, v, w rows loaded into registers, at the start of each step, so the copies
-// run while the current chunk is worked on; the wait at the next step's start finds them done.
+// The reverse chain contracts P, T, K_bar, Q_hat and E_hat over the other index than the forward
+// chain does, so once per chunk the block is transposed in LDS into row-major operands
+// (8x8 tiles: eight 4-element-unit reads, eight 16-byte writes per tile), after which every
+// matrix-core operand is two 8-byte reads:
+//   PT[m][s] = P[s][m], TT[m][s] = T[s][m], Kb[m][c] = K_bar^T[c][m], QT[c][r] = Q_hat[r][c],
+//   ET[c][r] = -E_hat[r][c].
+template <int DK>
+struct BwdChainSmem {
+    using BL = Blob<DK, true>;
+    static constexpr int RS = CH + 8;  // row stride (halves) of PT, TT, QT, ET: 36 dwords
+    static constexpr int KS = DK + 8;  // row stride of Kb
+    static constexpr int oPT = BL::bytes;
+    static constexpr int oTT = oPT + CH * RS * 2;
+    static constexpr int oKb = oTT + CH * RS * 2;
+    static constexpr int oQT = oKb + CH * KS * 2;
+    static constexpr int oET = oQT + DK * RS * 2;
+    static constexpr int oGam = oET + DK * RS * 2;  // float [DK]
+    // per wave: 64 rows x 16 columns of fp32 (row stride 20) to turn accumulator tiles into rows
+    static constexpr int SR = 20;
+    static constexpr int oStg = oGam + DK * 4;
+    static constexpr int bytes = oStg + (DK < 64 ? DK : 64) / 16 * CH * SR * 4;
+    static_assert(bytes <= 160 * 1024, "reverse chain LDS");
+};
+
+// Destination rows c0 + i (i = 0..7), elements r0 .. r0 + 7, from the 8x8 source tile at
+// (r0, c0); unit(r, c) returns the source's 4 elements (r, c .. c + 3).
+template <class Unit>
+__device__ __forceinline__ void tr_tile(Unit unit, _Float16* dst, int stride, int r0, int c0) {
+    h4 u[8][2];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+        u[a][0] = unit(r0 + a, c0);
+        u[a][1] = unit(r0 + a, c0 + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h8 o;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) o[a] = u[a][i >> 2][i & 3];
+        *reinterpret_cast<h8*>(dst + (c0 + i) * stride + r0) = o;
+    }
+}
+
+// Waves own 16 value columns each. The block of the next (earlier) chunk is copied into LDS while
+// the current one is worked on from its transposed copy, and the next chunk's dO, v, w rows are
+// loaded into registers at the start of each step. Rows go to and from memory 16 bytes per lane
+// through a per-wave LDS tile, which keeps a step at 52 vector-memory instructions per wave, few
+// enough that the next step's wait leaves this step's stores in flight.
 template <int DK>
 constexpr int bwd_chain_threads() {
     return ((DK < 64 ? DK : 64) / 16) * 64;
@@ -90,13 +135,27 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     using E = _Float16;
     using Frag = PR::Frag;
     using BL = Blob<DK, true>;
+    using SM = BwdChainSmem<DK>;
     constexpr int NKS = DK / 32, NMK = DK / 16;
     constexpr int DVT = DK < 64 ? DK : 64;
     constexpr int NW = DVT / 16;  // waves, 16 value columns each
+    constexpr int NTH = NW * 64;
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * BL::bytes];
+    __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
+    E* PT = reinterpret_cast<E*>(smem + SM::oPT);
+    E* TT = reinterpret_cast<E*>(smem + SM::oTT);
+    E* Kb = reinterpret_cast<E*>(smem + SM::oKb);
+    E* QT = reinterpret_cast<E*>(smem + SM::oQT);
+    E* ET = reinterpret_cast<E*>(smem + SM::oET);
+    float* gam = reinterpret_cast<float*>(smem + SM::oGam);
+    const E* sEn = reinterpret_cast<const E*>(smem + BL::oEn);
+    const E* sKbT = reinterpret_cast<const E*>(smem + BL::oKbT);
+    const E* sTm = reinterpret_cast<const E*>(smem + BL::oTm);
+    const E* sPm = reinterpret_cast<const E*>(smem + BL::oP);
+    const E* sQh = reinterpret_cast<const E*>(smem + BL::oQh);
+    const float* sgC = reinterpret_cast<const float*>(smem + BL::oGC);
 
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, DV = io.DV, nch = io.nch;
     const int vt = DV / DVT;
     const int bh = blockIdx.x / vt, tile = blockIdx.x % vt;
@@ -133,25 +192,57 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
         }
         return PR::make(t);
     };
+    // operand fragment of row `row` (k contiguous), k = 32 s + kap(g, .)
+    auto frag = [&](const E* row, int s) { return PR::lds_pair(row + 32 * s + 4 * g, row + 32 * s + 16 + 4 * g); };
 
-    // the rows one chunk needs from memory: dO as B operands (k = token row 32 s2 + kap(g, i),
-    // rows past T read as zero), v and w at rows 16 mt + 4 g + j
-    float xdO[16], xv[16], xw[16];
+    // Rows as lanes move them: lane (rr = lane / 4 + 16 q, cc = lane % 4), q = 0..3, holds
+    // columns 4 cc .. 4 cc + 3 of this wave's 16 at chunk row rr.
+    const int rr0 = lane >> 2, cc = lane & 3;
+    const int colw = tile * DVT + 16 * wv;  // this wave's first column
+    float* stg = reinterpret_cast<float*>(smem + SM::oStg) + wv * CH * SM::SR;
+    auto row_off = [&](int row) -> unsigned { return (((unsigned)row * H + hh) * DV + colw + 4 * cc) * 4u; };
+    // accumulator tiles (rows 16 mt + 4 g + j, column l16; mt < NT) into the staging tile
+    auto stage = [&](const f4* X, auto NTc) {
+        constexpr int NT = decltype(NTc)::value;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stg[(16 * mt + 4 * g + j) * SM::SR + l16] = X[mt][j];
+    };
+    auto staged = [&](int q) { return *reinterpret_cast<const float4*>(stg + (rr0 + 16 * q) * SM::SR + 4 * cc); };
+
+    // the next chunk's rows: dO (fp32), v and w (bf16), 16 bytes / 8 bytes per lane and row
+    u32x4 xdO[4];
+    uint32_t xv[4][2], xw[4][2];
     auto fetch = [&](int n) {
         const int t0 = n * CH;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xdO[8 * s2 + i] = bload_f32(rs_dO, elem(t0 + 32 * s2 + kap(g, i)) * 4u);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const unsigned e = elem(t0 + 16 * mt + 4 * g + j);
-                xv[4 * mt + j] = bload_bf16(rs_v, e * 2u);
-                xw[4 * mt + j] = bload_bf16(rs_w, e * 2u);
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int row = t0 + rr0 + 16 * q;
+            xdO[q] = __builtin_amdgcn_raw_buffer_load_b128(rs_dO, (int)row_off(row), 0, 0);
+            const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(row_off(row) / 2u), 0, 0);
+            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, (int)(row_off(row) / 2u), 0, 0);
+            xv[q][0] = v2[0];
+            xv[q][1] = v2[1];
+            xw[q][0] = w2[0];
+            xw[q][1] = w2[1];
+        }
     };
+    auto bf = [](uint32_t x, int h) { return __uint_as_float(h ? (x & 0xffff0000u) : (x << 16)); };
+    // G (rows 0 .. DK-1 of this wave's 16 columns) to [DK][DV] rows at dst, 64 rows at a time:
+    // one 16-byte store per lane and 16 rows
+    constexpr int NST = NMK < 4 ? NMK : 4;  // 16-row tiles per round
+    auto store_state = [&](float* dst) {
+#pragma unroll
+        for (int h2 = 0; h2 < NMK / NST; ++h2) {
+            stage(&G[NST * h2], std::integral_constant<int, NST>());
+#pragma unroll
+            for (int q = 0; q < NST; ++q)
+                *reinterpret_cast<float4*>(dst + (size_t)(64 * h2 + rr0 + 16 * q) * DV + colw + 4 * cc) = staged(q);
+        }
+    };
+    constexpr int kStepStores = NMK + 16;  // stores a step issues after its loads
+
     if (nch > 0) {
         dma_flat(blob_of(nch - 1), smem, BL::bytes, wv, NW, lane);
         fetch(nch - 1);
@@ -159,60 +250,80 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
 
     for (int idx = 0; idx < nch; ++idx) {
         const int n = nch - 1 - idx, t0 = n * CH;
-        wait_dma();     // this wave's part of block n and its rows of chunk n have arrived
-        lds_barrier();  // block n is whole; every read of the other buffer is done
-        if (n > 0) dma_flat(blob_of(n - 1), smem + ((idx + 1) & 1) * BL::bytes, BL::bytes, wv, NW, lane);
-        const char* buf = smem + (idx & 1) * BL::bytes;
-        const E* En = reinterpret_cast<const E*>(buf + BL::oEn);
-        const E* KbT = reinterpret_cast<const E*>(buf + BL::oKbT);
-        const E* Tm = reinterpret_cast<const E*>(buf + BL::oTm);
-        const E* Pm = reinterpret_cast<const E*>(buf + BL::oP);
-        const E* Qh = reinterpret_cast<const E*>(buf + BL::oQh);
-        const float* gC = reinterpret_cast<const float*>(buf + BL::oGC);
-
-        // this chunk's rows, then the loads for the next one (they complete while this one runs)
-        Frag dOf[2];
-        dOf[0] = PR::make(xdO);
-        dOf[1] = PR::make(xdO + 8);
-        float cv[16], cw[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            cv[u] = xv[u];
-            cw[u] = xw[u];
+        // block n and this wave's rows of chunk n have arrived (the previous step's stores,
+        // issued after them, may still be in flight)
+        if (idx == 0) {
+            wait_dma();
+        } else {
+            wait_vm_but<kStepStores>();
         }
+        lds_barrier();  // block n is whole; every read of the transposed copy is done
+        // ---- transpose block n ----
+        {
+            auto uQ = [&](int r, int c) { return *reinterpret_cast<const h4*>(sQh + BL::en(r, c)); };
+            auto uE = [&](int r, int c) { return *reinterpret_cast<const h4*>(sEn + BL::en(r, c)); };
+            auto uK = [&](int r, int c) { return *reinterpret_cast<const h4*>(sKbT + BL::kbt(r, c)); };
+            auto uP = [&](int r, int c) { return *reinterpret_cast<const h4*>(sPm + BL::tp(r, c)); };
+            auto uT = [&](int r, int c) { return *reinterpret_cast<const h4*>(sTm + BL::tp(r, c)); };
+            constexpr int NQ = 8 * (DK / 8);  // 8x8 tiles of Q_hat (and of E_hat, K_bar^T)
+            for (int x = tid; x < NQ; x += NTH) {
+                const int r0 = 8 * (x % 8), c0 = 8 * (x / 8);
+                tr_tile(uQ, QT, SM::RS, r0, c0);
+                tr_tile(uE, ET, SM::RS, r0, c0);
+                tr_tile(uK, Kb, SM::KS, 8 * (x % (DK / 8)), 8 * (x / (DK / 8)));
+            }
+            // P and T: the stored tiles (rows 0..31 hold columns 0..31, rows 32..63 all 64)
+            for (int x = tid; x < 48; x += NTH) {
+                const int r0 = x < 16 ? 8 * (x / 4) : 32 + 8 * ((x - 16) / 8);
+                const int c0 = x < 16 ? 8 * (x % 4) : 8 * ((x - 16) % 8);
+                tr_tile(uP, PT, SM::RS, r0, c0);
+                tr_tile(uT, TT, SM::RS, r0, c0);
+            }
+            for (int x = tid; x < DK; x += NTH) gam[x] = sgC[x];
+        }
+        lds_barrier();  // the transposed copy is whole; the block buffer is free
+        if (n > 0) dma_flat(blob_of(n - 1), smem, BL::bytes, wv, NW, lane);
+
+        // this chunk's rows: dO into operand fragments (k = token row 32 s2 + kap(g, i)) through
+        // the staging tile; v, w kept for dv, dw; then the loads for the next chunk
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x4*>(stg + (rr0 + 16 * q) * SM::SR + 4 * cc) = xdO[q];
+        Frag dOf[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = stg[(32 * s2 + kap(g, i)) * SM::SR + l16];
+            dOf[s2] = PR::make(x);
+        }
+        float cv[4][4], cw[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cv[q][e] = bf(xv[q][e >> 1], e & 1);
+                cw[q][e] = bf(xw[q][e >> 1], e & 1);
+            }
         if (n > 0) fetch(n - 1);
 
         // G' of this chunk, for the contraction kernel
-        float* gs = io.G_save + ((size_t)bh * nch + n) * DK * DV;
-#pragma unroll
-        for (int mk = 0; mk < NMK; ++mk)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gs[(size_t)(16 * mk + 4 * g + j) * DV + col] = G[mk][j];
+        store_state(io.G_save + ((size_t)bh * nch + n) * DK * DV);
 
         Frag Gf[NKS];
 #pragma unroll
         for (int s = 0; s < NKS; ++s) Gf[s] = stack(G[2 * s], G[2 * s + 1]);
 
-        // dDelta = P^T dO + K_bar G'   (P^T[r][s] = P[s][r] is zero for s < r)
+        // dDelta = P^T dO + K_bar G'   (P^T[m][s] = P[s][m] is zero for s < m)
         f4 dL[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             dL[mt] = f4{0.f, 0.f, 0.f, 0.f};
             const int m = 16 * mt + l16;
 #pragma unroll
-            for (int s2 = mt / 2; s2 < 2; ++s2) {
-                float a[8];
+            for (int s2 = mt / 2; s2 < 2; ++s2) PR::mma(dL[mt], frag(PT + m * SM::RS, s2), dOf[s2]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a[i] = tp_get<BL>(Pm, 32 * s2 + kap(g, i), m);
-                PR::mma(dL[mt], PR::make(a), dOf[s2]);
-            }
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                float a[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) a[i] = (float)KbT[BL::kbt(32 * s + kap(g, i), m)];
-                PR::mma(dL[mt], PR::make(a), Gf[s]);
-            }
+            for (int s = 0; s < NKS; ++s) PR::mma(dL[mt], frag(Kb + m * SM::KS, s), Gf[s]);
         }
         // dD' = T^T dDelta
         const Frag dLf[2] = {stack(dL[0], dL[1]), stack(dL[2], dL[3])};
@@ -222,51 +333,39 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             dP[mt] = f4{0.f, 0.f, 0.f, 0.f};
             const int m = 16 * mt + l16;
 #pragma unroll
-            for (int s2 = mt / 2; s2 < 2; ++s2) {
-                float a[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) a[i] = tp_get<BL>(Tm, 32 * s2 + kap(g, i), m);
-                PR::mma(dP[mt], PR::make(a), dLf[s2]);
-            }
+            for (int s2 = mt / 2; s2 < 2; ++s2) PR::mma(dP[mt], frag(TT + m * SM::RS, s2), dLf[s2]);
         }
         // rows of dDelta and dD'; dv = w dD', dw = v dD' (rows past T are dropped)
+        stage(dL, std::integral_constant<int, 4>());
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int q = 0; q < 4; ++q) {
+            const float4 x = staged(q);
+            store4(rs_dDl, row_off(t0 + rr0 + 16 * q), x.x, x.y, x.z, x.w);
+        }
+        stage(dP, std::integral_constant<int, 4>());
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const unsigned e = elem(t0 + 16 * mt + 4 * g + j);
-                bstore_f32(rs_dDl, e * 4u, dL[mt][j]);
-                bstore_f32(rs_dDp, e * 4u, dP[mt][j]);
-                bstore_f32(rs_dv, e * 4u, cw[4 * mt + j] * dP[mt][j]);
-                bstore_f32(rs_dw, e * 4u, cv[4 * mt + j] * dP[mt][j]);
-            }
-        // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (En = -E_hat)
+        for (int q = 0; q < 4; ++q) {
+            const float4 x = staged(q);
+            const unsigned off = row_off(t0 + rr0 + 16 * q);
+            store4(rs_dDp, off, x.x, x.y, x.z, x.w);
+            store4(rs_dv, off, cw[q][0] * x.x, cw[q][1] * x.y, cw[q][2] * x.z, cw[q][3] * x.w);
+            store4(rs_dw, off, cv[q][0] * x.x, cv[q][1] * x.y, cv[q][2] * x.z, cv[q][3] * x.w);
+        }
+        // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (ET holds -E_hat^T)
         const Frag dPf[2] = {stack(dP[0], dP[1]), stack(dP[2], dP[3])};
 #pragma unroll
         for (int mk = 0; mk < NMK; ++mk) {
             const int m = 16 * mk + l16;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) G[mk][j] *= gC[16 * mk + 4 * g + j];
+            for (int j = 0; j < 4; ++j) G[mk][j] *= gam[16 * mk + 4 * g + j];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                float aq[8], ae[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = 32 * s2 + kap(g, i);
-                    aq[i] = (float)Qh[BL::en(r, m)];
-                    ae[i] = (float)En[BL::en(r, m)];
-                }
-                PR::mma(G[mk], PR::make(aq), dOf[s2]);
-                PR::mma(G[mk], PR::make(ae), dPf[s2]);
+                PR::mma(G[mk], frag(QT + m * SM::RS, s2), dOf[s2]);
+                PR::mma(G[mk], frag(ET + m * SM::RS, s2), dPf[s2]);
             }
         }
     }
-    if (io.dS0) {
-#pragma unroll
-        for (int mk = 0; mk < NMK; ++mk)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) io.dS0[((size_t)bh * DK + 16 * mk + 4 * g + j) * DV + col] = G[mk][j];
-    }
+    if (io.dS0) store_state(io.dS0 + (size_t)bh * DK * DV);
 }
 
 // ------------------------------------------------------------------------------------------
