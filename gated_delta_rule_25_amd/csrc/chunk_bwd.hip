@@ -392,7 +392,7 @@ struct ContractIO {
 // fragment layout of the matrix cores: fp16 operands (as in the chains), fp32 accumulation. The
 // value channels are staged in slices of 64 columns; wave w owns output rows 16 w .. 16 w + 15.
 template <int DK>
-__global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO io) {
+__global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO io) {
     using PR = Prec<true>;
     using E = _Float16;
     using Frag = PR::Frag;
@@ -421,32 +421,63 @@ __global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO i
     const float* S = io.S_save + cbase * DK * DV;
     const float* Gp = io.G_save + cbase * DK * DV;
 
+    // T of the block (4-element units of the stored triangle), loaded now, used at the end
+    constexpr int TU = BL::TPE / 4;  // units
+    constexpr int TPT = (TU + 255) / 256;
+    const uint2* Tunits = reinterpret_cast<const uint2*>(io.blobs + cbase * BL::bytes + BL::oTm);
+    uint2 tun[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) tun[u] = (tid + 256 * u < TU) ? Tunits[tid + 256 * u] : make_uint2(0u, 0u);
+
     f4 aQ[NMK], aE[NMK], aK[NMK], aP[4], aT[4];
 #pragma unroll
     for (int c = 0; c < NMK; ++c) aQ[c] = aE[c] = aK[c] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) aP[c] = aT[c] = f4{0.f, 0.f, 0.f, 0.f};
 
+    // staging: thread x = tid + 256 u takes row x / (JS / 4), columns 4 (x % (JS / 4)) .. + 3;
+    // every load of a group is issued before the first conversion. dgamma_i = sum_j S_ij G'_ij
+    // is summed in fp32 from the same loads (per thread, then over the row's JS / 4 lanes).
+    constexpr int NSU = DK * JS / 4 / 256, NRU = CH * JS / 4 / 256;
+    static_assert(NSU * 256 == DK * JS / 4 && NRU * 256 == CH * JS / 4, "staging split");
+    float dg[NSU];
+#pragma unroll
+    for (int u = 0; u < NSU; ++u) dg[u] = 0.f;
     for (int js = 0; js < DV; js += JS) {
         __syncthreads();
-        for (int x = tid; x < DK * JS / 4; x += 256) {
-            const int i = x / (JS / 4), j = 4 * (x % (JS / 4));
-            const float4 a = *reinterpret_cast<const float4*>(S + (size_t)i * DV + js + j);
-            const float4 b = *reinterpret_cast<const float4*>(Gp + (size_t)i * DV + js + j);
+        float4 la[NSU], lb[NSU];
+#pragma unroll
+        for (int u = 0; u < NSU; ++u) {
+            const int x = tid + 256 * u, i = x / (JS / 4), j = 4 * (x % (JS / 4));
+            la[u] = *reinterpret_cast<const float4*>(S + (size_t)i * DV + js + j);
+            lb[u] = *reinterpret_cast<const float4*>(Gp + (size_t)i * DV + js + j);
+        }
+        const float* srcs[5] = {io.dO, io.dDp, io.Dl, io.dDl, io.Dp};
+        E* dsts[5] = {dOs, dDps, Dls, dDls, Dps};
+        float4 lr[5][NRU];
+#pragma unroll
+        for (int u = 0; u < NRU; ++u) {
+            const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
+            const int t = t0 + r;
+            const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DV + js + j;
+#pragma unroll
+            for (int m = 0; m < 5; ++m) lr[m][u] = *reinterpret_cast<const float4*>(srcs[m] + e);
+        }
+#pragma unroll
+        for (int u = 0; u < NSU; ++u) {
+            const int x = tid + 256 * u, i = x / (JS / 4), j = 4 * (x % (JS / 4));
+            const float4 a = la[u], b = lb[u];
             *reinterpret_cast<h4*>(Ss + i * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
             *reinterpret_cast<h4*>(Gs + i * JP + j) = h4{(E)b.x, (E)b.y, (E)b.z, (E)b.w};
+            dg[u] += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
         }
-        for (int x = tid; x < CH * JS / 4; x += 256) {
-            const int r = x / (JS / 4), j = 4 * (x % (JS / 4));
-            const int t = t0 + r;
-            const bool ok = t < T;
-            const size_t e = (((size_t)bb * T + (ok ? t : 0)) * H + hh) * DV + js + j;
-            const float* srcs[5] = {io.dO, io.dDp, io.Dl, io.dDl, io.Dp};
-            E* dsts[5] = {dOs, dDps, Dls, dDls, Dps};
+#pragma unroll
+        for (int u = 0; u < NRU; ++u) {
+            const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
+            const bool ok = t0 + r < T;
 #pragma unroll
             for (int m = 0; m < 5; ++m) {
-                float4 a = *reinterpret_cast<const float4*>(srcs[m] + e);
-                if (!ok) a = make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 a = ok ? lr[m][u] : make_float4(0.f, 0.f, 0.f, 0.f);
                 *reinterpret_cast<h4*>(dsts[m] + r * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
             }
         }
@@ -490,15 +521,14 @@ __global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO i
             const int r = 16 * wv + 4 * g + j, cc = 16 * c + l16;
             io.dPm[(cbase * CH + r) * CH + cc] = (c <= wv && cc <= r) ? aP[c][j] : 0.f;
         }
-    // dgamma_i = sum_j S_ij G'_ij in fp32
-    if (tid < DK) {
-        float ag = 0.f;
-        for (int j = 0; j < DV; j += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(S + (size_t)tid * DV + j);
-            const float4 b = *reinterpret_cast<const float4*>(Gp + (size_t)tid * DV + j);
-            ag += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-        }
-        io.dgam[cbase * DK + tid] = ag;
+    // dgamma: the row's JS / 4 lanes are consecutive; the first of them stores
+#pragma unroll
+    for (int u = 0; u < NSU; ++u) {
+        float v = dg[u];
+#pragma unroll
+        for (int m = 1; m < JS / 4; m <<= 1) v += __shfl_xor(v, m);
+        const int x = tid + 256 * u;
+        if (x % (JS / 4) == 0) io.dgam[cbase * DK + x / (JS / 4)] = v;
     }
 
     // dA = -T^T dT T^T (strictly lower), dT = dDelta D'^T on the lower triangle
@@ -506,11 +536,21 @@ __global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO i
     float* Tf = reinterpret_cast<float*>(lds);  // [64][TP] T
     float* Tg = Tf + CH * TP;                    // [64][TP] dT
     float* Xm = Tg + CH * TP;                    // [64][TP] T^T dT
-    const _Float16* Tb = reinterpret_cast<const _Float16*>(io.blobs + cbase * BL::bytes + BL::oTm);
-    for (int x = tid; x < CH * CH; x += 256) {
-        const int r = x / CH, c = x % CH;
-        Tf[r * TP + c] = tp_get<BL>(Tb, r, c);
+    // T into fp32 rows: unit u of the stored triangle is row r, columns 4 cu .. 4 cu + 3 (the
+    // inverse of the unit swizzle); rows 0..31 store columns 0..31, the rest are zero
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+        const int x = tid + 256 * u;
+        if (x < TU) {
+            const int r = x < 256 ? x / 8 : 32 + (x - 256) / 16;
+            const int up = x < 256 ? x % 8 : (x - 256) % 16;  // unit position in the stored row
+            const int cu = up ^ (x < 256 ? ((r >> 1) & 7) : (r & 15));
+            const h4 h = __builtin_bit_cast(h4, tun[u]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tf[r * TP + 4 * cu + e] = (float)h[e];
+        }
     }
+    for (int x = tid; x < 32 * 32; x += 256) Tf[(x / 32) * TP + 32 + x % 32] = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
