@@ -51,6 +51,12 @@ __device__ __forceinline__ float bload_bf16(__amdgpu_buffer_rsrc_t r, unsigned o
 __device__ __forceinline__ void bstore_f32(__amdgpu_buffer_rsrc_t r, unsigned off, float x) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
 }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// four values as fp16 (8 bytes) at byte offset off
+__device__ __forceinline__ void store_h4(__amdgpu_buffer_rsrc_t r, unsigned off, float4 x) {
+    const h4 h = {(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, (int)off, 0, 0);
+}
 
 // Element (r, c) of T or P in an fp16 operand block: blocks the block does not store (columns
 // 32..63 of rows 0..31) are zero.
@@ -68,8 +74,8 @@ struct ChainBwdIO {
     const float* dS_T;  // [B, H, DK, DV] or null
     const char* blobs;  // [b*h][nch] operand blocks
     float* G_save;      // [b*h][nch][DK][DV]: dL/dS at the end of each chunk
-    float* dDl;         // [B, T, H, DV]: dL/dDelta
-    float* dDp;         // [B, T, H, DV]: dL/dD'
+    uint16_t* dDl;      // [B, T, H, DV] fp16: dL/dDelta
+    uint16_t* dDp;      // [B, T, H, DV] fp16: dL/dD'
     float* dv;
     float* dw;
     float* dS0;  // [B, H, DK, DV] or null
@@ -166,8 +172,8 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     const long seq = (long)bb * T * H;
     const unsigned seq_f32 = (unsigned)T * H * DV * 4u;
     const auto rs_dO = make_rsrc(io.dO + seq * DV, seq_f32);
-    const auto rs_dDl = make_rsrc(io.dDl + seq * DV, seq_f32);
-    const auto rs_dDp = make_rsrc(io.dDp + seq * DV, seq_f32);
+    const auto rs_dDl = make_rsrc(io.dDl + seq * DV, seq_f32 / 2u);
+    const auto rs_dDp = make_rsrc(io.dDp + seq * DV, seq_f32 / 2u);
     const auto rs_dv = make_rsrc(io.dv + seq * DV, seq_f32);
     const auto rs_dw = make_rsrc(io.dw + seq * DV, seq_f32);
     const auto rs_v = make_rsrc(static_cast<const uint16_t*>(io.v) + seq * DV, (unsigned)T * H * DV * 2u);
@@ -340,14 +346,14 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float4 x = staged(q);
-            store4(rs_dDl, row_off(t0 + rr0 + 16 * q), x.x, x.y, x.z, x.w);
+            store_h4(rs_dDl, row_off(t0 + rr0 + 16 * q) / 2u, x);
         }
         stage(dP, std::integral_constant<int, 4>());
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float4 x = staged(q);
             const unsigned off = row_off(t0 + rr0 + 16 * q);
-            store4(rs_dDp, off, x.x, x.y, x.z, x.w);
+            store_h4(rs_dDp, off / 2u, x);
             store4(rs_dv, off, cw[q][0] * x.x, cw[q][1] * x.y, cw[q][2] * x.z, cw[q][3] * x.w);
             store4(rs_dw, off, cv[q][0] * x.x, cv[q][1] * x.y, cv[q][2] * x.z, cv[q][3] * x.w);
         }
@@ -372,10 +378,10 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
 // 3. contractions over the value channels, per (b, h, chunk)
 struct ContractIO {
     const float* dO;   // [B, T, H, DV]
-    const float* Dp;   // D'
-    const float* Dl;   // Delta
-    const float* dDl;  // dDelta
-    const float* dDp;  // dD'
+    const uint16_t* Dp;   // D' (fp16 bits, [B, T, H, DV])
+    const uint16_t* Dl;   // Delta
+    const uint16_t* dDl;  // dDelta
+    const uint16_t* dDp;  // dD'
     const float* S_save;
     const float* G_save;
     const char* blobs;
@@ -438,8 +444,9 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
     // staging: thread x = tid + 256 u takes row x / (JS / 4), columns 4 (x % (JS / 4)) .. + 3;
     // every load of a group is issued before the first conversion. dgamma_i = sum_j S_ij G'_ij
     // is summed in fp32 from the same loads (per thread, then over the row's JS / 4 lanes).
-    constexpr int NSU = DK * JS / 4 / 256, NRU = CH * JS / 4 / 256;
-    static_assert(NSU * 256 == DK * JS / 4 && NRU * 256 == CH * JS / 4, "staging split");
+    constexpr int NSU = DK * JS / 4 / 256, NRU = CH * JS / 4 / 256, NRH = CH * JS / 8 / 256;
+    static_assert(NSU * 256 == DK * JS / 4 && NRU * 256 == CH * JS / 4 && NRH * 256 == CH * JS / 8,
+                  "staging split");
     float dg[NSU];
 #pragma unroll
     for (int u = 0; u < NSU; ++u) dg[u] = 0.f;
@@ -452,16 +459,25 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
             la[u] = *reinterpret_cast<const float4*>(S + (size_t)i * DV + js + j);
             lb[u] = *reinterpret_cast<const float4*>(Gp + (size_t)i * DV + js + j);
         }
-        const float* srcs[5] = {io.dO, io.dDp, io.Dl, io.dDl, io.Dp};
-        E* dsts[5] = {dOs, dDps, Dls, dDls, Dps};
-        float4 lr[5][NRU];
+        // dO (fp32) 4 columns per thread; D', Delta, dDelta, dD' (fp16 rows) 8 columns per thread
+        const uint16_t* srch[4] = {io.dDp, io.Dl, io.dDl, io.Dp};
+        E* dsth[4] = {dDps, Dls, dDls, Dps};
+        float4 lr[NRU];
+        uint4 lh[4][NRH];
 #pragma unroll
         for (int u = 0; u < NRU; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
             const int t = t0 + r;
             const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DV + js + j;
+            lr[u] = *reinterpret_cast<const float4*>(io.dO + e);
+        }
 #pragma unroll
-            for (int m = 0; m < 5; ++m) lr[m][u] = *reinterpret_cast<const float4*>(srcs[m] + e);
+        for (int u = 0; u < NRH; ++u) {
+            const int x = tid + 256 * u, r = x / (JS / 8), j = 8 * (x % (JS / 8));
+            const int t = t0 + r;
+            const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DV + js + j;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) lh[m][u] = *reinterpret_cast<const uint4*>(srch[m] + e);
         }
 #pragma unroll
         for (int u = 0; u < NSU; ++u) {
@@ -474,11 +490,18 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 #pragma unroll
         for (int u = 0; u < NRU; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
+            const float4 a = t0 + r < T ? lr[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<h4*>(dOs + r * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
+        }
+#pragma unroll
+        for (int u = 0; u < NRH; ++u) {
+            const int x = tid + 256 * u, r = x / (JS / 8), j = 8 * (x % (JS / 8));
             const bool ok = t0 + r < T;
 #pragma unroll
-            for (int m = 0; m < 5; ++m) {
-                const float4 a = ok ? lr[m][u] : make_float4(0.f, 0.f, 0.f, 0.f);
-                *reinterpret_cast<h4*>(dsts[m] + r * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
+            for (int m = 0; m < 4; ++m) {
+                const uint4 a = ok ? lh[m][u] : make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint2*>(dsth[m] + r * JP + j) = make_uint2(a.x, a.y);
+                *reinterpret_cast<uint2*>(dsth[m] + r * JP + j + 4) = make_uint2(a.z, a.w);
             }
         }
         __syncthreads();
@@ -635,7 +658,11 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 
     const int tid = threadIdx.x, I = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, nch = io.nch;
-    const int cg = blockIdx.x % NG, item = blockIdx.x / NG;
+    // the NG channel groups of one chunk sit 8 workgroups apart, on one XCD (workgroups go round
+    // the 8 XCDs in order), so their reads of the chunk's dA and dP share that XCD's L2
+    const int w8 = blockIdx.x % 8, rest = blockIdx.x / 8;
+    const int cg = rest % NG, item = (rest / NG) * 8 + w8;
+    if (item >= io.B * io.H * io.nch) return;
     const int bh = item / nch, n = item % nch;
     const int hh = bh % H, bb = bh / H;
     const int t0 = n * CH, c0 = cg * CW;
@@ -950,7 +977,7 @@ BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
     o += st;
     L.G_save = o;
     o += st;
-    const size_t rows = up((size_t)B * T * H * DV * 4);
+    const size_t rows = up((size_t)B * T * H * DV * 2);  // fp16 rows
     L.Dp = o;
     o += rows;
     L.Dl = o;
@@ -985,10 +1012,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     char* blobs = ws + L.blobs;
     float* S_save = reinterpret_cast<float*>(ws + L.S_save);
     float* G_save = reinterpret_cast<float*>(ws + L.G_save);
-    float* Dp = reinterpret_cast<float*>(ws + L.Dp);
-    float* Dl = reinterpret_cast<float*>(ws + L.Dl);
-    float* dDl = reinterpret_cast<float*>(ws + L.dDl);
-    float* dDp = reinterpret_cast<float*>(ws + L.dDp);
+    uint16_t* Dp = reinterpret_cast<uint16_t*>(ws + L.Dp);
+    uint16_t* Dl = reinterpret_cast<uint16_t*>(ws + L.Dl);
+    uint16_t* dDl = reinterpret_cast<uint16_t*>(ws + L.dDl);
+    uint16_t* dDp = reinterpret_cast<uint16_t*>(ws + L.dDp);
     float* dQh = reinterpret_cast<float*>(ws + L.dQh);
     float* dEh = reinterpret_cast<float*>(ws + L.dEh);
     float* dKb = reinterpret_cast<float*>(ws + L.dKb);
@@ -1010,7 +1037,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_contract_kernel<DK>), dim3(BH * nch), dim3(256), 0, st, xio);
     const KeyIO kio{a.q, a.k, a.alpha, a.b, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
                     a.B, a.T, a.H, nch};
-    hipLaunchKernelGGL((bwd_key_kernel<DK>), dim3(BH * nch * (DK / 32)), dim3(256), 0, st, kio);
+    hipLaunchKernelGGL((bwd_key_kernel<DK>), dim3((BH * nch + 7) / 8 * 8 * (DK / 32)), dim3(256), 0, st, kio);
     return hipGetLastError();
 }
 

@@ -616,11 +616,11 @@ struct ChainIO {
     int out_last;  // only the last segment writes S_out
     int phi_tiles = 0;  // transition tiles (over d_k) after the value tiles, state-only pass
     // Saves for the backward pass (state-only pass, sequential): the state at the start of every
-    // chunk, S_save + ((bh * save_nch) + chunk) * DK * DV; D' and Delta rows, [B, T, H, DV] fp32
+    // chunk, S_save + ((bh * save_nch) + chunk) * DK * DV; D' and Delta rows, [B, T, H, DV] fp16
     float* S_save = nullptr;
     int save_nch = 0;
-    float* Dp_save = nullptr;
-    float* Dl_save = nullptr;
+    uint16_t* Dp_save = nullptr;  // fp16 bits
+    uint16_t* Dl_save = nullptr;
     // Packed batch (chain_kernel's VAR): workgroup (b·h, tile) runs every chunk of sequence b, the
     // blocks [h][chunk of the batch] with `ring` slots per head; B counts the sequences.
     VarTab var{};
@@ -763,10 +763,11 @@ chain_kernel(const ChainIO io) {
     };
 
     // accumulator tiles of 64 token rows x 16 columns ([mt][j]: row 16 mt + 4 g + j, column l16 of
-    // tile c) to [B, T, H, DV] rows of this sequence; rows past the end are dropped
+    // tile c) to [B, T, H, DV] fp16 rows of this sequence (their reader takes them as fp16 matrix-core
+    // operands); rows past the end are dropped
     int t0_cur = 0;
-    auto save_rows = [&](float* dst, const f4 (&X)[NT][4]) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + tbase * H * DV, (unsigned)Tq * H * DV * 4u);
+    auto save_rows = [&](uint16_t* dst, const f4 (&X)[NT][4]) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + tbase * H * DV, (unsigned)Tq * H * DV * 2u);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -774,8 +775,8 @@ chain_kernel(const ChainIO io) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const unsigned row = (unsigned)(t0_cur + 16 * mt + 4 * g + j);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(X[c][mt][j]), rs,
-                                                          (int)(((row * H + hh) * DV + col0 + 16 * c + l16) * 4u), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)X[c][mt][j]), rs,
+                                                          (int)(((row * H + hh) * DV + col0 + 16 * c + l16) * 2u), 0, 0);
                 }
     };
 
