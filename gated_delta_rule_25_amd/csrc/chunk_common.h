@@ -29,7 +29,8 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 // Logistic sigmoid, and log2 of it in a form that neither overflows nor cancels:
 // log2 sigma(x) = min(x, 0) log2(e) - log2(1 + 2^(-|x| log2(e))). sigma(-inf) = 0, sigma(+inf) = 1.
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + ex2(-1.4426950408889634f * x)); }
+// (the reciprocal is the hardware one, within 1 ulp: a gate needs no correctly rounded division)
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + ex2(-1.4426950408889634f * x)); }
 __device__ __forceinline__ float lg2_sigmoid(float x) {
     return fminf(x, 0.f) * 1.4426950408889634f - lg2(1.f + ex2(-1.4426950408889634f * fabsf(x)));
 }

@@ -29,7 +29,7 @@ namespace gdn2 {
 namespace {
 
 __device__ __forceinline__ float sigmoid(float x) {
-    return 1.f / (1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));  // rcp within 1 ulp
 }
 
 template <int DK, bool BF16, bool ASCALAR, bool BSCALAR, int PRO>
