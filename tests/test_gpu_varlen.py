@@ -148,3 +148,17 @@ def test_varlen_full_size_sampled():
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
     order = np.argsort(lengths)
     _check(ins, o, S, TOL16, seqs=[int(order[0]), int(order[len(order) // 2]), int(order[-1])])
+
+
+def test_varlen_many_sequences_span_several_table_tiles():
+    # 700 sequences (the sequence table is built in tiles of 256 bounds, carrying the running
+    # maximum and chunk count from tile to tile), lengths 0..70 with many empty ones
+    rng = np.random.default_rng(97)
+    lengths = [int(x) for x in rng.integers(0, 71, 700)]
+    lengths[255] = lengths[256] = lengths[511] = 0
+    lengths[257] = 129
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=1, d_k=32, d_v=32)
+    banner(f"varlen, {len(lengths)} sequences, {sum(lengths)} rows, H1 d32")
+    ins = make_packed_inputs(wl, lengths)
+    o, S = _run(ins)
+    _check(ins, o, S, TOL16)
