@@ -64,6 +64,13 @@ bool sizes_of(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, Sizes* s)
            (s->scalar = s->tok, true) && s->qk < (1ull << 62) && s->vw < (1ull << 62);
 }
 
+// The chunked kernels launch one workgroup per (b, h, chunk) (the backward's key kernel four per
+// chunk at d = 128); their grids, in threads, must stay below 2^31.
+bool chunk_grids_ok(int32_t B, int32_t T, int32_t H, int32_t dk) {
+    const long long nch = ((long long)T + 63) / 64;
+    return (long long)B * H * (nch + 1) * (dk / 32) * 256 < (1ll << 31);
+}
+
 // Shared validation for prefill (T >= 0 tokens) and decode (T == 1, S0 == S_out == S).
 gdn2_status validate(const void* q, const void* k, const void* v, const void* alpha,
                      const void* b, const void* w, const float* S0, const float* o,
@@ -147,6 +154,7 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
     gdn2_status st = validate(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
                               gate_flags, false);
     if (st != GDN2_OK) return st;
+    if (!chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
     const bool bf16 = in_dtype == GDN2_BF16;
     const bool split = workspace && workspace_bytes > 0 && gdn2::split_supported(T, H, d_k, d_v, bf16);
     if (split) {
@@ -206,8 +214,10 @@ gdn2_status gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
     const bool bf16 = in_dtype == GDN2_BF16;
     if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
-    // one workgroup per (chunk bound, head) in prep: the grid must stay below 2^31
-    if (gdn2::varlen_chunk_bound(N, T_total) * H >= (1l << 31)) return GDN2_ERR_SHAPE;
+    // one workgroup per (chunk bound, head) in prep and per (sequence, head, value tile) in the
+    // chain: both grids (in threads) must stay below 2^31
+    if (gdn2::varlen_chunk_bound(N, T_total) * H * 256 >= (1l << 31)) return GDN2_ERR_SHAPE;
+    if (((long)N * H + 7) / 8 * 8 * (d_v / (d_k < 64 ? d_k : 64)) * 512 >= (1l << 31)) return GDN2_ERR_SHAPE;
     Sizes sz, states;
     if (!sizes_of(1, T_total, H, d_k, d_v, &sz) || !sizes_of(N, 1, H, d_k, d_v, &states)) return GDN2_ERR_SHAPE;
     if (workspace_bytes < gdn2::varlen_workspace_bytes(N, T_total, H, d_k, d_v, bf16)) return GDN2_ERR_WORKSPACE;
@@ -292,7 +302,7 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const vo
     if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
     if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN2_ERR_UNSUPPORTED;
     Sizes sz;
-    if (!sizes_of(B, T, H, d_k, d_v, &sz)) return GDN2_ERR_SHAPE;
+    if (!sizes_of(B, T, H, d_k, d_v, &sz) || !chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
     if (!gdn2::bwd_supported(T, H, d_k, d_v, true, gate_flags)) return GDN2_ERR_UNSUPPORTED;
     if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !dO || !dq || !dk || !dv || !dalpha || !db || !dw))
         return GDN2_ERR_NULL;

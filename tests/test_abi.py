@@ -175,3 +175,12 @@ def test_varlen_rejects_bad_arguments(lib):
     q[7] = q[1]
     assert call(ptrs=q) == 5                           # o overlaps k
     assert call(ws=P(0x200000000 * 7)) == 5            # workspace over S0
+
+
+def test_chunked_calls_reject_grids_beyond_31_bits(lib):
+    # B*H*chunks workgroups of 256 threads (four per chunk in the backward's key pass at d = 128)
+    # past 2^31 threads: refused on the host. Pointers 1 TiB apart so nothing overlaps.
+    far = [P((1 << 40) * (i + 1)) for i in range(16)]
+    B, T, H = 32, 64 * 1024, 64
+    assert lib.gdn2_chunk_fwd(*far[:9], B, T, H, 128, 128, 0, 0, None, 0, None) == 2
+    assert lib.gdn2_chunk_bwd(*far[:16], B, T, H, 128, 128, 0, 0, P((1 << 40) * 20), 1 << 45, None) == 2
