@@ -212,10 +212,12 @@ def chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) 
 
 
 def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=None, stream=None):
-    """Gradients of sum <dO, o> + <dS_T, S_T> for the prefill (bf16 inputs, general gates).
+    """Gradients of sum <dO, o> + <dS_T, S_T> for the prefill (bf16 inputs).
 
     Returns a dict of float32 tensors: dq, dk, dalpha, db [B, T, H, d_k], dv, dw [B, T, H, d_v] and
-    dS0 [B, H, d_k, d_v]. `out` may supply any of them; the workspace is allocated here unless given.
+    dS0 [B, H, d_k, d_v]. Scalar gates (alpha [B, T, H]; beta passed as b [B, T, H] with w None)
+    give dalpha [B, T, H], and db [B, T, H] = dL/dbeta with no dw. `out` may supply any of them;
+    the workspace is allocated here unless given.
     """
     lib = load()
     flags = _check_inputs(q, k, v, alpha, b, w, 4)
@@ -226,10 +228,13 @@ def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=No
             raise TypeError(f"{name} must be a contiguous float32 GPU tensor")
     out = dict(out or {})
     f32 = dict(device=q.device, dtype=torch.float32)
-    for name in ("dq", "dk", "dalpha", "db"):
+    for name in ("dq", "dk"):
         out.setdefault(name, torch.empty(B, T, H, dk, **f32))
-    for name in ("dv", "dw"):
-        out.setdefault(name, torch.empty(B, T, H, dv, **f32))
+    out.setdefault("dalpha", torch.empty(B, T, H, **f32) if flags & ALPHA_SCALAR else torch.empty(B, T, H, dk, **f32))
+    out.setdefault("db", torch.empty(B, T, H, **f32) if flags & BETA_SCALAR else torch.empty(B, T, H, dk, **f32))
+    out.setdefault("dv", torch.empty(B, T, H, dv, **f32))
+    if not flags & BETA_SCALAR:
+        out.setdefault("dw", torch.empty(B, T, H, dv, **f32))
     out.setdefault("dS0", torch.empty(B, H, dk, dv, **f32))
     dt = _dtype_code(q)
     need = int(lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
@@ -238,7 +243,7 @@ def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
                             _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                            _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dS0"]),
+                            _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out.get("dw")), _ptr(out["dS0"]),
                             B, T, H, dk, dv, dt, flags, _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_bwd", st)

@@ -961,6 +961,34 @@ __global__ void __launch_bounds__(256) copy_or_zero(float* dst, const float* src
     if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// Scalar gates through the general backward: each scalar is repeated over the channels of its
+// row (bf16, exactly), and the gradient of the scalar is the sum of its copies' gradients.
+__global__ void __launch_bounds__(256) repeat_bf16(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                   long rows, int D) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;  // one 8-element group of a row
+    const int per = D / 8;
+    if (i >= rows * per) return;
+    const uint32_t x = in[i / per];
+    const uint32_t p = x | (x << 16);
+    *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(p, p, p, p);
+}
+
+// out[r] = sum over the Da entries of row r of a (plus the Db entries of row r of b, if given);
+// one wavefront per row
+__global__ void __launch_bounds__(256) row_sums(const float* __restrict__ a, int Da, const float* __restrict__ b,
+                                                int Db, float* __restrict__ out, long rows) {
+    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;  // whole wavefront
+    float acc = 0.f;
+    for (int c = lane; c < Da; c += 64) acc += a[r * Da + c];
+    if (b)
+        for (int c = lane; c < Db; c += 64) acc += b[r * Db + c];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (lane == 0) out[r] = acc;
+}
+
 struct BwdLayout {
     size_t blobs, S_save, G_save, Dp, Dl, dDl, dDp, dQh, dEh, dKb, dPm, dAm, dgam, total;
 };
@@ -1043,14 +1071,44 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Extra workspace for scalar gates: the repeated gates (bf16) and the per-channel gradients (fp32).
+struct ScalarLayout {
+    size_t alpha, b, w, dalpha, db, dw, total;
+};
+
+ScalarLayout scalar_layout(size_t base, int B, int T, int H, int DK, int DV, uint32_t flags) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t rows = (size_t)B * T * H;
+    const bool as = (flags & 1u) != 0, bs = (flags & 2u) != 0;
+    ScalarLayout L{};
+    size_t o = base;
+    L.alpha = o;
+    o += as ? up(rows * DK * 2) : 0;
+    L.b = o;
+    o += bs ? up(rows * DK * 2) : 0;
+    L.w = o;
+    o += bs ? up(rows * DV * 2) : 0;
+    L.dalpha = o;
+    o += as ? up(rows * DK * 4) : 0;
+    L.db = o;
+    o += bs ? up(rows * DK * 4) : 0;
+    L.dw = o;
+    o += bs ? up(rows * DV * 4) : 0;
+    L.total = o;
+    return L;
+}
+
 bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags) {
-    if (!bf16 || flags != 0u || DK != DV) return false;
+    if (!bf16 || (flags & ~3u) != 0u || DK != DV) return false;
     if (DK != 32 && DK != 64 && DK != 128) return false;
     // one sequence's rows, the last chunk's rows past T included, addressed with 32-bit offsets
     return ((long long)T + CH) * H * DV * 4 < (1ll << 32);
 }
 
-size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV) { return bwd_layout(B, T, H, DK, DV).total; }
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags) {
+    const size_t base = bwd_layout(B, T, H, DK, DV).total;
+    return (flags & 3u) ? scalar_layout(base, B, T, H, DK, DV, flags).total : base;
+}
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     if (!bwd_supported(a.T, a.H, a.DK, a.DV, a.bf16, a.flags)) return hipErrorNotSupported;
@@ -1060,12 +1118,45 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(copy_or_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dS0, a.dS_T, n);
         return hipGetLastError();
     }
-    if (!a.workspace || a.workspace_bytes < bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV)) return hipErrorInvalidValue;
-    switch (a.DK) {
-        case 32: return launch_bwd_t<32>(a, s);
-        case 64: return launch_bwd_t<64>(a, s);
-        default: return launch_bwd_t<128>(a, s);
+    if (!a.workspace || a.workspace_bytes < bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags))
+        return hipErrorInvalidValue;
+    BwdArgs g = a;  // the general-gate call
+    const bool as = (a.flags & 1u) != 0, bs = (a.flags & 2u) != 0;
+    if (as || bs) {
+        const ScalarLayout L = scalar_layout(bwd_layout(a.B, a.T, a.H, a.DK, a.DV).total, a.B, a.T, a.H, a.DK, a.DV,
+                                             a.flags);
+        char* ws = static_cast<char*>(a.workspace);
+        const long rows = (long)a.B * a.T * a.H;
+        auto repeat = [&](const void* in, size_t off, int D) {
+            const long n = rows * (D / 8);
+            hipLaunchKernelGGL(repeat_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                               static_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(ws + off), rows, D);
+            return static_cast<const void*>(ws + off);
+        };
+        if (as) {
+            g.alpha = repeat(a.alpha, L.alpha, a.DK);
+            g.dalpha = reinterpret_cast<float*>(ws + L.dalpha);
+        }
+        if (bs) {
+            g.b = repeat(a.b, L.b, a.DK);
+            g.w = repeat(a.b, L.w, a.DV);
+            g.db = reinterpret_cast<float*>(ws + L.db);
+            g.dw = reinterpret_cast<float*>(ws + L.dw);
+        }
+        g.flags = 0u;
     }
+    hipError_t e;
+    switch (a.DK) {
+        case 32: e = launch_bwd_t<32>(g, s); break;
+        case 64: e = launch_bwd_t<64>(g, s); break;
+        default: e = launch_bwd_t<128>(g, s); break;
+    }
+    if (e != hipSuccess || !(as || bs)) return e;
+    const long rows = (long)a.B * a.T * a.H;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (as) hipLaunchKernelGGL(row_sums, grid, dim3(256), 0, s, g.dalpha, a.DK, nullptr, 0, a.dalpha, rows);
+    if (bs) hipLaunchKernelGGL(row_sums, grid, dim3(256), 0, s, g.db, a.DK, g.dw, a.DV, a.db, rows);
+    return hipGetLastError();
 }
 
 }  // namespace gdn2

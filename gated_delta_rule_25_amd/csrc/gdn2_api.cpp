@@ -289,7 +289,7 @@ size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
     if (!gdn2::bwd_supported(T, H, d_k, d_v, in_dtype == GDN2_BF16, gate_flags)) return 0;
     Sizes sz;
     if (!sizes_of(B, T, H, d_k, d_v, &sz)) return 0;
-    return gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v);
+    return gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v, gate_flags);
 }
 
 gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,
@@ -298,28 +298,33 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const vo
                            float* db, float* dw, float* dS0, int32_t B, int32_t T, int32_t H,
                            int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    if (in_dtype != GDN2_BF16 || gate_flags != 0u) return GDN2_ERR_UNSUPPORTED;
+    if (in_dtype != GDN2_BF16 || (gate_flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR)) != 0u)
+        return GDN2_ERR_UNSUPPORTED;
+    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
+    if (bs && (w || dw)) return GDN2_ERR_UNSUPPORTED;  // w is implied by beta; dbeta goes to db
     if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
     if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN2_ERR_UNSUPPORTED;
     Sizes sz;
     if (!sizes_of(B, T, H, d_k, d_v, &sz) || !chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
     if (!gdn2::bwd_supported(T, H, d_k, d_v, true, gate_flags)) return GDN2_ERR_UNSUPPORTED;
-    if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !dO || !dq || !dk || !dv || !dalpha || !db || !dw))
+    if (T > 0 && (!q || !k || !v || !alpha || !b || (!bs && !w) || !dO || !dq || !dk || !dv || !dalpha || !db ||
+                  (!bs && !dw)))
         return GDN2_ERR_NULL;
     const void* ptrs[] = {q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
     size_t need = 0;
     if (T > 0) {
-        need = gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v);
+        need = gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v, gate_flags);
         if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
     }
+    const uint64_t na = as ? sz.scalar : sz.qk, nb = bs ? sz.scalar : sz.qk;  // alpha, b elements
     const Range ins[] = {range_of(q, sz.qk * 2), range_of(k, sz.qk * 2), range_of(v, sz.vw * 2),
-                         range_of(alpha, sz.qk * 2), range_of(b, sz.qk * 2), range_of(w, sz.vw * 2),
+                         range_of(alpha, na * 2), range_of(b, nb * 2), range_of(w, sz.vw * 2),
                          range_of(S0, sz.state * 4), range_of(dO, sz.vw * 4), range_of(dS_T, sz.state * 4)};
-    const Range outs[] = {range_of(dq, sz.qk * 4), range_of(dk, sz.qk * 4), range_of(dalpha, sz.qk * 4),
-                          range_of(db, sz.qk * 4), range_of(dv, sz.vw * 4), range_of(dw, sz.vw * 4),
+    const Range outs[] = {range_of(dq, sz.qk * 4), range_of(dk, sz.qk * 4), range_of(dalpha, na * 4),
+                          range_of(db, nb * 4), range_of(dv, sz.vw * 4), range_of(dw, sz.vw * 4),
                           range_of(dS0, sz.state * 4), range_of(T > 0 ? workspace : nullptr, need)};
     const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
     for (int i = 0; i < nout; ++i) {

@@ -73,6 +73,6 @@ struct BwdArgs {
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags);
-size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags);
 
 }  // namespace gdn2

@@ -207,14 +207,21 @@ gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const 
  *            dS_T [B, H, d_k, d_v] float32 (NULL = zeros)
  *   outputs  dq, dk, dalpha, db [B, T, H, d_k] float32; dv, dw [B, T, H, d_v] float32;
  *            dS0 [B, H, d_k, d_v] float32 (NULL = not stored). Every output is overwritten.
+ *   scalar gates (gate_flags GDN2_ALPHA_SCALAR, GDN2_BETA_SCALAR, the forms of gdn2_chunk_fwd):
+ *            alpha [B, T, H] and dalpha [B, T, H] = dL/dalpha; beta passed as b [B, T, H] with
+ *            w == NULL, and db [B, T, H] = dL/dbeta (the gradients through b and w summed), dw
+ *            == NULL. A scalar gate is the general gate with the scalar in every channel, so its
+ *            gradient is the sum of the per-channel gradients; the call computes it that way.
  *
- * Supported: bf16 inputs, general gates (gate_flags == 0), d_k == d_v in {32, 64, 128}, and one
- * sequence's rows below 4 GiB ((T + 64)*H*d_v*4 < 2^32 bytes); anything else returns
- * GDN2_ERR_UNSUPPORTED. Arithmetic as in the forward: fp16 matrix-core operands with fp32
+ * Supported: bf16 inputs, the general and scalar gate forms (no prologue flags), d_k == d_v in
+ * {32, 64, 128}, and one sequence's rows below 4 GiB ((T + 64)*H*d_v*4 < 2^32 bytes); anything
+ * else returns GDN2_ERR_UNSUPPORTED. Arithmetic as in the forward: fp16 matrix-core operands with fp32
  * accumulation for the state chains, fp32 for the per-chunk gradient work.
  * The workspace (required when T > 0, 256-byte aligned, at least
- * gdn2_chunk_bwd_workspace_bytes) holds the operand blocks, the state and its gradient at every
- * chunk boundary and the per-chunk intermediate products; its contents are scratch. No output may
+ * gdn2_chunk_bwd_workspace_bytes for the same gate_flags) holds the operand blocks, the state and
+ * its gradient at every chunk boundary and the per-chunk intermediate products (and, for scalar
+ * gates, the gates repeated over the channels and their per-channel gradients); its contents are
+ * scratch. No output may
  * overlap an input, another output or the workspace (GDN2_ERR_ALIAS). Other errors, ownership
  * and stream semantics as for gdn2_chunk_fwd.
  */

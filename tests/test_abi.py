@@ -184,3 +184,20 @@ def test_chunked_calls_reject_grids_beyond_31_bits(lib):
     B, T, H = 32, 64 * 1024, 64
     assert lib.gdn2_chunk_fwd(*far[:9], B, T, H, 128, 128, 0, 0, None, 0, None) == 2
     assert lib.gdn2_chunk_bwd(*far[:16], B, T, H, 128, 128, 0, 0, P((1 << 40) * 20), 1 << 45, None) == 2
+
+
+def test_bwd_gate_forms_on_the_host(lib):
+    # scalar beta implies w: passing w or dw with GDN2_BETA_SCALAR is refused; prologue flags are
+    # not taken by the backward; the workspace query grows for scalar gates (repeated gates and
+    # their per-channel gradients)
+    far = [P((1 << 40) * (i + 1)) for i in range(16)]
+    ws = P((1 << 40) * 20)
+    f = lib.gdn2_chunk_bwd
+    q = lib.gdn2_chunk_bwd_workspace_bytes
+    B, T, H = 1, 64, 2
+    assert f(*far[:16], B, T, H, 64, 64, 0, 2, ws, 1 << 30, None) == 3           # w given
+    p = list(far[:16])
+    p[5] = None
+    assert f(*p, B, T, H, 64, 64, 0, 2, ws, 1 << 30, None) == 3                  # dw given
+    assert f(*far[:16], B, T, H, 64, 64, 0, 4, ws, 1 << 30, None) == 3           # prologue flag
+    assert q(B, T, H, 64, 64, 0, 3) > q(B, T, H, 64, 64, 0, 1) > q(B, T, H, 64, 64, 0, 0) > 0

@@ -77,6 +77,30 @@ def test_bwd_without_final_state_cotangent():
     _check("no_dS_T", scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=2), final_state=False)
 
 
+@pytest.mark.parametrize("gates", ["gdn", "kda"])
+def test_bwd_scalar_gates(gates):
+    """Scalar gates: the oracle differentiates the general form with the scalars repeated over the
+    channels; the gradient of a scalar is the sum of its copies' gradients (for beta, through b and
+    through w)."""
+    wl = scaled(WORKLOADS[f"{gates}_scalar"], B=2, T=150, H=2)
+    banner(f"bwd scalar gates {gates} {wl}")
+    ins = make_inputs(wl)
+    cot = make_cotangents(wl)
+    dk, dv = wl.d_k, wl.d_v
+    a, b, w = oracle.broadcast_gates(ins["alpha"], ins["b"], ins["w"], dk, dv,
+                                     alpha_scalar=ins["alpha_scalar"], beta_scalar=ins["beta_scalar"])
+    ref = oracle.backward(ins["q"], ins["k"], ins["v"], a, b, w, ins["S0"], cot["dO"], cot["dS_T"])
+    got = _gpu(ins, cot)
+    exp = dict(dq=ref["dq"], dk=ref["dk"], dv=ref["dv"], dS0=ref["dS0"],
+               dalpha=np.asarray(ref["dalpha"]).sum(-1) if ins["alpha_scalar"] else ref["dalpha"],
+               db=np.asarray(ref["db"]).sum(-1) + np.asarray(ref["dw"]).sum(-1))
+    assert "dw" not in got
+    assert tuple(got["db"].shape) == (wl.B, wl.T, wl.H)
+    errs = {n: normwise_err(got[n], exp[n]) for n in exp}
+    print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= TOLB for e in errs.values()), errs
+
+
 def test_bwd_stages_match_oracle():
     """The chunk-start states the forward chain saves and the state gradients at chunk ends the
     reverse chain saves, read back from the workspace, equal the oracle's."""
