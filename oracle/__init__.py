@@ -209,3 +209,30 @@ def prologue(q, k, alpha, b, w, *, l2norm: bool, gate_logits: bool):
         alpha, b = sig(alpha), sig(b)
         w = None if w is None else sig(w)
     return q, k, alpha, b, w
+
+
+def prologue_backward(q, k, alpha, b, w, grads: dict, *, l2norm: bool, gate_logits: bool) -> dict:
+    """Gradients with respect to the raw inputs of prologue(), given the gradients `grads` (dq,
+    dk, dalpha, db and, when w is given, dw) with respect to its outputs; float64 (parity
+    pinned by finite differences of prologue() itself). For x_n = x / max(|x|, 1e-12):
+    dx = (dx_n - (dx_n . x_n) x_n) / |x| when |x| > 1e-12, else dx_n / 1e-12. For a = sigma(x):
+    dx = da * a (1 - a). Returns a dict with the same keys.
+    """
+    q, k, alpha, b = (_f64(x) for x in (q, k, alpha, b))
+    w = _f64(w)
+    out = {n: _f64(v) for n, v in grads.items()}
+    if l2norm:
+        for name, x in (("dq", q), ("dk", k)):
+            nrm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            big = nrm > 1e-12
+            xn = x / np.maximum(nrm, 1e-12)
+            g = out[name]
+            proj = g - np.sum(g * xn, axis=-1, keepdims=True) * xn
+            out[name] = np.where(big, proj / np.maximum(nrm, 1e-12), g / 1e-12)
+    if gate_logits:
+        sig = lambda x: 1.0 / (1.0 + np.exp(-x))
+        for name, x in (("dalpha", alpha), ("db", b), ("dw", w)):
+            if x is not None and name in out:
+                s = sig(x)
+                out[name] = out[name] * s * (1.0 - s)
+    return out

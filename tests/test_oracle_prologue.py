@@ -43,3 +43,41 @@ def test_prologue_off_is_the_identity():
     out = oracle.prologue(*xs, l2norm=False, gate_logits=False)
     for x, y in zip(xs, out):
         np.testing.assert_array_equal(x, y)
+
+
+def test_prologue_backward_matches_finite_differences():
+    # L = sum(G_out * prologue(x)) for fixed random G_out: its gradient from prologue_backward
+    # against central differences of prologue() itself, for every raw input
+    rng = np.random.default_rng(33)
+    shp, shpv = (1, 3, 2, 5), (1, 3, 2, 4)
+    raw = dict(q=_raw(rng, shp), k=_raw(rng, shp), alpha=rng.standard_normal(shp) + 2.0,
+               b=rng.standard_normal(shp), w=rng.standard_normal(shpv))
+    gout = dict(dq=rng.standard_normal(shp), dk=rng.standard_normal(shp), dalpha=rng.standard_normal(shp),
+                db=rng.standard_normal(shp), dw=rng.standard_normal(shpv))
+    names = ("q", "k", "alpha", "b", "w")
+
+    def loss(x):
+        outs = oracle.prologue(x["q"], x["k"], x["alpha"], x["b"], x["w"], l2norm=True, gate_logits=True)
+        return sum(float(np.sum(gout["d" + n] * o)) for n, o in zip(names, outs))
+
+    got = oracle.prologue_backward(raw["q"], raw["k"], raw["alpha"], raw["b"], raw["w"], gout,
+                                   l2norm=True, gate_logits=True)
+    h = 1e-6
+    for n in names:
+        fd = np.zeros_like(raw[n])
+        for idx in np.ndindex(raw[n].shape):
+            xp = {m: v.copy() for m, v in raw.items()}
+            xm = {m: v.copy() for m, v in raw.items()}
+            xp[n][idx] += h
+            xm[n][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        np.testing.assert_allclose(got["d" + n], fd, rtol=1e-6, atol=1e-8)
+
+
+def test_prologue_backward_off_is_the_identity():
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((1, 2, 1, 4))
+    g = {n: rng.standard_normal((1, 2, 1, 4)) for n in ("dq", "dk", "dalpha", "db", "dw")}
+    out = oracle.prologue_backward(x, x, x, x, x, g, l2norm=False, gate_logits=False)
+    for n in g:
+        assert np.array_equal(out[n], g[n])
