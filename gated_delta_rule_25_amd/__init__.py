@@ -211,16 +211,18 @@ def chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) 
                                                      BF16 if dtype == torch.bfloat16 else F32, flags))
 
 
-def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=None, stream=None):
+def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=None, l2norm=False,
+              gate_logits=False, stream=None):
     """Gradients of sum <dO, o> + <dS_T, S_T> for the prefill (bf16 inputs).
 
     Returns a dict of float32 tensors: dq, dk, dalpha, db [B, T, H, d_k], dv, dw [B, T, H, d_v] and
     dS0 [B, H, d_k, d_v]. Scalar gates (alpha [B, T, H]; beta passed as b [B, T, H] with w None)
-    give dalpha [B, T, H], and db [B, T, H] = dL/dbeta with no dw. `out` may supply any of them;
-    the workspace is allocated here unless given.
+    give dalpha [B, T, H], and db [B, T, H] = dL/dbeta with no dw. With l2norm / gate_logits the
+    inputs are the raw ones the forward takes with the same flags, and the gradients are with
+    respect to them. `out` may supply any of them; the workspace is allocated here unless given.
     """
     lib = load()
-    flags = _check_inputs(q, k, v, alpha, b, w, 4)
+    flags = _check_inputs(q, k, v, alpha, b, w, 4) | _prologue_flags(l2norm, gate_logits)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     for name, x in (("S0", S0), ("dO", dO), ("dS_T", dS_T)):

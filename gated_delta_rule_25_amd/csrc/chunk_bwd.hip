@@ -135,7 +135,9 @@ constexpr int bwd_chain_threads() {
     return ((DK < 64 ? DK : 64) / 16) * 64;
 }
 
-template <int DK>
+// WSIG: w holds pre-activations (the prologue's gate logits): the gate is sigma(w), and dw is
+// taken with respect to the pre-activation.
+template <int DK, bool WSIG = false>
 __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(const ChainBwdIO io) {
     using PR = Prec<true>;
     using E = _Float16;
@@ -303,13 +305,18 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             for (int i = 0; i < 8; ++i) x[i] = stg[(32 * s2 + kap(g, i)) * SM::SR + l16];
             dOf[s2] = PR::make(x);
         }
-        float cv[4][4], cw[4][4];
+        float cv[4][4], cw[4][4], cs[4][4];  // v, the gate w, and the factor dw takes
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 cv[q][e] = bf(xv[q][e >> 1], e & 1);
                 cw[q][e] = bf(xw[q][e >> 1], e & 1);
+                cs[q][e] = 1.f;
+                if constexpr (WSIG) {
+                    cw[q][e] = sigmoidf_(cw[q][e]);
+                    cs[q][e] = cw[q][e] * (1.f - cw[q][e]);
+                }
             }
         if (n > 0) fetch(n - 1);
 
@@ -355,7 +362,8 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             const unsigned off = row_off(t0 + rr0 + 16 * q);
             store_h4(rs_dDp, off / 2u, x);
             store4(rs_dv, off, cw[q][0] * x.x, cw[q][1] * x.y, cw[q][2] * x.z, cw[q][3] * x.w);
-            store4(rs_dw, off, cv[q][0] * x.x, cv[q][1] * x.y, cv[q][2] * x.z, cv[q][3] * x.w);
+            store4(rs_dw, off, cs[q][0] * cv[q][0] * x.x, cs[q][1] * cv[q][1] * x.y, cs[q][2] * cv[q][2] * x.z,
+                   cs[q][3] * cv[q][3] * x.w);
         }
         // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (ET holds -E_hat^T)
         const Frag dPf[2] = {stack(dP[0], dP[1]), stack(dP[2], dP[3])};
@@ -627,6 +635,7 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 // 4. key side, per (b, h, chunk)
 struct KeyIO {
     const void *q, *k, *alpha, *b;  // bf16 [B, T, H, DK]
+    const float *rnq, *rnk;         // 1 / max(|q|, 1e-12), 1 / max(|k|, 1e-12) per row (L2 norm)
     const float *dQh, *dEh, *dKb, *dPm, *dAm, *dgam;
     float *dq, *dk, *dalpha, *db;  // [B, T, H, DK]
     int B, T, H, nch;
@@ -645,8 +654,13 @@ struct KeyIO {
 // Wave w takes row block I = w; lane (g, l16) owns rows 16 I + 4 g + j (j = 0..3, sub-block
 // 4 I + g) and channels 2 l16 + c (c = 0, 1) of the group, which is the matrix cores' output
 // layout when column l16 of tile c stands for channel 2 l16 + c.
-template <int DK>
+// PRO (prologue, as prep_kernel's): bit 0, q and k are normalised here (io.rnq, io.rnk) and dq, dk
+// are left with respect to the normalised vectors (a later pass takes them through the norm);
+// bit 1, alpha and b are pre-activations: log2 alpha = log2 sigma(x), b = sigma(x), and dalpha, db
+// are taken with respect to the pre-activations.
+template <int DK, int PRO = 0>
 __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
+    constexpr bool L2N = (PRO & 1) != 0, GL = (PRO & 2) != 0;
     constexpr int CW = 32;       // key channels per workgroup
     constexpr int NG = DK / CW;  // channel groups
     static_assert(DK % CW == 0, "channel groups");
@@ -703,19 +717,31 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     }
     const float2 dgam = *reinterpret_cast<const float2*>(io.dgam + cbase * DK + c0 + ch0);
 
+    float nq[4] = {1.f, 1.f, 1.f, 1.f}, nk[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (L2N) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + rb + j;
+            const size_t row = ((size_t)bb * T + (t < T ? t : 0)) * H + hh;
+            nq[j] = io.rnq[row];
+            nk[j] = io.rnk[row];
+        }
+    }
     // this lane's inputs; rows past the end read as zero and do not decay
     float q[4][2], k[4][2], bb2[4][2], la[4][2], G[4][2];
+    auto lg2a = [](float x) { return GL ? lg2_sigmoid(x) : __builtin_amdgcn_logf(x); };
+    auto gate = [](float x) { return GL ? sigmoidf_(x) : x; };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const bool ok = t0 + rb + j < T;
-        q[j][0] = ok ? lo(rq[j]) : 0.f;
-        q[j][1] = ok ? hi(rq[j]) : 0.f;
-        k[j][0] = ok ? lo(rk[j]) : 0.f;
-        k[j][1] = ok ? hi(rk[j]) : 0.f;
-        bb2[j][0] = ok ? lo(rbv[j]) : 0.f;
-        bb2[j][1] = ok ? hi(rbv[j]) : 0.f;
-        la[j][0] = ok ? __builtin_amdgcn_logf(lo(ra[j])) : 0.f;
-        la[j][1] = ok ? __builtin_amdgcn_logf(hi(ra[j])) : 0.f;
+        q[j][0] = ok ? lo(rq[j]) * nq[j] : 0.f;
+        q[j][1] = ok ? hi(rq[j]) * nq[j] : 0.f;
+        k[j][0] = ok ? lo(rk[j]) * nk[j] : 0.f;
+        k[j][1] = ok ? hi(rk[j]) * nk[j] : 0.f;
+        bb2[j][0] = ok ? gate(lo(rbv[j])) : 0.f;
+        bb2[j][1] = ok ? gate(hi(rbv[j])) : 0.f;
+        la[j][0] = ok ? lg2a(lo(ra[j])) : 0.f;
+        la[j][1] = ok ? lg2a(hi(ra[j])) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -902,6 +928,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
             XA[j] = fmaf(gq, eG, XP[j]);                 // dq
             XP[j] = fmaf(gk, eK, Y[j]) + br * dEt;       // dk
             Y[j] = kr * dEt;                             // db
+            if constexpr (GL) Y[j] *= br * (1.f - br);   // with respect to the pre-activation
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {  // park the outputs of channel c in xa/xp/yy
@@ -943,7 +970,9 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
         for (int j = 3; j >= 0; --j) {
             acc += dG[j][c];
-            dal[j][c] = acc / __builtin_amdgcn_exp2f(la[j][c]);
+            // acc = dL/d ln(alpha); d ln sigma(x)/dx = 1 - sigma(x)
+            const float a = __builtin_amdgcn_exp2f(la[j][c]);
+            dal[j][c] = GL ? acc * (1.f - a) : acc / a;
         }
     }
 #pragma unroll
@@ -989,6 +1018,42 @@ __global__ void __launch_bounds__(256) row_sums(const float* __restrict__ a, int
     if (lane == 0) out[r] = acc;
 }
 
+// 1 / max(|x|, 1e-12) of each row of D bf16 values; one wavefront per row
+__global__ void __launch_bounds__(256) row_rnorm(const uint16_t* __restrict__ x, float* __restrict__ rn, long rows,
+                                                 int D) {
+    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;  // whole wavefront
+    float ss = 0.f;
+    for (int c = lane; c < D; c += 64) {
+        const float v = __uint_as_float((uint32_t)x[r * D + c] << 16);
+        ss = fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if (lane == 0) rn[r] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+}
+
+// Through the L2 norm, in place: dx (with respect to x_n = x rn) becomes
+// rn (dx - (dx . x_n) x_n), or dx rn where |x| <= 1e-12 (rn = 1e12: x_n = x / 1e-12 there).
+__global__ void __launch_bounds__(256) l2norm_bwd(float* __restrict__ dx, const uint16_t* __restrict__ x,
+                                                  const float* __restrict__ rn, long rows, int D) {
+    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;  // whole wavefront
+    const float n = rn[r];
+    float dot = 0.f;
+    for (int c = lane; c < D; c += 64) dot = fmaf(dx[r * D + c], __uint_as_float((uint32_t)x[r * D + c] << 16) * n, dot);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    const bool tiny = n >= 1e12f;
+    for (int c = lane; c < D; c += 64) {
+        const float xn = __uint_as_float((uint32_t)x[r * D + c] << 16) * n;
+        const float g = dx[r * D + c];
+        dx[r * D + c] = tiny ? g * n : n * fmaf(-dot, xn, g);
+    }
+}
+
 struct BwdLayout {
     size_t blobs, S_save, G_save, Dp, Dl, dDl, dDp, dQh, dEh, dKb, dPm, dAm, dgam, total;
 };
@@ -1032,8 +1097,8 @@ BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
     return L;
 }
 
-template <int DK>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+template <int DK, int PRO>
+hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hipStream_t st) {
     const BwdLayout L = bwd_layout(a.B, a.T, a.H, DK, a.DV);
     char* ws = static_cast<char*>(a.workspace);
     const int BH = a.B * a.H, nch = (a.T + CH - 1) / CH;
@@ -1052,28 +1117,36 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     float* dgam = reinterpret_cast<float*>(ws + L.dgam);
 
     const ChunkArgs fa{a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, nullptr, nullptr, a.B, a.T, a.H, DK, a.DV,
-                       true, 0u, nullptr, 0};
+                       true, (uint32_t)PRO << 2, nullptr, 0};
     hipError_t e = launch_split_states(fa, blobs, S_save, Dp, Dl, st);
     if (e != hipSuccess) return e;
 
     constexpr int DVT = DK < 64 ? DK : 64;
     const ChainBwdIO cio{a.v, a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0,
                          a.B, a.T, a.H, a.DV, nch};
-    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3(BH * (a.DV / DVT)), dim3(bwd_chain_threads<DK>()), 0, st, cio);
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0>), dim3(BH * (a.DV / DVT)), dim3(bwd_chain_threads<DK>()), 0,
+                       st, cio);
     const ContractIO xio{a.dO, Dp, Dl, dDl, dDp, S_save, G_save, blobs, dQh, dEh, dKb, dPm, dAm, dgam,
                          a.B, a.T, a.H, a.DV, nch};
     hipLaunchKernelGGL((bwd_contract_kernel<DK>), dim3(BH * nch), dim3(256), 0, st, xio);
-    const KeyIO kio{a.q, a.k, a.alpha, a.b, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
+    const KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
                     a.B, a.T, a.H, nch};
-    hipLaunchKernelGGL((bwd_key_kernel<DK>), dim3((BH * nch + 7) / 8 * 8 * (DK / 32)), dim3(256), 0, st, kio);
+    hipLaunchKernelGGL((bwd_key_kernel<DK, PRO>), dim3((BH * nch + 7) / 8 * 8 * (DK / 32)), dim3(256), 0, st, kio);
+    if constexpr ((PRO & 1) != 0) {  // dq, dk through the L2 norm
+        const long rows = (long)a.B * a.T * a.H;
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        hipLaunchKernelGGL(l2norm_bwd, grid, dim3(256), 0, st, a.dq, static_cast<const uint16_t*>(a.q), rnq, rows, DK);
+        hipLaunchKernelGGL(l2norm_bwd, grid, dim3(256), 0, st, a.dk, static_cast<const uint16_t*>(a.k), rnk, rows, DK);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Extra workspace for scalar gates: the repeated gates (bf16) and the per-channel gradients (fp32).
+// Extra workspace for scalar gates: the repeated gates (bf16) and the per-channel gradients
+// (fp32); for the L2 norm: the reciprocal row norms of q and k.
 struct ScalarLayout {
-    size_t alpha, b, w, dalpha, db, dw, total;
+    size_t alpha, b, w, dalpha, db, dw, rnq, rnk, total;
 };
 
 ScalarLayout scalar_layout(size_t base, int B, int T, int H, int DK, int DV, uint32_t flags) {
@@ -1094,12 +1167,17 @@ ScalarLayout scalar_layout(size_t base, int B, int T, int H, int DK, int DV, uin
     o += bs ? up(rows * DK * 4) : 0;
     L.dw = o;
     o += bs ? up(rows * DV * 4) : 0;
+    const bool l2n = (flags & 4u) != 0;  // the row norms of q and k
+    L.rnq = o;
+    o += l2n ? up(rows * 4) : 0;
+    L.rnk = o;
+    o += l2n ? up(rows * 4) : 0;
     L.total = o;
     return L;
 }
 
 bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags) {
-    if (!bf16 || (flags & ~3u) != 0u || DK != DV) return false;
+    if (!bf16 || (flags & ~15u) != 0u || DK != DV) return false;
     if (DK != 32 && DK != 64 && DK != 128) return false;
     // one sequence's rows, the last chunk's rows past T included, addressed with 32-bit offsets
     return ((long long)T + CH) * H * DV * 4 < (1ll << 32);
@@ -1107,7 +1185,7 @@ bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags) {
 
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags) {
     const size_t base = bwd_layout(B, T, H, DK, DV).total;
-    return (flags & 3u) ? scalar_layout(base, B, T, H, DK, DV, flags).total : base;
+    return (flags & 7u) ? scalar_layout(base, B, T, H, DK, DV, flags).total : base;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
@@ -1121,12 +1199,21 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     if (!a.workspace || a.workspace_bytes < bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags))
         return hipErrorInvalidValue;
     BwdArgs g = a;  // the general-gate call
-    const bool as = (a.flags & 1u) != 0, bs = (a.flags & 2u) != 0;
+    const bool as = (a.flags & 1u) != 0, bs = (a.flags & 2u) != 0, l2n = (a.flags & 4u) != 0;
+    const ScalarLayout L = scalar_layout(bwd_layout(a.B, a.T, a.H, a.DK, a.DV).total, a.B, a.T, a.H, a.DK, a.DV,
+                                         a.flags);
+    char* ws = static_cast<char*>(a.workspace);
+    const long rows = (long)a.B * a.T * a.H;
+    float* rnq = nullptr;
+    float* rnk = nullptr;
+    if (l2n) {  // the reciprocal row norms of q and k, as the forward takes them
+        rnq = reinterpret_cast<float*>(ws + L.rnq);
+        rnk = reinterpret_cast<float*>(ws + L.rnk);
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        hipLaunchKernelGGL(row_rnorm, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.q), rnq, rows, a.DK);
+        hipLaunchKernelGGL(row_rnorm, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.k), rnk, rows, a.DK);
+    }
     if (as || bs) {
-        const ScalarLayout L = scalar_layout(bwd_layout(a.B, a.T, a.H, a.DK, a.DV).total, a.B, a.T, a.H, a.DK, a.DV,
-                                             a.flags);
-        char* ws = static_cast<char*>(a.workspace);
-        const long rows = (long)a.B * a.T * a.H;
         auto repeat = [&](const void* in, size_t off, int D) {
             const long n = rows * (D / 8);
             hipLaunchKernelGGL(repeat_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
@@ -1143,16 +1230,24 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
             g.db = reinterpret_cast<float*>(ws + L.db);
             g.dw = reinterpret_cast<float*>(ws + L.dw);
         }
-        g.flags = 0u;
+        g.flags &= ~3u;
     }
+    auto go = [&](auto pro) -> hipError_t {
+        constexpr int PRO = decltype(pro)::value;
+        switch (a.DK) {
+            case 32: return launch_bwd_t<32, PRO>(g, rnq, rnk, s);
+            case 64: return launch_bwd_t<64, PRO>(g, rnq, rnk, s);
+            default: return launch_bwd_t<128, PRO>(g, rnq, rnk, s);
+        }
+    };
     hipError_t e;
-    switch (a.DK) {
-        case 32: e = launch_bwd_t<32>(g, s); break;
-        case 64: e = launch_bwd_t<64>(g, s); break;
-        default: e = launch_bwd_t<128>(g, s); break;
+    switch ((a.flags >> 2) & 3u) {
+        case 0: e = go(std::integral_constant<int, 0>()); break;
+        case 1: e = go(std::integral_constant<int, 1>()); break;
+        case 2: e = go(std::integral_constant<int, 2>()); break;
+        default: e = go(std::integral_constant<int, 3>()); break;
     }
     if (e != hipSuccess || !(as || bs)) return e;
-    const long rows = (long)a.B * a.T * a.H;
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (as) hipLaunchKernelGGL(row_sums, grid, dim3(256), 0, s, g.dalpha, a.DK, nullptr, 0, a.dalpha, rows);
     if (bs) hipLaunchKernelGGL(row_sums, grid, dim3(256), 0, s, g.db, a.DK, g.dw, a.DV, a.db, rows);

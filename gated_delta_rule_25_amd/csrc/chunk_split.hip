@@ -115,21 +115,21 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
     }
 }
 
-template <int DK>
+template <int DK, int PRO>
 hipError_t launch_states_t(const ChunkArgs& a, char* blobs, float* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                            hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
     const int nch = (a.T + CH - 1) / CH;
-    hipLaunchKernelGGL((prep_kernel<DK, true, false, false>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k, a.alpha,
-                       a.b, a.B, a.T, a.H, 0, nch, blobs, VarTab{});
+    hipLaunchKernelGGL((prep_kernel<DK, true, false, false, PRO>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k,
+                       a.alpha, a.b, a.B, a.T, a.H, 0, nch, blobs, VarTab{});
     ChainIO io{a.v, a.w, nullptr, blobs, nch, 0, nch, nch, 1, a.B, a.T, a.H, a.DV,
                a.S0, (long)DK * a.DV, 0, a.DV, nullptr, 0, 0, a.DV, 0};
     io.S_save = S_save;
     io.save_nch = nch;
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
-    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true>), dim3(BHp * (a.DV / DVT)),
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
                        dim3(kChainThreads), 0, st, io);
     return hipGetLastError();
 }
@@ -138,11 +138,20 @@ hipError_t launch_states_t(const ChunkArgs& a, char* blobs, float* S_save, uint1
 
 hipError_t launch_split_states(const ChunkArgs& a, char* blobs, float* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                                hipStream_t s) {
-    if (!a.bf16 || a.flags != 0u || !split_supported(a.T, a.H, a.DK, a.DV, true)) return hipErrorNotSupported;
-    switch (a.DK) {
-        case 32: return launch_states_t<32>(a, blobs, S_save, Dp_save, Dl_save, s);
-        case 64: return launch_states_t<64>(a, blobs, S_save, Dp_save, Dl_save, s);
-        default: return launch_states_t<128>(a, blobs, S_save, Dp_save, Dl_save, s);
+    if (!a.bf16 || (a.flags & ~12u) != 0u || !split_supported(a.T, a.H, a.DK, a.DV, true)) return hipErrorNotSupported;
+    auto go = [&](auto pro) -> hipError_t {
+        constexpr int PRO = decltype(pro)::value;
+        switch (a.DK) {
+            case 32: return launch_states_t<32, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            case 64: return launch_states_t<64, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            default: return launch_states_t<128, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+        }
+    };
+    switch ((a.flags >> 2) & 3u) {  // prologue flags, as the forward takes them
+        case 0: return go(std::integral_constant<int, 0>());
+        case 1: return go(std::integral_constant<int, 1>());
+        case 2: return go(std::integral_constant<int, 2>());
+        default: return go(std::integral_constant<int, 3>());
     }
 }
 

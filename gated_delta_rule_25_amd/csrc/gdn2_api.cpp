@@ -298,7 +298,8 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const vo
                            float* db, float* dw, float* dS0, int32_t B, int32_t T, int32_t H,
                            int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    if (in_dtype != GDN2_BF16 || (gate_flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR)) != 0u)
+    if (in_dtype != GDN2_BF16 ||
+        (gate_flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR | GDN2_QK_L2NORM | GDN2_GATE_LOGITS)) != 0u)
         return GDN2_ERR_UNSUPPORTED;
     const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
     if (bs && (w || dw)) return GDN2_ERR_UNSUPPORTED;  // w is implied by beta; dbeta goes to db

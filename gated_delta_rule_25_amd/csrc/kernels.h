@@ -56,7 +56,7 @@ size_t varlen_table_bytes(int n);
 size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16);
 // Prep over every chunk into `blobs` ([b*h][chunk] operand blocks), then the state-only chain in
 // order, saving the state at the start of every chunk ([b*h][chunk][DK][DV]) and the rows of D'
-// and Delta ([B, T, H, DV], fp16 bits). bf16 inputs, general gates.
+// and Delta ([B, T, H, DV], fp16 bits). bf16 inputs, general gates, the prologue flags allowed.
 hipError_t launch_split_states(const ChunkArgs& a, char* blobs, float* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                                hipStream_t s);
 

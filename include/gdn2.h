@@ -76,8 +76,9 @@ enum {
                                w must be NULL */
     /* Prologue flags: the steps in front of the recurrence done inside the kernels, in fp32, on
      * the inputs as given [GDN2-summary, paragraph "Архитектурно": L2-normalised q/k, sigmoid
-     * gates]. Taken by the two-kernel prefill (gdn2_chunk_fwd with a workspace), the token-by-token
-     * prefill and the decode step; the single-kernel prefill and gdn2_chunk_bwd return
+     * gates]. Taken by the two-kernel prefill (gdn2_chunk_fwd with a workspace), the packed
+     * prefill, the token-by-token prefill, the decode step and gdn2_chunk_bwd (which then gives
+     * the gradients with respect to the raw inputs); the single-kernel prefill returns
      * GDN2_ERR_UNSUPPORTED for them. */
     GDN2_QK_L2NORM = 4u,   /* q and k are normalised per token and head over d_k:
                               x / max(|x|_2, 1e-12) */
@@ -213,15 +214,19 @@ gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const 
  *            == NULL. A scalar gate is the general gate with the scalar in every channel, so its
  *            gradient is the sum of the per-channel gradients; the call computes it that way.
  *
- * Supported: bf16 inputs, the general and scalar gate forms (no prologue flags), d_k == d_v in
- * {32, 64, 128}, and one sequence's rows below 4 GiB ((T + 64)*H*d_v*4 < 2^32 bytes); anything
- * else returns GDN2_ERR_UNSUPPORTED. Arithmetic as in the forward: fp16 matrix-core operands with fp32
+ *   prologue flags (GDN2_QK_L2NORM, GDN2_GATE_LOGITS): q, k, alpha, b, w are the raw inputs the
+ *            forward takes with the same flags, and dq, dk, dalpha, db, dw are the gradients
+ *            with respect to them (through the norm and the sigmoids).
+ *
+ * Supported: bf16 inputs, every gate form and prologue flag, d_k == d_v in {32, 64, 128}, and one
+ * sequence's rows below 4 GiB ((T + 64)*H*d_v*4 < 2^32 bytes); anything else returns
+ * GDN2_ERR_UNSUPPORTED. Arithmetic as in the forward: fp16 matrix-core operands with fp32
  * accumulation for the state chains, fp32 for the per-chunk gradient work.
  * The workspace (required when T > 0, 256-byte aligned, at least
  * gdn2_chunk_bwd_workspace_bytes for the same gate_flags) holds the operand blocks, the state and
  * its gradient at every chunk boundary and the per-chunk intermediate products (and, for scalar
- * gates, the gates repeated over the channels and their per-channel gradients); its contents are
- * scratch. No output may
+ * gates, the gates repeated over the channels and their per-channel gradients; for the L2 norm,
+ * the row norms of q and k); its contents are scratch. No output may
  * overlap an input, another output or the workspace (GDN2_ERR_ALIAS). Other errors, ownership
  * and stream semantics as for gdn2_chunk_fwd.
  */

@@ -187,9 +187,9 @@ def test_chunked_calls_reject_grids_beyond_31_bits(lib):
 
 
 def test_bwd_gate_forms_on_the_host(lib):
-    # scalar beta implies w: passing w or dw with GDN2_BETA_SCALAR is refused; prologue flags are
-    # not taken by the backward; the workspace query grows for scalar gates (repeated gates and
-    # their per-channel gradients)
+    # scalar beta implies w: passing w or dw with GDN2_BETA_SCALAR is refused; an unknown flag is
+    # refused; the workspace query grows for scalar gates (repeated gates and their per-channel
+    # gradients) and for the L2 norm (row norms)
     far = [P((1 << 40) * (i + 1)) for i in range(16)]
     ws = P((1 << 40) * 20)
     f = lib.gdn2_chunk_bwd
@@ -199,5 +199,6 @@ def test_bwd_gate_forms_on_the_host(lib):
     p = list(far[:16])
     p[5] = None
     assert f(*p, B, T, H, 64, 64, 0, 2, ws, 1 << 30, None) == 3                  # dw given
-    assert f(*far[:16], B, T, H, 64, 64, 0, 4, ws, 1 << 30, None) == 3           # prologue flag
+    assert f(*far[:16], B, T, H, 64, 64, 0, 16, ws, 1 << 30, None) == 3          # unknown flag
     assert q(B, T, H, 64, 64, 0, 3) > q(B, T, H, 64, 64, 0, 1) > q(B, T, H, 64, 64, 0, 0) > 0
+    assert q(B, T, H, 64, 64, 0, 4) > q(B, T, H, 64, 64, 0, 0) == q(B, T, H, 64, 64, 0, 8)

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from parity import banner, normwise_err
-from gated_delta_rule_25_amd.inputs import WORKLOADS, make_cotangents, make_inputs, scaled
+from gated_delta_rule_25_amd.inputs import WORKLOADS, make_cotangents, make_inputs, make_prologue_inputs, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +96,54 @@ def test_bwd_scalar_gates(gates):
                db=np.asarray(ref["db"]).sum(-1) + np.asarray(ref["dw"]).sum(-1))
     assert "dw" not in got
     assert tuple(got["db"].shape) == (wl.B, wl.T, wl.H)
+    errs = {n: normwise_err(got[n], exp[n]) for n in exp}
+    print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= TOLB for e in errs.values()), errs
+
+
+PRO_CASES = [
+    ("general_both", scaled(WORKLOADS["prefill_1p3b"], B=2, T=150, H=2), True, True),
+    ("general_l2norm", scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=2), True, False),
+    ("general_logits", scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=2), False, True),
+    ("d64_both", scaled(WORKLOADS["prefill_1p3b"], B=1, T=100, H=2, d_k=64, d_v=64), True, True),
+    ("gdn_both", scaled(WORKLOADS["gdn_scalar"], B=1, T=130, H=2), True, True),
+    ("kda_logits", scaled(WORKLOADS["kda_scalar"], B=1, T=130, H=2), False, True),
+]
+
+
+@pytest.mark.parametrize("name,wl,l2n,gl", PRO_CASES, ids=[c[0] for c in PRO_CASES])
+def test_bwd_prologue(name, wl, l2n, gl):
+    """With the prologue flags the kernels take raw q, k (and gate pre-activations) and return the
+    gradients with respect to them. Reference: the oracle's prologue, its backward on the result
+    (scalar gates repeated over the channels, their gradients summed), then the oracle's
+    prologue backward."""
+    banner(f"bwd prologue {name} l2norm={l2n} logits={gl} {wl}")
+    ins = make_prologue_inputs(wl)
+    if not (l2n and gl):  # the step the kernel does not do is applied here (float64, then bf16)
+        q, k, a, b, w = oracle.prologue(ins["q"], ins["k"], ins["alpha"], ins["b"], ins["w"],
+                                        l2norm=not l2n, gate_logits=not gl)
+        t = lambda x: None if x is None else torch.from_numpy(np.asarray(x)).to(torch.bfloat16)
+        ins.update(q=t(q), k=t(k), alpha=t(a), b=t(b), w=t(w))
+    cot = make_cotangents(wl)
+    dk, dv = wl.d_k, wl.d_v
+    q, k, a, b, w = oracle.prologue(ins["q"], ins["k"], ins["alpha"], ins["b"], ins["w"], l2norm=l2n, gate_logits=gl)
+    ag, bg, wg = oracle.broadcast_gates(a, b, w, dk, dv, alpha_scalar=ins["alpha_scalar"],
+                                        beta_scalar=ins["beta_scalar"])
+    ref = oracle.backward(q, k, ins["v"], ag, bg, wg, ins["S0"], cot["dO"], cot["dS_T"])
+    grads = dict(dq=ref["dq"], dk=ref["dk"],
+                 dalpha=np.asarray(ref["dalpha"]).sum(-1) if ins["alpha_scalar"] else ref["dalpha"])
+    if ins["beta_scalar"]:
+        grads["db"] = np.asarray(ref["db"]).sum(-1) + np.asarray(ref["dw"]).sum(-1)
+    else:
+        grads.update(db=ref["db"], dw=ref["dw"])
+    exp = oracle.prologue_backward(ins["q"], ins["k"], ins["alpha"], ins["b"], ins["w"], grads,
+                                   l2norm=l2n, gate_logits=gl)
+    exp.update(dv=ref["dv"], dS0=ref["dS0"])
+    g = _g()
+    d = {n: _cuda(ins[n]) for n in ("q", "k", "v", "alpha", "b", "w", "S0")}
+    got = g.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"], _cuda(cot["dO"]),
+                      _cuda(cot["dS_T"]), l2norm=l2n, gate_logits=gl)
+    torch.cuda.synchronize()
     errs = {n: normwise_err(got[n], exp[n]) for n in exp}
     print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     assert all(e <= TOLB for e in errs.values()), errs
