@@ -228,9 +228,29 @@ def backward_leg(g, steps):
                tokens_per_s=round(B * T / (ms * 1e-3), 1), algorithmic_bytes=int(alg),
                gbs=round(alg / (ms * 1e-3) / 1e9, 1), frac=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                workspace_bytes=int(ws.numel()))
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / n
+
+    # the same shape with the prologue flags (inputs taken as raw q, k and gate pre-activations)
+    res["prologue_ms"] = round(timed(lambda: g.chunk_bwd(*args, l2norm=True, gate_logits=True), max(2, steps // 2)), 4)
+    # Gated DeltaNet form: scalar alpha and beta (the per-head first channel of the general gates)
+    sa = ins["alpha"][..., 0].contiguous()
+    sb = ins["b"][..., 0].contiguous()
+    sargs = [ins["q"], ins["k"], ins["v"], sa, sb, None, ins["S0"], cot["dO"], cot["dS_T"]]
+    res["scalar_gates_ms"] = round(timed(lambda: g.chunk_bwd(*sargs), max(2, steps // 2)), 4)
     print(f"[bench] backward: {ms:.3f} ms/call, {res['tokens_per_s']:.3e} tokens/s, {res['gbs']} GB/s "
-          f"algorithmic ({100 * res['frac']:.1f}% of HBM)", file=sys.stderr, flush=True)
-    del ins, cot, ws, out
+          f"algorithmic ({100 * res['frac']:.1f}% of HBM); with the prologue {res['prologue_ms']:.3f} ms, "
+          f"scalar gates {res['scalar_gates_ms']:.3f} ms", file=sys.stderr, flush=True)
+    del ins, cot, ws, out, sa, sb, sargs
     torch.cuda.empty_cache()
     return res
 
