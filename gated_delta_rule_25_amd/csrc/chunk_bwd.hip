@@ -166,7 +166,11 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, DV = io.DV, nch = io.nch;
     const int vt = DV / DVT;
-    const int bh = blockIdx.x / vt, tile = blockIdx.x % vt;
+    // the vt tiles of one (b, h) sit 8 workgroups apart, on one XCD (workgroups go round the 8
+    // XCDs in order), so the second tile's block reads hit that XCD's L2
+    const int grp = blockIdx.x / (8 * vt), within = blockIdx.x % (8 * vt);
+    const int bh = grp * 8 + within % 8, tile = within / 8;
+    if (bh >= io.B * io.H) return;  // (the grid is padded to a multiple of 8 (b, h))
     const int hh = bh % H, bb = bh / H;
     const int col = tile * DVT + 16 * wv + l16;
     auto blob_of = [&](int n) { return io.blobs + ((size_t)bh * nch + n) * BL::bytes; };
@@ -1124,7 +1128,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
     constexpr int DVT = DK < 64 ? DK : 64;
     const ChainBwdIO cio{a.v, a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0,
                          a.B, a.T, a.H, a.DV, nch};
-    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0>), dim3(BH * (a.DV / DVT)), dim3(bwd_chain_threads<DK>()), 0,
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0>), dim3((BH + 7) / 8 * 8 * (a.DV / DVT)),
+                       dim3(bwd_chain_threads<DK>()), 0,
                        st, cio);
     const ContractIO xio{a.dO, Dp, Dl, dDl, dDp, S_save, G_save, blobs, dQh, dEh, dKb, dPm, dAm, dgam,
                          a.B, a.T, a.H, a.DV, nch};
