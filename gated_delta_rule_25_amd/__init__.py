@@ -9,6 +9,8 @@ if the library is not built or no GPU is present, calls raise.
     o, S_T = recurrent_fwd(q, k, v, alpha, b, w, S0)    # token-by-token fp32 prefill
     o = decode_step(q, k, v, alpha, b, w, S)            # one token, S updated in place
     g = chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T)    # gradients (dict: dq, dk, dv, ...)
+    o, S_T = chunk_fwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0)  # packed [T_total, H, d] rows
+    g = chunk_bwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0, dO, dS_T)
 
 Shapes: q, k, alpha, b [B, T, H, d_k]; v, w [B, T, H, d_v]; states [B, H, d_k, d_v] float32;
 decode drops the T axis. Scalar gates: alpha [B, T, H] (alpha_scalar) and b = beta [B, T, H]
@@ -22,7 +24,7 @@ import os
 import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to it)
 
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
-           "chunk_bwd_workspace_bytes",
+           "chunk_bwd_workspace_bytes", "chunk_bwd_varlen", "chunk_bwd_varlen_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
            "decode_step_slots"]
 
@@ -67,6 +69,10 @@ def load():
     lib.gdn2_chunk_bwd.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
     lib.gdn2_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn2_chunk_bwd_varlen.argtypes = [p] * 17 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_varlen_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
+    lib.gdn2_chunk_bwd_varlen_workspace_bytes.restype = sz
     lib.gdn2_decode_step_slots.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p]
     lib.gdn2_decode_step_slots.restype = ctypes.c_int
     lib.gdn2_recurrent_fwd.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p]
@@ -221,34 +227,58 @@ def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=No
     inputs are the raw ones the forward takes with the same flags, and the gradients are with
     respect to them. `out` may supply any of them; the workspace is allocated here unless given.
     """
+    return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, None, workspace, out, l2norm, gate_logits, stream)
+
+
+def chunk_bwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
+    return int(load().gdn2_chunk_bwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v,
+                                                            BF16 if dtype == torch.bfloat16 else F32, flags))
+
+
+def chunk_bwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0, dO, dS_T=None, *, workspace=None, out=None,
+                     l2norm=False, gate_logits=False, stream=None):
+    """Gradients for the packed prefill chunk_fwd_varlen: the rows are [T_total, H, d] and the
+    states [N, H, d_k, d_v], N = len(cu_seqlens) - 1; otherwise as chunk_bwd."""
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or not cu_seqlens.is_cuda \
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise TypeError("cu_seqlens must be a contiguous 1-d int32 GPU tensor of N + 1 entries")
+    return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu_seqlens, workspace, out, l2norm, gate_logits, stream)
+
+
+def _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu, workspace, out, l2norm, gate_logits, stream):
     lib = load()
-    flags = _check_inputs(q, k, v, alpha, b, w, 4) | _prologue_flags(l2norm, gate_logits)
-    B, T, H, dk = q.shape
+    flags = _check_inputs(q, k, v, alpha, b, w, 4 if cu is None else 3) | _prologue_flags(l2norm, gate_logits)
+    lead = tuple(q.shape[:-2])  # (B, T), or (T_total,) for a packed batch
+    H, dk = q.shape[-2:]
     dv = v.shape[-1]
+    B, T = lead if cu is None else (cu.numel() - 1, lead[0])  # sequences (states), rows per call
     for name, x in (("S0", S0), ("dO", dO), ("dS_T", dS_T)):
         if x is not None and (x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda):
             raise TypeError(f"{name} must be a contiguous float32 GPU tensor")
     out = dict(out or {})
     f32 = dict(device=q.device, dtype=torch.float32)
     for name in ("dq", "dk"):
-        out.setdefault(name, torch.empty(B, T, H, dk, **f32))
-    out.setdefault("dalpha", torch.empty(B, T, H, **f32) if flags & ALPHA_SCALAR else torch.empty(B, T, H, dk, **f32))
-    out.setdefault("db", torch.empty(B, T, H, **f32) if flags & BETA_SCALAR else torch.empty(B, T, H, dk, **f32))
-    out.setdefault("dv", torch.empty(B, T, H, dv, **f32))
+        out.setdefault(name, torch.empty(*lead, H, dk, **f32))
+    out.setdefault("dalpha", torch.empty(*lead, H, **f32) if flags & ALPHA_SCALAR else torch.empty(*lead, H, dk, **f32))
+    out.setdefault("db", torch.empty(*lead, H, **f32) if flags & BETA_SCALAR else torch.empty(*lead, H, dk, **f32))
+    out.setdefault("dv", torch.empty(*lead, H, dv, **f32))
     if not flags & BETA_SCALAR:
-        out.setdefault("dw", torch.empty(B, T, H, dv, **f32))
+        out.setdefault("dw", torch.empty(*lead, H, dv, **f32))
     out.setdefault("dS0", torch.empty(B, H, dk, dv, **f32))
     dt = _dtype_code(q)
-    need = int(lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
+    fn = "gdn2_chunk_bwd" if cu is None else "gdn2_chunk_bwd_varlen"
+    need = int(getattr(lib, fn + "_workspace_bytes")(B, T, H, dk, dv, dt, flags))
     if need and workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
-                            _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                            _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out.get("dw")), _ptr(out["dS0"]),
-                            B, T, H, dk, dv, dt, flags, _ptr(workspace), ws_bytes, _stream(stream))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]),
+            _ptr(out.get("dw")), _ptr(out["dS0"])]
+    if cu is not None:
+        args.append(_ptr(cu))
+    st = getattr(lib, fn)(*args, B, T, H, dk, dv, dt, flags, _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
-        raise Gdn2Error("gdn2_chunk_bwd", st)
+        raise Gdn2Error(fn, st)
     return out
 
 

@@ -68,5 +68,30 @@ __device__ __forceinline__ void wait_vm_but() {
     __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Packed (ragged) batch: sequence s holds token rows [start[s], start[s] + len[s]) of the packed
+// inputs and chunks [coff[s], coff[s + 1]) of the batch; n sequences. Built on the device from
+// the caller's cumulative sequence lengths.
+struct VarTab {
+    const int* coff = nullptr;
+    const int* start = nullptr;
+    const int* len = nullptr;
+    int n = 0;
+};
+
+// The sequence that holds chunk gc of a packed batch: the last s with coff[s] <= gc (gc below the
+// chunk count, so that sequence has a chunk at gc - coff[s]).
+__device__ __forceinline__ int varlen_seq_of(const VarTab& vt, int gc) {
+    int lo = 0, hi = vt.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (vt.coff[mid] <= gc) {
+            lo = mid;
+        } else {
+            hi = mid - 1;
+        }
+    }
+    return lo;
+}
+
 }  // namespace chunk
 }  // namespace gdn2

@@ -80,6 +80,10 @@ struct ChainBwdIO {
     float* dw;
     float* dS0;  // [B, H, DK, DV] or null
     int B, T, H, DV, nch;
+    // packed batch (VAR): B sequences, T rows, blocks and saves [h][chunk of the batch] with `ring`
+    // slots per head
+    VarTab var{};
+    long ring = 0;
 };
 
 // The reverse chain contracts P, T, K_bar, Q_hat and E_hat over the other index than the forward
@@ -137,7 +141,7 @@ constexpr int bwd_chain_threads() {
 
 // WSIG: w holds pre-activations (the prologue's gate logits): the gate is sigma(w), and dw is
 // taken with respect to the pre-activation.
-template <int DK, bool WSIG = false>
+template <int DK, bool WSIG = false, bool VAR = false>
 __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(const ChainBwdIO io) {
     using PR = Prec<true>;
     using E = _Float16;
@@ -173,17 +177,33 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     if (bh >= io.B * io.H) return;  // (the grid is padded to a multiple of 8 (b, h))
     const int hh = bh % H, bb = bh / H;
     const int col = tile * DVT + 16 * wv + l16;
-    auto blob_of = [&](int n) { return io.blobs + ((size_t)bh * nch + n) * BL::bytes; };
+    // this sequence: its chunks (slots cbase0 ..), first token row and length
+    int nchs, Tq;
+    long tbase;
+    size_t cbase0;
+    if constexpr (VAR) {
+        const int cf = io.var.coff[bb];
+        nchs = io.var.coff[bb + 1] - cf;
+        tbase = io.var.start[bb];
+        Tq = io.var.len[bb];
+        cbase0 = (size_t)hh * io.ring + cf;
+    } else {
+        nchs = nch;
+        tbase = (long)bb * T;
+        Tq = T;
+        cbase0 = (size_t)bh * nch;
+    }
+    auto blob_of = [&](int n) { return io.blobs + (cbase0 + n) * BL::bytes; };
 
-    const long seq = (long)bb * T * H;
-    const unsigned seq_f32 = (unsigned)T * H * DV * 4u;
+    const long seq = tbase * H;
+    const unsigned seq_f32 = (unsigned)Tq * H * DV * 4u;
     const auto rs_dO = make_rsrc(io.dO + seq * DV, seq_f32);
     const auto rs_dDl = make_rsrc(io.dDl + seq * DV, seq_f32 / 2u);
     const auto rs_dDp = make_rsrc(io.dDp + seq * DV, seq_f32 / 2u);
     const auto rs_dv = make_rsrc(io.dv + seq * DV, seq_f32);
     const auto rs_dw = make_rsrc(io.dw + seq * DV, seq_f32);
-    const auto rs_v = make_rsrc(static_cast<const uint16_t*>(io.v) + seq * DV, (unsigned)T * H * DV * 2u);
-    const auto rs_w = make_rsrc(static_cast<const uint16_t*>(io.w) + seq * DV, (unsigned)T * H * DV * 2u);
+    const auto rs_v = make_rsrc(static_cast<const uint16_t*>(io.v) + seq * DV, (unsigned)Tq * H * DV * 2u);
+    const auto rs_w = make_rsrc(static_cast<const uint16_t*>(io.w) + seq * DV, (unsigned)Tq * H * DV * 2u);
     // element index of (token row 0 of the sequence, head hh, column col)
     auto elem = [&](int row) -> unsigned { return ((unsigned)row * H + hh) * DV + col; };
 
@@ -255,13 +275,13 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     };
     constexpr int kStepStores = NMK + 16;  // stores a step issues after its loads
 
-    if (nch > 0) {
-        dma_flat(blob_of(nch - 1), smem, BL::bytes, wv, NW, lane);
-        fetch(nch - 1);
+    if (nchs > 0) {
+        dma_flat(blob_of(nchs - 1), smem, BL::bytes, wv, NW, lane);
+        fetch(nchs - 1);
     }
 
-    for (int idx = 0; idx < nch; ++idx) {
-        const int n = nch - 1 - idx, t0 = n * CH;
+    for (int idx = 0; idx < nchs; ++idx) {
+        const int n = nchs - 1 - idx, t0 = n * CH;
         // block n and this wave's rows of chunk n have arrived (the previous step's stores,
         // issued after them, may still be in flight)
         if (idx == 0) {
@@ -325,7 +345,7 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
         if (n > 0) fetch(n - 1);
 
         // G' of this chunk, for the contraction kernel
-        store_state(io.G_save + ((size_t)bh * nch + n) * DK * DV);
+        store_state(io.G_save + (cbase0 + n) * DK * DV);
 
         Frag Gf[NKS];
 #pragma unroll
@@ -404,12 +424,14 @@ struct ContractIO {
     float* dAm;
     float* dgam;  // [b*h][nch][DK]
     int B, T, H, DV, nch;
+    VarTab var{};  // packed batch: as ChainBwdIO's
+    long ring = 0;
 };
 
 // All five products contract over the value channels j with both operands row-major in j, the
 // fragment layout of the matrix cores: fp16 operands (as in the chains), fp32 accumulation. The
 // value channels are staged in slices of 64 columns; wave w owns output rows 16 w .. 16 w + 15.
-template <int DK>
+template <int DK, bool VAR = false>
 __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO io) {
     using PR = Prec<true>;
     using E = _Float16;
@@ -432,10 +454,29 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, DV = io.DV, nch = io.nch;
-    const int bh = blockIdx.x / nch, n = blockIdx.x % nch;
-    const int hh = bh % H, bb = bh / H;
+    // this workgroup's chunk: its slot cbase, first row t0 in the sequence, the sequence's first
+    // token row tbase and length Tq (packed: workgroup x = (chunk of the batch) H + h)
+    int hh, n, Tq;
+    long tbase;
+    size_t cbase;
+    if constexpr (VAR) {
+        hh = blockIdx.x % H;
+        const int gc = blockIdx.x / H;
+        if (gc >= io.var.coff[io.var.n]) return;
+        const int sq = varlen_seq_of(io.var, gc);
+        n = gc - io.var.coff[sq];
+        tbase = io.var.start[sq];
+        Tq = io.var.len[sq];
+        cbase = (size_t)hh * io.ring + gc;
+    } else {
+        const int bh = blockIdx.x / nch;
+        n = blockIdx.x % nch;
+        hh = bh % H;
+        tbase = (long)(bh / H) * T;
+        Tq = T;
+        cbase = (size_t)bh * nch + n;
+    }
     const int t0 = n * CH;
-    const size_t cbase = (size_t)bh * nch + n;
     const float* S = io.S_save + cbase * DK * DV;
     const float* Gp = io.G_save + cbase * DK * DV;
 
@@ -480,14 +521,14 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
         for (int u = 0; u < NRU; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
             const int t = t0 + r;
-            const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DV + js + j;
+            const size_t e = ((tbase + (t < Tq ? t : 0)) * H + hh) * DV + js + j;
             lr[u] = *reinterpret_cast<const float4*>(io.dO + e);
         }
 #pragma unroll
         for (int u = 0; u < NRH; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 8), j = 8 * (x % (JS / 8));
             const int t = t0 + r;
-            const size_t e = (((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DV + js + j;
+            const size_t e = ((tbase + (t < Tq ? t : 0)) * H + hh) * DV + js + j;
 #pragma unroll
             for (int m = 0; m < 4; ++m) lh[m][u] = *reinterpret_cast<const uint4*>(srch[m] + e);
         }
@@ -502,13 +543,13 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 #pragma unroll
         for (int u = 0; u < NRU; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
-            const float4 a = t0 + r < T ? lr[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 a = t0 + r < Tq ? lr[u] : make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<h4*>(dOs + r * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
         }
 #pragma unroll
         for (int u = 0; u < NRH; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 8), j = 8 * (x % (JS / 8));
-            const bool ok = t0 + r < T;
+            const bool ok = t0 + r < Tq;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const uint4 a = ok ? lh[m][u] : make_uint4(0u, 0u, 0u, 0u);
@@ -643,6 +684,8 @@ struct KeyIO {
     const float *dQh, *dEh, *dKb, *dPm, *dAm, *dgam;
     float *dq, *dk, *dalpha, *db;  // [B, T, H, DK]
     int B, T, H, nch;
+    VarTab var{};  // packed batch: as ChainBwdIO's
+    long ring = 0;
 };
 
 // One workgroup per (b, h, chunk, 32 key channels): the decay-weighted sums are independent per
@@ -662,7 +705,7 @@ struct KeyIO {
 // are left with respect to the normalised vectors (a later pass takes them through the norm);
 // bit 1, alpha and b are pre-activations: log2 alpha = log2 sigma(x), b = sigma(x), and dalpha, db
 // are taken with respect to the pre-activations.
-template <int DK, int PRO = 0>
+template <int DK, int PRO = 0, bool VAR = false>
 __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     constexpr bool L2N = (PRO & 1) != 0, GL = (PRO & 2) != 0;
     constexpr int CW = 32;       // key channels per workgroup
@@ -680,11 +723,29 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     // the 8 XCDs in order), so their reads of the chunk's dA and dP share that XCD's L2
     const int w8 = blockIdx.x % 8, rest = blockIdx.x / 8;
     const int cg = rest % NG, item = (rest / NG) * 8 + w8;
-    if (item >= io.B * io.H * io.nch) return;
-    const int bh = item / nch, n = item % nch;
-    const int hh = bh % H, bb = bh / H;
+    // this workgroup's chunk (as in the contraction kernel; packed: item = (chunk of the batch) H + h)
+    int hh, n, Tq;
+    long tbase;
+    size_t cbase;
+    if constexpr (VAR) {
+        hh = item % H;
+        const int gc = item / H;
+        if (gc >= io.var.coff[io.var.n]) return;
+        const int sq = varlen_seq_of(io.var, gc);
+        n = gc - io.var.coff[sq];
+        tbase = io.var.start[sq];
+        Tq = io.var.len[sq];
+        cbase = (size_t)hh * io.ring + gc;
+    } else {
+        if (item >= io.B * io.H * io.nch) return;
+        const int bh = item / nch;
+        n = item % nch;
+        hh = bh % H;
+        tbase = (long)(bh / H) * T;
+        Tq = T;
+        cbase = (size_t)bh * nch + n;
+    }
     const int t0 = n * CH, c0 = cg * CW;
-    const size_t cbase = (size_t)bh * nch + n;
     const int ch0 = 2 * l16;  // this lane's first channel in the group
     const int rb = 16 * I + 4 * g;  // this lane's first row
     auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
@@ -699,7 +760,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
-        const size_t e = ((((size_t)bb * T + (t < T ? t : 0)) * H + hh) * DK + c0 + ch0) / 2;
+        const size_t e = (((tbase + (t < Tq ? t : 0)) * H + hh) * DK + c0 + ch0) / 2;
         rq[j] = q32[e];
         rk[j] = k32[e];
         rbv[j] = b32[e];
@@ -726,7 +787,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int t = t0 + rb + j;
-            const size_t row = ((size_t)bb * T + (t < T ? t : 0)) * H + hh;
+            const size_t row = (tbase + (t < Tq ? t : 0)) * H + hh;
             nq[j] = io.rnq[row];
             nk[j] = io.rnk[row];
         }
@@ -737,7 +798,7 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     auto gate = [](float x) { return GL ? sigmoidf_(x) : x; };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const bool ok = t0 + rb + j < T;
+        const bool ok = t0 + rb + j < Tq;
         q[j][0] = ok ? lo(rq[j]) * nq[j] : 0.f;
         q[j][1] = ok ? hi(rq[j]) * nq[j] : 0.f;
         k[j][0] = ok ? lo(rk[j]) * nk[j] : 0.f;
@@ -944,8 +1005,8 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
-        if (t < T) {
-            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + c0 + ch0;
+        if (t < Tq) {
+            const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
             *reinterpret_cast<float2*>(io.dq + e) = make_float2(xa[0][j], xa[1][j]);
             *reinterpret_cast<float2*>(io.dk + e) = make_float2(xp[0][j], xp[1][j]);
             *reinterpret_cast<float2*>(io.db + e) = make_float2(yy[0][j], yy[1][j]);
@@ -982,8 +1043,8 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
-        if (t < T) {
-            const size_t e = (((size_t)bb * T + t) * H + hh) * DK + c0 + ch0;
+        if (t < Tq) {
+            const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
             *reinterpret_cast<float2*>(io.dalpha + e) = make_float2(dal[j][0], dal[j][1]);
         }
     }
@@ -1062,19 +1123,21 @@ struct BwdLayout {
     size_t blobs, S_save, G_save, Dp, Dl, dDl, dDp, dQh, dEh, dKb, dPm, dAm, dgam, total;
 };
 
-BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
+// Workspace of the backward: `head` bytes first (the sequence table of a packed batch), then the
+// per-chunk buffers for `slots` chunks (b*h*chunks, or h * chunk bound of a packed batch) and the
+// per-row buffers for `tok_rows` token rows (b*t*h).
+BwdLayout bwd_layout_n(size_t slots, size_t tok_rows, int DK, int DV, size_t head) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t BH = (size_t)B * H, nch = ((size_t)T + CH - 1) / CH;
     BwdLayout L{};
-    size_t o = 0;
+    size_t o = up(head);
     L.blobs = o;
-    o += up(nch * split_chunk_bytes(B, H, DK, true));
-    const size_t st = up(BH * nch * DK * DV * 4);
+    o += up(slots * split_chunk_bytes(1, 1, DK, true));
+    const size_t st = up(slots * DK * DV * 4);
     L.S_save = o;
     o += st;
     L.G_save = o;
     o += st;
-    const size_t rows = up((size_t)B * T * H * DV * 2);  // fp16 rows
+    const size_t rows = up(tok_rows * DV * 2);  // fp16 rows
     L.Dp = o;
     o += rows;
     L.Dl = o;
@@ -1083,29 +1146,47 @@ BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
     o += rows;
     L.dDp = o;
     o += rows;
-    const size_t kr = up(BH * nch * CH * DK * 4);
+    const size_t kr = up(slots * CH * DK * 4);
     L.dQh = o;
     o += kr;
     L.dEh = o;
     o += kr;
     L.dKb = o;
     o += kr;
-    const size_t pm = up(BH * nch * CH * CH * 4);
+    const size_t pm = up(slots * CH * CH * 4);
     L.dPm = o;
     o += pm;
     L.dAm = o;
     o += pm;
     L.dgam = o;
-    o += up(BH * nch * DK * 4);
+    o += up(slots * DK * 4);
     L.total = o;
     return L;
 }
 
-template <int DK, int PRO>
+BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
+    const size_t nch = ((size_t)T + CH - 1) / CH;
+    return bwd_layout_n((size_t)B * H * nch, (size_t)B * T * H, DK, DV, 0);
+}
+
+// packed batch of n sequences, T rows
+BwdLayout bwd_layout_var(int n, int T, int H, int DK, int DV) {
+    return bwd_layout_n((size_t)H * varlen_chunk_bound(n, T), (size_t)T * H, DK, DV, varlen_table_bytes(n));
+}
+
+template <int DK, int PRO, bool VAR>
 hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hipStream_t st) {
-    const BwdLayout L = bwd_layout(a.B, a.T, a.H, DK, a.DV);
+    const BwdLayout L = VAR ? bwd_layout_var(a.B, a.T, a.H, DK, a.DV) : bwd_layout(a.B, a.T, a.H, DK, a.DV);
     char* ws = static_cast<char*>(a.workspace);
     const int BH = a.B * a.H, nch = (a.T + CH - 1) / CH;
+    const long ring = VAR ? varlen_chunk_bound(a.B, a.T) : 0;  // chunk slots per head (packed)
+    VarTab vt;
+    if constexpr (VAR) {
+        vt.coff = reinterpret_cast<const int*>(ws);
+        vt.start = vt.coff + a.B + 1;
+        vt.len = vt.start + a.B;
+        vt.n = a.B;
+    }
     char* blobs = ws + L.blobs;
     float* S_save = reinterpret_cast<float*>(ws + L.S_save);
     float* G_save = reinterpret_cast<float*>(ws + L.G_save);
@@ -1120,25 +1201,37 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
     float* dAm = reinterpret_cast<float*>(ws + L.dAm);
     float* dgam = reinterpret_cast<float*>(ws + L.dgam);
 
-    const ChunkArgs fa{a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, nullptr, nullptr, a.B, a.T, a.H, DK, a.DV,
-                       true, (uint32_t)PRO << 2, nullptr, 0};
-    hipError_t e = launch_split_states(fa, blobs, S_save, Dp, Dl, st);
+    ChunkArgs fa{a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, nullptr, nullptr, a.B, a.T, a.H, DK, a.DV,
+                 true, (uint32_t)PRO << 2, nullptr, 0};
+    fa.cu_seqlens = a.cu_seqlens;
+    hipError_t e = VAR ? launch_varlen_states(fa, ws, blobs, ring, S_save, Dp, Dl, st)
+                       : launch_split_states(fa, blobs, S_save, Dp, Dl, st);
     if (e != hipSuccess) return e;
 
     constexpr int DVT = DK < 64 ? DK : 64;
-    const ChainBwdIO cio{a.v, a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0,
-                         a.B, a.T, a.H, a.DV, nch};
-    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0>), dim3((BH + 7) / 8 * 8 * (a.DV / DVT)),
-                       dim3(bwd_chain_threads<DK>()), 0,
-                       st, cio);
-    const ContractIO xio{a.dO, Dp, Dl, dDl, dDp, S_save, G_save, blobs, dQh, dEh, dKb, dPm, dAm, dgam,
-                         a.B, a.T, a.H, a.DV, nch};
-    hipLaunchKernelGGL((bwd_contract_kernel<DK>), dim3(BH * nch), dim3(256), 0, st, xio);
-    const KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
-                    a.B, a.T, a.H, nch};
-    hipLaunchKernelGGL((bwd_key_kernel<DK, PRO>), dim3((BH * nch + 7) / 8 * 8 * (DK / 32)), dim3(256), 0, st, kio);
+    ChainBwdIO cio{a.v, a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0,
+                   a.B, a.T, a.H, a.DV, nch};
+    cio.var = vt;
+    cio.ring = ring;
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0, VAR>), dim3((BH + 7) / 8 * 8 * (a.DV / DVT)),
+                       dim3(bwd_chain_threads<DK>()), 0, st, cio);
+    // per-chunk kernels: b*h*chunks workgroups, or h * the chunk bound of a packed batch (the ones
+    // past the true chunk count leave at once)
+    const long items = VAR ? (long)a.H * ring : (long)BH * nch;
+    if (items == 0) return hipGetLastError();
+    ContractIO xio{a.dO, Dp, Dl, dDl, dDp, S_save, G_save, blobs, dQh, dEh, dKb, dPm, dAm, dgam,
+                   a.B, a.T, a.H, a.DV, nch};
+    xio.var = vt;
+    xio.ring = ring;
+    hipLaunchKernelGGL((bwd_contract_kernel<DK, VAR>), dim3((unsigned)items), dim3(256), 0, st, xio);
+    KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
+              a.B, a.T, a.H, nch};
+    kio.var = vt;
+    kio.ring = ring;
+    hipLaunchKernelGGL((bwd_key_kernel<DK, PRO, VAR>), dim3((unsigned)((items + 7) / 8 * 8 * (DK / 32))), dim3(256), 0,
+                       st, kio);
     if constexpr ((PRO & 1) != 0) {  // dq, dk through the L2 norm
-        const long rows = (long)a.B * a.T * a.H;
+        const long rows = (VAR ? 1l : (long)a.B) * a.T * a.H;
         const dim3 grid((unsigned)((rows + 3) / 4));
         hipLaunchKernelGGL(l2norm_bwd, grid, dim3(256), 0, st, a.dq, static_cast<const uint16_t*>(a.q), rnq, rows, DK);
         hipLaunchKernelGGL(l2norm_bwd, grid, dim3(256), 0, st, a.dk, static_cast<const uint16_t*>(a.k), rnk, rows, DK);
@@ -1154,9 +1247,8 @@ struct ScalarLayout {
     size_t alpha, b, w, dalpha, db, dw, rnq, rnk, total;
 };
 
-ScalarLayout scalar_layout(size_t base, int B, int T, int H, int DK, int DV, uint32_t flags) {
+ScalarLayout scalar_layout(size_t base, size_t rows, int DK, int DV, uint32_t flags) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t rows = (size_t)B * T * H;
     const bool as = (flags & 1u) != 0, bs = (flags & 2u) != 0;
     ScalarLayout L{};
     size_t o = base;
@@ -1190,7 +1282,12 @@ bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags) {
 
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags) {
     const size_t base = bwd_layout(B, T, H, DK, DV).total;
-    return (flags & 7u) ? scalar_layout(base, B, T, H, DK, DV, flags).total : base;
+    return (flags & 7u) ? scalar_layout(base, (size_t)B * T * H, DK, DV, flags).total : base;
+}
+
+size_t bwd_varlen_workspace_bytes(int n, int T, int H, int DK, int DV, uint32_t flags) {
+    const size_t base = bwd_layout_var(n, T, H, DK, DV).total;
+    return (flags & 7u) ? scalar_layout(base, (size_t)T * H, DK, DV, flags).total : base;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
@@ -1201,14 +1298,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(copy_or_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dS0, a.dS_T, n);
         return hipGetLastError();
     }
-    if (!a.workspace || a.workspace_bytes < bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags))
-        return hipErrorInvalidValue;
+    const bool var = a.cu_seqlens != nullptr;  // packed batch: a.B sequences, a.T rows in all
+    const size_t need = var ? bwd_varlen_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags)
+                            : bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags);
+    if (!a.workspace || a.workspace_bytes < need) return hipErrorInvalidValue;
     BwdArgs g = a;  // the general-gate call
     const bool as = (a.flags & 1u) != 0, bs = (a.flags & 2u) != 0, l2n = (a.flags & 4u) != 0;
-    const ScalarLayout L = scalar_layout(bwd_layout(a.B, a.T, a.H, a.DK, a.DV).total, a.B, a.T, a.H, a.DK, a.DV,
-                                         a.flags);
+    const long rows = (var ? 1l : (long)a.B) * a.T * a.H;  // token rows
+    const size_t base = var ? bwd_layout_var(a.B, a.T, a.H, a.DK, a.DV).total : bwd_layout(a.B, a.T, a.H, a.DK, a.DV).total;
+    const ScalarLayout L = scalar_layout(base, (size_t)rows, a.DK, a.DV, a.flags);
     char* ws = static_cast<char*>(a.workspace);
-    const long rows = (long)a.B * a.T * a.H;
     float* rnq = nullptr;
     float* rnk = nullptr;
     if (l2n) {  // the reciprocal row norms of q and k, as the forward takes them
@@ -1239,10 +1338,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     }
     auto go = [&](auto pro) -> hipError_t {
         constexpr int PRO = decltype(pro)::value;
+        if (var) {
+            switch (a.DK) {
+                case 32: return launch_bwd_t<32, PRO, true>(g, rnq, rnk, s);
+                case 64: return launch_bwd_t<64, PRO, true>(g, rnq, rnk, s);
+                default: return launch_bwd_t<128, PRO, true>(g, rnq, rnk, s);
+            }
+        }
         switch (a.DK) {
-            case 32: return launch_bwd_t<32, PRO>(g, rnq, rnk, s);
-            case 64: return launch_bwd_t<64, PRO>(g, rnq, rnk, s);
-            default: return launch_bwd_t<128, PRO>(g, rnq, rnk, s);
+            case 32: return launch_bwd_t<32, PRO, false>(g, rnq, rnk, s);
+            case 64: return launch_bwd_t<64, PRO, false>(g, rnq, rnk, s);
+            default: return launch_bwd_t<128, PRO, false>(g, rnq, rnk, s);
         }
     };
     hipError_t e;

@@ -98,16 +98,6 @@ struct PrepSmem {
 
 // PRO (prologue): bit 0, q and k are L2-normalised over d_k per token here; bit 1, alpha and b
 // (or beta) arrive as pre-activations: log2 alpha = log2 sigma(x), b = sigma(x).
-// Packed (ragged) batch: sequence s holds token rows [start[s], start[s] + len[s]) of the packed
-// inputs and chunks [coff[s], coff[s + 1]) of the batch; n sequences. Built on the device from
-// the caller's cumulative sequence lengths.
-struct VarTab {
-    const int* coff = nullptr;
-    const int* start = nullptr;
-    const int* len = nullptr;
-    int n = 0;
-};
-
 // VAR: packed batch (vt); workgroup x = (chunk of the batch) * H + h, grid an upper bound on the
 // chunk count; blocks [h][chunk of the batch] with n_count slots per head. Otherwise workgroup
 // x = (chunk - n_first) * B*H + b*H + h over equal-length sequences of T tokens.
@@ -144,15 +134,7 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
         bh = blockIdx.x % H;
         nc = blockIdx.x / H;
         if (nc >= vt.coff[vt.n]) return;
-        int lo = 0, hi = vt.n - 1;  // the last sequence whose first chunk is at most nc
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (vt.coff[mid] <= nc) {
-                lo = mid;
-            } else {
-                hi = mid - 1;
-            }
-        }
+        const int lo = varlen_seq_of(vt, nc);
         n = nc - vt.coff[lo];
         tbase = vt.start[lo];
         Tq = vt.len[lo];
@@ -673,6 +655,7 @@ chain_kernel(const ChainIO io) {
     int c_begin, c_end, Tq;
     long tbase;
     const char* blobs;
+    size_t save_base;  // chunk slot of the saves (SAVE): chunk n of this sequence is save_base + n
     if constexpr (VAR) {
         const int sq = bh / H, cf = io.var.coff[sq];
         c_begin = 0;
@@ -680,12 +663,14 @@ chain_kernel(const ChainIO io) {
         tbase = io.var.start[sq];
         Tq = io.var.len[sq];
         blobs = io.ws + ((size_t)hh * io.ring + cf) * BL::bytes;
+        save_base = (size_t)hh * io.ring + cf;
     } else {
         c_begin = io.first + seg * io.seg_len;
         c_end = min(c_begin + io.seg_len, io.end);
         tbase = (long)(bh / H) * T;
         Tq = T;
         blobs = io.ws + ((size_t)bh * io.ring + (c_begin - io.first)) * BL::bytes;
+        save_base = (size_t)bh * io.save_nch;
     }
     const int n_count = c_end - c_begin;
     if (!VAR && n_count <= 0) return;
@@ -814,7 +799,7 @@ chain_kernel(const ChainIO io) {
             }
             if constexpr (SAVE) {
                 // the state at the start of this chunk, for the backward pass
-                float* sv = io.S_save + ((size_t)bh * io.save_nch + n) * DK * DV;
+                float* sv = io.S_save + (save_base + n) * DK * DV;
 #pragma unroll
                 for (int c = 0; c < NT; ++c)
 #pragma unroll

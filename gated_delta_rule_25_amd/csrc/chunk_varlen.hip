@@ -95,6 +95,38 @@ hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The backward's forward pass over a packed batch: the sequence table (at `table`), prep into
+// `blobs` ([h][chunk of the batch], `ring` slots per head) and the state-only chain with saves:
+// the start state of every chunk ([h][chunk of the batch][DK][DV]) and the rows of D' and Delta
+// (fp16, packed rows). bf16, general gates, the prologue flags PRO.
+template <int DK, int PRO>
+hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, long ring, float* S_save,
+                                  uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t st) {
+    constexpr int DVT = DK < 64 ? DK : 64;
+    const int N = a.B;
+    VarTab vt;
+    vt.coff = reinterpret_cast<int*>(table);
+    vt.start = vt.coff + N + 1;
+    vt.len = vt.start + N;
+    vt.n = N;
+    hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, N, a.T, const_cast<int*>(vt.coff),
+                       const_cast<int*>(vt.start), const_cast<int*>(vt.len));
+    if (ring > 0)
+        hipLaunchKernelGGL((prep_kernel<DK, true, false, false, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0,
+                           st, a.q, a.k, a.alpha, a.b, 1, a.T, a.H, 0, (int)ring, blobs, vt);
+    const long ld = DK;
+    ChainIO io{a.v, a.w, nullptr, blobs, (int)ring, 0, 0, 0, 1, N, a.T, a.H, a.DV,
+               a.S0, ld * a.DV, 0, a.DV, nullptr, 0, 0, a.DV, 0};
+    io.var = vt;
+    io.S_save = S_save;
+    io.Dp_save = Dp_save;
+    io.Dl_save = Dl_save;
+    const int BH = N * a.H, BHp = (BH + 7) / 8 * 8;
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true, (PRO & 2) != 0, true>),
+                       dim3(BHp * (a.DV / DVT)), dim3(kChainThreads), 0, st, io);
+    return hipGetLastError();
+}
+
 template <int DK, bool BF16, int PRO>
 hipError_t launch_varlen_gates(const ChunkArgs& a, hipStream_t s) {
     switch (a.flags & 3u) {
@@ -126,6 +158,26 @@ size_t varlen_table_bytes(int n) { return ((size_t)(3 * (size_t)n + 1) * 4 + 255
 
 size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16) {
     return varlen_table_bytes(n) + (size_t)varlen_chunk_bound(n, T) * split_chunk_bytes(1, H, DK, bf16);
+}
+
+hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, float* S_save,
+                                uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t s) {
+    if (!a.bf16 || (a.flags & ~12u) != 0u || !a.cu_seqlens || !split_supported(a.T, a.H, a.DK, a.DV, true))
+        return hipErrorNotSupported;
+    auto go = [&](auto pro) -> hipError_t {
+        constexpr int PRO = decltype(pro)::value;
+        switch (a.DK) {
+            case 32: return launch_varlen_states_t<32, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            case 64: return launch_varlen_states_t<64, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            default: return launch_varlen_states_t<128, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+        }
+    };
+    switch ((a.flags >> 2) & 3u) {
+        case 0: return go(std::integral_constant<int, 0>());
+        case 1: return go(std::integral_constant<int, 1>());
+        case 2: return go(std::integral_constant<int, 2>());
+        default: return go(std::integral_constant<int, 3>());
+    }
 }
 
 hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s) {

@@ -122,6 +122,64 @@ gdn2_status run_recurrent(const void* q, const void* k, const void* v, const voi
     return gdn2::launch_recurrent(a, s) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+// The backward's checks and launch. cu == nullptr: B sequences of T tokens. Otherwise a packed
+// batch: B sequences delimited by cu (device), T rows in all ([T, H, d] rows, [B, H, d_k, d_v]
+// states).
+gdn2_status run_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                    const void* w, const float* S0, const float* dO, const float* dS_T, float* dq,
+                    float* dk, float* dv, float* dalpha, float* db, float* dw, float* dS0,
+                    const int32_t* cu, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                    gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (in_dtype != GDN2_BF16 ||
+        (gate_flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR | GDN2_QK_L2NORM | GDN2_GATE_LOGITS)) != 0u)
+        return GDN2_ERR_UNSUPPORTED;
+    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
+    if (bs && (w || dw)) return GDN2_ERR_UNSUPPORTED;  // w is implied by beta; dbeta goes to db
+    if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN2_ERR_UNSUPPORTED;
+    const int32_t Brow = cu ? 1 : B;  // sequences along the row axis
+    Sizes sz, st;
+    if (!sizes_of(Brow, T, H, d_k, d_v, &sz) || !sizes_of(B, 1, H, d_k, d_v, &st)) return GDN2_ERR_SHAPE;
+    if (cu ? gdn2::varlen_chunk_bound(B, T) * H * (d_k / 32) * 256 >= (1l << 31) : !chunk_grids_ok(B, T, H, d_k))
+        return GDN2_ERR_SHAPE;
+    if (!gdn2::bwd_supported(T, H, d_k, d_v, true, gate_flags)) return GDN2_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !alpha || !b || (!bs && !w) || !dO || !dq || !dk || !dv || !dalpha || !db ||
+                  (!bs && !dw)))
+        return GDN2_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
+    size_t need = 0;
+    if (T > 0) {
+        need = cu ? gdn2::bwd_varlen_workspace_bytes(B, T, H, d_k, d_v, gate_flags)
+                  : gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v, gate_flags);
+        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+    }
+    const uint64_t na = as ? sz.scalar : sz.qk, nb = bs ? sz.scalar : sz.qk;  // alpha, b elements
+    const Range ins[] = {range_of(q, sz.qk * 2), range_of(k, sz.qk * 2), range_of(v, sz.vw * 2),
+                         range_of(alpha, na * 2), range_of(b, nb * 2), range_of(w, sz.vw * 2),
+                         range_of(S0, st.state * 4), range_of(dO, sz.vw * 4), range_of(dS_T, st.state * 4),
+                         range_of(cu, cu ? ((uint64_t)B + 1) * 4 : 0)};
+    const Range outs[] = {range_of(dq, sz.qk * 4), range_of(dk, sz.qk * 4), range_of(dalpha, na * 4),
+                          range_of(db, nb * 4), range_of(dv, sz.vw * 4), range_of(dw, sz.vw * 4),
+                          range_of(dS0, st.state * 4), range_of(T > 0 ? workspace : nullptr, need)};
+    const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+    for (int i = 0; i < nout; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    gdn2::BwdArgs a{q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
+                    B, T, H, d_k, d_v, true, gate_flags, workspace, workspace_bytes};
+    a.cu_seqlens = cu;
+    const hipError_t e = gdn2::launch_bwd(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,47 +356,30 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const vo
                            float* db, float* dw, float* dS0, int32_t B, int32_t T, int32_t H,
                            int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    if (in_dtype != GDN2_BF16 ||
-        (gate_flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR | GDN2_QK_L2NORM | GDN2_GATE_LOGITS)) != 0u)
-        return GDN2_ERR_UNSUPPORTED;
-    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
-    if (bs && (w || dw)) return GDN2_ERR_UNSUPPORTED;  // w is implied by beta; dbeta goes to db
-    if (B <= 0 || H <= 0 || T < 0) return GDN2_ERR_SHAPE;
-    if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN2_ERR_UNSUPPORTED;
+    return run_bwd(q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0, nullptr, B, T, H, d_k, d_v,
+                   in_dtype, gate_flags, workspace, workspace_bytes, stream);
+}
+
+gdn2_status gdn2_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                                  const void* b, const void* w, const float* S0, const float* dO,
+                                  const float* dS_T, float* dq, float* dk, float* dv, float* dalpha,
+                                  float* db, float* dw, float* dS0, const int32_t* cu_seqlens, int32_t N,
+                                  int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                  gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_ERR_ALIGN;
+    return run_bwd(q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0, cu_seqlens, N, T_total, H,
+                   d_k, d_v, in_dtype, gate_flags, workspace, workspace_bytes, stream);
+}
+
+size_t gdn2_chunk_bwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                             gdn2_dtype in_dtype, uint32_t gate_flags) {
+    if (N <= 0 || H <= 0 || T_total <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    if (!gdn2::bwd_supported(T_total, H, d_k, d_v, in_dtype == GDN2_BF16, gate_flags)) return 0;
     Sizes sz;
-    if (!sizes_of(B, T, H, d_k, d_v, &sz) || !chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
-    if (!gdn2::bwd_supported(T, H, d_k, d_v, true, gate_flags)) return GDN2_ERR_UNSUPPORTED;
-    if (T > 0 && (!q || !k || !v || !alpha || !b || (!bs && !w) || !dO || !dq || !dk || !dv || !dalpha || !db ||
-                  (!bs && !dw)))
-        return GDN2_ERR_NULL;
-    const void* ptrs[] = {q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
-    size_t need = 0;
-    if (T > 0) {
-        need = gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v, gate_flags);
-        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
-    }
-    const uint64_t na = as ? sz.scalar : sz.qk, nb = bs ? sz.scalar : sz.qk;  // alpha, b elements
-    const Range ins[] = {range_of(q, sz.qk * 2), range_of(k, sz.qk * 2), range_of(v, sz.vw * 2),
-                         range_of(alpha, na * 2), range_of(b, nb * 2), range_of(w, sz.vw * 2),
-                         range_of(S0, sz.state * 4), range_of(dO, sz.vw * 4), range_of(dS_T, sz.state * 4)};
-    const Range outs[] = {range_of(dq, sz.qk * 4), range_of(dk, sz.qk * 4), range_of(dalpha, na * 4),
-                          range_of(db, nb * 4), range_of(dv, sz.vw * 4), range_of(dw, sz.vw * 4),
-                          range_of(dS0, sz.state * 4), range_of(T > 0 ? workspace : nullptr, need)};
-    const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
-    for (int i = 0; i < nout; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
-        for (int j = i + 1; j < nout; ++j)
-            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
-    }
-    gdn2::BwdArgs a{q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
-                    B, T, H, d_k, d_v, true, gate_flags, workspace, workspace_bytes};
-    const hipError_t e = gdn2::launch_bwd(a, static_cast<hipStream_t>(stream));
-    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
-    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    if (!sizes_of(1, T_total, H, d_k, d_v, &sz)) return 0;
+    return gdn2::bwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, gate_flags);
 }
 
 const char* gdn2_status_str(gdn2_status s) {

@@ -54,6 +54,13 @@ hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s);
 long varlen_chunk_bound(int n, int T);
 size_t varlen_table_bytes(int n);
 size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16);
+// The backward's forward pass over a packed batch (a.B sequences, a.T rows, a.cu_seqlens): the
+// sequence table into `table` (varlen_table_bytes), the operand blocks into `blobs` ([h][chunk of
+// the batch], `ring` = varlen_chunk_bound slots per head), the start state of every chunk
+// ([h][chunk of the batch][DK][DV] fp32) and the rows of D' and Delta (fp16, packed rows). bf16
+// inputs, general gates, the prologue flags allowed.
+hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, float* S_save,
+                                uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t s);
 // Prep over every chunk into `blobs` ([b*h][chunk] operand blocks), then the state-only chain in
 // order, saving the state at the start of every chunk ([b*h][chunk][DK][DV]) and the rows of D'
 // and Delta ([B, T, H, DV], fp16 bits). bf16 inputs, general gates, the prologue flags allowed.
@@ -70,9 +77,12 @@ struct BwdArgs {
     uint32_t flags;
     void* workspace;
     size_t workspace_bytes;
+    const int* cu_seqlens = nullptr;  // packed batch: B + 1 cumulative lengths (device), T = rows
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags);
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags);
+// The same for a packed batch of n sequences, T rows in all.
+size_t bwd_varlen_workspace_bytes(int n, int T, int H, int DK, int DV, uint32_t flags);
 
 }  // namespace gdn2

@@ -186,6 +186,17 @@ def make_cotangents(wl: Workload, *, device: str = "cpu", final_state: bool = Tr
                 dS_T=None if dS is None else torch.from_numpy(dS).to(device))
 
 
+def make_packed_cotangents(wl: Workload, lengths, *, device: str = "cpu", final_state: bool = True) -> dict:
+    """Cotangents for a packed batch (make_packed_inputs): dO [sum(lengths), H, d_v] and dS_T
+    [N, H, d_k, d_v] (or None), standard normal float32 from their own stream (seed + 7919)."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 7919))
+    f32 = np.float32
+    dO = rng.standard_normal((int(sum(lengths)), wl.H, wl.d_v), dtype=f32)
+    dS = rng.standard_normal((len(lengths), wl.H, wl.d_k, wl.d_v), dtype=f32) if final_state else None
+    return dict(dO=torch.from_numpy(dO).to(device),
+                dS_T=None if dS is None else torch.from_numpy(dS).to(device))
+
+
 def make_decode_inputs(B: int, H: int, d_k: int, d_v: int, steps: int, *, seed: int,
                        alpha_mu: float = 3.0, s0_std: float = 0.1, dtype: str = "bf16",
                        device: str = "cpu", generator: str = "numpy") -> dict:

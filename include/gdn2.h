@@ -243,6 +243,42 @@ size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
                                       gdn2_dtype in_dtype, uint32_t gate_flags);
 
 /*
+ * Backward of gdn2_chunk_fwd_varlen: the gradients of L = sum over the packed rows of <dO, o> plus
+ * sum over the sequences of <dS_T[s], S_T[s]>, for N sequences packed along the token axis and
+ * delimited by cu_seqlens (device memory, read as by gdn2_chunk_fwd_varlen: clamped to
+ * [0, T_total] and made non-decreasing). Each sequence is its own recurrence from S0[s], chunked
+ * from its own first token [GDN2-summary, paragraph "Реализация"], so its gradients are those
+ * gdn2_chunk_bwd gives for it alone.
+ *
+ *   inputs   q, k, alpha, b [T_total, H, d_k]; v, w [T_total, H, d_v] (scalar gates [T_total, H],
+ *            w == NULL with GDN2_BETA_SCALAR); S0 [N, H, d_k, d_v] float32 (NULL = zeros);
+ *            dO [T_total, H, d_v] float32; dS_T [N, H, d_k, d_v] float32 (NULL = zeros)
+ *   outputs  dq, dk, dalpha, db [T_total, H, d_k] (scalar gates [T_total, H]); dv, dw
+ *            [T_total, H, d_v]; dS0 [N, H, d_k, d_v] (NULL = not stored). Rows inside a sequence
+ *            are overwritten; rows that bounds out of order leave outside every sequence are not
+ *            written. A sequence without tokens gets dS0[s] = dS_T[s].
+ *   workspace  required when T_total > 0, 256-byte aligned, at least
+ *            gdn2_chunk_bwd_varlen_workspace_bytes: the sequence table and the blocks of
+ *            gdn2_chunk_bwd for (T_total + 63 N) / 64 chunks per head, which bounds the chunk count.
+ *
+ * Gate forms, prologue flags, supported sizes (T_total in place of T), arithmetic and errors as
+ * for gdn2_chunk_bwd; in addition GDN2_ERR_NULL without cu_seqlens and GDN2_ERR_ALIGN for a
+ * cu_seqlens not 4-byte aligned.
+ */
+gdn2_status gdn2_chunk_bwd_varlen(const void *q, const void *k, const void *v, const void *alpha,
+                                  const void *b, const void *w, const float *S0, const float *dO,
+                                  const float *dS_T, float *dq, float *dk, float *dv, float *dalpha,
+                                  float *db, float *dw, float *dS0, const int32_t *cu_seqlens,
+                                  int32_t N, int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                  gdn2_dtype in_dtype, uint32_t gate_flags, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Workspace bytes gdn2_chunk_bwd_varlen needs at these sizes; 0 when it does not take them (or
+ * T_total == 0, which needs none). */
+size_t gdn2_chunk_bwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t H, int32_t d_k,
+                                             int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
+
+/*
  * One decode step over a pool of states (serving: the batch rows name their sequences' slots).
  * Batch row b (inputs q, k, v, alpha, b, w and output o as in gdn2_decode_step, [B, H, d]) updates
  * S_pool[slots[b]] in place, S_pool being [n_slots, H, d_k, d_v] float32, and writes o[b]. slots

@@ -202,3 +202,37 @@ def test_bwd_gate_forms_on_the_host(lib):
     assert f(*far[:16], B, T, H, 64, 64, 0, 16, ws, 1 << 30, None) == 3          # unknown flag
     assert q(B, T, H, 64, 64, 0, 3) > q(B, T, H, 64, 64, 0, 1) > q(B, T, H, 64, 64, 0, 0) > 0
     assert q(B, T, H, 64, 64, 0, 4) > q(B, T, H, 64, 64, 0, 0) == q(B, T, H, 64, 64, 0, 8)
+
+
+def test_bwd_varlen_rejects_bad_arguments(lib):
+    # every call below is refused on the host before any launch
+    far = [P((1 << 40) * (i + 1)) for i in range(16)]
+    cu = P((1 << 40) * 17)
+    ws = P((1 << 40) * 20)
+    f = lib.gdn2_chunk_bwd_varlen
+    qs = lib.gdn2_chunk_bwd_varlen_workspace_bytes
+    need = qs(4, 1000, 2, 128, 128, 0, 0)
+    assert need > 0
+    assert qs(8, 1000, 2, 128, 128, 0, 0) > need       # more sequences: a larger chunk bound
+    assert qs(4, 1000, 2, 128, 128, 0, 3) > need       # scalar gates: repeated gates and gradients
+    assert qs(4, 1000, 2, 128, 128, 1, 0) == 0         # fp32 inputs
+    assert qs(0, 1000, 2, 128, 128, 0, 0) == 0
+    assert qs(4, 0, 2, 128, 128, 0, 0) == 0            # no rows: no workspace
+
+    def call(ptrs=far, cu=cu, N=4, T=1000, H=2, dk=128, dv=128, dt=0, flags=0, ws=ws, wsb=need):
+        return f(*ptrs, cu, N, T, H, dk, dv, dt, flags, ws, wsb, None)
+
+    assert call(N=0) == 2
+    assert call(T=-1) == 2
+    assert call(cu=None) == 1
+    assert call(cu=P((1 << 40) * 17 + 2)) == 4
+    assert call(ws=None) == 7
+    assert call(wsb=need - 1) == 7
+    assert call(ws=P((1 << 40) * 20 + 128)) == 4        # workspace not 256-byte aligned
+    assert call(dk=256, dv=256) == 3
+    assert call(dt=1) == 3
+    assert call(flags=16) == 3
+    assert call(flags=2) == 3                           # scalar beta with w and dw given
+    assert call(cu=far[9]) == 5                         # cu_seqlens overlaps dq
+    assert call(ws=far[12]) == 5                        # workspace over db
+    assert call(N=32, T=64 * 1024 * 32, H=64, wsb=1 << 45) == 2  # grid past 2^31 threads

@@ -1,0 +1,190 @@
+"""GPU parity: the backward of the packed prefill (gdn2_chunk_bwd_varlen) against the fp64
+oracle's backward run on each sequence alone.
+
+Every sequence of the packed batch is its own recurrence from its own initial state, so its
+gradients are the oracle's backward of [1, L, H, d] slices of the packed rows with its own S0,
+dO rows and dS_T. Bar: normwise relative error at most 2e-3 on every gradient (the bf16 bar of
+the batched backward). A sequence without tokens passes dS_T through to dS0 unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import banner, normwise_err
+from gated_delta_rule_25_amd.inputs import (WORKLOADS, make_packed_cotangents, make_packed_inputs,
+                                            packed_lengths, scaled)
+
+pytestmark = pytest.mark.gpu
+
+TOLB = 2e-3
+INS = ("q", "k", "v", "alpha", "b", "w")
+
+
+def _g():
+    import gated_delta_rule_25_amd as g
+    return g
+
+
+def _cuda(x):
+    return None if x is None else x.cuda()
+
+
+def _ref_seq(ins, cot, lo, hi, s, heads=None, l2n=False, gl=False):
+    """Oracle gradients of sequence s (rows lo..hi-1) alone, for the heads `heads` (a slice)."""
+    hs = slice(None) if heads is None else heads
+    x = {n: (None if ins[n] is None else ins[n][lo:hi, hs].unsqueeze(0)) for n in INS}
+    S0 = None if ins["S0"] is None else ins["S0"][s:s + 1, hs]
+    dS = None if cot["dS_T"] is None else cot["dS_T"][s:s + 1, hs]
+    dO = cot["dO"][lo:hi, hs].unsqueeze(0)
+    q, k, a, b, w = x["q"], x["k"], x["alpha"], x["b"], x["w"]
+    if l2n or gl:
+        q, k, a, b, w = oracle.prologue(q, k, a, b, w, l2norm=l2n, gate_logits=gl)
+    dk, dv = q.shape[-1], x["v"].shape[-1]
+    ag, bg, wg = a, b, w
+    if ins["alpha_scalar"] or ins["beta_scalar"]:  # scalars as [..., 1]: unambiguous at one head
+        sc = lambda x, on: (x.double().numpy() if torch.is_tensor(x) else np.asarray(x))[..., None] if on else x
+        ag, bg, wg = oracle.broadcast_gates(sc(a, ins["alpha_scalar"]), sc(b, ins["beta_scalar"]), w, dk, dv,
+                                            alpha_scalar=ins["alpha_scalar"],
+                                            beta_scalar=ins["beta_scalar"])
+    ref = oracle.backward(q, k, x["v"], ag, bg, wg, S0, dO, dS)
+    grads = dict(dq=ref["dq"], dk=ref["dk"],
+                 dalpha=np.asarray(ref["dalpha"]).sum(-1) if ins["alpha_scalar"] else ref["dalpha"])
+    if ins["beta_scalar"]:
+        grads["db"] = np.asarray(ref["db"]).sum(-1) + np.asarray(ref["dw"]).sum(-1)
+    else:
+        grads.update(db=ref["db"], dw=ref["dw"])
+    if l2n or gl:
+        grads = oracle.prologue_backward(x["q"], x["k"], x["alpha"], x["b"], x["w"], grads,
+                                         l2norm=l2n, gate_logits=gl)
+    grads.update(dv=ref["dv"], dS0=ref["dS0"])
+    return {n: np.asarray(v)[0] for n, v in grads.items()}
+
+
+def _run(ins, cot, **kw):
+    d = {n: _cuda(ins[n]) for n in INS + ("S0",)}
+    out = _g().chunk_bwd_varlen(*(d[n] for n in INS), ins["cu_seqlens"].cuda(), d["S0"], _cuda(cot["dO"]),
+                                _cuda(cot["dS_T"]), **kw)
+    torch.cuda.synchronize()
+    return {n: v.cpu() for n, v in out.items()}
+
+
+def _check(ins, cot, got, seqs=None, heads=None, l2n=False, gl=False):
+    cu = ins["cu_seqlens"].tolist()
+    hs = slice(None) if heads is None else heads
+    worst = {}
+    for s in (range(len(cu) - 1) if seqs is None else seqs):
+        lo, hi = cu[s], cu[s + 1]
+        if hi == lo:  # no tokens: dS0 = dS_T (zeros without one)
+            exp = torch.zeros_like(got["dS0"][s]) if cot["dS_T"] is None else cot["dS_T"][s]
+            assert torch.equal(got["dS0"][s][hs], exp[hs]), s
+            continue
+        ref = _ref_seq(ins, cot, lo, hi, s, heads, l2n, gl)
+        for n, r in ref.items():
+            x = got[n][s][hs] if n == "dS0" else got[n][lo:hi, hs]
+            e = normwise_err(x, r)
+            worst[n] = max(worst.get(n, 0.0), e)
+            assert e <= TOLB, (s, lo, hi, n, e)
+    print("  worst " + "  ".join(f"{n} {e:.2e}" for n, e in worst.items()), flush=True)
+
+
+MIX = [0, 1, 63, 64, 65, 200, 0, 130, 17, 257]
+CASES = [
+    ("d128_general", scaled(WORKLOADS["prefill_1p3b"], H=2), MIX),
+    ("d64_general", scaled(WORKLOADS["prefill_1p3b"], H=3, d_k=64, d_v=64), [5, 0, 128, 300]),
+    ("d32_general", scaled(WORKLOADS["prefill_1p3b"], H=2, d_k=32, d_v=32), [70, 1, 190]),
+    ("gdn", scaled(WORKLOADS["gdn_scalar"], H=2), [100, 64, 0, 3]),
+    ("kda", scaled(WORKLOADS["kda_scalar"], H=2), [3, 150, 0]),
+    ("zero_S0", scaled(WORKLOADS["prefill_1p3b"], H=2, s0_std=0.0), [90, 40]),
+]
+
+
+@pytest.mark.parametrize("name,wl,lengths", CASES, ids=[c[0] for c in CASES])
+def test_bwd_varlen_matches_oracle_per_sequence(name, wl, lengths):
+    banner(f"bwd varlen {name} lengths={lengths} {wl}")
+    ins = make_packed_inputs(wl, lengths)
+    cot = make_packed_cotangents(wl, lengths)
+    _check(ins, cot, _run(ins, cot))
+
+
+def test_bwd_varlen_without_final_state_cotangent():
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=2)
+    lengths = [40, 0, 150]
+    banner(f"bwd varlen, dS_T = None, lengths={lengths}")
+    ins = make_packed_inputs(wl, lengths)
+    cot = make_packed_cotangents(wl, lengths, final_state=False)
+    _check(ins, cot, _run(ins, cot))
+
+
+@pytest.mark.parametrize("gates,l2n,gl", [("prefill_1p3b", True, True), ("prefill_1p3b", False, True),
+                                          ("gdn_scalar", True, True)])
+def test_bwd_varlen_prologue(gates, l2n, gl):
+    wl = scaled(WORKLOADS[gates], H=2)
+    lengths = [70, 0, 129, 5]
+    banner(f"bwd varlen prologue {gates} l2norm={l2n} logits={gl} lengths={lengths}")
+    ins = make_packed_inputs(wl, lengths, raw=True)
+    if not l2n:  # the kernel normalises nothing: hand it unit keys and queries
+        q, k, _, _, _ = oracle.prologue(ins["q"], ins["k"], ins["alpha"], ins["b"], ins["w"],
+                                        l2norm=True, gate_logits=False)
+        ins["q"], ins["k"] = (torch.from_numpy(np.asarray(x)).to(torch.bfloat16) for x in (q, k))
+    cot = make_packed_cotangents(wl, lengths)
+    _check(ins, cot, _run(ins, cot, l2norm=l2n, gate_logits=gl), l2n=l2n, gl=gl)
+
+
+def test_bwd_varlen_equal_lengths_equal_the_batched_call():
+    # N sequences of one length packed: the same per-chunk arithmetic as chunk_bwd with B = N
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=3)
+    N, L = 4, 200
+    banner(f"bwd varlen vs batched, N={N} L={L}")
+    ins = make_packed_inputs(wl, [L] * N)
+    cot = make_packed_cotangents(wl, [L] * N)
+    got = _run(ins, cot)
+    d = {n: ins[n].reshape(N, L, *ins[n].shape[1:]).cuda() for n in INS}
+    ref = _g().chunk_bwd(*(d[n] for n in INS), ins["S0"].cuda(), cot["dO"].reshape(N, L, *cot["dO"].shape[1:]).cuda(),
+                         cot["dS_T"].cuda())
+    torch.cuda.synchronize()
+    for n, v in ref.items():
+        v = v.cpu()
+        x = got[n] if n == "dS0" else got[n].reshape(v.shape)
+        assert torch.equal(x, v), (n, (x - v).abs().max().item())
+
+
+def test_bwd_varlen_all_sequences_empty():
+    banner("bwd varlen, every sequence empty")
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=2)
+    ins = make_packed_inputs(wl, [0, 0, 0])
+    cot = make_packed_cotangents(wl, [0, 0, 0])
+    got = _run(ins, cot)
+    assert got["dq"].shape[0] == 0
+    assert torch.equal(got["dS0"], cot["dS_T"])
+
+
+def test_bwd_varlen_many_sequences():
+    # 300 sequences, lengths 0..70 with runs of empty ones, H1 d32: the sequence table spans
+    # two tiles of 256 bounds
+    rng = np.random.default_rng(131)
+    lengths = [int(x) for x in rng.integers(0, 71, 300)]
+    lengths[255] = lengths[256] = 0
+    lengths[257] = 129
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=1, d_k=32, d_v=32)
+    banner(f"bwd varlen, {len(lengths)} sequences, {sum(lengths)} rows, H1 d32")
+    ins = make_packed_inputs(wl, lengths)
+    cot = make_packed_cotangents(wl, lengths)
+    _check(ins, cot, _run(ins, cot))
+
+
+def test_bwd_varlen_full_size_sampled():
+    # 32 sequences in a length mix, 32,768 rows, 16 heads of 128 x 128; the shortest, a middle
+    # and the longest sequence checked on two heads
+    wl = WORKLOADS["prefill_1p3b"]
+    lengths = packed_lengths(32, 32768, seed=wl.seed)
+    banner("bwd varlen full size, 32 sequences, 32768 rows, H16 d128")
+    ins = make_packed_inputs(wl, lengths)
+    cot = make_packed_cotangents(wl, lengths)
+    got = _run(ins, cot)
+    for n, v in got.items():
+        assert torch.isfinite(v).all(), n
+    order = np.argsort(lengths)
+    for hh in (0, 13):
+        _check(ins, cot, got, seqs=[int(order[0]), int(order[len(order) // 2]), int(order[-1])],
+               heads=slice(hh, hh + 1))
