@@ -15,6 +15,8 @@ The readout o_t = S_t^T q_t (updated state) is a reading, not printed on the pag
 ``backward`` (reverse mode of the same recurrence) is pinned by ``tests/oracle_bwd_pins.py``
 against finite differences, a closed form, the affine dependence on S0 and automatic
 differentiation of a transition-matrix formulation.
+``rmsnorm`` / ``rmsnorm_backward`` (the output normalisation, numpy float64) are pinned by
+``tests/test_oracle_rmsnorm.py`` against closed forms, invariants and finite differences.
 Every forward function is pinned by ``tests/test_oracle_pins.py`` against a hand-worked example,
 brute-force transition products, closed forms and textbook special cases.
 """
@@ -236,3 +238,31 @@ def prologue_backward(q, k, alpha, b, w, grads: dict, *, l2norm: bool, gate_logi
                 s = sig(x)
                 out[name] = out[name] * s * (1.0 - s)
     return out
+
+
+def rmsnorm(x, weight=None, *, eps: float):
+    """The RMS normalisation the recurrent layer's output passes through (page "NVIDIA
+    представила Gated DeltaNet-2 с канал-wise гейтами …", paragraph "Архитектурно"), per row
+    over the last axis (one head's d_v outputs of one token), in float64:
+    y = x / sqrt(mean(x^2) + eps) * weight; weight None means ones.
+    """
+    x = _f64(x)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * r
+    return y if weight is None else y * _f64(weight)
+
+
+def rmsnorm_backward(x, weight, dy, *, eps: float) -> dict:
+    """Gradients of L = sum(dy * rmsnorm(x, weight)) with respect to x and weight, float64 (pinned
+    by central differences of rmsnorm() itself). With r = (mean(x^2) + eps)^(-1/2),
+    xh = x r and u = dy * weight: dx = r (u - xh mean(xh u)) per row, and dweight = the sum of
+    dy * xh over every row.
+    """
+    x, dy = _f64(x), _f64(dy)
+    g = np.ones(x.shape[-1]) if weight is None else _f64(weight)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xh = x * r
+    u = dy * g
+    dx = r * (u - xh * np.mean(xh * u, axis=-1, keepdims=True))
+    dweight = (dy * xh).reshape(-1, x.shape[-1]).sum(axis=0)
+    return dict(dx=dx, dweight=dweight)
