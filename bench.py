@@ -247,10 +247,65 @@ def backward_leg(g, steps):
     sb = ins["b"][..., 0].contiguous()
     sargs = [ins["q"], ins["k"], ins["v"], sa, sb, None, ins["S0"], cot["dO"], cot["dS_T"]]
     res["scalar_gates_ms"] = round(timed(lambda: g.chunk_bwd(*sargs), max(2, steps // 2)), 4)
+    del sa, sb, sargs
+    # packed batch: the same rows as 32 sequences in a length mix (gdn2_chunk_bwd_varlen)
+    from gated_delta_rule_25_amd.inputs import make_packed_inputs, packed_lengths
+    lengths = packed_lengths(32, B * T, seed=wl.seed)
+    pk = make_packed_inputs(wl, lengths, device="cuda")
+    pdO = cot["dO"].reshape(B * T, H, dv)
+    pdS = torch.randn(len(lengths), H, dk, dv, device="cuda")
+    pws = torch.empty(g.chunk_bwd_varlen_workspace_bytes(len(lengths), B * T, H, dk, dv), dtype=torch.uint8,
+                      device="cuda")
+    pargs = [pk[n] for n in ("q", "k", "v", "alpha", "b", "w")] + [pk["cu_seqlens"], pk["S0"], pdO, pdS]
+    res["packed_ms"] = round(timed(lambda: g.chunk_bwd_varlen(*pargs, workspace=pws), max(2, steps // 2)), 4)
+    del pk, pdO, pdS, pws, pargs
     print(f"[bench] backward: {ms:.3f} ms/call, {res['tokens_per_s']:.3e} tokens/s, {res['gbs']} GB/s "
           f"algorithmic ({100 * res['frac']:.1f}% of HBM); with the prologue {res['prologue_ms']:.3f} ms, "
-          f"scalar gates {res['scalar_gates_ms']:.3f} ms", file=sys.stderr, flush=True)
-    del ins, cot, ws, out, sa, sb, sargs
+          f"scalar gates {res['scalar_gates_ms']:.3f} ms, packed (32 sequences) {res['packed_ms']:.3f} ms",
+          file=sys.stderr, flush=True)
+    del ins, cot, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def rmsnorm_leg(g, steps):
+    """gdn2_rmsnorm_fwd / _bwd on the o of the B8 H16 T4096 d128 prefill (524,288 rows of 128
+    fp32): forward to fp32 and to bf16, backward with dweight; warm, back to back. Algorithmic
+    bytes per row: x read + y written (4 d + 4 d, or 4 d + 2 d for bf16); backward x, dy read and
+    dx written (12 d)."""
+    import torch
+    rows, d = 8 * 4096 * 16, 128
+    gen = torch.Generator(device="cuda").manual_seed(20256)
+    x = torch.randn(rows, d, device="cuda", generator=gen)
+    dy = torch.randn(rows, d, device="cuda", generator=gen)
+    w = torch.randn(d, device="cuda", generator=gen)
+    y = torch.empty_like(x)
+    y16 = torch.empty(rows, d, device="cuda", dtype=torch.bfloat16)
+    dx = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / steps
+
+    res = dict(config=f"{rows} rows x {d} fp32 (o of B8 H16 T4096)")
+    for name, fn, nbytes in (("fwd_f32", lambda: g.rmsnorm_fwd(x, w, out=y), 8 * d),
+                             ("fwd_bf16", lambda: g.rmsnorm_fwd(x, w, out=y16), 6 * d),
+                             ("bwd", lambda: g.rmsnorm_bwd(x, w, dy, dx=dx), 12 * d)):
+        ms = timed(fn)
+        gbs = nbytes * rows / (ms * 1e-3) / 1e9
+        res[name] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    print("[bench] output RMS norm: " + ", ".join(f"{n} {res[n]['ms']:.4f} ms ({res[n]['gbs']} GB/s)"
+                                                 for n in ("fwd_f32", "fwd_bf16", "bwd")),
+          file=sys.stderr, flush=True)
+    del x, dy, w, y, y16, dx
     torch.cuda.empty_cache()
     return res
 
@@ -399,6 +454,9 @@ def main(argv=None):
         packed = varlen_leg(g, 10, kern_avg)
     if not args.skip_backward and args.workload == "prefill_1p3b":
         bwd = backward_leg(g, 5)
+    norm = None
+    if not args.skip_others and args.workload == "prefill_1p3b":
+        norm = rmsnorm_leg(g, 20)
     if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
         for name, steps in (("long_prefill", 3), ("gdn_scalar", 10), ("kda_scalar", 10)):
             others[name] = prefill_leg(g, name, steps, args.impl)
@@ -454,6 +512,7 @@ def main(argv=None):
         "other_prefill": others,
         "backward": bwd,
         "packed_prefill": packed,
+        "output_rmsnorm": norm,
         "prologue": prologue,
         "decode": dec,
         "cpu_baseline": cpu,

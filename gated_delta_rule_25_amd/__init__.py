@@ -11,6 +11,7 @@ if the library is not built or no GPU is present, calls raise.
     g = chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T)    # gradients (dict: dq, dk, dv, ...)
     o, S_T = chunk_fwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0)  # packed [T_total, H, d] rows
     g = chunk_bwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0, dO, dS_T)
+    y = rmsnorm_fwd(o, weight, eps=1e-6)                # output RMS norm per head row
 
 Shapes: q, k, alpha, b [B, T, H, d_k]; v, w [B, T, H, d_v]; states [B, H, d_k, d_v] float32;
 decode drops the T axis. Scalar gates: alpha [B, T, H] (alpha_scalar) and b = beta [B, T, H]
@@ -26,7 +27,7 @@ import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
            "chunk_bwd_workspace_bytes", "chunk_bwd_varlen", "chunk_bwd_varlen_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
-           "decode_step_slots"]
+           "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
@@ -79,6 +80,13 @@ def load():
     lib.gdn2_recurrent_fwd.restype = ctypes.c_int
     lib.gdn2_decode_step.argtypes = [p] * 8 + [i32] * 4 + [ctypes.c_int, u32, p]
     lib.gdn2_decode_step.restype = ctypes.c_int
+    i64, f32 = ctypes.c_int64, ctypes.c_float
+    lib.gdn2_rmsnorm_fwd.argtypes = [p] * 3 + [i64, i32, f32, ctypes.c_int, p]
+    lib.gdn2_rmsnorm_fwd.restype = ctypes.c_int
+    lib.gdn2_rmsnorm_bwd.argtypes = [p] * 5 + [i64, i32, f32, p, sz, p]
+    lib.gdn2_rmsnorm_bwd.restype = ctypes.c_int
+    lib.gdn2_rmsnorm_bwd_workspace_bytes.argtypes = [i64, i32]
+    lib.gdn2_rmsnorm_bwd_workspace_bytes.restype = sz
     lib.gdn2_status_str.argtypes = [ctypes.c_int]
     lib.gdn2_status_str.restype = ctypes.c_char_p
     lib.gdn2_abi_version.argtypes = []
@@ -130,6 +138,15 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _scratch(nbytes, device, stream):
+    """A temporary workspace allocated on the stream the kernels run on, so that once it is
+    freed here the caching allocator hands it out again only in that stream's order."""
+    if stream is None:
+        return torch.empty(nbytes, device=device, dtype=torch.uint8)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, device=device, dtype=torch.uint8)
+
+
 def _state_out(S0, B, H, dk, dv, device, S_out):
     if S_out is None:
         S_out = torch.empty(B, H, dk, dv, device=device, dtype=torch.float32)
@@ -162,7 +179,7 @@ def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspa
     dt = _dtype_code(q)
     need = 0 if fused else int(lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
     if need and workspace is None:
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
                             _ptr(o), _ptr(S_out), B, T, H, dk, dv, dt, flags, _ptr(workspace),
@@ -202,7 +219,7 @@ def chunk_fwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0=None, *, o=None, S_out
         need = int(lib.gdn2_chunk_fwd_varlen_workspace_bytes(N, T, H, dk, dv, dt, flags))
         if need == 0:
             raise Gdn2Error("gdn2_chunk_fwd_varlen", 3)
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.gdn2_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
                                    _ptr(o), _ptr(S_out), _ptr(cu_seqlens), N, T, H, dk, dv, dt, flags,
@@ -269,7 +286,7 @@ def _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu, workspace, out, l2norm, gate_lo
     fn = "gdn2_chunk_bwd" if cu is None else "gdn2_chunk_bwd_varlen"
     need = int(getattr(lib, fn + "_workspace_bytes")(B, T, H, dk, dv, dt, flags))
     if need and workspace is None:
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T),
             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]),
@@ -338,3 +355,43 @@ def decode_step_slots(q, k, v, alpha, b, w, S_pool, slots, *, o=None, l2norm=Fal
     if st != 0:
         raise Gdn2Error("gdn2_decode_step_slots", st)
     return o
+
+
+def _norm_rows(x, name):
+    if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 GPU tensor")
+    d = x.shape[-1]
+    return x.numel() // d if d else 0, d
+
+
+def rmsnorm_fwd(x, weight=None, *, eps: float = 1e-6, out=None, out_dtype=torch.float32, stream=None):
+    """Output RMS norm over the last axis of x (float32, e.g. o [B, T, H, d_v]):
+    y = x / sqrt(mean(x^2) + eps) * weight. out may be x itself (float32, in place)."""
+    lib = load()
+    rows, d = _norm_rows(x, "x")
+    if weight is not None:
+        _norm_rows(weight, "weight")
+    if out is None:
+        out = torch.empty(x.shape, device=x.device, dtype=out_dtype)
+    dt = BF16 if out.dtype == torch.bfloat16 else F32
+    st = lib.gdn2_rmsnorm_fwd(_ptr(x), _ptr(weight), _ptr(out), rows, d, float(eps), dt, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_rmsnorm_fwd", st)
+    return out
+
+
+def rmsnorm_bwd(x, weight, dy, *, eps: float = 1e-6, dx=None, need_dweight: bool = True, stream=None):
+    """Gradients of rmsnorm_fwd: returns dict(dx, dweight) (dweight None unless need_dweight)."""
+    lib = load()
+    rows, d = _norm_rows(x, "x")
+    _norm_rows(dy, "dy")
+    if dx is None:
+        dx = torch.empty_like(x)
+    dweight = torch.empty(d, device=x.device, dtype=torch.float32) if need_dweight else None
+    need = int(lib.gdn2_rmsnorm_bwd_workspace_bytes(rows, d)) if need_dweight else 0
+    ws = _scratch(need, x.device, stream) if need else None
+    st = lib.gdn2_rmsnorm_bwd(_ptr(x), _ptr(weight), _ptr(dy), _ptr(dx), _ptr(dweight), rows, d, float(eps),
+                              _ptr(ws), need, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_rmsnorm_bwd", st)
+    return dict(dx=dx, dweight=dweight)

@@ -382,6 +382,59 @@ size_t gdn2_chunk_bwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t
     return gdn2::bwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, gate_flags);
 }
 
+gdn2_status gdn2_rmsnorm_fwd(const float* x, const float* weight, void* y, int64_t rows, int32_t d, float eps,
+                             gdn2_dtype y_dtype, void* stream) {
+    if (rows < 0) return GDN2_ERR_SHAPE;
+    if (!dim_ok_tok(d) || (y_dtype != GDN2_BF16 && y_dtype != GDN2_F32) || !(eps >= 0.f && eps <= 3.0e38f))
+        return GDN2_ERR_UNSUPPORTED;
+    if (rows == 0) return GDN2_OK;
+    if (!x || !y) return GDN2_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y) || (weight && !aligned16(weight))) return GDN2_ERR_ALIGN;
+    const uint64_t n = (uint64_t)rows * (uint64_t)d;
+    if ((uint64_t)rows > (1ull << 40) || (n + 1023) / 1024 * 256 >= (1ull << 31)) return GDN2_ERR_SHAPE;  // grid threads
+    const bool bf = y_dtype == GDN2_BF16;
+    const Range rx = range_of(x, n * 4), ry = range_of(y, n * (bf ? 2 : 4)), rw = range_of(weight, (uint64_t)d * 4);
+    if (overlap(ry, rw) || (overlap(ry, rx) && !(y == x && !bf))) return GDN2_ERR_ALIAS;
+    gdn2::RmsNormArgs a{x, weight, y, bf, nullptr, nullptr, nullptr, nullptr, (long)rows, d, eps};
+    const hipError_t e = gdn2::launch_rmsnorm_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+size_t gdn2_rmsnorm_bwd_workspace_bytes(int64_t rows, int32_t d) {
+    if (rows < 0 || (uint64_t)rows > (1ull << 40) || !dim_ok_tok(d)) return 0;
+    return gdn2::rmsnorm_bwd_workspace_bytes((long)rows, d);
+}
+
+gdn2_status gdn2_rmsnorm_bwd(const float* x, const float* weight, const float* dy, float* dx, float* dweight,
+                             int64_t rows, int32_t d, float eps, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (rows < 0 || (uint64_t)rows > (1ull << 40)) return GDN2_ERR_SHAPE;
+    if (!dim_ok_tok(d) || !(eps >= 0.f && eps <= 3.0e38f)) return GDN2_ERR_UNSUPPORTED;
+    if (rows > 0 && (!x || !dy || !dx)) return GDN2_ERR_NULL;
+    const void* ptrs[] = {x, weight, dy, dx, dweight};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
+    const size_t need = dweight ? gdn2::rmsnorm_bwd_workspace_bytes((long)rows, d) : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return GDN2_ERR_ALIGN;
+    }
+    if (rows == 0 && !dweight) return GDN2_OK;
+    const uint64_t n = (uint64_t)rows * (uint64_t)d;
+    const Range rx = range_of(x, n * 4), rwt = range_of(weight, (uint64_t)d * 4), rdy = range_of(dy, n * 4),
+                rdx = range_of(dx, n * 4), rdw = range_of(dweight, (uint64_t)d * 4),
+                rws = range_of(need ? workspace : nullptr, need);
+    // dx may be dy itself (each lane reads its dy before it writes the same elements of dx)
+    if (overlap(rdx, rx) || overlap(rdx, rwt) || (overlap(rdx, rdy) && dx != dy) || overlap(rdx, rdw) ||
+        overlap(rdx, rws))
+        return GDN2_ERR_ALIAS;
+    if (overlap(rdw, rx) || overlap(rdw, rwt) || overlap(rdw, rdy) || overlap(rdw, rws)) return GDN2_ERR_ALIAS;
+    if (overlap(rws, rx) || overlap(rws, rwt) || overlap(rws, rdy)) return GDN2_ERR_ALIAS;
+    gdn2::RmsNormArgs a{x, weight, nullptr, false, dy, dx, dweight, workspace, (long)rows, d, eps};
+    const hipError_t e = gdn2::launch_rmsnorm_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 const char* gdn2_status_str(gdn2_status s) {
     switch (s) {
         case GDN2_OK: return "ok";

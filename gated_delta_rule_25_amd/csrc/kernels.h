@@ -21,6 +21,24 @@ struct RecurrentArgs {
 };
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t s);
 
+// Output RMS normalisation per row of D values (D in {32, 64, 128, 256}).
+struct RmsNormArgs {
+    const float* x;
+    const float* weight;  // [D] or null (ones)
+    void* y;              // forward: [rows, D], fp32 or bf16
+    bool y_bf16;
+    const float* dy;  // backward: [rows, D] fp32
+    float* dx;
+    float* dweight;   // [D] or null; needs rmsnorm_bwd_workspace_bytes of workspace
+    void* workspace;
+    long rows;
+    int D;
+    float eps;
+};
+hipError_t launch_rmsnorm_fwd(const RmsNormArgs& a, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const RmsNormArgs& a, hipStream_t s);
+size_t rmsnorm_bwd_workspace_bytes(long rows, int D);
+
 // Arguments of the chunkwise (C = 64) prefill kernels.
 struct ChunkArgs {
     const void *q, *k, *v, *alpha, *b, *w;

@@ -293,6 +293,40 @@ gdn2_status gdn2_decode_step_slots(const void *q, const void *k, const void *v, 
                                    int32_t n_slots, gdn2_dtype in_dtype, uint32_t gate_flags,
                                    void *stream);
 
+/*
+ * Output RMS normalisation: the recurrent layer's output passes through an RMS norm
+ * [GDN2-summary, paragraph "Архитектурно"]. Per row of d values (one head's d_v outputs of one
+ * token; rows = B*T*H for a prefill's o, B*H for a decode step's):
+ *     y = x / sqrt(mean(x^2) + eps) * weight
+ *
+ *   x       [rows, d] float32 (the o of any call above)
+ *   weight  [d] float32, shared by the rows (NULL = ones)
+ *   y       [rows, d], y_dtype GDN2_F32 or GDN2_BF16 (rounded to nearest even); y == x is
+ *           allowed with GDN2_F32 (in place); any other overlap is GDN2_ERR_ALIAS
+ *   eps     >= 0 and finite (GDN2_ERR_UNSUPPORTED otherwise); a zero row with eps == 0 gives
+ *           NaN, as the formula does
+ * Supported: d in {32, 64, 128, 256}; rows == 0 enqueues nothing. fp32 arithmetic, one read of x
+ * and one write of y. Pointers 16-byte aligned. No workspace.
+ */
+gdn2_status gdn2_rmsnorm_fwd(const float *x, const float *weight, void *y, int64_t rows, int32_t d,
+                             float eps, gdn2_dtype y_dtype, void *stream);
+
+/*
+ * Backward of gdn2_rmsnorm_fwd: given dy = dL/dy [rows, d] float32, writes dx = dL/dx [rows, d]
+ * float32 and, when dweight != NULL, dweight = dL/dweight [d] (the sum over every row of
+ * dy * x / sqrt(mean(x^2) + eps)). With s = (mean(x^2) + eps)^(-1/2), xh = x s and
+ * u = dy * weight: dx = s (u - xh mean(xh u)) per row. dx == dy is allowed (in place); no other
+ * overlap. dweight is summed in a fixed order (per-workgroup partials in the workspace, then one
+ * pass over them), so it is the same from run to run. The workspace (needed only with dweight,
+ * gdn2_rmsnorm_bwd_workspace_bytes, 16-byte aligned) is scratch. rows == 0 writes dweight = 0.
+ */
+gdn2_status gdn2_rmsnorm_bwd(const float *x, const float *weight, const float *dy, float *dx,
+                             float *dweight, int64_t rows, int32_t d, float eps, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Workspace bytes gdn2_rmsnorm_bwd needs for dweight at these sizes (0: none, or unsupported). */
+size_t gdn2_rmsnorm_bwd_workspace_bytes(int64_t rows, int32_t d);
+
 /* A static, human-readable name for a status code. */
 const char *gdn2_status_str(gdn2_status s);
 

@@ -236,3 +236,37 @@ def test_bwd_varlen_rejects_bad_arguments(lib):
     assert call(cu=far[9]) == 5                         # cu_seqlens overlaps dq
     assert call(ws=far[12]) == 5                        # workspace over db
     assert call(N=32, T=64 * 1024 * 32, H=64, wsb=1 << 45) == 2  # grid past 2^31 threads
+
+
+def test_rmsnorm_rejects_bad_arguments(lib):
+    # every call below is refused on the host (or has nothing to do) before any launch
+    far = [P((1 << 40) * (i + 1)) for i in range(8)]
+    fwd, bwd, qs = lib.gdn2_rmsnorm_fwd, lib.gdn2_rmsnorm_bwd, lib.gdn2_rmsnorm_bwd_workspace_bytes
+    x, w, y = far[0], far[1], far[2]
+    assert fwd(x, w, y, -1, 128, 1e-6, 1, None) == 2
+    assert fwd(x, w, y, 10, 48, 1e-6, 1, None) == 3
+    assert fwd(x, w, y, 10, 128, 1e-6, 5, None) == 3          # unknown output dtype
+    assert fwd(x, w, y, 10, 128, -1.0, 1, None) == 3          # eps < 0
+    assert fwd(x, w, y, 10, 128, float("inf"), 1, None) == 3
+    assert fwd(x, w, y, 10, 128, float("nan"), 1, None) == 3
+    assert fwd(x, w, y, 0, 128, 1e-6, 1, None) == 0           # no rows: nothing enqueued
+    assert fwd(None, w, y, 10, 128, 1e-6, 1, None) == 1
+    assert fwd(P((1 << 40) + 8), w, y, 10, 128, 1e-6, 1, None) == 4
+    assert fwd(x, w, x, 10, 128, 1e-6, 0, None) == 5          # in place only with float32 output
+    assert fwd(x, w, P((1 << 40) + 512), 10, 128, 1e-6, 1, None) == 5  # partial overlap with x
+    assert fwd(x, w, P((1 << 40) * 2 - 256), 10, 128, 1e-6, 1, None) == 5  # y runs into weight
+    assert fwd(x, w, y, 1 << 36, 128, 1e-6, 1, None) == 2    # grid past 2^31 threads
+    # backward: dweight partials, one [d] row per workgroup step of 4096 / d rows, at most 1024
+    assert qs(1000, 128) == 32 * 128 * 4
+    assert qs(10 ** 7, 128) == 1024 * 128 * 4
+    assert qs(10, 48) == 0 and qs(-1, 128) == 0
+    dy, dx, dw, ws = far[3], far[4], far[5], far[6]
+    need = qs(1000, 128)
+    assert bwd(x, w, dy, dx, dw, 1000, 128, 1e-6, None, 0, None) == 7
+    assert bwd(x, w, dy, dx, dw, 1000, 128, 1e-6, ws, need - 1, None) == 7
+    assert bwd(x, w, dy, dx, dw, 1000, 128, -1.0, ws, need, None) == 3
+    assert bwd(x, w, None, dx, dw, 1000, 128, 1e-6, ws, need, None) == 1
+    assert bwd(x, w, dy, x, dw, 1000, 128, 1e-6, ws, need, None) == 5      # dx over x
+    assert bwd(x, w, dy, dx, dy, 1000, 128, 1e-6, ws, need, None) == 5     # dweight over dy
+    assert bwd(x, w, dy, dx, dw, 1000, 128, 1e-6, dx, need, None) == 5     # workspace over dx
+    assert bwd(x, w, dy, dx, None, 0, 128, 1e-6, None, 0, None) == 0       # nothing to do

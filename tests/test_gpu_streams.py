@@ -5,7 +5,8 @@ import pytest
 import torch
 
 from parity import banner
-from gated_delta_rule_25_amd.inputs import WORKLOADS, make_cotangents, make_inputs, make_packed_inputs, scaled
+from gated_delta_rule_25_amd.inputs import (WORKLOADS, make_cotangents, make_inputs, make_packed_cotangents,
+                                            make_packed_inputs, scaled)
 
 pytestmark = pytest.mark.gpu
 NAMES = ("q", "k", "v", "alpha", "b", "w")
@@ -27,7 +28,7 @@ def _side_copies(src, stream):
 
 
 def test_entry_points_follow_the_given_stream():
-    banner("streams: chunk_fwd, chunk_fwd_varlen, chunk_bwd, decode_step on a side stream")
+    banner("streams: chunk_fwd, chunk_fwd_varlen, chunk_bwd, chunk_bwd_varlen, decode_step, rmsnorm on a side stream")
     g = _g()
     wl = scaled(WORKLOADS["prefill_1p3b"], B=2, T=300, H=4)
     ins = make_inputs(wl)
@@ -36,6 +37,8 @@ def test_entry_points_follow_the_given_stream():
     d.update(dO=cot["dO"].cuda(), dS_T=cot["dS_T"].cuda())
     d.update({n + "1": d[n][:, 0].contiguous() for n in NAMES})  # one decode token
     packed = make_packed_inputs(scaled(wl, H=2), [70, 0, 130, 5], device="cuda")
+    pcot = make_packed_cotangents(scaled(wl, H=2), [70, 0, 130, 5], device="cuda")
+    packed.update(dO=pcot["dO"], dS_T=pcot["dS_T"])
 
     def run(x, p, stream):
         o, S = g.chunk_fwd(*(x[n] for n in NAMES), x["S0"], stream=stream)
@@ -46,7 +49,12 @@ def test_entry_points_follow_the_given_stream():
             with torch.cuda.stream(stream):
                 Sd = x["S0"].clone()
         od = g.decode_step(*(x[n + "1"] for n in NAMES), Sd, stream=stream)
-        return [o, S, ov, Sv, od, Sd] + [gr[k] for k in sorted(gr)]
+        gv = g.chunk_bwd_varlen(*(p[n] for n in NAMES), p["cu_seqlens"], p["S0"], p["dO"], p["dS_T"],
+                                stream=stream)
+        y = g.rmsnorm_fwd(x["dO"], None, eps=1e-6, stream=stream)
+        gn = g.rmsnorm_bwd(x["dO"], None, x["dO"], eps=1e-6, stream=stream)
+        return ([o, S, ov, Sv, od, Sd, y, gn["dx"], gn["dweight"]] + [gr[k] for k in sorted(gr)]
+                + [gv[k] for k in sorted(gv)])
 
     ref = run(d, packed, None)
     torch.cuda.synchronize()
