@@ -73,7 +73,7 @@ struct ChainBwdIO {
     const float* dO;    // [B, T, H, DV]
     const float* dS_T;  // [B, H, DK, DV] or null
     const char* blobs;  // [b*h][nch] operand blocks
-    float* G_save;      // [b*h][nch][DK][DV]: dL/dS at the end of each chunk
+    uint16_t* G_save;   // [b*h][nch][DK][DV] fp16: dL/dS at the end of each chunk
     uint16_t* dDl;      // [B, T, H, DV] fp16: dL/dDelta
     uint16_t* dDp;      // [B, T, H, DV] fp16: dL/dD'
     float* dv;
@@ -273,6 +273,19 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
                 *reinterpret_cast<float4*>(dst + (size_t)(64 * h2 + rr0 + 16 * q) * DV + colw + 4 * cc) = staged(q);
         }
     };
+    // the same as fp16 (the G' saves): one 8-byte store per lane and 16 rows
+    auto store_state_h = [&](uint16_t* dst) {
+#pragma unroll
+        for (int h2 = 0; h2 < NMK / NST; ++h2) {
+            stage(&G[NST * h2], std::integral_constant<int, NST>());
+#pragma unroll
+            for (int q = 0; q < NST; ++q) {
+                const float4 x = staged(q);
+                *reinterpret_cast<h4*>(dst + (size_t)(64 * h2 + rr0 + 16 * q) * DV + colw + 4 * cc) =
+                    h4{(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+            }
+        }
+    };
     constexpr int kStepStores = NMK + 16;  // stores a step issues after its loads
 
     if (nchs > 0) {
@@ -345,7 +358,7 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
         if (n > 0) fetch(n - 1);
 
         // G' of this chunk, for the contraction kernel
-        store_state(io.G_save + (cbase0 + n) * DK * DV);
+        store_state_h(io.G_save + (cbase0 + n) * DK * DV);
 
         Frag Gf[NKS];
 #pragma unroll
@@ -414,8 +427,8 @@ struct ContractIO {
     const uint16_t* Dl;   // Delta
     const uint16_t* dDl;  // dDelta
     const uint16_t* dDp;  // dD'
-    const float* S_save;
-    const float* G_save;
+    const uint16_t* S_save;  // fp16
+    const uint16_t* G_save;
     const char* blobs;
     float* dQh;  // [b*h][nch][64][DK]
     float* dEh;
@@ -477,8 +490,8 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
         cbase = (size_t)bh * nch + n;
     }
     const int t0 = n * CH;
-    const float* S = io.S_save + cbase * DK * DV;
-    const float* Gp = io.G_save + cbase * DK * DV;
+    const uint16_t* S = io.S_save + cbase * DK * DV;
+    const uint16_t* Gp = io.G_save + cbase * DK * DV;
 
     // T of the block (4-element units of the stored triangle), loaded now, used at the end
     constexpr int TU = BL::TPE / 4;  // units
@@ -505,12 +518,12 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
     for (int u = 0; u < NSU; ++u) dg[u] = 0.f;
     for (int js = 0; js < DV; js += JS) {
         __syncthreads();
-        float4 la[NSU], lb[NSU];
+        h4 la[NSU], lb[NSU];
 #pragma unroll
         for (int u = 0; u < NSU; ++u) {
             const int x = tid + 256 * u, i = x / (JS / 4), j = 4 * (x % (JS / 4));
-            la[u] = *reinterpret_cast<const float4*>(S + (size_t)i * DV + js + j);
-            lb[u] = *reinterpret_cast<const float4*>(Gp + (size_t)i * DV + js + j);
+            la[u] = *reinterpret_cast<const h4*>(S + (size_t)i * DV + js + j);
+            lb[u] = *reinterpret_cast<const h4*>(Gp + (size_t)i * DV + js + j);
         }
         // dO (fp32) 4 columns per thread; D', Delta, dDelta, dD' (fp16 rows) 8 columns per thread
         const uint16_t* srch[4] = {io.dDp, io.Dl, io.dDl, io.Dp};
@@ -535,10 +548,11 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 #pragma unroll
         for (int u = 0; u < NSU; ++u) {
             const int x = tid + 256 * u, i = x / (JS / 4), j = 4 * (x % (JS / 4));
-            const float4 a = la[u], b = lb[u];
-            *reinterpret_cast<h4*>(Ss + i * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
-            *reinterpret_cast<h4*>(Gs + i * JP + j) = h4{(E)b.x, (E)b.y, (E)b.z, (E)b.w};
-            dg[u] += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+            const h4 a = la[u], b = lb[u];
+            *reinterpret_cast<h4*>(Ss + i * JP + j) = a;
+            *reinterpret_cast<h4*>(Gs + i * JP + j) = b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dg[u] = fmaf((float)a[e], (float)b[e], dg[u]);
         }
 #pragma unroll
         for (int u = 0; u < NRU; ++u) {
@@ -1132,7 +1146,7 @@ BwdLayout bwd_layout_n(size_t slots, size_t tok_rows, int DK, int DV, size_t hea
     size_t o = up(head);
     L.blobs = o;
     o += up(slots * split_chunk_bytes(1, 1, DK, true));
-    const size_t st = up(slots * DK * DV * 4);
+    const size_t st = up(slots * DK * DV * 2);  // fp16 states
     L.S_save = o;
     o += st;
     L.G_save = o;
@@ -1188,8 +1202,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
         vt.n = a.B;
     }
     char* blobs = ws + L.blobs;
-    float* S_save = reinterpret_cast<float*>(ws + L.S_save);
-    float* G_save = reinterpret_cast<float*>(ws + L.G_save);
+    uint16_t* S_save = reinterpret_cast<uint16_t*>(ws + L.S_save);
+    uint16_t* G_save = reinterpret_cast<uint16_t*>(ws + L.G_save);
     uint16_t* Dp = reinterpret_cast<uint16_t*>(ws + L.Dp);
     uint16_t* Dl = reinterpret_cast<uint16_t*>(ws + L.Dl);
     uint16_t* dDl = reinterpret_cast<uint16_t*>(ws + L.dDl);

@@ -116,7 +116,7 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
 }
 
 template <int DK, int PRO>
-hipError_t launch_states_t(const ChunkArgs& a, char* blobs, float* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
+hipError_t launch_states_t(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                            hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
@@ -136,7 +136,7 @@ hipError_t launch_states_t(const ChunkArgs& a, char* blobs, float* S_save, uint1
 
 }  // namespace
 
-hipError_t launch_split_states(const ChunkArgs& a, char* blobs, float* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
+hipError_t launch_split_states(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                                hipStream_t s) {
     if (!a.bf16 || (a.flags & ~12u) != 0u || !split_supported(a.T, a.H, a.DK, a.DV, true)) return hipErrorNotSupported;
     auto go = [&](auto pro) -> hipError_t {

@@ -598,8 +598,9 @@ struct ChainIO {
     int out_last;  // only the last segment writes S_out
     int phi_tiles = 0;  // transition tiles (over d_k) after the value tiles, state-only pass
     // Saves for the backward pass (state-only pass, sequential): the state at the start of every
-    // chunk, S_save + ((bh * save_nch) + chunk) * DK * DV; D' and Delta rows, [B, T, H, DV] fp16
-    float* S_save = nullptr;
+    // chunk (fp16: the precision its readers take it in as matrix-core operands),
+    // S_save + ((bh * save_nch) + chunk) * DK * DV; D' and Delta rows, [B, T, H, DV] fp16
+    uint16_t* S_save = nullptr;
     int save_nch = 0;
     uint16_t* Dp_save = nullptr;  // fp16 bits
     uint16_t* Dl_save = nullptr;
@@ -799,14 +800,15 @@ chain_kernel(const ChainIO io) {
             }
             if constexpr (SAVE) {
                 // the state at the start of this chunk, for the backward pass
-                float* sv = io.S_save + (save_base + n) * DK * DV;
+                uint16_t* sv = io.S_save + (save_base + n) * DK * DV;
 #pragma unroll
                 for (int c = 0; c < NT; ++c)
 #pragma unroll
                     for (int mk = 0; mk < NMK; ++mk)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            sv[(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16] = Sacc[c][mk][j];
+                            sv[(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16] =
+                                __builtin_bit_cast(uint16_t, (_Float16)Sacc[c][mk][j]);
             }
             f4 D[NT][4];
 #pragma unroll

@@ -100,7 +100,7 @@ hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
 // the start state of every chunk ([h][chunk of the batch][DK][DV]) and the rows of D' and Delta
 // (fp16, packed rows). bf16, general gates, the prologue flags PRO.
 template <int DK, int PRO>
-hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, long ring, float* S_save,
+hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, long ring, uint16_t* S_save,
                                   uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
     const int N = a.B;
@@ -160,7 +160,7 @@ size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16) {
     return varlen_table_bytes(n) + (size_t)varlen_chunk_bound(n, T) * split_chunk_bytes(1, H, DK, bf16);
 }
 
-hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, float* S_save,
+hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, uint16_t* S_save,
                                 uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t s) {
     if (!a.bf16 || (a.flags & ~12u) != 0u || !a.cu_seqlens || !split_supported(a.T, a.H, a.DK, a.DV, true))
         return hipErrorNotSupported;

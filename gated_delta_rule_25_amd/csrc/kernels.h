@@ -77,12 +77,12 @@ size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16);
 // the batch], `ring` = varlen_chunk_bound slots per head), the start state of every chunk
 // ([h][chunk of the batch][DK][DV] fp32) and the rows of D' and Delta (fp16, packed rows). bf16
 // inputs, general gates, the prologue flags allowed.
-hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, float* S_save,
+hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, uint16_t* S_save,
                                 uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t s);
 // Prep over every chunk into `blobs` ([b*h][chunk] operand blocks), then the state-only chain in
 // order, saving the state at the start of every chunk ([b*h][chunk][DK][DV]) and the rows of D'
 // and Delta ([B, T, H, DV], fp16 bits). bf16 inputs, general gates, the prologue flags allowed.
-hipError_t launch_split_states(const ChunkArgs& a, char* blobs, float* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
+hipError_t launch_split_states(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                                hipStream_t s);
 
 // Backward of the chunkwise prefill (bf16 inputs, general gates, d_k = d_v in {32, 64, 128}).

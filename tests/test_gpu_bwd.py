@@ -151,7 +151,7 @@ def test_bwd_prologue(name, wl, l2n, gl):
 
 def test_bwd_stages_match_oracle():
     """The chunk-start states the forward chain saves and the state gradients at chunk ends the
-    reverse chain saves, read back from the workspace, equal the oracle's."""
+    reverse chain saves (both fp16), read back from the workspace, equal the oracle's."""
     banner("bwd stages")
     g = _g()
     wl = scaled(WORKLOADS["prefill_1p3b"], B=1, T=150, H=2)
@@ -164,9 +164,9 @@ def test_bwd_stages_match_oracle():
     _gpu(ins, cot, workspace=ws)
     blob_bytes = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv) - B * H * dk * dv * 4  # one slot
     off = (nch * blob_bytes + 255) // 256 * 256
-    st_bytes = B * H * nch * dk * dv * 4
-    S_save = ws[off:off + st_bytes].view(torch.float32).view(B * H, nch, dk, dv).cpu().double().numpy()
-    G_save = ws[off + st_bytes:off + 2 * st_bytes].view(torch.float32).view(B * H, nch, dk, dv).cpu().double().numpy()
+    st_bytes = B * H * nch * dk * dv * 2  # fp16, as the contraction takes them
+    S_save = ws[off:off + st_bytes].view(torch.float16).view(B * H, nch, dk, dv).cpu().double().numpy()
+    G_save = ws[off + st_bytes:off + 2 * st_bytes].view(torch.float16).view(B * H, nch, dk, dv).cpu().double().numpy()
     x = {n: ins[n] for n in ("q", "k", "v", "alpha", "b", "w")}
     for n in range(nch):
         t0, t1 = 64 * n, min(64 * n + 64, T)
