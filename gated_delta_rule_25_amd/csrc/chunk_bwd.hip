@@ -426,42 +426,34 @@ struct ContractIO {
     const uint16_t* Dp;   // D' (fp16 bits, [B, T, H, DV])
     const uint16_t* Dl;   // Delta
     const uint16_t* dDl;  // dDelta
-    const uint16_t* dDp;  // dD'
-    const uint16_t* S_save;  // fp16
-    const uint16_t* G_save;
     const char* blobs;
-    float* dQh;  // [b*h][nch][64][DK]
-    float* dEh;
-    float* dKb;
     float* dPm;  // [b*h][nch][64][64]
     float* dAm;
-    float* dgam;  // [b*h][nch][DK]
     int B, T, H, DV, nch;
     VarTab var{};  // packed batch: as ChainBwdIO's
     long ring = 0;
 };
 
-// All five products contract over the value channels j with both operands row-major in j, the
-// fragment layout of the matrix cores: fp16 operands (as in the chains), fp32 accumulation. The
-// value channels are staged in slices of 64 columns; wave w owns output rows 16 w .. 16 w + 15.
+// The two 64 x 64 products dP = lower(dO Delta^T) and dT = lower(dDelta D'^T) contract over the
+// value channels j with both operands row-major in j, the fragment layout of the matrix cores:
+// fp16 operands (as in the chains), fp32 accumulation. The value channels are staged in slices of
+// 64 columns; wave w owns output rows 16 w .. 16 w + 15. Then dA = -T^T dT T^T in fp32. (The
+// products over the key channels, dQ_hat, dE_hat, dK_bar and dgamma, are formed where they are
+// used, in the key kernel.)
 template <int DK, bool VAR = false>
-__global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO io) {
+__global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO io) {
     using PR = Prec<true>;
     using E = _Float16;
     using Frag = PR::Frag;
     using BL = Blob<DK, true>;
     constexpr int JS = DK < 64 ? DK : 64;  // value columns per slice (d_v == d_k)
     constexpr int JP = JS + 4;    // row stride (halves): 2 dwords past a multiple of 32 banks
-    constexpr int NMK = DK / 16;  // 16-channel tiles of the key axis
-    constexpr int SMB = (2 * DK + 5 * CH) * JP * 2;  // bytes of one slice
+    constexpr int SMB = 4 * CH * JP * 2;  // bytes of one slice
     constexpr int TP = CH + 1;
     constexpr int UTB = 3 * CH * TP * 4;  // the UT adjoint reuses the slice buffers
     __shared__ __attribute__((aligned(16))) char lds[SMB > UTB ? SMB : UTB];
-    E* Ss = reinterpret_cast<E*>(lds);  // [DK][JP]
-    E* Gs = Ss + DK * JP;               // [DK][JP]
-    E* dOs = Gs + DK * JP;              // [64][JP]: dO, dD', Delta, dDelta, D'
-    E* dDps = dOs + CH * JP;
-    E* Dls = dDps + CH * JP;
+    E* dOs = reinterpret_cast<E*>(lds);  // [64][JP]: dO, Delta, dDelta, D'
+    E* Dls = dOs + CH * JP;
     E* dDls = Dls + CH * JP;
     E* Dps = dDls + CH * JP;
 
@@ -490,8 +482,6 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
         cbase = (size_t)bh * nch + n;
     }
     const int t0 = n * CH;
-    const uint16_t* S = io.S_save + cbase * DK * DV;
-    const uint16_t* Gp = io.G_save + cbase * DK * DV;
 
     // T of the block (4-element units of the stored triangle), loaded now, used at the end
     constexpr int TU = BL::TPE / 4;  // units
@@ -501,35 +491,22 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 #pragma unroll
     for (int u = 0; u < TPT; ++u) tun[u] = (tid + 256 * u < TU) ? Tunits[tid + 256 * u] : make_uint2(0u, 0u);
 
-    f4 aQ[NMK], aE[NMK], aK[NMK], aP[4], aT[4];
-#pragma unroll
-    for (int c = 0; c < NMK; ++c) aQ[c] = aE[c] = aK[c] = f4{0.f, 0.f, 0.f, 0.f};
+    f4 aP[4], aT[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) aP[c] = aT[c] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // staging: thread x = tid + 256 u takes row x / (JS / 4), columns 4 (x % (JS / 4)) .. + 3;
-    // every load of a group is issued before the first conversion. dgamma_i = sum_j S_ij G'_ij
-    // is summed in fp32 from the same loads (per thread, then over the row's JS / 4 lanes).
-    constexpr int NSU = DK * JS / 4 / 256, NRU = CH * JS / 4 / 256, NRH = CH * JS / 8 / 256;
-    static_assert(NSU * 256 == DK * JS / 4 && NRU * 256 == CH * JS / 4 && NRH * 256 == CH * JS / 8,
-                  "staging split");
-    float dg[NSU];
-#pragma unroll
-    for (int u = 0; u < NSU; ++u) dg[u] = 0.f;
+    // staging: thread x = tid + 256 u takes row x / (JS / 4), columns 4 (x % (JS / 4)) .. + 3
+    // (fp32 dO), or row x / (JS / 8), columns 8 (x % (JS / 8)) .. + 7 (fp16 rows); every load of
+    // a slice is issued before the first conversion
+    constexpr int NRU = CH * JS / 4 / 256, NRH = CH * JS / 8 / 256;
+    static_assert(NRU * 256 == CH * JS / 4 && NRH * 256 == CH * JS / 8, "staging split");
     for (int js = 0; js < DV; js += JS) {
         __syncthreads();
-        h4 la[NSU], lb[NSU];
-#pragma unroll
-        for (int u = 0; u < NSU; ++u) {
-            const int x = tid + 256 * u, i = x / (JS / 4), j = 4 * (x % (JS / 4));
-            la[u] = *reinterpret_cast<const h4*>(S + (size_t)i * DV + js + j);
-            lb[u] = *reinterpret_cast<const h4*>(Gp + (size_t)i * DV + js + j);
-        }
-        // dO (fp32) 4 columns per thread; D', Delta, dDelta, dD' (fp16 rows) 8 columns per thread
-        const uint16_t* srch[4] = {io.dDp, io.Dl, io.dDl, io.Dp};
-        E* dsth[4] = {dDps, Dls, dDls, Dps};
+        // dO (fp32) 4 columns per thread; Delta, dDelta, D' (fp16 rows) 8 columns per thread
+        const uint16_t* srch[3] = {io.Dl, io.dDl, io.Dp};
+        E* dsth[3] = {Dls, dDls, Dps};
         float4 lr[NRU];
-        uint4 lh[4][NRH];
+        uint4 lh[3][NRH];
 #pragma unroll
         for (int u = 0; u < NRU; ++u) {
             const int x = tid + 256 * u, r = x / (JS / 4), j = 4 * (x % (JS / 4));
@@ -543,16 +520,7 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
             const int t = t0 + r;
             const size_t e = ((tbase + (t < Tq ? t : 0)) * H + hh) * DV + js + j;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) lh[m][u] = *reinterpret_cast<const uint4*>(srch[m] + e);
-        }
-#pragma unroll
-        for (int u = 0; u < NSU; ++u) {
-            const int x = tid + 256 * u, i = x / (JS / 4), j = 4 * (x % (JS / 4));
-            const h4 a = la[u], b = lb[u];
-            *reinterpret_cast<h4*>(Ss + i * JP + j) = a;
-            *reinterpret_cast<h4*>(Gs + i * JP + j) = b;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dg[u] = fmaf((float)a[e], (float)b[e], dg[u]);
+            for (int m = 0; m < 3; ++m) lh[m][u] = *reinterpret_cast<const uint4*>(srch[m] + e);
         }
 #pragma unroll
         for (int u = 0; u < NRU; ++u) {
@@ -565,7 +533,7 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
             const int x = tid + 256 * u, r = x / (JS / 8), j = 8 * (x % (JS / 8));
             const bool ok = t0 + r < Tq;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < 3; ++m) {
                 const uint4 a = ok ? lh[m][u] : make_uint4(0u, 0u, 0u, 0u);
                 *reinterpret_cast<uint2*>(dsth[m] + r * JP + j) = make_uint2(a.x, a.y);
                 *reinterpret_cast<uint2*>(dsth[m] + r * JP + j + 4) = make_uint2(a.z, a.w);
@@ -577,14 +545,7 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
             const int c0 = 32 * ks + 4 * g;
             auto frag = [&](const E* M, int row) { return PR::lds_pair(M + row * JP + c0, M + row * JP + c0 + 16); };
             const int r = 16 * wv + l16;
-            const Frag fO = frag(dOs, r), fDp = frag(dDps, r), fL = frag(Dls, r), fdL = frag(dDls, r);
-#pragma unroll
-            for (int c = 0; c < NMK; ++c) {
-                const Frag fS = frag(Ss, 16 * c + l16), fG = frag(Gs, 16 * c + l16);
-                PR::mma(aQ[c], fO, fS);
-                PR::mma(aE[c], fDp, fS);
-                PR::mma(aK[c], fL, fG);
-            }
+            const Frag fO = frag(dOs, r), fdL = frag(dDls, r);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (c <= wv) {
@@ -596,30 +557,12 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
     }
     // accumulator [c][j]: row 16 wv + 4 g + j, column 16 c + l16
 #pragma unroll
-    for (int c = 0; c < NMK; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const size_t e = (cbase * CH + 16 * wv + 4 * g + j) * DK + 16 * c + l16;
-            io.dQh[e] = aQ[c][j];
-            io.dEh[e] = -aE[c][j];
-            io.dKb[e] = aK[c][j];
-        }
-#pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * wv + 4 * g + j, cc = 16 * c + l16;
             io.dPm[(cbase * CH + r) * CH + cc] = (c <= wv && cc <= r) ? aP[c][j] : 0.f;
         }
-    // dgamma: the row's JS / 4 lanes are consecutive; the first of them stores
-#pragma unroll
-    for (int u = 0; u < NSU; ++u) {
-        float v = dg[u];
-#pragma unroll
-        for (int m = 1; m < JS / 4; m <<= 1) v += __shfl_xor(v, m);
-        const int x = tid + 256 * u;
-        if (x % (JS / 4) == 0) io.dgam[cbase * DK + x / (JS / 4)] = v;
-    }
 
     // dA = -T^T dT T^T (strictly lower), dT = dDelta D'^T on the lower triangle
     __syncthreads();
@@ -695,7 +638,10 @@ __global__ void __launch_bounds__(256, 1) bwd_contract_kernel(const ContractIO i
 struct KeyIO {
     const void *q, *k, *alpha, *b;  // bf16 [B, T, H, DK]
     const float *rnq, *rnk;         // 1 / max(|q|, 1e-12), 1 / max(|k|, 1e-12) per row (L2 norm)
-    const float *dQh, *dEh, *dKb, *dPm, *dAm, *dgam;
+    const float* dO;                  // [B, T, H, DK] (d_v == d_k)
+    const uint16_t *dDp, *Dl;         // dL/dD' and Delta rows (fp16, [B, T, H, DK])
+    const uint16_t *S_save, *G_save;  // chunk-start states and chunk-end gradients (fp16)
+    const float *dPm, *dAm;           // [slot][64][64]
     float *dq, *dk, *dalpha, *db;  // [B, T, H, DK]
     int B, T, H, nch;
     VarTab var{};  // packed batch: as ChainBwdIO's
@@ -725,11 +671,28 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     constexpr int CW = 32;       // key channels per workgroup
     constexpr int NG = DK / CW;  // channel groups
     static_assert(DK % CW == 0, "channel groups");
-    __shared__ __attribute__((aligned(16))) float dA[CH * CH];
-    __shared__ __attribute__((aligned(16))) float dPs[CH * CH];
-    __shared__ float G2[CH * CW];                         // cumulative log2 decay
-    __shared__ float Xk[CH * CW], Xe[CH * CW], Xq[CH * CW];  // pre-scaled rows of k, b*k, q
-    __shared__ float part[16 * CW];                       // per sub-block sums over rows
+    using PR = Prec<true>;
+    using E = _Float16;
+    using Frag = PR::Frag;
+    // LDS: first the staged operands of the contraction over the value channels, then, in the
+    // same bytes, the arrays of the decay-weighted sums
+    constexpr int JP = DK + 4;  // staged row stride (halves): 2 dwords past a multiple of 32 banks
+    constexpr int kStage = (3 * CH + 2 * CW) * JP * 2;
+    constexpr int kSums = (2 * CH * CH + 4 * CH * CW + 16 * CW) * 4;
+    __shared__ __attribute__((aligned(16))) char smem[kStage > kSums ? kStage : kSums];
+    __shared__ float dgS[CW];  // dgamma of the group's channels, by staged row
+    float* dA = reinterpret_cast<float*>(smem);
+    float* dPs = dA + CH * CH;
+    float* G2 = dPs + CH * CH;  // cumulative log2 decay
+    float* Xk = G2 + CH * CW;   // pre-scaled rows of k, b*k, q
+    float* Xe = Xk + CH * CW;
+    float* Xq = Xe + CH * CW;
+    float* part = Xq + CH * CW;  // per sub-block sums over rows
+    E* Os = reinterpret_cast<E*>(smem);  // [CH][JP] rows of dO, dD', Delta
+    E* DPs = Os + CH * JP;
+    E* Ls = DPs + CH * JP;
+    E* Sg = Ls + CH * JP;  // [CW][JP] the group's rows of S and G': staged row 16 t + l is channel 2 l + t
+    E* Gg = Sg + CW * JP;
 
     const int tid = threadIdx.x, I = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, nch = io.nch;
@@ -780,21 +743,112 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         rbv[j] = b32[e];
         ra[j] = a32[e];
     }
-    float lA[16], lP[16];
+
+    // ---- dQ_hat = dO S^T, dE_hat = -dD' S^T, dK_bar = Delta G'^T for this group's channels,
+    // contracted over the value channels on the matrix cores (fp16 operands as in the chains,
+    // fp32 accumulate), and dgamma = rowsum(S o G') of the group in fp32 from the same values.
+    // Thread x = tid + 256 u stages row x / (DK / 4), columns 4 (x % (DK / 4)) .. + 3 of dO, or
+    // row x / (DK / 8), columns 8 (x % (DK / 8)) .. + 7 of an fp16 row; rows past the end are
+    // read at row 0 and staged as zeros. ----
+    constexpr int NO = CH * DK / 4 / 256, NH = CH * DK / 8 / 256;
+    constexpr int NSR = CW * DK / 8, NSU = (NSR + 255) / 256;  // S, G' units of 8
+    static_assert(NO * 256 == CH * DK / 4 && NH * 256 == CH * DK / 8, "staging split");
+    float4 lo4[NO];
+    uint4 lh[2][NH], ls[2][NSU];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int x = tid + 256 * u, r = x / (DK / 4), j = 4 * (x % (DK / 4)), t = t0 + r;
+        lo4[u] = *reinterpret_cast<const float4*>(io.dO + ((tbase + (t < Tq ? t : 0)) * H + hh) * DK + j);
+    }
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+        const int x = tid + 256 * u, r = x / (DK / 8), j = 8 * (x % (DK / 8)), t = t0 + r;
+        const size_t e = ((tbase + (t < Tq ? t : 0)) * H + hh) * DK + j;
+        lh[0][u] = *reinterpret_cast<const uint4*>(io.dDp + e);
+        lh[1][u] = *reinterpret_cast<const uint4*>(io.Dl + e);
+    }
+#pragma unroll
+    for (int u = 0; u < NSU; ++u) {
+        const int x = tid + 256 * u, sr = x / (DK / 8), j = 8 * (x % (DK / 8));
+        ls[0][u] = ls[1][u] = make_uint4(0u, 0u, 0u, 0u);
+        if (x < NSR) {
+            const size_t e = (cbase * DK + c0 + 2 * (sr % 16) + sr / 16) * DK + j;
+            ls[0][u] = *reinterpret_cast<const uint4*>(io.S_save + e);
+            ls[1][u] = *reinterpret_cast<const uint4*>(io.G_save + e);
+        }
+    }
+    auto put8 = [&](E* dst, uint4 a) {  // 8 halves at an 8-byte aligned row position
+        *reinterpret_cast<uint2*>(dst) = make_uint2(a.x, a.y);
+        *reinterpret_cast<uint2*>(dst + 4) = make_uint2(a.z, a.w);
+    };
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int x = tid + 256 * u, r = x / (DK / 4), j = 4 * (x % (DK / 4));
+        const float4 a = t0 + r < Tq ? lo4[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<h4*>(Os + r * JP + j) = h4{(E)a.x, (E)a.y, (E)a.z, (E)a.w};
+    }
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+        const int x = tid + 256 * u, r = x / (DK / 8), j = 8 * (x % (DK / 8));
+        const bool ok = t0 + r < Tq;
+        put8(DPs + r * JP + j, ok ? lh[0][u] : make_uint4(0u, 0u, 0u, 0u));
+        put8(Ls + r * JP + j, ok ? lh[1][u] : make_uint4(0u, 0u, 0u, 0u));
+    }
+#pragma unroll
+    for (int u = 0; u < NSU; ++u) {
+        const int x = tid + 256 * u, sr = x / (DK / 8), j = 8 * (x % (DK / 8));
+        float p = 0.f;
+        if (x < NSR) {
+            put8(Sg + sr * JP + j, ls[0][u]);
+            put8(Gg + sr * JP + j, ls[1][u]);
+            const uint32_t sa[4] = {ls[0][u].x, ls[0][u].y, ls[0][u].z, ls[0][u].w};
+            const uint32_t ga[4] = {ls[1][u].x, ls[1][u].y, ls[1][u].z, ls[1][u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const E* s2 = reinterpret_cast<const E*>(&sa[e]);
+                const E* g2 = reinterpret_cast<const E*>(&ga[e]);
+                p = fmaf((float)s2[0], (float)g2[0], p);
+                p = fmaf((float)s2[1], (float)g2[1], p);
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < DK / 8; m <<= 1) p += __shfl_xor(p, m);  // the row's DK / 8 lanes
+        if (x < NSR && x % (DK / 8) == 0) dgS[sr] = p;
+    }
+    float lA[16], lP[16];  // dA and dP of the chunk, for the sums below
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         lA[u] = io.dAm[cbase * CH * CH + tid + 256 * u];
         lP[u] = io.dPm[cbase * CH * CH + tid + 256 * u];
     }
+    __syncthreads();
+    f4 aQ[2], aE[2], aK[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) aQ[t] = aE[t] = aK[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+        const int k0 = 32 * ks + 4 * g;
+        auto frag = [&](const E* M, int row) { return PR::lds_pair(M + row * JP + k0, M + row * JP + k0 + 16); };
+        const int r = 16 * I + l16;
+        const Frag fO = frag(Os, r), fDp = frag(DPs, r), fL = frag(Ls, r);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const Frag fS = frag(Sg, 16 * t + l16), fG = frag(Gg, 16 * t + l16);
+            PR::mma(aQ[t], fO, fS);
+            PR::mma(aE[t], fDp, fS);
+            PR::mma(aK[t], fL, fG);
+        }
+    }
+    __syncthreads();  // the staged operands are read; their bytes are reused below
+    // accumulator [t][j]: row 16 I + 4 g + j = rb + j, column l16 of tile t = channel 2 l16 + t
     float2 gQ[4], gE[4], gK[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const size_t ce = (cbase * CH + rb + j) * DK + c0 + ch0;
-        gQ[j] = *reinterpret_cast<const float2*>(io.dQh + ce);
-        gE[j] = *reinterpret_cast<const float2*>(io.dEh + ce);
-        gK[j] = *reinterpret_cast<const float2*>(io.dKb + ce);
+        gQ[j] = make_float2(aQ[0][j], aQ[1][j]);
+        gE[j] = make_float2(-aE[0][j], -aE[1][j]);
+        gK[j] = make_float2(aK[0][j], aK[1][j]);
     }
-    const float2 dgam = *reinterpret_cast<const float2*>(io.dgam + cbase * DK + c0 + ch0);
+    const float2 dgam = make_float2(dgS[l16], dgS[16 + l16]);
 
     float nq[4] = {1.f, 1.f, 1.f, 1.f}, nk[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (L2N) {
@@ -1134,7 +1188,7 @@ __global__ void __launch_bounds__(256) l2norm_bwd(float* __restrict__ dx, const 
 }
 
 struct BwdLayout {
-    size_t blobs, S_save, G_save, Dp, Dl, dDl, dDp, dQh, dEh, dKb, dPm, dAm, dgam, total;
+    size_t blobs, S_save, G_save, Dp, Dl, dDl, dDp, dPm, dAm, total;
 };
 
 // Workspace of the backward: `head` bytes first (the sequence table of a packed batch), then the
@@ -1160,20 +1214,11 @@ BwdLayout bwd_layout_n(size_t slots, size_t tok_rows, int DK, int DV, size_t hea
     o += rows;
     L.dDp = o;
     o += rows;
-    const size_t kr = up(slots * CH * DK * 4);
-    L.dQh = o;
-    o += kr;
-    L.dEh = o;
-    o += kr;
-    L.dKb = o;
-    o += kr;
     const size_t pm = up(slots * CH * CH * 4);
     L.dPm = o;
     o += pm;
     L.dAm = o;
     o += pm;
-    L.dgam = o;
-    o += up(slots * DK * 4);
     L.total = o;
     return L;
 }
@@ -1208,12 +1253,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
     uint16_t* Dl = reinterpret_cast<uint16_t*>(ws + L.Dl);
     uint16_t* dDl = reinterpret_cast<uint16_t*>(ws + L.dDl);
     uint16_t* dDp = reinterpret_cast<uint16_t*>(ws + L.dDp);
-    float* dQh = reinterpret_cast<float*>(ws + L.dQh);
-    float* dEh = reinterpret_cast<float*>(ws + L.dEh);
-    float* dKb = reinterpret_cast<float*>(ws + L.dKb);
     float* dPm = reinterpret_cast<float*>(ws + L.dPm);
     float* dAm = reinterpret_cast<float*>(ws + L.dAm);
-    float* dgam = reinterpret_cast<float*>(ws + L.dgam);
 
     ChunkArgs fa{a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, nullptr, nullptr, a.B, a.T, a.H, DK, a.DV,
                  true, (uint32_t)PRO << 2, nullptr, 0};
@@ -1233,12 +1274,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
     // past the true chunk count leave at once)
     const long items = VAR ? (long)a.H * ring : (long)BH * nch;
     if (items == 0) return hipGetLastError();
-    ContractIO xio{a.dO, Dp, Dl, dDl, dDp, S_save, G_save, blobs, dQh, dEh, dKb, dPm, dAm, dgam,
-                   a.B, a.T, a.H, a.DV, nch};
+    ContractIO xio{a.dO, Dp, Dl, dDl, blobs, dPm, dAm, a.B, a.T, a.H, a.DV, nch};
     xio.var = vt;
     xio.ring = ring;
     hipLaunchKernelGGL((bwd_contract_kernel<DK, VAR>), dim3((unsigned)items), dim3(256), 0, st, xio);
-    KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, dQh, dEh, dKb, dPm, dAm, dgam, a.dq, a.dk, a.dalpha, a.db,
+    KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, a.dO, dDp, Dl, S_save, G_save, dPm, dAm, a.dq, a.dk, a.dalpha, a.db,
               a.B, a.T, a.H, nch};
     kio.var = vt;
     kio.ring = ring;
