@@ -141,7 +141,9 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
     } else {
         const int BH = B * H;
         bh = blockIdx.x % BH;
-        nc = blockIdx.x / BH;
+        // last chunk first: the blocks written last, those the chain reads first, are then the
+        // ones most likely still in the Infinity Cache when the chain starts
+        nc = n_count - 1 - (int)(blockIdx.x / BH);
         n = n_first + nc;
         tbase = (long)(bh / H) * T;
         Tq = T;
