@@ -36,7 +36,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # HBM bytes per gdn2_chunk_fwd call at B8 H16 T4096 d128 bf16, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB copy (profiles/chunk_fwd_bf16_B8_H16_T4096_d128.txt), for the
 # kernels as they stand; set to None when a kernel changes until the counters are taken again.
-MEASURED_TRAFFIC = {"chunk": 2112.3e6, "fused": None, "recurrent": None}
+MEASURED_TRAFFIC = {"chunk": 2125.9e6, "fused": None, "recurrent": None}
 
 
 def prefill_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
