@@ -75,6 +75,7 @@ struct VarTab {
     const int* coff = nullptr;
     const int* start = nullptr;
     const int* len = nullptr;
+    const int* perm = nullptr;  // the sequences, longest first (the chains' dispatch order)
     int n = 0;
 };
 

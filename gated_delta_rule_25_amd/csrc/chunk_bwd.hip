@@ -173,8 +173,10 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     // the vt tiles of one (b, h) sit 8 workgroups apart, on one XCD (workgroups go round the 8
     // XCDs in order), so the second tile's block reads hit that XCD's L2
     const int grp = blockIdx.x / (8 * vt), within = blockIdx.x % (8 * vt);
-    const int bh = grp * 8 + within % 8, tile = within / 8;
+    int bh = grp * 8 + within % 8;
+    const int tile = within / 8;
     if (bh >= io.B * io.H) return;  // (the grid is padded to a multiple of 8 (b, h))
+    if constexpr (VAR) bh = io.var.perm[bh / H] * H + bh % H;  // longest sequences first
     const int hh = bh % H, bb = bh / H;
     const int col = tile * DVT + 16 * wv + l16;
     // this sequence: its chunks (slots cbase0 ..), first token row and length
@@ -1244,6 +1246,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
         vt.coff = reinterpret_cast<const int*>(ws);
         vt.start = vt.coff + a.B + 1;
         vt.len = vt.start + a.B;
+        vt.perm = vt.len + a.B;
         vt.n = a.B;
     }
     char* blobs = ws + L.blobs;

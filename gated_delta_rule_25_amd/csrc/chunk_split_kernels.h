@@ -650,8 +650,11 @@ chain_kernel(const ChainIO io) {
     const int x = blockIdx.x % (BHp * tiles);
     const int grp = x / (8 * tiles), within = x % (8 * tiles);
     const int tile = within / 8;
-    const int bh = grp * 8 + (within % 8);
+    int bh = grp * 8 + (within % 8);
     if (bh >= BH || seg >= io.nseg) return;
+    // packed batch: the workgroups take the sequences longest first, so the longest chains start
+    // at once and the short ones fill in behind them
+    if constexpr (VAR) bh = io.var.perm[bh / H] * H + bh % H;
     const int hh = bh % H;
     // chunks [c_begin, c_end) of this sequence, whose blocks start at `blobs`; the sequence's
     // first token row tbase and its length Tq

@@ -21,11 +21,17 @@ using namespace chunk;
 // non-decreasing (a running maximum), so any input gives sequences that partition rows inside
 // the batch; start[s] = cu'[s], len[s] = cu'[s+1] - cu'[s], and coff[s] = the sum of
 // ceil(len / C) over the sequences before s (coff[n] = the chunk count). One workgroup walks the
-// bounds in tiles of 256 with two block scans per tile.
+// bounds in tiles of 256 with two block scans per tile. Then perm[0..n) lists the sequences by
+// decreasing chunk count (a counting sort over min(chunks, kBuckets - 1); the order inside a
+// bucket is whatever the atomics give, which changes no result: the chains of different
+// sequences share nothing).
+constexpr int kBuckets = 1024;
+
 __global__ void __launch_bounds__(256) varlen_table_kernel(const int* __restrict__ cu, int n, int T,
                                                            int* __restrict__ coff, int* __restrict__ start,
-                                                           int* __restrict__ len) {
+                                                           int* __restrict__ len, int* __restrict__ perm) {
     __shared__ int smax[256], ssum[256], tail[2];
+    __shared__ int hist[kBuckets];
     const int tid = threadIdx.x;
     int cmax = 0, csum = 0;  // running maximum and chunk sum carried from the previous tiles
     for (int base = 0; base <= n; base += 256) {
@@ -62,6 +68,36 @@ __global__ void __launch_bounds__(256) varlen_table_kernel(const int* __restrict
         csum = tail[1];
         __syncthreads();  // tail and the scan arrays are rewritten by the next tile
     }
+    // bucket b = kBuckets - 1 - min(chunks, kBuckets - 1): bucket 0 holds the longest sequences
+    for (int i = tid; i < kBuckets; i += 256) hist[i] = 0;
+    __syncthreads();  // (also orders this workgroup's writes of len above before the reads below)
+    auto bucket = [&](int s) {
+        const int c = (len[s] + CH - 1) / CH;
+        return kBuckets - 1 - (c < kBuckets - 1 ? c : kBuckets - 1);
+    };
+    for (int s = tid; s < n; s += 256) atomicAdd(&hist[bucket(s)], 1);
+    __syncthreads();
+    // exclusive scan of the kBuckets counts: 4 per thread, then one block scan of the sums
+    constexpr int PER = kBuckets / 256;
+    int loc[PER], acc = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        loc[e] = acc;
+        acc += hist[tid * PER + e];
+    }
+    ssum[tid] = acc;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {  // inclusive sum scan
+        const int y = tid >= d ? ssum[tid - d] : 0;
+        __syncthreads();
+        ssum[tid] += y;
+        __syncthreads();
+    }
+    const int before = ssum[tid] - acc;  // the counts of the buckets below this thread's
+#pragma unroll
+    for (int e = 0; e < PER; ++e) hist[tid * PER + e] = before + loc[e];
+    __syncthreads();
+    for (int s = tid; s < n; s += 256) perm[atomicAdd(&hist[bucket(s)], 1)] = s;
 }
 
 template <int DK, bool BF16, bool AS, bool BS, int PRO>
@@ -74,13 +110,15 @@ hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
     int* coff = reinterpret_cast<int*>(ws);
     int* start = coff + N + 1;
     int* len = start + N;
+    int* perm = len + N;
     char* blobs = ws + varlen_table_bytes(N);
     VarTab vt;
     vt.coff = coff;
     vt.start = start;
     vt.len = len;
+    vt.perm = perm;
     vt.n = N;
-    hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, N, a.T, coff, start, len);
+    hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, N, a.T, coff, start, len, perm);
     if (ring > 0)
         hipLaunchKernelGGL((prep_kernel<DK, BF16, AS, BS, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0, st,
                            a.q, a.k, a.alpha, a.b, 1, a.T, a.H, 0, (int)ring, blobs, vt);
@@ -108,9 +146,10 @@ hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, 
     vt.coff = reinterpret_cast<int*>(table);
     vt.start = vt.coff + N + 1;
     vt.len = vt.start + N;
+    vt.perm = vt.len + N;
     vt.n = N;
     hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, N, a.T, const_cast<int*>(vt.coff),
-                       const_cast<int*>(vt.start), const_cast<int*>(vt.len));
+                       const_cast<int*>(vt.start), const_cast<int*>(vt.len), const_cast<int*>(vt.perm));
     if (ring > 0)
         hipLaunchKernelGGL((prep_kernel<DK, true, false, false, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0,
                            st, a.q, a.k, a.alpha, a.b, 1, a.T, a.H, 0, (int)ring, blobs, vt);
@@ -154,7 +193,7 @@ long varlen_chunk_bound(int n, int T) {
     return ((long)T + (long)(CH - 1) * n) / CH;
 }
 
-size_t varlen_table_bytes(int n) { return ((size_t)(3 * (size_t)n + 1) * 4 + 255) / 256 * 256; }
+size_t varlen_table_bytes(int n) { return ((size_t)(4 * (size_t)n + 1) * 4 + 255) / 256 * 256; }
 
 size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16) {
     return varlen_table_bytes(n) + (size_t)varlen_chunk_bound(n, T) * split_chunk_bytes(1, H, DK, bf16);

@@ -152,7 +152,7 @@ def test_varlen_rejects_bad_arguments(lib):
     cu = P(0x200000000 * 10)
     ws = P(0x200000000 * 11)
     need = qs(4, 1000, 2, 128, 128, 0, 0)
-    # table (3 N + 1 ints, padded to 256 B) then (T + 63 N) / 64 = 19 chunks per head
+    # table (4 N + 1 ints, padded to 256 B) then (T + 63 N) / 64 = 19 chunks per head
     assert need == 256 + 19 * 2 * (qs(1, 64, 1, 128, 128, 0, 0) - 256)
     assert qs(4, 1000, 2, 128, 128, 1, 0) == 0      # fp32 at d = 128: not supported
     assert qs(0, 1000, 2, 128, 128, 0, 0) == 0
