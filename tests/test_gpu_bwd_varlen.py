@@ -188,3 +188,13 @@ def test_bwd_varlen_full_size_sampled():
     for hh in (0, 13):
         _check(ins, cot, got, seqs=[int(order[0]), int(order[len(order) // 2]), int(order[-1])],
                heads=slice(hh, hh + 1))
+
+
+def test_bwd_varlen_sequences_past_the_top_length_bucket():
+    # as the forward's test: two sequences of more than 1023 chunks share the top length bucket
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=1, d_k=32, d_v=32)
+    lengths = [5, 66000, 0, 70000]
+    banner(f"bwd varlen, lengths {lengths}, H1 d32")
+    ins = make_packed_inputs(wl, lengths)
+    cot = make_packed_cotangents(wl, lengths)
+    _check(ins, cot, _run(ins, cot))

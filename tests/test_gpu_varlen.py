@@ -162,3 +162,14 @@ def test_varlen_many_sequences_span_several_table_tiles():
     ins = make_packed_inputs(wl, lengths)
     o, S = _run(ins)
     _check(ins, o, S, TOL16)
+
+
+def test_varlen_sequences_past_the_top_length_bucket():
+    # the chains take the sequences longest first, ordered by chunk count in 1024 buckets; two
+    # sequences of more than 1023 chunks share the top bucket (H1 d32, 136,075 rows)
+    wl = scaled(WORKLOADS["prefill_1p3b"], H=1, d_k=32, d_v=32)
+    lengths = [70000, 5, 0, 66000, 70]
+    banner(f"varlen, lengths {lengths}, H1 d32")
+    ins = make_packed_inputs(wl, lengths)
+    o, S = _run(ins)
+    _check(ins, o, S, TOL16)
