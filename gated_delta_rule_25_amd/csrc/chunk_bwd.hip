@@ -1153,40 +1153,60 @@ __global__ void __launch_bounds__(256) row_sums(const float* __restrict__ a, int
     if (lane == 0) out[r] = acc;
 }
 
-// 1 / max(|x|, 1e-12) of each row of D bf16 values; one wavefront per row
-__global__ void __launch_bounds__(256) row_rnorm(const uint16_t* __restrict__ x, float* __restrict__ rn, long rows,
-                                                 int D) {
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (r >= rows) return;  // whole wavefront
+// 1 / max(|x|, 1e-12) of each row of D bf16 values. A group of D / 8 lanes owns a row, one
+// 16-byte load per lane; the row's sum is a butterfly inside the group.
+template <int D>
+__global__ void __launch_bounds__(256) row_rnorm(const uint16_t* __restrict__ x, float* __restrict__ rn, long rows) {
+    constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per workgroup
+    const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = (threadIdx.x % LPR) * 8;
     float ss = 0.f;
-    for (int c = lane; c < D; c += 64) {
-        const float v = __uint_as_float((uint32_t)x[r * D + c] << 16);
-        ss = fmaf(v, v, ss);
+    if (r < rows) {  // groups are row-aligned: a group is all in or all out
+        const uint4 u = *reinterpret_cast<const uint4*>(x + r * D + c);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+        }
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-    if (lane == 0) rn[r] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+    for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if (r < rows && threadIdx.x % LPR == 0) rn[r] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
 }
 
 // Through the L2 norm, in place: dx (with respect to x_n = x rn) becomes
 // rn (dx - (dx . x_n) x_n), or dx rn where |x| <= 1e-12 (rn = 1e12: x_n = x / 1e-12 there).
+// A group of D / 4 lanes owns a row: 16 bytes of dx and 8 of x per lane.
+template <int D>
 __global__ void __launch_bounds__(256) l2norm_bwd(float* __restrict__ dx, const uint16_t* __restrict__ x,
-                                                  const float* __restrict__ rn, long rows, int D) {
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (r >= rows) return;  // whole wavefront
-    const float n = rn[r];
-    float dot = 0.f;
-    for (int c = lane; c < D; c += 64) dot = fmaf(dx[r * D + c], __uint_as_float((uint32_t)x[r * D + c] << 16) * n, dot);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
-    const bool tiny = n >= 1e12f;
-    for (int c = lane; c < D; c += 64) {
-        const float xn = __uint_as_float((uint32_t)x[r * D + c] << 16) * n;
-        const float g = dx[r * D + c];
-        dx[r * D + c] = tiny ? g * n : n * fmaf(-dot, xn, g);
+                                                  const float* __restrict__ rn, long rows) {
+    constexpr int LPR = D / 4, RPB = 256 / LPR;
+    const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = (threadIdx.x % LPR) * 4;
+    const bool live = r < rows;
+    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint2 u = make_uint2(0u, 0u);
+    float n = 0.f;
+    if (live) {
+        gv = *reinterpret_cast<const float4*>(dx + r * D + c);
+        u = *reinterpret_cast<const uint2*>(x + r * D + c);
+        n = rn[r];
     }
+    const float g[4] = {gv.x, gv.y, gv.z, gv.w};
+    const float xn[4] = {__uint_as_float(u.x << 16) * n, __uint_as_float(u.x & 0xffff0000u) * n,
+                         __uint_as_float(u.y << 16) * n, __uint_as_float(u.y & 0xffff0000u) * n};
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot = fmaf(g[e], xn[e], dot);
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    const bool tiny = n >= 1e12f;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = tiny ? g[e] * n : n * fmaf(-dot, xn[e], g[e]);
+    if (live) *reinterpret_cast<float4*>(dx + r * D + c) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
 struct BwdLayout {
@@ -1289,9 +1309,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
                        st, kio);
     if constexpr ((PRO & 1) != 0) {  // dq, dk through the L2 norm
         const long rows = (VAR ? 1l : (long)a.B) * a.T * a.H;
-        const dim3 grid((unsigned)((rows + 3) / 4));
-        hipLaunchKernelGGL(l2norm_bwd, grid, dim3(256), 0, st, a.dq, static_cast<const uint16_t*>(a.q), rnq, rows, DK);
-        hipLaunchKernelGGL(l2norm_bwd, grid, dim3(256), 0, st, a.dk, static_cast<const uint16_t*>(a.k), rnk, rows, DK);
+        constexpr int RPB = 256 / (DK / 4);
+        const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+        hipLaunchKernelGGL(l2norm_bwd<DK>, grid, dim3(256), 0, st, a.dq, static_cast<const uint16_t*>(a.q), rnq, rows);
+        hipLaunchKernelGGL(l2norm_bwd<DK>, grid, dim3(256), 0, st, a.dk, static_cast<const uint16_t*>(a.k), rnk, rows);
     }
     return hipGetLastError();
 }
@@ -1370,9 +1391,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     if (l2n) {  // the reciprocal row norms of q and k, as the forward takes them
         rnq = reinterpret_cast<float*>(ws + L.rnq);
         rnk = reinterpret_cast<float*>(ws + L.rnk);
-        const dim3 grid((unsigned)((rows + 3) / 4));
-        hipLaunchKernelGGL(row_rnorm, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.q), rnq, rows, a.DK);
-        hipLaunchKernelGGL(row_rnorm, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.k), rnk, rows, a.DK);
+        auto norms = [&](auto dk) {
+            constexpr int D = decltype(dk)::value, RPB = 256 / (D / 8);
+            const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+            hipLaunchKernelGGL(row_rnorm<D>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.q), rnq, rows);
+            hipLaunchKernelGGL(row_rnorm<D>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.k), rnk, rows);
+        };
+        if (a.DK == 32) norms(std::integral_constant<int, 32>());
+        else if (a.DK == 64) norms(std::integral_constant<int, 64>());
+        else norms(std::integral_constant<int, 128>());
     }
     if (as || bs) {
         auto repeat = [&](const void* in, size_t off, int D) {
