@@ -1137,20 +1137,25 @@ __global__ void __launch_bounds__(256) repeat_bf16(const uint16_t* __restrict__ 
     *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(p, p, p, p);
 }
 
-// out[r] = sum over the Da entries of row r of a (plus the Db entries of row r of b, if given);
-// one wavefront per row
-__global__ void __launch_bounds__(256) row_sums(const float* __restrict__ a, int Da, const float* __restrict__ b,
-                                                int Db, float* __restrict__ out, long rows) {
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (r >= rows) return;  // whole wavefront
+// out[r] = sum over the D entries of row r of a (plus the D entries of row r of b, if given)
+template <int D>
+__global__ void __launch_bounds__(256) row_sums(const float* __restrict__ a, const float* __restrict__ b,
+                                                float* __restrict__ out, long rows) {
+    constexpr int LPR = D / 4, RPB = 256 / LPR;  // a group of D / 4 lanes per row, 16 bytes each
+    const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = (threadIdx.x % LPR) * 4;
     float acc = 0.f;
-    for (int c = lane; c < Da; c += 64) acc += a[r * Da + c];
-    if (b)
-        for (int c = lane; c < Db; c += 64) acc += b[r * Db + c];
+    if (r < rows) {  // groups are row-aligned: a group is all in or all out
+        const float4 x = *reinterpret_cast<const float4*>(a + r * D + c);
+        acc = (x.x + x.y) + (x.z + x.w);
+        if (b) {
+            const float4 y = *reinterpret_cast<const float4*>(b + r * D + c);
+            acc += (y.x + y.y) + (y.z + y.w);
+        }
+    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (lane == 0) out[r] = acc;
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (r < rows && threadIdx.x % LPR == 0) out[r] = acc;
 }
 
 // 1 / max(|x|, 1e-12) of each row of D bf16 values. A group of D / 8 lanes owns a row, one
@@ -1443,9 +1448,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
         default: e = go(std::integral_constant<int, 3>()); break;
     }
     if (e != hipSuccess || !(as || bs)) return e;
-    const dim3 grid((unsigned)((rows + 3) / 4));
-    if (as) hipLaunchKernelGGL(row_sums, grid, dim3(256), 0, s, g.dalpha, a.DK, nullptr, 0, a.dalpha, rows);
-    if (bs) hipLaunchKernelGGL(row_sums, grid, dim3(256), 0, s, g.db, a.DK, g.dw, a.DV, a.db, rows);
+    auto sums = [&](auto dk) {
+        constexpr int D = decltype(dk)::value, RPB = 256 / (D / 4);
+        const dim3 sg((unsigned)((rows + RPB - 1) / RPB));
+        if (as) hipLaunchKernelGGL(row_sums<D>, sg, dim3(256), 0, s, g.dalpha, nullptr, a.dalpha, rows);
+        if (bs) hipLaunchKernelGGL(row_sums<D>, sg, dim3(256), 0, s, g.db, g.dw, a.db, rows);
+    };
+    if (a.DK == 32) sums(std::integral_constant<int, 32>());
+    else if (a.DK == 64) sums(std::integral_constant<int, 64>());
+    else sums(std::integral_constant<int, 128>());
     return hipGetLastError();
 }
 
