@@ -221,7 +221,9 @@ gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const 
  * Supported: bf16 inputs, every gate form and prologue flag, d_k == d_v in {32, 64, 128}, and one
  * sequence's rows below 4 GiB ((T + 64)*H*d_v*4 < 2^32 bytes); anything else returns
  * GDN2_ERR_UNSUPPORTED. Arithmetic as in the forward: fp16 matrix-core operands with fp32
- * accumulation for the state chains, fp32 for the per-chunk gradient work.
+ * accumulation for the state chains and for the per-chunk products over the value channels (the
+ * chunk-start states and chunk-end state gradients are kept in fp16, the precision those
+ * products take them in), fp32 for the rest of the per-chunk gradient work.
  * The workspace (required when T > 0, 256-byte aligned, at least
  * gdn2_chunk_bwd_workspace_bytes for the same gate_flags) holds the operand blocks, the state and
  * its gradient at every chunk boundary and the per-chunk intermediate products (and, for scalar
