@@ -110,23 +110,23 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
     }
 }
 
-// dweight[c] = the sum of the nblk partials, in a fixed order: a workgroup per 16 columns,
-// thread (i, col) sums the partials j = i, i + 16, ... of its column, then the 16 sums are added
-// in order of i.
+// dweight[c] = the sum of the nblk partials, in a fixed order: a workgroup per 4 columns; thread
+// (i, q) sums the partials j = i, i + 64, ... of column 4 blockIdx + q, then the 64 sums of a
+// column are added in LDS as a fixed tree.
 __global__ void __launch_bounds__(256) rmsnorm_wsum_kernel(const float* __restrict__ part, float* __restrict__ dw,
                                                            int nblk, int D) {
     __shared__ float red[256];
-    const int col = blockIdx.x * 16 + (threadIdx.x & 15), i = threadIdx.x >> 4;
+    const int q = threadIdx.x & 3, i = threadIdx.x >> 2, col = blockIdx.x * 4 + q;
     float t = 0.f;
     if (col < D)
-        for (int j = i; j < nblk; j += 16) t += part[(size_t)j * D + col];
+        for (int j = i; j < nblk; j += 64) t += part[(size_t)j * D + col];
     red[threadIdx.x] = t;
     __syncthreads();
-    if (threadIdx.x < 16 && col < D) {
-        float u = 0.f;
-        for (int k = 0; k < 16; ++k) u += red[k * 16 + threadIdx.x];
-        dw[col] = u;
+    for (int h = 32; h >= 1; h >>= 1) {  // red[4 i + q] += red[4 (i + h) + q] for i < h
+        if (i < h) red[threadIdx.x] += red[threadIdx.x + 4 * h];
+        __syncthreads();
     }
+    if (i == 0 && col < D) dw[col] = red[q];
 }
 
 int bwd_blocks(long rows, int D) {
@@ -155,7 +155,7 @@ hipError_t launch_bwd_t(const RmsNormArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((rmsnorm_bwd_kernel<D>), dim3(nblk), dim3(256), 0, st, a.x, a.weight, a.dy, a.dx, part,
                            a.rows, a.eps);
     if (a.dweight)  // no rows: nblk = 0 and dweight = 0
-        hipLaunchKernelGGL(rmsnorm_wsum_kernel, dim3((D + 15) / 16), dim3(256), 0, st, part, a.dweight, nblk, D);
+        hipLaunchKernelGGL(rmsnorm_wsum_kernel, dim3((D + 3) / 4), dim3(256), 0, st, part, a.dweight, nblk, D);
     return hipGetLastError();
 }
 
