@@ -36,7 +36,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # HBM bytes per gdn2_chunk_fwd call at B8 H16 T4096 d128 bf16, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB copy (profiles/chunk_fwd_bf16_B8_H16_T4096_d128.txt), for the
 # kernels as they stand; set to None when a kernel changes until the counters are taken again.
-MEASURED_TRAFFIC = {"chunk": 2125.9e6, "fused": None, "recurrent": None}
+MEASURED_TRAFFIC = {"split": None, "fused": None, "recurrent": None}
 
 
 def prefill_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
@@ -51,10 +51,29 @@ def prefill_flops_per_head_token(dk: int, dv: int, C: int = 64) -> float:
 
 
 KERNELS = {
-    "chunk": "prep_kernel + chain_kernel (one gdn2_chunk_fwd call with a workspace)",
-    "fused": "chunk_kernel (one gdn2_chunk_fwd call without a workspace)",
+    "split": "prep_kernel + chain_kernel (one gdn2_chunk_fwd call with the two-kernel workspace)",
+    "fused": "fused_kernel (one gdn2_chunk_fwd call without a workspace: allocation-free)",
     "recurrent": "recurrent_kernel (gdn2_recurrent_fwd)",
 }
+
+
+def prefill_kwargs(g, impl, B, T, H, dk, dv, ring_mb=None):
+    """Keyword arguments of chunk_fwd for one schedule, with any workspace allocated up front so
+    that no allocation falls inside a timed region."""
+    import torch
+    if impl == "recurrent":
+        return {}
+    kw = dict(schedule=impl)
+    if impl == "split":
+        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
+        if need and ring_mb is not None:
+            state = B * H * dk * dv * 4
+            per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv) - state
+            slots = max(1, int(ring_mb * 2**20) // per_chunk)
+            need = min(need, state + slots * per_chunk)
+        if need:
+            kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
+    return kw
 
 
 def decode_bytes_per_head(dk: int, dv: int) -> float:
@@ -69,18 +88,7 @@ def time_prefill(g, ins, steps, warmup, impl, ring_mb=None, **flags):
     dv = ins["v"].shape[-1]
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.float32)
     S_out = torch.empty(B, H, dk, dv, device="cuda", dtype=torch.float32)
-    kw = dict(o=o, S_out=S_out)
-    if impl == "chunk":
-        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
-        if need and ring_mb is not None:
-            state = B * H * dk * dv * 4
-            per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv) - state
-            slots = max(1, int(ring_mb * 2**20) // per_chunk)
-            need = min(need, state + slots * per_chunk)
-        if need:
-            kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
-    elif impl == "fused":
-        kw["fused"] = True
+    kw = dict(o=o, S_out=S_out, **prefill_kwargs(g, impl, B, T, H, dk, dv, ring_mb))
     kw.update(flags)
     for _ in range(warmup):
         fn(*args, ins["S0"], **kw)
@@ -109,13 +117,7 @@ def time_prefill_cold(g, ins, reps, impl):
     dv = ins["v"].shape[-1]
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.float32)
     S_out = torch.empty(B, H, dk, dv, device="cuda", dtype=torch.float32)
-    kw = dict(o=o, S_out=S_out)
-    if impl == "fused":
-        kw["fused"] = True
-    elif impl == "chunk":
-        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
-        if need:
-            kw["workspace"] = torch.empty(need, device="cuda", dtype=torch.uint8)
+    kw = dict(o=o, S_out=S_out, **prefill_kwargs(g, impl, B, T, H, dk, dv))
     fn = g.recurrent_fwd if impl == "recurrent" else g.chunk_fwd
     scrub = torch.empty(1 << 27, device="cuda", dtype=torch.float32)  # 512 MiB
     stream = torch.cuda.current_stream()
@@ -372,9 +374,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--impl", choices=["chunk", "fused", "recurrent"], default="chunk",
-                    help="chunk: two-kernel chunkwise path (with workspace); fused: single-kernel "
-                         "chunkwise path; recurrent: token-by-token kernel")
+    ap.add_argument("--impl", choices=["split", "fused", "recurrent"], default="split",
+                    help="split: two-kernel chunkwise path (with its workspace, the fastest); fused: "
+                         "fused chunkwise kernel (no workspace, allocation-free); recurrent: "
+                         "token-by-token kernel")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128)
@@ -425,7 +428,7 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     prologue = None
-    if args.impl == "chunk" and args.workload == "prefill_1p3b":
+    if args.impl != "recurrent" and args.workload == "prefill_1p3b":
         # the same call with the fused prologue (q, k normalised and the gates taken from
         # pre-activations inside the kernels; the inputs serve as pre-activations)
         _, pk = time_prefill(g, ins, max(5, args.steps // 2), 1, args.impl, l2norm=True, gate_logits=True)
@@ -450,7 +453,7 @@ def main(argv=None):
     others = {}
     bwd = None
     packed = None
-    if not args.skip_others and args.workload == "prefill_1p3b" and args.impl == "chunk":
+    if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
         packed = varlen_leg(g, 10, kern_avg)
     if not args.skip_backward and args.workload == "prefill_1p3b":
         bwd = backward_leg(g, 5)

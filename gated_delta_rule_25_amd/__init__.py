@@ -156,18 +156,20 @@ def _state_out(S0, B, H, dk, dv, device, S_out):
 
 
 def chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
+    """Workspace bytes of gdn2_chunk_fwd's two-kernel path at these sizes (0: it does not take them)."""
     return int(load().gdn2_chunk_fwd_workspace_bytes(B, T, H, d_k, d_v,
                                                      BF16 if dtype == torch.bfloat16 else F32,
                                                      flags))
 
 
 def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspace=None,
-              fused=False, l2norm=False, gate_logits=False, stream=None):
+              schedule="split", l2norm=False, gate_logits=False, stream=None):
     """Chunkwise prefill (C = 64). Returns (o [B, T, H, d_v] fp32, S_T [B, H, d_k, d_v]).
 
-    With a workspace (allocated here unless given) the library runs its two-kernel path;
-    fused=True passes none and runs the single-kernel path. l2norm / gate_logits: the kernels
-    normalise q, k and take the gates through the sigmoid themselves (two-kernel path only).
+    schedule: "split" (the default) passes the two-kernel path's workspace where it takes the sizes
+    (allocated here unless given); "fused" passes none: the fused kernel, allocating nothing (or the
+    single kernel for sizes the fused kernel does not take). l2norm / gate_logits: the kernels
+    normalise q, k and take the gates through the sigmoid themselves.
     """
     lib = load()
     flags = _check_inputs(q, k, v, alpha, b, w, 4) | _prologue_flags(l2norm, gate_logits)
@@ -177,7 +179,9 @@ def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspa
         o = torch.empty(B, T, H, dv, device=q.device, dtype=torch.float32)
     S_out = _state_out(S0, B, H, dk, dv, q.device, S_out)
     dt = _dtype_code(q)
-    need = 0 if fused else int(lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
+    if schedule not in ("fused", "split"):
+        raise ValueError("schedule must be 'split' or 'fused'")
+    need = 0 if schedule == "fused" else int(lib.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
     if need and workspace is None:
         workspace = _scratch(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -141,6 +141,8 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && S0) ? S0[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] : 0.f;
+    int esc = 0;  // the state is held times sc = 2^esc (fp16 operands; see rescale_state)
+    float sc = 1.f, isc = 1.f;
 
     // Inputs of one chunk row for this lane, loaded one chunk ahead. The loads of the next
     // chunk are issued in portions spread over the current one, each as soon as its registers
@@ -544,6 +546,13 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         // ---------------- F: the state chain for this wave's 16 columns ----------------
         if (more) fetch(n + 1, 2);
         if (chain) {
+            // D' starts as U = w v (times sc for fp16 operands, see chunk_common.h rescale_state)
+            f4 D[4], O[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) D[mt][j] = U32[(16 * mt + 4 * g + j) * UP + 16 * wv + l16];
+            if constexpr (F16) rescale_state<NMK>(Sacc, D, esc, sc, isc);
             // state as B operand: K-step s covers channels 32s..32s+31 = tiles 2s, 2s+1
             Frag Sf[NKS];
 #pragma unroll
@@ -559,11 +568,8 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
             // D' = U - E_hat S, and O^T = S^T Q_hat^T: the state fragments serve as the A
             // operand of the transposed product, so O^T tile nt holds, per lane, four
             // consecutive state columns (rows 4g..4g+3) of token 16 nt + l16.
-            f4 D[4], O[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) D[mt][j] = U32[(16 * mt + 4 * g + j) * UP + 16 * wv + l16];
                 O[mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NKS; ++s) {
@@ -615,8 +621,8 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
                 }
                 const unsigned row = (unsigned)(t0 + 16 * nt + l16);
-                store4(rs_o, ((row * H + hh) * DV + tile * DVT + 16 * wv + 4 * g) * 4u, O[nt][0], O[nt][1], O[nt][2],
-                       O[nt][3]);
+                store4(rs_o, ((row * H + hh) * DV + tile * DVT + 16 * wv + 4 * g) * 4u, O[nt][0] * isc, O[nt][1] * isc,
+                       O[nt][2] * isc, O[nt][3] * isc);
             }
             // S <- Diag(gamma_last) S + K_bar^T Delta
 #pragma unroll
@@ -643,7 +649,7 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         for (int mk = 0; mk < NMK; ++mk)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                S_out[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] = Sacc[mk][j];
+                S_out[sbase + (long)(16 * mk + 4 * g + j) * DV + mycol] = Sacc[mk][j] * isc;
     }
 }
 

@@ -209,6 +209,71 @@ __device__ __forceinline__ void lds_read8f(const float* p, float* x) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Largest value over the wavefront: rotations within each row of 16 lanes (DPP row_ror), then the
+// four row results read into scalars.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, row_ror<8>(x));
+    x = fmaxf(x, row_ror<4>(x));
+    x = fmaxf(x, row_ror<2>(x));
+    x = fmaxf(x, row_ror<1>(x));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Range of the fp16 matrix-core operands. A chain wave holds its state columns times sc = 2^esc
+// (the same for the wave) and multiplies this chunk's U = w v, the first operand it forms from
+// them, by the same sc; D', Delta, O and the state update are then all times sc, and o and the
+// final state are multiplied by isc = 2^-esc on the way out (exact: powers of two). Before the
+// state and D' are rounded to fp16 for a chunk's products, esc is renewed when the wave's largest
+// |S sc| or |U sc| leaves [2^-4, 2^8]: the new esc brings it to [2^3, 2^4). The upper end keeps
+// E_hat S and the products after it far below fp16's largest finite value (65504) for gates in
+// [0, 1] and keys of norm 1; the lower end keeps the state's leading digits out of fp16's
+// subnormal range. esc stays within [-100, 100] (a state that has decayed below about 2^-96 along
+// with its inputs is let go to fp16's subnormals and zero, where it no longer matters next to
+// anything of normal size) and moves by at most 120 per chunk, so sc, isc and the step factor are
+// finite normal floats. A non-finite maximum (a NaN in the inputs) leaves esc as it is.
+// Sacc: the wave's state tiles (NMK 16-row tiles of its 16 columns); D: this chunk's U = w v rows
+// in accumulator layout, multiplied by sc here.
+template <int NMK>
+__device__ __forceinline__ void rescale_state(f4 (&Sacc)[NMK], f4 (&D)[4], int& esc, float& sc, float& isc) {
+    float ms = 0.f, mu = 0.f;
+#pragma unroll
+    for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ms = fmaxf(ms, fabsf(Sacc[mk][j]));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mu = fmaxf(mu, fabsf(D[mt][j]));
+    const float mm = wave_max(fmaxf(ms, mu * sc));
+    if ((mm > 256.f && mm <= 3.0e38f) || (mm < 0.0625f && mm > 0.f)) {  // uniform over the wave
+        const int e = __builtin_amdgcn_frexp_expf(mm);                  // mm in [2^(e-1), 2^e)
+        const int step = min(max(4 - e, -120), 120);
+        const int en = min(max(esc + step, -100), 100);
+        if (en != esc) {
+            const float r = __builtin_ldexpf(1.f, en - esc);
+            esc = en;
+            sc = __builtin_ldexpf(1.f, en);
+            isc = __builtin_ldexpf(1.f, -en);
+#pragma unroll
+            for (int mk = 0; mk < NMK; ++mk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Sacc[mk][j] *= r;
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) D[mt][j] *= sc;
+}
+
 // Per-(block, channel) decay tables, index t of tab[t][DK] (log2 domain, X = local value at a
 // block's 8th row, G_I = sum of earlier block totals, gC = chunk total):
 //   0..3 exp2(X_I)   4..7 exp2(G_I)   8..11 exp2(tot_I - X_I)   12..15 exp2(gC - G_{I+1})

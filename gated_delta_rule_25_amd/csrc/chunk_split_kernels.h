@@ -712,6 +712,15 @@ chain_kernel(const ChainIO io) {
                 Sacc[c][mk][j] = x0;
             }
 
+    // fp16 operands (bf16 inputs): the state and each chunk's products are held times sc, a power
+    // of two per wave (isc = 1 / sc), so that they stay inside fp16's range whatever the state's
+    // magnitude; exact in binary. The state-only pass that saves states for the backward keeps
+    // sc = 1 (its saved fp16 values are read unscaled).
+    constexpr bool SCALE = F16 && !SAVE;
+    static_assert(!SCALE || NT == 1, "the scale is renewed over one 16-column tile per wave");
+    int esc = 0;
+    float sc = 1.f, isc = 1.f;
+
     // v and w rows of this wave's columns for one chunk, copied into the wave's LDS slot through
     // buffer resources over this sequence's rows: rows past the sequence end fall outside the
     // buffer and arrive as zeros. The host keeps the byte offsets below 2^31. A scalar beta comes
@@ -827,6 +836,7 @@ chain_kernel(const ChainIO io) {
                         if constexpr (WSIG && !BS) ww = sigmoidf_(ww);
                         D[c][mt][j] = phi ? 0.f : ww * raw_f(v_l[slot * ROW + cl]);
                     }
+            if constexpr (SCALE) rescale_state<NMK>(Sacc[0], D[0], esc, sc, isc);
             float4 gcv[NMK];  // gamma_last of this lane's state rows
 #pragma unroll
             for (int mk = 0; mk < NMK; ++mk) gcv[mk] = *reinterpret_cast<const float4*>(gC + 16 * mk + 4 * g);
@@ -927,8 +937,8 @@ chain_kernel(const ChainIO io) {
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                     for (int c = 0; c < NT; ++c)
-                        store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0], O[c][nt][1], O[c][nt][2],
-                               O[c][nt][3]);
+                        store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0] * isc, O[c][nt][1] * isc,
+                               O[c][nt][2] * isc, O[c][nt][3] * isc);
             }
         } else if (copier) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
@@ -948,7 +958,7 @@ chain_kernel(const ChainIO io) {
             for (int mk = 0; mk < NMK; ++mk)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    s_out[(long)(16 * mk + 4 * g + j) * io.out_ld + col0 + 16 * c + l16] = Sacc[c][mk][j];
+                    s_out[(long)(16 * mk + 4 * g + j) * io.out_ld + col0 + 16 * c + l16] = Sacc[c][mk][j] * isc;
     }
 }
 

@@ -214,6 +214,7 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
     if (st != GDN2_OK) return st;
     if (!chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
     const bool bf16 = in_dtype == GDN2_BF16;
+    const bool fused = gdn2::fused_supported(T, H, d_k, d_v, bf16);
     const bool split = workspace && workspace_bytes > 0 && gdn2::split_supported(T, H, d_k, d_v, bf16);
     if (split) {
         const size_t min_bytes = split_min_bytes(B, H, d_k, d_v, bf16);
@@ -230,8 +231,8 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                                 range_of(S0, sz.state * 4), range_of(o, sz.vw * 4), range_of(S_out, sz.state * 4)};
         for (const Range& r : others)
             if (overlap(rws, r)) return GDN2_ERR_ALIAS;
-    } else if (!gdn2::chunk_supported(T, H, d_k, d_v, bf16) ||
-               (gate_flags & (GDN2_QK_L2NORM | GDN2_GATE_LOGITS))) {  // no prologue on this path
+    } else if (!fused && (!gdn2::chunk_supported(T, H, d_k, d_v, bf16) ||
+                          (gate_flags & (GDN2_QK_L2NORM | GDN2_GATE_LOGITS)))) {  // no prologue on the single kernel
         return GDN2_ERR_UNSUPPORTED;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -240,8 +241,8 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                              gate_flags, s);
     }
     gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, bf16, gate_flags,
-                      workspace, workspace_bytes};
-    const hipError_t e = split ? gdn2::launch_split(a, s) : gdn2::launch_chunk(a, s);
+                      split ? workspace : nullptr, split ? workspace_bytes : 0};
+    const hipError_t e = split ? gdn2::launch_split(a, s) : fused ? gdn2::launch_fused(a, s) : gdn2::launch_chunk(a, s);
     if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }

@@ -57,6 +57,12 @@ struct ChunkArgs {
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
 bool chunk_supported(int T, int H, int DK, int DV, bool bf16);
 
+// Fused path (no workspace): one kernel per (b, h, 64-column tile) whose prep wavefronts build the
+// next chunk's operands in LDS while its chain wavefronts run the current chunk. bf16, d_k = d_v in
+// {64, 128}, every gate form and prologue flag.
+hipError_t launch_fused(const ChunkArgs& a, hipStream_t s);
+bool fused_supported(int T, int H, int DK, int DV, bool bf16);
+
 // Two-kernel path (prep + chain) through a workspace ring of per-chunk operand blobs.
 // Workspace = state buffer (B*H*DK*DV fp32) + R chunk slots of split_chunk_bytes each; with a
 // slot for every chunk plus the segment buffers (split_workspace_bytes), a long sequence with few

@@ -30,9 +30,11 @@ __device__ __forceinline__ float group_sum(float v) {  // over the LPR lanes of 
     return v;
 }
 
+// x and y are not __restrict__: y may be x (in place, fp32); each lane loads its four elements
+// before it stores the same four.
 template <int D, bool BF16OUT>
-__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, const float* __restrict__ wt,
-                                                          void* __restrict__ y, long rows, float eps) {
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* x, const float* __restrict__ wt, void* y,
+                                                          long rows, float eps) {
     constexpr int LPR = D / 4, RPB = 256 / LPR;  // lanes per row, rows per workgroup
     const int c = (threadIdx.x % LPR) * 4;
     const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -81,7 +83,9 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
             const long r = r0 + j * RPB + threadIdx.x / LPR;
             const float4 a = v[j], e = d[j];
             const float ss = group_sum<LPR>(a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w);
-            const float s = 1.f / sqrtf(ss * (1.f / D) + eps);
+            // rows past the end (x = dy = 0) take s = 0, so that they add nothing to the weight
+            // gradient even when eps = 0 (where 1 / sqrt(0) would make 0 * inf = NaN)
+            const float s = r < rows ? 1.f / sqrtf(ss * (1.f / D) + eps) : 0.f;
             const float4 xh{a.x * s, a.y * s, a.z * s, a.w * s};
             const float4 u{e.x * g.x, e.y * g.y, e.z * g.z, e.w * g.w};
             const float m = group_sum<LPR>(xh.x * u.x + xh.y * u.y + xh.z * u.z + xh.w * u.w) * (1.f / D);

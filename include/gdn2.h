@@ -42,8 +42,9 @@
  * synchronisation. Nothing is printed and nothing aborts.
  *
  * Preconditions not checked on the device: finite inputs; alpha in (0, 1] on the prefill
- * path (it takes log alpha); |S|, |o| and the per-chunk intermediates below 6.5e4 on the
- * bf16 prefill path (its matrix-core operands are fp16).
+ * path (it takes log alpha); on the bf16 prefill paths, the per-chunk operands formed from q, k,
+ * b and the decay below 6.5e4 (their matrix-core operands are fp16; see gdn2_chunk_fwd), and for
+ * the backward also the state and its gradient below 6.5e4.
  */
 #ifndef GDN2_H
 #define GDN2_H
@@ -76,10 +77,10 @@ enum {
                                w must be NULL */
     /* Prologue flags: the steps in front of the recurrence done inside the kernels, in fp32, on
      * the inputs as given [GDN2-summary, paragraph "Архитектурно": L2-normalised q/k, sigmoid
-     * gates]. Taken by the two-kernel prefill (gdn2_chunk_fwd with a workspace), the packed
-     * prefill, the token-by-token prefill, the decode step and gdn2_chunk_bwd (which then gives
-     * the gradients with respect to the raw inputs); the single-kernel prefill returns
-     * GDN2_ERR_UNSUPPORTED for them. */
+     * gates]. Taken by the two-kernel and the fused prefill, the packed prefill, the
+     * token-by-token prefill, the decode step and gdn2_chunk_bwd (which then gives the gradients
+     * with respect to the raw inputs); the single-kernel prefill (no workspace, sizes the fused
+     * kernel does not take) returns GDN2_ERR_UNSUPPORTED for them. */
     GDN2_QK_L2NORM = 4u,   /* q and k are normalised per token and head over d_k:
                               x / max(|x|_2, 1e-12) */
     GDN2_GATE_LOGITS = 8u  /* alpha, b, w (or the scalar forms) hold pre-activations x; the
@@ -98,25 +99,34 @@ enum {
  * fp32 accumulation and an fp32 state; fp32 inputs are computed in fp32 throughout.
  *
  * The workspace selects how the chunks are scheduled; the result is the same either way.
- *  - workspace != NULL with workspace_bytes > 0 (and the sizes supported below): two kernels. A prep kernel, parallel
- *    over every (b, h, chunk), computes each chunk's decay-scaled factors, its 64x64 Gram
- *    products and the UT inverse T, and stores them as one operand block per chunk in the
- *    workspace; a chain kernel then runs the state recurrence chunk by chunk from those blocks.
- *    Supported: bf16 with d in {32, 64, 128}, fp32 with d = 32. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v] first
- *    when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand blocks.
- *    R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with
+ *  - workspace != NULL with workspace_bytes > 0 (and the sizes supported below): two kernels. A
+ *    prep kernel, parallel over every (b, h, chunk), computes each chunk's decay-scaled factors,
+ *    its 64x64 Gram products and the UT inverse T, and stores them as one operand block per chunk
+ *    in the workspace; a chain kernel then runs the state recurrence chunk by chunk from those
+ *    blocks. The fastest schedule at every size it takes. Supported: bf16 with d in {32, 64, 128},
+ *    fp32 with d = 32, any flags. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v]
+ *    first when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand
+ *    blocks. R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with
  *    fewer slots than chunks the two kernels alternate over rounds of R chunks. When B*H is too
  *    small to fill the GPU and the sequence is long, a workspace of the size the query returns
  *    also holds per-segment buffers: the sequence is cut into segments whose state transitions
- *    are computed in parallel and combined by a scan, so the chain runs all segments at once
- *    (the result is the same recurrence, up to rounding). The buffer must
- *    be 256-byte aligned (else GDN2_ERR_ALIGN), hold the state and one slot (else
- *    GDN2_ERR_WORKSPACE) and overlap no input or output (else GDN2_ERR_ALIAS). Its contents
- *    are scratch on entry and on return.
- *  - no workspace, or sizes the two-kernel path does not take: one kernel, one workgroup
- *    per (b, h, 64-column tile of the state) computing each chunk's factors and then its part
- *    of the state recurrence. Supported: bf16 with d in {32, 64, 128}, fp32 with d in {32, 64};
- *    other sizes return GDN2_ERR_UNSUPPORTED.
+ *    are computed in parallel and combined by a scan, so the chain runs all segments at once (the
+ *    result is the same recurrence, up to rounding). The buffer must be 256-byte aligned (else
+ *    GDN2_ERR_ALIGN), hold the state and one slot (else GDN2_ERR_WORKSPACE) and overlap no input or
+ *    output (else GDN2_ERR_ALIAS). Its contents are scratch on entry and on return.
+ *  - no workspace (NULL or workspace_bytes == 0), bf16 with d in {64, 128}: the fused kernel, which
+ *    allocates nothing and takes every gate form and prologue flag. One workgroup per (b, h,
+ *    64-column tile of the state): four of its wavefronts run the state recurrence of chunk n while
+ *    four others compute chunk n + 1's factors, Gram products and T into a second LDS buffer, so no
+ *    operand goes through HBM (the algorithmic bytes only).
+ *  - no workspace, other sizes: one kernel, one workgroup per (b, h, 64-column tile) computing
+ *    each chunk's factors and then its part of the state recurrence. Supported: bf16 with d = 32,
+ *    fp32 with d in {32, 64}; no prologue flags (GDN2_ERR_UNSUPPORTED).
+ * Range: the bf16 paths round their products' operands to fp16. The state, and every per-chunk
+ * product formed from it and from v, are held times a power of two chosen per wavefront and chunk
+ * (exact), so the state may take any magnitude fp32 holds; the operands formed from q, k, b and the
+ * decay (scaled q and k, the Gram blocks and T) must stay below 6.5e4, which holds for
+ * L2-normalised q and k and gates in [0, 1].
  * d_k must equal d_v, and one sequence's o must stay below 4 GiB (T*H*d_v*4 < 2^32 bytes: the
  * kernels address a sequence's rows with 32-bit offsets), else GDN2_ERR_UNSUPPORTED. Any flags
  * above.
@@ -130,7 +140,7 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
 /* Workspace bytes for the two-kernel path of gdn2_chunk_fwd at these sizes: the state buffer
  * (when S_out may be NULL), one slot per chunk so that one round covers the sequence, and the
  * segment buffers when the sizes are segmented. 0 when the two-kernel path does not take these
- * sizes (pass NULL; the single kernel runs). */
+ * sizes (pass NULL; the fused or the single kernel runs). */
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags);
 

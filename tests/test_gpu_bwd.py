@@ -63,6 +63,10 @@ CASES = [
     ("d128_T65", scaled(WORKLOADS["prefill_1p3b"], B=1, T=65, H=2)),
     ("d128_zero_s0", scaled(WORKLOADS["prefill_1p3b"], B=1, T=300, H=2, s0_std=0.0)),
     ("d128_slow_decay", scaled(WORKLOADS["long_prefill"], B=1, T=700, H=2)),
+    # alpha = sigmoid(N(-2, 1)): most of a chunk's decay products reach far below 2^-24, which
+    # the key kernel's block-reference factors and the reverse chain's gamma must carry
+    ("d128_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=1, T=260, H=3, alpha_mu=-2.0)),
+    ("d64_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=2, T=130, H=2, d_k=64, d_v=64, alpha_mu=-2.0)),
 ]
 
 

@@ -43,12 +43,17 @@ def _run(ins, **kw):
     return out
 
 
-def _check(name, ins, tol, fused=False):
+def _check(name, ins, tol, schedule="split"):
     o_ref, S_ref = _oracle(ins)
-    o, S_T = _run(ins, fused=fused)
+    o, S_T = _run(ins, schedule=schedule)
     eo, es = normwise_err(o, o_ref), normwise_err(S_T, S_ref)
-    print(f"  {name} ({'fused' if fused else 'split'}): o err {eo:.2e}  S_T err {es:.2e}", flush=True)
+    print(f"  {name} ({schedule}): o err {eo:.2e}  S_T err {es:.2e}", flush=True)
     assert eo <= tol and es <= tol, (eo, es)
+
+
+# split: two kernels through operand blocks (with a workspace); fused: no workspace (the fused
+# kernel, or the single kernel for sizes it does not take)
+SCHEDULES = ["split", "fused"]
 
 
 FP32_CASES = [
@@ -63,11 +68,11 @@ FP32_CASES = [
 ]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("name,wl", FP32_CASES, ids=[c[0] for c in FP32_CASES])
-def test_chunk_fp32_matches_oracle(name, wl, fused):
-    banner(f"chunk fp32 {name} fused={fused} {wl}")
-    _check(name, make_inputs(wl), TOL32, fused)
+def test_chunk_fp32_matches_oracle(name, wl, schedule):
+    banner(f"chunk fp32 {name} schedule={schedule} {wl}")
+    _check(name, make_inputs(wl), TOL32, schedule)
 
 
 BF16_CASES = [
@@ -87,11 +92,11 @@ BF16_CASES = [
 ]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("name,wl", BF16_CASES, ids=[c[0] for c in BF16_CASES])
-def test_chunk_bf16_matches_oracle(name, wl, fused):
-    banner(f"chunk bf16 {name} fused={fused} {wl}")
-    _check(name, make_inputs(wl), TOL16, fused)
+def test_chunk_bf16_matches_oracle(name, wl, schedule):
+    banner(f"chunk bf16 {name} schedule={schedule} {wl}")
+    _check(name, make_inputs(wl), TOL16, schedule)
 
 
 def test_chunk_zero_tokens_copies_state():
@@ -176,12 +181,12 @@ FULL = [
 ]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("name,wl", FULL, ids=[c[0] for c in FULL])
-def test_chunk_full_size_all_heads(name, wl, fused):
+def test_chunk_full_size_all_heads(name, wl, schedule):
     """The benchmark's launch configuration, B8 H16 T4096 d128, every head against the oracle."""
-    banner(f"chunk full {name} fused={fused}")
-    _check(name, make_inputs(wl), TOL16, fused)
+    banner(f"chunk full {name} schedule={schedule}")
+    _check(name, make_inputs(wl), TOL16, schedule)
 
 
 def test_chunk_split_small_ring():
@@ -196,7 +201,7 @@ def test_chunk_split_small_ring():
     per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dk) - B * H * dk * dk * 4
     ws = torch.empty(B * H * dk * dk * 4 + 3 * per_chunk, dtype=torch.uint8, device="cuda")
     o, S_T = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"],
-                         workspace=ws)
+                         workspace=ws, schedule="split")
     torch.cuda.synchronize()
     o_ref, S_ref = _oracle(ins)
     assert normwise_err(o, o_ref) <= TOL16 and normwise_err(S_T, S_ref) <= TOL16
@@ -212,6 +217,8 @@ SEGMENTED = [
     ("seg_bf16_kda", scaled(WORKLOADS["kda_scalar"], B=1, T=2100, H=2), TOL16),
     ("seg_bf16_d64", scaled(WORKLOADS["prefill_1p3b"], B=1, T=2500, H=2, d_k=64, d_v=64), TOL16),
     ("seg_fp32_d32", scaled(WORKLOADS["tiny_fp32"], B=1, T=2100, H=1, s0_std=0.1), TOL32),
+    # strong decay: the segments' transitions decay far below fp32's normal range over a segment
+    ("seg_bf16_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=1, T=3000, H=2, alpha_mu=-2.0), TOL16),
 ]
 
 
@@ -224,7 +231,7 @@ def test_chunk_segmented_matches_oracle(name, wl, tol):
     # the workspace query includes the segment buffers exactly when the sizes are segmented
     assert g.chunk_fwd_workspace_bytes(B, T, H, d, d, dtype=dt) > B * H * d * d * 4 + \
         ((T + 63) // 64) * (g.chunk_fwd_workspace_bytes(B, 64, H, d, d, dtype=dt) - B * H * d * d * 4)
-    _check(name, make_inputs(wl), tol)
+    _check(name, make_inputs(wl), tol, "split")
 
 
 def test_chunk_segmented_in_place_state():

@@ -62,14 +62,17 @@ def _inputs(wl, l2n, gl):
     return ins
 
 
+@pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("name,wl,l2n,gl,tol", CASES, ids=[c[0] for c in CASES])
-def test_chunk_prologue_matches_oracle(name, wl, l2n, gl, tol):
-    banner(f"prologue chunk {name} l2norm={l2n} logits={gl} {wl}")
+def test_chunk_prologue_matches_oracle(name, wl, l2n, gl, tol, schedule):
+    if schedule == "fused" and wl.dtype == "fp32":
+        pytest.skip("fp32 inputs run the single kernel without a workspace, which takes no prologue flags")
+    banner(f"prologue chunk {name} l2norm={l2n} logits={gl} schedule={schedule} {wl}")
     ins = _inputs(wl, l2n, gl)
     o_ref, S_ref = _oracle(ins, l2n, gl)
     d = _cuda(ins)
     o, S_T = _g().chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"],
-                            l2norm=l2n, gate_logits=gl)
+                            l2norm=l2n, gate_logits=gl, schedule=schedule)
     torch.cuda.synchronize()
     eo, es = normwise_err(o, o_ref), normwise_err(S_T, S_ref)
     print(f"  {name}: o err {eo:.2e}  S_T err {es:.2e}", flush=True)
@@ -107,9 +110,10 @@ def test_decode_prologue_matches_oracle():
 
 
 def test_single_kernel_path_refuses_the_prologue():
+    """fp32 inputs without a workspace run the single kernel, which does not take the flags."""
     g = _g()
-    wl = scaled(WORKLOADS["prefill_1p3b"], B=1, T=64, H=1)
+    wl = scaled(WORKLOADS["tiny_fp32"], B=1, T=64, H=1)
     d = _cuda(make_prologue_inputs(wl))
     with pytest.raises(g.Gdn2Error) as e:
-        g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"], fused=True, l2norm=True)
+        g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"], schedule="fused", l2norm=True)
     assert e.value.status == 3

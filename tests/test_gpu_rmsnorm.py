@@ -36,7 +36,7 @@ CASES = [(d, rows) for d in (32, 64, 128, 256) for rows in (1, 7, 1000)] + [(128
 
 
 @pytest.mark.parametrize("d,rows", CASES, ids=[f"d{d}_rows{r}" for d, r in CASES])
-@pytest.mark.parametrize("eps", [1e-6, 0.1])
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.1])
 def test_rmsnorm_matches_oracle(d, rows, eps):
     banner(f"rmsnorm d={d} rows={rows} eps={eps}")
     g = _g()
