@@ -27,7 +27,7 @@ import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
            "chunk_bwd_workspace_bytes", "chunk_bwd_varlen", "chunk_bwd_varlen_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
-           "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd"]
+           "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
@@ -36,7 +36,8 @@ _lib = None
 BF16, F32 = 0, 1
 ALPHA_SCALAR, BETA_SCALAR, QK_L2NORM, GATE_LOGITS = 1, 2, 4, 8
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
-           4: "GDN2_ERR_ALIGN", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP", 7: "GDN2_ERR_WORKSPACE"}
+           4: "GDN2_ERR_ALIGN", 5: "GDN2_ERR_ALIAS", 6: "GDN2_ERR_HIP", 7: "GDN2_ERR_WORKSPACE",
+           8: "GDN2_ERR_SCRATCH"}
 
 
 class Gdn2Error(RuntimeError):
@@ -85,6 +86,8 @@ def load():
     lib.gdn2_rmsnorm_fwd.restype = ctypes.c_int
     lib.gdn2_rmsnorm_bwd.argtypes = [p] * 5 + [i64, i32, f32, p, sz, p]
     lib.gdn2_rmsnorm_bwd.restype = ctypes.c_int
+    lib.gdn2_rmsnorm_bwd_noalloc.argtypes = [p] * 5 + [i64, i32, f32, p]
+    lib.gdn2_rmsnorm_bwd_noalloc.restype = ctypes.c_int
     lib.gdn2_rmsnorm_bwd_workspace_bytes.argtypes = [i64, i32]
     lib.gdn2_rmsnorm_bwd_workspace_bytes.restype = sz
     lib.gdn2_status_str.argtypes = [ctypes.c_int]
@@ -398,4 +401,22 @@ def rmsnorm_bwd(x, weight, dy, *, eps: float = 1e-6, dx=None, need_dweight: bool
                               _ptr(ws), need, _stream(stream))
     if st != 0:
         raise Gdn2Error("gdn2_rmsnorm_bwd", st)
+    return dict(dx=dx, dweight=dweight)
+
+
+def rmsnorm_bwd_noalloc(x, weight, dy, *, eps: float = 1e-6, dx, dweight=None, stream=None):
+    """rmsnorm_bwd through gdn2_rmsnorm_bwd_noalloc: the caller passes every output (dx [rows, d],
+    dweight [d] float32 or None) and the library uses its own fixed device scratch, so this call
+    allocates nothing. Returns dict(dx, dweight)."""
+    lib = load()
+    rows, d = _norm_rows(x, "x")
+    _norm_rows(dy, "dy")
+    if dx is None or dx.shape != x.shape or dx.dtype != torch.float32 or not dx.is_contiguous():
+        raise ValueError("dx must be a contiguous float32 tensor shaped like x")
+    if dweight is not None and (dweight.dtype != torch.float32 or dweight.numel() != d or not dweight.is_contiguous()):
+        raise ValueError("dweight must be a contiguous float32 tensor of d elements")
+    st = lib.gdn2_rmsnorm_bwd_noalloc(_ptr(x), _ptr(weight), _ptr(dy), _ptr(dx), _ptr(dweight), rows, d, float(eps),
+                                      _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_rmsnorm_bwd_noalloc", st)
     return dict(dx=dx, dweight=dweight)

@@ -180,6 +180,45 @@ gdn2_status run_bwd(const void* q, const void* k, const void* v, const void* alp
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+// The checks and launch of gdn2_rmsnorm_bwd. With fixed_scratch, the dweight partials go to the
+// library's own device array (no workspace argument, nothing allocated).
+gdn2_status rmsnorm_bwd_checked(const float* x, const float* weight, const float* dy, float* dx, float* dweight,
+                                int64_t rows, int32_t d, float eps, void* workspace, size_t workspace_bytes,
+                                bool fixed_scratch, void* stream) {
+    if (rows < 0 || (uint64_t)rows > (1ull << 40)) return GDN2_ERR_SHAPE;
+    if (!dim_ok_tok(d) || !(eps >= 0.f && eps <= 3.0e38f)) return GDN2_ERR_UNSUPPORTED;
+    if (rows > 0 && (!x || !dy || !dx)) return GDN2_ERR_NULL;
+    const void* ptrs[] = {x, weight, dy, dx, dweight};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
+    const size_t need = dweight ? gdn2::rmsnorm_bwd_workspace_bytes((long)rows, d) : 0;
+    if (fixed_scratch) {
+        workspace = nullptr;  // looked up below, after every argument check
+    } else if (need > 0) {
+        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return GDN2_ERR_ALIGN;
+    }
+    if (rows == 0 && !dweight) return GDN2_OK;
+    const uint64_t n = (uint64_t)rows * (uint64_t)d;
+    const Range rx = range_of(x, n * 4), rwt = range_of(weight, (uint64_t)d * 4), rdy = range_of(dy, n * 4),
+                rdx = range_of(dx, n * 4), rdw = range_of(dweight, (uint64_t)d * 4),
+                rws = range_of(need && !fixed_scratch ? workspace : nullptr, need);
+    // dx may be dy itself (each lane reads its dy before it writes the same elements of dx)
+    if (overlap(rdx, rx) || overlap(rdx, rwt) || (overlap(rdx, rdy) && dx != dy) || overlap(rdx, rdw) ||
+        overlap(rdx, rws))
+        return GDN2_ERR_ALIAS;
+    if (overlap(rdw, rx) || overlap(rdw, rwt) || overlap(rdw, rdy) || overlap(rdw, rws)) return GDN2_ERR_ALIAS;
+    if (overlap(rws, rx) || overlap(rws, rwt) || overlap(rws, rdy)) return GDN2_ERR_ALIAS;
+    if (fixed_scratch && need > 0) {  // the library's own array on the current device
+        size_t have = 0;
+        if (gdn2::rmsnorm_scratch(&workspace, &have) != hipSuccess) return GDN2_ERR_HIP;
+        if (need > have) return GDN2_ERR_SCRATCH;
+    }
+    gdn2::RmsNormArgs a{x, weight, nullptr, false, dy, dx, dweight, workspace, (long)rows, d, eps};
+    const hipError_t e = gdn2::launch_rmsnorm_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,31 +448,12 @@ size_t gdn2_rmsnorm_bwd_workspace_bytes(int64_t rows, int32_t d) {
 gdn2_status gdn2_rmsnorm_bwd(const float* x, const float* weight, const float* dy, float* dx, float* dweight,
                              int64_t rows, int32_t d, float eps, void* workspace, size_t workspace_bytes,
                              void* stream) {
-    if (rows < 0 || (uint64_t)rows > (1ull << 40)) return GDN2_ERR_SHAPE;
-    if (!dim_ok_tok(d) || !(eps >= 0.f && eps <= 3.0e38f)) return GDN2_ERR_UNSUPPORTED;
-    if (rows > 0 && (!x || !dy || !dx)) return GDN2_ERR_NULL;
-    const void* ptrs[] = {x, weight, dy, dx, dweight};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
-    const size_t need = dweight ? gdn2::rmsnorm_bwd_workspace_bytes((long)rows, d) : 0;
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return GDN2_ERR_ALIGN;
-    }
-    if (rows == 0 && !dweight) return GDN2_OK;
-    const uint64_t n = (uint64_t)rows * (uint64_t)d;
-    const Range rx = range_of(x, n * 4), rwt = range_of(weight, (uint64_t)d * 4), rdy = range_of(dy, n * 4),
-                rdx = range_of(dx, n * 4), rdw = range_of(dweight, (uint64_t)d * 4),
-                rws = range_of(need ? workspace : nullptr, need);
-    // dx may be dy itself (each lane reads its dy before it writes the same elements of dx)
-    if (overlap(rdx, rx) || overlap(rdx, rwt) || (overlap(rdx, rdy) && dx != dy) || overlap(rdx, rdw) ||
-        overlap(rdx, rws))
-        return GDN2_ERR_ALIAS;
-    if (overlap(rdw, rx) || overlap(rdw, rwt) || overlap(rdw, rdy) || overlap(rdw, rws)) return GDN2_ERR_ALIAS;
-    if (overlap(rws, rx) || overlap(rws, rwt) || overlap(rws, rdy)) return GDN2_ERR_ALIAS;
-    gdn2::RmsNormArgs a{x, weight, nullptr, false, dy, dx, dweight, workspace, (long)rows, d, eps};
-    const hipError_t e = gdn2::launch_rmsnorm_bwd(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    return rmsnorm_bwd_checked(x, weight, dy, dx, dweight, rows, d, eps, workspace, workspace_bytes, false, stream);
+}
+
+gdn2_status gdn2_rmsnorm_bwd_noalloc(const float* x, const float* weight, const float* dy, float* dx,
+                                     float* dweight, int64_t rows, int32_t d, float eps, void* stream) {
+    return rmsnorm_bwd_checked(x, weight, dy, dx, dweight, rows, d, eps, nullptr, 0, true, stream);
 }
 
 const char* gdn2_status_str(gdn2_status s) {
@@ -446,6 +466,7 @@ const char* gdn2_status_str(gdn2_status s) {
         case GDN2_ERR_ALIAS: return "an output overlaps an input";
         case GDN2_ERR_HIP: return "HIP launch error";
         case GDN2_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN2_ERR_SCRATCH: return "size beyond the library's fixed scratch";
     }
     return "unknown status";
 }

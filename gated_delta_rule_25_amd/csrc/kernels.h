@@ -38,6 +38,9 @@ struct RmsNormArgs {
 hipError_t launch_rmsnorm_fwd(const RmsNormArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const RmsNormArgs& a, hipStream_t s);
 size_t rmsnorm_bwd_workspace_bytes(long rows, int D);
+// The library's fixed device scratch for the backward's dweight partials on the current device
+// (looked up once per device): its device address and size.
+hipError_t rmsnorm_scratch(void** ptr, size_t* bytes);
 
 // Arguments of the chunkwise (C = 64) prefill kernels.
 struct ChunkArgs {

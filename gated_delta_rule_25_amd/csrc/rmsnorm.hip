@@ -8,6 +8,8 @@
 // group. The backward's weight gradient, a sum over every row, is reduced deterministically:
 // each workgroup sums its rows into a [D] partial in the workspace, then one pass adds the
 // partials in workgroup order.
+#include <mutex>
+
 #include "kernels.h"
 
 namespace gdn2 {
@@ -174,9 +176,38 @@ hipError_t dispatch(const RmsNormArgs& a, hipStream_t s) {
     }
 }
 
+// Fixed scratch for callers that cannot allocate: the dweight partials of one backward call,
+// at most kNormBlocks rows of D <= 256 floats (1 MiB). Each GPU holds its own copy of the array
+// for the life of the process. In host code its name is a host-side stand-in, so the device
+// address is looked up once per device and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = (size_t)kNormBlocks * 256 * sizeof(float);
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
 }  // namespace
 
 size_t rmsnorm_bwd_workspace_bytes(long rows, int D) { return (size_t)bwd_blocks(rows, D) * D * 4; }
+
+hipError_t rmsnorm_scratch(void** ptr, size_t* bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {  // first call on this device: it is the current one
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_addr[dev] = p;
+    }
+    *ptr = scratch_addr[dev];
+    *bytes = kScratchBytes;
+    return hipSuccess;
+}
 
 hipError_t launch_rmsnorm_fwd(const RmsNormArgs& a, hipStream_t s) { return dispatch<false>(a, s); }
 hipError_t launch_rmsnorm_bwd(const RmsNormArgs& a, hipStream_t s) { return dispatch<true>(a, s); }

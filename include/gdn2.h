@@ -66,7 +66,8 @@ typedef enum {
     GDN2_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     GDN2_ERR_ALIAS = 5,       /* an output overlaps an input (other than S_out == S0) */
     GDN2_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-    GDN2_ERR_WORKSPACE = 7    /* workspace missing or smaller than required */
+    GDN2_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
+    GDN2_ERR_SCRATCH = 8      /* the call needs more than the library's fixed scratch holds */
 } gdn2_status;
 
 typedef enum { GDN2_BF16 = 0, GDN2_F32 = 1 } gdn2_dtype;
@@ -338,6 +339,21 @@ gdn2_status gdn2_rmsnorm_bwd(const float *x, const float *weight, const float *d
 
 /* Workspace bytes gdn2_rmsnorm_bwd needs for dweight at these sizes (0: none, or unsupported). */
 size_t gdn2_rmsnorm_bwd_workspace_bytes(int64_t rows, int32_t d);
+
+/*
+ * gdn2_rmsnorm_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same checks, kernels and results
+ * (bit for bit), with the dweight partials in a fixed device array inside the library instead
+ * of a caller workspace. The array holds 1 MiB (1024 partials of d <= 256 floats), which covers
+ * every supported size; a call needing more would return GDN2_ERR_SCRATCH. Each GPU the library
+ * runs on keeps its own copy until the process ends; its address is looked up on the first call
+ * made with that device current. Nothing is allocated or freed and no workspace is taken. Calls
+ * on one GPU share the array: two calls in flight at once on one GPU (on different streams, or
+ * from different threads without ordering) race and give unspecified dweight. The array needs no
+ * clearing between calls (every partial a call reads is written by that call).
+ */
+gdn2_status gdn2_rmsnorm_bwd_noalloc(const float *x, const float *weight, const float *dy, float *dx,
+                                     float *dweight, int64_t rows, int32_t d, float eps, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *gdn2_status_str(gdn2_status s);

@@ -39,8 +39,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.gdn2_abi_version() == 1
-    for code in range(8):
+    for code in range(9):
         assert lib.gdn2_status_str(code)
+    assert lib.gdn2_status_str(8) == b"size beyond the library's fixed scratch"
     assert lib.gdn2_status_str(0) == b"ok"
 
 
@@ -270,3 +271,13 @@ def test_rmsnorm_rejects_bad_arguments(lib):
     assert bwd(x, w, dy, dx, dy, 1000, 128, 1e-6, ws, need, None) == 5     # dweight over dy
     assert bwd(x, w, dy, dx, dw, 1000, 128, 1e-6, dx, need, None) == 5     # workspace over dx
     assert bwd(x, w, dy, dx, None, 0, 128, 1e-6, None, 0, None) == 0       # nothing to do
+    # the allocation-free variant: the same argument checks, without a workspace argument
+    na = lib.gdn2_rmsnorm_bwd_noalloc
+    assert na(x, w, dy, dx, dw, -1, 128, 1e-6, None) == 2
+    assert na(x, w, dy, dx, dw, 1000, 48, 1e-6, None) == 3
+    assert na(x, w, dy, dx, dw, 1000, 128, float("nan"), None) == 3
+    assert na(x, w, None, dx, dw, 1000, 128, 1e-6, None) == 1
+    assert na(x, w, dy, P((1 << 40) * 5 + 8), dw, 1000, 128, 1e-6, None) == 4
+    assert na(x, w, dy, x, dw, 1000, 128, 1e-6, None) == 5                 # dx over x
+    assert na(x, w, dy, dx, dy, 1000, 128, 1e-6, None) == 5                # dweight over dy
+    assert na(x, w, dy, dx, None, 0, 128, 1e-6, None) == 0                 # nothing to do
