@@ -33,10 +33,42 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
-# HBM bytes per gdn2_chunk_fwd call at B8 H16 T4096 d128 bf16, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE scaled by a 1 GiB copy (profiles/chunk_fwd_bf16_B8_H16_T4096_d128.txt), for the
-# kernels as they stand; set to None when a kernel changes until the counters are taken again.
-MEASURED_TRAFFIC = {"split": None, "fused": None, "recurrent": None}
+CSRC = os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def sources_digest() -> str:
+    """sha256 over the kernel sources (every file under csrc/, in name order): names the build
+    that a profile's counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        path = os.path.join(CSRC, name)
+        if os.path.isfile(path) and name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode() + b"\0")
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(impl: str, digest: str):
+    """HBM bytes per gdn2_chunk_fwd call at B8 H16 T4096 d128 bf16 that a summary in profiles/
+    states for these exact kernel sources (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated),
+    from its line "bench-traffic: impl=<impl> bytes=<n> sources=<digest>". None when no summary
+    was taken on these sources: counters of another build say nothing about this one."""
+    if not os.path.isdir(PROFILES):
+        return None
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith((".txt", ".md")):
+            continue
+        with open(os.path.join(PROFILES, name), encoding="utf-8") as f:
+            for line in f:
+                if not line.startswith("bench-traffic:"):
+                    continue
+                kv = dict(x.split("=", 1) for x in line.split()[1:] if "=" in x)
+                if kv.get("impl") == impl and kv.get("sources") == digest:
+                    return float(kv["bytes"])
+    return None
 
 
 def prefill_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
@@ -471,12 +503,17 @@ def main(argv=None):
         dwall, dms = time_decode(g, Bd, 16, 128, steps, 10, seed=20254)
         davg = sum(dms) / len(dms)
         dbytes = decode_bytes_per_head(128, 128) * Bd * 16
-        dec[f"B{Bd}"] = dict(steps=steps, kernel_ms=round(davg, 5),
-                             ms_per_step_wall=round(dwall * 1e3 / steps, 5),
-                             gbs=round(dbytes / (davg * 1e-3) / 1e9, 1),
-                             frac=round(dbytes / (davg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                             head_state_updates_per_s=round(Bd * 16 / (davg * 1e-3), 1))
-        print(f"[bench] decode B={Bd}: {davg * 1e3:.1f} us/step, {dec[f'B{Bd}']['gbs']} GB/s",
+        rate = dbytes / (davg * 1e-3) / 1e9
+        # The 256 MiB state of B256 is partly served by the 256 MB Infinity Cache from one step to
+        # the next, so its rate is an effective bandwidth (algorithmic bytes / time), not HBM
+        # bandwidth. The 1 GiB state of B1024 cannot stay in that cache: its rate is the HBM figure.
+        kind = "hbm" if Bd * 16 * 128 * 128 * 4 >= 1 << 30 else "effective (Infinity Cache assisted)"
+        pre = "" if kind == "hbm" else "effective_"
+        dec[f"B{Bd}"] = {"steps": steps, "kernel_ms": round(davg, 5),
+                         "ms_per_step_wall": round(dwall * 1e3 / steps, 5), "bandwidth": kind,
+                         pre + "gbs": round(rate, 1), pre + "frac": round(rate / HBM_PEAK_GBS, 4),
+                         "head_state_updates_per_s": round(Bd * 16 / (davg * 1e-3), 1)}
+        print(f"[bench] decode B={Bd}: {davg * 1e3:.1f} us/step, {rate:.1f} GB/s ({kind})",
               file=sys.stderr, flush=True)
 
     if args.copy_calibration:
@@ -487,6 +524,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    digest = sources_digest()
     rec = {
         "metric": "GDN-2 chunk fwd tokens/s (B8,H16,T4k,d128) + decode state HBM GB/s",
         "value": round(B * T / (ms_per_step * 1e-3), 1),
@@ -505,8 +543,9 @@ def main(argv=None):
                    "impl": args.impl, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": (MEASURED_TRAFFIC.get(args.impl)
+                     "traffic": (profiled_traffic(args.impl, digest)
                                  if args.workload == "prefill_1p3b" else None),
+                     "sources": digest,
                      "kernels": KERNELS[args.impl],
                      "kernel_ms": round(kern_avg, 4),
                      "algorithmic_bytes": int(bytes_launch),
