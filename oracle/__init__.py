@@ -15,6 +15,8 @@ The readout o_t = S_t^T q_t (updated state) is a reading, not printed on the pag
 ``backward`` (reverse mode of the same recurrence) is pinned by ``tests/oracle_bwd_pins.py``
 against finite differences, a closed form, the affine dependence on S0 and automatic
 differentiation of a transition-matrix formulation.
+``pkm_address`` / ``sdm_forward`` / ``sdm_step`` (the sparse delta memory, numpy float64, in
+``sdm.py`` with its readings) are pinned by ``tests/test_oracle_sdm.py``.
 ``rmsnorm`` / ``rmsnorm_backward`` (the output normalisation, numpy float64) are pinned by
 ``tests/test_oracle_rmsnorm.py`` against closed forms, invariants and finite differences.
 Every forward function is pinned by ``tests/test_oracle_pins.py`` against a hand-worked example,
@@ -266,3 +268,6 @@ def rmsnorm_backward(x, weight, dy, *, eps: float) -> dict:
     dx = r * (u - xh * np.mean(xh * u, axis=-1, keepdims=True))
     dweight = (dy * xh).reshape(-1, x.shape[-1]).sum(axis=0)
     return dict(dx=dx, dweight=dweight)
+
+
+from .sdm import pkm_address, sdm_forward, sdm_step  # noqa: E402  (the sparse delta memory, numpy float64)
