@@ -344,6 +344,69 @@ def rmsnorm_leg(g, steps):
     return res
 
 
+def sdm_leg(g, steps):
+    """Sparse delta memory at B8 H16, N = 65,536 slots of d_v = 128 per head (32 MiB; 4 GiB in all),
+    W = R = 64: one decode step (gdn2_sdm_fwd with T = 1), the product-key addressing of a
+    B8 T4096 prefill's keys (524,288 queries, gdn2_sdm_address), and a 256-token token-by-token
+    prefill. Bytes per head-token: the W write slots read and written and the R read slots read
+    (3 x 64 x 128 x 4 B = 96 KiB) plus the token's inputs."""
+    import torch
+    from gated_delta_rule_25_amd.inputs import make_sdm_inputs
+    B, H, n, dv, W = 8, 16, 256, 128, 64
+    N = n * n
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, k):
+        fn()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / k
+
+    gen = torch.Generator(device="cuda").manual_seed(20257)
+    state = g.sdm_state(torch.randn(B, H, N, dv, device="cuda", generator=gen) * 0.1)
+    res = dict(config=f"B{B} H{H} N={N} slots x d_v={dv} fp32 (memory {B * H * N * dv * 4 >> 30} GiB), W=R={W}")
+    dec = make_sdm_inputs(B, 64, H, 128, dv, n, W, W, seed=20258, with_memory=False, device="cuda")
+    pool = [{k: dec[k][:, i:i + 1].contiguous() for k in ("v", "alpha", "b", "w", "widx", "wwt", "ridx", "rwt")}
+            for i in range(64)]
+    it = [0]
+
+    def step():
+        x = pool[it[0] % 64]
+        it[0] += 1
+        g.sdm_fwd(x["v"], x["alpha"], x["b"], x["w"], x["widx"], x["wwt"], x["ridx"], x["rwt"], state)
+    ms = timed(step, steps)
+    # W rows read and written, R rows read (fp32), their stamps (fp64; W written), the token's
+    # v and w (bf16), alpha and b, the 2 x 64 slot indices and weights, o written (fp32)
+    per_ht = 3 * W * dv * 4 + 3 * W * 8 + dv * 2 * 2 + 2 * 2 + 2 * W * 8 + dv * 4
+    gbs = per_ht * B * H / (ms * 1e-3) / 1e9
+    res["decode"] = dict(us_per_step=round(ms * 1e3, 2), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                         head_tokens_per_s=round(B * H / (ms * 1e-3), 1))
+    del dec, pool
+    T = 4096
+    ad = make_sdm_inputs(B, T, H, 128, dv, n, 1, 1, seed=20259, with_memory=False, device="cuda")
+    ms = timed(lambda: g.sdm_address(ad["k"], ad["C1"], ad["C2"], W), max(2, steps // 20))
+    res["address"] = dict(queries=B * T * H, ms=round(ms, 4), queries_per_s=round(B * T * H / (ms * 1e-3), 1))
+    del ad
+    Tp = 256
+    pf = make_sdm_inputs(B, Tp, H, 128, dv, n, W, W, seed=20260, with_memory=False, device="cuda")
+    ms = timed(lambda: g.sdm_fwd(pf["v"], pf["alpha"], pf["b"], pf["w"], pf["widx"], pf["wwt"], pf["ridx"],
+                                 pf["rwt"], state), 2)
+    gbs = per_ht * B * H * Tp / (ms * 1e-3) / 1e9
+    res["prefill"] = dict(T=Tp, ms=round(ms, 4), us_per_token=round(ms * 1e3 / Tp, 3), gbs=round(gbs, 1),
+                          tokens_per_s=round(B * Tp / (ms * 1e-3), 1))
+    print(f"[bench] sdm: decode {res['decode']['us_per_step']} us/step ({res['decode']['gbs']} GB/s), "
+          f"address {res['address']['ms']} ms for {B * T * H} queries, prefill {res['prefill']['us_per_token']} "
+          f"us/token", file=sys.stderr, flush=True)
+    del pf, state
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(g, B, H, d, steps, warmup, seed):
     import torch
     from gated_delta_rule_25_amd.inputs import make_decode_inputs
@@ -492,6 +555,9 @@ def main(argv=None):
     norm = None
     if not args.skip_others and args.workload == "prefill_1p3b":
         norm = rmsnorm_leg(g, 20)
+    sdm = None
+    if not args.skip_others and args.workload == "prefill_1p3b":
+        sdm = sdm_leg(g, 100)
     if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
         for name, steps in (("long_prefill", 3), ("gdn_scalar", 10), ("kda_scalar", 10)):
             others[name] = prefill_leg(g, name, steps, args.impl)
@@ -555,6 +621,7 @@ def main(argv=None):
         "backward": bwd,
         "packed_prefill": packed,
         "output_rmsnorm": norm,
+        "sparse_delta_memory": sdm,
         "prologue": prologue,
         "decode": dec,
         "cpu_baseline": cpu,

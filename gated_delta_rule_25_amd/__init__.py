@@ -27,7 +27,8 @@ import torch  # noqa: F401  (load torch's HIP runtime before libgdn2.so binds to
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", "recurrent_fwd", "decode_step", "chunk_fwd_workspace_bytes", "chunk_bwd",
            "chunk_bwd_workspace_bytes", "chunk_bwd_varlen", "chunk_bwd_varlen_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
-           "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc"]
+           "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc",
+           "sdm_address", "sdm_state", "sdm_fwd", "sdm_fold"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
@@ -90,6 +91,12 @@ def load():
     lib.gdn2_rmsnorm_bwd_noalloc.restype = ctypes.c_int
     lib.gdn2_rmsnorm_bwd_workspace_bytes.argtypes = [i64, i32]
     lib.gdn2_rmsnorm_bwd_workspace_bytes.restype = sz
+    lib.gdn2_sdm_address.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p]
+    lib.gdn2_sdm_address.restype = ctypes.c_int
+    lib.gdn2_sdm_fwd.argtypes = [p] * 12 + [i32, i32, i32, i64, i32, i32, i32, i32, p]
+    lib.gdn2_sdm_fwd.restype = ctypes.c_int
+    lib.gdn2_sdm_fold.argtypes = [p, p, p, i32, i32, i64, i32, p]
+    lib.gdn2_sdm_fold.restype = ctypes.c_int
     lib.gdn2_status_str.argtypes = [ctypes.c_int]
     lib.gdn2_status_str.restype = ctypes.c_char_p
     lib.gdn2_abi_version.argtypes = []
@@ -420,3 +427,93 @@ def rmsnorm_bwd_noalloc(x, weight, dy, *, eps: float = 1e-6, dx, dweight=None, s
     if st != 0:
         raise Gdn2Error("gdn2_rmsnorm_bwd_noalloc", st)
     return dict(dx=dx, dweight=dweight)
+
+
+def _contig(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def sdm_address(x, C1, C2, m: int, *, idx=None, weight=None, stream=None):
+    """Product-key addressing (gdn2_sdm_address) of queries x [..., H, d_k] against sub-key
+    tables C1, C2 [H, n, d_k/2]: returns (idx [..., H, m] int32, weight [..., H, m] float32)."""
+    lib = load()
+    _contig(x, "x")
+    H, dk = x.shape[-2], x.shape[-1]
+    rows = x.numel() // (H * dk) if x.numel() else 0
+    _contig(C1, "C1", x.dtype)
+    _contig(C2, "C2", x.dtype, C1.shape)
+    if C1.dim() != 3 or C1.shape[0] != H or C1.shape[2] * 2 != dk:
+        raise ValueError("C1, C2 must be [H, n, d_k/2]")
+    n = C1.shape[1]
+    shp = tuple(x.shape[:-1]) + (m,)
+    if idx is None:
+        idx = torch.empty(shp, device=x.device, dtype=torch.int32)
+    if weight is None:
+        weight = torch.empty(shp, device=x.device, dtype=torch.float32)
+    st = lib.gdn2_sdm_address(_ptr(x), _ptr(C1), _ptr(C2), rows, H, dk, n, m, _dtype_code(x), _ptr(idx),
+                              _ptr(weight), _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_sdm_address", st)
+    return idx, weight
+
+
+def sdm_state(M0):
+    """The memory state gdn2_sdm_fwd takes, from an initial memory M0 [B, H, N, d_v] float32 (used
+    in place): (M0, stamp [B, H, d_v/64, N] float64 zeros, L [B, H, d_v/64] float64 zeros)."""
+    _contig(M0, "M0", torch.float32)
+    B, H, N, dv = M0.shape
+    stamp = torch.zeros(B, H, dv // 64, N, device=M0.device, dtype=torch.float64)
+    L = torch.zeros(B, H, dv // 64, device=M0.device, dtype=torch.float64)
+    return M0, stamp, L
+
+
+def sdm_fwd(v, alpha, b, w, widx, wwt, ridx, rwt, state, *, o=None, stream=None):
+    """The sparse delta memory over [B, T, H, ...] tokens (gdn2_sdm_fwd): v, w [B, T, H, d_v]
+    (w None: ones), alpha, b [B, T, H]; widx/wwt [B, T, H, W], ridx/rwt [B, T, H, R]; state =
+    (M, stamp, L) as sdm_state makes it, updated in place. Returns o [B, T, H, d_v] float32."""
+    lib = load()
+    M, stamp, L = state
+    _contig(v, "v")
+    B, T, H, dv = v.shape
+    for name, t in (("alpha", alpha), ("b", b)):
+        _contig(t, name, v.dtype, (B, T, H))
+    if w is not None:
+        _contig(w, "w", v.dtype, v.shape)
+    W, R = widx.shape[-1], ridx.shape[-1]
+    _contig(widx, "widx", torch.int32, (B, T, H, W))
+    _contig(wwt, "wwt", torch.float32, (B, T, H, W))
+    _contig(ridx, "ridx", torch.int32, (B, T, H, R))
+    _contig(rwt, "rwt", torch.float32, (B, T, H, R))
+    _contig(M, "M", torch.float32)
+    if M.dim() != 4 or M.shape[0] != B or M.shape[1] != H or M.shape[3] != dv:
+        raise ValueError("M must be [B, H, N, d_v]")
+    N = M.shape[2]
+    _contig(stamp, "stamp", torch.float64, (B, H, dv // 64, N))
+    _contig(L, "L", torch.float64, (B, H, dv // 64))
+    if o is None:
+        o = torch.empty(B, T, H, dv, device=v.device, dtype=torch.float32)
+    st = lib.gdn2_sdm_fwd(_ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt),
+                          _ptr(M), _ptr(stamp), _ptr(L), _ptr(o), B, T, H, N, dv, W, R, _dtype_code(v),
+                          _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_sdm_fwd", st)
+    return o
+
+
+def sdm_fold(state, *, stream=None):
+    """Brings the memory up to date (gdn2_sdm_fold): afterwards state[0] is the memory itself."""
+    lib = load()
+    M, stamp, L = state
+    _contig(M, "M", torch.float32)
+    B, H, N, dv = M.shape
+    _contig(stamp, "stamp", torch.float64, (B, H, dv // 64, N))
+    _contig(L, "L", torch.float64, (B, H, dv // 64))
+    st = lib.gdn2_sdm_fold(_ptr(M), _ptr(stamp), _ptr(L), B, H, N, dv, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_sdm_fold", st)
+    return M

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn2.so")
-SOURCES = ["gdn2_api.cpp", "recurrent.hip", "chunk.hip", "chunk_fused.hip", "chunk_split.hip", "chunk_varlen.hip", "chunk_bwd.hip", "rmsnorm.hip"]
+SOURCES = ["gdn2_api.cpp", "recurrent.hip", "chunk.hip", "chunk_fused.hip", "chunk_split.hip", "chunk_varlen.hip", "chunk_bwd.hip", "rmsnorm.hip", "sdm.hip"]
 ARCH = "gfx950"
 
 

@@ -188,8 +188,8 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
         }
     };
 
-    // o of this sequence as a buffer: rows past the end are dropped, so stores need no branch
-    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + (long)bb * T * H * DV, (unsigned)T * H * DV * 4u);
+    // o of one chunk's rows as a buffer (rebased per chunk): rows past the end are dropped, so
+    // stores need no branch
     const int nch = (T + CH - 1) / CH;
     for (int part = 0; part < 4; ++part) fetch(0, part);
     for (int n = 0; n < nch; ++n) {
@@ -620,7 +620,8 @@ chunk_kernel(const void* __restrict__ q, const void* __restrict__ k, const void*
                     const E* pr = &Pm[(16 * nt + l16) * CHP + 32 * s2];
                     PR::mma(O[nt], Df[s2], PR::lds_pair(pr + 4 * g, pr + 16 + 4 * g));
                 }
-                const unsigned row = (unsigned)(t0 + 16 * nt + l16);
+                const __amdgpu_buffer_rsrc_t rs_o = rows_rsrc(o, (long)bb * T, t0, T, (unsigned)(H * DV * 4), CH);
+                const unsigned row = (unsigned)(16 * nt + l16);
                 store4(rs_o, ((row * H + hh) * DV + tile * DVT + 16 * wv + 4 * g) * 4u, O[nt][0] * isc, O[nt][1] * isc,
                        O[nt][2] * isc, O[nt][3] * isc);
             }
@@ -678,9 +679,7 @@ hipError_t launch_flags(const ChunkArgs& a, hipStream_t s) {
 }  // namespace
 
 bool chunk_supported(int T, int H, int DK, int DV, bool bf16) {
-    if (DK != DV) return false;
-    // o of one sequence is addressed with 32-bit byte offsets
-    if ((long long)T * H * DV * 4 >= (1ll << 32)) return false;
+    if (DK != DV || T < 0) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
     return DK == 32 || DK == 64;  // fp32 operand tiles of d = 128 exceed the LDS budget
 }

@@ -41,6 +41,16 @@ __device__ __forceinline__ float lg2_sigmoid(float x) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Raw buffer over token rows [r0, r0 + min(len - r0, maxrows)) of a sequence whose first token
+// row is `first` in a tensor of row_bytes per token row. The base is advanced in 64-bit
+// arithmetic, so a sequence may span more than 4 GiB; offsets inside stay below
+// maxrows * row_bytes, and rows past the sequence end fall outside the buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, long first, long r0, long len,
+                                                            unsigned row_bytes, int maxrows) {
+    const long left = len - r0;
+    const unsigned rows = left <= 0 ? 0u : (left < maxrows ? (unsigned)left : (unsigned)maxrows);
+    return make_rsrc(static_cast<const char*>(base) + (first + r0) * (long)row_bytes, rows * row_bytes);
+}
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, unsigned off, float a, float b, float c, float d) {
     const u32x4 x = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};

@@ -264,14 +264,14 @@ fused_kernel(const void* q, const void* k, const void* v, const void* alpha, con
             for (int s = 0; s < NKS; ++s) ra[s] = gload8<BF16>(alpha, tok * DK + 32 * s + 8 * g);
         }
     };
-    // q, k, b through buffer resources over this sequence's rows: rows past the end read as zeros
-    const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(static_cast<const char*>(q) + tbase * H * DK * 2, (unsigned)T * H * DK * 2u);
-    const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(static_cast<const char*>(k) + tbase * H * DK * 2, (unsigned)T * H * DK * 2u);
-    const __amdgpu_buffer_rsrc_t rs_b =
-        make_rsrc(static_cast<const char*>(b) + tbase * H * (BS ? 1 : DK) * 2, (unsigned)T * H * (BS ? 1 : DK) * 2u);
+    // q, k, b through buffer resources over chunk m's rows (rebased per chunk): rows past the end
+    // read as zeros
     auto load_qkb = [&](int m) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs_q = rows_rsrc(q, tbase, (long)m * CH, T, (unsigned)(H * DK * 2), CH);
+        const __amdgpu_buffer_rsrc_t rs_k = rows_rsrc(k, tbase, (long)m * CH, T, (unsigned)(H * DK * 2), CH);
+        const __amdgpu_buffer_rsrc_t rs_b = rows_rsrc(b, tbase, (long)m * CH, T, (unsigned)(H * (BS ? 1 : DK) * 2), CH);
         const int ln = opaque_lane(), g = ln >> 4;
-        const unsigned row = (unsigned)(m * CH + 16 * I + (ln & 15)) * H + hh;
+        const unsigned row = (unsigned)(16 * I + (ln & 15)) * H + hh;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             const int off = (int)((row * DK + 32 * s + 8 * g) * 2u);
@@ -626,7 +626,6 @@ fused_kernel(const void* q, const void* k, const void* v, const void* alpha, con
 
     // ================================ chain waves' state ================================
     const int col0 = tile * DVT + (chain ? wv : 0) * 16;
-    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tbase * H * DV, (unsigned)T * H * DV * 4u);
     const unsigned o_lane = (((unsigned)l16 * H + hh) * DV + col0 + 4 * g) * 4u;
     const unsigned o_tok = (unsigned)H * DV * 4u;
     f4 Sacc[NMK];
@@ -639,19 +638,17 @@ fused_kernel(const void* q, const void* k, const void* v, const void* alpha, con
         for (int j = 0; j < 4; ++j)
             Sacc[mk][j] = (chain && s_in) ? s_in[(long)(16 * mk + 4 * g + j) * DV + col0 + l16] : 0.f;
     // v, w of this wave's 16 columns for one chunk, straight into registers in the accumulator
-    // layout (rows 16 mt + 4 g + j, column col0 + l16), through buffer resources over this
-    // sequence's rows: rows past the end arrive as zeros
-    const __amdgpu_buffer_rsrc_t rs_v =
-        make_rsrc(static_cast<const char*>(v) + tbase * H * DV * 2, (unsigned)T * H * DV * 2u);
-    const __amdgpu_buffer_rsrc_t rs_w =
-        make_rsrc(static_cast<const char*>(BS ? v : w) + tbase * H * DV * 2, (unsigned)T * H * DV * 2u);
+    // layout (rows 16 mt + 4 g + j, column col0 + l16), through buffer resources over chunk n's
+    // rows (rebased per chunk): rows past the end arrive as zeros
     uint16_t vr[16], wr[16];
     auto load_vw = [&](int n) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs_v = rows_rsrc(v, tbase, (long)n * CH, T, (unsigned)(H * DV * 2), CH);
+        const __amdgpu_buffer_rsrc_t rs_w = rows_rsrc(BS ? v : w, tbase, (long)n * CH, T, (unsigned)(H * DV * 2), CH);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const unsigned row = (unsigned)(n * CH + 16 * mt + 4 * g + j);
+                const unsigned row = (unsigned)(16 * mt + 4 * g + j);
                 const int off = (int)(((row * H + hh) * DV + (unsigned)col0 + l16) * 2u);
                 vr[4 * mt + j] = __builtin_amdgcn_raw_buffer_load_b16(rs_v, off, 0, 0);
                 if constexpr (!BS) wr[4 * mt + j] = __builtin_amdgcn_raw_buffer_load_b16(rs_w, off, 0, 0);
@@ -772,7 +769,8 @@ fused_kernel(const void* q, const void* k, const void* v, const void* alpha, con
         }
         fused_lookahead<6 + 2 * NMK, 6, 1>();
         // o rows of this chunk: four consecutive columns per lane, one 16-byte store each
-        const unsigned op = o_lane + (unsigned)(n * CH) * o_tok;
+        const __amdgpu_buffer_rsrc_t rs_o = rows_rsrc(o, tbase, (long)n * CH, T, o_tok, CH);
+        const unsigned op = o_lane;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
             store4(rs_o, op + 16u * nt * o_tok, O[nt][0] * isc, O[nt][1] * isc, O[nt][2] * isc, O[nt][3] * isc);
@@ -825,8 +823,7 @@ hipError_t launch_fused_dk(const ChunkArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fused_supported(int T, int H, int DK, int DV, bool bf16) {
-    if (!bf16 || DK != DV) return false;
-    if ((long long)T * H * DV * 4 >= (1ll << 32)) return false;  // 32-bit row offsets per sequence
+    if (!bf16 || DK != DV || T < 0) return false;
     return DK == 64 || DK == 128;
 }
 

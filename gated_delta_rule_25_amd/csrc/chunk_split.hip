@@ -156,9 +156,7 @@ hipError_t launch_split_states(const ChunkArgs& a, char* blobs, uint16_t* S_save
 }
 
 bool split_supported(int T, int H, int DK, int DV, bool bf16) {
-    if (DK != DV) return false;
-    // the chain kernel addresses one sequence's v, w and o rows with 32-bit byte offsets
-    if ((long long)T * H * DV * 4 >= (1ll << 32)) return false;
+    if (DK != DV || T < 0) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
     return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
 }

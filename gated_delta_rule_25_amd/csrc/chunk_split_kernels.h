@@ -688,9 +688,9 @@ chain_kernel(const ChainIO io) {
     float* const o = io.o;
     const void* const v = io.v;
     const void* const w = io.w;
-    // o of this sequence as a buffer (rows past the end are dropped): byte offset of token row
-    // l16 of chunk 0 at this lane's four columns of tile 0, and the byte stride of one token
-    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tbase * H * DV, (unsigned)Tq * H * DV * 4u);
+    // o of one chunk's rows as a buffer (rebased per chunk; rows past the end are dropped): byte
+    // offset of the chunk's token row l16 at this lane's four columns of tile 0, and the byte
+    // stride of one token
     const unsigned o_lane = (((unsigned)l16 * H + hh) * DV + col0 + 4 * g) * 4u;
     const unsigned o_tok = (unsigned)H * DV * 4u;
 
@@ -722,27 +722,26 @@ chain_kernel(const ChainIO io) {
     float sc = 1.f, isc = 1.f;
 
     // v and w rows of this wave's columns for one chunk, copied into the wave's LDS slot through
-    // buffer resources over this sequence's rows: rows past the sequence end fall outside the
-    // buffer and arrive as zeros. The host keeps the byte offsets below 2^31. A scalar beta comes
-    // with the chunk's block instead of w.
+    // buffer resources over the chunk's rows (rebased per chunk, so offsets stay small whatever the
+    // sequence length): rows past the sequence end fall outside the buffer and arrive as zeros. A
+    // scalar beta comes with the chunk's block instead of w.
     using Raw = typename std::conditional<BF16, uint16_t, uint32_t>::type;
     constexpr int IES = (int)sizeof(Raw);
     constexpr int ROW = 16 * NT;             // elements per slot row
     constexpr int LPR = ROW * IES / 16;      // lanes per slot row in a copy
     constexpr int RPI = 64 / LPR;            // rows per copy instruction
-    const long seq = tbase * H;              // first token row of this sequence
-    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(static_cast<const char*>(v) + seq * DV * IES, (unsigned)Tq * H * DV * IES);
-    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(static_cast<const char*>(BS ? v : w) + seq * DV * IES, (unsigned)Tq * H * DV * IES);
     char* vw_lds = svw + (chain ? wv : 0) * 2 * SM::VWB;
     const Raw* v_l = reinterpret_cast<const Raw*>(vw_lds);
     const Raw* w_l = reinterpret_cast<const Raw*>(vw_lds + SM::VWB);
     auto dma_vw = [&](int n) {
+        const __amdgpu_buffer_rsrc_t rs_v = rows_rsrc(v, tbase, (long)n * CH, Tq, (unsigned)(H * DV * IES), CH);
+        const __amdgpu_buffer_rsrc_t rs_w = rows_rsrc(BS ? v : w, tbase, (long)n * CH, Tq, (unsigned)(H * DV * IES), CH);
 #pragma unroll
         for (int k = 0; k < CH / RPI; ++k) {
             // slot row p holds token row 16 (p / 16) + 4 (p % 4) + (p / 4) % 4, so that the four
             // rows 4 g + j (g = 0..3) read together sit in consecutive slot rows
             const int p = k * RPI + lane / LPR;
-            const unsigned row = (unsigned)(n * CH + 16 * (p / 16) + 4 * (p % 4) + (p / 4) % 4);
+            const unsigned row = (unsigned)(16 * (p / 16) + 4 * (p % 4) + (p / 4) % 4);
             const unsigned off = ((row * H + hh) * DV + (unsigned)col0) * IES + (lane % LPR) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lds_ptr_t)(vw_lds + k * 1024), 16, off, 0, 0, 0);
             if constexpr (!BS)
@@ -767,14 +766,14 @@ chain_kernel(const ChainIO io) {
     // operands); rows past the end are dropped
     int t0_cur = 0;
     auto save_rows = [&](uint16_t* dst, const f4 (&X)[NT][4]) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + tbase * H * DV, (unsigned)Tq * H * DV * 2u);
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(dst, tbase, t0_cur, Tq, (unsigned)(H * DV * 2), CH);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const unsigned row = (unsigned)(t0_cur + 16 * mt + 4 * g + j);
+                    const unsigned row = (unsigned)(16 * mt + 4 * g + j);
                     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)X[c][mt][j]), rs,
                                                           (int)(((row * H + hh) * DV + col0 + 16 * c + l16) * 2u), 0, 0);
                 }
@@ -932,7 +931,8 @@ chain_kernel(const ChainIO io) {
             if constexpr (!STATE) {
                 // o rows of this chunk: four consecutive columns per lane and tile, one 16-byte
                 // store each (always 4 NT stores per chunk; rows past the end are dropped)
-                const unsigned op = o_lane + (unsigned)t0 * o_tok;
+                const __amdgpu_buffer_rsrc_t rs_o = rows_rsrc(o, tbase, t0, Tq, o_tok, CH);
+                const unsigned op = o_lane;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll

@@ -471,6 +471,89 @@ const char* gdn2_status_str(gdn2_status s) {
     return "unknown status";
 }
 
+gdn2_status gdn2_sdm_address(const void* x, const void* C1, const void* C2, int64_t rows, int32_t H, int32_t d_k,
+                             int32_t n, int32_t m, gdn2_dtype dtype, int32_t* idx, float* weight, void* stream) {
+    if (rows < 0 || H <= 0) return GDN2_ERR_SHAPE;
+    if ((dtype != GDN2_BF16 && dtype != GDN2_F32) || !gdn2::sdm_address_supported(d_k, n, m))
+        return GDN2_ERR_UNSUPPORTED;
+    if (!C1 || !C2) return GDN2_ERR_NULL;
+    if (rows > 0 && (!x || !idx || !weight)) return GDN2_ERR_NULL;
+    if (!aligned16(C1) || !aligned16(C2) || (x && !aligned16(x)) || (idx && !aligned16(idx)) ||
+        (weight && !aligned16(weight)))
+        return GDN2_ERR_ALIGN;
+    uint64_t queries, xs;
+    if (!mul_ok((uint64_t)rows, (uint64_t)H, &queries) || !mul_ok(queries, (uint64_t)d_k, &xs) ||
+        queries > (1ull << 40))
+        return GDN2_ERR_SHAPE;
+    if (rows == 0) return GDN2_OK;
+    const uint64_t es = dtype == GDN2_BF16 ? 2 : 4;
+    const uint64_t table = (uint64_t)H * n * (d_k / 2) * es;
+    const Range ins[] = {range_of(x, xs * es), range_of(C1, table), range_of(C2, table)};
+    const Range ri = range_of(idx, queries * m * 4), rw = range_of(weight, queries * m * 4);
+    for (const Range& r : ins)
+        if (overlap(ri, r) || overlap(rw, r)) return GDN2_ERR_ALIAS;
+    if (overlap(ri, rw)) return GDN2_ERR_ALIAS;
+    gdn2::SdmAddressArgs a{x, C1, C2, (long)queries, H, d_k, n, m, dtype == GDN2_BF16, idx, weight};
+    return gdn2::launch_sdm_address(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status gdn2_sdm_fwd(const void* v, const void* alpha, const void* b, const void* w, const int32_t* widx,
+                         const float* wwt, const int32_t* ridx, const float* rwt, float* M, double* stamp,
+                         double* L, float* o, int32_t B, int32_t T, int32_t H, int64_t N, int32_t d_v, int32_t W,
+                         int32_t R, gdn2_dtype dtype, void* stream) {
+    if (B < 0 || T < 0 || H <= 0 || N <= 0 || N > 0x7fffffff) return GDN2_ERR_SHAPE;
+    if ((dtype != GDN2_BF16 && dtype != GDN2_F32) || !gdn2::sdm_fwd_supported(d_v, W, R)) return GDN2_ERR_UNSUPPORTED;
+    if (W > N || R > N) return GDN2_ERR_SHAPE;
+    if (B == 0) return GDN2_OK;
+    if (!M || !stamp || !L) return GDN2_ERR_NULL;
+    if (T > 0 && (!v || !alpha || !b || !widx || !wwt || !ridx || !rwt || !o)) return GDN2_ERR_NULL;
+    const void* ptrs[] = {v, alpha, b, w, widx, wwt, ridx, rwt, M, stamp, L, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_ALIGN;
+    uint64_t bh, tok, mem, vw, bookkeeping;
+    const uint64_t tiles = (uint64_t)(d_v / 64);
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || !mul_ok(bh, (uint64_t)T, &tok) ||
+        !mul_ok(bh, (uint64_t)N, &mem) || !mul_ok(mem, (uint64_t)d_v, &mem) || !mul_ok(tok, (uint64_t)d_v, &vw) ||
+        !mul_ok(bh * tiles, (uint64_t)N, &bookkeeping) || bh * tiles >= (1ull << 31))
+        return GDN2_ERR_SHAPE;
+    if (T == 0) return GDN2_OK;
+    const uint64_t es = dtype == GDN2_BF16 ? 2 : 4;
+    const Range ins[] = {range_of(v, vw * es), range_of(alpha, tok * es), range_of(b, tok * es), range_of(w, vw * es),
+                         range_of(widx, tok * W * 4), range_of(wwt, tok * W * 4), range_of(ridx, tok * R * 4),
+                         range_of(rwt, tok * R * 4)};
+    const Range outs[] = {range_of(M, mem * 4), range_of(stamp, bookkeeping * 8), range_of(L, bh * tiles * 8),
+                          range_of(o, vw * 4)};
+    const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+    for (int i = 0; i < nout; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    gdn2::SdmFwdArgs a{v, alpha, b, w, widx, wwt, ridx, rwt, M, stamp, L, o, B, T, H, (long)N, d_v, W, R,
+                       dtype == GDN2_BF16};
+    return gdn2::launch_sdm_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status gdn2_sdm_fold(float* M, double* stamp, double* L, int32_t B, int32_t H, int64_t N, int32_t d_v,
+                          void* stream) {
+    if (B < 0 || H <= 0 || N <= 0 || N > 0x7fffffff) return GDN2_ERR_SHAPE;
+    if (d_v != 64 && d_v != 128 && d_v != 256) return GDN2_ERR_UNSUPPORTED;
+    if (B == 0) return GDN2_OK;
+    if (!M || !stamp || !L) return GDN2_ERR_NULL;
+    if (!aligned16(M) || !aligned16(stamp) || !aligned16(L)) return GDN2_ERR_ALIGN;
+    uint64_t bh, mem, bookkeeping;
+    const uint64_t tiles = (uint64_t)(d_v / 64);
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || !mul_ok(bh, (uint64_t)N, &mem) || !mul_ok(mem, (uint64_t)d_v, &mem) ||
+        !mul_ok(bh * tiles, (uint64_t)N, &bookkeeping) || bh * tiles * 64 >= (1ull << 31))
+        return GDN2_ERR_SHAPE;
+    const Range rM = range_of(M, mem * 4), rS = range_of(stamp, bookkeeping * 8), rL = range_of(L, bh * tiles * 8);
+    if (overlap(rM, rS) || overlap(rM, rL) || overlap(rS, rL)) return GDN2_ERR_ALIAS;
+    return gdn2::launch_sdm_fold(M, stamp, L, (long)bh, (long)N, d_v, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GDN2_OK
+               : GDN2_ERR_HIP;
+}
+
 int gdn2_abi_version(void) { return GDN2_ABI_VERSION; }
 
 }  // extern "C"

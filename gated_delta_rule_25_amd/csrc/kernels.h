@@ -60,6 +60,38 @@ struct ChunkArgs {
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
 bool chunk_supported(int T, int H, int DK, int DV, bool bf16);
 
+// Sparse delta memory: product-key addressing of queries [queries = rows * H, dk] against per-head
+// sub-key tables [H, n, dk/2] (two of them), giving m slots and weights per query; the
+// token-by-token update of the slot memory M [B, H, N, dv] with its decay stamps [B, H, dv/64, N]
+// and running log-decay sums L [B, H, dv/64] (fp64); and the fold of the stamps into M.
+struct SdmAddressArgs {
+    const void *x, *C1, *C2;
+    long queries;
+    int H, dk, n, m;
+    bool bf16;
+    int* idx;
+    float* wt;
+};
+struct SdmFwdArgs {
+    const void *v, *alpha, *b, *w;
+    const int* widx;
+    const float* wwt;
+    const int* ridx;
+    const float* rwt;
+    float* M;
+    double *stamp, *L;
+    float* o;
+    int B, T, H;
+    long N;
+    int dv, W, R;
+    bool bf16;
+};
+bool sdm_address_supported(int dk, int n, int m);
+bool sdm_fwd_supported(int dv, int W, int R);
+hipError_t launch_sdm_address(const SdmAddressArgs& a, hipStream_t s);
+hipError_t launch_sdm_fwd(const SdmFwdArgs& a, hipStream_t s);
+hipError_t launch_sdm_fold(float* M, double* stamp, double* L, long heads, long N, int dv, hipStream_t s);
+
 // Fused path (no workspace): one kernel per (b, h, 64-column tile) whose prep wavefronts build the
 // next chunk's operands in LDS while its chain wavefronts run the current chunk. bf16, d_k = d_v in
 // {64, 128}, every gate form and prologue flag.

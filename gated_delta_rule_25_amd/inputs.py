@@ -272,3 +272,71 @@ def make_inputs_torch(wl: Workload, *, device: str) -> dict:
         w = None
     return dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=S0,
                 alpha_scalar=(wl.gates == "gdn"), beta_scalar=beta_scalar)
+
+
+def _distinct_slots(rng, rows: int, N: int, m: int) -> np.ndarray:
+    """rows x m slot indices in [0, N), distinct within each row, uniformly drawn."""
+    if N <= 8192:  # the first m of a random order of all N slots
+        return np.argpartition(rng.random((rows, N), dtype=np.float32), m - 1, axis=1)[:, :m].astype(np.int32)
+    out = rng.integers(0, N, (rows, m), dtype=np.int64)
+    while True:  # redraw repeated entries until every row is distinct
+        srt = np.sort(out, axis=1)
+        dup_rows = np.nonzero((srt[:, 1:] == srt[:, :-1]).any(axis=1))[0]
+        if dup_rows.size == 0:
+            return out.astype(np.int32)
+        for r in dup_rows:
+            _, first = np.unique(out[r], return_index=True)
+            again = np.setdiff1d(np.arange(m), first)
+            out[r, again] = rng.integers(0, N, again.size)
+
+
+def make_sdm_inputs(B: int, T: int, H: int, d_k: int, d_v: int, n: int, W: int, R: int, *, seed: int,
+                    dtype: str = "bf16", alpha_mu: float = 3.0, m0_std: float = 0.1,
+                    with_memory: bool = True, device: str = "cpu") -> dict:
+    """Seeded inputs of the sparse delta memory (aiweekly.co, "Meta FAIR dévoile SDM ...": N slots
+    addressed by product keys, W write and R read slots per token).
+
+    q, k = L2normalize(N(0,1)) [B, T, H, d_k]; v = N(0,1), w = sigmoid(N(0,1)) [B, T, H, d_v];
+    alpha = sigmoid(N(alpha_mu, 1)), b = sigmoid(N(0,1)) per token [B, T, H]; sub-key tables
+    C1, C2 = N(0,1) [H, n, d_k/2]; M0 = N(0, m0_std^2) [B, H, N = n^2, d_v] float32 (zeros when
+    m0_std = 0, None without with_memory; the draws after it do not depend on it). Independent addresses for the update alone: widx [B, T, H, W] and ridx [B, T, H, R]
+    uniform distinct slots per token, weights wwt, rwt the softmax of N(0, 2^2) draws (positive,
+    summing to one like the product-key weights). Draw order: q, k, v, w, alpha, b, C1, C2, M0,
+    widx, wwt, ridx, rwt. Token inputs and tables are rounded to bf16 when dtype is bf16.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    N = n * n
+    q = _l2n(rng.standard_normal((B, T, H, d_k), dtype=f32))
+    k = _l2n(rng.standard_normal((B, T, H, d_k), dtype=f32))
+    v = rng.standard_normal((B, T, H, d_v), dtype=f32)
+    w = _sigmoid(rng.standard_normal((B, T, H, d_v), dtype=f32))
+    alpha = _sigmoid(rng.standard_normal((B, T, H), dtype=f32) + f32(alpha_mu))
+    b = _sigmoid(rng.standard_normal((B, T, H), dtype=f32))
+    C1 = rng.standard_normal((H, n, d_k // 2), dtype=f32)
+    C2 = rng.standard_normal((H, n, d_k // 2), dtype=f32)
+    if not with_memory:  # the caller makes the memory itself (e.g. on the device, at full size)
+        M0 = None
+    elif m0_std > 0:
+        M0 = rng.standard_normal((B, H, N, d_v), dtype=f32) * f32(m0_std)
+    else:
+        M0 = np.zeros((B, H, N, d_v), dtype=f32)
+    rows = B * T * H
+
+    def weights(m):
+        z = rng.standard_normal((rows, m), dtype=f32) * f32(2.0)
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        return (e / e.sum(axis=1, keepdims=True)).astype(f32).reshape(B, T, H, m)
+
+    widx = _distinct_slots(rng, rows, N, W).reshape(B, T, H, W)
+    wwt = weights(W)
+    ridx = _distinct_slots(rng, rows, N, R).reshape(B, T, H, R)
+    rwt = weights(R)
+    dt = _torch_dtype(dtype)
+
+    def t(x, to=dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(to).to(device)
+
+    return dict(q=t(q), k=t(k), v=t(v), w=t(w), alpha=t(alpha), b=t(b), C1=t(C1), C2=t(C2),
+                M0=t(M0, torch.float32), widx=t(widx, torch.int32), wwt=t(wwt, torch.float32),
+                ridx=t(ridx, torch.int32), rwt=t(rwt, torch.float32), N=N)

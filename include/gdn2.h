@@ -128,9 +128,9 @@ enum {
  * (exact), so the state may take any magnitude fp32 holds; the operands formed from q, k, b and the
  * decay (scaled q and k, the Gram blocks and T) must stay below 6.5e4, which holds for
  * L2-normalised q and k and gates in [0, 1].
- * d_k must equal d_v, and one sequence's o must stay below 4 GiB (T*H*d_v*4 < 2^32 bytes: the
- * kernels address a sequence's rows with 32-bit offsets), else GDN2_ERR_UNSUPPORTED. Any flags
- * above.
+ * d_k must equal d_v, else GDN2_ERR_UNSUPPORTED. A sequence may be of any length the grid and
+ * the workspace allow: the kernels address each chunk's rows from a 64-bit base, so one call takes
+ * sequences whose rows span more than 4 GiB (T >= 524,288 at H = 16, d = 128). Any flags above.
  */
 gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *alpha,
                            const void *b, const void *w, const float *S0, float *o,
@@ -168,8 +168,7 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
  *
  * Same two kernels as the workspace path of gdn2_chunk_fwd (one round, no segments), preceded by
  * a one-workgroup kernel that builds the sequence table. Supported sizes and errors as there:
- * bf16 with d in {32, 64, 128}, fp32 with d = 32, d_k == d_v, T_total*H*d_v*4 < 2^32, any
- * flags; GDN2_ERR_NULL without cu_seqlens, GDN2_ERR_WORKSPACE without a workspace or with
+ * bf16 with d in {32, 64, 128}, fp32 with d = 32, d_k == d_v, any flags; GDN2_ERR_NULL without cu_seqlens, GDN2_ERR_WORKSPACE without a workspace or with
  * fewer bytes than the query returns, GDN2_ERR_ALIGN for a cu_seqlens not 4-byte aligned or a
  * workspace not 256-byte aligned, GDN2_ERR_ALIAS when an output or the workspace overlaps
  * anything else (S_out == S0 excepted), GDN2_ERR_SHAPE for N <= 0 or T_total < 0.
@@ -357,6 +356,58 @@ gdn2_status gdn2_rmsnorm_bwd_noalloc(const float *x, const float *weight, const 
 
 /* A static, human-readable name for a status code. */
 const char *gdn2_status_str(gdn2_status s);
+
+/* ---------------------------------------------------------------------------------------
+ * Sparse delta memory (SDM) [SDM-news: aiweekly.co, "Meta FAIR dévoile SDM, un RNN linéaire à
+ * mémoire sparse massive", second paragraph; SDM-review: gonzo_ML, "Sparse Delta Memory:
+ * Scaling the State of Linear RNNs through Sparsity", TL;DR]: Gated DeltaNet with the dense
+ * key-value outer product replaced by sparse writes and reads of a memory of N slots, each slot
+ * holding d_v values; a product-key index picks W write and R read slots per token (W = R = 64
+ * on the pages). The pages leave the update on the chosen slots open; these calls take the
+ * Gated DeltaNet-2 update ["Техническая схема"] with the key replaced by the N-vector a_t of
+ * write weights (zero off the W slots), per-token scalar decay alpha_t and erase b_t (they act
+ * on the slot axis), the value-axis write gate w_t, and the read o_t = M_t^T r_t from the updated
+ * memory with the read weights r_t:
+ *     M_t = (I - b_t a_t a_t^T) alpha_t M_{t-1} + a_t (w_t * v_t)^T.
+ * ------------------------------------------------------------------------------------- */
+
+/* Product-key addressing. For each of rows*H queries x [rows, H, d_k] (bf16 or fp32, rows = B*T
+ * tokens): the first and second half of x are scored against the head's sub-key tables
+ * C1, C2 [H, n, d_k/2] (same dtype; fp32 dot products in channel order); the m best sub-keys of
+ * each half are kept and the m best of their pair sums give the slots i*n + j (of N = n*n) with
+ * the softmax of the sums as weights, best first (equal scores or sums: lower index first).
+ * Writes idx [rows, H, m] int32 and weight [rows, H, m] fp32. Use it with x = k for the write
+ * addresses (m = W) and x = q for the read addresses (m = R).
+ * Supported: d_k in {64, 128, 256}, n in {64, 128, 256, 512}, 1 <= m <= min(64, n). All pointers
+ * 16-byte aligned device memory; outputs overlap no input. rows = 0 returns GDN2_OK. */
+gdn2_status gdn2_sdm_address(const void *x, const void *C1, const void *C2, int64_t rows, int32_t H,
+                             int32_t d_k, int32_t n, int32_t m, gdn2_dtype dtype, int32_t *idx,
+                             float *weight, void *stream);
+
+/* The SDM recurrence over T tokens of B sequences, one token after another.
+ * v, w: [B, T, H, d_v] (w NULL: all ones); alpha, b: [B, T, H] scalars, all in dtype; alpha in
+ * (0, 1] (alpha = 0 is taken as a decay of e^-1e6, which wipes the memory);
+ * widx/wwt: [B, T, H, W] int32 slots / fp32 weights of the writes (distinct slots per token, as
+ * gdn2_sdm_address gives; a slot outside [0, N) is skipped, as if its weight were 0); ridx/rwt:
+ * [B, T, H, R] those of the reads.
+ * The memory state, updated in place: M [B, H, N, d_v] fp32, and its decay bookkeeping, stamp
+ * [B, H, d_v/64, N] and L [B, H, d_v/64] fp64. L is the running sum of log alpha; slot s holds
+ * M[s] as of its last write and stamp[s] the L of that write, so its value now is
+ * M[s] * exp(L - stamp[s]). A token therefore reads and writes only its W + R slots. Start from
+ * M = M0 with stamp = 0 and L = 0; gdn2_sdm_fold brings every slot up to date (after it
+ * M[s] is the memory itself). o: [B, T, H, d_v] fp32. Arithmetic fp32, the decay sums fp64.
+ * Supported: d_v in {64, 128, 256}, 1 <= W, R <= 64 (and <= N), N <= 2^31 - 1. All pointers
+ * 16-byte aligned; M, stamp, L and o overlap no input and each other. T = 0 or B = 0: GDN2_OK,
+ * nothing changes. */
+gdn2_status gdn2_sdm_fwd(const void *v, const void *alpha, const void *b, const void *w,
+                         const int32_t *widx, const float *wwt, const int32_t *ridx, const float *rwt,
+                         float *M, double *stamp, double *L, float *o, int32_t B, int32_t T, int32_t H,
+                         int64_t N, int32_t d_v, int32_t W, int32_t R, gdn2_dtype dtype, void *stream);
+
+/* Brings the memory of gdn2_sdm_fwd up to date: M[s] *= exp(L - stamp[s]) and stamp[s] = L for
+ * every slot (shapes as there). */
+gdn2_status gdn2_sdm_fold(float *M, double *stamp, double *L, int32_t B, int32_t H, int64_t N,
+                          int32_t d_v, void *stream);
 
 /* GDN2_ABI_VERSION of the built library. */
 int gdn2_abi_version(void);

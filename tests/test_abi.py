@@ -77,15 +77,19 @@ def test_chunk_rejects_bad_arguments(lib):
     assert chunk_call(lib, p, flags=2) == 3  # beta scalar but w given
 
 
-def test_chunk_rejects_sequences_beyond_32bit_offsets(lib):
-    # o of one sequence (T*H*d_v fp32) must stay below 4 GiB: both prefill schedules address a
-    # sequence's rows with 32-bit byte offsets. Pointers 8 GiB apart so nothing overlaps.
-    far = [P(0x200000000 * (i + 1)) for i in range(9)]
-    T = 600_000  # 600000 * 16 * 128 * 4 B = 4.9 GB of o per sequence
-    assert chunk_call(lib, far, B=1, T=T, H=16, dk=128, dv=128) == 3
-    ws = P(0x200000000 * 20)
-    assert chunk_call(lib, far, B=1, T=T, H=16, dk=128, dv=128, ws=ws, wsb=1 << 40) == 3
-    assert lib.gdn2_chunk_fwd_workspace_bytes(1, T, 16, 128, 128, 0, 0) == 0
+def test_long_sequences_take_the_forward_not_the_backward(lib):
+    # One sequence whose o spans more than 4 GiB (600,000 x 16 x 128 x 4 B = 4.9 GB): the forward
+    # kernels address each chunk's rows from a 64-bit base, so the two-kernel path sizes a
+    # workspace for it (a slot per chunk plus the segment buffers); the backward still addresses
+    # a sequence's rows with 32-bit offsets and refuses it.
+    T = 600_000
+    nch = (T + 63) // 64
+    state = 16 * 128 * 128 * 4
+    per_chunk = lib.gdn2_chunk_fwd_workspace_bytes(1, 64, 16, 128, 128, 0, 0) - state
+    assert lib.gdn2_chunk_fwd_workspace_bytes(1, T, 16, 128, 128, 0, 0) >= state + nch * per_chunk
+    assert lib.gdn2_chunk_bwd_workspace_bytes(1, T, 16, 128, 128, 0, 0) == 0
+    far = [P(0x200000000 * (i + 1)) for i in range(16)]
+    assert lib.gdn2_chunk_bwd(*far[:16], 1, T, 16, 128, 128, 0, 0, P(0x200000000 * 20), 1 << 40, None) == 3
 
 
 def test_workspace_query_is_state_plus_one_slot_per_chunk(lib):
@@ -281,3 +285,49 @@ def test_rmsnorm_rejects_bad_arguments(lib):
     assert na(x, w, dy, x, dw, 1000, 128, 1e-6, None) == 5                 # dx over x
     assert na(x, w, dy, dx, dy, 1000, 128, 1e-6, None) == 5                # dweight over dy
     assert na(x, w, dy, dx, None, 0, 128, 1e-6, None) == 0                 # nothing to do
+
+
+def test_sdm_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    x, c1, c2, idx, wt = P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000)
+    a = lib.gdn2_sdm_address
+    assert a(x, c1, c2, -1, 2, 128, 256, 64, 0, idx, wt, None) == 2       # rows < 0
+    assert a(x, c1, c2, 4, 2, 96, 256, 64, 0, idx, wt, None) == 3         # d_k
+    assert a(x, c1, c2, 4, 2, 128, 100, 64, 0, idx, wt, None) == 3        # n not a power of two in range
+    assert a(x, c1, c2, 4, 2, 128, 64, 65, 0, idx, wt, None) == 3         # m > 64
+    assert a(x, c1, c2, 4, 2, 128, 64, 0, 0, idx, wt, None) == 3          # m = 0
+    assert a(x, None, c2, 4, 2, 128, 64, 8, 0, idx, wt, None) == 1
+    assert a(P(0x10004), c1, c2, 4, 2, 128, 64, 8, 0, idx, wt, None) == 4
+    assert a(x, c1, c2, 4, 2, 128, 64, 8, 0, P(0x10000), wt, None) == 5   # idx over x
+    assert a(x, c1, c2, 0, 2, 128, 64, 8, 0, None, None, None) == 0       # no rows: nothing to do
+    f = lib.gdn2_sdm_fwd
+    p = [P(0x100000 * (i + 1)) for i in range(12)]  # v, alpha, b, w, widx, wwt, ridx, rwt, M, stamp, L, o
+
+    def call(*ptrs, B=2, T=3, H=2, N=4096, dv=128, W=64, R=64, dt=0):
+        return f(*ptrs, B, T, H, N, dv, W, R, dt, None)
+    assert call(*p, dv=96) == 3
+    assert call(*p, W=65) == 3 and call(*p, R=0) == 3
+    assert call(*p, N=32) == 2                       # W > N
+    assert call(*p, N=0) == 2 and call(*p, N=1 << 31) == 2
+    assert call(*p, T=-1) == 2
+    q = list(p)
+    q[0] = None
+    assert call(*q) == 1
+    q = list(p)
+    q[8] = P(0x100008)
+    assert call(*q) == 4
+    q = list(p)
+    q[11] = p[10]                                    # o over L
+    assert call(*q) == 5
+    q = list(p)
+    q[9] = p[0]                                      # stamp over v
+    assert call(*q) == 5
+    q = list(p)
+    q[10] = None
+    assert call(*q) == 1
+    assert call(*p, T=0) == 0 and call(*p, B=0) == 0
+    fo = lib.gdn2_sdm_fold
+    assert fo(p[8], p[9], p[10], 2, 2, 4096, 96, None) == 3
+    assert fo(None, p[9], p[10], 2, 2, 4096, 128, None) == 1
+    assert fo(p[8], p[8], p[10], 2, 2, 4096, 128, None) == 5
+    assert fo(p[8], p[9], p[10], 0, 2, 4096, 128, None) == 0

@@ -271,3 +271,36 @@ def test_chunk_long_context_sampled_heads():
         es = normwise_err(S_T[:, h:h + 1], S_ref[:, i:i + 1])
         print(f"  head {h}: o err {eo:.2e}  S_T err {es:.2e}", flush=True)
         assert eo <= TOL16 and es <= TOL16, (h, eo, es)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_chunk_sequence_beyond_4gib(schedule):
+    """One sequence of T = 600,000 tokens at H16 d128: its o rows span 4.9 GB, past the 4 GiB a
+    32-bit byte offset reaches (rows from token 524,288 on). The first P = 520,000 tokens of every
+    head carry alpha = 1, b = w = 0 (the state stays S0, so o_t = S0^T q_t, checked in closed
+    form); the last 80,000 tokens carry the workload's gates and are checked against the oracle
+    started from S0. Two sampled heads."""
+    from gated_delta_rule_25_amd.inputs import make_inputs_torch
+    T, P = 600_000, 520_000
+    banner(f"chunk T={T} (o past 4 GiB), schedule {schedule}, heads 3 and 14")
+    g = _g()
+    wl = scaled(WORKLOADS["long_prefill"], T=T, seed=20261)
+    ins = make_inputs_torch(wl, device="cuda")
+    ins["alpha"][:, :P] = 1.0
+    ins["b"][:, :P] = 0.0
+    ins["w"][:, :P] = 0.0
+    names = ("q", "k", "v", "alpha", "b", "w")
+    o, S_T = g.chunk_fwd(*[ins[n] for n in names], ins["S0"], schedule=schedule)
+    torch.cuda.synchronize()
+    heads = [3, 14]
+    S0 = ins["S0"][:, heads].double().cpu().numpy()
+    sub = {n: ins[n][:, P:, heads].cpu() for n in names}
+    o_tail, S_ref = oracle.forward(*[sub[n] for n in names], S0)
+    for i, h in enumerate(heads):
+        q_pre = ins["q"][0, :P, h].double().cpu().numpy()
+        o_pre = q_pre @ S0[0, i]  # o_t = S0^T q_t while the state stays S0
+        e_pre = normwise_err(o[0, :P, h], o_pre)
+        e_tail = normwise_err(o[:, P:, h:h + 1], o_tail[:, :, i:i + 1])
+        es = normwise_err(S_T[:, h:h + 1], S_ref[:, i:i + 1])
+        print(f"  head {h}: o[:P] {e_pre:.2e}  o[P:] {e_tail:.2e}  S_T {es:.2e}", flush=True)
+        assert e_pre <= TOL16 and e_tail <= TOL16 and es <= TOL16, (h, e_pre, e_tail, es)
