@@ -561,6 +561,8 @@ def main(argv=None):
     if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
         for name, steps in (("long_prefill", 3), ("gdn_scalar", 10), ("kda_scalar", 10)):
             others[name] = prefill_leg(g, name, steps, args.impl)
+        if args.impl == "split":  # head size 256 runs on the two-kernel path only
+            others["d256_prefill"] = prefill_leg(g, "d256_prefill", 10, args.impl)
 
     dec = {}
     decode_runs = () if args.skip_decode else ((256, args.decode_steps),

@@ -68,12 +68,12 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         ChainIO trp = tr;
         trp.phi_tiles = DK / DVT;
         hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true, false, WS>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
-                           dim3(kChainThreads), 0, st, trp);
+                           dim3(ChainSmem<DK, DVT, BF16>::threads), 0, st, trp);
         hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 8)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
         const ChainIO fu{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G, a.B, a.T, a.H, a.DV,
                          sseg, (long)G * DK * a.DV, ld * a.DV, a.DV,
                          Sbuf, ld * a.DV, 0, a.DV, 1};
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS>), dim3(G * BHp * tiles), dim3(kChainThreads), 0,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS>), dim3(G * BHp * tiles), dim3(ChainSmem<DK, DVT, BF16>::threads), 0,
                            st, fu);
         return hipGetLastError();
     }
@@ -87,7 +87,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         const ChainIO io{a.v, a.w, a.o, ws, cnt, n0, n0 + cnt, cnt, 1, a.B, a.T, a.H, a.DV,
                          n0 == 0 ? a.S0 : Sbuf, ld * a.DV, 0, a.DV,
                          Sbuf, ld * a.DV, 0, a.DV, 0};
-        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS>), dim3(BHp * tiles), dim3(kChainThreads), 0, st,
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS>), dim3(BHp * tiles), dim3(ChainSmem<DK, DVT, BF16>::threads), 0, st,
                            io);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -130,7 +130,7 @@ hipError_t launch_states_t(const ChunkArgs& a, char* blobs, uint16_t* S_save, ui
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
     hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
-                       dim3(kChainThreads), 0, st, io);
+                       dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
     return hipGetLastError();
 }
 
@@ -144,7 +144,8 @@ hipError_t launch_split_states(const ChunkArgs& a, char* blobs, uint16_t* S_save
         switch (a.DK) {
             case 32: return launch_states_t<32, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
             case 64: return launch_states_t<64, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
-            default: return launch_states_t<128, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            case 128: return launch_states_t<128, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            default: return hipErrorNotSupported;
         }
     };
     switch ((a.flags >> 2) & 3u) {  // prologue flags, as the forward takes them
@@ -161,6 +162,12 @@ bool split_supported(int T, int H, int DK, int DV, bool bf16) {
     return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
 }
 
+// gdn2_chunk_fwd's equal-length batches also take bf16 at d = 256 (one block buffer in the chain
+// kernel); the packed batches and the backward's state pass stay at d <= 128.
+bool split_fwd_supported(int T, int H, int DK, int DV, bool bf16) {
+    return split_supported(T, H, DK, DV, bf16) || (bf16 && DK == 256 && DV == 256 && T >= 0);
+}
+
 size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16) {
     const size_t nch = ((size_t)T + CH - 1) / CH;
     const SplitPlan plan = split_plan(B, T, H, DK, DV);
@@ -170,7 +177,10 @@ size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16) {
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16) {
     size_t blob = 0;
     if (bf16) {
-        blob = DK == 32 ? Blob<32, true>::bytes : DK == 64 ? Blob<64, true>::bytes : Blob<128, true>::bytes;
+        blob = DK == 32    ? Blob<32, true>::bytes
+               : DK == 64  ? Blob<64, true>::bytes
+               : DK == 128 ? Blob<128, true>::bytes
+                           : Blob<256, true>::bytes;
     } else {
         blob = Blob<32, false>::bytes;
     }
@@ -178,15 +188,17 @@ size_t split_chunk_bytes(int B, int H, int DK, bool bf16) {
 }
 
 hipError_t launch_split(const ChunkArgs& a, hipStream_t s) {
-    if (!split_supported(a.T, a.H, a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
+    if (!split_fwd_supported(a.T, a.H, a.DK, a.DV, a.bf16)) return hipErrorNotSupported;
     if (a.bf16) {
         switch (a.DK) {
             case 32: return launch_split_flags<32, true>(a, s);
             case 64: return launch_split_flags<64, true>(a, s);
-            default: return launch_split_flags<128, true>(a, s);
+            case 128: return launch_split_flags<128, true>(a, s);
+            case 256: return launch_split_flags<256, true>(a, s);
+            default: return hipErrorNotSupported;
         }
     }
-    return launch_split_flags<32, false>(a, s);
+    return a.DK == 32 ? launch_split_flags<32, false>(a, s) : hipErrorNotSupported;
 }
 
 }  // namespace gdn2

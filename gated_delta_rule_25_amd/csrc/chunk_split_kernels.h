@@ -93,7 +93,8 @@ struct PrepSmem {
     static constexpr int oAd = oA + CH * AP * ES;
     static constexpr int bytes = oAd + 4 * ADS * 4;
     static_assert(BL::oTm - BL::oKbT == DK * CHP * ES && out1Bytes == DK * CHP * ES + BL::TPE * ES, "layout");
-    static_assert(bytes <= 80 * 1024, "prep LDS must allow two workgroups per CU");
+    // two workgroups per CU up to d = 128; at d = 256 one (its block alone is 110 KB)
+    static_assert(bytes <= (DK <= 128 ? 80 : 160) * 1024, "prep LDS budget");
 };
 
 // PRO (prologue): bit 0, q and k are L2-normalised over d_k per token here; bit 1, alpha and b
@@ -567,12 +568,16 @@ struct ChainSmem {
     static constexpr int NT = kChainNT;
     static constexpr int NWC = DVT / (16 * NT);                 // chain waves
     static constexpr int CW0 = NT == 1 ? 4 : 2;                 // first copy wave = copy waves
-    static constexpr int threads = kChainThreads;
-    static_assert(threads == 2 * CW0 * 64, "wave layout");
     static constexpr int VWB = CH * 16 * NT * (F16 ? 2 : 4);  // one of v, w: 64 rows x 16 NT columns
+    // Two block buffers (the copy of chunk n + 1 overlaps chunk n) when they fit; at d = 256 one
+    // block is 110 KB, so there is one buffer, the copy follows the chunk, and the chain waves
+    // make it themselves: no copy waves, so each chain wave has a SIMD and its 512 registers.
+    static constexpr bool ONEBUF = 2 * BL::bytes + NWC * 2 * VWB > 160 * 1024;
+    static constexpr int threads = ONEBUF ? NWC * 64 : kChainThreads;
+    static_assert(ONEBUF || threads == 2 * CW0 * 64, "wave layout");
     static constexpr int oBuf0 = 0;
-    static constexpr int oBuf1 = BL::bytes;
-    static constexpr int oVW = 2 * BL::bytes;                   // per chain wave: v then w
+    static constexpr int oBuf1 = ONEBUF ? 0 : BL::bytes;
+    static constexpr int oVW = (ONEBUF ? 1 : 2) * BL::bytes;    // per chain wave: v then w
     static constexpr int bytes = oVW + NWC * 2 * VWB;
     static constexpr bool fits = bytes <= 160 * 1024 && NWC >= 1 && NWC <= CW0;
 };
@@ -621,7 +626,7 @@ struct ChainIO {
 // VAR: packed batch (ChainIO::var); a sequence without tokens only carries S_in to S_out.
 template <int DK, int DVT, bool BF16, bool BS, bool STATE, bool SAVE = false, bool WSIG = false,
           bool VAR = false>
-__global__ void __launch_bounds__(kChainThreads, 1)
+__global__ void __launch_bounds__((ChainSmem<DK, DVT, BF16>::threads), 1)
 chain_kernel(const ChainIO io) {
     constexpr bool F16 = BF16;
     using PR = Prec<F16>;
@@ -682,7 +687,7 @@ chain_kernel(const ChainIO io) {
     if (!VAR && n_count <= 0) return;
     const bool phi = STATE && tile >= vt;     // transition tile: U = 0, identity start
     const bool chain = wv < NWC;
-    const bool copier = wv >= CW0;
+    const bool copier = !SM::ONEBUF && wv >= CW0;  // one buffer: the chain waves copy
     // this wave's first state column: in v space, or in k space for a transition tile
     const int col0 = (phi ? (tile - vt) : tile) * DVT + (chain ? wv : 0) * 16 * NT;
     float* const o = io.o;
@@ -785,6 +790,10 @@ chain_kernel(const ChainIO io) {
             wait_dma();
         } else if (chain && !phi) {
             dma_vw(c_begin);
+        }
+        if constexpr (SM::ONEBUF) {
+            dma_flat(blobs, smem + SM::oBuf0, COPY, wv, NWC, lane);
+            wait_dma();
         }
     }
 
@@ -940,12 +949,19 @@ chain_kernel(const ChainIO io) {
                         store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0] * isc, O[c][nt][1] * isc,
                                O[c][nt][2] * isc, O[c][nt][3] * isc);
             }
-        } else if (copier) {
+        } else if (copier && !SM::ONEBUF) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
             // chunk's barrier
             if (nc + 1 < n_count)
                 dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + ((nc & 1) ? SM::oBuf0 : SM::oBuf1), COPY,
                          wv - CW0, CW0, lane);
+            wait_dma();
+        }
+        if constexpr (SM::ONEBUF) {
+            // one buffer: the next chunk's blob replaces this one once every chain wave is done
+            // with it (the barrier at the top of the loop then waits for the copy)
+            lds_barrier();
+            if (nc + 1 < n_count) dma_flat(blobs + (size_t)(nc + 1) * BL::bytes, smem + SM::oBuf0, COPY, wv, NWC, lane);
             wait_dma();
         }
     }

@@ -129,7 +129,7 @@ hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
     io.var = vt;
     const int BH = N * a.H, BHp = (BH + 7) / 8 * 8;
     hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, false, false, WS, true>), dim3(BHp * (a.DV / DVT)),
-                       dim3(kChainThreads), 0, st, io);
+                       dim3(ChainSmem<DK, DVT, BF16>::threads), 0, st, io);
     return hipGetLastError();
 }
 
@@ -162,7 +162,7 @@ hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, 
     io.Dl_save = Dl_save;
     const int BH = N * a.H, BHp = (BH + 7) / 8 * 8;
     hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true, (PRO & 2) != 0, true>),
-                       dim3(BHp * (a.DV / DVT)), dim3(kChainThreads), 0, st, io);
+                       dim3(BHp * (a.DV / DVT)), dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
     return hipGetLastError();
 }
 
@@ -208,7 +208,8 @@ hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, lo
         switch (a.DK) {
             case 32: return launch_varlen_states_t<32, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
             case 64: return launch_varlen_states_t<64, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
-            default: return launch_varlen_states_t<128, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            case 128: return launch_varlen_states_t<128, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            default: return hipErrorNotSupported;
         }
     };
     switch ((a.flags >> 2) & 3u) {
@@ -225,7 +226,8 @@ hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s) {
         switch (a.DK) {
             case 32: return launch_varlen_flags<32, true>(a, s);
             case 64: return launch_varlen_flags<64, true>(a, s);
-            default: return launch_varlen_flags<128, true>(a, s);
+            case 128: return launch_varlen_flags<128, true>(a, s);
+            default: return hipErrorNotSupported;
         }
     }
     return launch_varlen_flags<32, false>(a, s);

@@ -237,9 +237,9 @@ gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v, cons
 
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                       int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags) {
-    if (B <= 0 || H <= 0 || T <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    if (B <= 0 || H <= 0 || T <= 0 || !dim_ok_tok(d_k) || !dim_ok_tok(d_v)) return 0;
     const bool bf16 = in_dtype == GDN2_BF16;
-    if (!gdn2::split_supported(T, H, d_k, d_v, bf16)) return 0;
+    if (!gdn2::split_fwd_supported(T, H, d_k, d_v, bf16)) return 0;
     return gdn2::split_workspace_bytes(B, T, H, d_k, d_v, bf16);
 }
 
@@ -248,13 +248,14 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const vo
                            float* S_out, int32_t B, int32_t T, int32_t H, int32_t d_k,
                            int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                            void* workspace, size_t workspace_bytes, void* stream) {
+    // head size 256 passes here and is taken by the two-kernel path only (bf16, with a workspace)
     gdn2_status st = validate(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype,
-                              gate_flags, false);
+                              gate_flags, false, true);
     if (st != GDN2_OK) return st;
     if (!chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
     const bool bf16 = in_dtype == GDN2_BF16;
     const bool fused = gdn2::fused_supported(T, H, d_k, d_v, bf16);
-    const bool split = workspace && workspace_bytes > 0 && gdn2::split_supported(T, H, d_k, d_v, bf16);
+    const bool split = workspace && workspace_bytes > 0 && gdn2::split_fwd_supported(T, H, d_k, d_v, bf16);
     if (split) {
         const size_t min_bytes = split_min_bytes(B, H, d_k, d_v, bf16);
         if (workspace_bytes < min_bytes) return GDN2_ERR_WORKSPACE;

@@ -53,6 +53,8 @@ WORKLOADS = {
                            seed=20253),
     "kda_scalar": Workload("kda_scalar", B=8, T=4096, H=16, d_k=128, d_v=128, gates="kda",
                            seed=20253),
+    # head size 256 with the same 262,144 state floats per batch element (4 heads of 256 x 256)
+    "d256_prefill": Workload("d256_prefill", B=8, T=4096, H=4, d_k=256, d_v=256, seed=20262),
 }
 
 DECODE_WORKLOAD = dict(B=256, H=16, d_k=128, d_v=128, steps=1000, alpha_mu=3.0, s0_std=0.1,

@@ -144,10 +144,21 @@ def test_decode_slots_rejects_bad_arguments(lib):
     assert f(*p, P(0x10000), slots, o, 2, 1, 128, 128, 4, 0, 0, None) == 5
 
 
-def test_head_size_256_is_taken_by_decode_and_token_paths_only(lib):
-    # the chunked prefill refuses d = 256 on the host (no launch); decode accepts the size and
-    # fails later only for the fake pointers' aliasing, not for the size
-    assert chunk_call(lib, dk=256, dv=256) == 3
+def test_head_size_256_on_the_chunked_prefill(lib):
+    # d = 256 is taken by the two-kernel path only: bf16 with a workspace. Without a workspace,
+    # with fp32, or in packed batches and the backward, it is refused on the host (no launch).
+    far = [P(0x200000000 * (i + 1)) for i in range(9)]  # 8 GiB apart: nothing overlaps
+    assert chunk_call(lib, far, dk=256, dv=256) == 3                  # no workspace
+    assert chunk_call(lib, far, dk=256, dv=256, dt=1, ws=P(0x200000000 * 20), wsb=1 << 30) == 3  # fp32
+    q = lib.gdn2_chunk_fwd_workspace_bytes
+    state = 2 * 16 * 256 * 256 * 4
+    one = q(2, 64, 16, 256, 256, 0, 0)
+    assert one > state and (one - state) % 256 == 0
+    # a slot per chunk (plus segment buffers: 2 x 16 heads x 4 tiles do not fill the chip)
+    assert q(2, 4096, 16, 256, 256, 0, 0) >= state + 64 * (one - state)
+    assert q(2, 4096, 16, 256, 256, 1, 0) == 0
+    assert lib.gdn2_chunk_fwd_varlen_workspace_bytes(4, 4096, 16, 256, 256, 0, 0) == 0
+    assert lib.gdn2_chunk_bwd_workspace_bytes(2, 4096, 16, 256, 256, 0, 0) == 0
 
 
 def test_varlen_rejects_bad_arguments(lib):

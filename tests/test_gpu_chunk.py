@@ -304,3 +304,33 @@ def test_chunk_sequence_beyond_4gib(schedule):
         es = normwise_err(S_T[:, h:h + 1], S_ref[:, i:i + 1])
         print(f"  head {h}: o[:P] {e_pre:.2e}  o[P:] {e_tail:.2e}  S_T {es:.2e}", flush=True)
         assert e_pre <= TOL16 and e_tail <= TOL16 and es <= TOL16, (h, e_pre, e_tail, es)
+
+
+D256_CASES = [
+    ("bf16_d256_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=2, d_k=256, d_v=256)),
+    ("bf16_d256_T1", scaled(WORKLOADS["prefill_1p3b"], B=1, T=1, H=2, d_k=256, d_v=256)),
+    ("bf16_d256_T65", scaled(WORKLOADS["prefill_1p3b"], B=1, T=65, H=3, d_k=256, d_v=256)),
+    ("bf16_d256_gdn", scaled(WORKLOADS["gdn_scalar"], B=1, T=257, H=2, d_k=256, d_v=256)),
+    ("bf16_d256_kda", scaled(WORKLOADS["kda_scalar"], B=2, T=130, H=2, d_k=256, d_v=256)),
+    ("bf16_d256_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=1, T=190, H=2, d_k=256, d_v=256,
+                                      alpha_mu=-2.0)),
+    # one sequence of 47 chunks on 2 heads: few enough workgroups that the sequence is cut into
+    # segments (the state-only transition pass, the scan, then all segments at once)
+    ("bf16_d256_segmented", scaled(WORKLOADS["long_prefill"], B=1, T=3000, H=2, d_k=256, d_v=256)),
+]
+
+
+@pytest.mark.parametrize("name,wl", D256_CASES, ids=[c[0] for c in D256_CASES])
+def test_chunk_d256_matches_oracle(name, wl):
+    """Head size 256 on the two-kernel path (bf16, with a workspace: one block buffer in the
+    chain kernel); the page "NVIDIA улучшила память LLM…", section "Аналитика", sizes the state by
+    its total, which a 256 x 256 head also meets."""
+    banner(f"chunk d256 {name} {wl}")
+    _check(name, make_inputs(wl), TOL16, "split")
+
+
+def test_chunk_d256_needs_a_workspace():
+    g = _g()
+    ins = _cuda(make_inputs(scaled(WORKLOADS["prefill_1p3b"], B=1, T=64, H=1, d_k=256, d_v=256)))
+    with pytest.raises(g.Gdn2Error):
+        g.chunk_fwd(ins["q"], ins["k"], ins["v"], ins["alpha"], ins["b"], ins["w"], ins["S0"], schedule="fused")
