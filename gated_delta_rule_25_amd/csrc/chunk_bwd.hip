@@ -594,45 +594,37 @@ __global__ void __launch_bounds__(256, 2) bwd_contract_kernel(const ContractIO i
             Tg[r * TP + cc] = (c <= wv && cc <= r) ? aT[c][j] : 0.f;
         }
     __syncthreads();
-    const int rb = tid / 16, cb = tid % 16;  // 4 x 4 tile of rows 4 rb.., columns 4 cb..
-    float xacc[4][4] = {};
-    for (int m = 0; m < CH; ++m) {
-        float tr[4], tc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            tr[q] = Tf[m * TP + 4 * rb + q];
-            tc[q] = Tg[m * TP + 4 * cb + q];
+    // X = T^T dT, then dA = -X T^T on the strictly lower triangle, on the matrix cores in fp32
+    // (16x16x4 steps): wave wv computes rows 16 wv .. 16 wv + 15 as four 16-column tiles. Lane
+    // (l16, g) supplies A[l16][g] and B[g][l16] of a step and receives rows 16 wv + 4 g + v,
+    // column l16 of the tile. T and dT are lower triangular, so X's tile (wv, c) sums over
+    // k >= 16 max(wv, c) only, and dA's tile c <= wv over k < 16 (c + 1); tiles c > wv are zero.
+    for (int c = 0; c < 4; ++c) {
+        f4 xt = f4{0.f, 0.f, 0.f, 0.f};
+        const int k0 = 4 * (wv > c ? wv : c);
+        for (int ks = k0; ks < 16; ++ks) {
+            const int m = 4 * ks + g;
+            xt = __builtin_amdgcn_mfma_f32_16x16x4f32(Tf[m * TP + 16 * wv + l16], Tg[m * TP + 16 * c + l16], xt, 0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) xacc[q][c] = fmaf(tr[q], tc[c], xacc[q][c]);
+        for (int v = 0; v < 4; ++v) Xm[(16 * wv + 4 * g + v) * TP + 16 * c + l16] = xt[v];
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) Xm[(4 * rb + q) * TP + 4 * cb + c] = xacc[q][c];
     __syncthreads();
-    float dacc[4][4] = {};
-    for (int m = 0; m < CH; ++m) {
-        float xr[4], tc[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xr[q] = Xm[(4 * rb + q) * TP + m];
-            tc[q] = Tf[(4 * cb + q) * TP + m];
+    for (int c = 0; c < 4; ++c) {
+        f4 d = f4{0.f, 0.f, 0.f, 0.f};
+        if (c <= wv) {
+            for (int ks = 0; ks < 4 * (c + 1); ++ks) {
+                const int m = 4 * ks + g;
+                d = __builtin_amdgcn_mfma_f32_16x16x4f32(Xm[(16 * wv + l16) * TP + m], Tf[(16 * c + l16) * TP + m], d, 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) dacc[q][c] = fmaf(xr[q], tc[c], dacc[q][c]);
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * wv + 4 * g + v, cc = 16 * c + l16;
+            io.dAm[(cbase * CH + r) * CH + cc] = cc < r ? -d[v] : 0.f;
+        }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int r = 4 * rb + q, cc = 4 * cb + c;
-            io.dAm[(cbase * CH + r) * CH + cc] = cc < r ? -dacc[q][c] : 0.f;
-        }
 }
 
 // ------------------------------------------------------------------------------------------
