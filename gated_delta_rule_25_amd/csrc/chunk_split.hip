@@ -68,7 +68,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
         ChainIO trp = tr;
         trp.phi_tiles = DK / DVT;
         hipLaunchKernelGGL((chain_kernel<DK, DVT, BF16, BS, true, false, WS>), dim3((G - 1) * BHp * (tiles + DK / DVT)),
-                           dim3(ChainSmem<DK, DVT, BF16>::threads), 0, st, trp);
+                           dim3(ChainSmem<DK, DVT, BF16, true>::threads), 0, st, trp);
         hipLaunchKernelGGL((scan_kernel<DK>), dim3(BH * (a.DV / 8)), dim3(256), 0, st, a.S0, psiphi, sseg, G, a.DV);
         const ChainIO fu{a.v, a.w, a.o, ws, nch, 0, nch, plan.seg_len, G, a.B, a.T, a.H, a.DV,
                          sseg, (long)G * DK * a.DV, ld * a.DV, a.DV,

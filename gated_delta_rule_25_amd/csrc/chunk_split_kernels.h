@@ -562,7 +562,11 @@ prep_kernel(const void* q, const void* k, const void* alpha, const void* b, int 
 constexpr int kChainNT = 1;
 constexpr int kChainThreads = 2 * (kChainNT == 1 ? 4 : 2) * 64;
 
-template <int DK, int DVT, bool F16>
+// SMALL: the state-only pass of a segmented sequence (no saves). It copies only the block's
+// prefix, into one buffer, so its workgroups take under 80 KB of LDS and two share a CU: its grid
+// (segments x heads x state and transition tiles) is larger than the chip, and a second
+// workgroup on the CU covers the copy that the one buffer leaves exposed.
+template <int DK, int DVT, bool F16, bool SMALL = false>
 struct ChainSmem {
     using BL = Blob<DK, F16>;
     static constexpr int NT = kChainNT;
@@ -572,13 +576,15 @@ struct ChainSmem {
     // Two block buffers (the copy of chunk n + 1 overlaps chunk n) when they fit; at d = 256 one
     // block is 110 KB, so there is one buffer, the copy follows the chunk, and the chain waves
     // make it themselves: no copy waves, so each chain wave has a SIMD and its 512 registers.
-    static constexpr bool ONEBUF = 2 * BL::bytes + NWC * 2 * VWB > 160 * 1024;
+    static constexpr int BUF = SMALL ? (BL::stateBytes + 255) / 256 * 256 : BL::bytes;
+    static constexpr bool ONEBUF = SMALL || 2 * BL::bytes + NWC * 2 * VWB > 160 * 1024;
     static constexpr int threads = ONEBUF ? NWC * 64 : kChainThreads;
     static_assert(ONEBUF || threads == 2 * CW0 * 64, "wave layout");
     static constexpr int oBuf0 = 0;
-    static constexpr int oBuf1 = ONEBUF ? 0 : BL::bytes;
-    static constexpr int oVW = (ONEBUF ? 1 : 2) * BL::bytes;    // per chain wave: v then w
+    static constexpr int oBuf1 = ONEBUF ? 0 : BUF;
+    static constexpr int oVW = (ONEBUF ? 1 : 2) * BUF;          // per chain wave: v then w
     static constexpr int bytes = oVW + NWC * 2 * VWB;
+    static constexpr int min_blocks = (SMALL && bytes <= 80 * 1024) ? 2 : 1;
     static constexpr bool fits = bytes <= 160 * 1024 && NWC >= 1 && NWC <= CW0;
 };
 
@@ -626,14 +632,15 @@ struct ChainIO {
 // VAR: packed batch (ChainIO::var); a sequence without tokens only carries S_in to S_out.
 template <int DK, int DVT, bool BF16, bool BS, bool STATE, bool SAVE = false, bool WSIG = false,
           bool VAR = false>
-__global__ void __launch_bounds__((ChainSmem<DK, DVT, BF16>::threads), 1)
+__global__ void __launch_bounds__((ChainSmem<DK, DVT, BF16, STATE && !SAVE>::threads),
+                                  (ChainSmem<DK, DVT, BF16, STATE && !SAVE>::min_blocks))
 chain_kernel(const ChainIO io) {
     constexpr bool F16 = BF16;
     using PR = Prec<F16>;
     using E = typename PR::E;
     using Frag = typename PR::Frag;
     using BL = Blob<DK, F16>;
-    using SM = ChainSmem<DK, DVT, F16>;
+    using SM = ChainSmem<DK, DVT, F16, STATE && !SAVE>;
     static_assert(SM::fits, "chain LDS budget or wave layout");
     constexpr int NT = SM::NT, NWC = SM::NWC, CW0 = SM::CW0;
     constexpr int NKS = DK / 32, NMK = DK / 16;
