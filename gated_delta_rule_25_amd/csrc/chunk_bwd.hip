@@ -79,6 +79,10 @@ struct ChainBwdIO {
     float* dv;
     float* dw;
     float* dS0;  // [B, H, DK, DV] or null
+    // scalar beta (BS): w points at the [B, T, H] scalars, and the reverse chain writes per token
+    // row and 16-column group the partial sums of dL/dbeta through w, dwp[row][npw]
+    float* dwp = nullptr;
+    int npw = 0;
     int B, T, H, DV, nch;
     // packed batch (VAR): B sequences, T rows, blocks and saves [h][chunk of the batch] with `ring`
     // slots per head
@@ -141,7 +145,8 @@ constexpr int bwd_chain_threads() {
 
 // WSIG: w holds pre-activations (the prologue's gate logits): the gate is sigma(w), and dw is
 // taken with respect to the pre-activation.
-template <int DK, bool WSIG = false, bool VAR = false>
+// BS: a scalar beta per token row stands for w (its partial gradients go to io.dwp).
+template <int DK, bool WSIG = false, bool VAR = false, bool BS = false>
 __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(const ChainBwdIO io) {
     using PR = Prec<true>;
     using E = _Float16;
@@ -205,7 +210,8 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     const auto rs_dv = make_rsrc(io.dv + seq * DV, seq_f32);
     const auto rs_dw = make_rsrc(io.dw + seq * DV, seq_f32);
     const auto rs_v = make_rsrc(static_cast<const uint16_t*>(io.v) + seq * DV, (unsigned)Tq * H * DV * 2u);
-    const auto rs_w = make_rsrc(static_cast<const uint16_t*>(io.w) + seq * DV, (unsigned)Tq * H * DV * 2u);
+    const auto rs_w = BS ? make_rsrc(static_cast<const uint16_t*>(io.w) + seq, (unsigned)Tq * H * 2u)
+                         : make_rsrc(static_cast<const uint16_t*>(io.w) + seq * DV, (unsigned)Tq * H * DV * 2u);
     // element index of (token row 0 of the sequence, head hh, column col)
     auto elem = [&](int row) -> unsigned { return ((unsigned)row * H + hh) * DV + col; };
 
@@ -255,11 +261,16 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             const int row = t0 + rr0 + 16 * q;
             xdO[q] = __builtin_amdgcn_raw_buffer_load_b128(rs_dO, (int)row_off(row), 0, 0);
             const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(row_off(row) / 2u), 0, 0);
-            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, (int)(row_off(row) / 2u), 0, 0);
             xv[q][0] = v2[0];
             xv[q][1] = v2[1];
-            xw[q][0] = w2[0];
-            xw[q][1] = w2[1];
+            if constexpr (BS) {  // the row's scalar beta, in both halves of both words
+                const uint32_t x = __builtin_amdgcn_raw_buffer_load_b16(rs_w, (int)(((unsigned)row * H + hh) * 2u), 0, 0);
+                xw[q][0] = xw[q][1] = x | (x << 16);
+            } else {
+                const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, (int)(row_off(row) / 2u), 0, 0);
+                xw[q][0] = w2[0];
+                xw[q][1] = w2[1];
+            }
         }
     };
     auto bf = [](uint32_t x, int h) { return __uint_as_float(h ? (x & 0xffff0000u) : (x << 16)); };
@@ -401,8 +412,18 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             const unsigned off = row_off(t0 + rr0 + 16 * q);
             store_h4(rs_dDp, off / 2u, x);
             store4(rs_dv, off, cw[q][0] * x.x, cw[q][1] * x.y, cw[q][2] * x.z, cw[q][3] * x.w);
-            store4(rs_dw, off, cs[q][0] * cv[q][0] * x.x, cs[q][1] * cv[q][1] * x.y, cs[q][2] * cv[q][2] * x.z,
-                   cs[q][3] * cv[q][3] * x.w);
+            if constexpr (BS) {
+                // this row's sum over the wave's 16 columns (the four lanes of the row), one
+                // partial per row and 16-column group
+                float p = cs[q][0] * (cv[q][0] * x.x + cv[q][1] * x.y + cv[q][2] * x.z + cv[q][3] * x.w);
+                p += __shfl_xor(p, 1);
+                p += __shfl_xor(p, 2);
+                const int t = t0 + rr0 + 16 * q;
+                if (cc == 0 && t < Tq) io.dwp[((tbase + t) * H + hh) * io.npw + colw / 16] = p;
+            } else {
+                store4(rs_dw, off, cs[q][0] * cv[q][0] * x.x, cs[q][1] * cv[q][1] * x.y, cs[q][2] * cv[q][2] * x.z,
+                       cs[q][3] * cv[q][3] * x.w);
+            }
         }
         // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (ET holds -E_hat^T)
         const Frag dPf[2] = {stack(dP[0], dP[1]), stack(dP[2], dP[3])};
@@ -637,6 +658,9 @@ struct KeyIO {
     const uint16_t *S_save, *G_save;  // chunk-start states and chunk-end gradients (fp16)
     const float *dPm, *dAm;           // [slot][64][64]
     float *dq, *dk, *dalpha, *db;  // [B, T, H, DK]
+    // scalar gates (AS, BS): alpha and b are [B, T, H]; the kernel writes per token row and
+    // channel group the partial sums of the scalar's gradient, dap / dbp [row][DK / 32]
+    float *dap = nullptr, *dbp = nullptr;
     int B, T, H, nch;
     VarTab var{};  // packed batch: as ChainBwdIO's
     long ring = 0;
@@ -659,7 +683,7 @@ struct KeyIO {
 // are left with respect to the normalised vectors (a later pass takes them through the norm);
 // bit 1, alpha and b are pre-activations: log2 alpha = log2 sigma(x), b = sigma(x), and dalpha, db
 // are taken with respect to the pre-activations.
-template <int DK, int PRO = 0, bool VAR = false>
+template <int DK, int PRO = 0, bool VAR = false, bool AS = false, bool BS = false>
 __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
     constexpr bool L2N = (PRO & 1) != 0, GL = (PRO & 2) != 0;
     constexpr int CW = 32;       // key channels per workgroup
@@ -731,11 +755,23 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
-        const size_t e = (((tbase + (t < Tq ? t : 0)) * H + hh) * DK + c0 + ch0) / 2;
+        const size_t rowi = (tbase + (t < Tq ? t : 0)) * H + hh;
+        const size_t e = (rowi * DK + c0 + ch0) / 2;
         rq[j] = q32[e];
         rk[j] = k32[e];
-        rbv[j] = b32[e];
-        ra[j] = a32[e];
+        // a scalar gate goes in both halves of the word, as if repeated over the channel pair
+        if constexpr (BS) {
+            const uint32_t x = static_cast<const uint16_t*>(io.b)[rowi];
+            rbv[j] = x | (x << 16);
+        } else {
+            rbv[j] = b32[e];
+        }
+        if constexpr (AS) {
+            const uint32_t x = static_cast<const uint16_t*>(io.alpha)[rowi];
+            ra[j] = x | (x << 16);
+        } else {
+            ra[j] = a32[e];
+        }
     }
 
     // ---- dQ_hat = dO S^T, dE_hat = -dD' S^T, dK_bar = Delta G'^T for this group's channels,
@@ -1064,14 +1100,29 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
             yy[c][j] = Y[j];
         }
     }
+    // a scalar gate's gradient: the row's sum over the group's 32 channels (the 16 lanes of the
+    // row, two channels each), one partial per row and channel group
+    auto row_partial = [&](float x) {
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        return x;
+    };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
+        float pb = 0.f;
+        if constexpr (BS) pb = row_partial(yy[0][j] + yy[1][j]);
         if (t < Tq) {
             const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
             *reinterpret_cast<float2*>(io.dq + e) = make_float2(xa[0][j], xa[1][j]);
             *reinterpret_cast<float2*>(io.dk + e) = make_float2(xp[0][j], xp[1][j]);
-            *reinterpret_cast<float2*>(io.db + e) = make_float2(yy[0][j], yy[1][j]);
+            if constexpr (BS) {
+                if (l16 == 0) io.dbp[((tbase + t) * H + hh) * NG + cg] = pb;
+            } else {
+                *reinterpret_cast<float2*>(io.db + e) = make_float2(yy[0][j], yy[1][j]);
+            }
         }
     }
 
@@ -1105,9 +1156,15 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
+        float pa = 0.f;
+        if constexpr (AS) pa = row_partial(dal[j][0] + dal[j][1]);
         if (t < Tq) {
-            const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
-            *reinterpret_cast<float2*>(io.dalpha + e) = make_float2(dal[j][0], dal[j][1]);
+            if constexpr (AS) {
+                if (l16 == 0) io.dap[((tbase + t) * H + hh) * NG + cg] = pa;
+            } else {
+                const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
+                *reinterpret_cast<float2*>(io.dalpha + e) = make_float2(dal[j][0], dal[j][1]);
+            }
         }
     }
 }
@@ -1117,37 +1174,26 @@ __global__ void __launch_bounds__(256) copy_or_zero(float* dst, const float* src
     if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-// Scalar gates through the general backward: each scalar is repeated over the channels of its
-// row (bf16, exactly), and the gradient of the scalar is the sum of its copies' gradients.
-__global__ void __launch_bounds__(256) repeat_bf16(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                   long rows, int D) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;  // one 8-element group of a row
-    const int per = D / 8;
-    if (i >= rows * per) return;
-    const uint32_t x = in[i / per];
-    const uint32_t p = x | (x << 16);
-    *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(p, p, p, p);
-}
-
-// out[r] = sum over the D entries of row r of a (plus the D entries of row r of b, if given)
-template <int D>
-__global__ void __launch_bounds__(256) row_sums(const float* __restrict__ a, const float* __restrict__ b,
-                                                float* __restrict__ out, long rows) {
-    constexpr int LPR = D / 4, RPB = 256 / LPR;  // a group of D / 4 lanes per row, 16 bytes each
-    const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
-    const int c = (threadIdx.x % LPR) * 4;
-    float acc = 0.f;
-    if (r < rows) {  // groups are row-aligned: a group is all in or all out
-        const float4 x = *reinterpret_cast<const float4*>(a + r * D + c);
-        acc = (x.x + x.y) + (x.z + x.w);
-        if (b) {
-            const float4 y = *reinterpret_cast<const float4*>(b + r * D + c);
-            acc += (y.x + y.y) + (y.z + y.w);
-        }
+// The gradients of the scalar gates from the kernels' per-row partial sums, added in a fixed
+// order: dalpha[r] = sum of dap[r][0 .. na), db[r] = sum of dbp[r][0 .. nb) + sum of dwp[r][0 .. nw).
+__global__ void __launch_bounds__(256) scalar_gate_sums(const float* __restrict__ dap, int na,
+                                                        const float* __restrict__ dbp, int nb,
+                                                        const float* __restrict__ dwp, int nw,
+                                                        float* __restrict__ dalpha, float* __restrict__ db, long rows) {
+    const long r = (long)blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    if (dap) {
+        float x = 0.f;
+        for (int i = 0; i < na; ++i) x += dap[r * na + i];
+        dalpha[r] = x;
     }
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (r < rows && threadIdx.x % LPR == 0) out[r] = acc;
+    if (dbp) {
+        float x = 0.f;
+        for (int i = 0; i < nb; ++i) x += dbp[r * nb + i];
+        float y = 0.f;
+        for (int i = 0; i < nw; ++i) y += dwp[r * nw + i];
+        db[r] = x + y;
+    }
 }
 
 // 1 / max(|x|, 1e-12) of each row of D bf16 values. A group of D / 8 lanes owns a row, one
@@ -1252,8 +1298,12 @@ BwdLayout bwd_layout_var(int n, int T, int H, int DK, int DV) {
     return bwd_layout_n((size_t)H * varlen_chunk_bound(n, T), (size_t)T * H, DK, DV, varlen_table_bytes(n));
 }
 
-template <int DK, int PRO, bool VAR>
-hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hipStream_t st) {
+// Scalar gates (AS, BS): the kernels read the [B, T, H] scalars themselves and write per-row
+// partial sums of their gradients into dap (DK / 32 per row), dbp (DK / 32) and dwp (DV / 16);
+// scalar_gate_sums adds them up.
+template <int DK, int PRO, bool VAR, bool AS, bool BS>
+hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, float* dap, float* dbp, float* dwp,
+                        hipStream_t st) {
     const BwdLayout L = VAR ? bwd_layout_var(a.B, a.T, a.H, DK, a.DV) : bwd_layout(a.B, a.T, a.H, DK, a.DV);
     char* ws = static_cast<char*>(a.workspace);
     const int BH = a.B * a.H, nch = (a.T + CH - 1) / CH;
@@ -1277,18 +1327,24 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
     float* dAm = reinterpret_cast<float*>(ws + L.dAm);
 
     ChunkArgs fa{a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, nullptr, nullptr, a.B, a.T, a.H, DK, a.DV,
-                 true, (uint32_t)PRO << 2, nullptr, 0};
+                 true, ((uint32_t)PRO << 2) | (AS ? 1u : 0u) | (BS ? 2u : 0u), nullptr, 0};
     fa.cu_seqlens = a.cu_seqlens;
     hipError_t e = VAR ? launch_varlen_states(fa, ws, blobs, ring, S_save, Dp, Dl, st)
                        : launch_split_states(fa, blobs, S_save, Dp, Dl, st);
     if (e != hipSuccess) return e;
 
     constexpr int DVT = DK < 64 ? DK : 64;
-    ChainBwdIO cio{a.v, a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0,
-                   a.B, a.T, a.H, a.DV, nch};
+    ChainBwdIO cio{a.v, BS ? a.b : a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0};
+    cio.dwp = dwp;
+    cio.npw = a.DV / 16;
+    cio.B = a.B;
+    cio.T = a.T;
+    cio.H = a.H;
+    cio.DV = a.DV;
+    cio.nch = nch;
     cio.var = vt;
     cio.ring = ring;
-    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0, VAR>), dim3((BH + 7) / 8 * 8 * (a.DV / DVT)),
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, (PRO & 2) != 0, VAR, BS>), dim3((BH + 7) / 8 * 8 * (a.DV / DVT)),
                        dim3(bwd_chain_threads<DK>()), 0, st, cio);
     // per-chunk kernels: b*h*chunks workgroups, or h * the chunk bound of a packed batch (the ones
     // past the true chunk count leave at once)
@@ -1298,12 +1354,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
     xio.var = vt;
     xio.ring = ring;
     hipLaunchKernelGGL((bwd_contract_kernel<DK, VAR>), dim3((unsigned)items), dim3(256), 0, st, xio);
-    KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, a.dO, dDp, Dl, S_save, G_save, dPm, dAm, a.dq, a.dk, a.dalpha, a.db,
-              a.B, a.T, a.H, nch};
+    KeyIO kio{a.q, a.k, a.alpha, a.b, rnq, rnk, a.dO, dDp, Dl, S_save, G_save, dPm, dAm, a.dq, a.dk, a.dalpha, a.db};
+    kio.dap = dap;
+    kio.dbp = dbp;
+    kio.B = a.B;
+    kio.T = a.T;
+    kio.H = a.H;
+    kio.nch = nch;
     kio.var = vt;
     kio.ring = ring;
-    hipLaunchKernelGGL((bwd_key_kernel<DK, PRO, VAR>), dim3((unsigned)((items + 7) / 8 * 8 * (DK / 32))), dim3(256), 0,
-                       st, kio);
+    hipLaunchKernelGGL((bwd_key_kernel<DK, PRO, VAR, AS, BS>), dim3((unsigned)((items + 7) / 8 * 8 * (DK / 32))),
+                       dim3(256), 0, st, kio);
     if constexpr ((PRO & 1) != 0) {  // dq, dk through the L2 norm
         const long rows = (VAR ? 1l : (long)a.B) * a.T * a.H;
         constexpr int RPB = 256 / (DK / 4);
@@ -1316,10 +1377,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, hi
 
 }  // namespace
 
-// Extra workspace for scalar gates: the repeated gates (bf16) and the per-channel gradients
-// (fp32); for the L2 norm: the reciprocal row norms of q and k.
+// Extra workspace for scalar gates: the per-row partial sums of their gradients (fp32: DK / 32
+// per row for alpha and for b, DV / 16 for the w side of a scalar beta); for the L2 norm: the
+// reciprocal row norms of q and k.
 struct ScalarLayout {
-    size_t alpha, b, w, dalpha, db, dw, rnq, rnk, total;
+    size_t dap, dbp, dwp, rnq, rnk, total;
 };
 
 ScalarLayout scalar_layout(size_t base, size_t rows, int DK, int DV, uint32_t flags) {
@@ -1327,18 +1389,12 @@ ScalarLayout scalar_layout(size_t base, size_t rows, int DK, int DV, uint32_t fl
     const bool as = (flags & 1u) != 0, bs = (flags & 2u) != 0;
     ScalarLayout L{};
     size_t o = base;
-    L.alpha = o;
-    o += as ? up(rows * DK * 2) : 0;
-    L.b = o;
-    o += bs ? up(rows * DK * 2) : 0;
-    L.w = o;
-    o += bs ? up(rows * DV * 2) : 0;
-    L.dalpha = o;
-    o += as ? up(rows * DK * 4) : 0;
-    L.db = o;
-    o += bs ? up(rows * DK * 4) : 0;
-    L.dw = o;
-    o += bs ? up(rows * DV * 4) : 0;
+    L.dap = o;
+    o += as ? up(rows * (DK / 32) * 4) : 0;
+    L.dbp = o;
+    o += bs ? up(rows * (DK / 32) * 4) : 0;
+    L.dwp = o;
+    o += bs ? up(rows * (DV / 16) * 4) : 0;
     const bool l2n = (flags & 4u) != 0;  // the row norms of q and k
     L.rnq = o;
     o += l2n ? up(rows * 4) : 0;
@@ -1377,7 +1433,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     const size_t need = var ? bwd_varlen_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags)
                             : bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags);
     if (!a.workspace || a.workspace_bytes < need) return hipErrorInvalidValue;
-    BwdArgs g = a;  // the general-gate call
+    const BwdArgs& g = a;
     const bool as = (a.flags & 1u) != 0, bs = (a.flags & 2u) != 0, l2n = (a.flags & 4u) != 0;
     const long rows = (var ? 1l : (long)a.B) * a.T * a.H;  // token rows
     const size_t base = var ? bwd_layout_var(a.B, a.T, a.H, a.DK, a.DV).total : bwd_layout(a.B, a.T, a.H, a.DK, a.DV).total;
@@ -1398,39 +1454,29 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
         else if (a.DK == 64) norms(std::integral_constant<int, 64>());
         else norms(std::integral_constant<int, 128>());
     }
-    if (as || bs) {
-        auto repeat = [&](const void* in, size_t off, int D) {
-            const long n = rows * (D / 8);
-            hipLaunchKernelGGL(repeat_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                               static_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(ws + off), rows, D);
-            return static_cast<const void*>(ws + off);
-        };
-        if (as) {
-            g.alpha = repeat(a.alpha, L.alpha, a.DK);
-            g.dalpha = reinterpret_cast<float*>(ws + L.dalpha);
+    float* dap = as ? reinterpret_cast<float*>(ws + L.dap) : nullptr;
+    float* dbp = bs ? reinterpret_cast<float*>(ws + L.dbp) : nullptr;
+    float* dwp = bs ? reinterpret_cast<float*>(ws + L.dwp) : nullptr;
+    auto gates = [&](auto dk, auto pro, auto vr) -> hipError_t {
+        constexpr int D = decltype(dk)::value, PRO = decltype(pro)::value;
+        constexpr bool V = decltype(vr)::value;
+        switch (a.flags & 3u) {
+            case 0: return launch_bwd_t<D, PRO, V, false, false>(g, rnq, rnk, dap, dbp, dwp, s);
+            case 1: return launch_bwd_t<D, PRO, V, true, false>(g, rnq, rnk, dap, dbp, dwp, s);
+            case 2: return launch_bwd_t<D, PRO, V, false, true>(g, rnq, rnk, dap, dbp, dwp, s);
+            default: return launch_bwd_t<D, PRO, V, true, true>(g, rnq, rnk, dap, dbp, dwp, s);
         }
-        if (bs) {
-            g.b = repeat(a.b, L.b, a.DK);
-            g.w = repeat(a.b, L.w, a.DV);
-            g.db = reinterpret_cast<float*>(ws + L.db);
-            g.dw = reinterpret_cast<float*>(ws + L.dw);
-        }
-        g.flags &= ~3u;
-    }
+    };
     auto go = [&](auto pro) -> hipError_t {
-        constexpr int PRO = decltype(pro)::value;
-        if (var) {
+        auto with = [&](auto vr) -> hipError_t {
             switch (a.DK) {
-                case 32: return launch_bwd_t<32, PRO, true>(g, rnq, rnk, s);
-                case 64: return launch_bwd_t<64, PRO, true>(g, rnq, rnk, s);
-                default: return launch_bwd_t<128, PRO, true>(g, rnq, rnk, s);
+                case 32: return gates(std::integral_constant<int, 32>(), pro, vr);
+                case 64: return gates(std::integral_constant<int, 64>(), pro, vr);
+                case 128: return gates(std::integral_constant<int, 128>(), pro, vr);
+                default: return hipErrorNotSupported;
             }
-        }
-        switch (a.DK) {
-            case 32: return launch_bwd_t<32, PRO, false>(g, rnq, rnk, s);
-            case 64: return launch_bwd_t<64, PRO, false>(g, rnq, rnk, s);
-            default: return launch_bwd_t<128, PRO, false>(g, rnq, rnk, s);
-        }
+        };
+        return var ? with(std::true_type()) : with(std::false_type());
     };
     hipError_t e;
     switch ((a.flags >> 2) & 3u) {
@@ -1440,15 +1486,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
         default: e = go(std::integral_constant<int, 3>()); break;
     }
     if (e != hipSuccess || !(as || bs)) return e;
-    auto sums = [&](auto dk) {
-        constexpr int D = decltype(dk)::value, RPB = 256 / (D / 4);
-        const dim3 sg((unsigned)((rows + RPB - 1) / RPB));
-        if (as) hipLaunchKernelGGL(row_sums<D>, sg, dim3(256), 0, s, g.dalpha, nullptr, a.dalpha, rows);
-        if (bs) hipLaunchKernelGGL(row_sums<D>, sg, dim3(256), 0, s, g.db, g.dw, a.db, rows);
-    };
-    if (a.DK == 32) sums(std::integral_constant<int, 32>());
-    else if (a.DK == 64) sums(std::integral_constant<int, 64>());
-    else sums(std::integral_constant<int, 128>());
+    hipLaunchKernelGGL(scalar_gate_sums, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, dap, a.DK / 32, dbp,
+                       a.DK / 32, dwp, a.DV / 16, a.dalpha, a.db, rows);
     return hipGetLastError();
 }
 

@@ -115,13 +115,13 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
     }
 }
 
-template <int DK, int PRO>
+template <int DK, int PRO, bool AS, bool BS>
 hipError_t launch_states_t(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                            hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
     const int nch = (a.T + CH - 1) / CH;
-    hipLaunchKernelGGL((prep_kernel<DK, true, false, false, PRO>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k,
+    hipLaunchKernelGGL((prep_kernel<DK, true, AS, BS, PRO>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k,
                        a.alpha, a.b, a.B, a.T, a.H, 0, nch, blobs, VarTab{});
     ChainIO io{a.v, a.w, nullptr, blobs, nch, 0, nch, nch, 1, a.B, a.T, a.H, a.DV,
                a.S0, (long)DK * a.DV, 0, a.DV, nullptr, 0, 0, a.DV, 0};
@@ -129,22 +129,33 @@ hipError_t launch_states_t(const ChunkArgs& a, char* blobs, uint16_t* S_save, ui
     io.save_nch = nch;
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
-    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, true, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
                        dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
     return hipGetLastError();
+}
+
+template <int DK, int PRO>
+hipError_t launch_states_gates(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save,
+                               uint16_t* Dl_save, hipStream_t s) {
+    switch (a.flags & 3u) {
+        case 0: return launch_states_t<DK, PRO, false, false>(a, blobs, S_save, Dp_save, Dl_save, s);
+        case 1: return launch_states_t<DK, PRO, true, false>(a, blobs, S_save, Dp_save, Dl_save, s);
+        case 2: return launch_states_t<DK, PRO, false, true>(a, blobs, S_save, Dp_save, Dl_save, s);
+        default: return launch_states_t<DK, PRO, true, true>(a, blobs, S_save, Dp_save, Dl_save, s);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_split_states(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                                hipStream_t s) {
-    if (!a.bf16 || (a.flags & ~12u) != 0u || !split_supported(a.T, a.H, a.DK, a.DV, true)) return hipErrorNotSupported;
+    if (!a.bf16 || (a.flags & ~15u) != 0u || !split_supported(a.T, a.H, a.DK, a.DV, true)) return hipErrorNotSupported;
     auto go = [&](auto pro) -> hipError_t {
         constexpr int PRO = decltype(pro)::value;
         switch (a.DK) {
-            case 32: return launch_states_t<32, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
-            case 64: return launch_states_t<64, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
-            case 128: return launch_states_t<128, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            case 32: return launch_states_gates<32, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            case 64: return launch_states_gates<64, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
+            case 128: return launch_states_gates<128, PRO>(a, blobs, S_save, Dp_save, Dl_save, s);
             default: return hipErrorNotSupported;
         }
     };

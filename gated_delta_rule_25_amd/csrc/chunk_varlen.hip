@@ -136,8 +136,8 @@ hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
 // The backward's forward pass over a packed batch: the sequence table (at `table`), prep into
 // `blobs` ([h][chunk of the batch], `ring` slots per head) and the state-only chain with saves:
 // the start state of every chunk ([h][chunk of the batch][DK][DV]) and the rows of D' and Delta
-// (fp16, packed rows). bf16, general gates, the prologue flags PRO.
-template <int DK, int PRO>
+// (fp16, packed rows). bf16, scalar gate forms AS / BS, the prologue flags PRO.
+template <int DK, int PRO, bool AS, bool BS>
 hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, long ring, uint16_t* S_save,
                                   uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t st) {
     constexpr int DVT = DK < 64 ? DK : 64;
@@ -151,7 +151,7 @@ hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, 
     hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, N, a.T, const_cast<int*>(vt.coff),
                        const_cast<int*>(vt.start), const_cast<int*>(vt.len), const_cast<int*>(vt.perm));
     if (ring > 0)
-        hipLaunchKernelGGL((prep_kernel<DK, true, false, false, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0,
+        hipLaunchKernelGGL((prep_kernel<DK, true, AS, BS, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0,
                            st, a.q, a.k, a.alpha, a.b, 1, a.T, a.H, 0, (int)ring, blobs, vt);
     const long ld = DK;
     ChainIO io{a.v, a.w, nullptr, blobs, (int)ring, 0, 0, 0, 1, N, a.T, a.H, a.DV,
@@ -161,9 +161,20 @@ hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, 
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
     const int BH = N * a.H, BHp = (BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, false, true, true, (PRO & 2) != 0, true>),
+    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, true, true, (PRO & 2) != 0, true>),
                        dim3(BHp * (a.DV / DVT)), dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
     return hipGetLastError();
+}
+
+template <int DK, int PRO>
+hipError_t launch_varlen_states_gates(const ChunkArgs& a, char* table, char* blobs, long ring, uint16_t* S_save,
+                                      uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t s) {
+    switch (a.flags & 3u) {
+        case 0: return launch_varlen_states_t<DK, PRO, false, false>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+        case 1: return launch_varlen_states_t<DK, PRO, true, false>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+        case 2: return launch_varlen_states_t<DK, PRO, false, true>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+        default: return launch_varlen_states_t<DK, PRO, true, true>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+    }
 }
 
 template <int DK, bool BF16, int PRO>
@@ -201,14 +212,14 @@ size_t varlen_workspace_bytes(int n, int T, int H, int DK, int DV, bool bf16) {
 
 hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, long ring, uint16_t* S_save,
                                 uint16_t* Dp_save, uint16_t* Dl_save, hipStream_t s) {
-    if (!a.bf16 || (a.flags & ~12u) != 0u || !a.cu_seqlens || !split_supported(a.T, a.H, a.DK, a.DV, true))
+    if (!a.bf16 || (a.flags & ~15u) != 0u || !a.cu_seqlens || !split_supported(a.T, a.H, a.DK, a.DV, true))
         return hipErrorNotSupported;
     auto go = [&](auto pro) -> hipError_t {
         constexpr int PRO = decltype(pro)::value;
         switch (a.DK) {
-            case 32: return launch_varlen_states_t<32, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
-            case 64: return launch_varlen_states_t<64, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
-            case 128: return launch_varlen_states_t<128, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            case 32: return launch_varlen_states_gates<32, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            case 64: return launch_varlen_states_gates<64, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
+            case 128: return launch_varlen_states_gates<128, PRO>(a, table, blobs, ring, S_save, Dp_save, Dl_save, s);
             default: return hipErrorNotSupported;
         }
     };

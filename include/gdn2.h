@@ -222,7 +222,8 @@ gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const 
  *            alpha [B, T, H] and dalpha [B, T, H] = dL/dalpha; beta passed as b [B, T, H] with
  *            w == NULL, and db [B, T, H] = dL/dbeta (the gradients through b and w summed), dw
  *            == NULL. A scalar gate is the general gate with the scalar in every channel, so its
- *            gradient is the sum of the per-channel gradients; the call computes it that way.
+ *            gradient is the sum of the per-channel gradients; the kernels read the scalars
+ *            themselves and sum those gradients over the channels of each row.
  *
  *   prologue flags (GDN2_QK_L2NORM, GDN2_GATE_LOGITS): q, k, alpha, b, w are the raw inputs the
  *            forward takes with the same flags, and dq, dk, dalpha, db, dw are the gradients
@@ -237,8 +238,9 @@ gdn2_status gdn2_decode_step(const void *q, const void *k, const void *v, const 
  * The workspace (required when T > 0, 256-byte aligned, at least
  * gdn2_chunk_bwd_workspace_bytes for the same gate_flags) holds the operand blocks, the state and
  * its gradient at every chunk boundary and the per-chunk intermediate products (and, for scalar
- * gates, the gates repeated over the channels and their per-channel gradients; for the L2 norm,
- * the row norms of q and k); its contents are scratch. No output may
+ * gates, per token row the partial sums of their gradients over groups of channels, added up
+ * by the call's last kernel; for the L2 norm, the row norms of q and k); its contents are
+ * scratch. No output may
  * overlap an input, another output or the workspace (GDN2_ERR_ALIAS). Other errors, ownership
  * and stream semantics as for gdn2_chunk_fwd.
  */
