@@ -11,13 +11,15 @@
 // alpha_t and b_t per-token scalars (they act on the slot axis), w_t on the value axis, r the
 // sparse read weights.
 //
-// Addressing (sdm_address_kernel), one wavefront per query: the two halves of the query are
-// scored against their sub-key tables (fp32 dot products in channel order); each half's n scores
-// are sorted by a bitonic network in LDS (score descending, equal scores: lower index first) and
-// the first m kept. A pair of ranks (i, j) can be among the m best pair sums only if
-// (i + 1)(j + 1) <= m (every pair of lower ranks in both halves precedes it), so only those pairs
-// (280 for m = 64) are formed, sorted the same way (equal sums: lower slot first), and the first
-// m are the slots i_sub * n + j_sub; their weights are the softmax of the sums.
+// Addressing (sdm_address_kernel): the two halves of each query are scored against their sub-key
+// tables on the matrix cores (exact products, fp32 accumulation), 16 queries of a head at a time;
+// then one wavefront per query selects: each half's best 64
+// (score descending, equal scores: lower index first) come from bitonic sorts over the lanes of
+// each 64-score column and merges of the sorted columns, all in registers. A pair of ranks (i, j)
+// can be among the m best pair sums only if (i + 1)(j + 1) <= m (every pair of lower ranks in both
+// halves precedes it), so only those pairs (280 for m = 64) are formed, reduced the same way
+// (equal sums: lower slot first), and the first m are the slots i_sub * n + j_sub; their weights
+// are the softmax of the sums.
 //
 // Update (sdm_fwd_kernel), one wavefront per (batch, head, 64 value columns), a lane per column:
 // value columns do not interact, so each lane gathers its column of the W write slots and the R
@@ -33,118 +35,254 @@ namespace gdn2 {
 namespace {
 
 constexpr int kMaxSlots = 64;     // W, R and m at most one wavefront wide
-constexpr int kCand = 512;        // candidate pairs (at most 280 for m = 64), padded for the sort
 constexpr float kFoldBelow = 0x1p-60f;
 
-// Total order of (score, index) keys: higher score first, equal scores lower index first.
-__device__ __forceinline__ bool before(float sa, int ia, float sb, int ib) {
-    return sa > sb || (sa == sb && ia < ib);
+// Keys of the selection: (score, index) as one 64-bit integer whose ascending order is score
+// descending, then index ascending (the total order of the oracle's selection): the score's bits
+// mapped to an order-preserving unsigned integer and inverted, above the index.
+__device__ __forceinline__ uint64_t sel_key(float s, int i) {
+    const uint32_t u = __float_as_uint(s + 0.f);  // -0 counts as +0
+    const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)(~asc) << 32) | (uint32_t)i;
+}
+__device__ __forceinline__ float key_score(uint64_t k) {
+    const uint32_t asc = ~(uint32_t)(k >> 32);
+    return __uint_as_float((asc & 0x80000000u) ? (asc & 0x7fffffffu) : ~asc);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)(uint32_t)k; }
+constexpr uint64_t kNoKey = ~0ull;  // sorts after every real key
+
+// x from lane (lane ^ j), j a power of two below 64 (a constant once the callers' loops unroll),
+// without the LDS crossbar: DPP within rows of 16 lanes, the gfx950 permlane swaps across rows.
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t x, int j, int lane) {
+    switch (j) {
+        case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+        case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+        case 4: {
+            const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x104, 0xF, 0xF, true);  // row_shl:4
+            const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+            return (lane & 4) ? dn : up;
+        }
+        case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);   // row_ror:8
+        case 15: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, true);  // row_mirror
+        case 16: {  // odd rows of the first copy trade places with even rows of the second
+            const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+            return (lane & 16) ? r[0] : r[1];
+        }
+        case 32: {  // upper half of the first copy trades places with lower half of the second
+            const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+            return (lane & 32) ? r[0] : r[1];
+        }
+        default: return (uint32_t)__shfl_xor((int)x, j);
+    }
+}
+__device__ __forceinline__ uint64_t xor_lanes64(uint64_t x, int j, int lane) {
+    const uint32_t lo = xor_lanes((uint32_t)x, j, lane), hi = xor_lanes((uint32_t)(x >> 32), j, lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Ascending sort of NC columns of 64 keys (one key per lane and column) by a bitonic network over
+// the lanes, the columns in lockstep so that their exchanges overlap. At each stage a lane keeps
+// the smaller of its key and its partner's where `keep_min`, else the larger.
+template <int NC>
+__device__ __forceinline__ void sort64(uint64_t (&c)[NC], int lane) {
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const bool keep_min = ((lane & j) == 0) == ((lane & k) == 0);
+            uint64_t p[NC];
+#pragma unroll
+            for (int i = 0; i < NC; ++i) p[i] = xor_lanes64(c[i], j, lane);
+#pragma unroll
+            for (int i = 0; i < NC; ++i) c[i] = ((p[i] < c[i]) == keep_min) ? p[i] : c[i];
+        }
 }
 
-// Sorts P keys held in LDS (ks, ki) into the order `before` defines, with a bitonic network run
-// by the workgroup's single wavefront. P is a power of two.
-template <int P>
-__device__ __forceinline__ void wave_sort(float* ks, int* ki, int lane) {
-#pragma unroll 1
-    for (int k = 2; k <= P; k <<= 1) {
-#pragma unroll 1
-        for (int j = k >> 1; j > 0; j >>= 1) {
+// a[i] := the 64 smallest keys of the ascending 64-key lists a[i] and b[i], ascending: the lanewise
+// minimum of a list and the other reversed is a bitonic sequence holding them, which one
+// half-cleaner cascade sorts.
+template <int NP>
+__device__ __forceinline__ void merge64(uint64_t (&a)[NP], const uint64_t (&b)[NP], int lane) {
 #pragma unroll
-            for (int t = lane; t < P / 2; t += kWave) {
-                const int i = (t / j) * 2 * j + (t % j), l = i + j;
-                const float si = ks[i], sl = ks[l];
-                const int ii = ki[i], il = ki[l];
-                // ascending runs (in `before` order) where bit k of i is clear
-                const bool swap = ((i & k) == 0) ? before(sl, il, si, ii) : before(si, ii, sl, il);
-                if (swap) {
-                    ks[i] = sl;
-                    ks[l] = si;
-                    ki[i] = il;
-                    ki[l] = ii;
-                }
-            }
-            __syncthreads();
-        }
+    for (int i = 0; i < NP; ++i) {
+        const uint64_t rev = xor_lanes64(xor_lanes64(xor_lanes64(b[i], 15, lane), 16, lane), 32, lane);  // lane 63 - l
+        a[i] = rev < a[i] ? rev : a[i];
+    }
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) {
+        const bool keep_min = (lane & j) == 0;
+        uint64_t p[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) p[i] = xor_lanes64(a[i], j, lane);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) a[i] = ((p[i] < a[i]) == keep_min) ? p[i] : a[i];
     }
 }
 
+// out[g] := the 64 smallest keys of the E sorted columns c[g][.], ascending (lane l holds rank l),
+// by a tree of pairwise merges, the G groups in lockstep.
+template <int G, int E>
+__device__ __forceinline__ void best64(const uint64_t (&c)[G][E], uint64_t (&out)[G], int lane) {
+    if constexpr (E == 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) out[g] = c[g][0];
+    } else {
+        constexpr int P = E / 2;
+        uint64_t a[G * P], b[G * P];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int i = 0; i < P; ++i) a[g * P + i] = c[g][2 * i], b[g * P + i] = c[g][2 * i + 1];
+        merge64<G * P>(a, b, lane);
+        uint64_t n[G][E - P];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int i = 0; i < P; ++i) n[g][i] = a[g * P + i];
+            if constexpr (E % 2 == 1) n[g][P] = c[g][E - 1];
+        }
+        best64<G, E - P>(n, out, lane);
+    }
+}
+
+// Operand fragments of the score products on the matrix cores: lane (r, g) of a fragment holds
+// the 8 consecutive channels 32 ks + 8 g .. + 7 of row r (a sub-key, or a query). bf16 runs as one
+// 16x16x32 product; fp32 as eight 16x16x4 fp32 passes, pass i contracting slot i of every lane
+// group. Both multiply exactly and accumulate in fp32.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <bool BF16>
+struct ScoreFrag;
+template <>
+struct ScoreFrag<true> {
+    bf16x8 v;
+    __device__ void load(const void* base, long i) {
+        v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i));
+    }
+    __device__ void zero() { v = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u)); }
+    __device__ static void mma(f32x4& c, const ScoreFrag& a, const ScoreFrag& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+    }
+};
+template <>
+struct ScoreFrag<false> {
+    float v[8];
+    __device__ void load(const void* base, long i) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+        const float4 lo = p[0], hi = p[1];
+        v[0] = lo.x, v[1] = lo.y, v[2] = lo.z, v[3] = lo.w, v[4] = hi.x, v[5] = hi.y, v[6] = hi.z, v[7] = hi.w;
+    }
+    __device__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+    __device__ static void mma(f32x4& c, const ScoreFrag& a, const ScoreFrag& b) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], c, 0, 0, 0);
+    }
+};
+
+// A workgroup of four wavefronts takes 16 queries of one head at a time (grid-stride over
+// (16-query tile, head)). The sub-key scores of both halves are 16 x 16 (sub-keys x queries) matrix
+// core products into LDS, so each sub-key table is read once per tile, not once per query. Then
+// each wavefront selects for 4 of the queries: lane l takes sub-keys l, l + 64, ... of each half;
+// the best m of each half (ranks in lanes 0 .. m-1) come from the sorted columns and their merges;
+// the candidate pairs, listed once per workgroup in LDS (slot c holds ranks (i, j)), are scored
+// from the two rank lists by lane shuffles and reduced the same way.
+constexpr int kCandCols = 5;  // 320 candidate slots: at most 280 pairs for m = 64
+constexpr int kAddrQ = 16;    // queries per tile
+
 template <int HALF, int NSUB, bool BF16>
-__global__ void __launch_bounds__(64) sdm_address_kernel(const void* __restrict__ x, const void* __restrict__ C1,
-                                                         const void* __restrict__ C2, long queries, int H, int m,
-                                                         int* __restrict__ idx, float* __restrict__ wt) {
+__global__ void __launch_bounds__(256) sdm_address_kernel(const void* __restrict__ x, const void* __restrict__ C1,
+                                                          const void* __restrict__ C2, long rows, int H, int m,
+                                                          int* __restrict__ idx, float* __restrict__ wt) {
     constexpr int DK = 2 * HALF;
-    __shared__ float xs[DK];
-    __shared__ float ks[NSUB > kCand ? NSUB : kCand];
-    __shared__ int ki[NSUB > kCand ? NSUB : kCand];
-    __shared__ float top_s[2][kMaxSlots];
-    __shared__ int top_i[2][kMaxSlots];
-    __shared__ int cstart[kMaxSlots + 1];
-    const int lane = threadIdx.x;
+    constexpr int E = NSUB / 64;   // score columns per lane
+    constexpr int KS = HALF / 32;  // 32-channel steps per half
+    constexpr int LD = NSUB + 4;   // score row stride: rows start 4 banks apart
+    static_assert(HALF % 32 == 0 && NSUB % 64 == 0, "tile shape");
+    __shared__ float sc[2][kAddrQ][LD];
+    __shared__ uint16_t cand[kCandCols * 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    // candidate pairs (i, j) with (i + 1)(j + 1) <= m: rank i contributes m / (i + 1) of them
+    for (int c = tid; c < kCandCols * 64; c += 256) cand[c] = 0xffffu;
+    __syncthreads();
+    if (tid < m) {
+        int c0 = 0;
+        for (int i = 0; i < tid; ++i) c0 += m / (i + 1);
+        const int cnt = m / (tid + 1);
+        for (int j = 0; j < cnt; ++j) cand[c0 + j] = (uint16_t)((tid << 8) | j);
+    }
+    const long work = (rows + kAddrQ - 1) / kAddrQ * H;
 #pragma unroll 1
-    for (long qy = blockIdx.x; qy < queries; qy += gridDim.x) {
-        const int h = (int)(qy % H);
-        for (int d = lane; d < DK; d += kWave) xs[d] = load_one<BF16>(x, qy * DK + d);
-        __syncthreads();
-#pragma unroll 1
+    for (long wi = blockIdx.x; wi < work; wi += gridDim.x) {
+        const int h = (int)(wi % H);
+        const long r0 = wi / H * kAddrQ;
+        // scores: sc[half][q][p] = <x_q half, C_half[h][p]>, fp32 accumulation
+        const long rq = r0 + r16;
+#pragma unroll
         for (int half = 0; half < 2; ++half) {
             const void* C = half ? C2 : C1;
-            const long row0 = (long)h * NSUB;
-            for (int p = lane; p < NSUB; p += kWave) {  // score of sub-key p: fp32, channel order
-                float s = 0.f;
+            ScoreFrag<BF16> xf[KS];
 #pragma unroll
-                for (int d0 = 0; d0 < HALF; d0 += 8) {
-                    float c[8];
-                    load_vec<8, BF16>(C, (row0 + p) * HALF + d0, c);
+            for (int ks = 0; ks < KS; ++ks) {
+                if (rq < rows)
+                    xf[ks].load(x, (rq * H + h) * DK + half * HALF + 32 * ks + 8 * g);
+                else
+                    xf[ks].zero();
+            }
+#pragma unroll 2
+            for (int pb = wv; pb < NSUB / 16; pb += 4) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) s = fmaf(c[u], xs[half * HALF + d0 + u], s);
+                for (int ks = 0; ks < KS; ++ks) {
+                    ScoreFrag<BF16> cf;
+                    cf.load(C, ((long)h * NSUB + pb * 16 + r16) * HALF + 32 * ks + 8 * g);
+                    ScoreFrag<BF16>::mma(acc, cf, xf[ks]);
                 }
-                ks[p] = s;
-                ki[p] = p;
-            }
-            __syncthreads();
-            wave_sort<NSUB>(ks, ki, lane);
-            if (lane < m) {
-                top_s[half][lane] = ks[lane];
-                top_i[half][lane] = ki[lane];
-            }
-            __syncthreads();
-        }
-        // candidate pairs (i, j) with (i + 1)(j + 1) <= m: row i holds m / (i + 1) of them
-        if (lane == 0) {
-            int acc = 0;
-            for (int i = 0; i < m; ++i) {
-                cstart[i] = acc;
-                acc += m / (i + 1);
-            }
-            cstart[m] = acc;
-        }
-        for (int c = lane; c < kCand; c += kWave) {  // padding sorts last
-            ks[c] = -__builtin_inff();
-            ki[c] = 0x7fffffff;
-        }
-        __syncthreads();
-        if (lane < m) {
-            const int c0 = cstart[lane], cnt = m / (lane + 1);
-            const float a = top_s[0][lane];
-            const int ia = top_i[0][lane];
-            for (int j = 0; j < cnt; ++j) {
-                ks[c0 + j] = a + top_s[1][j];
-                ki[c0 + j] = ia * NSUB + top_i[1][j];
+                // acc[i]: sub-key pb * 16 + 4 g + i against query r16
+                *reinterpret_cast<float4*>(&sc[half][r16][pb * 16 + 4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
         }
         __syncthreads();
-        wave_sort<kCand>(ks, ki, lane);
-        // softmax of the m best sums (the first is the largest)
-        const float best = ks[0];
-        const float e = lane < m ? expf(ks[lane] - best) : 0.f;
-        float sum = e;
+#pragma unroll 1
+        for (int q = wv; q < kAddrQ && r0 + q < rows; q += 4) {
+            const long qy = (r0 + q) * H + h;
+            uint64_t col[2][E], top[2];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-        if (lane < m) {
-            idx[qy * m + lane] = ki[lane];
-            wt[qy * m + lane] = e / sum;
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int e = 0; e < E; ++e) col[half][e] = sel_key(sc[half][q][64 * e + lane], 64 * e + lane);
+            sort64<2 * E>(reinterpret_cast<uint64_t(&)[2 * E]>(col), lane);
+            best64<2, E>(col, top, lane);
+            // the candidate pairs' sums and slots, then the best m of them
+            const float s1 = key_score(top[0]), s2 = key_score(top[1]);
+            const int i1 = key_index(top[0]), i2 = key_index(top[1]);
+            uint64_t cc[1][kCandCols], best[1];
+#pragma unroll
+            for (int u = 0; u < kCandCols; ++u) {
+                const uint32_t ent = cand[64 * u + lane];
+                const int ri = ent == 0xffffu ? 0 : (int)(ent >> 8), rj = ent == 0xffffu ? 0 : (int)(ent & 255u);
+                const float a = __shfl(s1, ri), bsc = __shfl(s2, rj);
+                const int slot = __shfl(i1, ri) * NSUB + __shfl(i2, rj);
+                cc[0][u] = ent == 0xffffu ? kNoKey : sel_key(a + bsc, slot);
+            }
+            sort64<kCandCols>(cc[0], lane);
+            best64<1, kCandCols>(cc, best, lane);
+            // softmax of the m best sums (rank 0 is the largest)
+            const float sb = key_score(best[0]);
+            const float top0 = __shfl(sb, 0);
+            const float ex = lane < m ? expf(sb - top0) : 0.f;
+            float sum = ex;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            if (lane < m) {
+                idx[qy * m + lane] = key_index(best[0]);
+                wt[qy * m + lane] = ex / sum;
+            }
         }
-        __syncthreads();  // LDS is reused by the next query
+        __syncthreads();  // sc is rewritten by the next tile
     }
 }
 
@@ -281,12 +419,12 @@ __global__ void __launch_bounds__(256) sdm_fold_kernel(float* M, double* stamp, 
 }
 
 template <int HALF, bool BF16>
-hipError_t launch_address_n(const SdmAddressArgs& a, hipStream_t st, int grid) {
+hipError_t launch_address_n(const SdmAddressArgs& a, hipStream_t st, int grid, long rows) {
     switch (a.n) {
-        case 64: hipLaunchKernelGGL((sdm_address_kernel<HALF, 64, BF16>), dim3(grid), dim3(64), 0, st, a.x, a.C1, a.C2, a.queries, a.H, a.m, a.idx, a.wt); break;
-        case 128: hipLaunchKernelGGL((sdm_address_kernel<HALF, 128, BF16>), dim3(grid), dim3(64), 0, st, a.x, a.C1, a.C2, a.queries, a.H, a.m, a.idx, a.wt); break;
-        case 256: hipLaunchKernelGGL((sdm_address_kernel<HALF, 256, BF16>), dim3(grid), dim3(64), 0, st, a.x, a.C1, a.C2, a.queries, a.H, a.m, a.idx, a.wt); break;
-        case 512: hipLaunchKernelGGL((sdm_address_kernel<HALF, 512, BF16>), dim3(grid), dim3(64), 0, st, a.x, a.C1, a.C2, a.queries, a.H, a.m, a.idx, a.wt); break;
+        case 64: hipLaunchKernelGGL((sdm_address_kernel<HALF, 64, BF16>), dim3(grid), dim3(256), 0, st, a.x, a.C1, a.C2, rows, a.H, a.m, a.idx, a.wt); break;
+        case 128: hipLaunchKernelGGL((sdm_address_kernel<HALF, 128, BF16>), dim3(grid), dim3(256), 0, st, a.x, a.C1, a.C2, rows, a.H, a.m, a.idx, a.wt); break;
+        case 256: hipLaunchKernelGGL((sdm_address_kernel<HALF, 256, BF16>), dim3(grid), dim3(256), 0, st, a.x, a.C1, a.C2, rows, a.H, a.m, a.idx, a.wt); break;
+        case 512: hipLaunchKernelGGL((sdm_address_kernel<HALF, 512, BF16>), dim3(grid), dim3(256), 0, st, a.x, a.C1, a.C2, rows, a.H, a.m, a.idx, a.wt); break;
         default: return hipErrorNotSupported;
     }
     return hipGetLastError();
@@ -294,12 +432,13 @@ hipError_t launch_address_n(const SdmAddressArgs& a, hipStream_t st, int grid) {
 
 template <bool BF16>
 hipError_t launch_address_t(const SdmAddressArgs& a, hipStream_t st) {
-    const long want = a.queries;
-    const int grid = (int)(want < 256L * 64 ? want : 256L * 64);  // grid-stride beyond 64 waves per CU
+    const long rows = a.queries / a.H;
+    const long work = (rows + kAddrQ - 1) / kAddrQ * a.H;       // (16-query tile, head) pairs
+    const int grid = (int)(work < 256L * 32 ? work : 256L * 32);  // grid-stride beyond 32 per CU
     switch (a.dk) {
-        case 64: return launch_address_n<32, BF16>(a, st, grid);
-        case 128: return launch_address_n<64, BF16>(a, st, grid);
-        case 256: return launch_address_n<128, BF16>(a, st, grid);
+        case 64: return launch_address_n<32, BF16>(a, st, grid, rows);
+        case 128: return launch_address_n<64, BF16>(a, st, grid, rows);
+        case 256: return launch_address_n<128, BF16>(a, st, grid, rows);
         default: return hipErrorNotSupported;
     }
 }

@@ -375,7 +375,8 @@ const char *gdn2_status_str(gdn2_status s);
 
 /* Product-key addressing. For each of rows*H queries x [rows, H, d_k] (bf16 or fp32, rows = B*T
  * tokens): the first and second half of x are scored against the head's sub-key tables
- * C1, C2 [H, n, d_k/2] (same dtype; fp32 dot products in channel order); the m best sub-keys of
+ * C1, C2 [H, n, d_k/2] (same dtype; exact products summed in fp32, in an order the matrix cores
+ * fix, so near-equal scores may rank either way within that rounding); the m best sub-keys of
  * each half are kept and the m best of their pair sums give the slots i*n + j (of N = n*n) with
  * the softmax of the sums as weights, best first (equal scores or sums: lower index first).
  * Writes idx [rows, H, m] int32 and weight [rows, H, m] fp32. Use it with x = k for the write
