@@ -21,10 +21,11 @@
 // (equal sums: lower slot first), and the first m are the slots i_sub * n + j_sub; their weights
 // are the softmax of the sums.
 //
-// Update (sdm_fwd_kernel), one wavefront per (batch, head, 64 value columns), a lane per column:
+// Update (sdm_fwd_kernel), one workgroup per (batch, head, 64 value columns), a lane per column:
 // value columns do not interact, so each lane gathers its column of the W write slots and the R
-// read slots in one round trip, forms e = a^T M, and writes the W updated entries back; a read
-// slot that the token also writes takes the written value from registers. The decay is a scalar
+// read slots in one round trip (the slots split over four wavefronts), forms e = a^T M, and
+// writes the W updated entries back; a read slot that the token also writes takes the written
+// value. The decay is a scalar
 // on every slot, applied lazily: each slot carries the running sum of log alpha at its last
 // write (fp64), and its value now is the stored one times exp(L - stamp). So a token reads and
 // writes only its W + R slots and their stamps, never the whole memory.
@@ -314,19 +315,28 @@ __device__ __forceinline__ float lane_f(float x, int j) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
 }
 
-// One wavefront per (batch, head, 64 value columns), a lane per column. The memory is kept in
-// plain units per slot as of that slot's last write; stamp[s] holds the running sum of log alpha
-// (fp64) at that write, and the slot's value now is M[s] * exp(L - stamp[s]). A token therefore
-// touches only its W + R slots. Each wavefront keeps its own stamps and L (the column tiles of a
-// head run independently), so no wavefront reads another's bookkeeping.
+// One workgroup per (batch, head, 64 value columns), a lane per column; its four wavefronts each
+// own 16 positions of the token's write list and 16 of its read list. The memory is kept in plain
+// units per slot as of that slot's last write; stamp[s] holds the running sum of log alpha (fp64)
+// at that write, and the slot's value now is M[s] * exp(L - stamp[s]). A token therefore touches
+// only its W + R slots. Per token: each wavefront gathers its rows and stamps and forms its part
+// of e = a^T M; the parts meet in LDS (summed in wavefront order); each wavefront writes its
+// updated rows and forms its part of the read; a read slot that the token also writes is read
+// from the writer's new value (its own gathered copy is weighted 0). The barrier that closes a
+// token orders its row and stamp stores before every wavefront's next gathers. Each workgroup
+// keeps its own stamps and L (the column tiles of a head run independently).
+constexpr int kFwdWaves = 4;
+constexpr int kPart = kMaxSlots / kFwdWaves;  // list positions per wavefront
+
 template <bool BF16>
-__global__ void __launch_bounds__(64) sdm_fwd_kernel(const void* __restrict__ v, const void* __restrict__ alpha,
-                                                     const void* __restrict__ b, const void* __restrict__ w,
-                                                     const int* __restrict__ widx, const float* __restrict__ wwt,
-                                                     const int* __restrict__ ridx, const float* __restrict__ rwt,
-                                                     float* M, double* stamp, double* Lbuf, float* __restrict__ o,
-                                                     int T, int H, long N, int dv, int W, int R) {
-    const int lane = threadIdx.x;
+__global__ void __launch_bounds__(kFwdWaves * 64) sdm_fwd_kernel(
+    const void* __restrict__ v, const void* __restrict__ alpha, const void* __restrict__ b, const void* __restrict__ w,
+    const int* __restrict__ widx, const float* __restrict__ wwt, const int* __restrict__ ridx,
+    const float* __restrict__ rwt, float* M, double* stamp, double* Lbuf, float* __restrict__ o, int T, int H, long N,
+    int dv, int W, int R) {
+    __shared__ float ep[kFwdWaves][kWave], op[kFwdWaves][kWave], rmp[kFwdWaves][kWave];
+    __shared__ int ovp[kFwdWaves][kWave];
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int tiles = dv / kWave;
     const long bh = blockIdx.x / tiles;
     const int tile = (int)(blockIdx.x % tiles);
@@ -336,6 +346,8 @@ __global__ void __launch_bounds__(64) sdm_fwd_kernel(const void* __restrict__ v,
     float* Mb = M + bh * N * dv + c;
     double* Sb = stamp + (bh * tiles + tile) * N;
     double L = Lbuf[bh * tiles + tile];
+    const int j0 = wv * kPart;  // this wavefront's list positions j0 .. j0 + kPart - 1
+    const bool mine = lane >= j0 && lane < j0 + kPart;
     TokIn x = load_tok<BF16>(v, alpha, b, w, widx, wwt, ridx, rwt, (bb * T) * H + h, dv, c, W, R, lane);
 #pragma unroll 1
     for (int t = 0; t < T; ++t) {
@@ -343,57 +355,77 @@ __global__ void __launch_bounds__(64) sdm_fwd_kernel(const void* __restrict__ v,
         // alpha = 0 wipes the memory: a decay of e^-1e6, zero in any float, keeps L finite
         L += x.al > 0.f ? log((double)x.al) : -1e6;
         const bool wok = (unsigned)x.wi < (unsigned long)N, rok = (unsigned)x.ri < (unsigned long)N;
-        // read slots this token also writes take the written value (held in registers below);
-        // rmatch: the read weight that falls on this lane's write slot
-        bool ov = false;
-        float rmatch = 0.f;
+        const double sw = (mine && wok) ? Sb[x.wi] : L, sr = (mine && rok) ? Sb[x.ri] : L;
+        float mw[kPart], mr[kPart];
 #pragma unroll
-        for (int j = 0; j < kMaxSlots; ++j) {
-            const int wj = __builtin_amdgcn_readlane(x.wi, j), rj = __builtin_amdgcn_readlane(x.ri, j);
-            ov |= (j < W) && rok && wj == x.ri;
-            rmatch += ((j < R) && wok && rj == x.wi) ? lane_f(x.ra, j) : 0.f;
-        }
-        const bool rload = rok && !ov;
-        const double sw = wok ? Sb[x.wi] : L, sr = rload ? Sb[x.ri] : L;
-        float mw[kMaxSlots], mr[kMaxSlots];
-#pragma unroll
-        for (int j = 0; j < kMaxSlots; ++j) {
-            const int s = __builtin_amdgcn_readlane(x.wi, j);
-            mw[j] = (j < W && (unsigned)s < (unsigned long)N) ? Mb[(long)s * dv] : 0.f;
+        for (int k = 0; k < kPart; ++k) {
+            const int s = __builtin_amdgcn_readlane(x.wi, j0 + k);
+            mw[k] = (j0 + k < W && (unsigned)s < (unsigned long)N) ? Mb[(long)s * dv] : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < kMaxSlots; ++j) {
-            const int s = __builtin_amdgcn_readlane(x.ri, j);
-            const bool ld = __builtin_amdgcn_readlane((int)rload, j) != 0;
-            mr[j] = (j < R && ld) ? Mb[(long)s * dv] : 0.f;
+        for (int k = 0; k < kPart; ++k) {
+            const int s = __builtin_amdgcn_readlane(x.ri, j0 + k);
+            mr[k] = (j0 + k < R && (unsigned)s < (unsigned long)N) ? Mb[(long)s * dv] : 0.f;
         }
         TokIn nx = x;  // the next token's inputs, in flight meanwhile
         if (t + 1 < T) nx = load_tok<BF16>(v, alpha, b, w, widx, wwt, ridx, rwt, tok + H, dv, c, W, R, lane);
-        // decay since each slot's last write (slot j's factor in lane j)
-        const float dw = wok ? (float)exp(L - sw) : 0.f;
-        const float dr = rload ? (float)exp(L - sr) : 0.f;
-        float e = 0.f;  // a^T (decayed M) over the write slots, in slot order
+        // overlaps against this wavefront's positions of the other list: in lane r, whether read
+        // slot r is written; in lane j, the read weight falling on write slot j
+        int ovw = 0;
+        float rmw = 0.f;
 #pragma unroll
-        for (int j = 0; j < kMaxSlots; ++j) {
-            mw[j] *= lane_f(dw, j);
-            e = fmaf(lane_f(x.wa, j), mw[j], e);
+        for (int k = 0; k < kPart; ++k) {
+            const int p = j0 + k;
+            const int wp = __builtin_amdgcn_readlane(x.wi, p), rp = __builtin_amdgcn_readlane(x.ri, p);
+            ovw |= (p < W) && rok && wp == x.ri;
+            rmw += ((p < R) && wok && rp == x.wi) ? lane_f(x.ra, p) : 0.f;
+        }
+        ovp[wv][lane] = ovw;
+        rmp[wv][lane] = rmw;
+        // decay since each own slot's last write (slot j's factor in lane j)
+        const float dw = (mine && wok) ? (float)exp(L - sw) : 0.f;
+        const float dr = (mine && rok) ? (float)exp(L - sr) : 0.f;
+        float e = 0.f;  // this wavefront's part of a^T (decayed M), in list order
+#pragma unroll
+        for (int k = 0; k < kPart; ++k) {
+            mw[k] *= lane_f(dw, j0 + k);
+            e = fmaf(lane_f(x.wa, j0 + k), mw[k], e);
+        }
+        ep[wv][lane] = e;
+        __syncthreads();
+        e = ep[0][lane];
+        int ov = ovp[0][lane];
+        float rmatch = rmp[0][lane];
+#pragma unroll
+        for (int q = 1; q < kFwdWaves; ++q) {
+            e += ep[q][lane];
+            ov |= ovp[q][lane];
+            rmatch += rmp[q][lane];
         }
         const float u = x.ww * x.vv - x.be * e;
+        const float rw = (rok && !ov) ? x.ra * dr : 0.f;  // read weight times decay; 0 where written
         float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < kMaxSlots; ++j) {
-            const int s = __builtin_amdgcn_readlane(x.wi, j);
-            const float nv = fmaf(lane_f(x.wa, j), u, mw[j]);
-            if (j < W && (unsigned)s < (unsigned long)N) Mb[(long)s * dv] = nv;
-            acc = fmaf(lane_f(rmatch, j), nv, acc);
+        for (int k = 0; k < kPart; ++k) {
+            const int s = __builtin_amdgcn_readlane(x.wi, j0 + k);
+            const float nv = fmaf(lane_f(x.wa, j0 + k), u, mw[k]);
+            if (j0 + k < W && (unsigned)s < (unsigned long)N) Mb[(long)s * dv] = nv;
+            acc = fmaf(lane_f(rmatch, j0 + k), nv, acc);
         }
 #pragma unroll
-        for (int j = 0; j < kMaxSlots; ++j) acc = fmaf(lane_f(x.ra, j) * lane_f(dr, j), mr[j], acc);
-        o[tok * dv + c] = acc;
-        if (wok) Sb[x.wi] = L;
+        for (int k = 0; k < kPart; ++k) acc = fmaf(lane_f(rw, j0 + k), mr[k], acc);
+        if (mine && wok) Sb[x.wi] = L;
+        op[wv][lane] = acc;
+        __syncthreads();  // also orders this token's row and stamp stores before the next gathers
+        if (wv == 0) {
+            float oc = op[0][lane];
+#pragma unroll
+            for (int q = 1; q < kFwdWaves; ++q) oc += op[q][lane];
+            o[tok * dv + c] = oc;
+        }
         x = nx;
     }
-    if (lane == 0) Lbuf[bh * tiles + tile] = L;
+    if (threadIdx.x == 0) Lbuf[bh * tiles + tile] = L;
 }
 
 // M[s] *= exp(L - stamp[s]) for every slot, then stamp = L: the memory in plain units as of the
@@ -463,10 +495,10 @@ hipError_t launch_sdm_fwd(const SdmFwdArgs& a, hipStream_t st) {
     if (a.T == 0 || a.B == 0) return hipSuccess;
     const long grid = (long)a.B * a.H * (a.dv / kWave);
     if (a.bf16)
-        hipLaunchKernelGGL((sdm_fwd_kernel<true>), dim3((unsigned)grid), dim3(64), 0, st, a.v, a.alpha, a.b, a.w, a.widx,
+        hipLaunchKernelGGL((sdm_fwd_kernel<true>), dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, st, a.v, a.alpha, a.b, a.w, a.widx,
                            a.wwt, a.ridx, a.rwt, a.M, a.stamp, a.L, a.o, a.T, a.H, a.N, a.dv, a.W, a.R);
     else
-        hipLaunchKernelGGL((sdm_fwd_kernel<false>), dim3((unsigned)grid), dim3(64), 0, st, a.v, a.alpha, a.b, a.w, a.widx,
+        hipLaunchKernelGGL((sdm_fwd_kernel<false>), dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, st, a.v, a.alpha, a.b, a.w, a.widx,
                            a.wwt, a.ridx, a.rwt, a.M, a.stamp, a.L, a.o, a.T, a.H, a.N, a.dv, a.W, a.R);
     return hipGetLastError();
 }
