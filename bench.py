@@ -380,12 +380,34 @@ def sdm_leg(g, steps):
         it[0] += 1
         g.sdm_fwd(x["v"], x["alpha"], x["b"], x["w"], x["widx"], x["wwt"], x["ridx"], x["rwt"], state)
     ms = timed(step, steps)
+    # the same steps replayed from a HIP graph of 64 steps: the device's time per step, without
+    # the host's cost per call (a serving loop would capture its steps the same way)
+    ms_graph = None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                step()
+        stream.wait_stream(side)
+        with torch.cuda.graph(graph):
+            for _ in range(64):
+                step()
+        ms_graph = timed(graph.replay, max(2, steps // 64)) / 64
+        del graph
+    except RuntimeError as e:  # capture unavailable: report the per-call time only
+        print(f"[bench] sdm decode graph capture failed: {e}", file=sys.stderr, flush=True)
     # W rows read and written, R rows read (fp32), their stamps (fp64; W written), the token's
     # v and w (bf16), alpha and b, the 2 x 64 slot indices and weights, o written (fp32)
     per_ht = 3 * W * dv * 4 + 3 * W * 8 + dv * 2 * 2 + 2 * 2 + 2 * W * 8 + dv * 4
     gbs = per_ht * B * H / (ms * 1e-3) / 1e9
     res["decode"] = dict(us_per_step=round(ms * 1e3, 2), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
                          head_tokens_per_s=round(B * H / (ms * 1e-3), 1))
+    if ms_graph is not None:
+        gg = per_ht * B * H / (ms_graph * 1e-3) / 1e9
+        res["decode"].update(graph_us_per_step=round(ms_graph * 1e3, 2), graph_gbs=round(gg, 1),
+                             graph_frac=round(gg / HBM_PEAK_GBS, 4))
     del dec, pool
     T = 4096
     ad = make_sdm_inputs(B, T, H, 128, dv, n, 1, 1, seed=20259, with_memory=False, device="cuda")
@@ -399,7 +421,8 @@ def sdm_leg(g, steps):
     gbs = per_ht * B * H * Tp / (ms * 1e-3) / 1e9
     res["prefill"] = dict(T=Tp, ms=round(ms, 4), us_per_token=round(ms * 1e3 / Tp, 3), gbs=round(gbs, 1),
                           tokens_per_s=round(B * Tp / (ms * 1e-3), 1))
-    print(f"[bench] sdm: decode {res['decode']['us_per_step']} us/step ({res['decode']['gbs']} GB/s), "
+    print(f"[bench] sdm: decode {res['decode']['us_per_step']} us/step ({res['decode']['gbs']} GB/s; from a graph "
+          f"{res['decode'].get('graph_us_per_step')} us/step), "
           f"address {res['address']['ms']} ms for {B * T * H} queries, prefill {res['prefill']['us_per_token']} "
           f"us/token", file=sys.stderr, flush=True)
     del pf, state
