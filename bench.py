@@ -37,17 +37,28 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def sources_digest() -> str:
-    """sha256 over the kernel sources (every file under csrc/, in name order): names the build
-    that a profile's counters were taken on."""
+IMPL_SOURCES = {"split": "chunk_split.hip", "fused": "chunk_fused.hip", "recurrent": "recurrent.hip"}
+
+
+def sources_digest(impl: str) -> str:
+    """sha256 over the sources that the impl's kernels are built from: its .hip file under csrc/
+    and every csrc/ header it includes, directly or through another header, in name order. It
+    names the build that a profile's counters were taken on."""
     import hashlib
+    import re
+    seen, todo = set(), [IMPL_SOURCES[impl]]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.isfile(os.path.join(CSRC, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            todo += re.findall(r'^\s*#\s*include\s+"([^"]+)"', f.read(), flags=re.M)
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        path = os.path.join(CSRC, name)
-        if os.path.isfile(path) and name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode() + b"\0")
-            with open(path, "rb") as f:
-                h.update(f.read())
+    for name in sorted(seen):
+        h.update(name.encode() + b"\0")
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -615,7 +626,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    digest = sources_digest()
+    digest = sources_digest(args.impl)
     rec = {
         "metric": "GDN-2 chunk fwd tokens/s (B8,H16,T4k,d128) + decode state HBM GB/s",
         "value": round(B * T / (ms_per_step * 1e-3), 1),
