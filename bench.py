@@ -304,9 +304,25 @@ def backward_leg(g, steps):
     pargs = [pk[n] for n in ("q", "k", "v", "alpha", "b", "w")] + [pk["cu_seqlens"], pk["S0"], pdO, pdS]
     res["packed_ms"] = round(timed(lambda: g.chunk_bwd_varlen(*pargs, workspace=pws), max(2, steps // 2)), 4)
     del pk, pdO, pdS, pws, pargs
+    # a training step without the recomputation: the forward that saves into the backward's
+    # workspace (gdn2_chunk_fwd_save), then the backward that reads the saves (gdn2_chunk_bwd_saved);
+    # against it, the forward with its own workspace (gdn2_chunk_fwd) then gdn2_chunk_bwd
+    fargs = args[:7]
+    o = torch.empty(B, T, H, dv, device="cuda")
+    S_T = torch.empty(B, H, dk, dv, device="cuda")
+    fws = torch.empty(g.chunk_fwd_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8, device="cuda")
+    res["fwd_save_ms"] = round(timed(lambda: g.chunk_fwd_save(*fargs, o=o, S_out=S_T, workspace=ws), max(2, steps // 2)), 4)
+    res["bwd_saved_ms"] = round(timed(lambda: g.chunk_bwd(*args, saved=ws, out=out), steps), 4)
+    res["train_step_saved_ms"] = round(timed(lambda: (g.chunk_fwd_save(*fargs, o=o, S_out=S_T, workspace=ws),
+                                                      g.chunk_bwd(*args, saved=ws, out=out)), max(2, steps // 2)), 4)
+    res["train_step_recompute_ms"] = round(timed(lambda: (g.chunk_fwd(*fargs, o=o, S_out=S_T, workspace=fws),
+                                                          g.chunk_bwd(*args, workspace=ws, out=out)), max(2, steps // 2)), 4)
+    del o, S_T, fws
     print(f"[bench] backward: {ms:.3f} ms/call, {res['tokens_per_s']:.3e} tokens/s, {res['gbs']} GB/s "
           f"algorithmic ({100 * res['frac']:.1f}% of HBM); with the prologue {res['prologue_ms']:.3f} ms, "
-          f"scalar gates {res['scalar_gates_ms']:.3f} ms, packed (32 sequences) {res['packed_ms']:.3f} ms",
+          f"scalar gates {res['scalar_gates_ms']:.3f} ms, packed (32 sequences) {res['packed_ms']:.3f} ms; "
+          f"saved forward {res['fwd_save_ms']:.3f} ms + saved backward {res['bwd_saved_ms']:.3f} ms "
+          f"(step {res['train_step_saved_ms']:.3f} ms against {res['train_step_recompute_ms']:.3f} ms recomputing)",
           file=sys.stderr, flush=True)
     del ins, cot, ws, out
     torch.cuda.empty_cache()

@@ -28,7 +28,7 @@ __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", 
            "chunk_bwd_workspace_bytes", "chunk_bwd_varlen", "chunk_bwd_varlen_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
            "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc",
-           "sdm_address", "sdm_state", "sdm_fwd", "sdm_fold"]
+           "sdm_address", "sdm_state", "sdm_fwd", "sdm_fold", "chunk_fwd_save"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
@@ -72,6 +72,10 @@ def load():
     lib.gdn2_chunk_bwd.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
     lib.gdn2_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn2_chunk_fwd_save.argtypes = [p] * 9 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_fwd_save.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_saved.argtypes = [p] * 16 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_bwd_saved.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_varlen.argtypes = [p] * 17 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
     lib.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_varlen_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
@@ -203,6 +207,32 @@ def chunk_fwd(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspa
     return o, S_out
 
 
+def chunk_fwd_save(q, k, v, alpha, b, w=None, S0=None, *, o=None, S_out=None, workspace=None,
+                   l2norm=False, gate_logits=False, stream=None):
+    """The forward of a training step (gdn2_chunk_fwd_save): (o, S_T) as chunk_fwd computes them,
+    and the backward workspace, which then holds what chunk_bwd(..., saved=workspace) reads
+    instead of recomputing the forward. Returns (o, S_T, workspace); the workspace is allocated
+    here unless given (gdn2_chunk_bwd_workspace_bytes for these sizes and flags)."""
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 4) | _prologue_flags(l2norm, gate_logits)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty(B, T, H, dv, device=q.device, dtype=torch.float32)
+    S_out = _state_out(S0, B, H, dk, dv, q.device, S_out)
+    dt = _dtype_code(q)
+    need = int(lib.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dt, flags))
+    if need and workspace is None:
+        workspace = _scratch(need, q.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn2_chunk_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                 _ptr(o), _ptr(S_out), B, T, H, dk, dv, dt, flags, _ptr(workspace),
+                                 ws_bytes, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd_save", st)
+    return o, S_out, workspace
+
+
 def chunk_fwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
     return int(load().gdn2_chunk_fwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v,
                                                             BF16 if dtype == torch.bfloat16 else F32,
@@ -249,7 +279,7 @@ def chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) 
 
 
 def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=None, l2norm=False,
-              gate_logits=False, stream=None):
+              gate_logits=False, saved=None, stream=None):
     """Gradients of sum <dO, o> + <dS_T, S_T> for the prefill (bf16 inputs).
 
     Returns a dict of float32 tensors: dq, dk, dalpha, db [B, T, H, d_k], dv, dw [B, T, H, d_v] and
@@ -257,7 +287,14 @@ def chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, workspace=None, out=No
     give dalpha [B, T, H], and db [B, T, H] = dL/dbeta with no dw. With l2norm / gate_logits the
     inputs are the raw ones the forward takes with the same flags, and the gradients are with
     respect to them. `out` may supply any of them; the workspace is allocated here unless given.
+    saved: the workspace a chunk_fwd_save call on the same inputs returned (gdn2_chunk_bwd_saved):
+    the forward is then read from it, not recomputed.
     """
+    if saved is not None:
+        if workspace is not None and workspace is not saved:
+            raise ValueError("pass the saved workspace as `saved` alone")
+        return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, None, saved, out, l2norm, gate_logits, stream,
+                    fn="gdn2_chunk_bwd_saved")
     return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, None, workspace, out, l2norm, gate_logits, stream)
 
 
@@ -276,7 +313,7 @@ def chunk_bwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0, dO, dS_T=None, *, wor
     return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu_seqlens, workspace, out, l2norm, gate_logits, stream)
 
 
-def _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu, workspace, out, l2norm, gate_logits, stream):
+def _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu, workspace, out, l2norm, gate_logits, stream, fn=None):
     lib = load()
     flags = _check_inputs(q, k, v, alpha, b, w, 4 if cu is None else 3) | _prologue_flags(l2norm, gate_logits)
     lead = tuple(q.shape[:-2])  # (B, T), or (T_total,) for a packed batch
@@ -297,8 +334,9 @@ def _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu, workspace, out, l2norm, gate_lo
         out.setdefault("dw", torch.empty(*lead, H, dv, **f32))
     out.setdefault("dS0", torch.empty(B, H, dk, dv, **f32))
     dt = _dtype_code(q)
-    fn = "gdn2_chunk_bwd" if cu is None else "gdn2_chunk_bwd_varlen"
-    need = int(getattr(lib, fn + "_workspace_bytes")(B, T, H, dk, dv, dt, flags))
+    base = "gdn2_chunk_bwd" if cu is None else "gdn2_chunk_bwd_varlen"
+    fn = fn or base
+    need = int(getattr(lib, base + "_workspace_bytes")(B, T, H, dk, dv, dt, flags))
     if need and workspace is None:
         workspace = _scratch(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

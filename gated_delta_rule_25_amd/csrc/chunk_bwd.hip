@@ -1329,9 +1329,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, const float* rnq, const float* rnk, fl
     ChunkArgs fa{a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, nullptr, nullptr, a.B, a.T, a.H, DK, a.DV,
                  true, ((uint32_t)PRO << 2) | (AS ? 1u : 0u) | (BS ? 2u : 0u), nullptr, 0};
     fa.cu_seqlens = a.cu_seqlens;
-    hipError_t e = VAR ? launch_varlen_states(fa, ws, blobs, ring, S_save, Dp, Dl, st)
-                       : launch_split_states(fa, blobs, S_save, Dp, Dl, st);
-    if (e != hipSuccess) return e;
+    if (!a.saved) {  // recompute the forward's blocks, chunk-start states and D', Delta rows
+        const hipError_t e = VAR ? launch_varlen_states(fa, ws, blobs, ring, S_save, Dp, Dl, st)
+                                 : launch_split_states(fa, blobs, S_save, Dp, Dl, st);
+        if (e != hipSuccess) return e;
+    }
 
     constexpr int DVT = DK < 64 ? DK : 64;
     ChainBwdIO cio{a.v, BS ? a.b : a.w, a.dO, a.dS_T, blobs, G_save, dDl, dDp, a.dv, a.dw, a.dS0};
@@ -1421,8 +1423,20 @@ size_t bwd_varlen_workspace_bytes(int n, int T, int H, int DK, int DV, uint32_t 
     return (flags & 7u) ? scalar_layout(base, (size_t)T * H, DK, DV, flags).total : base;
 }
 
+hipError_t launch_fwd_save(const ChunkArgs& a, hipStream_t s) {
+    if (!a.bf16 || a.cu_seqlens || !bwd_supported(a.T, a.H, a.DK, a.DV, true, a.flags)) return hipErrorNotSupported;
+    if (a.T == 0) return hipSuccess;
+    if (!a.workspace || a.workspace_bytes < bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags))
+        return hipErrorInvalidValue;
+    const BwdLayout L = bwd_layout(a.B, a.T, a.H, a.DK, a.DV);
+    char* ws = static_cast<char*>(a.workspace);
+    return launch_split_states(a, ws + L.blobs, reinterpret_cast<uint16_t*>(ws + L.S_save),
+                               reinterpret_cast<uint16_t*>(ws + L.Dp), reinterpret_cast<uint16_t*>(ws + L.Dl), s);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     if (!bwd_supported(a.T, a.H, a.DK, a.DV, a.bf16, a.flags)) return hipErrorNotSupported;
+    if (a.saved && a.cu_seqlens) return hipErrorNotSupported;
     if (a.T == 0) {  // no tokens: dS0 = dS_T (or zeros), nothing else to write
         if (!a.dS0) return hipSuccess;
         const long n = (long)a.B * a.H * a.DK * a.DV;

@@ -123,14 +123,19 @@ hipError_t launch_states_t(const ChunkArgs& a, char* blobs, uint16_t* S_save, ui
     const int nch = (a.T + CH - 1) / CH;
     hipLaunchKernelGGL((prep_kernel<DK, true, AS, BS, PRO>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k,
                        a.alpha, a.b, a.B, a.T, a.H, 0, nch, blobs, VarTab{});
-    ChainIO io{a.v, a.w, nullptr, blobs, nch, 0, nch, nch, 1, a.B, a.T, a.H, a.DV,
-               a.S0, (long)DK * a.DV, 0, a.DV, nullptr, 0, 0, a.DV, 0};
+    // with a.o: the forward itself (o and S_T) with the saves; without: the saves alone
+    ChainIO io{a.v, a.w, a.o, blobs, nch, 0, nch, nch, 1, a.B, a.T, a.H, a.DV,
+               a.S0, (long)DK * a.DV, 0, a.DV, a.o ? a.S_out : nullptr, (long)DK * a.DV, 0, a.DV, 0};
     io.S_save = S_save;
     io.save_nch = nch;
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
-    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, true, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
-                       dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
+    if (a.o)
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, false, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
+                           dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
+    else
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, true, true, (PRO & 2) != 0>), dim3(BHp * (a.DV / DVT)),
+                           dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
     return hipGetLastError();
 }
 

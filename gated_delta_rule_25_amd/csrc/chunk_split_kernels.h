@@ -610,7 +610,7 @@ struct ChainIO {
     int out_ld;
     int out_last;  // only the last segment writes S_out
     int phi_tiles = 0;  // transition tiles (over d_k) after the value tiles, state-only pass
-    // Saves for the backward pass (state-only pass, sequential): the state at the start of every
+    // Saves for the backward pass (a single sequential pass, no segments): the state at the start of every
     // chunk (fp16: the precision its readers take it in as matrix-core operands),
     // S_save + ((bh * save_nch) + chunk) * DK * DV; D' and Delta rows, [B, T, H, DV] fp16
     uint16_t* S_save = nullptr;
@@ -626,8 +626,10 @@ struct ChainIO {
 // below DV / DVT run it from a zero state with the true U (their final state is the segment's
 // inhomogeneous part Psi); tiles above run it with U = 0 from the identity on their columns (the
 // transition Phi). No o, and only the block prefix the recurrence reads is copied.
-// SAVE (state-only pass, for the backward): also write the start state of every chunk and the
-// rows of D' and Delta (ChainIO's save fields).
+// SAVE (for the backward): also write the start state of every chunk and the rows of D' and
+// Delta (ChainIO's save fields); with STATE the backward's own recomputation, without it a
+// forward that computes o as well and leaves the backward nothing to recompute. Saving keeps the
+// state operands unscaled (the saved fp16 values are read as they are).
 // WSIG: w arrives as pre-activations (the prologue's gate logits); U = sigma(w) v.
 // VAR: packed batch (ChainIO::var); a sequence without tokens only carries S_in to S_out.
 template <int DK, int DVT, bool BF16, bool BS, bool STATE, bool SAVE = false, bool WSIG = false,
@@ -656,7 +658,6 @@ chain_kernel(const ChainIO io) {
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int vt = DV / DVT;                  // value tiles
     const int tiles = vt + (STATE ? io.phi_tiles : 0);
-    static_assert(STATE || !SAVE, "saves belong to the state-only pass");
     const int BH = io.B * H, BHp = (BH + 7) / 8 * 8;
     const int seg = blockIdx.x / (BHp * tiles);
     const int x = blockIdx.x % (BHp * tiles);
@@ -779,16 +780,20 @@ chain_kernel(const ChainIO io) {
     int t0_cur = 0;
     auto save_rows = [&](uint16_t* dst, const f4 (&X)[NT][4]) {
         const __amdgpu_buffer_rsrc_t rs = rows_rsrc(dst, tbase, t0_cur, Tq, (unsigned)(H * DV * 2), CH);
+        // this lane's byte offset in the chunk's row 4 g; opaque to the compiler, so that the 16
+        // rows' offsets are formed at each store (one add of a uniform row stride) instead of
+        // being hoisted out of the chunk loop and held in registers
+        unsigned lb = (((unsigned)(4 * g) * H + hh) * DV + col0 + l16) * 2u;
+        __asm__ volatile("" : "+v"(lb));
+        const unsigned rstride = (unsigned)(H * DV) * 2u;
 #pragma unroll
         for (int c = 0; c < NT; ++c)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const unsigned row = (unsigned)(16 * mt + 4 * g + j);
+                for (int j = 0; j < 4; ++j)
                     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)X[c][mt][j]), rs,
-                                                          (int)(((row * H + hh) * DV + col0 + 16 * c + l16) * 2u), 0, 0);
-                }
+                                                          (int)(lb + (unsigned)(16 * mt + j) * rstride + 32u * c), 0, 0);
     };
 
     if (n_count > 0) {  // (no copies in flight when there is no chunk to wait for them)
@@ -829,15 +834,19 @@ chain_kernel(const ChainIO io) {
             }
             if constexpr (SAVE) {
                 // the state at the start of this chunk, for the backward pass
-                uint16_t* sv = io.S_save + (save_base + n) * DK * DV;
+                // (offsets formed at each store from an opaque lane base, as in save_rows)
+                const __amdgpu_buffer_rsrc_t rsv = make_rsrc(io.S_save + (save_base + n) * DK * DV, DK * DV * 2u);
+                unsigned sb = ((unsigned)(4 * g) * DV + col0 + l16) * 2u;
+                __asm__ volatile("" : "+v"(sb));
 #pragma unroll
                 for (int c = 0; c < NT; ++c)
 #pragma unroll
                     for (int mk = 0; mk < NMK; ++mk)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            sv[(16 * mk + 4 * g + j) * DV + col0 + 16 * c + l16] =
-                                __builtin_bit_cast(uint16_t, (_Float16)Sacc[c][mk][j]);
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                __builtin_bit_cast(uint16_t, (_Float16)Sacc[c][mk][j]), rsv,
+                                (int)(sb + (unsigned)(16 * mk + j) * (unsigned)DV * 2u + 32u * c), 0, 0);
             }
             f4 D[NT][4];
 #pragma unroll

@@ -130,7 +130,7 @@ gdn2_status run_bwd(const void* q, const void* k, const void* v, const void* alp
                     float* dk, float* dv, float* dalpha, float* db, float* dw, float* dS0,
                     const int32_t* cu, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                     gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool saved = false) {
     if (in_dtype != GDN2_BF16 ||
         (gate_flags & ~(uint32_t)(GDN2_ALPHA_SCALAR | GDN2_BETA_SCALAR | GDN2_QK_L2NORM | GDN2_GATE_LOGITS)) != 0u)
         return GDN2_ERR_UNSUPPORTED;
@@ -175,6 +175,7 @@ gdn2_status run_bwd(const void* q, const void* k, const void* v, const void* alp
     gdn2::BwdArgs a{q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
                     B, T, H, d_k, d_v, true, gate_flags, workspace, workspace_bytes};
     a.cu_seqlens = cu;
+    a.saved = saved;
     const hipError_t e = gdn2::launch_bwd(a, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
@@ -399,6 +400,48 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes, void* stream) {
     return run_bwd(q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0, nullptr, B, T, H, d_k, d_v,
                    in_dtype, gate_flags, workspace, workspace_bytes, stream);
+}
+
+gdn2_status gdn2_chunk_fwd_save(const void* q, const void* k, const void* v, const void* alpha,
+                                const void* b, const void* w, const float* S0, float* o, float* S_out,
+                                int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    gdn2_status st = validate(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype, gate_flags, false);
+    if (st != GDN2_OK) return st;
+    if (in_dtype != GDN2_BF16 || !gdn2::bwd_supported(T, H, d_k, d_v, true, gate_flags)) return GDN2_ERR_UNSUPPORTED;
+    if (!chunk_grids_ok(B, T, H, d_k)) return GDN2_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)  // nothing to save: S_out <- S0 (or zeros)
+        return run_recurrent(q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, in_dtype, gate_flags, s);
+    const size_t need = gdn2::bwd_workspace_bytes(B, T, H, d_k, d_v, gate_flags);
+    if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+    Sizes sz;
+    sizes_of(B, T, H, d_k, d_v, &sz);
+    const Range rws = range_of(workspace, need);
+    const Range others[] = {range_of(q, sz.qk * 2), range_of(k, sz.qk * 2), range_of(v, sz.vw * 2),
+                            range_of(alpha, ((gate_flags & GDN2_ALPHA_SCALAR) ? sz.scalar : sz.qk) * 2),
+                            range_of(b, ((gate_flags & GDN2_BETA_SCALAR) ? sz.scalar : sz.qk) * 2),
+                            range_of(w, sz.vw * 2), range_of(S0, sz.state * 4), range_of(o, sz.vw * 4),
+                            range_of(S_out, sz.state * 4)};
+    for (const Range& r : others)
+        if (overlap(rws, r)) return GDN2_ERR_ALIAS;
+    gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, T, H, d_k, d_v, true, gate_flags, workspace,
+                      workspace_bytes};
+    const hipError_t e = gdn2::launch_fwd_save(a, s);
+    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* alpha,
+                                 const void* b, const void* w, const float* S0, const float* dO,
+                                 const float* dS_T, float* dq, float* dk, float* dv, float* dalpha,
+                                 float* db, float* dw, float* dS0, int32_t B, int32_t T, int32_t H,
+                                 int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return run_bwd(q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0, nullptr, B, T, H, d_k, d_v,
+                   in_dtype, gate_flags, workspace, workspace_bytes, stream, true);
 }
 
 gdn2_status gdn2_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* alpha,

@@ -138,8 +138,15 @@ struct BwdArgs {
     void* workspace;
     size_t workspace_bytes;
     const int* cu_seqlens = nullptr;  // packed batch: B + 1 cumulative lengths (device), T = rows
+    // the workspace already holds what launch_fwd_save left in it for these inputs: the operand
+    // blocks, chunk-start states and D', Delta rows are read, not recomputed
+    bool saved = false;
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
+// The forward (o, S_T) of equal-length batches that also leaves in a backward workspace (of
+// bwd_workspace_bytes) the operand blocks, the chunk-start states and the D', Delta rows that
+// launch_bwd with `saved` reads.
+hipError_t launch_fwd_save(const ChunkArgs& a, hipStream_t s);
 bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags);
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags);
 // The same for a packed batch of n sequences, T rows in all.

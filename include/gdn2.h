@@ -257,6 +257,40 @@ size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
                                       gdn2_dtype in_dtype, uint32_t gate_flags);
 
 /*
+ * A training step's forward and backward without the recomputation: gdn2_chunk_fwd_save computes
+ * o and S_T as gdn2_chunk_fwd does [GDN2-summary, paragraph "Реализация"] and, in the same pass,
+ * leaves in a backward workspace what gdn2_chunk_bwd would otherwise recompute at its start (the
+ * per-chunk operand blocks, the state at every chunk start and the D', Delta rows of every
+ * chunk, all in the precision the backward takes them in); gdn2_chunk_bwd_saved then gives the
+ * gradients gdn2_chunk_bwd gives, reading those instead of recomputing them.
+ *
+ *   gdn2_chunk_fwd_save: arguments as gdn2_chunk_fwd; the workspace is required when T > 0,
+ *            256-byte aligned, at least gdn2_chunk_bwd_workspace_bytes for the same sizes and
+ *            gate_flags, and overlaps no input or output (GDN2_ERR_ALIAS). Supported where
+ *            gdn2_chunk_bwd is (bf16, d_k == d_v in {32, 64, 128}, every gate form and prologue
+ *            flag); one sequence is one pass, never cut into segments. The state operands of the
+ *            products are fp16 without the power-of-two rescaling gdn2_chunk_fwd applies (as in
+ *            the backward's own recomputation), so the state's entries must stay inside fp16's
+ *            range; o agrees with gdn2_chunk_fwd's to fp16 operand rounding.
+ *   gdn2_chunk_bwd_saved: arguments and outputs as gdn2_chunk_bwd, with the workspace that a
+ *            gdn2_chunk_fwd_save call on the same inputs, sizes and gate_flags filled, unchanged
+ *            since (other calls may run in between). The call reads the saved parts and uses the
+ *            rest as scratch, so it may be repeated on the same saves. Given any other
+ *            workspace contents its gradients are undefined (no error can tell).
+ */
+gdn2_status gdn2_chunk_fwd_save(const void *q, const void *k, const void *v, const void *alpha,
+                                const void *b, const void *w, const float *S0, float *o, float *S_out,
+                                int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                gdn2_dtype in_dtype, uint32_t gate_flags, void *workspace,
+                                size_t workspace_bytes, void *stream);
+gdn2_status gdn2_chunk_bwd_saved(const void *q, const void *k, const void *v, const void *alpha,
+                                 const void *b, const void *w, const float *S0, const float *dO,
+                                 const float *dS_T, float *dq, float *dk, float *dv, float *dalpha,
+                                 float *db, float *dw, float *dS0, int32_t B, int32_t T, int32_t H,
+                                 int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Backward of gdn2_chunk_fwd_varlen: the gradients of L = sum over the packed rows of <dO, o> plus
  * sum over the sequences of <dS_T[s], S_T[s]>, for N sequences packed along the token axis and
  * delimited by cu_seqlens (device memory, read as by gdn2_chunk_fwd_varlen: clamped to

@@ -220,6 +220,31 @@ def test_bwd_gate_forms_on_the_host(lib):
     assert q(B, T, H, 64, 64, 0, 4) > q(B, T, H, 64, 64, 0, 0) == q(B, T, H, 64, 64, 0, 8)
 
 
+def test_saved_training_step_rejects_bad_arguments(lib):
+    # gdn2_chunk_fwd_save and gdn2_chunk_bwd_saved, refused on the host before any launch: the
+    # saving forward takes what the backward takes (bf16, d_k == d_v <= 128) and needs the
+    # backward's workspace; the saved backward checks as gdn2_chunk_bwd
+    far = [P((1 << 40) * (i + 1)) for i in range(16)]
+    ws = P((1 << 40) * 20)
+    fs, bs = lib.gdn2_chunk_fwd_save, lib.gdn2_chunk_bwd_saved
+    need = lib.gdn2_chunk_bwd_workspace_bytes(1, 64, 2, 64, 64, 0, 0)
+    assert need > 0
+    assert fs(*far[:9], 1, 64, 2, 64, 64, 0, 0, None, 0, None) == 7                  # no workspace
+    assert fs(*far[:9], 1, 64, 2, 64, 64, 0, 0, ws, need - 1, None) == 7             # too small
+    assert fs(*far[:9], 1, 64, 2, 64, 64, 0, 0, P((1 << 40) * 20 + 16), need, None) == 4  # misaligned
+    assert fs(*far[:9], 1, 64, 2, 64, 64, 1, 0, ws, 1 << 30, None) == 3              # fp32 inputs
+    assert fs(*far[:9], 1, 64, 2, 256, 256, 0, 0, ws, 1 << 30, None) == 3            # head size 256
+    assert fs(*far[:9], 1, 64, 2, 64, 32, 0, 0, ws, 1 << 30, None) == 3              # d_k != d_v
+    assert fs(*far[:9], 1, 64, 2, 64, 64, 0, 16, ws, 1 << 30, None) == 3             # unknown flag
+    p = list(far[:9])
+    p[7] = None
+    assert fs(*p, 1, 64, 2, 64, 64, 0, 0, ws, 1 << 30, None) == 1                    # no o
+    assert fs(*far[:9], 1, 64, 2, 64, 64, 0, 0, far[0], 1 << 30, None) == 5          # workspace on q
+    assert bs(*far[:16], 1, 64, 2, 64, 64, 0, 0, None, 0, None) == 7                 # no workspace
+    assert bs(*far[:16], 1, 64, 2, 64, 64, 0, 2, ws, 1 << 30, None) == 3             # w with scalar beta
+    assert bs(*far[:16], 1, 64, 2, 64, 64, 1, 0, ws, 1 << 30, None) == 3             # fp32 inputs
+
+
 def test_bwd_varlen_rejects_bad_arguments(lib):
     # every call below is refused on the host before any launch
     far = [P((1 << 40) * (i + 1)) for i in range(16)]
