@@ -38,8 +38,15 @@ __device__ __forceinline__ float lg2_sigmoid(float x) {
 // Raw buffer over [base, base + bytes): loads at byte offsets past the end return zero and
 // stores there are dropped, so a ragged last chunk needs no branch (and the compiler can count
 // the memory operations in flight exactly).
+// Every caller passes a base and size that are the same in all lanes of the wavefront; reading
+// them from the first active lane says so to the compiler, which otherwise may keep a descriptor
+// it cannot prove uniform in vector registers and issue each access in a loop over its distinct
+// values (one pass, but a loop that splits the code around every access).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 // Raw buffer over token rows [r0, r0 + min(len - r0, maxrows)) of a sequence whose first token
 // row is `first` in a tensor of row_bytes per token row. The base is advanced in 64-bit

@@ -784,7 +784,6 @@ chain_kernel(const ChainIO io) {
         // rows' offsets are formed at each store (one add of a uniform row stride) instead of
         // being hoisted out of the chunk loop and held in registers
         unsigned lb = (((unsigned)(4 * g) * H + hh) * DV + col0 + l16) * 2u;
-        __asm__ volatile("" : "+v"(lb));
         const unsigned rstride = (unsigned)(H * DV) * 2u;
 #pragma unroll
         for (int c = 0; c < NT; ++c)
@@ -826,18 +825,18 @@ chain_kernel(const ChainIO io) {
 
         if (chain) {
             // D' starts as U = w v, from this wave's slot. Its copy was issued before the previous
-            // chunk's 4 NT o stores, so this wait covers it and leaves those stores in flight.
-            if (nc == 0 || STATE) {
+            // chunk's 32 NT D', Delta saves (SAVE) and 4 NT o stores (not STATE), so this wait
+            // covers it and leaves those stores in flight.
+            if (nc == 0 || (STATE && !SAVE)) {
                 wait_dma();
             } else {
-                wait_vm_but<4 * NT>();
+                wait_vm_but<(SAVE ? 32 * NT : 0) + (STATE ? 0 : 4 * NT)>();
             }
             if constexpr (SAVE) {
                 // the state at the start of this chunk, for the backward pass
                 // (offsets formed at each store from an opaque lane base, as in save_rows)
                 const __amdgpu_buffer_rsrc_t rsv = make_rsrc(io.S_save + (save_base + n) * DK * DV, DK * DV * 2u);
                 unsigned sb = ((unsigned)(4 * g) * DV + col0 + l16) * 2u;
-                __asm__ volatile("" : "+v"(sb));
 #pragma unroll
                 for (int c = 0; c < NT; ++c)
 #pragma unroll
