@@ -780,10 +780,8 @@ chain_kernel(const ChainIO io) {
     int t0_cur = 0;
     auto save_rows = [&](uint16_t* dst, const f4 (&X)[NT][4]) {
         const __amdgpu_buffer_rsrc_t rs = rows_rsrc(dst, tbase, t0_cur, Tq, (unsigned)(H * DV * 2), CH);
-        // this lane's byte offset in the chunk's row 4 g; opaque to the compiler, so that the 16
-        // rows' offsets are formed at each store (one add of a uniform row stride) instead of
-        // being hoisted out of the chunk loop and held in registers
-        unsigned lb = (((unsigned)(4 * g) * H + hh) * DV + col0 + l16) * 2u;
+        // this lane's byte offset in the chunk's row 4 g, plus a uniform stride per stored row
+        const unsigned lb = (((unsigned)(4 * g) * H + hh) * DV + col0 + l16) * 2u;
         const unsigned rstride = (unsigned)(H * DV) * 2u;
 #pragma unroll
         for (int c = 0; c < NT; ++c)
@@ -834,9 +832,8 @@ chain_kernel(const ChainIO io) {
             }
             if constexpr (SAVE) {
                 // the state at the start of this chunk, for the backward pass
-                // (offsets formed at each store from an opaque lane base, as in save_rows)
                 const __amdgpu_buffer_rsrc_t rsv = make_rsrc(io.S_save + (save_base + n) * DK * DV, DK * DV * 2u);
-                unsigned sb = ((unsigned)(4 * g) * DV + col0 + l16) * 2u;
+                const unsigned sb = ((unsigned)(4 * g) * DV + col0 + l16) * 2u;
 #pragma unroll
                 for (int c = 0; c < NT; ++c)
 #pragma unroll
