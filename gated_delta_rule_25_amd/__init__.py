@@ -28,7 +28,7 @@ __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_bytes", 
            "chunk_bwd_workspace_bytes", "chunk_bwd_varlen", "chunk_bwd_varlen_workspace_bytes",
            "Gdn2Error", "library_path", "load", "ALPHA_SCALAR", "BETA_SCALAR", "QK_L2NORM", "GATE_LOGITS",
            "decode_step_slots", "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc",
-           "sdm_address", "sdm_state", "sdm_fwd", "sdm_fold", "chunk_fwd_save"]
+           "sdm_address", "sdm_state", "sdm_fwd", "sdm_fold", "chunk_fwd_save", "chunk_fwd_varlen_save"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn2.so")
@@ -76,6 +76,10 @@ def load():
     lib.gdn2_chunk_fwd_save.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_saved.argtypes = [p] * 16 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
     lib.gdn2_chunk_bwd_saved.restype = ctypes.c_int
+    lib.gdn2_chunk_fwd_varlen_save.argtypes = [p] * 10 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_fwd_varlen_save.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_varlen_saved.argtypes = [p] * 17 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
+    lib.gdn2_chunk_bwd_varlen_saved.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_varlen.argtypes = [p] * 17 + [i32] * 5 + [ctypes.c_int, u32, p, sz, p]
     lib.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_varlen_workspace_bytes.argtypes = [i32] * 5 + [ctypes.c_int, u32]
@@ -273,6 +277,35 @@ def chunk_fwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0=None, *, o=None, S_out
     return o, S_out
 
 
+def chunk_fwd_varlen_save(q, k, v, alpha, b, w, cu_seqlens, S0=None, *, o=None, S_out=None, workspace=None,
+                          l2norm=False, gate_logits=False, stream=None):
+    """The packed forward of a training step (gdn2_chunk_fwd_varlen_save): (o, S_T) as
+    chunk_fwd_varlen computes them, and the backward workspace holding what
+    chunk_bwd_varlen(..., saved=workspace) reads. Returns (o, S_T, workspace)."""
+    lib = load()
+    flags = _check_inputs(q, k, v, alpha, b, w, 3) | _prologue_flags(l2norm, gate_logits)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or not cu_seqlens.is_cuda \
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise TypeError("cu_seqlens must be a contiguous 1-d int32 GPU tensor of N + 1 entries")
+    N = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty(T, H, dv, device=q.device, dtype=torch.float32)
+    S_out = _state_out(S0, N, H, dk, dv, q.device, S_out)
+    dt = _dtype_code(q)
+    need = int(lib.gdn2_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, dt, flags))
+    if need and workspace is None:
+        workspace = _scratch(need, q.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn2_chunk_fwd_varlen_save(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                        _ptr(o), _ptr(S_out), _ptr(cu_seqlens), N, T, H, dk, dv, dt, flags,
+                                        _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd_varlen_save", st)
+    return o, S_out, workspace
+
+
 def chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype=torch.bfloat16, flags=0) -> int:
     return int(load().gdn2_chunk_bwd_workspace_bytes(B, T, H, d_k, d_v,
                                                      BF16 if dtype == torch.bfloat16 else F32, flags))
@@ -304,12 +337,18 @@ def chunk_bwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, dtype=torch.bfloat
 
 
 def chunk_bwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0, dO, dS_T=None, *, workspace=None, out=None,
-                     l2norm=False, gate_logits=False, stream=None):
+                     l2norm=False, gate_logits=False, saved=None, stream=None):
     """Gradients for the packed prefill chunk_fwd_varlen: the rows are [T_total, H, d] and the
-    states [N, H, d_k, d_v], N = len(cu_seqlens) - 1; otherwise as chunk_bwd."""
+    states [N, H, d_k, d_v], N = len(cu_seqlens) - 1; otherwise as chunk_bwd (saved: the workspace
+    a chunk_fwd_varlen_save call on the same inputs returned)."""
     if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or not cu_seqlens.is_cuda \
             or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise TypeError("cu_seqlens must be a contiguous 1-d int32 GPU tensor of N + 1 entries")
+    if saved is not None:
+        if workspace is not None and workspace is not saved:
+            raise ValueError("pass the saved workspace as `saved` alone")
+        return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu_seqlens, saved, out, l2norm, gate_logits, stream,
+                    fn="gdn2_chunk_bwd_varlen_saved")
     return _bwd(q, k, v, alpha, b, w, S0, dO, dS_T, cu_seqlens, workspace, out, l2norm, gate_logits, stream)
 
 

@@ -1424,19 +1424,25 @@ size_t bwd_varlen_workspace_bytes(int n, int T, int H, int DK, int DV, uint32_t 
 }
 
 hipError_t launch_fwd_save(const ChunkArgs& a, hipStream_t s) {
-    if (!a.bf16 || a.cu_seqlens || !bwd_supported(a.T, a.H, a.DK, a.DV, true, a.flags)) return hipErrorNotSupported;
+    if (!a.bf16 || !bwd_supported(a.T, a.H, a.DK, a.DV, true, a.flags)) return hipErrorNotSupported;
     if (a.T == 0) return hipSuccess;
-    if (!a.workspace || a.workspace_bytes < bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags))
-        return hipErrorInvalidValue;
-    const BwdLayout L = bwd_layout(a.B, a.T, a.H, a.DK, a.DV);
+    const bool var = a.cu_seqlens != nullptr;  // packed batch: a.B sequences, a.T rows in all
+    const size_t need = var ? bwd_varlen_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags)
+                            : bwd_workspace_bytes(a.B, a.T, a.H, a.DK, a.DV, a.flags);
+    if (!a.workspace || a.workspace_bytes < need) return hipErrorInvalidValue;
+    // the places launch_bwd reads them from: the blocks, the saves and (packed) the sequence
+    // table at the start of the workspace
+    const BwdLayout L = var ? bwd_layout_var(a.B, a.T, a.H, a.DK, a.DV) : bwd_layout(a.B, a.T, a.H, a.DK, a.DV);
     char* ws = static_cast<char*>(a.workspace);
-    return launch_split_states(a, ws + L.blobs, reinterpret_cast<uint16_t*>(ws + L.S_save),
-                               reinterpret_cast<uint16_t*>(ws + L.Dp), reinterpret_cast<uint16_t*>(ws + L.Dl), s);
+    uint16_t* S_save = reinterpret_cast<uint16_t*>(ws + L.S_save);
+    uint16_t* Dp = reinterpret_cast<uint16_t*>(ws + L.Dp);
+    uint16_t* Dl = reinterpret_cast<uint16_t*>(ws + L.Dl);
+    return var ? launch_varlen_states(a, ws, ws + L.blobs, varlen_chunk_bound(a.B, a.T), S_save, Dp, Dl, s)
+               : launch_split_states(a, ws + L.blobs, S_save, Dp, Dl, s);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     if (!bwd_supported(a.T, a.H, a.DK, a.DV, a.bf16, a.flags)) return hipErrorNotSupported;
-    if (a.saved && a.cu_seqlens) return hipErrorNotSupported;
     if (a.T == 0) {  // no tokens: dS0 = dS_T (or zeros), nothing else to write
         if (!a.dS0) return hipSuccess;
         const long n = (long)a.B * a.H * a.DK * a.DV;

@@ -134,7 +134,8 @@ hipError_t launch_varlen_t(const ChunkArgs& a, hipStream_t st) {
 }
 
 // The backward's forward pass over a packed batch: the sequence table (at `table`), prep into
-// `blobs` ([h][chunk of the batch], `ring` slots per head) and the state-only chain with saves:
+// `blobs` ([h][chunk of the batch], `ring` slots per head) and the chain with saves (state-only,
+// or with o and S_T when a.o is set):
 // the start state of every chunk ([h][chunk of the batch][DK][DV]) and the rows of D' and Delta
 // (fp16, packed rows). bf16, scalar gate forms AS / BS, the prologue flags PRO.
 template <int DK, int PRO, bool AS, bool BS>
@@ -154,15 +155,20 @@ hipError_t launch_varlen_states_t(const ChunkArgs& a, char* table, char* blobs, 
         hipLaunchKernelGGL((prep_kernel<DK, true, AS, BS, PRO, true>), dim3((unsigned)(a.H * ring)), dim3(256), 0,
                            st, a.q, a.k, a.alpha, a.b, 1, a.T, a.H, 0, (int)ring, blobs, vt);
     const long ld = DK;
-    ChainIO io{a.v, a.w, nullptr, blobs, (int)ring, 0, 0, 0, 1, N, a.T, a.H, a.DV,
-               a.S0, ld * a.DV, 0, a.DV, nullptr, 0, 0, a.DV, 0};
+    // with a.o: the forward itself (o and S_T) with the saves; without: the saves alone
+    ChainIO io{a.v, a.w, a.o, blobs, (int)ring, 0, 0, 0, 1, N, a.T, a.H, a.DV,
+               a.S0, ld * a.DV, 0, a.DV, a.o ? a.S_out : nullptr, ld * a.DV, 0, a.DV, 0};
     io.var = vt;
     io.S_save = S_save;
     io.Dp_save = Dp_save;
     io.Dl_save = Dl_save;
     const int BH = N * a.H, BHp = (BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, true, true, (PRO & 2) != 0, true>),
-                       dim3(BHp * (a.DV / DVT)), dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
+    if (a.o)
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, false, true, (PRO & 2) != 0, true>),
+                           dim3(BHp * (a.DV / DVT)), dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
+    else
+        hipLaunchKernelGGL((chain_kernel<DK, DVT, true, BS, true, true, (PRO & 2) != 0, true>),
+                           dim3(BHp * (a.DV / DVT)), dim3(ChainSmem<DK, DVT, true>::threads), 0, st, io);
     return hipGetLastError();
 }
 

@@ -220,6 +220,58 @@ gdn2_status rmsnorm_bwd_checked(const float* x, const float* weight, const float
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+// The checks and launch of gdn2_chunk_fwd_varlen, and with `save` of gdn2_chunk_fwd_varlen_save
+// (the workspace is then the backward's, which keeps what gdn2_chunk_bwd_varlen_saved reads).
+gdn2_status varlen_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b, const void* w,
+                       const float* S0, float* o, float* S_out, const int32_t* cu_seqlens, int32_t N, int32_t T_total,
+                       int32_t H, int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                       size_t workspace_bytes, void* stream, bool save) {
+    if (N <= 0) return GDN2_ERR_SHAPE;
+    // the token rows are one sequence of T_total tokens as far as sizes go; the states separately
+    gdn2_status st = validate(q, k, v, alpha, b, w, nullptr, o, nullptr, 1, T_total, H, d_k, d_v,
+                              in_dtype, gate_flags, false);
+    if (st != GDN2_OK) return st;
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    const bool bf16 = in_dtype == GDN2_BF16;
+    if (save && (!bf16 || !gdn2::bwd_supported(T_total, H, d_k, d_v, true, gate_flags))) return GDN2_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_ERR_ALIGN;
+    if ((S0 && !aligned16(S0)) || (S_out && !aligned16(S_out))) return GDN2_ERR_ALIGN;
+    if (save && T_total == 0)  // no rows: nothing to save; S_out <- S0 (or zeros) per sequence
+        return run_recurrent(q, k, v, alpha, b, w, S0, o, S_out, N, 0, H, d_k, d_v, in_dtype, gate_flags,
+                             static_cast<hipStream_t>(stream));
+    if (!workspace) return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+    if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
+    // one workgroup per (chunk bound, head) in prep and per (sequence, head, value tile) in the
+    // chain: both grids (in threads) must stay below 2^31
+    if (gdn2::varlen_chunk_bound(N, T_total) * H * 256 >= (1l << 31)) return GDN2_ERR_SHAPE;
+    if (((long)N * H + 7) / 8 * 8 * (d_v / (d_k < 64 ? d_k : 64)) * 512 >= (1l << 31)) return GDN2_ERR_SHAPE;
+    Sizes sz, states;
+    if (!sizes_of(1, T_total, H, d_k, d_v, &sz) || !sizes_of(N, 1, H, d_k, d_v, &states)) return GDN2_ERR_SHAPE;
+    const size_t need = save ? gdn2::bwd_varlen_workspace_bytes(N, T_total, H, d_k, d_v, gate_flags)
+                             : gdn2::varlen_workspace_bytes(N, T_total, H, d_k, d_v, bf16);
+    if (workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+    const uint64_t es = bf16 ? 2 : 4;
+    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
+    const Range ins[] = {range_of(q, sz.qk * es), range_of(k, sz.qk * es), range_of(v, sz.vw * es),
+                         range_of(alpha, (as ? sz.scalar : sz.qk) * es), range_of(b, (bs ? sz.scalar : sz.qk) * es),
+                         range_of(w, sz.vw * es), range_of(cu_seqlens, ((uint64_t)N + 1) * 4)};
+    const Range rS0 = range_of(S0, states.state * 4), rSo = range_of(S_out, states.state * 4);
+    const Range ro = range_of(o, sz.vw * 4), rws = range_of(workspace, save ? need : workspace_bytes);
+    for (const Range& r : ins)
+        if (overlap(rSo, r) || overlap(ro, r) || overlap(rws, r)) return GDN2_ERR_ALIAS;
+    if (overlap(ro, rS0) || overlap(ro, rSo) || overlap(rws, rS0) || overlap(rws, rSo) || overlap(rws, ro))
+        return GDN2_ERR_ALIAS;
+    if (overlap(rS0, rSo) && !(rS0.lo == rSo.lo && rS0.hi == rSo.hi)) return GDN2_ERR_ALIAS;
+    gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, N, T_total, H, d_k, d_v, bf16, gate_flags,
+                      workspace, workspace_bytes};
+    a.cu_seqlens = cu_seqlens;
+    const hipError_t e = save ? gdn2::launch_fwd_save(a, static_cast<hipStream_t>(stream))
+                              : gdn2::launch_split_varlen(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,43 +354,18 @@ gdn2_status gdn2_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
                                   int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
                                   gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-    if (N <= 0) return GDN2_ERR_SHAPE;
-    // the token rows are one sequence of T_total tokens as far as sizes go; the states separately
-    gdn2_status st = validate(q, k, v, alpha, b, w, nullptr, o, nullptr, 1, T_total, H, d_k, d_v,
-                              in_dtype, gate_flags, false);
-    if (st != GDN2_OK) return st;
-    if (!cu_seqlens) return GDN2_ERR_NULL;
-    if (!workspace) return GDN2_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_ERR_ALIGN;
-    if ((S0 && !aligned16(S0)) || (S_out && !aligned16(S_out))) return GDN2_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
-    const bool bf16 = in_dtype == GDN2_BF16;
-    if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
-    // one workgroup per (chunk bound, head) in prep and per (sequence, head, value tile) in the
-    // chain: both grids (in threads) must stay below 2^31
-    if (gdn2::varlen_chunk_bound(N, T_total) * H * 256 >= (1l << 31)) return GDN2_ERR_SHAPE;
-    if (((long)N * H + 7) / 8 * 8 * (d_v / (d_k < 64 ? d_k : 64)) * 512 >= (1l << 31)) return GDN2_ERR_SHAPE;
-    Sizes sz, states;
-    if (!sizes_of(1, T_total, H, d_k, d_v, &sz) || !sizes_of(N, 1, H, d_k, d_v, &states)) return GDN2_ERR_SHAPE;
-    if (workspace_bytes < gdn2::varlen_workspace_bytes(N, T_total, H, d_k, d_v, bf16)) return GDN2_ERR_WORKSPACE;
-    const uint64_t es = bf16 ? 2 : 4;
-    const bool as = (gate_flags & GDN2_ALPHA_SCALAR) != 0, bs = (gate_flags & GDN2_BETA_SCALAR) != 0;
-    const Range ins[] = {range_of(q, sz.qk * es), range_of(k, sz.qk * es), range_of(v, sz.vw * es),
-                         range_of(alpha, (as ? sz.scalar : sz.qk) * es), range_of(b, (bs ? sz.scalar : sz.qk) * es),
-                         range_of(w, sz.vw * es), range_of(cu_seqlens, ((uint64_t)N + 1) * 4)};
-    const Range rS0 = range_of(S0, states.state * 4), rSo = range_of(S_out, states.state * 4);
-    const Range ro = range_of(o, sz.vw * 4), rws = range_of(workspace, workspace_bytes);
-    for (const Range& r : ins)
-        if (overlap(rSo, r) || overlap(ro, r) || overlap(rws, r)) return GDN2_ERR_ALIAS;
-    if (overlap(ro, rS0) || overlap(ro, rSo) || overlap(rws, rS0) || overlap(rws, rSo) || overlap(rws, ro))
-        return GDN2_ERR_ALIAS;
-    if (overlap(rS0, rSo) && !(rS0.lo == rSo.lo && rS0.hi == rSo.hi)) return GDN2_ERR_ALIAS;
-    gdn2::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, N, T_total, H, d_k, d_v, bf16, gate_flags,
-                      workspace, workspace_bytes};
-    a.cu_seqlens = cu_seqlens;
-    const hipError_t e = gdn2::launch_split_varlen(a, static_cast<hipStream_t>(stream));
-    if (e == hipErrorNotSupported) return GDN2_ERR_UNSUPPORTED;
-    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    return varlen_fwd(q, k, v, alpha, b, w, S0, o, S_out, cu_seqlens, N, T_total, H, d_k, d_v, in_dtype, gate_flags,
+                      workspace, workspace_bytes, stream, false);
+}
+
+gdn2_status gdn2_chunk_fwd_varlen_save(const void* q, const void* k, const void* v, const void* alpha,
+                                       const void* b, const void* w, const float* S0, float* o,
+                                       float* S_out, const int32_t* cu_seqlens, int32_t N,
+                                       int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                       gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return varlen_fwd(q, k, v, alpha, b, w, S0, o, S_out, cu_seqlens, N, T_total, H, d_k, d_v, in_dtype, gate_flags,
+                      workspace, workspace_bytes, stream, true);
 }
 
 gdn2_status gdn2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
@@ -455,6 +482,19 @@ gdn2_status gdn2_chunk_bwd_varlen(const void* q, const void* k, const void* v, c
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_ERR_ALIGN;
     return run_bwd(q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0, cu_seqlens, N, T_total, H,
                    d_k, d_v, in_dtype, gate_flags, workspace, workspace_bytes, stream);
+}
+
+gdn2_status gdn2_chunk_bwd_varlen_saved(const void* q, const void* k, const void* v, const void* alpha,
+                                        const void* b, const void* w, const float* S0, const float* dO,
+                                        const float* dS_T, float* dq, float* dk, float* dv, float* dalpha,
+                                        float* db, float* dw, float* dS0, const int32_t* cu_seqlens, int32_t N,
+                                        int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                        gdn2_dtype in_dtype, uint32_t gate_flags, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_ERR_ALIGN;
+    return run_bwd(q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0, cu_seqlens, N, T_total, H,
+                   d_k, d_v, in_dtype, gate_flags, workspace, workspace_bytes, stream, true);
 }
 
 size_t gdn2_chunk_bwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,

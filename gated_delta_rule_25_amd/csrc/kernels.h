@@ -143,9 +143,9 @@ struct BwdArgs {
     bool saved = false;
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
-// The forward (o, S_T) of equal-length batches that also leaves in a backward workspace (of
-// bwd_workspace_bytes) the operand blocks, the chunk-start states and the D', Delta rows that
-// launch_bwd with `saved` reads.
+// The forward (o, S_T) that also leaves in a backward workspace (of bwd_workspace_bytes, or
+// bwd_varlen_workspace_bytes for a packed batch) the operand blocks, the chunk-start states and
+// the D', Delta rows (and, packed, the sequence table) that launch_bwd with `saved` reads.
 hipError_t launch_fwd_save(const ChunkArgs& a, hipStream_t s);
 bool bwd_supported(int T, int H, int DK, int DV, bool bf16, uint32_t flags);
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV, uint32_t flags);

@@ -289,6 +289,24 @@ gdn2_status gdn2_chunk_bwd_saved(const void *q, const void *k, const void *v, co
                                  float *db, float *dw, float *dS0, int32_t B, int32_t T, int32_t H,
                                  int32_t d_k, int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags,
                                  void *workspace, size_t workspace_bytes, void *stream);
+/* The same pair over a packed batch (the layouts, cu_seqlens and sizes of gdn2_chunk_fwd_varlen and
+ * gdn2_chunk_bwd_varlen): gdn2_chunk_fwd_varlen_save takes a workspace of at least
+ * gdn2_chunk_bwd_varlen_workspace_bytes (it also keeps the sequence table there) and
+ * gdn2_chunk_bwd_varlen_saved reads it, with the same cu_seqlens contents. T_total == 0: the
+ * forward writes S_out = S0 (or zeros) and needs no workspace. */
+gdn2_status gdn2_chunk_fwd_varlen_save(const void *q, const void *k, const void *v, const void *alpha,
+                                       const void *b, const void *w, const float *S0, float *o,
+                                       float *S_out, const int32_t *cu_seqlens, int32_t N, int32_t T_total,
+                                       int32_t H, int32_t d_k, int32_t d_v, gdn2_dtype in_dtype,
+                                       uint32_t gate_flags, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+gdn2_status gdn2_chunk_bwd_varlen_saved(const void *q, const void *k, const void *v, const void *alpha,
+                                        const void *b, const void *w, const float *S0, const float *dO,
+                                        const float *dS_T, float *dq, float *dk, float *dv, float *dalpha,
+                                        float *db, float *dw, float *dS0, const int32_t *cu_seqlens,
+                                        int32_t N, int32_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                        gdn2_dtype in_dtype, uint32_t gate_flags, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /*
  * Backward of gdn2_chunk_fwd_varlen: the gradients of L = sum over the packed rows of <dO, o> plus

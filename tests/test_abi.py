@@ -243,6 +243,18 @@ def test_saved_training_step_rejects_bad_arguments(lib):
     assert bs(*far[:16], 1, 64, 2, 64, 64, 0, 0, None, 0, None) == 7                 # no workspace
     assert bs(*far[:16], 1, 64, 2, 64, 64, 0, 2, ws, 1 << 30, None) == 3             # w with scalar beta
     assert bs(*far[:16], 1, 64, 2, 64, 64, 1, 0, ws, 1 << 30, None) == 3             # fp32 inputs
+    # the packed pair: cu_seqlens required; the saving forward takes the backward's workspace size
+    fv, bv = lib.gdn2_chunk_fwd_varlen_save, lib.gdn2_chunk_bwd_varlen_saved
+    cu = P((1 << 40) * 30)
+    vneed = lib.gdn2_chunk_bwd_varlen_workspace_bytes(3, 200, 2, 64, 64, 0, 0)
+    assert vneed > 0
+    assert fv(*far[:9], None, 3, 200, 2, 64, 64, 0, 0, ws, 1 << 30, None) == 1       # no cu_seqlens
+    assert fv(*far[:9], cu, 3, 200, 2, 64, 64, 0, 0, None, 0, None) == 7             # no workspace
+    assert fv(*far[:9], cu, 3, 200, 2, 64, 64, 0, 0, ws, vneed - 1, None) == 7       # too small
+    assert fv(*far[:9], cu, 3, 200, 2, 64, 64, 1, 0, ws, 1 << 30, None) == 3         # fp32 inputs
+    assert fv(*far[:9], cu, 0, 200, 2, 64, 64, 0, 0, ws, 1 << 30, None) == 2         # no sequences
+    assert bv(*far[:16], None, 3, 200, 2, 64, 64, 0, 0, ws, 1 << 30, None) == 1      # no cu_seqlens
+    assert bv(*far[:16], cu, 3, 200, 2, 64, 64, 0, 0, None, 0, None) == 7            # no workspace
 
 
 def test_bwd_varlen_rejects_bad_arguments(lib):

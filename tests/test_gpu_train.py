@@ -160,3 +160,64 @@ def test_train_step_no_tokens():
     torch.cuda.synchronize()
     assert ws is None and o.numel() == 0
     assert torch.equal(S_T, S0) and torch.equal(out["dS0"], dS)
+
+
+# ---- packed batches: gdn2_chunk_fwd_varlen_save + gdn2_chunk_bwd_varlen_saved ----------------
+
+VAR_CASES = [
+    ("d128_mix", scaled(WORKLOADS["prefill_1p3b"], H=2), [0, 1, 63, 64, 65, 200, 0, 130, 17, 257], False, False),
+    ("d64", scaled(WORKLOADS["prefill_1p3b"], H=3, d_k=64, d_v=64), [5, 0, 128, 300], False, False),
+    ("d32", scaled(WORKLOADS["prefill_1p3b"], H=2, d_k=32, d_v=32), [70, 1, 190], False, False),
+    ("gdn", scaled(WORKLOADS["gdn_scalar"], H=2), [100, 64, 0, 3], False, False),
+    ("kda_prologue", scaled(WORKLOADS["kda_scalar"], H=2), [3, 150, 0], True, True),
+    ("general_prologue", scaled(WORKLOADS["prefill_1p3b"], H=2), [70, 0, 129, 5], True, True),
+]
+
+
+@pytest.mark.parametrize("name,wl,lengths,l2n,gl", VAR_CASES, ids=[c[0] for c in VAR_CASES])
+def test_train_step_packed(name, wl, lengths, l2n, gl):
+    """The packed forward that saves against gdn2_chunk_fwd_varlen (o and S_T within the bf16 bar;
+    each sequence's o against the oracle's forward of it alone where no prologue flag applies),
+    and the saved packed backward bit-equal to gdn2_chunk_bwd_varlen."""
+    from gated_delta_rule_25_amd.inputs import make_packed_cotangents, make_packed_inputs
+    banner(f"train step packed {name} lengths={lengths} {wl}")
+    g = _g()
+    ins = make_packed_inputs(wl, lengths, raw=l2n or gl)
+    cot = make_packed_cotangents(wl, lengths)
+    names = ("q", "k", "v", "alpha", "b", "w")
+    x = [_cuda(ins[n]) for n in names]
+    cu = ins["cu_seqlens"].cuda()
+    S0 = _cuda(ins["S0"])
+    dO, dS = _cuda(cot["dO"]), _cuda(cot["dS_T"])
+    o, S_T, ws = g.chunk_fwd_varlen_save(*x, cu, S0, l2norm=l2n, gate_logits=gl)
+    saved = g.chunk_bwd_varlen(*x, cu, S0, dO, dS, l2norm=l2n, gate_logits=gl, saved=ws)
+    again = g.chunk_bwd_varlen(*x, cu, S0, dO, dS, l2norm=l2n, gate_logits=gl, saved=ws)
+    recomputed = g.chunk_bwd_varlen(*x, cu, S0, dO, dS, l2norm=l2n, gate_logits=gl)
+    o_r, S_r = g.chunk_fwd_varlen(*x, cu, S0, l2norm=l2n, gate_logits=gl)
+    torch.cuda.synchronize()
+    eo, es = normwise_err(o, o_r), normwise_err(S_T, S_r)
+    print(f"  o vs chunk_fwd_varlen {eo:.2e}  S_T {es:.2e}", flush=True)
+    assert eo <= TOL and es <= TOL, (eo, es)
+    _same(saved, recomputed, "saved vs recomputed packed backward")
+    _same(saved, again, "second call on the same saves")
+    if not (l2n or gl or ins["alpha_scalar"] or ins["beta_scalar"]):
+        bounds = ins["cu_seqlens"].tolist()
+        for s in range(len(lengths)):
+            lo, hi = bounds[s], bounds[s + 1]
+            if hi == lo:
+                assert torch.equal(S_T[s].cpu(), ins["S0"][s]), s
+                continue
+            o_ref, S_ref = oracle.forward(*[ins[n][lo:hi].unsqueeze(0) for n in names], S0=ins["S0"][s:s + 1])
+            e1, e2 = normwise_err(o[lo:hi].unsqueeze(0), o_ref), normwise_err(S_T[s:s + 1], S_ref)
+            assert e1 <= TOL and e2 <= TOL, (s, e1, e2)
+
+
+def test_train_step_packed_no_rows():
+    banner("train step packed, T_total = 0")
+    g = _g()
+    S0 = torch.randn(3, 2, 64, 64, device="cuda")
+    e = torch.empty(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    o, S_T, ws = g.chunk_fwd_varlen_save(e, e, e, e, e, e, cu, S0)
+    torch.cuda.synchronize()
+    assert ws is None and o.numel() == 0 and torch.equal(S_T, S0)
