@@ -40,10 +40,35 @@ PROFILES = os.path.join(ROOT, "profiles")
 IMPL_SOURCES = {"split": "chunk_split.hip", "fused": "chunk_fused.hip", "recurrent": "recurrent.hip"}
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with runs of whitespace collapsed: two sources that
+    differ only in comments or layout compile to the same code and get the same digest."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":  # a string or character literal, copied whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_digest(impl: str) -> str:
-    """sha256 over the sources that the impl's kernels are built from: its .hip file under csrc/
-    and every csrc/ header it includes, directly or through another header, in name order. It
-    names the build that a profile's counters were taken on."""
+    """sha256 over the code (comments and layout aside) of the sources that the impl's kernels are
+    built from: its .hip file under csrc/ and every csrc/ header it includes, directly or through
+    another header, in name order. It names the build that a profile's counters were taken on."""
     import hashlib
     import re
     seen, todo = set(), [IMPL_SOURCES[impl]]
@@ -57,8 +82,8 @@ def sources_digest(impl: str) -> str:
     h = hashlib.sha256()
     for name in sorted(seen):
         h.update(name.encode() + b"\0")
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

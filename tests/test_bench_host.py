@@ -34,3 +34,15 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""  # no JSON line
+
+
+def test_sources_digest_ignores_comments_and_layout_only():
+    import bench
+    a = 'int f(int x) { return x + 1; }  // one\n/* two */ const char* s = "// kept";\n'
+    b = 'int f(int x)\n{\n    return x + 1;  /* changed comment */\n}\nconst char* s = "// kept";'
+    c = 'int f(int x) { return x + 2; }\nconst char* s = "// kept";'
+    d = 'int f(int x) { return x + 1; }\nconst char* s = "// changed";'
+    assert bench._code_only(a).replace(" ", "") == bench._code_only(b).replace(" ", "")
+    assert bench._code_only(a) != bench._code_only(c)
+    assert bench._code_only(a) != bench._code_only(d)
+    assert bench.sources_digest("split") != bench.sources_digest("fused")
