@@ -32,7 +32,10 @@ __device__ __forceinline__ float sigmoid(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));  // rcp within 1 ulp
 }
 
-template <int DK, bool BF16, bool ASCALAR, bool BSCALAR, int PRO>
+// ONE: exactly one token (the decode step): no next-token prefetch, so fewer registers and more
+// wavefronts per SIMD (which helps while the state sits in the Infinity Cache; streaming it from
+// HBM, the general kernel is faster).
+template <int DK, bool BF16, bool ASCALAR, bool BSCALAR, int PRO, bool ONE>
 __global__ void __launch_bounds__(256)
 recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const void* __restrict__ alpha,
@@ -73,9 +76,6 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         for (int m = 0; m < R; ++m) S[m][0] = S[m][1] = S[m][2] = S[m][3] = 0.f;
     }
 
-    // per-token inputs for this lane (current and next, for prefetch)
-    float qa[R], ka[R], aa[R], ba[R], va[4], wa[4];
-    float qn[R], kn[R], an[R], bn[R], vn[4], wn[4];
     auto fetch = [&](int t, float* qx, float* kx, float* ax, float* bx, float* vx, float* wx) {
         const long tok = ((long)bb * T + t) * H + hh;
         load_vec<R, BF16>(q, tok * DK + row0, qx);
@@ -109,10 +109,9 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         }
     };
 
-    if (T > 0) fetch(0, qa, ka, aa, ba, va, wa);
-    for (int t = 0; t < T; ++t) {
-        if (t + 1 < T) fetch(t + 1, qn, kn, an, bn, vn, wn);
-
+    // one token: the two reductions, delta, the readout and the state update
+    auto token = [&](int t, const float* qa, const float* ka, const float* aa, const float* ba, const float* va,
+                     const float* wa) {
         float r[4] = {0.f, 0.f, 0.f, 0.f}, po[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f, sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int m = 0; m < R; ++m) {
@@ -169,13 +168,28 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
             const long tok = ((long)bb * T + t) * H + hh;
             *reinterpret_cast<float4*>(o + tok * DV + col0) = make_float4(oc[0], oc[1], oc[2], oc[3]);
         }
-        if (t + 1 < T) {
+    };
+
+    if constexpr (ONE) {
+        float qa[R], ka[R], aa[R], ba[R], va[4], wa[4];
+        fetch(0, qa, ka, aa, ba, va, wa);
+        token(0, qa, ka, aa, ba, va, wa);
+    } else {
+        // per-token inputs for this lane (current and next, for prefetch)
+        float qa[R], ka[R], aa[R], ba[R], va[4], wa[4];
+        float qn[R], kn[R], an[R], bn[R], vn[4], wn[4];
+        if (T > 0) fetch(0, qa, ka, aa, ba, va, wa);
+        for (int t = 0; t < T; ++t) {
+            if (t + 1 < T) fetch(t + 1, qn, kn, an, bn, vn, wn);
+            token(t, qa, ka, aa, ba, va, wa);
+            if (t + 1 < T) {
 #pragma unroll
-            for (int m = 0; m < R; ++m) {
-                qa[m] = qn[m]; ka[m] = kn[m]; aa[m] = an[m]; ba[m] = bn[m];
+                for (int m = 0; m < R; ++m) {
+                    qa[m] = qn[m]; ka[m] = kn[m]; aa[m] = an[m]; ba[m] = bn[m];
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) { va[c] = vn[c]; wa[c] = wn[c]; }
             }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) { va[c] = vn[c]; wa[c] = wn[c]; }
         }
     }
 
@@ -191,17 +205,26 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
 template <int DK, bool BF16, bool AS, bool BS, int PRO>
 hipError_t launch_t(const RecurrentArgs& a, hipStream_t s) {
     const int items = a.B * a.H * (a.DV / 32);
-    // A decode step (T = 1) whose states fit in the 256 MB Infinity Cache runs one wave per
-    // workgroup: step after step the state largely stays in that cache, and the finer
-    // workgroups stream it faster (B256 H16 d128, 256 MiB: 85.8 us against 102.8 us with four
-    // waves). Past about 400 MB of state the cache no longer holds it and four waves per
-    // workgroup are faster (B1024: 384 against 423 us); so also the token-by-token prefill.
+    // A decode step (T = 1) whose states fit in the 256 MB Infinity Cache runs the one-token kernel
+    // with two waves per workgroup: step after step the state largely stays in that cache, and
+    // finer workgroups with more of them per SIMD stream it faster (B256 H16 d128, 256 MiB:
+    // 87.0 us against 93.0 us for the general kernel with one wave per workgroup and 102.8 us with
+    // four). Past about 400 MB of state the cache no longer holds it and the general kernel with
+    // four waves per workgroup is faster, at its two waves per SIMD (B1024: 383 us against 399 us
+    // for the one-token kernel held to the same occupancy and 410 us at its own three per SIMD;
+    // 423 us with one wave per workgroup); so also the token-by-token prefill.
     const size_t state_bytes = (size_t)a.B * a.H * DK * a.DV * 4;
-    const int waves_per_block = (a.T == 1 && state_bytes <= (size_t(320) << 20)) ? 1 : 4;
+    const bool cached = a.T == 1 && state_bytes <= (size_t(320) << 20);
+    const int waves_per_block = cached ? 2 : 4;
     const int blocks = (items + waves_per_block - 1) / waves_per_block;
-    hipLaunchKernelGGL((recurrent_kernel<DK, BF16, AS, BS, PRO>), dim3(blocks), dim3(64 * waves_per_block),
-                       0, s, a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, a.o, a.S_out, a.B, a.T, a.H,
-                       a.DV, a.slots, a.n_slots);
+    if (cached)
+        hipLaunchKernelGGL((recurrent_kernel<DK, BF16, AS, BS, PRO, true>), dim3(blocks), dim3(64 * waves_per_block),
+                           0, s, a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, a.o, a.S_out, a.B, a.T, a.H,
+                           a.DV, a.slots, a.n_slots);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<DK, BF16, AS, BS, PRO, false>), dim3(blocks), dim3(64 * waves_per_block),
+                           0, s, a.q, a.k, a.v, a.alpha, a.b, a.w, a.S0, a.o, a.S_out, a.B, a.T, a.H,
+                           a.DV, a.slots, a.n_slots);
     return hipGetLastError();
 }
 
