@@ -63,6 +63,10 @@ CASES = {
     "bf16_dv256_N256_overlaps": (1, 40, 2, 16, 256, 64, 64, "bf16", 3.0),
     "strong_decay_folds": (1, 300, 2, 32, 128, 32, 32, "bf16", -1.0),
     "decode_T1": (4, 1, 3, 64, 128, 64, 64, "bf16", 3.0),
+    # list lengths that split unevenly over the four wavefronts' 16-position parts, in a memory
+    # of 64 slots, so nearly every read slot is also written and every token rewrites the last
+    "bf16_dv64_W37_R50_N64": (2, 60, 2, 8, 64, 37, 50, "bf16", 3.0),
+    "fp32_dv128_W1_R1": (1, 50, 2, 16, 128, 1, 1, "fp32", 3.0),
 }
 
 
