@@ -923,15 +923,24 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         part[(4 * I + g) * CW + ch0 + c] = acc;
     }
     __syncthreads();
+    {
+        // the sub-blocks before this lane's, added in order; every read issued at once
+        float pre[2] = {0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        float pre = 0.f;
-        for (int sb = 0; sb < 4 * I + g; ++sb) pre += part[sb * CW + ch0 + c];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            G[j][c] += pre;
-            G2[(rb + j) * CW + ch0 + c] = G[j][c];
+        for (int sb = 0; sb < 15; ++sb) {
+            const float2 p = *reinterpret_cast<const float2*>(&part[sb * CW + ch0]);
+            if (sb < 4 * I + g) {
+                pre[0] += p.x;
+                pre[1] += p.y;
+            }
         }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                G[j][c] += pre[c];
+                G2[(rb + j) * CW + ch0 + c] = G[j][c];
+            }
     }
     __syncthreads();
 
@@ -1144,13 +1153,17 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         float acc = (c ? dgam.y : dgam.x) * __builtin_amdgcn_exp2f(G63c[c]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) acc += G2[w * CW + ch0 + c];
-        for (int sb = 4 * I + g + 1; sb < 16; ++sb) acc += part[sb * CW + ch0 + c];
+        float later[15];  // the sub-blocks after this lane's, added in order; reads issued at once
+#pragma unroll
+        for (int sb = 1; sb < 16; ++sb) later[sb - 1] = part[sb * CW + ch0 + c];
+#pragma unroll
+        for (int sb = 1; sb < 16; ++sb)
+            if (sb > 4 * I + g) acc += later[sb - 1];
 #pragma unroll
         for (int j = 3; j >= 0; --j) {
             acc += dG[j][c];
-            // acc = dL/d ln(alpha); d ln sigma(x)/dx = 1 - sigma(x)
-            const float a = __builtin_amdgcn_exp2f(la[j][c]);
-            dal[j][c] = GL ? acc * (1.f - a) : acc / a;
+            // acc = dL/d ln(alpha), alpha = 2^la; d ln sigma(x)/dx = 1 - sigma(x)
+            dal[j][c] = GL ? acc * (1.f - __builtin_amdgcn_exp2f(la[j][c])) : acc * __builtin_amdgcn_exp2f(-la[j][c]);
         }
     }
 #pragma unroll
