@@ -146,6 +146,22 @@ constexpr int bwd_chain_threads() {
 // WSIG: w holds pre-activations (the prologue's gate logits): the gate is sigma(w), and dw is
 // taken with respect to the pre-activation.
 // BS: a scalar beta per token row stands for w (its partial gradients go to io.dwp).
+// The reverse chain's copy of a block into LDS, issued so that the compiler does not track it.
+// Tracked, it makes the compiler wait for the whole copy at the first LDS access it cannot
+// separate from it (in practice right after issuing it, before the staging writes), and at every
+// LDS barrier. The kernel waits for its copies itself, by count, before the barrier that starts
+// each step; no LDS access the compiler can see touches the block buffer before that.
+// The instruction writes no register: only LDS (at M0 + 16 lane) and the vector memory count;
+// M0 is an input the compiler sets, and the nop covers the wait a write of M0 needs before it.
+__device__ __forceinline__ void dma_flat_untracked(const char* g, char* l, int bytes, int cw, int nw, int lane) {
+    for (int off = cw * 1024; off < bytes; off += nw * 1024) {
+        if (off + lane * 16 < bytes) {
+            const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_ptr_t)(l + off));
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g + off + lane * 16), "{m0}"(m) : "memory");
+        }
+    }
+}
+
 template <int DK, bool WSIG = false, bool VAR = false, bool BS = false>
 __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(const ChainBwdIO io) {
     using PR = Prec<true>;
@@ -263,9 +279,8 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(row_off(row) / 2u), 0, 0);
             xv[q][0] = v2[0];
             xv[q][1] = v2[1];
-            if constexpr (BS) {  // the row's scalar beta, in both halves of both words
-                const uint32_t x = __builtin_amdgcn_raw_buffer_load_b16(rs_w, (int)(((unsigned)row * H + hh) * 2u), 0, 0);
-                xw[q][0] = xw[q][1] = x | (x << 16);
+            if constexpr (BS) {  // the row's scalar beta, as loaded (widened where it is used)
+                xw[q][0] = __builtin_amdgcn_raw_buffer_load_b16(rs_w, (int)(((unsigned)row * H + hh) * 2u), 0, 0);
             } else {
                 const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, (int)(row_off(row) / 2u), 0, 0);
                 xw[q][0] = w2[0];
@@ -299,22 +314,23 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             }
         }
     };
-    constexpr int kStepStores = NMK + 16;  // stores a step issues after its loads
+    // stores a step issues after its loads, whatever the rows: the dD', Delta and dv (and dw) rows;
+    // a scalar beta's partial sums are stored only where rows exist, so they are not counted
+    constexpr int kStepStores = BS ? 12 : 16;
 
     if (nchs > 0) {
-        dma_flat(blob_of(nchs - 1), smem, BL::bytes, wv, NW, lane);
+        dma_flat_untracked(blob_of(nchs - 1), smem, BL::bytes, wv, NW, lane);
         fetch(nchs - 1);
     }
+    // (the first step's wait, outside the loop: a wait under a branch in the loop leaves the
+    // compiler a path without it, and it then waits again, for everything, at the first use)
+    wait_dma();
 
     for (int idx = 0; idx < nchs; ++idx) {
         const int n = nchs - 1 - idx, t0 = n * CH;
         // block n and this wave's rows of chunk n have arrived (the previous step's stores,
         // issued after them, may still be in flight)
-        if (idx == 0) {
-            wait_dma();
-        } else {
-            wait_vm_but<kStepStores>();
-        }
+        wait_vm_but<kStepStores>();
         lds_barrier();  // block n is whole; every read of the transposed copy is done
         // ---- transpose block n ----
         {
@@ -340,7 +356,10 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             for (int x = tid; x < DK; x += NTH) gam[x] = sgC[x];
         }
         lds_barrier();  // the transposed copy is whole; the block buffer is free
-        if (n > 0) dma_flat(blob_of(n - 1), smem, BL::bytes, wv, NW, lane);
+        // G' of this chunk, for the contraction kernel: stored before this step's loads are
+        // issued, so that its staging reads wait for nothing in flight
+        store_state_h(io.G_save + (cbase0 + n) * DK * DV);
+        if (n > 0) dma_flat_untracked(blob_of(n - 1), smem, BL::bytes, wv, NW, lane);
 
         // this chunk's rows: dO into operand fragments (k = token row 32 s2 + kap(g, i)) through
         // the staging tile; v, w kept for dv, dw; then the loads for the next chunk
@@ -361,7 +380,7 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 cv[q][e] = bf(xv[q][e >> 1], e & 1);
-                cw[q][e] = bf(xw[q][e >> 1], e & 1);
+                cw[q][e] = BS ? __uint_as_float(xw[q][0] << 16) : bf(xw[q][e >> 1], e & 1);
                 cs[q][e] = 1.f;
                 if constexpr (WSIG) {
                     cw[q][e] = sigmoidf_(cw[q][e]);
@@ -369,9 +388,6 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
                 }
             }
         if (n > 0) fetch(n - 1);
-
-        // G' of this chunk, for the contraction kernel
-        store_state_h(io.G_save + (cbase0 + n) * DK * DV);
 
         Frag Gf[NKS];
 #pragma unroll
