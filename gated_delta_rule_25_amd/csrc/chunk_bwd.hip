@@ -91,51 +91,34 @@ struct ChainBwdIO {
 };
 
 // The reverse chain contracts P, T, K_bar, Q_hat and E_hat over the other index than the forward
-// chain does, so once per chunk the block is transposed in LDS into row-major operands
-// (8x8 tiles: eight 4-element-unit reads, eight 16-byte writes per tile), after which every
-// matrix-core operand is two 8-byte reads:
-//   PT[m][s] = P[s][m], TT[m][s] = T[s][m], Kb[m][c] = K_bar^T[c][m], QT[c][r] = Q_hat[r][c],
-//   ET[c][r] = -E_hat[r][c].
+// chain does, and reads them straight from the block with the transposing LDS read of gfx950
+// (ds_read_b64_tr_b16). Within each group of 16 lanes, lane 4 e + a gives the address of four
+// consecutive 16-bit elements, and lane 4 a + c receives element c of what lanes 4 e + a
+// (e = 0..3) address. Pointed at rows k0 .. k0 + 3 (by e), columns c0 + 4 a .. c0 + 4 a + 3 of a
+// row-major Y, lane i of the group thus receives Y[k0 .. k0 + 3][c0 + i]: four k-consecutive
+// elements of row c0 + i of Y^T, half of a matrix-core operand. The block layouts permute whole
+// 4-element units only, so each lane's address is an ordinary element address. Two block buffers:
+// the next block is copied into one while the other is read.
 template <int DK>
 struct BwdChainSmem {
     using BL = Blob<DK, true>;
-    static constexpr int RS = CH + 8;  // row stride (halves) of PT, TT, QT, ET: 36 dwords
-    static constexpr int KS = DK + 8;  // row stride of Kb
-    static constexpr int oPT = BL::bytes;
-    static constexpr int oTT = oPT + CH * RS * 2;
-    static constexpr int oKb = oTT + CH * RS * 2;
-    static constexpr int oQT = oKb + CH * KS * 2;
-    static constexpr int oET = oQT + DK * RS * 2;
-    static constexpr int oGam = oET + DK * RS * 2;  // float [DK]
+    static constexpr int oBuf0 = 0, oBuf1 = BL::bytes;
     // per wave: 64 rows x 16 columns of fp32 (row stride 20) to turn accumulator tiles into rows
     static constexpr int SR = 20;
-    static constexpr int oStg = oGam + DK * 4;
+    static constexpr int oStg = 2 * BL::bytes;
     static constexpr int bytes = oStg + (DK < 64 ? DK : 64) / 16 * CH * SR * 4;
-    static_assert(bytes <= 160 * 1024, "reverse chain LDS");
+    static_assert(BL::bytes % 16 == 0 && bytes <= 160 * 1024, "reverse chain LDS");
 };
 
-// Destination rows c0 + i (i = 0..7), elements r0 .. r0 + 7, from the 8x8 source tile at
-// (r0, c0); unit(r, c) returns the source's 4 elements (r, c .. c + 3).
-template <class Unit>
-__device__ __forceinline__ void tr_tile(Unit unit, _Float16* dst, int stride, int r0, int c0) {
-    h4 u[8][2];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        u[a][0] = unit(r0 + a, c0);
-        u[a][1] = unit(r0 + a, c0 + 4);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h8 o;
-#pragma unroll
-        for (int a = 0; a < 8; ++a) o[a] = u[a][i >> 2][i & 3];
-        *reinterpret_cast<h8*>(dst + (c0 + i) * stride + r0) = o;
-    }
+__device__ __forceinline__ h4 lds_read_tr(const _Float16* p) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4* lds_s4;
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
 }
 
 // Waves own 16 value columns each. The block of the next (earlier) chunk is copied into LDS while
-// the current one is worked on from its transposed copy, and the next chunk's dO, v, w rows are
-// loaded into registers at the start of each step. Rows go to and from memory 16 bytes per lane
+// the current one is worked on, and the next chunk's dO, v, w rows are loaded into registers at
+// the start of each step. Rows go to and from memory 16 bytes per lane
 // through a per-wave LDS tile, which keeps a step at 52 vector-memory instructions per wave, few
 // enough that the next step's wait leaves this step's stores in flight.
 template <int DK>
@@ -175,18 +158,6 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     constexpr int NTH = NW * 64;
 
     __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
-    E* PT = reinterpret_cast<E*>(smem + SM::oPT);
-    E* TT = reinterpret_cast<E*>(smem + SM::oTT);
-    E* Kb = reinterpret_cast<E*>(smem + SM::oKb);
-    E* QT = reinterpret_cast<E*>(smem + SM::oQT);
-    E* ET = reinterpret_cast<E*>(smem + SM::oET);
-    float* gam = reinterpret_cast<float*>(smem + SM::oGam);
-    const E* sEn = reinterpret_cast<const E*>(smem + BL::oEn);
-    const E* sKbT = reinterpret_cast<const E*>(smem + BL::oKbT);
-    const E* sTm = reinterpret_cast<const E*>(smem + BL::oTm);
-    const E* sPm = reinterpret_cast<const E*>(smem + BL::oP);
-    const E* sQh = reinterpret_cast<const E*>(smem + BL::oQh);
-    const float* sgC = reinterpret_cast<const float*>(smem + BL::oGC);
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = io.H, T = io.T, DV = io.DV, nch = io.nch;
@@ -248,8 +219,18 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
         }
         return PR::make(t);
     };
-    // operand fragment of row `row` (k contiguous), k = 32 s + kap(g, .)
-    auto frag = [&](const E* row, int s) { return PR::lds_pair(row + 32 * s + 4 * g, row + 32 * s + 16 + 4 * g); };
+    // operand fragment of row c0 + l16 of Y^T, k = 32 s + kap(g, .), for a block matrix Y with
+    // element (r, c) at Y + at(r, c): transposing reads of rows 32 s + 4 g + e and
+    // 32 s + 16 + 4 g + e (e = l16 / 4), columns c0 + 4 (l16 % 4) .. + 3
+    const int te = l16 >> 2, ta = 4 * (l16 & 3);
+    auto frag_t = [&](const E* Y, auto at, int c0, int s) {
+        const h4 lo = lds_read_tr(Y + at(32 * s + 4 * g + te, c0 + ta));
+        const h4 hi = lds_read_tr(Y + at(32 * s + 16 + 4 * g + te, c0 + ta));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    const auto at_en = [](int r, int c) { return BL::en(r, c); };
+    const auto at_kbt = [](int r, int c) { return BL::kbt(r, c); };
+    const auto at_tp = [](int r, int c) { return BL::tp(r, c); };
 
     // Rows as lanes move them: lane (rr = lane / 4 + 16 q, cc = lane % 4), q = 0..3, holds
     // columns 4 cc .. 4 cc + 3 of this wave's 16 at chunk row rr.
@@ -319,7 +300,7 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
     constexpr int kStepStores = BS ? 12 : 16;
 
     if (nchs > 0) {
-        dma_flat_untracked(blob_of(nchs - 1), smem, BL::bytes, wv, NW, lane);
+        dma_flat_untracked(blob_of(nchs - 1), smem + SM::oBuf0, BL::bytes, wv, NW, lane);
         fetch(nchs - 1);
     }
     // (the first step's wait, outside the loop: a wait under a branch in the loop leaves the
@@ -331,35 +312,18 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
         // block n and this wave's rows of chunk n have arrived (the previous step's stores,
         // issued after them, may still be in flight)
         wait_vm_but<kStepStores>();
-        lds_barrier();  // block n is whole; every read of the transposed copy is done
-        // ---- transpose block n ----
-        {
-            auto uQ = [&](int r, int c) { return *reinterpret_cast<const h4*>(sQh + BL::en(r, c)); };
-            auto uE = [&](int r, int c) { return *reinterpret_cast<const h4*>(sEn + BL::en(r, c)); };
-            auto uK = [&](int r, int c) { return *reinterpret_cast<const h4*>(sKbT + BL::kbt(r, c)); };
-            auto uP = [&](int r, int c) { return *reinterpret_cast<const h4*>(sPm + BL::tp(r, c)); };
-            auto uT = [&](int r, int c) { return *reinterpret_cast<const h4*>(sTm + BL::tp(r, c)); };
-            constexpr int NQ = 8 * (DK / 8);  // 8x8 tiles of Q_hat (and of E_hat, K_bar^T)
-            for (int x = tid; x < NQ; x += NTH) {
-                const int r0 = 8 * (x % 8), c0 = 8 * (x / 8);
-                tr_tile(uQ, QT, SM::RS, r0, c0);
-                tr_tile(uE, ET, SM::RS, r0, c0);
-                tr_tile(uK, Kb, SM::KS, 8 * (x % (DK / 8)), 8 * (x / (DK / 8)));
-            }
-            // P and T: the stored tiles (rows 0..31 hold columns 0..31, rows 32..63 all 64)
-            for (int x = tid; x < 48; x += NTH) {
-                const int r0 = x < 16 ? 8 * (x / 4) : 32 + 8 * ((x - 16) / 8);
-                const int c0 = x < 16 ? 8 * (x % 4) : 8 * ((x - 16) % 8);
-                tr_tile(uP, PT, SM::RS, r0, c0);
-                tr_tile(uT, TT, SM::RS, r0, c0);
-            }
-            for (int x = tid; x < DK; x += NTH) gam[x] = sgC[x];
-        }
-        lds_barrier();  // the transposed copy is whole; the block buffer is free
+        lds_barrier();  // block n is whole; every read of the other buffer (the previous step's) is done
+        const char* blk = smem + ((idx & 1) ? SM::oBuf1 : SM::oBuf0);
+        const E* En = reinterpret_cast<const E*>(blk + BL::oEn);
+        const E* KbT = reinterpret_cast<const E*>(blk + BL::oKbT);
+        const E* Tm = reinterpret_cast<const E*>(blk + BL::oTm);
+        const E* Pm = reinterpret_cast<const E*>(blk + BL::oP);
+        const E* Qh = reinterpret_cast<const E*>(blk + BL::oQh);
+        const float* gC = reinterpret_cast<const float*>(blk + BL::oGC);
         // G' of this chunk, for the contraction kernel: stored before this step's loads are
         // issued, so that its staging reads wait for nothing in flight
         store_state_h(io.G_save + (cbase0 + n) * DK * DV);
-        if (n > 0) dma_flat_untracked(blob_of(n - 1), smem, BL::bytes, wv, NW, lane);
+        if (n > 0) dma_flat_untracked(blob_of(n - 1), smem + ((idx & 1) ? SM::oBuf0 : SM::oBuf1), BL::bytes, wv, NW, lane);
 
         // this chunk's rows: dO into operand fragments (k = token row 32 s2 + kap(g, i)) through
         // the staging tile; v, w kept for dv, dw; then the loads for the next chunk
@@ -398,11 +362,10 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             dL[mt] = f4{0.f, 0.f, 0.f, 0.f};
-            const int m = 16 * mt + l16;
 #pragma unroll
-            for (int s2 = mt / 2; s2 < 2; ++s2) PR::mma(dL[mt], frag(PT + m * SM::RS, s2), dOf[s2]);
+            for (int s2 = mt / 2; s2 < 2; ++s2) PR::mma(dL[mt], frag_t(Pm, at_tp, 16 * mt, s2), dOf[s2]);
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) PR::mma(dL[mt], frag(Kb + m * SM::KS, s), Gf[s]);
+            for (int s = 0; s < NKS; ++s) PR::mma(dL[mt], frag_t(KbT, at_kbt, 16 * mt, s), Gf[s]);
         }
         // dD' = T^T dDelta
         const Frag dLf[2] = {stack(dL[0], dL[1]), stack(dL[2], dL[3])};
@@ -410,9 +373,8 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             dP[mt] = f4{0.f, 0.f, 0.f, 0.f};
-            const int m = 16 * mt + l16;
 #pragma unroll
-            for (int s2 = mt / 2; s2 < 2; ++s2) PR::mma(dP[mt], frag(TT + m * SM::RS, s2), dLf[s2]);
+            for (int s2 = mt / 2; s2 < 2; ++s2) PR::mma(dP[mt], frag_t(Tm, at_tp, 16 * mt, s2), dLf[s2]);
         }
         // rows of dDelta and dD'; dv = w dD', dw = v dD' (rows past T are dropped)
         stage(dL, std::integral_constant<int, 4>());
@@ -441,17 +403,19 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
                        cs[q][3] * cv[q][3] * x.w);
             }
         }
-        // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (ET holds -E_hat^T)
+        // dL/dS at the chunk start = Q_hat^T dO + Diag(gamma) G' - E_hat^T dD'  (the block holds -E_hat)
         const Frag dPf[2] = {stack(dP[0], dP[1]), stack(dP[2], dP[3])};
 #pragma unroll
         for (int mk = 0; mk < NMK; ++mk) {
-            const int m = 16 * mk + l16;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) G[mk][j] *= gam[16 * mk + 4 * g + j];
+            const float4 gm = *reinterpret_cast<const float4*>(gC + 16 * mk + 4 * g);
+            G[mk][0] *= gm.x;
+            G[mk][1] *= gm.y;
+            G[mk][2] *= gm.z;
+            G[mk][3] *= gm.w;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                PR::mma(G[mk], frag(QT + m * SM::RS, s2), dOf[s2]);
-                PR::mma(G[mk], frag(ET + m * SM::RS, s2), dPf[s2]);
+                PR::mma(G[mk], frag_t(Qh, at_en, 16 * mk, s2), dOf[s2]);
+                PR::mma(G[mk], frag_t(En, at_en, 16 * mk, s2), dPf[s2]);
             }
         }
     }
