@@ -28,11 +28,12 @@
 //   2. bwd_chain_kernel: dL/dS backwards over the chunks, one workgroup per (b, h, 64 value
 //      columns), the gradient state in MFMA accumulators; writes G' of every chunk, dDelta, dD',
 //      dv, dw and dS0.
-//   3. bwd_contract_kernel: per (b, h, chunk), the products contracted over the value channels
-//      (dQ_hat, dE_hat, dK_bar, dP, dT) on the matrix cores, dgamma, and dA in fp32.
-//   4. bwd_key_kernel: per (b, h, chunk, 32 key channels), the decay-weighted sums XA, XP, Y
-//      through block references (no factor above 1), the elementwise terms and the reverse
-//      cumulative sum; writes dq, dk, db, dalpha.
+//   3. bwd_contract_kernel: per (b, h, chunk), dP = lower(dO Delta^T) and dT = lower(dDelta D'^T),
+//      contracted over the value channels on the matrix cores, then dA = -T^T dT T^T in fp32.
+//   4. bwd_key_kernel: per (b, h, chunk, 32 key channels), its channels' dQ_hat = dO S^T,
+//      dE_hat = -dD' S^T and dK_bar = Delta G'^T on the matrix cores and dgamma, then the
+//      decay-weighted sums XA, XP, Y through block references (no factor above 1), the
+//      elementwise terms and the reverse cumulative sum; writes dq, dk, db, dalpha.
 #include "chunk_blob.h"
 #include "kernels.h"
 
