@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -107,9 +108,10 @@ def profiled_traffic(impl: str, digest: str):
     return None
 
 
-def prefill_bytes_per_head_token(dk: int, dv: int, T: int) -> float:
-    # q, k, alpha, b (bf16) + v, w (bf16) + o (fp32) + S0 read and S_T write amortised over T
-    return 4 * dk * 2 + 2 * dv * 2 + 4 * dv + 8 * dk * dv / T
+def prefill_bytes_per_head_token(dk: int, dv: int, T: int, es: int = 2) -> float:
+    # q, k, alpha, b + v, w (es bytes each: 2 for bf16, 4 for fp32) + o (fp32) + S0 read and S_T
+    # write amortised over T
+    return 4 * dk * es + 2 * dv * es + 4 * dv + 8 * dk * dv / T
 
 
 def prefill_flops_per_head_token(dk: int, dv: int, C: int = 64) -> float:
@@ -125,18 +127,19 @@ KERNELS = {
 }
 
 
-def prefill_kwargs(g, impl, B, T, H, dk, dv, ring_mb=None):
+def prefill_kwargs(g, impl, B, T, H, dk, dv, ring_mb=None, dtype=None):
     """Keyword arguments of chunk_fwd for one schedule, with any workspace allocated up front so
     that no allocation falls inside a timed region."""
     import torch
     if impl == "recurrent":
         return {}
+    dtype = torch.bfloat16 if dtype is None else dtype
     kw = dict(schedule=impl)
     if impl == "split":
-        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv)
+        need = g.chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype=dtype)
         if need and ring_mb is not None:
             state = B * H * dk * dv * 4
-            per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv) - state
+            per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dv, dtype=dtype) - state
             slots = max(1, int(ring_mb * 2**20) // per_chunk)
             need = min(need, state + slots * per_chunk)
         if need:
@@ -156,7 +159,7 @@ def time_prefill(g, ins, steps, warmup, impl, ring_mb=None, **flags):
     dv = ins["v"].shape[-1]
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.float32)
     S_out = torch.empty(B, H, dk, dv, device="cuda", dtype=torch.float32)
-    kw = dict(o=o, S_out=S_out, **prefill_kwargs(g, impl, B, T, H, dk, dv, ring_mb))
+    kw = dict(o=o, S_out=S_out, **prefill_kwargs(g, impl, B, T, H, dk, dv, ring_mb, ins["q"].dtype))
     kw.update(flags)
     for _ in range(warmup):
         fn(*args, ins["S0"], **kw)
@@ -185,7 +188,7 @@ def time_prefill_cold(g, ins, reps, impl):
     dv = ins["v"].shape[-1]
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.float32)
     S_out = torch.empty(B, H, dk, dv, device="cuda", dtype=torch.float32)
-    kw = dict(o=o, S_out=S_out, **prefill_kwargs(g, impl, B, T, H, dk, dv))
+    kw = dict(o=o, S_out=S_out, **prefill_kwargs(g, impl, B, T, H, dk, dv, dtype=ins["q"].dtype))
     fn = g.recurrent_fwd if impl == "recurrent" else g.chunk_fwd
     scrub = torch.empty(1 << 27, device="cuda", dtype=torch.float32)  # 512 MiB
     stream = torch.cuda.current_stream()
@@ -213,12 +216,16 @@ def prefill_leg(g, name, steps, impl):
     _, kern_ms = time_prefill(g, ins, steps, 1, impl)
     avg = sum(kern_ms) / len(kern_ms)
     head_tokens = wl.B * wl.T * wl.H
-    alg = prefill_bytes_per_head_token(wl.d_k, wl.d_v, wl.T) * head_tokens
+    fp32 = wl.dtype == "fp32"
+    alg = prefill_bytes_per_head_token(wl.d_k, wl.d_v, wl.T, 4 if fp32 else 2) * head_tokens
     res = dict(config=f"B{wl.B} H{wl.H} T{wl.T} d{wl.d_k} {wl.dtype} gates={wl.gates}",
                kernel_ms=round(avg, 4), tokens_per_s=round(wl.B * wl.T / (avg * 1e-3), 1))
     if wl.gates == "general":  # (scalar gates move fewer input bytes; no byte roofline quoted)
         res.update(gbs=round(alg / (avg * 1e-3) / 1e9, 1),
                    frac=round(alg / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    if fp32:  # fp32 operands run at the fp32 matrix-core rate, which bounds this path before HBM
+        tf = prefill_flops_per_head_token(wl.d_k, wl.d_v) * head_tokens / (avg * 1e-3) / 1e12
+        res.update(mfma_f32_tflops=round(tf, 1), mfma_f32_frac=round(tf / MFMA_F32_PEAK_TFLOPS, 4))
     print(f"[bench] {name}: {avg:.3f} ms/launch, {res['tokens_per_s']:.3e} tokens/s", file=sys.stderr,
           flush=True)
     del ins
@@ -636,8 +643,9 @@ def main(argv=None):
     if not args.skip_others and args.workload == "prefill_1p3b" and args.impl != "recurrent":
         for name, steps in (("long_prefill", 3), ("gdn_scalar", 10), ("kda_scalar", 10)):
             others[name] = prefill_leg(g, name, steps, args.impl)
-        if args.impl == "split":  # head size 256 runs on the two-kernel path only
+        if args.impl == "split":  # head size 256 and fp32 at d = 128 run on the two-kernel path only
             others["d256_prefill"] = prefill_leg(g, "d256_prefill", 10, args.impl)
+            others["fp32_prefill"] = prefill_leg(g, "fp32_prefill", 5, args.impl)
 
     dec = {}
     decode_runs = () if args.skip_decode else ((256, args.decode_steps),

@@ -10,6 +10,10 @@ namespace {
 using namespace chunk;
 
 
+// Value columns per chain workgroup: 64, or d below that; fp32 blocks at d = 128 (135 KB) leave
+// the chain kernel room for one block buffer and the v, w slots of 32 columns only.
+constexpr int split_dvt(int DK, bool bf16) { return !bf16 && DK >= 128 ? 32 : (DK < 64 ? DK : 64); }
+
 // Segments for a long sequence with few (b, h): enough that the chain fills the chip, each at
 // least 16 chunks long. nseg = 1 means no segmentation.
 struct SplitPlan {
@@ -17,9 +21,9 @@ struct SplitPlan {
     size_t extra_bytes;  // Psi/Phi and the segment start states
 };
 
-SplitPlan split_plan(int B, int T, int H, int DK, int DV) {
+SplitPlan split_plan(int B, int T, int H, int DK, int DV, bool bf16) {
     const int nch = (T + CH - 1) / CH;
-    const int DVT = DK < 64 ? DK : 64;
+    const int DVT = split_dvt(DK, bf16);
     const long wgs = (long)B * H * (DV / DVT);
     SplitPlan p{1, nch, 0};
     if (wgs < 256 && nch >= 32) {
@@ -38,7 +42,7 @@ SplitPlan split_plan(int B, int T, int H, int DK, int DV) {
 template <int DK, bool BF16, bool AS, bool BS, int PRO>
 hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     constexpr bool WS = (PRO & 2) != 0 && !BS;  // w through the sigmoid in the chain
-    constexpr int DVT = DK < 64 ? DK : 64;
+    constexpr int DVT = split_dvt(DK, BF16);
     using BL = Blob<DK, BF16>;
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
     const int nch = (a.T + CH - 1) / CH;
@@ -52,7 +56,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     const size_t avail = a.workspace_bytes - (a.S_out ? 0 : state_bytes);
     const size_t per_chunk = (size_t)BH * BL::bytes;
     const int tiles = a.DV / DVT;
-    const SplitPlan plan = split_plan(a.B, a.T, a.H, DK, a.DV);
+    const SplitPlan plan = split_plan(a.B, a.T, a.H, DK, a.DV, BF16);
     const long ld = DK;  // state rows are DK long in k, DV in v
     if (plan.nseg > 1 && avail >= (size_t)nch * per_chunk + plan.extra_bytes) {
         // segments: prep over all chunks; each segment's transition (Psi, Phi) from the state
@@ -175,18 +179,21 @@ hipError_t launch_split_states(const ChunkArgs& a, char* blobs, uint16_t* S_save
 bool split_supported(int T, int H, int DK, int DV, bool bf16) {
     if (DK != DV || T < 0) return false;
     if (bf16) return DK == 32 || DK == 64 || DK == 128;
-    return DK == 32;  // fp32 blobs of d = 64 or 128 exceed the chain kernel's LDS budget
+    return DK == 32;  // packed batches take fp32 blocks of d = 32 only
 }
 
-// gdn2_chunk_fwd's equal-length batches also take bf16 at d = 256 (one block buffer in the chain
-// kernel); the packed batches and the backward's state pass stay at d <= 128.
+// gdn2_chunk_fwd's equal-length batches also take bf16 at d = 256 and fp32 at d = 64 and 128 (one
+// block buffer in the chain kernel); the packed batches and the backward's state pass stay at
+// the sizes above.
 bool split_fwd_supported(int T, int H, int DK, int DV, bool bf16) {
-    return split_supported(T, H, DK, DV, bf16) || (bf16 && DK == 256 && DV == 256 && T >= 0);
+    if (split_supported(T, H, DK, DV, bf16)) return true;
+    if (DK != DV || T < 0) return false;
+    return bf16 ? DK == 256 : (DK == 64 || DK == 128);
 }
 
 size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16) {
     const size_t nch = ((size_t)T + CH - 1) / CH;
-    const SplitPlan plan = split_plan(B, T, H, DK, DV);
+    const SplitPlan plan = split_plan(B, T, H, DK, DV, bf16);
     return (size_t)B * H * DK * DV * 4 + nch * split_chunk_bytes(B, H, DK, bf16) + plan.extra_bytes;
 }
 
@@ -198,7 +205,7 @@ size_t split_chunk_bytes(int B, int H, int DK, bool bf16) {
                : DK == 128 ? Blob<128, true>::bytes
                            : Blob<256, true>::bytes;
     } else {
-        blob = Blob<32, false>::bytes;
+        blob = DK == 32 ? Blob<32, false>::bytes : DK == 64 ? Blob<64, false>::bytes : Blob<128, false>::bytes;
     }
     return (size_t)B * H * blob;
 }
@@ -214,7 +221,12 @@ hipError_t launch_split(const ChunkArgs& a, hipStream_t s) {
             default: return hipErrorNotSupported;
         }
     }
-    return a.DK == 32 ? launch_split_flags<32, false>(a, s) : hipErrorNotSupported;
+    switch (a.DK) {
+        case 32: return launch_split_flags<32, false>(a, s);
+        case 64: return launch_split_flags<64, false>(a, s);
+        case 128: return launch_split_flags<128, false>(a, s);
+        default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace gdn2

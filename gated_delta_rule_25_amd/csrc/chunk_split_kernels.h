@@ -93,8 +93,9 @@ struct PrepSmem {
     static constexpr int oAd = oA + CH * AP * ES;
     static constexpr int bytes = oAd + 4 * ADS * 4;
     static_assert(BL::oTm - BL::oKbT == DK * CHP * ES && out1Bytes == DK * CHP * ES + BL::TPE * ES, "layout");
-    // two workgroups per CU up to d = 128; at d = 256 one (its block alone is 110 KB)
-    static_assert(bytes <= (DK <= 128 ? 80 : 160) * 1024, "prep LDS budget");
+    // two workgroups per CU for fp16 blocks up to d = 128 and fp32 blocks of d = 32; one for fp16
+    // at d = 256 (its block alone is 110 KB) and fp32 at d = 64 and 128
+    static_assert(bytes <= ((F16 ? DK <= 128 : DK <= 32) ? 80 : 160) * 1024, "prep LDS budget");
 };
 
 // PRO (prologue): bit 0, q and k are L2-normalised over d_k per token here; bit 1, alpha and b

@@ -55,6 +55,8 @@ WORKLOADS = {
                            seed=20253),
     # head size 256 with the same 262,144 state floats per batch element (4 heads of 256 x 256)
     "d256_prefill": Workload("d256_prefill", B=8, T=4096, H=4, d_k=256, d_v=256, seed=20262),
+    # the 1.3B layer's shape with fp32 inputs (fp32 operands throughout)
+    "fp32_prefill": Workload("fp32_prefill", B=8, T=4096, H=16, d_k=128, d_v=128, dtype="fp32", seed=20263),
 }
 
 DECODE_WORKLOAD = dict(B=256, H=16, d_k=128, d_v=128, steps=1000, alpha_mu=3.0, s0_std=0.1,

@@ -104,8 +104,11 @@ enum {
  *    prep kernel, parallel over every (b, h, chunk), computes each chunk's decay-scaled factors,
  *    its 64x64 Gram products and the UT inverse T, and stores them as one operand block per chunk
  *    in the workspace; a chain kernel then runs the state recurrence chunk by chunk from those
- *    blocks. The fastest schedule at every size it takes. Supported: bf16 with d in {32, 64, 128},
- *    fp32 with d = 32, any flags. Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v]
+ *    blocks. The fastest schedule at every size it takes. Supported: bf16 with d in {32, 64, 128,
+ *    256}, fp32 with d in {32, 64, 128}, any flags (the operand blocks of bf16 at d = 256 and of
+ *    fp32 at d >= 64 are too large for two in the chain kernel's LDS: it keeps one and copies the
+ *    next after each chunk; fp32 at d = 128 runs 32 state columns per chain workgroup).
+ *    Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v]
  *    first when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand
  *    blocks. R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with
  *    fewer slots than chunks the two kernels alternate over rounds of R chunks. When B*H is too

@@ -100,7 +100,11 @@ def test_workspace_query_is_state_plus_one_slot_per_chunk(lib):
     assert per_chunk > 0 and per_chunk % 256 == 0
     assert q(8, 4096, 16, 128, 128, 0, 0) == state + 64 * per_chunk
     assert q(8, 4097, 16, 128, 128, 0, 0) == state + 65 * per_chunk  # ragged last chunk
-    assert q(8, 4096, 16, 128, 128, 1, 0) == 0  # fp32 at d = 128: no two-kernel path
+    # fp32 at d = 128: the two-kernel path with fp32 operand blocks, larger than the bf16 ones
+    per_chunk32 = q(8, 64, 16, 128, 128, 1, 0) - state
+    assert per_chunk32 > per_chunk and per_chunk32 % 256 == 0
+    assert q(8, 4096, 16, 128, 128, 1, 0) == state + 64 * per_chunk32
+    assert q(8, 4096, 16, 256, 256, 1, 0) == 0  # fp32 at d = 256: no two-kernel path
 
 
 def test_chunk_rejects_partial_state_alias(lib):

@@ -15,6 +15,8 @@ def test_prefill_bytes_per_head_token():
     # (2 x 128 x 128 x 4 = 131072) over T = 4096 tokens: 32
     assert bench.prefill_bytes_per_head_token(128, 128, 4096) == 1536 + 512 + 32
     assert bench.prefill_bytes_per_head_token(32, 32, 256) == 6 * 32 * 2 + 32 * 4 + 2 * 32 * 32 * 4 / 256
+    # fp32 inputs: 6 x 128 x 4 = 3072, o 512, the states 32
+    assert bench.prefill_bytes_per_head_token(128, 128, 4096, 4) == 3072 + 512 + 32
 
 
 def test_decode_bytes_per_head():

@@ -75,6 +75,43 @@ def test_chunk_fp32_matches_oracle(name, wl, schedule):
     _check(name, make_inputs(wl), TOL32, schedule)
 
 
+# fp32 at d = 128 runs the two-kernel path only (fp32 operand blocks, one block buffer and 32
+# state columns per chain workgroup): ragged T, S0 = 0, the scalar gate forms, strong decay, a
+# single token, and several rounds of a small workspace ring.
+FP32_D128_CASES = [
+    ("fp32_d128_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=2, dtype="fp32")),
+    ("fp32_d128_zero_s0", scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=3, s0_std=0.0, dtype="fp32")),
+    ("fp32_d128_gdn", scaled(WORKLOADS["gdn_scalar"], B=1, T=150, H=2, dtype="fp32")),
+    ("fp32_d128_kda", scaled(WORKLOADS["kda_scalar"], B=1, T=100, H=2, dtype="fp32")),
+    ("fp32_d128_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=1, T=190, H=2, alpha_mu=-2.0, dtype="fp32")),
+    ("fp32_d128_T1", scaled(WORKLOADS["prefill_1p3b"], B=2, T=1, H=2, dtype="fp32")),
+]
+
+
+@pytest.mark.parametrize("name,wl", FP32_D128_CASES, ids=[c[0] for c in FP32_D128_CASES])
+def test_chunk_fp32_d128_matches_oracle(name, wl):
+    banner(f"chunk fp32 d128 {name} {wl}")
+    _check(name, make_inputs(wl), TOL32, "split")
+
+
+def test_chunk_fp32_d128_small_ring():
+    banner("chunk fp32 d128, workspace ring of 2 chunk slots")
+    g = _g()
+    wl = scaled(WORKLOADS["prefill_1p3b"], B=1, T=300, H=2, dtype="fp32")
+    ins = make_inputs(wl)
+    d = _cuda(ins)
+    B, T, H, dk = d["q"].shape
+    per_chunk = g.chunk_fwd_workspace_bytes(B, 64, H, dk, dk, dtype=torch.float32) - B * H * dk * dk * 4
+    ws = torch.empty(B * H * dk * dk * 4 + 2 * per_chunk, dtype=torch.uint8, device="cuda")  # 2 of 5 slots
+    o, S_T = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["S0"], workspace=ws,
+                         schedule="split")
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(ins)
+    eo, es = normwise_err(o, o_ref), normwise_err(S_T, S_ref)
+    print(f"  fp32 d128 ring of 2: o err {eo:.2e}  S_T err {es:.2e}", flush=True)
+    assert eo <= TOL32 and es <= TOL32
+
+
 BF16_CASES = [
     ("bf16_d128_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=3)),
     ("bf16_d128_T1", scaled(WORKLOADS["prefill_1p3b"], B=1, T=1, H=2)),
@@ -217,6 +254,8 @@ SEGMENTED = [
     ("seg_bf16_kda", scaled(WORKLOADS["kda_scalar"], B=1, T=2100, H=2), TOL16),
     ("seg_bf16_d64", scaled(WORKLOADS["prefill_1p3b"], B=1, T=2500, H=2, d_k=64, d_v=64), TOL16),
     ("seg_fp32_d32", scaled(WORKLOADS["tiny_fp32"], B=1, T=2100, H=1, s0_std=0.1), TOL32),
+    ("seg_fp32_d128", scaled(WORKLOADS["prefill_1p3b"], B=1, T=2100, H=1, dtype="fp32"), TOL32),
+    ("seg_fp32_d64", scaled(WORKLOADS["prefill_1p3b"], B=1, T=2100, H=1, d_k=64, d_v=64, dtype="fp32"), TOL32),
     # strong decay: the segments' transitions decay far below fp32's normal range over a segment
     ("seg_bf16_strong_decay", scaled(WORKLOADS["prefill_1p3b"], B=1, T=3000, H=2, alpha_mu=-2.0), TOL16),
 ]
