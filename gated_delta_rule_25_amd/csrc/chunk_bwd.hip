@@ -390,7 +390,7 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
             const float4 x = staged(q);
             const unsigned off = row_off(t0 + rr0 + 16 * q);
             store_h4(rs_dDp, off / 2u, x);
-            store4(rs_dv, off, cw[q][0] * x.x, cw[q][1] * x.y, cw[q][2] * x.z, cw[q][3] * x.w);
+            store4<kStreamStore>(rs_dv, off, cw[q][0] * x.x, cw[q][1] * x.y, cw[q][2] * x.z, cw[q][3] * x.w);
             if constexpr (BS) {
                 // this row's sum over the wave's 16 columns (the four lanes of the row), one
                 // partial per row and 16-column group
@@ -400,7 +400,7 @@ __global__ void __launch_bounds__(bwd_chain_threads<DK>(), 1) bwd_chain_kernel(c
                 const int t = t0 + rr0 + 16 * q;
                 if (cc == 0 && t < Tq) io.dwp[((tbase + t) * H + hh) * io.npw + colw / 16] = p;
             } else {
-                store4(rs_dw, off, cs[q][0] * cv[q][0] * x.x, cs[q][1] * cv[q][1] * x.y, cs[q][2] * cv[q][2] * x.z,
+                store4<kStreamStore>(rs_dw, off, cs[q][0] * cv[q][0] * x.x, cs[q][1] * cv[q][1] * x.y, cs[q][2] * cv[q][2] * x.z,
                        cs[q][3] * cv[q][3] * x.w);
             }
         }
@@ -1099,20 +1099,25 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         x += __shfl_xor(x, 8);
         return x;
     };
+    // dq, dk, db, dalpha go out with the streaming store policy (no later kernel reads them),
+    // through buffer resources over the chunk's rows (rows past the end are dropped)
+    const unsigned gb = (unsigned)(H * DK * 4);
+    auto stream2 = [&](float* dst, int j, float x, float y) {
+        const unsigned off = (unsigned)((((rb + j) * H + hh) * DK + c0 + ch0) * 4);
+        const u32x2 v = {__float_as_uint(x), __float_as_uint(y)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rows_rsrc(dst, tbase, t0, Tq, gb, CH), (int)off, 0, kStreamStore);
+    };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = t0 + rb + j;
         float pb = 0.f;
         if constexpr (BS) pb = row_partial(yy[0][j] + yy[1][j]);
-        if (t < Tq) {
-            const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
-            *reinterpret_cast<float2*>(io.dq + e) = make_float2(xa[0][j], xa[1][j]);
-            *reinterpret_cast<float2*>(io.dk + e) = make_float2(xp[0][j], xp[1][j]);
-            if constexpr (BS) {
-                if (l16 == 0) io.dbp[((tbase + t) * H + hh) * NG + cg] = pb;
-            } else {
-                *reinterpret_cast<float2*>(io.db + e) = make_float2(yy[0][j], yy[1][j]);
-            }
+        stream2(io.dq, j, xa[0][j], xa[1][j]);
+        stream2(io.dk, j, xp[0][j], xp[1][j]);
+        if constexpr (BS) {
+            if (t < Tq && l16 == 0) io.dbp[((tbase + t) * H + hh) * NG + cg] = pb;
+        } else {
+            stream2(io.db, j, yy[0][j], yy[1][j]);
         }
     }
 
@@ -1152,13 +1157,10 @@ __global__ void __launch_bounds__(256, 2) bwd_key_kernel(const KeyIO io) {
         const int t = t0 + rb + j;
         float pa = 0.f;
         if constexpr (AS) pa = row_partial(dal[j][0] + dal[j][1]);
-        if (t < Tq) {
-            if constexpr (AS) {
-                if (l16 == 0) io.dap[((tbase + t) * H + hh) * NG + cg] = pa;
-            } else {
-                const size_t e = ((tbase + t) * H + hh) * DK + c0 + ch0;
-                *reinterpret_cast<float2*>(io.dalpha + e) = make_float2(dal[j][0], dal[j][1]);
-            }
+        if constexpr (AS) {
+            if (t < Tq && l16 == 0) io.dap[((tbase + t) * H + hh) * NG + cg] = pa;
+        } else {
+            stream2(io.dalpha, j, dal[j][0], dal[j][1]);
         }
     }
 }

@@ -959,8 +959,8 @@ chain_kernel(const ChainIO io) {
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                     for (int c = 0; c < NT; ++c)
-                        store4(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0] * isc, O[c][nt][1] * isc,
-                               O[c][nt][2] * isc, O[c][nt][3] * isc);
+                        store4<kStreamStore>(rs_o, op + 16u * nt * o_tok + 64u * c, O[c][nt][0] * isc,
+                                             O[c][nt][1] * isc, O[c][nt][2] * isc, O[c][nt][3] * isc);
             }
         } else if (copier && !SM::ONEBUF) {
             // copy waves: the next chunk's blob, then wait for the copies before the next
