@@ -10,9 +10,8 @@ namespace {
 using namespace chunk;
 
 
-// Value columns per chain workgroup: 64, or d below that; fp32 blocks at d = 128 (135 KB) leave
-// the chain kernel room for one block buffer and the v, w slots of 32 columns only.
-constexpr int split_dvt(int DK, bool bf16) { return !bf16 && DK >= 128 ? 32 : (DK < 64 ? DK : 64); }
+// Value columns per chain workgroup: 64, or d below that.
+constexpr int split_dvt(int DK, bool bf16) { return DK < 64 ? DK : 64; }
 
 // Segments for a long sequence with few (b, h): enough that the chain fills the chip, each at
 // least 16 chunks long. nseg = 1 means no segmentation.

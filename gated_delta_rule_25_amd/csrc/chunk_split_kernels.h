@@ -574,17 +574,20 @@ struct ChainSmem {
     static constexpr int NWC = DVT / (16 * NT);                 // chain waves
     static constexpr int CW0 = NT == 1 ? 4 : 2;                 // first copy wave = copy waves
     static constexpr int VWB = CH * 16 * NT * (F16 ? 2 : 4);  // one of v, w: 64 rows x 16 NT columns
+    // fp32 at d = 128: the v, w slots do not fit beside the 135 KB block, so the chain waves load
+    // their v, w straight into registers instead
+    static constexpr bool VWREG = !F16 && DK == 128;
     // Two block buffers (the copy of chunk n + 1 overlaps chunk n) when they fit; at d = 256 one
     // block is 110 KB, so there is one buffer, the copy follows the chunk, and the chain waves
     // make it themselves: no copy waves, so each chain wave has a SIMD and its 512 registers.
     static constexpr int BUF = SMALL ? (BL::stateBytes + 255) / 256 * 256 : BL::bytes;
-    static constexpr bool ONEBUF = SMALL || 2 * BL::bytes + NWC * 2 * VWB > 160 * 1024;
+    static constexpr bool ONEBUF = SMALL || 2 * BL::bytes + (VWREG ? 0 : NWC * 2 * VWB) > 160 * 1024;
     static constexpr int threads = ONEBUF ? NWC * 64 : kChainThreads;
     static_assert(ONEBUF || threads == 2 * CW0 * 64, "wave layout");
     static constexpr int oBuf0 = 0;
     static constexpr int oBuf1 = ONEBUF ? 0 : BUF;
     static constexpr int oVW = (ONEBUF ? 1 : 2) * BUF;          // per chain wave: v then w
-    static constexpr int bytes = oVW + NWC * 2 * VWB;
+    static constexpr int bytes = oVW + (VWREG ? 16 : NWC * 2 * VWB);
     static constexpr int min_blocks = (SMALL && bytes <= 80 * 1024) ? 2 : 1;
     static constexpr bool fits = bytes <= 160 * 1024 && NWC >= 1 && NWC <= CW0;
 };
@@ -763,6 +766,29 @@ chain_kernel(const ChainIO io) {
                                                          0, 0, 0);
         }
     };
+    // (VWREG) this lane's v, w of a chunk in registers, in the accumulator layout: rows
+    // 16 mt + 4 g + j, column col0 + 16 c + l16, through buffer resources over the chunk's rows
+    // (rows past the end arrive as zeros)
+    Raw vreg[NT][16], wreg[NT][16];
+    auto load_vw = [&](int n) {
+        if constexpr (SM::VWREG) {
+            const __amdgpu_buffer_rsrc_t rs_v = rows_rsrc(v, tbase, (long)n * CH, Tq, (unsigned)(H * DV * IES), CH);
+            const __amdgpu_buffer_rsrc_t rs_w = rows_rsrc(BS ? v : w, tbase, (long)n * CH, Tq, (unsigned)(H * DV * IES), CH);
+#pragma unroll
+            for (int c = 0; c < NT; ++c)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const unsigned row = (unsigned)(16 * mt + 4 * g + j);
+                        const int off = (int)(((row * H + hh) * DV + (unsigned)(col0 + 16 * c + l16)) * IES);
+                        vreg[c][4 * mt + j] = (Raw)__builtin_amdgcn_raw_buffer_load_b32(rs_v, off, 0, 0);
+                        if constexpr (!BS) wreg[c][4 * mt + j] = (Raw)__builtin_amdgcn_raw_buffer_load_b32(rs_w, off, 0, 0);
+                    }
+        } else {
+            dma_vw(n);
+        }
+    };
     auto raw_f = [](Raw r) { return BF16 ? __uint_as_float((uint32_t)r << 16) : __uint_as_float((uint32_t)r); };
     // two stacked 16-row accumulator tiles as one operand fragment (the kap() slot order)
     auto stack = [](const f4& lo, const f4& hi) {
@@ -799,7 +825,7 @@ chain_kernel(const ChainIO io) {
             dma_flat(blobs, smem + SM::oBuf0, COPY, wv - CW0, CW0, lane);
             wait_dma();
         } else if (chain && !phi) {
-            dma_vw(c_begin);
+            load_vw(c_begin);
         }
         if constexpr (SM::ONEBUF) {
             dma_flat(blobs, smem + SM::oBuf0, COPY, wv, NWC, lane);
@@ -853,9 +879,11 @@ chain_kernel(const ChainIO io) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * mt + 4 * g + j, slot = 16 * mt + 4 * j + g, cl = 16 * c + l16;
-                        float ww = BS ? betaL[row] : raw_f(w_l[slot * ROW + cl]);
+                        const Raw wr = SM::VWREG ? wreg[c][4 * mt + j] : w_l[slot * ROW + cl];
+                        const Raw vr = SM::VWREG ? vreg[c][4 * mt + j] : v_l[slot * ROW + cl];
+                        float ww = BS ? betaL[row] : raw_f(wr);
                         if constexpr (WSIG && !BS) ww = sigmoidf_(ww);
-                        D[c][mt][j] = phi ? 0.f : ww * raw_f(v_l[slot * ROW + cl]);
+                        D[c][mt][j] = phi ? 0.f : ww * raw_f(vr);
                     }
             if constexpr (SCALE) rescale_state<NMK>(Sacc[0], D[0], esc, sc, isc);
             float4 gcv[NMK];  // gamma_last of this lane's state rows
@@ -889,7 +917,7 @@ chain_kernel(const ChainIO io) {
             }
             if constexpr (F16) lookahead_schedule<(STATE ? 4 : 8) * NKS, 6, NT>();
             // the next chunk's v, w into this wave's slot, now that its reads are long done
-            if (nc + 1 < n_count && !phi) dma_vw(n + 1);
+            if (nc + 1 < n_count && !phi) load_vw(n + 1);
             if constexpr (SAVE) save_rows(io.Dp_save, D);
             // Delta = T D'
             Frag Df[NT][2];

@@ -107,7 +107,8 @@ enum {
  *    blocks. The fastest schedule at every size it takes. Supported: bf16 with d in {32, 64, 128,
  *    256}, fp32 with d in {32, 64, 128}, any flags (the operand blocks of bf16 at d = 256 and of
  *    fp32 at d >= 64 are too large for two in the chain kernel's LDS: it keeps one and copies the
- *    next after each chunk; fp32 at d = 128 runs 32 state columns per chain workgroup).
+ *    next after each chunk; at fp32 d = 128 its chain wavefronts also load v and w straight into
+ *    registers, for want of LDS room).
  *    Layout of the workspace: the fp32 state buffer [B, H, d_k, d_v]
  *    first when S_out is NULL (none when S_out is given), then R chunk slots of B*H operand
  *    blocks. R = (workspace_bytes - state bytes) / slot bytes chunks are prepared per round; with

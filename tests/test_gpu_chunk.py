@@ -75,9 +75,9 @@ def test_chunk_fp32_matches_oracle(name, wl, schedule):
     _check(name, make_inputs(wl), TOL32, schedule)
 
 
-# fp32 at d = 128 runs the two-kernel path only (fp32 operand blocks, one block buffer and 32
-# state columns per chain workgroup): ragged T, S0 = 0, the scalar gate forms, strong decay, a
-# single token, and several rounds of a small workspace ring.
+# fp32 at d = 128 runs the two-kernel path only (fp32 operand blocks, one block buffer, v and w
+# loaded into registers): ragged T, S0 = 0, the scalar gate forms, strong decay, a single token,
+# and several rounds of a small workspace ring.
 FP32_D128_CASES = [
     ("fp32_d128_ragged", scaled(WORKLOADS["prefill_1p3b"], B=2, T=200, H=2, dtype="fp32")),
     ("fp32_d128_zero_s0", scaled(WORKLOADS["prefill_1p3b"], B=1, T=130, H=3, s0_std=0.0, dtype="fp32")),
