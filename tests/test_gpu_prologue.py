@@ -45,6 +45,11 @@ CASES = [
     ("bf16_gdn_both", scaled(WORKLOADS["gdn_scalar"], B=1, T=200, H=2), True, True, TOL16),
     ("bf16_kda_both", scaled(WORKLOADS["kda_scalar"], B=1, T=200, H=2), True, True, TOL16),
     ("fp32_d32_both", scaled(WORKLOADS["tiny_fp32"], B=1, T=150, H=2, s0_std=0.1), True, True, TOL32),
+    # fp32 at d = 64 and 128 on the two-kernel path (one block buffer; v, w in registers at 128)
+    ("fp32_d128_both", scaled(WORKLOADS["prefill_1p3b"], B=1, T=150, H=2, dtype="fp32"), True, True, TOL32),
+    ("fp32_d128_kda_both", scaled(WORKLOADS["kda_scalar"], B=1, T=100, H=2, dtype="fp32"), True, True, TOL32),
+    ("fp32_d64_logits", scaled(WORKLOADS["prefill_1p3b"], B=2, T=90, H=2, d_k=64, d_v=64, dtype="fp32"), False, True,
+     TOL32),
 ]
 
 
@@ -66,7 +71,8 @@ def _inputs(wl, l2n, gl):
 @pytest.mark.parametrize("name,wl,l2n,gl,tol", CASES, ids=[c[0] for c in CASES])
 def test_chunk_prologue_matches_oracle(name, wl, l2n, gl, tol, schedule):
     if schedule == "fused" and wl.dtype == "fp32":
-        pytest.skip("fp32 inputs run the single kernel without a workspace, which takes no prologue flags")
+        pytest.skip("without a workspace fp32 inputs run the single kernel (d <= 64), which takes no "
+                    "prologue flags; fp32 at d = 128 runs with a workspace only")
     banner(f"prologue chunk {name} l2norm={l2n} logits={gl} schedule={schedule} {wl}")
     ins = _inputs(wl, l2n, gl)
     o_ref, S_ref = _oracle(ins, l2n, gl)
