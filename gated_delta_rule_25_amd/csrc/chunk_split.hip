@@ -11,7 +11,7 @@ using namespace chunk;
 
 
 // Value columns per chain workgroup: 64, or d below that.
-constexpr int split_dvt(int DK, bool bf16) { return DK < 64 ? DK : 64; }
+constexpr int split_dvt(int DK) { return DK < 64 ? DK : 64; }
 
 // Segments for a long sequence with few (b, h): enough that the chain fills the chip, each at
 // least 16 chunks long. nseg = 1 means no segmentation.
@@ -20,9 +20,9 @@ struct SplitPlan {
     size_t extra_bytes;  // Psi/Phi and the segment start states
 };
 
-SplitPlan split_plan(int B, int T, int H, int DK, int DV, bool bf16) {
+SplitPlan split_plan(int B, int T, int H, int DK, int DV) {
     const int nch = (T + CH - 1) / CH;
-    const int DVT = split_dvt(DK, bf16);
+    const int DVT = split_dvt(DK);
     const long wgs = (long)B * H * (DV / DVT);
     SplitPlan p{1, nch, 0};
     if (wgs < 256 && nch >= 32) {
@@ -41,7 +41,7 @@ SplitPlan split_plan(int B, int T, int H, int DK, int DV, bool bf16) {
 template <int DK, bool BF16, bool AS, bool BS, int PRO>
 hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     constexpr bool WS = (PRO & 2) != 0 && !BS;  // w through the sigmoid in the chain
-    constexpr int DVT = split_dvt(DK, BF16);
+    constexpr int DVT = split_dvt(DK);
     using BL = Blob<DK, BF16>;
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
     const int nch = (a.T + CH - 1) / CH;
@@ -55,7 +55,7 @@ hipError_t launch_split_t(const ChunkArgs& a, hipStream_t st) {
     const size_t avail = a.workspace_bytes - (a.S_out ? 0 : state_bytes);
     const size_t per_chunk = (size_t)BH * BL::bytes;
     const int tiles = a.DV / DVT;
-    const SplitPlan plan = split_plan(a.B, a.T, a.H, DK, a.DV, BF16);
+    const SplitPlan plan = split_plan(a.B, a.T, a.H, DK, a.DV);
     const long ld = DK;  // state rows are DK long in k, DV in v
     if (plan.nseg > 1 && avail >= (size_t)nch * per_chunk + plan.extra_bytes) {
         // segments: prep over all chunks; each segment's transition (Psi, Phi) from the state
@@ -121,7 +121,7 @@ hipError_t launch_split_flags(const ChunkArgs& a, hipStream_t s) {
 template <int DK, int PRO, bool AS, bool BS>
 hipError_t launch_states_t(const ChunkArgs& a, char* blobs, uint16_t* S_save, uint16_t* Dp_save, uint16_t* Dl_save,
                            hipStream_t st) {
-    constexpr int DVT = DK < 64 ? DK : 64;
+    constexpr int DVT = split_dvt(DK);
     const int BH = a.B * a.H, BHp = (BH + 7) / 8 * 8;
     const int nch = (a.T + CH - 1) / CH;
     hipLaunchKernelGGL((prep_kernel<DK, true, AS, BS, PRO>), dim3(BH * nch), dim3(256), 0, st, a.q, a.k,
@@ -192,7 +192,7 @@ bool split_fwd_supported(int T, int H, int DK, int DV, bool bf16) {
 
 size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16) {
     const size_t nch = ((size_t)T + CH - 1) / CH;
-    const SplitPlan plan = split_plan(B, T, H, DK, DV, bf16);
+    const SplitPlan plan = split_plan(B, T, H, DK, DV);
     return (size_t)B * H * DK * DV * 4 + nch * split_chunk_bytes(B, H, DK, bf16) + plan.extra_bytes;
 }
 

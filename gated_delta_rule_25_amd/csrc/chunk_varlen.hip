@@ -237,8 +237,14 @@ hipError_t launch_varlen_states(const ChunkArgs& a, char* table, char* blobs, lo
     }
 }
 
+// The packed forward takes the sizes of the equal-length two-kernel path except head size 256:
+// bf16 and fp32 at d in {32, 64, 128}.
+bool varlen_fwd_supported(int T, int H, int DK, int DV, bool bf16) {
+    return DK == DV && T >= 0 && (DK == 32 || DK == 64 || DK == 128);
+}
+
 hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s) {
-    if (!split_supported(a.T, a.H, a.DK, a.DV, a.bf16) || !a.cu_seqlens) return hipErrorNotSupported;
+    if (!varlen_fwd_supported(a.T, a.H, a.DK, a.DV, a.bf16) || !a.cu_seqlens) return hipErrorNotSupported;
     if (a.bf16) {
         switch (a.DK) {
             case 32: return launch_varlen_flags<32, true>(a, s);
@@ -247,7 +253,12 @@ hipError_t launch_split_varlen(const ChunkArgs& a, hipStream_t s) {
             default: return hipErrorNotSupported;
         }
     }
-    return launch_varlen_flags<32, false>(a, s);
+    switch (a.DK) {
+        case 32: return launch_varlen_flags<32, false>(a, s);
+        case 64: return launch_varlen_flags<64, false>(a, s);
+        case 128: return launch_varlen_flags<128, false>(a, s);
+        default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace gdn2

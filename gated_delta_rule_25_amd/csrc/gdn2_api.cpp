@@ -241,7 +241,7 @@ gdn2_status varlen_fwd(const void* q, const void* k, const void* v, const void* 
                              static_cast<hipStream_t>(stream));
     if (!workspace) return GDN2_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
-    if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
+    if (!gdn2::varlen_fwd_supported(T_total, H, d_k, d_v, bf16)) return GDN2_ERR_UNSUPPORTED;
     // one workgroup per (chunk bound, head) in prep and per (sequence, head, value tile) in the
     // chain: both grids (in threads) must stay below 2^31
     if (gdn2::varlen_chunk_bound(N, T_total) * H * 256 >= (1l << 31)) return GDN2_ERR_SHAPE;
@@ -344,7 +344,7 @@ size_t gdn2_chunk_fwd_varlen_workspace_bytes(int32_t N, int32_t T_total, int32_t
                                              int32_t d_v, gdn2_dtype in_dtype, uint32_t gate_flags) {
     if (N <= 0 || H <= 0 || T_total < 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
     const bool bf16 = in_dtype == GDN2_BF16;
-    if (!gdn2::split_supported(T_total, H, d_k, d_v, bf16)) return 0;
+    if (!gdn2::varlen_fwd_supported(T_total, H, d_k, d_v, bf16)) return 0;
     return gdn2::varlen_workspace_bytes(N, T_total, H, d_k, d_v, bf16);
 }
 

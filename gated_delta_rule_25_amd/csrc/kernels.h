@@ -105,6 +105,7 @@ bool fused_supported(int T, int H, int DK, int DV, bool bf16);
 hipError_t launch_split(const ChunkArgs& a, hipStream_t s);
 bool split_supported(int T, int H, int DK, int DV, bool bf16);
 bool split_fwd_supported(int T, int H, int DK, int DV, bool bf16);  // also bf16 d = 256
+bool varlen_fwd_supported(int T, int H, int DK, int DV, bool bf16);  // packed batches, forward
 size_t split_chunk_bytes(int B, int H, int DK, bool bf16);
 size_t split_workspace_bytes(int B, int T, int H, int DK, int DV, bool bf16);
 // Two-kernel path over a packed batch of a.B sequences, a.T rows in all, delimited by

@@ -174,7 +174,8 @@ def test_varlen_rejects_bad_arguments(lib):
     need = qs(4, 1000, 2, 128, 128, 0, 0)
     # table (4 N + 1 ints, padded to 256 B) then (T + 63 N) / 64 = 19 chunks per head
     assert need == 256 + 19 * 2 * (qs(1, 64, 1, 128, 128, 0, 0) - 256)
-    assert qs(4, 1000, 2, 128, 128, 1, 0) == 0      # fp32 at d = 128: not supported
+    assert qs(4, 1000, 2, 128, 128, 1, 0) > need    # fp32 at d = 128: larger operand blocks
+    assert qs(4, 1000, 2, 256, 256, 0, 0) == 0      # head size 256: not in packed batches
     assert qs(0, 1000, 2, 128, 128, 0, 0) == 0
 
     def call(ptrs=p, cu=cu, N=4, T=1000, H=2, dk=128, dv=128, dt=0, flags=0, ws=ws, wsb=need):
@@ -188,7 +189,7 @@ def test_varlen_rejects_bad_arguments(lib):
     assert call(wsb=need - 1) == 7
     assert call(ws=P(0x200000000 * 11 + 128)) == 4     # workspace not 256-byte aligned
     assert call(dk=256, dv=256) == 3
-    assert call(dt=1) == 3                             # fp32 at d = 128
+    assert call(dt=1) == 7                             # fp32 at d = 128: the bf16 workspace is too small
     assert call(flags=32) == 3
     assert call(cu=P(0x200000000 * 8)) == 5            # cu_seqlens overlaps o
     q = list(p)

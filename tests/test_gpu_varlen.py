@@ -75,6 +75,9 @@ CASES = [
     ("bf16_kda", scaled(WORKLOADS["kda_scalar"], H=2), [3, 150, 0], TOL16),
     ("bf16_zero_S0", scaled(WORKLOADS["prefill_1p3b"], H=2, s0_std=0.0), [90, 40], TOL16),
     ("fp32_d32", scaled(WORKLOADS["tiny_fp32"], s0_std=0.1), [0, 77, 64, 129], TOL32),
+    ("fp32_d64", scaled(WORKLOADS["prefill_1p3b"], H=2, d_k=64, d_v=64, dtype="fp32"), [5, 130, 1, 64], TOL32),
+    ("fp32_d128", scaled(WORKLOADS["prefill_1p3b"], H=2, dtype="fp32"), [0, 77, 200, 65], TOL32),
+    ("fp32_d128_kda", scaled(WORKLOADS["kda_scalar"], H=2, dtype="fp32"), [90, 3], TOL32),
 ]
 
 
