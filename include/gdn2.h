@@ -172,7 +172,7 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
  *
  * Same two kernels as the workspace path of gdn2_chunk_fwd (one round, no segments), preceded by
  * a one-workgroup kernel that builds the sequence table. Supported sizes and errors as there:
- * bf16 with d in {32, 64, 128}, fp32 with d = 32, d_k == d_v, any flags; GDN2_ERR_NULL without cu_seqlens, GDN2_ERR_WORKSPACE without a workspace or with
+ * bf16 and fp32 with d in {32, 64, 128}, d_k == d_v, any flags; GDN2_ERR_NULL without cu_seqlens, GDN2_ERR_WORKSPACE without a workspace or with
  * fewer bytes than the query returns, GDN2_ERR_ALIGN for a cu_seqlens not 4-byte aligned or a
  * workspace not 256-byte aligned, GDN2_ERR_ALIAS when an output or the workspace overlaps
  * anything else (S_out == S0 excepted), GDN2_ERR_SHAPE for N <= 0 or T_total < 0.
