@@ -67,15 +67,16 @@ struct FusedSmem {
 };
 
 // Barrier over the four prep waves: each adds one to an LDS counter and waits until all four
-// have arrived at this step (target advances by 4 per step). The wait is bounded (about 0.1 s),
-// so a wave can never hang here.
+// have arrived at this step (target advances by 4 per step). The wait polls the counter without
+// sleeping between reads (a sleep of one unit, 64 cycles, between polls measured 1.3% slower on
+// the whole call) and is bounded at 2^22 polls (well under a second), so a wave can never hang
+// here.
 __device__ __forceinline__ void prep_sync(unsigned* ctr, unsigned& target, int lane) {
     target += 4u;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     for (unsigned spin = 0; spin < (1u << 22); ++spin) {
         if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
